@@ -1,0 +1,187 @@
+"""Python access to the double-precision oracle in ``ss_oracle.c``.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It never touches the
+GPU library and shares no code with it.
+
+Every input is widened exactly to float64 (float32 and bfloat16 values are
+representable in double), passed to the C routines, and the results come
+back as float64 numpy arrays.  The arithmetic itself lives entirely in
+``ss_oracle.c``; this file only marshals arrays and, when asked for more
+than one thread, splits independent rows (forward, state update) or batch
+entries (backward) across threads and folds the per-thread parameter
+gradients in ascending batch order.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ss_oracle.c")
+_LIB = os.path.join(_HERE, "libss_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ``ss_oracle.c`` with gcc (-O2, IEEE semantics, no fast-math)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    fd, tmp = tempfile.mkstemp(suffix=".so", dir=_HERE)
+    os.close(fd)
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            # The mutation test points this at a deliberately broken copy of
+            # the oracle to show that the pins catch each planted mistake.
+            path = os.environ.get("SS_ORACLE_LIB_OVERRIDE") or build()
+            lib = ctypes.CDLL(path)
+            i64, dp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+            lib.sso_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 8 + [c_int] + [dp] * 3 + [i64, i64]
+            lib.sso_fwd.restype = None
+            lib.sso_bwd.argtypes = ([i64, i64, i64, i64] + [dp] * 8 + [c_int] + [dp] * 12
+                                    + [i64, i64])
+            lib.sso_bwd.restype = c_int
+            lib.sso_state_update.argtypes = ([i64, i64, i64] + [dp] * 9 + [c_int] + [dp]
+                                             + [i64, i64])
+            lib.sso_state_update.restype = None
+            _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _split(n: int, parts: int):
+    parts = max(1, min(parts, n)) if n > 0 else 1
+    edges = [n * i // parts for i in range(parts + 1)]
+    return [(edges[i], edges[i + 1]) for i in range(parts)]
+
+
+def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+        h0=None, threads: int = 1):
+    """Forward scan.  Returns ``(y, last_state)`` as float64 arrays.
+
+    u, delta, z: (batch, dim, L); A: (dim, N); B, C: (batch, N, L);
+    D, delta_bias: (dim,); h0: (batch, dim, N) or None (zero initial state).
+    """
+    lib = _load()
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
+    nb, nd, nl = u.shape
+    ns = A.shape[1]
+    y = np.zeros((nb, nd, nl))
+    last = np.zeros((nb, nd, ns))
+    args = (nb, nd, ns, nl, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
+            _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(y), _p(last))
+    rows = nb * nd
+    if threads <= 1 or rows < 2:
+        lib.sso_fwd(*args, 0, rows)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda rg: lib.sso_fwd(*args, rg[0], rg[1]), _split(rows, threads)))
+    return y, last
+
+
+def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+        dout=None, h0=None, dlast=None, threads: int = 1):
+    """Backward of ``sum(dout * y) (+ sum(dlast * last_state))``.
+
+    Returns a dict with du, ddelta, dA, dB, dC and, for the optional inputs
+    that were given, dD, dz, ddelta_bias, dh0 (float64 arrays).
+    """
+    lib = _load()
+    u, delta, A, B, C, dout = map(_f64, (u, delta, A, B, C, dout))
+    D, z, delta_bias, h0, dlast = map(_f64, (D, z, delta_bias, h0, dlast))
+    nb, nd, nl = u.shape
+    ns = A.shape[1]
+    du = np.zeros((nb, nd, nl))
+    ddelta = np.zeros((nb, nd, nl))
+    dB = np.zeros((nb, ns, nl))
+    dC = np.zeros((nb, ns, nl))
+    dz = np.zeros((nb, nd, nl)) if z is not None else None
+    dh0 = np.zeros((nb, nd, ns)) if h0 is not None else None
+    pieces = _split(nb, threads)
+    # per-piece parameter gradients, folded below in ascending batch order
+    part = [(np.zeros((nd, ns)), np.zeros(nd), np.zeros(nd)) for _ in pieces]
+
+    def run(i):
+        b0, b1 = pieces[i]
+        dA_i, dD_i, db_i = part[i]
+        rc = lib.sso_bwd(nb, nd, ns, nl, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
+                         _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(dout),
+                         _p(dlast), _p(du), _p(ddelta), _p(dA_i), _p(dB), _p(dC), _p(dD_i),
+                         _p(dz), _p(db_i), _p(dh0), b0, b1)
+        if rc != 0:
+            raise MemoryError("oracle backward could not allocate scratch")
+
+    if len(pieces) == 1:
+        run(0)
+    else:
+        with ThreadPoolExecutor(len(pieces)) as ex:
+            list(ex.map(run, range(len(pieces))))
+    dA = np.zeros((nd, ns))
+    dD = np.zeros(nd)
+    dbias = np.zeros(nd)
+    for dA_i, dD_i, db_i in part:
+        dA += dA_i
+        dD += dD_i
+        dbias += db_i
+    out = dict(du=du, ddelta=ddelta, dA=dA, dB=dB, dC=dC)
+    if D is not None:
+        out["dD"] = dD
+    if z is not None:
+        out["dz"] = dz
+    if delta_bias is not None:
+        out["ddelta_bias"] = dbias
+    if h0 is not None:
+        out["dh0"] = dh0
+    return out
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                 delta_softplus=False, threads: int = 1):
+    """One-token update.  Returns ``(new_state, y)``; the input is not modified.
+
+    state: (batch, dim, N); u, delta, z: (batch, dim); B, C: (batch, N).
+    """
+    lib = _load()
+    st = _f64(state).copy()
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias = map(_f64, (D, z, delta_bias))
+    nb, nd = u.shape
+    ns = A.shape[1]
+    y = np.zeros((nb, nd))
+    args = (nb, nd, ns, _p(st), _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
+            _p(delta_bias), int(bool(delta_softplus)), _p(y))
+    rows = nb * nd
+    if threads <= 1 or rows < 2:
+        lib.sso_state_update(*args, 0, rows)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda rg: lib.sso_state_update(*args, rg[0], rg[1]),
+                        _split(rows, threads)))
+    return st, y

@@ -1,0 +1,247 @@
+/*
+ * ss_oracle.c -- plain, sequential, double-precision reference of the Mamba
+ * selective scan: forward, reverse-time backward and the one-token state
+ * update.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this code.  The GPU library neither
+ * includes, links nor calls it, and the two share no source, header, table
+ * or helper.  Everything here is written for a reader to check by eye: one
+ * row at a time, one time step at a time, one state index at a time, in
+ * double precision, with no blocking, no fusion and no reordering.
+ *
+ * What is computed.  The state-spaces/mamba README (section "Usage",
+ * subsection "Selective SSM") names the selective SSM layer of the Mamba
+ * paper (its Section 3 and Algorithm 2) as the operation; the mamba-rs
+ * README (section "Features") adds the full backward pass through the
+ * recurrent state, and its "Quick start (CPU)" section the single-token
+ * step on a carried state.  The pages print no formula.  The reading used
+ * here is the input-dependent diagonal SSM with a zero-order-hold decay and
+ * an Euler input term, per channel d and state index n:
+ *
+ *   delta_t  = delta_raw_t + bias[d]            (bias optional, else 0)
+ *   delta_t  = softplus(delta_t)                (only if the flag is set)
+ *   h_t[n]   = exp(delta_t * A[d,n]) * h_{t-1}[n] + delta_t * B_t[n] * u_t
+ *   y_t      = (sum_n C_t[n] * h_t[n] + D[d] * u_t) * silu(z_t)
+ *
+ * with h_{-1} = h0 (zero when no initial state is given), silu(z) =
+ * z * sigmoid(z), the gate applied only when z is given and the D term only
+ * when D is given.  The bias enters the range of delta as the projection
+ * bias the README's "Troubleshooting / Initialization" section describes.
+ *
+ * Layouts (row-major, contiguous):
+ *   u, delta, z, y, dout, du, ddelta, dz : (nb, nd, nl)
+ *   B, C, dB, dC                         : (nb, ns, nl)
+ *   A, dA                                : (nd, ns)
+ *   D, bias, dD, dbias                   : (nd)
+ *   h0, last_state, dlast, dh0           : (nb, nd, ns)
+ * where nb = batch, nd = channels (d_inner), ns = d_state, nl = sequence
+ * length.  A "row" is one (b, d) pair, row index r = b * nd + d.
+ *
+ * Parity: pinned.  The tests check this file against closed forms (one
+ * step, pure decay, geometric series), a brute-force time-invariant
+ * convolution written independently, hand-derived worked examples, and
+ * central finite differences / adjoint identities for the backward.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* softplus(x) = log(1 + exp(x)), evaluated without overflow. */
+static double sso_softplus(double x)
+{
+    double ax = x < 0 ? -x : x;
+    return (x > 0 ? x : 0.0) + log1p(exp(-ax));
+}
+
+/* sigmoid(x) = 1 / (1 + exp(-x)), evaluated without overflow. */
+static double sso_sigmoid(double x)
+{
+    if (x >= 0) return 1.0 / (1.0 + exp(-x));
+    double e = exp(x);
+    return e / (1.0 + e);
+}
+
+/* delta after the optional bias and the optional softplus. */
+static double sso_prep_delta(double raw, const double *bias, int64_t d, int softplus)
+{
+    double x = raw + (bias ? bias[d] : 0.0);
+    return softplus ? sso_softplus(x) : x;
+}
+
+/*
+ * Forward scan for rows [row_begin, row_end).
+ * y (nb, nd, nl) is required; last_state (nb, nd, ns) may be NULL.
+ */
+void sso_fwd(int64_t nb, int64_t nd, int64_t ns, int64_t nl,
+             const double *u, const double *delta, const double *A,
+             const double *B, const double *C, const double *D,
+             const double *z, const double *bias, int softplus,
+             const double *h0, double *y, double *last_state,
+             int64_t row_begin, int64_t row_end)
+{
+    (void)nb;
+    double *h = (double *)malloc(sizeof(double) * (size_t)(ns > 0 ? ns : 1));
+    if (!h) abort();
+    for (int64_t r = row_begin; r < row_end; r++) {
+        int64_t b = r / nd, d = r % nd;
+        for (int64_t n = 0; n < ns; n++)
+            h[n] = h0 ? h0[r * ns + n] : 0.0;
+        for (int64_t t = 0; t < nl; t++) {
+            double ut = u[r * nl + t];
+            double dt = sso_prep_delta(delta[r * nl + t], bias, d, softplus);
+            double acc = 0.0;
+            for (int64_t n = 0; n < ns; n++) {
+                double abar = exp(dt * A[d * ns + n]);
+                double bt = B[(b * ns + n) * nl + t];
+                h[n] = abar * h[n] + dt * bt * ut;
+                acc += C[(b * ns + n) * nl + t] * h[n];
+            }
+            double ypre = acc + (D ? D[d] * ut : 0.0);
+            if (z) {
+                double zt = z[r * nl + t];
+                ypre *= zt * sso_sigmoid(zt);
+            }
+            y[r * nl + t] = ypre;
+        }
+        if (last_state)
+            for (int64_t n = 0; n < ns; n++)
+                last_state[r * ns + n] = h[n];
+    }
+    free(h);
+}
+
+/*
+ * Backward (reverse-time BPTT) of the loss  sum_{r,t} dout[r,t] * y[r,t]
+ * (+ sum dlast * last_state when dlast is given) for batch entries
+ * [b_begin, b_end).
+ *
+ * Per-step outputs du, ddelta (with respect to the raw delta argument) and
+ * dz (when z is given) are written for the rows of those batch entries;
+ * dB and dC are written for those batch entries (summed over every channel
+ * d in ascending d).  dA, dD and dbias are ADDED to (the caller zeroes them
+ * and, when it splits the batch, folds the pieces in ascending b); dh0 is
+ * written when non-NULL.  Returns 0, or -1 if scratch memory is unavailable.
+ *
+ * The adjoint g_t[n] = dLoss/dh_t[n] obeys, going backward in time,
+ *   g_t = C_t * dy_t + exp(delta_{t+1} A) * g_{t+1},  g_{nl-1} seeded by dlast,
+ * where dy_t = dout_t * silu(z_t) is the gradient at the pre-gate output.
+ */
+int sso_bwd(int64_t nb, int64_t nd, int64_t ns, int64_t nl,
+            const double *u, const double *delta, const double *A,
+            const double *B, const double *C, const double *D,
+            const double *z, const double *bias, int softplus,
+            const double *h0, const double *dout, const double *dlast,
+            double *du, double *ddelta, double *dA, double *dB, double *dC,
+            double *dD, double *dz, double *dbias, double *dh0,
+            int64_t b_begin, int64_t b_end)
+{
+    (void)nb;
+    size_t nsz = (size_t)(ns > 0 ? ns : 1);
+    size_t nlz = (size_t)(nl > 0 ? nl : 1);
+    double *hs = (double *)malloc(sizeof(double) * nsz * (nlz + 1)); /* h_{t-1} at hs[t*ns] */
+    double *dl = (double *)malloc(sizeof(double) * nlz);
+    double *g = (double *)malloc(sizeof(double) * nsz);
+    if (!hs || !dl || !g) {
+        free(hs); free(dl); free(g);
+        return -1;
+    }
+    for (int64_t b = b_begin; b < b_end; b++) {
+        for (int64_t n = 0; n < ns; n++)
+            for (int64_t t = 0; t < nl; t++) {
+                dB[(b * ns + n) * nl + t] = 0.0;
+                dC[(b * ns + n) * nl + t] = 0.0;
+            }
+        for (int64_t d = 0; d < nd; d++) {
+            int64_t r = b * nd + d;
+            /* forward again, keeping every state: hs[(t+1)*ns + n] = h_t[n] */
+            for (int64_t n = 0; n < ns; n++)
+                hs[n] = h0 ? h0[r * ns + n] : 0.0;
+            for (int64_t t = 0; t < nl; t++) {
+                dl[t] = sso_prep_delta(delta[r * nl + t], bias, d, softplus);
+                for (int64_t n = 0; n < ns; n++) {
+                    double abar = exp(dl[t] * A[d * ns + n]);
+                    hs[(t + 1) * ns + n] = abar * hs[t * ns + n]
+                                         + dl[t] * B[(b * ns + n) * nl + t] * u[r * nl + t];
+                }
+            }
+            /* backward in time */
+            for (int64_t n = 0; n < ns; n++)
+                g[n] = dlast ? dlast[r * ns + n] : 0.0;
+            for (int64_t t = nl - 1; t >= 0; t--) {
+                double ut = u[r * nl + t];
+                double dout_t = dout[r * nl + t];
+                const double *h_t = hs + (t + 1) * ns;
+                const double *h_prev = hs + t * ns;
+                double dy = dout_t;
+                if (z) {
+                    double ypre = D ? D[d] * ut : 0.0;
+                    for (int64_t n = 0; n < ns; n++)
+                        ypre += C[(b * ns + n) * nl + t] * h_t[n];
+                    double zt = z[r * nl + t];
+                    double s = sso_sigmoid(zt);
+                    dy = dout_t * zt * s;
+                    dz[r * nl + t] = dout_t * ypre * s * (1.0 + zt * (1.0 - s));
+                }
+                if (D) dD[d] += dy * ut;
+                double sum_gb = 0.0, d_dt = 0.0;
+                for (int64_t n = 0; n < ns; n++) {
+                    double bt = B[(b * ns + n) * nl + t];
+                    double ct = C[(b * ns + n) * nl + t];
+                    double a = A[d * ns + n];
+                    double abar = exp(dl[t] * a);
+                    g[n] += ct * dy;                          /* g_t */
+                    dC[(b * ns + n) * nl + t] += dy * h_t[n];
+                    dB[(b * ns + n) * nl + t] += g[n] * dl[t] * ut;
+                    sum_gb += g[n] * bt;
+                    d_dt += g[n] * (a * abar * h_prev[n] + bt * ut);
+                    dA[d * ns + n] += g[n] * dl[t] * abar * h_prev[n];
+                    g[n] *= abar;                             /* carried to t-1 */
+                }
+                du[r * nl + t] = dl[t] * sum_gb + (D ? D[d] * dy : 0.0);
+                double raw_grad = d_dt;
+                if (softplus)
+                    raw_grad *= sso_sigmoid(delta[r * nl + t] + (bias ? bias[d] : 0.0));
+                ddelta[r * nl + t] = raw_grad;
+                if (bias) dbias[d] += raw_grad;
+            }
+            if (dh0)
+                for (int64_t n = 0; n < ns; n++)
+                    dh0[r * ns + n] = g[n];
+        }
+    }
+    free(hs); free(dl); free(g);
+    return 0;
+}
+
+/*
+ * One-token state update for rows [row_begin, row_end): the forward
+ * recurrence advanced by a single step from the carried state, which is
+ * overwritten in place (mamba-rs README, "Quick start (CPU)": the step call
+ * on a carried MambaState).
+ *   u, delta, z, y : (nb, nd);  B, C : (nb, ns);  state : (nb, nd, ns).
+ */
+void sso_state_update(int64_t nb, int64_t nd, int64_t ns,
+                      double *state, const double *u, const double *delta,
+                      const double *A, const double *B, const double *C,
+                      const double *D, const double *z, const double *bias,
+                      int softplus, double *y, int64_t row_begin, int64_t row_end)
+{
+    (void)nb;
+    for (int64_t r = row_begin; r < row_end; r++) {
+        int64_t b = r / nd, d = r % nd;
+        double ut = u[r];
+        double dt = sso_prep_delta(delta[r], bias, d, softplus);
+        double acc = 0.0;
+        for (int64_t n = 0; n < ns; n++) {
+            double abar = exp(dt * A[d * ns + n]);
+            double *h = state + r * ns + n;
+            *h = abar * *h + dt * B[b * ns + n] * ut;
+            acc += C[b * ns + n] * *h;
+        }
+        double ypre = acc + (D ? D[d] * ut : 0.0);
+        if (z) ypre *= z[r] * sso_sigmoid(z[r]);
+        y[r] = ypre;
+    }
+}
