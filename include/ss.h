@@ -1,0 +1,144 @@
+/*
+ * ss.h -- C ABI of the MI355X (gfx950) selective state-space scan library
+ * (libss.so).
+ *
+ * The operation is the selective SSM layer of Mamba -- named by the
+ * state-spaces/mamba README, section "Usage", subsection "Selective SSM"
+ * (the paper's Section 3, Algorithm 2) -- with the full backward pass
+ * through the recurrent state and the single-token step on a carried state
+ * (mamba-rs README, sections "Features" and "Quick start (CPU)").  The pages
+ * print no formula; this library computes, for every batch entry b, channel
+ * d and state index n:
+ *
+ *   delta_t  = delta_raw_t + delta_bias[d]          (bias optional)
+ *   delta_t  = softplus(delta_t)                    (if delta_softplus != 0)
+ *   h_t[n]   = exp(delta_t * A[d,n]) * h_{t-1}[n] + delta_t * B[b,n,t] * u_t
+ *   y_t      = (sum_n C[b,n,t] * h_t[n] + D[d] * u_t) * silu(z_t)
+ *
+ * with h_{-1} = h0 (zero when h0 is NULL), silu(z) = z * sigmoid(z) applied
+ * only when z is given, and the D term only when D is given.
+ *
+ * Layouts: row-major and contiguous (no strides).
+ *   u, delta, z, out, dout, du, ddelta, dz : (batch, dim, seqlen)   io dtype
+ *   B, C, dB, dC                           : (batch, dstate, seqlen) io dtype
+ *   A, dA                                  : (dim, dstate)           float
+ *   D, delta_bias, dD, ddelta_bias         : (dim)                   float
+ *   h0, last_state, dlast, dh0             : (batch, dim, dstate)    float
+ *   decode: u, delta, z, out (batch, dim); B, C (batch, dstate);
+ *           state (batch, dim, dstate) float, updated in place.
+ *
+ * Numerics.  Inputs are widened exactly to f32; every step, state and
+ * reduction runs in f32 (mamba-rs README, "Features": every kernel
+ * accumulates in f32; state-spaces/mamba README, "Troubleshooting /
+ * Precision": recurrent parameters kept in f32).  bf16 outputs are rounded
+ * to nearest-even once, at the store.  Results are deterministic: the same
+ * inputs give the same bits on every call, there are no floating-point
+ * atomics, and every reduction runs in an order fixed by (dim, dstate,
+ * seqlen) alone -- so a row's forward output and decode step are
+ * bit-identical whatever the batch size (the batch-invariance contract of
+ * the mamba-rs GEMM-modes page, "What is guaranteed").
+ *
+ * Ownership and streams.  Every pointer except the host scalars is device
+ * memory owned by the caller; the library allocates nothing.  Outputs are
+ * overwritten, never accumulated into, and must not alias any input (the
+ * decode state is the one in-place operand).  Every call enqueues its
+ * kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ * returns without synchronizing.
+ *
+ * Errors.  Arguments are validated on the host before anything is
+ * launched; on failure nothing is enqueued, the call returns a non-zero
+ * ss_status and ss_last_error() (thread-local) names the argument or the
+ * HIP call that failed.  Launch failures return SS_EDEVICE.
+ */
+#ifndef SS_H
+#define SS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_ABI_VERSION 1
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+typedef enum {
+    SS_OK = 0,
+    SS_EINVAL = 1,       /* bad argument: null/misaligned pointer, bad size, bad combination */
+    SS_EUNSUPPORTED = 2, /* valid request this build does not implement (e.g. dstate != 16) */
+    SS_EDEVICE = 3       /* a HIP call or kernel launch failed */
+} ss_status;
+
+/* SS_ABI_VERSION of the loaded library. */
+int ss_abi_version(void);
+
+/* Message of the last failed call on this thread ("" after a success). */
+const char *ss_last_error(void);
+
+/*
+ * Forward scan.  Writes out (batch, dim, seqlen) and, when last_state is
+ * non-NULL, the final state h_{seqlen-1} (h0 when seqlen == 0).
+ *   dstate            must be 16 (SS_EUNSUPPORTED otherwise).
+ *   io_dtype          SS_F32 or SS_BF16: dtype of u, delta, B, C, z, out.
+ *   D, z, delta_bias, h0, last_state may be NULL.
+ *   batch, dim, seqlen >= 0; a zero size enqueues nothing but the
+ *   last_state copy/zero fill it implies.
+ *   All pointers 16-byte aligned.
+ */
+ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *B,
+                 const void *C, const float *D, const void *z, const float *delta_bias,
+                 int delta_softplus, const float *h0, void *out, float *last_state,
+                 void *stream);
+
+/* Bytes of device workspace ss_bwd needs for this shape (0 for empty shapes). */
+size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                             int io_dtype);
+
+/*
+ * Backward (reverse-time BPTT) of the loss
+ *     sum(dout * out) + sum(dlast * last_state)
+ * with respect to every input of ss_fwd with the same arguments.
+ *   dout               (batch, dim, seqlen) io dtype; required.
+ *   dlast              (batch, dim, dstate) f32 or NULL (no gradient on last_state).
+ *   du, ddelta         required; ddelta is the gradient w.r.t. the raw delta argument.
+ *   dA                 required, (dim, dstate); summed over batch and time.
+ *   dB, dC             required, (batch, dstate, seqlen); summed over channels.
+ *   dD                 NULL iff D is NULL; summed over batch and time.
+ *   dz                 NULL iff z is NULL.
+ *   ddelta_bias        NULL iff delta_bias is NULL; summed over batch and time.
+ *   dh0                optional (may be non-NULL with h0 NULL: gradient at a zero start).
+ *   workspace          device memory of at least ss_bwd_workspace_size() bytes,
+ *                      16-byte aligned, owned by the caller, not read before written.
+ * Every sum over batch, time or channels runs in a fixed order, with no
+ * atomics, so the gradients are bit-reproducible.
+ */
+ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *B,
+                 const void *C, const float *D, const void *z, const float *delta_bias,
+                 int delta_softplus, const float *h0, const void *dout, const float *dlast,
+                 void *du, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
+                 float *ddelta_bias, float *dh0, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
+ * One-token state update (decode): advances `state` (batch, dim, dstate,
+ * f32, in place) by one step of the recurrence with the token's u, delta,
+ * z (batch, dim) and B, C (batch, dstate), and writes out (batch, dim).
+ * Each (b, d) row is computed by its own lanes in one fixed order, so a row
+ * gives the same bits whether it is stepped alone or inside any batch.
+ *   dstate must be 16; D, z, delta_bias may be NULL.
+ */
+ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
+                          float *state, const void *u, const void *delta, const float *A,
+                          const void *B, const void *C, const float *D, const void *z,
+                          const float *delta_bias, int delta_softplus, void *out,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_H */

@@ -39,6 +39,7 @@ def build(force: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
            "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
+    os.chmod(tmp, 0o755)
     os.replace(tmp, _LIB)
     return _LIB
 

@@ -1,0 +1,192 @@
+"""Python binding of libss.so: marshals PyTorch tensors into the C ABI.
+
+Every function here only checks that the tensors can be handed over
+(contiguous, on the GPU, of a dtype the ABI knows), allocates outputs with
+PyTorch, and calls the library on the current HIP stream.  All arithmetic
+runs in the library's kernels; there is no other code path.  If libss.so is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
+_lock = threading.Lock()
+_lib = None
+
+SS_F32, SS_BF16 = 0, 1
+SS_OK, SS_EINVAL, SS_EUNSUPPORTED, SS_EDEVICE = 0, 1, 2, 3
+
+
+class SSError(RuntimeError):
+    """A libss call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libss status {status}: {message}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libss.so (built by ``python -m selective_state_space_scan_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    f"{_LIB_PATH} is missing: build it with "
+                    "`python -m selective_state_space_scan_amd.build`")
+            lib = ctypes.CDLL(_LIB_PATH)
+            i64, vp, c_int, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+            lib.ss_abi_version.restype = c_int
+            lib.ss_abi_version.argtypes = []
+            lib.ss_last_error.restype = ctypes.c_char_p
+            lib.ss_last_error.argtypes = []
+            lib.ss_fwd.restype = c_int
+            lib.ss_fwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 4)
+            lib.ss_bwd_workspace_size.restype = sz
+            lib.ss_bwd_workspace_size.argtypes = [i64] * 4 + [c_int]
+            lib.ss_bwd.restype = c_int
+            lib.ss_bwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 13
+                                   + [sz, vp])
+            lib.ss_state_update.restype = c_int
+            lib.ss_state_update.argtypes = ([i64] * 3 + [c_int] + [vp] * 9 + [c_int]
+                                            + [vp] * 2)
+            _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != SS_OK:
+        raise SSError(status, load().ss_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _ptr(t)
+
+
+def _io_dtype(t) -> int:
+    if t.dtype == torch.float32:
+        return SS_F32
+    if t.dtype == torch.bfloat16:
+        return SS_BF16
+    raise TypeError(f"unsupported io dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _same_io(io, *ts):
+    for t in ts:
+        if t is not None and _io_dtype(t) != io:
+            raise TypeError("u, delta, B, C, z (and dout) must share one dtype")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def abi_version() -> int:
+    return load().ss_abi_version()
+
+
+def ss_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+           h0=None, out=None, last_state=None, return_last_state=False):
+    """Forward scan; returns ``out`` or ``(out, last_state)``.
+
+    u, delta, z: (batch, dim, L); B, C: (batch, dstate, L) in float32 or bfloat16;
+    A: (dim, dstate), D, delta_bias: (dim,), h0: (batch, dim, dstate) float32.
+    """
+    lib = load()
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    io = _io_dtype(u)
+    _same_io(io, delta, B, C, z)
+    if out is None:
+        out = torch.empty_like(u)
+    if return_last_state and last_state is None:
+        last_state = torch.empty(batch, dim, dstate, dtype=torch.float32, device=u.device)
+    _check(lib.ss_fwd(batch, dim, dstate, seqlen, io, _ptr(u), _ptr(delta), _f32(A, "A"),
+                      _ptr(B), _ptr(C), _f32(D, "D"), _ptr(z), _f32(delta_bias, "delta_bias"),
+                      int(bool(delta_softplus)), _f32(h0, "h0"), _ptr(out),
+                      _f32(last_state, "last_state"), _stream()))
+    return (out, last_state) if (return_last_state or last_state is not None) else out
+
+
+def ss_bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SS_F32) -> int:
+    return int(load().ss_bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype))
+
+
+def ss_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+           dout=None, h0=None, dlast=None, want_dh0=False, workspace=None):
+    """Backward of ``sum(dout * out) + sum(dlast * last_state)``.
+
+    Returns a dict with du, ddelta, dA, dB, dC and, for the optional inputs
+    given, dD, dz, ddelta_bias, plus dh0 when ``want_dh0`` or h0 is given.
+    """
+    lib = load()
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    io = _io_dtype(u)
+    _same_io(io, delta, B, C, z, dout)
+    dev = u.device
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta),
+             dA=torch.empty(dim, dstate, dtype=torch.float32, device=dev),
+             dB=torch.empty_like(B), dC=torch.empty_like(C))
+    if D is not None:
+        g["dD"] = torch.empty(dim, dtype=torch.float32, device=dev)
+    if z is not None:
+        g["dz"] = torch.empty_like(z)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty(dim, dtype=torch.float32, device=dev)
+    if want_dh0 or h0 is not None:
+        g["dh0"] = torch.empty(batch, dim, dstate, dtype=torch.float32, device=dev)
+    need = ss_bwd_workspace_size(batch, dim, dstate, seqlen, io)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.ss_bwd(batch, dim, dstate, seqlen, io, _ptr(u), _ptr(delta), _f32(A, "A"),
+                      _ptr(B), _ptr(C), _f32(D, "D"), _ptr(z), _f32(delta_bias, "delta_bias"),
+                      int(bool(delta_softplus)), _f32(h0, "h0"), _ptr(dout), _f32(dlast, "dlast"),
+                      _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                      _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+                      _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")), _ptr(workspace),
+                      workspace.numel(), _stream()))
+    return g
+
+
+def ss_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                    delta_softplus=False, out=None):
+    """One-token update of ``state`` (batch, dim, dstate) float32 in place.
+
+    u, delta, z: (batch, dim); B, C: (batch, dstate).  Returns the output (batch, dim).
+    """
+    lib = load()
+    batch, dim = u.shape
+    dstate = A.shape[1]
+    io = _io_dtype(u)
+    _same_io(io, delta, B, C, z)
+    if out is None:
+        out = torch.empty_like(u)
+    _check(lib.ss_state_update(batch, dim, dstate, io, _f32(state, "state"), _ptr(u),
+                               _ptr(delta), _f32(A, "A"), _ptr(B), _ptr(C), _f32(D, "D"),
+                               _ptr(z), _f32(delta_bias, "delta_bias"), int(bool(delta_softplus)),
+                               _ptr(out), _stream()))
+    return out

@@ -1,0 +1,209 @@
+// ss_api.cpp -- the C ABI of libss.so (declared in include/ss.h).
+//
+// Validates every argument on the host before anything is enqueued, keeps a
+// thread-local message naming what failed, and hands valid requests to the
+// kernel launchers.  Nothing here allocates device memory or synchronizes.
+#include "ss.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ss_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ss_status fail(ss_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+ss_status ok() {
+    g_err[0] = '\0';
+    return SS_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest extents the kernels index with 32-bit grid coordinates.
+constexpr int64_t kMaxBatch = 65535;
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxSeq = int64_t(1) << 40;
+
+struct Check {
+    ss_status st = SS_OK;
+    // first failure wins
+    void need(const void *p, const char *name) {
+        if (st != SS_OK) return;
+        if (!p) st = fail(SS_EINVAL, "%s must not be NULL", name);
+        else if (!aligned16(p)) st = fail(SS_EINVAL, "%s must be 16-byte aligned", name);
+    }
+    void opt(const void *p, const char *name) {
+        if (st != SS_OK || !p) return;
+        if (!aligned16(p)) st = fail(SS_EINVAL, "%s must be 16-byte aligned", name);
+    }
+    void pair(const void *grad, const void *input, const char *gname, const char *iname) {
+        if (st != SS_OK) return;
+        if ((grad == nullptr) != (input == nullptr))
+            st = fail(SS_EINVAL, "%s must be given exactly when %s is given", gname, iname);
+    }
+};
+
+ss_status check_dims(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io,
+                     bool scan) {
+    if (batch < 0) return fail(SS_EINVAL, "batch must be >= 0 (got %lld)", (long long)batch);
+    if (dim < 0) return fail(SS_EINVAL, "dim must be >= 0 (got %lld)", (long long)dim);
+    if (scan && seqlen < 0)
+        return fail(SS_EINVAL, "seqlen must be >= 0 (got %lld)", (long long)seqlen);
+    if (dstate <= 0) return fail(SS_EINVAL, "dstate must be > 0 (got %lld)", (long long)dstate);
+    if (io != SS_F32 && io != SS_BF16)
+        return fail(SS_EINVAL, "io_dtype must be SS_F32 (0) or SS_BF16 (1) (got %d)", io);
+    if (dstate != 16)
+        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (this build handles 16)",
+                    (long long)dstate);
+    if (scan && batch > kMaxBatch)
+        return fail(SS_EUNSUPPORTED, "batch %lld exceeds %lld", (long long)batch,
+                    (long long)kMaxBatch);
+    if (dim > kMaxDim)
+        return fail(SS_EUNSUPPORTED, "dim %lld exceeds %lld", (long long)dim, (long long)kMaxDim);
+    if (scan && seqlen > kMaxSeq)
+        return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
+                    (long long)kMaxSeq);
+    if (!scan && batch * dim > (int64_t(1) << 31) * 64)
+        return fail(SS_EUNSUPPORTED, "batch * dim too large");
+    return SS_OK;
+}
+
+ss_status device_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(SS_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_abi_version(void) { return SS_ABI_VERSION; }
+
+const char *ss_last_error(void) { return g_err; }
+
+ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                 const float *h0, void *out, float *last_state, void *stream) {
+    ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
+    if (st != SS_OK) return st;
+    const bool has_rows = batch > 0 && dim > 0;
+    Check c;
+    if (has_rows && seqlen > 0) {
+        c.need(u, "u");
+        c.need(delta, "delta");
+        c.need(B, "B");
+        c.need(C, "C");
+        c.need(out, "out");
+    } else {
+        c.opt(u, "u"); c.opt(delta, "delta"); c.opt(B, "B"); c.opt(C, "C"); c.opt(out, "out");
+    }
+    if (dim > 0) c.need(A, "A"); else c.opt(A, "A");
+    c.opt(D, "D");
+    c.opt(z, "z");
+    c.opt(delta_bias, "delta_bias");
+    c.opt(h0, "h0");
+    c.opt(last_state, "last_state");
+    if (c.st != SS_OK) return c.st;
+    if (h0 && last_state && h0 == last_state)
+        return fail(SS_EINVAL, "last_state must not alias h0");
+    ssk::FwdParams p{};
+    p.batch = batch; p.dim = dim; p.seqlen = seqlen;
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+    p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
+    p.out = out; p.last_state = last_state;
+    return device_status(ssk::launch_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+                         "ss_fwd launch");
+}
+
+size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                             int io_dtype) {
+    if (check_dims(batch, dim, dstate, seqlen, io_dtype, true) != SS_OK) return 0;
+    return ssk::bwd_workspace_bytes(batch, dim, seqlen);
+}
+
+ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                 const float *h0, const void *dout, const float *dlast, void *du, void *ddelta,
+                 float *dA, void *dB, void *dC, float *dD, void *dz, float *ddelta_bias,
+                 float *dh0, void *workspace, size_t workspace_bytes, void *stream) {
+    ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
+    if (st != SS_OK) return st;
+    const bool has_rows = batch > 0 && dim > 0;
+    const bool has_elems = has_rows && seqlen > 0;
+    Check c;
+    if (has_elems) {
+        c.need(u, "u"); c.need(delta, "delta"); c.need(dout, "dout");
+        c.need(du, "du"); c.need(ddelta, "ddelta");
+    } else {
+        c.opt(u, "u"); c.opt(delta, "delta"); c.opt(dout, "dout");
+        c.opt(du, "du"); c.opt(ddelta, "ddelta");
+    }
+    if (batch > 0 && seqlen > 0) {
+        c.need(B, "B"); c.need(C, "C"); c.need(dB, "dB"); c.need(dC, "dC");
+    } else {
+        c.opt(B, "B"); c.opt(C, "C"); c.opt(dB, "dB"); c.opt(dC, "dC");
+    }
+    if (dim > 0) { c.need(A, "A"); c.need(dA, "dA"); } else { c.opt(A, "A"); c.opt(dA, "dA"); }
+    c.opt(D, "D"); c.opt(z, "z"); c.opt(delta_bias, "delta_bias"); c.opt(h0, "h0");
+    c.opt(dlast, "dlast"); c.opt(dD, "dD"); c.opt(dz, "dz"); c.opt(ddelta_bias, "ddelta_bias");
+    c.opt(dh0, "dh0");
+    c.pair(dD, D, "dD", "D");
+    c.pair(dz, z, "dz", "z");
+    c.pair(ddelta_bias, delta_bias, "ddelta_bias", "delta_bias");
+    if (c.st != SS_OK) return c.st;
+    const size_t need = ssk::bwd_workspace_bytes(batch, dim, seqlen);
+    if (need > 0) {
+        if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
+        if (!aligned16(workspace)) return fail(SS_EINVAL, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(SS_EINVAL, "workspace_bytes %zu is smaller than the %zu bytes needed",
+                        workspace_bytes, need);
+    }
+    ssk::BwdParams p{};
+    p.batch = batch; p.dim = dim; p.seqlen = seqlen;
+    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+    p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
+    p.dout = dout; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB;
+    p.dC = dC; p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
+    p.workspace = workspace;
+    return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+                         "ss_bwd launch");
+}
+
+ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
+                          float *state, const void *u, const void *delta, const float *A,
+                          const void *B, const void *C, const float *D, const void *z,
+                          const float *delta_bias, int delta_softplus, void *out,
+                          void *stream) {
+    ss_status st = check_dims(batch, dim, dstate, 1, io_dtype, false);
+    if (st != SS_OK) return st;
+    Check c;
+    if (batch > 0 && dim > 0) {
+        c.need(state, "state"); c.need(u, "u"); c.need(delta, "delta"); c.need(A, "A");
+        c.need(B, "B"); c.need(C, "C"); c.need(out, "out");
+    }
+    c.opt(D, "D"); c.opt(z, "z"); c.opt(delta_bias, "delta_bias");
+    if (c.st != SS_OK) return c.st;
+    ssk::DecodeParams p{};
+    p.batch = batch; p.dim = dim; p.state = state; p.u = u; p.delta = delta; p.A = A;
+    p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias; p.softplus = delta_softplus != 0;
+    p.out = out;
+    return device_status(
+        ssk::launch_state_update(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+        "ss_state_update launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+"""C ABI contract tests that need no GPU.
+
+libss.so must load, export every function include/ss.h declares, report its
+ABI version, and reject bad arguments on the host -- with a status and a
+message naming the argument -- before anything reaches the device.  Every
+call below either fails validation or has nothing to enqueue, so no HIP
+call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_scan_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss.h")
+EINVAL, EUNSUP = binding.SS_EINVAL, binding.SS_EUNSUPPORTED
+FAKE = 0x10000          # a 16-byte aligned non-null address (never dereferenced)
+MISALIGNED = 0x10004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.lib_path()):
+        from selective_state_space_scan_amd import build
+        build.build()
+    return binding.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = re.findall(r"^\w[\w\s\*]*?\b(ss_\w+)\s*\(", open(HEADER).read(), flags=re.M)
+    assert set(names) >= {"ss_fwd", "ss_bwd", "ss_bwd_workspace_size", "ss_state_update",
+                          "ss_last_error", "ss_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), f"libss.so does not export {n}"
+
+
+def test_abi_version(lib):
+    assert lib.ss_abi_version() == 1
+
+
+def _fwd(lib, batch=2, dim=32, dstate=16, seqlen=64, io=0, u=FAKE, delta=FAKE, A=FAKE, B=FAKE,
+         C=FAKE, D=None, z=None, bias=None, h0=None, out=FAKE, last=None):
+    return lib.ss_fwd(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, bias, 1, h0, out,
+                      last, None)
+
+
+def _msg(lib):
+    return lib.ss_last_error().decode()
+
+
+@pytest.mark.parametrize("arg", ["u", "delta", "A", "B", "C", "out"])
+def test_fwd_null_required_pointer(lib, arg):
+    assert _fwd(lib, **{arg: None}) == EINVAL
+    assert arg in _msg(lib)
+
+
+@pytest.mark.parametrize("arg", ["u", "A", "D", "z", "bias", "h0", "last"])
+def test_fwd_misaligned_pointer(lib, arg):
+    assert _fwd(lib, **{arg: MISALIGNED}) == EINVAL
+    name = {"bias": "delta_bias", "last": "last_state"}.get(arg, arg)
+    assert name in _msg(lib) and "aligned" in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(batch=-1), EINVAL, "batch"), (dict(dim=-3), EINVAL, "dim"),
+    (dict(seqlen=-1), EINVAL, "seqlen"), (dict(dstate=0), EINVAL, "dstate"),
+    (dict(dstate=8), EUNSUP, "dstate"), (dict(dstate=64), EUNSUP, "dstate"),
+    (dict(io=7), EINVAL, "io_dtype"), (dict(batch=70000), EUNSUP, "batch"),
+])
+def test_fwd_bad_sizes(lib, kw, status, word):
+    assert _fwd(lib, **kw) == status
+    assert word in _msg(lib)
+
+
+def test_fwd_empty_batch_is_a_noop(lib):
+    # nothing to compute and no state to write: succeeds without touching the device
+    assert _fwd(lib, batch=0, u=None, delta=None, B=None, C=None, out=None) == 0
+    assert _msg(lib) == ""
+    assert _fwd(lib, dim=0, u=None, delta=None, A=None, B=None, C=None, out=None) == 0
+
+
+def test_fwd_last_state_must_not_alias_h0(lib):
+    assert _fwd(lib, h0=FAKE, last=FAKE) == EINVAL
+    assert "alias" in _msg(lib)
+
+
+def _bwd(lib, batch=2, dim=32, dstate=16, seqlen=64, D=None, z=None, bias=None, dD=None, dz=None,
+         dbias=None, ws=FAKE, ws_bytes=None, **over):
+    args = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, dout=FAKE, du=FAKE, ddelta=FAKE,
+                dA=FAKE, dB=FAKE, dC=FAKE)
+    args.update(over)
+    if ws_bytes is None:
+        ws_bytes = lib.ss_bwd_workspace_size(batch, dim, dstate, seqlen, 0)
+    return lib.ss_bwd(batch, dim, dstate, seqlen, 0, args["u"], args["delta"], args["A"],
+                      args["B"], args["C"], D, z, bias, 1, None, args["dout"], None, args["du"],
+                      args["ddelta"], args["dA"], args["dB"], args["dC"], dD, dz, dbias, None,
+                      ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("arg", ["u", "delta", "dout", "du", "ddelta", "dA", "dB", "dC", "A"])
+def test_bwd_null_required_pointer(lib, arg):
+    assert _bwd(lib, **{arg: None}) == EINVAL
+    assert arg in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,word", [
+    (dict(D=FAKE), "dD"), (dict(dD=FAKE), "dD"), (dict(z=FAKE), "dz"), (dict(dz=FAKE), "dz"),
+    (dict(bias=FAKE), "ddelta_bias"), (dict(dbias=FAKE), "ddelta_bias"),
+])
+def test_bwd_gradient_presence_matches_input(lib, kw, word):
+    assert _bwd(lib, **kw) == EINVAL
+    assert word in _msg(lib)
+
+
+def test_bwd_workspace_checks(lib):
+    need = lib.ss_bwd_workspace_size(2, 32, 16, 64, 0)
+    assert need > 0
+    assert _bwd(lib, ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
+    assert _bwd(lib, ws=None) == EINVAL and "workspace" in _msg(lib)
+    assert _bwd(lib, ws=MISALIGNED) == EINVAL and "aligned" in _msg(lib)
+
+
+def test_workspace_size_is_monotone_and_zero_when_invalid(lib):
+    base = lib.ss_bwd_workspace_size(2, 32, 16, 64, 0)
+    assert lib.ss_bwd_workspace_size(4, 32, 16, 64, 0) > base
+    assert lib.ss_bwd_workspace_size(2, 64, 16, 64, 0) > base
+    assert lib.ss_bwd_workspace_size(2, 32, 16, 128, 0) > base
+    assert lib.ss_bwd_workspace_size(2, 32, 8, 64, 0) == 0
+    assert lib.ss_bwd_workspace_size(-1, 32, 16, 64, 0) == 0
+
+
+def test_decode_checks(lib):
+    st = lib.ss_state_update(4, 32, 16, 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                             1, FAKE, None)
+    assert st == EINVAL and "state" in _msg(lib)
+    st = lib.ss_state_update(4, 32, 12, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                             1, FAKE, None)
+    assert st == EUNSUP and "dstate" in _msg(lib)
+    assert lib.ss_state_update(0, 32, 16, 1, None, None, None, None, None, None, None, None,
+                               None, 1, None, None) == 0
+
+
+def test_error_message_is_per_thread(lib):
+    import threading
+    assert _fwd(lib, u=None) == EINVAL
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.ss_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "u" in _msg(lib)

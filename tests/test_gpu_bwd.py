@@ -1,0 +1,126 @@
+"""GPU parity of the backward (ss_bwd through the C ABI) with the oracle.
+
+Small shapes are compared element by element for every gradient; they span
+several chunks, ragged time tails and channel counts, the scalar-load path,
+each optional input on and off, an initial state with its gradient and a
+gradient on the last state.  The full-size workload runs in the benchmark's
+launch configuration and is checked on sampled rows (du, ddelta, dz), one
+whole batch entry (dB, dC) and sampled channels (dA, dD, ddelta_bias), plus
+run-to-run bit equality.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from selective_state_space_scan_amd import binding
+from selective_state_space_scan_amd import inputs as ssin
+
+from gpu_util import DEV, dev_inputs, require_gpu, say, to_dev, to_host, widen
+from metrics import TOL, assert_close
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ["du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias", "dh0"]
+
+
+def run_bwd(d, w, h0=None, dlast=None, want_dh0=False):
+    return binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d.get("D"), d.get("z"),
+                          d.get("delta_bias"), w.softplus, d["dout"], h0=h0, dlast=dlast,
+                          want_dh0=want_dh0)
+
+
+def oracle_bwd(arr, w, h0=None, dlast=None, threads=8):
+    x = {k: widen(v) for k, v in arr.items()}
+    return oracle.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x.get("D"), x.get("z"),
+                      x.get("delta_bias"), w.softplus, x["dout"], h0, dlast, threads=threads)
+
+
+SMALL = [
+    (2, 40, 100, "f32", {}),
+    (1, 17, 33, "f32", {}),
+    (2, 32, 64, "f32", dict(has_z=False)),
+    (2, 32, 64, "f32", dict(has_D=False)),
+    (2, 32, 64, "f32", dict(has_bias=False)),
+    (2, 32, 64, "f32", dict(softplus=False)),
+    (3, 16, 1, "f32", {}),
+    (2, 24, 70, "bf16", {}),
+]
+
+
+@pytest.mark.parametrize("batch,dim,L,io,flags", SMALL)
+def test_bwd_small_elementwise(batch, dim, L, io, flags):
+    require_gpu()
+    w = ssin.custom("bwd", batch, dim, 16, L, io, seed=7 * batch + dim + L, **flags)
+    arr = ssin.make(w)
+    if not w.softplus:
+        arr["delta"] = (np.abs(ssin.widen(arr["delta"])) + 0.05).astype(np.float32)
+        if "delta_bias" in arr:
+            arr["delta_bias"] = np.linspace(0.0, 0.1, dim).astype(np.float32)
+    say(f"bwd small {w.name}")
+    d = dev_inputs(arr)
+    rng = np.random.default_rng(9)
+    h0 = rng.standard_normal((batch, dim, 16)).astype(np.float32)
+    dl = rng.standard_normal((batch, dim, 16)).astype(np.float32)
+    for use_state in (False, True):
+        g = run_bwd(d, w, h0=to_dev(h0) if use_state else None,
+                    dlast=to_dev(dl) if use_state else None, want_dh0=True)
+        torch.cuda.synchronize()
+        ref = oracle_bwd(arr, w, h0=h0.astype(np.float64) if use_state else None,
+                         dlast=dl.astype(np.float64) if use_state else None)
+        if not use_state:
+            # gradient at a zero initial state: the oracle reports it when h0 is given
+            ref["dh0"] = oracle_bwd(arr, w, h0=np.zeros((batch, dim, 16)))["dh0"]
+        for k in KEYS:
+            if k not in ref:
+                assert k not in g
+                continue
+            tol = TOL["f32"] if k in ("dA", "dD", "ddelta_bias", "dh0") else TOL[io]
+            assert_close(to_host(g[k]), ref[k], tol, f"{k} state={use_state}")
+
+
+def test_bwd_zero_length_passes_dlast_through():
+    require_gpu()
+    w = ssin.custom("bwd", 2, 32, 16, 0, "f32", seed=4)
+    d = dev_inputs(ssin.make(w))
+    dl = torch.randn(2, 32, 16, device=DEV)
+    g = run_bwd(d, w, dlast=dl, want_dh0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dl)
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert torch.count_nonzero(g[k]).item() == 0
+
+
+def test_bwd_full_size_sampled():
+    require_gpu()
+    w = ssin.WORKLOADS["mamba130m_bwd_f32_8x1536x2048"]
+    say("bwd full: generating inputs")
+    arr = ssin.make(w)
+    d = dev_inputs(arr)
+    say("bwd full: running twice")
+    g1 = run_bwd(d, w)
+    g2 = run_bwd(d, w)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), f"{k} not deterministic"
+    x = {k: widen(v) for k, v in arr.items()}
+    tol = TOL["f32"]
+    # one whole batch entry: per-step gradients of every row and its dB, dC
+    b = 5
+    say("bwd full: oracle on batch entry 5")
+    sub = {k: (v[b:b + 1] if k in ("u", "delta", "z", "B", "C", "dout") else v)
+           for k, v in x.items()}
+    ref = oracle.bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"],
+                     sub["delta_bias"], True, sub["dout"], threads=8)
+    for k in ("du", "ddelta", "dz", "dB", "dC"):
+        e = assert_close(to_host(g1[k][b:b + 1]), ref[k], tol, f"{k}[b={b}]")
+        say(f"  {k} err {e:.3e}")
+    # sampled channels over the whole batch: dA, dD, ddelta_bias
+    ds = [0, 1, 777, 1535]
+    say("bwd full: oracle on 4 channels x 8 batch entries")
+    sub = {k: (v[:, ds] if k in ("u", "delta", "z", "dout") else v) for k, v in x.items()}
+    ref = oracle.bwd(sub["u"], sub["delta"], x["A"][ds], x["B"], x["C"], x["D"][ds], sub["z"],
+                     x["delta_bias"][ds], True, sub["dout"], threads=8)
+    for k in ("dA", "dD", "ddelta_bias"):
+        e = assert_close(to_host(g1[k][ds]), ref[k], tol, k)
+        say(f"  {k} err {e:.3e}")
