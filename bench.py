@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective scan on one MI355X.
+
+A step is one forward (ss_fwd) and one backward (ss_bwd) over a batch of the
+Mamba-130m-shaped layer: batch 8, d_inner 1536, d_state 16, L 2048, float32
+inputs and outputs, z gate, D skip, delta bias and softplus, synthetic seeded
+inputs already resident in HBM.  The line printed is
+
+  value = batch * d_inner * L / (time of one step)   [elements/s]
+
+with each library kernel also timed on its own (HIP events recorded between
+the kernels on the stream they run on), the dominant kernel set against the
+MI355X roofline, and the plain f64 oracle timed on a bounded sample of the
+same workload on the host cores.  The forward-only and decode workloads are
+timed as well and reported under "detail".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan fwd+bwd elements/s and achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+N = 16
+
+
+def hip_runtime():
+    names = ["libamdhip64.so.7", "libamdhip64.so"]
+    import torch
+    names.append(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    for n in names:
+        try:
+            lib = ctypes.CDLL(n)
+            lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            return lib
+        except OSError:
+            continue
+    raise RuntimeError("HIP runtime library not found")
+
+
+class KernelTimer:
+    """Arms libss's profiling hook with HIP events and reads back durations."""
+
+    def __init__(self, hip, sslib, count):
+        self.hip, self.ss = hip, sslib
+        self.events = (ctypes.c_void_p * count)()
+        for i in range(count):
+            ev = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+            self.events[i] = ev
+        self.count = count
+        self.ss.ss_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        self.ss.ss_profile_events_used.restype = ctypes.c_int
+
+    def arm(self):
+        self.ss.ss_profile_events(ctypes.cast(self.events, ctypes.c_void_p), self.count)
+
+    def disarm(self):
+        used = self.ss.ss_profile_events_used()
+        self.ss.ss_profile_events(None, 0)
+        return used
+
+    def ms(self, i, j):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.events[i], self.events[j]) == 0
+        return out.value
+
+    def close(self):
+        for i in range(self.count):
+            self.hip.hipEventDestroy(self.events[i])
+
+
+def algorithmic_bytes(kernel, batch, dim, L, esize):
+    """Bytes each kernel must move if every tensor it reads or writes crosses
+    HBM exactly once (workspace traffic excluded)."""
+    E = batch * dim * L
+    bc = batch * N * L * esize           # one of B, C, dB, dC
+    params = dim * N * 4 + 2 * dim * 4     # A, D, delta_bias (or their gradients)
+    if kernel == "ss_fwd_kernel":
+        return 3 * E * esize + 2 * bc + params + E * esize
+    if kernel == "ss_bwd_ckpt_kernel":
+        return 2 * E * esize + bc + dim * N * 4 + dim * 4
+    if kernel == "ss_bwd_reverse_kernel":
+        return 4 * E * esize + 2 * bc + params + 3 * E * esize
+    if kernel == "ss_bwd_fold_kernel":
+        return 2 * bc + params
+    if kernel == "ss_state_update_kernel":
+        return 2 * batch * dim * N * 4 + 4 * batch * dim * esize + 2 * batch * N * esize + params
+    raise KeyError(kernel)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the selective scan's "
+              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from selective_state_space_scan_amd import binding
+    from selective_state_space_scan_amd import inputs as ssin
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = "cuda:0"
+    lib = binding.load()
+    hip = hip_runtime()
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---------------- the step: fwd + bwd at 8 x 1536 x 2048, f32 ----------------
+    w = ssin.WORKLOADS["mamba130m_bwd_f32_8x1536x2048"]
+    arr = ssin.make(w)
+    d = {k: to_dev(v) for k, v in arr.items()}
+    y = torch.empty_like(d["u"])
+    ws = torch.empty(binding.ss_bwd_workspace_size(w.batch, w.dim, 16, w.seqlen, 0),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                       d["delta_bias"], True, out=y)
+        return binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                              d["delta_bias"], True, d["dout"], workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per step: fwd = [call start, after fwd kernel]; bwd = [call start, after each of 3 kernels]
+    per_step = 6
+    timer = KernelTimer(hip, lib, per_step * args.steps)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    timer.arm()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    used = timer.disarm()
+    assert used == per_step * args.steps, f"recorded {used} events"
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    names = ["ss_fwd_kernel", "ss_bwd_ckpt_kernel", "ss_bwd_reverse_kernel", "ss_bwd_fold_kernel"]
+    pairs = [(0, 1), (2, 3), (3, 4), (4, 5)]
+    kern_ms = {n: float(np.mean([timer.ms(s * per_step + i, s * per_step + j)
+                                 for s in range(args.steps)])) for n, (i, j) in zip(names, pairs)}
+    timer.close()
+    E = w.batch * w.dim * w.seqlen
+    kb = {n: algorithmic_bytes(n, w.batch, w.dim, w.seqlen, 4) for n in names}
+    step_bytes = kb["ss_fwd_kernel"] + (4 * E * 4 + 2 * w.batch * N * w.seqlen * 4
+                                        + 3 * E * 4 + 2 * w.batch * N * w.seqlen * 4
+                                        + 3 * (w.dim * N * 4 + 2 * w.dim * 4))
+    dom = max(names, key=lambda n: kern_ms[n])
+    ach = kb[dom] / (kern_ms[dom] * 1e-3) / 1e9
+    kernels = {n: {"avg_ms": round(kern_ms[n], 5), "algorithmic_bytes": kb[n],
+                   "algorithmic_GBps": round(kb[n] / (kern_ms[n] * 1e-3) / 1e9, 1)}
+               for n in names}
+
+    result = {
+        "metric": METRIC,
+        "value": E / (ms_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mamba130m-layer scan fwd+bwd, f32 io", "batch": w.batch,
+                   "d_inner": w.dim, "d_state": 16, "seqlen": w.seqlen, "io_dtype": "f32",
+                   "z_gate": True, "D_skip": True, "delta_bias_softplus": True},
+        "hbm_GBps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "kernels": kernels,
+    }
+
+    # ---------------- detail: forward-only and decode workloads ----------------
+    if not args.no_detail:
+        detail = {}
+        for name, reps in (("mamba130m_fwd_bf16_8x1536x2048", 2), ("mamba2p8b_fwd_bf16_4x5120x4096", 1)):
+            wf = ssin.WORKLOADS[name]
+            af = ssin.make(wf)
+            sets = [{k: to_dev(v) for k, v in af.items()} for _ in range(reps)]
+            outs = [torch.empty_like(s["u"]) for s in sets]
+            last = torch.empty(wf.batch, wf.dim, 16, device=dev) if wf.last_state else None
+            del af
+
+            def run(i):
+                s = sets[i % reps]
+                binding.ss_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"],
+                               s["delta_bias"], True, out=outs[i % reps], last_state=last)
+            for i in range(3):
+                run(i)
+            iters = 20
+            tm = KernelTimer(hip, lib, 2 * iters)
+            torch.cuda.synchronize()
+            tm.arm()
+            for i in range(iters):
+                run(i)
+            torch.cuda.synchronize()
+            tm.disarm()
+            ms = float(np.mean([tm.ms(2 * i, 2 * i + 1) for i in range(iters)]))
+            tm.close()
+            Ef = wf.batch * wf.dim * wf.seqlen
+            by = algorithmic_bytes("ss_fwd_kernel", wf.batch, wf.dim, wf.seqlen, 2)
+            if wf.last_state:
+                by += wf.batch * wf.dim * 16 * 4
+            detail[name] = {"kernel_ms": round(ms, 5), "elements_per_s": Ef / (ms * 1e-3),
+                            "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                            "hbm_frac_of_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "input_sets_rotated": reps}
+            del sets, outs
+        wd = ssin.WORKLOADS["decode_bf16_256x5120"]
+        ad = ssin.make(wd)
+        reps = 4
+        sets = [{k: to_dev(v) for k, v in ad.items()} for _ in range(reps)]
+        outs = [torch.empty_like(s["u"]) for s in sets]
+
+        def dec(i):
+            s = sets[i % reps]
+            binding.ss_state_update(s["state"], s["u"], s["delta"], s["A"], s["B"], s["C"],
+                                    s["D"], s["z"], s["delta_bias"], True, out=outs[i % reps])
+        for i in range(4):
+            dec(i)
+        iters = 40
+        tm = KernelTimer(hip, lib, 2 * iters)
+        torch.cuda.synchronize()
+        tm.arm()
+        for i in range(iters):
+            dec(i)
+        torch.cuda.synchronize()
+        tm.disarm()
+        ms = float(np.mean([tm.ms(2 * i, 2 * i + 1) for i in range(iters)]))
+        tm.close()
+        by = algorithmic_bytes("ss_state_update_kernel", wd.batch, wd.dim, 1, 2)
+        detail["decode_bf16_256x5120"] = {
+            "kernel_ms": round(ms, 5), "rows_per_s": wd.batch * wd.dim / (ms * 1e-3),
+            "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac_of_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "input_sets_rotated": reps}
+        del sets, outs
+        result["detail"] = detail
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        threads = min(8, os.cpu_count() or 1)
+        nd = 96  # channels of the sample: 8 x 96 x 2048 = 1.57 M elements
+        x = {k: (v[:, :nd] if k in ("u", "delta", "z", "dout") else v).astype(np.float64)
+             for k, v in arr.items()}
+        x["A"], x["D"], x["delta_bias"] = (arr["A"][:nd].astype(np.float64),
+                                           arr["D"][:nd].astype(np.float64),
+                                           arr["delta_bias"][:nd].astype(np.float64))
+        t0 = time.perf_counter()
+        oracle.fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                   True, threads=threads)
+        oracle.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                   True, x["dout"], threads=threads)
+        dt = time.perf_counter() - t0
+        Es = w.batch * nd * w.seqlen
+        result["cpu_baseline"] = {"value": Es / dt, "unit": "elements/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"fwd+bwd of the same workload restricted to its first "
+                                            f"{nd} of {w.dim} channels (8 x {nd} x {w.seqlen} = "
+                                            f"{Es} elements), f64, {dt:.2f} s wall"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,6 +137,19 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dty
                           const float *delta_bias, int delta_softplus, void *out,
                           void *stream);
 
+/*
+ * Profiling aid for callers that time the library's kernels one by one
+ * (not needed for normal use).  When `events` is non-NULL, every later
+ * ss_fwd / ss_bwd / ss_state_update call on this thread records the next
+ * unused entry of `events` (each a hipEvent_t created by the caller) on its
+ * stream before its first kernel and after each kernel it launches, until
+ * `count` entries are used.  ss_profile_events(NULL, 0) switches it off.
+ * ss_profile_events_used() returns how many entries have been recorded.
+ * Recording events does not change what the kernels compute.
+ */
+ss_status ss_profile_events(void **events, int count);
+int ss_profile_events_used(void);
+
 #ifdef __cplusplus
 }
 #endif

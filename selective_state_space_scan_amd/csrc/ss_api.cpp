@@ -14,6 +14,9 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t *g_prof = nullptr;
+thread_local int g_prof_count = 0;
+thread_local int g_prof_used = 0;
 
 ss_status fail(ss_status st, const char *fmt, ...) {
     va_list ap;
@@ -86,7 +89,24 @@ ss_status device_status(hipError_t e, const char *what) {
 
 }  // namespace
 
+namespace ssk {
+void profile_mark(hipStream_t stream) {
+    if (g_prof && g_prof_used < g_prof_count) (void)hipEventRecord(g_prof[g_prof_used++], stream);
+}
+}  // namespace ssk
+
 extern "C" {
+
+ss_status ss_profile_events(void **events, int count) {
+    if (events && count < 0) return fail(SS_EINVAL, "count must be >= 0");
+    g_prof = events ? reinterpret_cast<hipEvent_t *>(events) : nullptr;
+    g_prof_count = events ? count : 0;
+    g_prof_used = 0;
+    return ok();
+}
+
+int ss_profile_events_used(void) { return g_prof_used; }
+
 
 int ss_abi_version(void) { return SS_ABI_VERSION; }
 
@@ -123,6 +143,7 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.out = out; p.last_state = last_state;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
                          "ss_fwd launch");
 }
@@ -179,6 +200,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.dout = dout; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB;
     p.dC = dC; p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
     p.workspace = workspace;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
                          "ss_bwd launch");
 }
@@ -201,6 +223,7 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dty
     p.batch = batch; p.dim = dim; p.state = state; p.u = u; p.delta = delta; p.A = A;
     p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias; p.softplus = delta_softplus != 0;
     p.out = out;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(
         ssk::launch_state_update(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
         "ss_state_update launch");

@@ -16,89 +16,40 @@
 // "Features").
 //
 // Three kernels on the caller's stream:
-//   1. checkpoint: the forward recurrence again, writing the state at the
-//      start of every 32-step chunk to the workspace;
-//   2. reverse: per workgroup of 16 channels x 16 states (one lane per
-//      state entry, as in the forward), chunks are visited last to first.
-//      Each chunk re-runs its 32 forward steps from its checkpoint, keeping
-//      every decay and state in registers, then walks the steps backward.
-//      Sums over the 16 states go through a per-wave LDS transpose; sums
-//      over the workgroup's 16 channels (dB, dC) through a workgroup LDS
-//      tile, written out as one partial per 16 channels;
+//   1. checkpoint: the forward recurrence again, writing the state entering
+//      every 32-step chunk to the workspace;
+//   2. reverse: per workgroup of 16 channels x 16 states (one lane per state
+//      entry, as in the forward), chunks are visited last to first.  Each
+//      chunk re-runs its 32 forward steps from its checkpoint, keeping every
+//      decay and state in registers, then walks the steps backward.
+//        - sums over the 16 states (pre-gate output, the two sums behind du
+//          and ddelta) go through padded per-wave LDS transposes;
+//        - sums over channels (dB, dC) run on the matrix cores: with the
+//          lane layout (row = lane / 16, state = lane % 16) a 16x16x4 f32
+//          MFMA contracts exactly over the 4 rows of a wavefront, taking the
+//          per-lane adjoint (or state) as A and the row's delta*u (or dy),
+//          placed in the column of the current step, as B -- so one MFMA per
+//          step both multiplies and adds the 4 rows, and 16 steps fill one
+//          16 x 16 accumulator.  The 4 wavefronts' partial sums are then
+//          added through LDS and written as one partial per 16 channels;
 //   3. fold: adds the dB/dC partials over channel groups in ascending group
 //      order and the dA/dD/dbias partials over the batch in ascending batch
 //      order.
 // Every sum runs in an order fixed by the shape, with no atomics.
 #include "ss_device.h"
 #include "ss_kernels.h"
+#include "ss_tiles.h"
 
 namespace ssk {
 namespace {
 
 constexpr int kRows = 16;
-constexpr int kT = 32;  // chunk length (checkpoint spacing)
+constexpr int kC = 32;          // checkpoint spacing = reverse-pass chunk length
 constexpr int kThreads = 256;
-constexpr int kPitch = kT + 4;
-constexpr int kYBlock = kN * 16 + 16;
+constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
+constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row
 
-struct alignas(16) Raw16 {
-    uint32_t w[4];
-};
-
-template <typename T, int VEC>
-__device__ __forceinline__ void load_vec(const T *__restrict__ p, int64_t t, int64_t L,
-                                         bool row_ok, T (&dst)[VEC]) {
-    if (row_ok && t + VEC <= L) {
-        if constexpr (VEC * sizeof(T) == 16) {
-            Raw16 r = *reinterpret_cast<const Raw16 *>(p + t);
-            __builtin_memcpy(dst, &r, 16);
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; e++) dst[e] = p[t + e];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < VEC; e++) dst[e] = (row_ok && t + e < L) ? p[t + e] : T(0);
-    }
-}
-
-template <typename T, int VEC>
-__device__ __forceinline__ void store_vec(T *__restrict__ p, int64_t t, int64_t L, const T *src) {
-    if (t + VEC <= L) {
-        if constexpr (VEC * sizeof(T) == 16) {
-            *reinterpret_cast<Raw16 *>(p + t) = *reinterpret_cast<const Raw16 *>(src);
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; e++) p[t + e] = src[e];
-        }
-    } else {
-        for (int e = 0; e < VEC && t + e < L; e++) p[t + e] = src[e];
-    }
-}
-
-#define SS_BCAST_CASES(X, OUT, J)                                                        \
-    switch (J) {                                                                         \
-        case 0: OUT = row_bcast<0>(X); break;   case 1: OUT = row_bcast<1>(X); break;    \
-        case 2: OUT = row_bcast<2>(X); break;   case 3: OUT = row_bcast<3>(X); break;    \
-        case 4: OUT = row_bcast<4>(X); break;   case 5: OUT = row_bcast<5>(X); break;    \
-        case 6: OUT = row_bcast<6>(X); break;   case 7: OUT = row_bcast<7>(X); break;    \
-        case 8: OUT = row_bcast<8>(X); break;   case 9: OUT = row_bcast<9>(X); break;    \
-        case 10: OUT = row_bcast<10>(X); break; case 11: OUT = row_bcast<11>(X); break;  \
-        case 12: OUT = row_bcast<12>(X); break; case 13: OUT = row_bcast<13>(X); break;  \
-        case 14: OUT = row_bcast<14>(X); break; default: OUT = row_bcast<15>(X); break;  \
-    }
-
-template <int M>
-__device__ __forceinline__ float xor_add(float v) {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                                     (M << 10) | 0x1f));
-}
-
-// Sum over the 16 lanes of a DPP row; pairs are combined commutatively, so
-// every lane of the row ends with the same bits.
-__device__ __forceinline__ float row_sum16(float v) {
-    return xor_add<8>(xor_add<4>(xor_add<2>(xor_add<1>(v))));
-}
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Workspace carve-up (all f32, 256-byte aligned pieces).
 struct Workspace {
@@ -114,7 +65,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 
 __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L,
                                            size_t *total) {
-    const int64_t nck = (L + kT - 1) / kT;
+    const int64_t nck = (L + kC - 1) / kC;
     const int64_t groups = (dim + kRows - 1) / kRows;
     size_t off = 0;
     Workspace w;
@@ -134,92 +85,128 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
     return w;
 }
 
+template <int M>
+__device__ __forceinline__ float xor_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                     (M << 10) | 0x1f));
+}
+
+// Sum over the 16 lanes of a DPP row; pairs are combined commutatively, so
+// every lane of the row ends with the same bits.
+__device__ __forceinline__ float row_sum16(float v) {
+    return xor_add<8>(xor_add<4>(xor_add<2>(xor_add<1>(v))));
+}
+
+// value of lane (n + 8) mod 16 of the same DPP row
+__device__ __forceinline__ float row_ror8(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+}
+
+// fixed pairwise sum of 16 values
+__device__ __forceinline__ float tree16(float (&x)[16]) {
+#pragma unroll
+    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+        for (int k = 0; k < 16; k += 2 * w) x[k] += x[k + w];
+    return x[0];
+}
+
 // ---------------------------------------------------------------------------
-// kernel 1: checkpoints
+// kernel 1: checkpoints (64-step staging chunks, a checkpoint every 32 steps)
 // ---------------------------------------------------------------------------
+constexpr int kT1 = 64;
+constexpr int kPitch1 = kT1 + 4;
+
+template <typename T>
+struct CkptSmem {
+    static constexpr uint32_t kB = 0;
+    static constexpr uint32_t kU = kB + kN * kPitch1 * 4;
+    static constexpr uint32_t kDl = kU + kRows * kT1 * sizeof(T);
+    static constexpr uint32_t kSize = kDl + kRows * kT1 * sizeof(T);
+};
+
+template <int J>
+__device__ __forceinline__ void fwd_step(float dl, float dlu, float a2, float b, float &h) {
+    h = __builtin_fmaf(exp2_hw(row_bcast<J>(dl) * a2), h, row_bcast<J>(dlu) * b);
+}
+
 template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Workspace ws) {
-    constexpr int kVecPerRow = kT / VEC;
-    constexpr int kVecPerTile = 16 * kVecPerRow;
-    constexpr int kTiles = 3;  // B, u, delta
-    constexpr int kSlots = (kTiles * kVecPerTile + kThreads - 1) / kThreads;
-    __shared__ float sB[kN][kPitch];
-    __shared__ __attribute__((aligned(16))) T sU[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sDl[kRows][kT];
+    using SM = CkptSmem<T>;
+    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
+    float(*sB)[kPitch1] = reinterpret_cast<float(*)[kPitch1]>(smem + SM::kB);
+    T(*sU)[kT1] = reinterpret_cast<T(*)[kT1]>(smem + SM::kU);
+    T(*sDl)[kT1] = reinterpret_cast<T(*)[kT1]>(smem + SM::kDl);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, r = wave * 4 + (lane >> 4);
     const int64_t L = p.seqlen, Dm = p.dim, b = blockIdx.y;
     const int64_t d0 = int64_t(blockIdx.x) * kRows, d = d0 + r;
     const bool row_ok = d < Dm;
-    const T *gu = static_cast<const T *>(p.u);
-    const T *gdl = static_cast<const T *>(p.delta);
-    const T *gB = static_cast<const T *>(p.B);
+    const int valid_rows = int(Dm - d0 < kRows ? Dm - d0 : kRows);
     const float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float h = (row_ok && p.h0) ? p.h0[(b * Dm + d) * kN + n] : 0.0f;
-    const int64_t nck = (L + kT - 1) / kT;
+    const int64_t nck = (L + kC - 1) / kC;
     float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
 
-    T pre[kSlots][VEC];
-    auto fetch = [&](int64_t t0) {
-#pragma unroll
-        for (int k = 0; k < kSlots; k++) {
-            const int slot = tid + k * kThreads;
-            const int tile = slot / kVecPerTile, rem = slot % kVecPerTile;
-            const int row = rem / kVecPerRow;
-            const int64_t t = t0 + (rem % kVecPerRow) * VEC;
-            const T *base = gu;
-            bool ok = false;
-            if (tile == 0) {
-                base = gB + (b * kN + row) * L; ok = true;
-            } else if (tile < kTiles && d0 + row < Dm) {
-                base = (tile == 1 ? gu : gdl) + (b * Dm + d0 + row) * L; ok = true;
+    const T *gB = static_cast<const T *>(p.B) + b * kN * L;
+    const T *gu = static_cast<const T *>(p.u) + (b * Dm + d0) * L;
+    const T *gdl = static_cast<const T *>(p.delta) + (b * Dm + d0) * L;
+    ChunkStager<T, VEC, kT1, 3, kThreads> st;
+    st.init(
+        [&](int i) -> TileSrc<T> {
+            switch (i) {
+                case 0: return {gB, L, kN, SM::kB, kPitch1, true};
+                case 1: return {gu, L, valid_rows, SM::kU, kT1, false};
+                default: return {gdl, L, valid_rows, SM::kDl, kT1, false};
             }
-            load_vec<T, VEC>(base, t, L, ok, pre[k]);
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int k = 0; k < kSlots; k++) {
-            const int slot = tid + k * kThreads;
-            const int tile = slot / kVecPerTile, rem = slot % kVecPerTile;
-            if (tile >= kTiles) continue;
-            const int row = rem / kVecPerRow, col = (rem % kVecPerRow) * VEC;
-            if (tile == 0) {
-#pragma unroll
-                for (int e = 0; e < VEC; e++) sB[row][col + e] = to_f32<T>(pre[k][e]);
-            } else {
-                T *dst = tile == 1 ? &sU[row][col] : &sDl[row][col];
-#pragma unroll
-                for (int e = 0; e < VEC; e++) dst[e] = pre[k][e];
-            }
-        }
-    };
+        },
+        tid);
 
-    if (nck > 0) { fetch(0); stash(); }
+    const int64_t nchunks = (L + kT1 - 1) / kT1;
+    if (nchunks > 0) {
+        st.fetch(0, L);
+        st.stash(smem);
+    }
     __syncthreads();
-    for (int64_t c = 0; c < nck; c++) {
-        const int64_t t0 = c * kT;
-        if (row_ok) ck[c * kN] = h;
-        if (c + 1 < nck) fetch(t0 + kT);
+    for (int64_t c = 0; c < nchunks; c++) {
+        const int64_t t0 = c * kT1;
+        if (c + 1 < nchunks) st.fetch(t0 + kT1, L);
+        float dl[kT1 / 16], dlu[kT1 / 16];
 #pragma unroll
-        for (int s = 0; s < kT / 16; s++) {
+        for (int s = 0; s < kT1 / 16; s++) {
             const int col = 16 * s + n;
-            float dl = to_f32<T>(sDl[r][col]) + bias;
-            if (p.softplus) dl = softplus_f32(dl);
-            if (t0 + col >= L) dl = 0.0f;
-            const float dlu = dl * to_f32<T>(sU[r][col]);
+            float x = to_f32<T>(sDl[r][col]) + bias;
+            if (p.softplus) x = softplus_f32(x);
+            dl[s] = (t0 + col < L) ? x : 0.0f;
+            dlu[s] = dl[s] * to_f32<T>(sU[r][col]);
+        }
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                float dj, duj;
-                SS_BCAST_CASES(dl, dj, j)
-                SS_BCAST_CASES(dlu, duj, j)
-                h = __builtin_fmaf(exp2_hw(dj * a2), h, duj * sB[n][16 * s + j]);
+        for (int s = 0; s < kT1 / 16; s++) {
+            if (s % (kC / 16) == 0) {
+                const int64_t k = (t0 + 16 * s) / kC;
+                if (row_ok && k < nck) ck[k * kN] = h;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
+                switch (q) {
+#define SS_FSTEP4(Q)                                            \
+    case Q:                                                     \
+        fwd_step<4 * Q + 0>(dl[s], dlu[s], a2, b4.x, h);        \
+        fwd_step<4 * Q + 1>(dl[s], dlu[s], a2, b4.y, h);        \
+        fwd_step<4 * Q + 2>(dl[s], dlu[s], a2, b4.z, h);        \
+        fwd_step<4 * Q + 3>(dl[s], dlu[s], a2, b4.w, h);        \
+        break;
+                    SS_FSTEP4(0) SS_FSTEP4(1) SS_FSTEP4(2) SS_FSTEP4(3)
+#undef SS_FSTEP4
+                }
             }
         }
         __syncthreads();
-        if (c + 1 < nck) stash();
+        if (c + 1 < nchunks) st.stash(smem);
         __syncthreads();
     }
 }
@@ -227,23 +214,44 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
 // ---------------------------------------------------------------------------
 // kernel 2: reverse pass
 // ---------------------------------------------------------------------------
+constexpr int kPitch2 = kC + 4;
+
+template <typename T>
+struct RevSmem {
+    static constexpr uint32_t kB = 0;
+    static constexpr uint32_t kCc = kB + kN * kPitch2 * 4;
+    static constexpr uint32_t kUn = kCc + kN * kPitch2 * 4;         // union: raw tiles / transposes
+    static constexpr uint32_t kU = kUn;
+    static constexpr uint32_t kDl = kU + kRows * kC * sizeof(T);
+    static constexpr uint32_t kZ = kDl + kRows * kC * sizeof(T);
+    static constexpr uint32_t kG = kZ + kRows * kC * sizeof(T);
+    static constexpr uint32_t kRawEnd = kG + kRows * kC * sizeof(T);
+    static constexpr uint32_t kTr = kUn;
+    static constexpr uint32_t kTrEnd = kTr + 4 * 4 * kYRow * 4;
+    static constexpr uint32_t kUnEnd = kRawEnd > kTrEnd ? kRawEnd : kTrEnd;
+    static constexpr uint32_t kDu = kUnEnd;                          // output tiles
+    static constexpr uint32_t kDd = kDu + kRows * kC * sizeof(T);
+    static constexpr uint32_t kDz = kDd + kRows * kC * sizeof(T);
+    // channel sums: [block 2][wave 4][quantity 2][step 16][state 16 + 4 pad]
+    static constexpr uint32_t kCh = kDz + kRows * kC * sizeof(T);
+    static constexpr int kChRow = 20;
+    static constexpr uint32_t kSize = kCh + 2 * 4 * 2 * 16 * kChRow * 4;
+};
+
 template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
-    constexpr int kVecPerRow = kT / VEC;
-    constexpr int kVecPerTile = 16 * kVecPerRow;
-    constexpr int kTiles = 6;  // B, C, u, delta, z, dout
-    constexpr int kSlots = (kTiles * kVecPerTile + kThreads - 1) / kThreads;
-    __shared__ float sB[kN][kPitch];
-    __shared__ float sC[kN][kPitch];
-    __shared__ __attribute__((aligned(16))) T sU[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sDl[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sZ[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sG[kRows][kT];   // dout
-    __shared__ __attribute__((aligned(16))) T sDu[kRows][kT];  // outputs
-    __shared__ __attribute__((aligned(16))) T sDd[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sDz[kRows][kT];
-    // shared by the per-wave state transposes and the workgroup channel sums
-    __shared__ __attribute__((aligned(16))) float sR[4 * 2 * 4 * kYBlock];
+__global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
+    using SM = RevSmem<T>;
+    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
+    float(*sB)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kB);
+    float(*sC)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kCc);
+    T(*sU)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kU);
+    T(*sDl)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDl);
+    T(*sZ)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kZ);
+    T(*sG)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kG);
+    T(*sDu)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDu);
+    T(*sDd)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDd);
+    T(*sDz)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDz);
+    float *chan = reinterpret_cast<float *>(smem + SM::kCh);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rw = lane >> 4, n = lane & 15, r = wave * 4 + rw;
@@ -251,78 +259,56 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_reverse_kernel(BwdParams p, W
     const int64_t d0 = int64_t(blockIdx.x) * kRows, d = d0 + r;
     const int64_t group = blockIdx.x, groups = gridDim.x;
     const bool row_ok = d < Dm;
+    const int valid_rows = int(Dm - d0 < kRows ? Dm - d0 : kRows);
     const bool has_z = p.z != nullptr;
-    const T *gu = static_cast<const T *>(p.u);
-    const T *gdl = static_cast<const T *>(p.delta);
-    const T *gz = static_cast<const T *>(p.z);
-    const T *gdo = static_cast<const T *>(p.dout);
-    const T *gB = static_cast<const T *>(p.B);
-    const T *gC = static_cast<const T *>(p.C);
 
     const float aval = row_ok ? p.A[d * kN + n] : 0.0f;
     const float a2 = aval * kLog2e;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
-    const int64_t nck = (L + kT - 1) / kT;
+    const int64_t nck = (L + kC - 1) / kC;
     const float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
 
     float g = (row_ok && p.dlast) ? p.dlast[(b * Dm + d) * kN + n] : 0.0f;
-    float dA_acc = 0.0f;   // this lane's state entry
-    float dD_acc = 0.0f;   // elements t = 16 s + n of this lane's row
+    float dA_acc = 0.0f;     // this lane's state entry, summed over time
+    float dD_acc = 0.0f;     // elements owned by this lane
     float dbias_acc = 0.0f;
 
-    T pre[kSlots][VEC];
-    auto fetch = [&](int64_t t0) {
-#pragma unroll
-        for (int k = 0; k < kSlots; k++) {
-            const int slot = tid + k * kThreads;
-            const int tile = slot / kVecPerTile, rem = slot % kVecPerTile;
-            const int row = rem / kVecPerRow;
-            const int64_t t = t0 + (rem % kVecPerRow) * VEC;
-            const T *base = gu;
-            bool ok = false;
-            if (tile == 0) {
-                base = gB + (b * kN + row) * L; ok = true;
-            } else if (tile == 1) {
-                base = gC + (b * kN + row) * L; ok = true;
-            } else if (tile < kTiles && d0 + row < Dm && (tile != 4 || has_z)) {
-                const T *g0 = tile == 2 ? gu : tile == 3 ? gdl : tile == 4 ? gz : gdo;
-                base = g0 + (b * Dm + d0 + row) * L; ok = true;
+    const T *gB = static_cast<const T *>(p.B) + b * kN * L;
+    const T *gC = static_cast<const T *>(p.C) + b * kN * L;
+    const int64_t rowbase = (b * Dm + d0) * L;
+    const T *gu = static_cast<const T *>(p.u) + rowbase;
+    const T *gdl = static_cast<const T *>(p.delta) + rowbase;
+    const T *gz = has_z ? static_cast<const T *>(p.z) + rowbase : nullptr;
+    const T *gdo = static_cast<const T *>(p.dout) + rowbase;
+    ChunkStager<T, VEC, kC, 6, kThreads> st;
+    st.init(
+        [&](int i) -> TileSrc<T> {
+            switch (i) {
+                case 0: return {gB, L, kN, SM::kB, kPitch2, true};
+                case 1: return {gC, L, kN, SM::kCc, kPitch2, true};
+                case 2: return {gu, L, valid_rows, SM::kU, kC, false};
+                case 3: return {gdl, L, valid_rows, SM::kDl, kC, false};
+                case 4: return {gz, L, valid_rows, SM::kZ, kC, false};
+                default: return {gdo, L, valid_rows, SM::kG, kC, false};
             }
-            load_vec<T, VEC>(base, t, L, ok, pre[k]);
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int k = 0; k < kSlots; k++) {
-            const int slot = tid + k * kThreads;
-            const int tile = slot / kVecPerTile, rem = slot % kVecPerTile;
-            if (tile >= kTiles) continue;
-            const int row = rem / kVecPerRow, col = (rem % kVecPerRow) * VEC;
-            if (tile < 2) {
-                float *dst = tile == 0 ? &sB[row][col] : &sC[row][col];
-#pragma unroll
-                for (int e = 0; e < VEC; e++) dst[e] = to_f32<T>(pre[k][e]);
-            } else {
-                T *dst = tile == 2 ? &sU[row][col] : tile == 3 ? &sDl[row][col]
-                       : tile == 4 ? &sZ[row][col] : &sG[row][col];
-#pragma unroll
-                for (int e = 0; e < VEC; e++) dst[e] = pre[k][e];
-            }
-        }
-    };
+        },
+        tid);
 
-    if (nck > 0) { fetch((nck - 1) * kT); stash(); }
+    if (nck > 0) {
+        st.fetch((nck - 1) * kC, L);
+        st.stash(smem);
+    }
     __syncthreads();
 
-    float *wbuf = &sR[wave * 2 * 4 * kYBlock];  // this wave's transpose region
+    float *tr = reinterpret_cast<float *>(smem + SM::kTr) + wave * 4 * kYRow + rw * kYRow;
     for (int64_t c = nck - 1; c >= 0; c--) {
-        const int64_t t0 = c * kT;
-        if (c > 0) fetch(t0 - kT);
+        const int64_t t0 = c * kC;
+        if (c > 0) st.fetch(t0 - kC, L);
         const float hstart = row_ok ? ck[c * kN] : 0.0f;
 
-        // per-element values, lane (r, n) owns elements 16 s + n
-        float dl[2], dlu[2], uu[2], sgd[2], dy[2];
+        // per-element values: lane (r, n) owns elements 16 s + n of its row
+        float dl[2], dlu[2], uu[2], sgd[2], dout[2], zz[2], dy[2];
 #pragma unroll
         for (int s = 0; s < 2; s++) {
             const int col = 16 * s + n;
@@ -333,126 +319,140 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_reverse_kernel(BwdParams p, W
                 x = softplus_f32(raw);
                 sgd[s] = sigmoid_f32(raw);
             }
-            if (t0 + col >= L) x = 0.0f;
+            dl[s] = (t0 + col < L) ? x : 0.0f;   // padding steps: no decay, no input
             uu[s] = to_f32<T>(sU[r][col]);
-            dl[s] = x;
-            dlu[s] = x * uu[s];
+            dlu[s] = dl[s] * uu[s];
+            dout[s] = to_f32<T>(sG[r][col]);
+            zz[s] = to_f32<T>(sZ[r][col]);
         }
+        __syncthreads();  // the transpose region aliases the raw tiles
 
-        // forward over the chunk from its checkpoint: decays and states
-        float ab[kT], hs[kT];
+        // ---- forward over the chunk: decays and states in registers ----
+        float ab[kC], hs[kC];
         float h = hstart;
 #pragma unroll
         for (int s = 0; s < 2; s++) {
-            float v[16];
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                float dj, duj;
-                SS_BCAST_CASES(dl[s], dj, j)
-                SS_BCAST_CASES(dlu[s], duj, j)
-                const int t = 16 * s + j;
-                ab[t] = exp2_hw(dj * a2);
-                h = __builtin_fmaf(ab[t], h, duj * sB[n][t]);
-                hs[t] = h;
-                v[j] = sC[n][t] * h;
+            for (int q = 0; q < 4; q++) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
+                const float4 c4 = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
+                const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+                const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int t = 16 * s + 4 * q + e;
+                    float dj, duj;
+                    switch (4 * q + e) {
+#define SS_BC(J) case J: dj = row_bcast<J>(dl[s]); duj = row_bcast<J>(dlu[s]); break;
+                        SS_BC(0) SS_BC(1) SS_BC(2) SS_BC(3) SS_BC(4) SS_BC(5) SS_BC(6) SS_BC(7)
+                        SS_BC(8) SS_BC(9) SS_BC(10) SS_BC(11) SS_BC(12) SS_BC(13) SS_BC(14)
+                        default: dj = row_bcast<15>(dl[s]); duj = row_bcast<15>(dlu[s]); break;
+#undef SS_BC
+                    }
+                    ab[t] = exp2_hw(dj * a2);
+                    h = __builtin_fmaf(ab[t], h, duj * bb[e]);
+                    hs[t] = h;
+                    v[e] = cc[e] * h;
+                }
+                if (has_z)
+                    *reinterpret_cast<float4 *>(&tr[n * kYN + 4 * q]) =
+                        make_float4(v[0], v[1], v[2], v[3]);
             }
             const int col = 16 * s + n;
-            const float dout = to_f32<T>(sG[r][col]);
             if (has_z) {
-                // pre-gate output of element (r, col): transpose-sum over states
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-                    *reinterpret_cast<float4 *>(&wbuf[rw * kYBlock + n * 16 + 4 * q]) =
-                        make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
                 __builtin_amdgcn_wave_barrier();
                 float part[16];
 #pragma unroll
-                for (int k = 0; k < 16; k++) part[k] = wbuf[rw * kYBlock + k * 16 + n];
+                for (int k = 0; k < 16; k++) part[k] = tr[k * kYN + n];
                 __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int w = 1; w < 16; w *= 2)
-#pragma unroll
-                    for (int k = 0; k < 16; k += 2 * w) part[k] += part[k + w];
-                const float ypre = part[0] + dskip * uu[s];
-                const float zz = to_f32<T>(sZ[r][col]);
-                const float sz = sigmoid_f32(zz);
-                dy[s] = dout * zz * sz;
-                sDz[r][col] = from_f32<T>(dout * ypre * sz * (1.0f + zz * (1.0f - sz)));
+                const float ypre = tree16(part) + dskip * uu[s];
+                const float sz = sigmoid_f32(zz[s]);
+                dy[s] = dout[s] * zz[s] * sz;
+                sDz[r][col] = from_f32<T>(dout[s] * ypre * sz * (1.0f + zz[s] * (1.0f - sz)));
             } else {
-                dy[s] = dout;
+                dy[s] = dout[s];
             }
             if (t0 + col < L) dD_acc = __builtin_fmaf(dy[s], uu[s], dD_acc);
         }
 
-        // backward over the chunk, 16 steps at a time
+        // ---- backward over the chunk, 16 steps at a time ----
 #pragma unroll
         for (int s = 1; s >= 0; s--) {
-            float qa[16], qb[16], qdb[16], qdc[16];
+            floatx4 accB = {0.0f, 0.0f, 0.0f, 0.0f};
+            floatx4 accC = {0.0f, 0.0f, 0.0f, 0.0f};
+            float sumA = 0.0f, sumB = 0.0f;
 #pragma unroll
-            for (int j = 15; j >= 0; j--) {
-                const int t = 16 * s + j;
-                float dyj, dj, duj;
-                SS_BCAST_CASES(dy[s], dyj, j)
-                SS_BCAST_CASES(dl[s], dj, j)
-                SS_BCAST_CASES(dlu[s], duj, j)
-                g = __builtin_fmaf(sC[n][t], dyj, g);                 // g_t
-                const float hprev = t > 0 ? hs[t - 1] : hstart;
-                const float gp = g * (ab[t] * hprev);
-                dA_acc = __builtin_fmaf(gp, dj, dA_acc);
-                qa[j] = aval * gp;
-                qb[j] = g * sB[n][t];
-                qdb[j] = g * duj;
-                qdc[j] = dyj * hs[t];
-                g = ab[t] * g;                                        // carried to t-1
-            }
-            // sums over the 16 states (per-wave transpose)
+            for (int hh = 1; hh >= 0; hh--) {
+                float qa[8], qb[8];
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                *reinterpret_cast<float4 *>(&wbuf[rw * kYBlock + n * 16 + 4 * q]) =
-                    make_float4(qa[4 * q], qa[4 * q + 1], qa[4 * q + 2], qa[4 * q + 3]);
-                *reinterpret_cast<float4 *>(&wbuf[4 * kYBlock + rw * kYBlock + n * 16 + 4 * q]) =
-                    make_float4(qb[4 * q], qb[4 * q + 1], qb[4 * q + 2], qb[4 * q + 3]);
-            }
-            __builtin_amdgcn_wave_barrier();
-            float pa[16], pb[16];
-#pragma unroll
-            for (int k = 0; k < 16; k++) {
-                pa[k] = wbuf[rw * kYBlock + k * 16 + n];
-                pb[k] = wbuf[4 * kYBlock + rw * kYBlock + k * 16 + n];
-            }
-#pragma unroll
-            for (int w = 1; w < 16; w *= 2)
-#pragma unroll
-                for (int k = 0; k < 16; k += 2 * w) {
-                    pa[k] += pa[k + w];
-                    pb[k] += pb[k + w];
+                for (int jj = 7; jj >= 0; jj--) {
+                    const int j = 8 * hh + jj;
+                    const int t = 16 * s + j;
+                    float dyj, dj;
+                    switch (j) {
+#define SS_BC(J) case J: dyj = row_bcast<J>(dy[s]); dj = row_bcast<J>(dl[s]); break;
+                        SS_BC(0) SS_BC(1) SS_BC(2) SS_BC(3) SS_BC(4) SS_BC(5) SS_BC(6) SS_BC(7)
+                        SS_BC(8) SS_BC(9) SS_BC(10) SS_BC(11) SS_BC(12) SS_BC(13) SS_BC(14)
+                        default: dyj = row_bcast<15>(dy[s]); dj = row_bcast<15>(dl[s]); break;
+#undef SS_BC
+                    }
+                    g = __builtin_fmaf(sC[n][t], dyj, g);                 // g_t
+                    const float hprev = t > 0 ? hs[t - 1] : hstart;
+                    const float gp = g * (ab[t] * hprev);
+                    dA_acc = __builtin_fmaf(gp, dj, dA_acc);
+                    qa[jj] = aval * gp;
+                    qb[jj] = g * sB[n][t];
+                    // channel sums on the matrix core: column j of the 16 x 16 result
+                    const bool mine = (n == j);
+                    accB = __builtin_amdgcn_mfma_f32_16x16x4f32(g, mine ? dlu[s] : 0.0f, accB, 0, 0, 0);
+                    accC = __builtin_amdgcn_mfma_f32_16x16x4f32(hs[t], mine ? dy[s] : 0.0f, accC, 0, 0, 0);
+                    g = ab[t] * g;                                        // carried to t - 1
                 }
+                // sums over the 16 states: columns 0-7 carry A*g*abar*h, 8-15 g*B
+                *reinterpret_cast<float4 *>(&tr[n * kYN + 0]) = make_float4(qa[0], qa[1], qa[2], qa[3]);
+                *reinterpret_cast<float4 *>(&tr[n * kYN + 4]) = make_float4(qa[4], qa[5], qa[6], qa[7]);
+                *reinterpret_cast<float4 *>(&tr[n * kYN + 8]) = make_float4(qb[0], qb[1], qb[2], qb[3]);
+                *reinterpret_cast<float4 *>(&tr[n * kYN + 12]) = make_float4(qb[4], qb[5], qb[6], qb[7]);
+                __builtin_amdgcn_wave_barrier();
+                float part[16];
+#pragma unroll
+                for (int k = 0; k < 16; k++) part[k] = tr[k * kYN + n];
+                __builtin_amdgcn_wave_barrier();
+                const float sum = tree16(part);
+                const float other = row_ror8(sum);
+                // owner lanes of steps 8 hh .. 8 hh + 7 pick up both sums
+                if (hh == 0 && n < 8) { sumA = sum; sumB = other; }
+                if (hh == 1 && n >= 8) { sumA = other; sumB = sum; }
+            }
             {
                 const int col = 16 * s + n;
-                const float sumA = pa[0], sumB = pb[0];
                 const float du = __builtin_fmaf(dl[s], sumB, dskip * dy[s]);
                 const float dd = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];
                 sDu[r][col] = from_f32<T>(du);
                 sDd[r][col] = from_f32<T>(dd);
                 if (t0 + col < L) dbias_acc += dd;
             }
-            __syncthreads();  // transposes done: the region becomes the channel-sum tile
-            // sums over the workgroup's 16 channels: tile [q][row][state][step]
+            // this wave's channel sums (4 rows): lane (rw, j) holds states 4 rw .. 4 rw + 3 of step j
+            float *cb = chan + ((s * 4 + wave) * 2) * 16 * SM::kChRow;
+            *reinterpret_cast<float4 *>(&cb[n * SM::kChRow + 4 * rw]) =
+                make_float4(accB[0], accB[1], accB[2], accB[3]);
+            *reinterpret_cast<float4 *>(&cb[16 * SM::kChRow + n * SM::kChRow + 4 * rw]) =
+                make_float4(accC[0], accC[1], accC[2], accC[3]);
+        }
+        __syncthreads();
+
+        // add the 4 wavefronts' channel sums: thread (state sn, step sj)
+        {
+            const int sn = tid >> 4, sj = tid & 15;
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                *reinterpret_cast<float4 *>(&sR[(0 * 16 + r) * 256 + n * 16 + 4 * q]) =
-                    make_float4(qdb[4 * q], qdb[4 * q + 1], qdb[4 * q + 2], qdb[4 * q + 3]);
-                *reinterpret_cast<float4 *>(&sR[(1 * 16 + r) * 256 + n * 16 + 4 * q]) =
-                    make_float4(qdc[4 * q], qdc[4 * q + 1], qdc[4 * q + 2], qdc[4 * q + 3]);
-            }
-            __syncthreads();
-            {
-                const int sn = tid >> 4, sj = tid & 15;  // state, step of this thread's sum
+            for (int s = 0; s < 2; s++) {
                 float accb = 0.0f, accc = 0.0f;
 #pragma unroll
-                for (int rr = 0; rr < kRows; rr++) {
-                    accb += sR[(0 * 16 + rr) * 256 + sn * 16 + sj];
-                    accc += sR[(1 * 16 + rr) * 256 + sn * 16 + sj];
+                for (int w = 0; w < 4; w++) {
+                    const float *cb = chan + ((s * 4 + w) * 2) * 16 * SM::kChRow;
+                    accb += cb[sj * SM::kChRow + sn];
+                    accc += cb[16 * SM::kChRow + sj * SM::kChRow + sn];
                 }
                 const int64_t t = t0 + 16 * s + sj;
                 if (t < L) {
@@ -461,32 +461,21 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_reverse_kernel(BwdParams p, W
                     ws.dCp[o] = accc;
                 }
             }
-            __syncthreads();
         }
-
-        // store this chunk's du, ddelta, dz
-        constexpr int kOutVecs = kRows * kT / VEC;
-#pragma unroll
-        for (int k = 0; k < (kOutVecs + kThreads - 1) / kThreads; k++) {
-            const int slot = tid + k * kThreads;
-            if (slot < kOutVecs) {
-                const int row = slot / (kT / VEC), col = (slot % (kT / VEC)) * VEC;
-                if (d0 + row < Dm) {
-                    const int64_t base = (b * Dm + d0 + row) * L;
-                    store_vec<T, VEC>(static_cast<T *>(p.du) + base, t0 + col, L, &sDu[row][col]);
-                    store_vec<T, VEC>(static_cast<T *>(p.ddelta) + base, t0 + col, L, &sDd[row][col]);
-                    if (has_z)
-                        store_vec<T, VEC>(static_cast<T *>(p.dz) + base, t0 + col, L, &sDz[row][col]);
-                }
-            }
+        T *du_g = static_cast<T *>(p.du) + rowbase;
+        T *dd_g = static_cast<T *>(p.ddelta) + rowbase;
+        store_tile<T, VEC, kC, kThreads>(du_g, L, valid_rows, t0, L, &sDu[0][0], tid);
+        store_tile<T, VEC, kC, kThreads>(dd_g, L, valid_rows, t0, L, &sDd[0][0], tid);
+        if (has_z) {
+            T *dz_g = static_cast<T *>(p.dz) + rowbase;
+            store_tile<T, VEC, kC, kThreads>(dz_g, L, valid_rows, t0, L, &sDz[0][0], tid);
         }
-        if (c > 0) stash();
+        if (c > 0) st.stash(smem);
         __syncthreads();
     }
 
     // per-row partials of the parameter gradients
     if (row_ok) ws.dAp[(b * Dm + d) * kN + n] = dA_acc;
-    // sum the 16 lanes of the row (commutative butterfly: all lanes agree)
     dD_acc = row_sum16(dD_acc);
     dbias_acc = row_sum16(dbias_acc);
     if (row_ok && n == 0) {
@@ -539,13 +528,17 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
     if (p.batch > 0 && p.dim > 0) {
         dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch));
         constexpr int kVec = 16 / sizeof(T);
-        if ((p.seqlen * int64_t(sizeof(T))) % 16 == 0) {
+        const bool vec = (p.seqlen * int64_t(sizeof(T))) % 16 == 0;
+        if (vec)
             hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
-            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
-        } else {
+        else
             hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
+        profile_mark(stream);
+        if (vec)
+            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
+        else
             hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
-        }
+        profile_mark(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -553,6 +546,7 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
     if (total > 0) {
         hipLaunchKernelGGL((ss_bwd_fold_kernel<T>), dim3(unsigned((total + 255) / 256)), dim3(256),
                            0, stream, p, ws);
+        profile_mark(stream);
     }
     return hipGetLastError();
 }

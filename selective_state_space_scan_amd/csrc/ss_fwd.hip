@@ -6,246 +6,192 @@
 // with delta_t = softplus(delta_raw_t + bias[d]) -- the selective SSM that
 // the state-spaces/mamba README names under "Usage / Selective SSM".
 //
-// Work mapping (chosen for the MI355X execution model, not taken from any
-// other GPU's kernel):
+// Work mapping (chosen for the MI355X execution model):
 //   * one lane per (row, state index n): a 64-wide wavefront holds 4 rows x
 //     16 states, one row per 16-lane DPP row; a 256-thread workgroup holds
 //     16 consecutive channels of one batch entry;
 //   * each lane runs the recurrence sequentially in time.  This is the
-//     cheapest form of the scan in arithmetic (one exp, one multiply for
-//     delta*A, one for delta*u*B and one FMA per step and state); the
+//     cheapest form of the scan in arithmetic (per step and state: one
+//     exp, a multiply for delta*A, one for delta*u*B and one FMA); the
 //     parallelism comes from the batch x channel x state lanes, which fill
 //     3-5 waves per SIMD at the Mamba layer shapes;
-//   * time is staged through LDS in chunks of 32 steps with coalesced
-//     16-byte global loads, prefetched one chunk ahead in registers;
+//   * time is staged through LDS in chunks of 64 steps with coalesced
+//     16-byte loads, prefetched one chunk ahead into registers;
 //   * per-element work (softplus, delta*u, gate) is done once per element by
-//     the lane whose index within the DPP row equals the step within a
-//     16-step block; the scan lanes pick delta and delta*u up with a DPP row
-//     broadcast instead of a memory round trip;
-//   * the output sum over the 16 states goes through a padded per-wave LDS
-//     transpose every 16 steps and is added in a fixed order, so a row's
-//     bits do not depend on the batch size or on which other rows share the
-//     workgroup.
+//     the lane whose index in its DPP row equals the element's step within a
+//     16-step block; the scan lanes take delta and delta*u from it with a DPP
+//     row broadcast folded into their multiplies;
+//   * the output's sum over the 16 states goes through a per-wave LDS
+//     transpose every 16 steps, padded so that neither the 16-byte writes
+//     nor the 4-byte reads hit the same bank twice, and is added in a fixed
+//     order -- a row's bits do not depend on the batch size or on the other
+//     rows of its workgroup.
 #include "ss_device.h"
 #include "ss_kernels.h"
+#include "ss_tiles.h"
 
 namespace ssk {
 namespace {
 
-constexpr int kRows = 16;             // channels per workgroup
-constexpr int kT = 32;                // time steps per LDS chunk
-constexpr int kThreads = 256;         // 4 wavefronts
-constexpr int kPitch = kT + 4;        // padded pitch of the f32 B / C tiles
-constexpr int kYBlock = kN * 16 + 16; // per-row block of the output transpose (padded)
+constexpr int kRows = 16;       // channels per workgroup
+constexpr int kT = 64;          // time steps per LDS chunk
+constexpr int kThreads = 256;   // 4 wavefronts
+constexpr int kPitch = kT + 4;  // f32 B / C tile pitch (conflict-free 16-byte reads)
+constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
+constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row (row offset = 16 banks)
 
-template <typename T, int VEC>
-struct Tiles {
-    static constexpr int kVecPerRow = kT / VEC;
-    static constexpr int kVecPerTile = 16 * kVecPerRow;
-    static constexpr int kNumTiles = 5;  // B, C, u, delta, z
-    static constexpr int kSlots = (kNumTiles * kVecPerTile + kThreads - 1) / kThreads;
+template <typename T>
+struct FwdSmem {
+    static constexpr uint32_t kB = 0;
+    static constexpr uint32_t kC = kB + kN * kPitch * 4;
+    static constexpr uint32_t kU = kC + kN * kPitch * 4;                  // union start
+    static constexpr uint32_t kDl = kU + kRows * kT * sizeof(T);
+    static constexpr uint32_t kZ = kDl + kRows * kT * sizeof(T);
+    static constexpr uint32_t kY = kU;                                    // aliases u / delta / z
+    static constexpr uint32_t kRawEnd = kZ + kRows * kT * sizeof(T);
+    static constexpr uint32_t kYEnd = kY + 4 * 4 * kYRow * 4;
+    static constexpr uint32_t kO = kRawEnd > kYEnd ? kRawEnd : kYEnd;
+    static constexpr uint32_t kSize = kO + kRows * kT * sizeof(T);
 };
 
-struct alignas(16) Raw16 {
-    uint32_t w[4];
-};
-
-template <typename T, int VEC>
-__device__ __forceinline__ void load_vec(const T *__restrict__ p, int64_t t, int64_t L,
-                                         bool row_ok, T (&dst)[VEC]) {
-    if (row_ok && t + VEC <= L) {
-        if constexpr (VEC * sizeof(T) == 16) {
-            Raw16 r = *reinterpret_cast<const Raw16 *>(p + t);
-            __builtin_memcpy(dst, &r, 16);
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; e++) dst[e] = p[t + e];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < VEC; e++) dst[e] = (row_ok && t + e < L) ? p[t + e] : T(0);
-    }
+template <int J>
+__device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b, float c,
+                                          float &h, float &v) {
+    const float abar = exp2_hw(row_bcast<J>(dl) * a2);
+    h = __builtin_fmaf(abar, h, row_bcast<J>(dlu) * b);
+    v = c * h;
 }
 
 template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
-    using TL = Tiles<T, VEC>;
-    __shared__ float sB[kN][kPitch];
-    __shared__ float sC[kN][kPitch];
-    __shared__ __attribute__((aligned(16))) T sU[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sDl[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sZ[kRows][kT];
-    __shared__ __attribute__((aligned(16))) T sO[kRows][kT];
-    __shared__ __attribute__((aligned(16))) float sY[4][4 * kYBlock];
+    using SM = FwdSmem<T>;
+    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
+    float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + SM::kB);
+    float(*sC)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + SM::kC);
+    T(*sU)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kU);
+    T(*sDl)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kDl);
+    T(*sZ)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kZ);
+    T(*sO)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kO);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int rw = lane >> 4;       // row within the wavefront (DPP row)
-    const int n = lane & 15;        // state index; also the step within a 16-step block
-    const int r = wave * 4 + rw;    // row within the workgroup
+    const int rw = lane >> 4;      // row within the wavefront (DPP row)
+    const int n = lane & 15;       // state index; also the step within a 16-step block
+    const int r = wave * 4 + rw;   // row within the workgroup
     const int64_t L = p.seqlen;
     const int64_t Dm = p.dim;
     const int64_t b = blockIdx.y;
     const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kRows;
     const int64_t d = d0 + r;
     const bool row_ok = d < Dm;
-
-    const T *__restrict__ gu = static_cast<const T *>(p.u);
-    const T *__restrict__ gdl = static_cast<const T *>(p.delta);
-    const T *__restrict__ gz = static_cast<const T *>(p.z);
-    const T *__restrict__ gB = static_cast<const T *>(p.B);
-    const T *__restrict__ gC = static_cast<const T *>(p.C);
-    T *__restrict__ gy = static_cast<T *>(p.out);
+    const int valid_rows = static_cast<int>(Dm - d0 < kRows ? Dm - d0 : kRows);
     const bool has_z = p.z != nullptr;
 
-    // per-lane constants
     const float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;  // A in base-2 exponent units
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
     float h = (row_ok && p.h0) ? p.h0[(b * Dm + d) * kN + n] : 0.0f;
 
-    // global -> register staging of one chunk
-    T pre[TL::kSlots][VEC];
-    auto fetch = [&](int64_t t0) {
-#pragma unroll
-        for (int k = 0; k < TL::kSlots; k++) {
-            const int slot = tid + k * kThreads;
-            const int tile = slot / TL::kVecPerTile;
-            const int rem = slot % TL::kVecPerTile;
-            const int row = rem / TL::kVecPerRow;
-            const int64_t t = t0 + (rem % TL::kVecPerRow) * VEC;
-            const T *base;
-            bool ok;
-            if (tile == 0) {
-                base = gB + (b * kN + row) * L; ok = true;
-            } else if (tile == 1) {
-                base = gC + (b * kN + row) * L; ok = true;
-            } else {
-                const T *g = tile == 2 ? gu : (tile == 3 ? gdl : gz);
-                ok = (tile < TL::kNumTiles) && (d0 + row < Dm) && (tile != 4 || has_z);
-                base = ok ? g + (b * Dm + d0 + row) * L : gu;
+    const T *gu = static_cast<const T *>(p.u) + (b * Dm + d0) * L;
+    const T *gdl = static_cast<const T *>(p.delta) + (b * Dm + d0) * L;
+    const T *gz = has_z ? static_cast<const T *>(p.z) + (b * Dm + d0) * L : nullptr;
+    const T *gB = static_cast<const T *>(p.B) + b * kN * L;
+    const T *gC = static_cast<const T *>(p.C) + b * kN * L;
+    ChunkStager<T, VEC, kT, 5, kThreads> st;
+    st.init(
+        [&](int i) -> TileSrc<T> {
+            switch (i) {
+                case 0: return {gB, L, kN, SM::kB, kPitch, true};
+                case 1: return {gC, L, kN, SM::kC, kPitch, true};
+                case 2: return {gu, L, valid_rows, SM::kU, kT, false};
+                case 3: return {gdl, L, valid_rows, SM::kDl, kT, false};
+                default: return {gz, L, valid_rows, SM::kZ, kT, false};
             }
-            load_vec<T, VEC>(base, t, L, ok, pre[k]);
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int k = 0; k < TL::kSlots; k++) {
-            const int slot = tid + k * kThreads;
-            const int tile = slot / TL::kVecPerTile;
-            if (tile >= TL::kNumTiles) continue;
-            const int rem = slot % TL::kVecPerTile;
-            const int row = rem / TL::kVecPerRow;
-            const int col = (rem % TL::kVecPerRow) * VEC;
-            if (tile < 2) {
-                float *dst = tile == 0 ? &sB[row][col] : &sC[row][col];
-#pragma unroll
-                for (int e = 0; e < VEC; e++) dst[e] = to_f32<T>(pre[k][e]);
-            } else {
-                T *dst = tile == 2 ? &sU[row][col] : (tile == 3 ? &sDl[row][col] : &sZ[row][col]);
-#pragma unroll
-                for (int e = 0; e < VEC; e++) dst[e] = pre[k][e];
-            }
-        }
-    };
+        },
+        tid);
 
     const int64_t nchunks = (L + kT - 1) / kT;
     if (nchunks > 0) {
-        fetch(0);
-        stash();
+        st.fetch(0, L);
+        st.stash(smem);
     }
     __syncthreads();
 
-    float *ybuf = &sY[wave][0];
+    float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
+    T *gy = static_cast<T *>(p.out) + (b * Dm + d0) * L;
     for (int64_t c = 0; c < nchunks; c++) {
         const int64_t t0 = c * kT;
-        if (c + 1 < nchunks) fetch(t0 + kT);
+        if (c + 1 < nchunks) st.fetch(t0 + kT, L);
 
+        // per-element work: lane (r, n) owns elements 16 s + n of its row
+        float dl[kT / 16], dlu[kT / 16], uu[kT / 16], zz[kT / 16];
 #pragma unroll
         for (int s = 0; s < kT / 16; s++) {
-            // per-element work for element (r, t0 + 16 s + n)
             const int col = 16 * s + n;
-            const bool t_ok = t0 + col < L;
-            const float uu = to_f32<T>(sU[r][col]);
-            const float zz = to_f32<T>(sZ[r][col]);
-            float dl = to_f32<T>(sDl[r][col]) + bias;
-            if (p.softplus) dl = softplus_f32(dl);
-            if (!t_ok) dl = 0.0f;        // padding steps leave the state unchanged
-            const float dlu = dl * uu;
+            uu[s] = to_f32<T>(sU[r][col]);
+            zz[s] = to_f32<T>(sZ[r][col]);
+            float x = to_f32<T>(sDl[r][col]) + bias;
+            if (p.softplus) x = softplus_f32(x);
+            dl[s] = (t0 + col < L) ? x : 0.0f;   // padding steps leave the state unchanged
+            dlu[s] = dl[s] * uu[s];
+        }
+        __syncthreads();  // the transpose region aliases u / delta / z
 
-            // 16 recurrence steps: lane (r, n) advances state entry n of row r
-            float v[16];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const float4 b4 = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
-                const float4 c4 = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
-                const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-                const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    float dj, duj;
-                    switch (4 * q + e) {
-#define SS_BCAST(J) case J: dj = row_bcast<J>(dl); duj = row_bcast<J>(dlu); break;
-                        SS_BCAST(0) SS_BCAST(1) SS_BCAST(2) SS_BCAST(3)
-                        SS_BCAST(4) SS_BCAST(5) SS_BCAST(6) SS_BCAST(7)
-                        SS_BCAST(8) SS_BCAST(9) SS_BCAST(10) SS_BCAST(11)
-                        SS_BCAST(12) SS_BCAST(13) SS_BCAST(14) SS_BCAST(15)
-#undef SS_BCAST
-                    }
-                    const float abar = exp2_hw(dj * a2);
-                    h = __builtin_fmaf(abar, h, duj * bb[e]);
-                    v[4 * q + e] = cc[e] * h;
-                }
-            }
-
-            // sum over the 16 states: per-wave transpose through LDS
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-                *reinterpret_cast<float4 *>(&ybuf[rw * kYBlock + n * 16 + 4 * q]) =
-                    make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-            __builtin_amdgcn_wave_barrier();
-            float part[16];
-#pragma unroll
-            for (int k = 0; k < 16; k++) part[k] = ybuf[rw * kYBlock + k * 16 + n];
-            __builtin_amdgcn_wave_barrier();
-            // fixed pairwise order over the state index
+        // Output sums over the 16 states go through this wave's LDS region:
+        // block s writes its per-state terms four steps at a time; their
+        // transposed reads are issued at the start of block s + 1 and summed
+        // at its end, so the LDS round trip overlaps the next 16 steps.
+        float part[16];
+        auto finish = [&](int s) {
 #pragma unroll
             for (int w = 1; w < 16; w *= 2)
 #pragma unroll
                 for (int k = 0; k < 16; k += 2 * w) part[k] += part[k + w];
-            float y = part[0] + dskip * uu;
-            if (has_z) y *= zz * sigmoid_f32(zz);
-            sO[r][col] = from_f32<T>(y);
+            float y = part[0] + dskip * uu[s];
+            if (has_z) y *= zz[s] * sigmoid_f32(zz[s]);
+            sO[r][16 * s + n] = from_f32<T>(y);
+        };
+#pragma unroll
+        for (int s = 0; s < kT / 16; s++) {
+            float4 bq[4], cq[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                bq[q] = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
+                cq[q] = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
+            }
+            if (s > 0) {
+#pragma unroll
+                for (int k = 0; k < 16; k++) part[k] = ybuf[k * kYN + n];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                float v[4];
+                switch (q) {
+#define SS_STEP4(Q)                                                                  \
+    case Q:                                                                          \
+        scan_step<4 * Q + 0>(dl[s], dlu[s], a2, bq[Q].x, cq[Q].x, h, v[0]);          \
+        scan_step<4 * Q + 1>(dl[s], dlu[s], a2, bq[Q].y, cq[Q].y, h, v[1]);          \
+        scan_step<4 * Q + 2>(dl[s], dlu[s], a2, bq[Q].z, cq[Q].z, h, v[2]);          \
+        scan_step<4 * Q + 3>(dl[s], dlu[s], a2, bq[Q].w, cq[Q].w, h, v[3]);          \
+        break;
+                    SS_STEP4(0) SS_STEP4(1) SS_STEP4(2) SS_STEP4(3)
+#undef SS_STEP4
+                }
+                // in-order LDS: this write lands after the reads issued above
+                *reinterpret_cast<float4 *>(&ybuf[n * kYN + 4 * q]) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+            if (s > 0) finish(s - 1);
         }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int k = 0; k < 16; k++) part[k] = ybuf[k * kYN + n];
+        finish(kT / 16 - 1);
         __syncthreads();
 
-        // store the output chunk (coalesced 16-byte vectors)
-        constexpr int kOutVecs = kRows * kT / VEC;
-#pragma unroll
-        for (int k = 0; k < (kOutVecs + kThreads - 1) / kThreads; k++) {
-            const int slot = tid + k * kThreads;
-            if (slot < kOutVecs) {
-                const int row = slot / (kT / VEC);
-                const int col = (slot % (kT / VEC)) * VEC;
-                const int64_t t = t0 + col;
-                if (d0 + row < Dm) {
-                    T *dst = gy + (b * Dm + d0 + row) * L;
-                    if (t + VEC <= L) {
-                        if constexpr (VEC * sizeof(T) == 16) {
-                            *reinterpret_cast<Raw16 *>(dst + t) =
-                                *reinterpret_cast<const Raw16 *>(&sO[row][col]);
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < VEC; e++) dst[t + e] = sO[row][col + e];
-                        }
-                    } else {
-                        for (int e = 0; e < VEC && t + e < L; e++) dst[t + e] = sO[row][col + e];
-                    }
-                }
-            }
-        }
-        if (c + 1 < nchunks) stash();
+        store_tile<T, VEC, kT, kThreads>(gy, L, valid_rows, t0, L, &sO[0][0], tid);
+        if (c + 1 < nchunks) st.stash(smem);
         __syncthreads();
     }
 
@@ -261,6 +207,7 @@ hipError_t launch_typed(const FwdParams &p, hipStream_t stream) {
         hipLaunchKernelGGL((ss_fwd_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((ss_fwd_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p);
+    profile_mark(stream);
     return hipGetLastError();
 }
 

@@ -52,6 +52,9 @@ struct DecodeParams {
     void *out;
 };
 
+// Records the next armed profiling event on `stream` (no-op when unarmed).
+void profile_mark(hipStream_t stream);
+
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen);
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);

@@ -95,6 +95,7 @@ hipError_t launch_state_update(const DecodeParams &p, bool bf16, hipStream_t str
         hipLaunchKernelGGL((ss_state_update_kernel<bf16_t>), grid, dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((ss_state_update_kernel<float>), grid, dim3(kThreads), 0, stream, p);
+    profile_mark(stream);
     return hipGetLastError();
 }
 

@@ -1,0 +1,188 @@
+// ss_tiles.h -- global -> LDS staging of time chunks for the scan kernels.
+//
+// A chunk is a set of tiles, each 16 rows x KT time steps of one tensor
+// (rows are channels for u / delta / z / dout and state indices for B / C).
+// Every thread owns a fixed set of 16-byte slots of those tiles.  Source
+// pointers and LDS offsets of the slots are computed once.  A full chunk is
+// then staged with one unguarded 16-byte global load per slot, kept as raw
+// words in registers until the chunk before it is done (so the loads stay in
+// flight across a whole chunk of compute), and only the ragged last chunk
+// takes the guarded element path.  Tiles span whole wavefronts of slots, so
+// the tile a slot belongs to is uniform across a wavefront.
+#pragma once
+
+#include "ss_device.h"
+
+namespace ssk {
+
+struct alignas(16) Raw16 {
+    uint32_t w[4];
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte loads / stores through explicit global-address-space pointers, so
+// the compiler issues global (not flat) memory instructions.
+__device__ __forceinline__ u32x4 ld_global16(const void *p) {
+    return *(const __attribute__((address_space(1))) u32x4 *)(p);
+}
+__device__ __forceinline__ void st_global16(void *p, u32x4 v) {
+    *(__attribute__((address_space(1))) u32x4 *)(p) = v;
+}
+
+// One tile of a chunk.
+template <typename T>
+struct TileSrc {
+    const T *base;     // element (row 0, t = 0) of the tile; nullptr = absent (zeros)
+    int64_t row_stride;
+    int valid_rows;    // rows >= valid_rows read as zeros
+    uint32_t lds_off;  // byte offset of the tile in the kernel's LDS buffer
+    int pitch;         // LDS row pitch in elements of the LDS type
+    bool to_f32;       // stash as f32 (else as T)
+};
+
+template <typename T, int VEC, int KT, int NTILES, int NTHREADS>
+struct ChunkStager {
+    static_assert(VEC * sizeof(T) == 16 || VEC == 1, "slots are 16 bytes or single elements");
+    static constexpr int kVecPerRow = KT / VEC;
+    static constexpr int kVecPerTile = 16 * kVecPerRow;
+    static constexpr int kSlots = (NTILES * kVecPerTile + NTHREADS - 1) / NTHREADS;
+    static constexpr int kWords = (VEC * sizeof(T) + 3) / 4;
+
+    const T *src[kSlots];  // slot's first element at t = 0, or nullptr
+    uint32_t dst[kSlots];  // LDS byte offset, or ~0u for slots past the last tile
+    int col[kSlots];       // slot's first time offset within the chunk
+    bool f32[kSlots];
+    uint32_t reg[kSlots][kWords];
+
+    // `desc(i)` returns the TileSrc of tile i (called with constant i only).
+    template <typename Desc>
+    __device__ __forceinline__ void init(Desc desc, int tid) {
+#pragma unroll
+        for (int k = 0; k < kSlots; k++) {
+            const int slot = tid + k * NTHREADS;
+            // tiles span whole wavefronts of slots: the tile index is wave-uniform
+            const int tile = __builtin_amdgcn_readfirstlane(slot / kVecPerTile);
+            const int rem = slot % kVecPerTile;
+            const int row = rem / kVecPerRow;
+            col[k] = (rem % kVecPerRow) * VEC;
+            src[k] = nullptr;
+            dst[k] = ~0u;
+            f32[k] = false;
+            if (tile < NTILES) {
+                TileSrc<T> ts = desc(0);
+#pragma unroll
+                for (int i = 1; i < NTILES; i++)
+                    if (tile == i) ts = desc(i);
+                if (ts.base && row < ts.valid_rows) src[k] = ts.base + row * ts.row_stride + col[k];
+                f32[k] = ts.to_f32;
+                const uint32_t esz = ts.to_f32 ? 4u : uint32_t(sizeof(T));
+                dst[k] = ts.lds_off + uint32_t(row * ts.pitch + col[k]) * esz;
+            }
+        }
+    }
+
+    // Issues the loads of a full chunk that starts at t0 (t0 + KT <= L).
+    __device__ __forceinline__ void fetch_full(int64_t t0) {
+#pragma unroll
+        for (int k = 0; k < kSlots; k++) {
+            if constexpr (VEC * sizeof(T) == 16) {
+                u32x4 r = {0u, 0u, 0u, 0u};
+                if (src[k]) r = ld_global16(src[k] + t0);
+                reg[k][0] = r.x;
+                reg[k][1] = r.y;
+                reg[k][2] = r.z;
+                reg[k][3] = r.w;
+            } else {
+                T v = src[k] ? src[k][t0] : T(0);
+                uint32_t tmp = 0;
+                __builtin_memcpy(&tmp, &v, sizeof(T));
+                reg[k][0] = tmp;
+            }
+        }
+    }
+
+    // Guarded loads of the ragged chunk that starts at t0 (t0 + KT > L).
+    __device__ __forceinline__ void fetch_tail(int64_t t0, int64_t L) {
+#pragma unroll
+        for (int k = 0; k < kSlots; k++) {
+            T v[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; e++)
+                v[e] = (src[k] && t0 + col[k] + e < L) ? src[k][t0 + e] : T(0);
+            uint32_t tmp[kWords] = {};
+            __builtin_memcpy(tmp, v, sizeof(v));
+#pragma unroll
+            for (int w = 0; w < kWords; w++) reg[k][w] = tmp[w];
+        }
+    }
+
+    __device__ __forceinline__ void fetch(int64_t t0, int64_t L) {
+        if (t0 + KT <= L) fetch_full(t0);
+        else fetch_tail(t0, L);
+    }
+
+    __device__ __forceinline__ void stash(char *smem) {
+#pragma unroll
+        for (int k = 0; k < kSlots; k++) {
+            if (dst[k] == ~0u) continue;
+            T v[VEC];
+            __builtin_memcpy(v, reg[k], sizeof(v));
+            if (f32[k]) {
+                float *d = reinterpret_cast<float *>(smem + dst[k]);
+                if constexpr (VEC % 4 == 0) {
+#pragma unroll
+                    for (int e = 0; e < VEC; e += 4)
+                        *reinterpret_cast<float4 *>(d + e) =
+                            make_float4(to_f32<T>(v[e]), to_f32<T>(v[e + 1]), to_f32<T>(v[e + 2]),
+                                        to_f32<T>(v[e + 3]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; e++) d[e] = to_f32<T>(v[e]);
+                }
+            } else {
+                T *d = reinterpret_cast<T *>(smem + dst[k]);
+                if constexpr (VEC * sizeof(T) == 16) {
+                    Raw16 r;
+#pragma unroll
+                    for (int w = 0; w < 4; w++) r.w[w] = reg[k][w];
+                    *reinterpret_cast<Raw16 *>(d) = r;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; e++) d[e] = v[e];
+                }
+            }
+        }
+    }
+};
+
+// Writes a [16 rows][KT] tile of T from LDS to global rows (guarded for the
+// ragged tail and for rows past the last channel).
+template <typename T, int VEC, int KT, int NTHREADS>
+__device__ __forceinline__ void store_tile(T *__restrict__ base, int64_t row_stride,
+                                           int valid_rows, int64_t t0, int64_t L,
+                                           const T *tile, int tid) {
+    constexpr int kVecPerRow = KT / VEC;
+    constexpr int kVecs = 16 * kVecPerRow;
+#pragma unroll
+    for (int k = 0; k < (kVecs + NTHREADS - 1) / NTHREADS; k++) {
+        const int slot = tid + k * NTHREADS;
+        if (slot < kVecs) {
+            const int row = slot / kVecPerRow;
+            const int c = (slot % kVecPerRow) * VEC;
+            if (row < valid_rows) {
+                T *dst = base + row * row_stride + t0 + c;
+                const T *s = tile + row * KT + c;
+                if (VEC * sizeof(T) == 16 && t0 + c + VEC <= L) {
+                    st_global16(dst, *reinterpret_cast<const u32x4 *>(s));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; e++)
+                        if (t0 + c + e < L) dst[e] = s[e];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace ssk
