@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 1
+#define SS_ABI_VERSION 2
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -78,8 +78,19 @@ int ss_abi_version(void);
 const char *ss_last_error(void);
 
 /*
+ * Bytes of the chunk checkpoints ss_fwd can save for ss_bwd: the state
+ * entering every 32-step chunk, f32 (batch, dim, ceil(seqlen / 32), dstate).
+ * 0 for empty or unsupported shapes.
+ */
+size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
+
+/*
  * Forward scan.  Writes out (batch, dim, seqlen) and, when last_state is
- * non-NULL, the final state h_{seqlen-1} (h0 when seqlen == 0).
+ * non-NULL, the final state h_{seqlen-1} (h0 when seqlen == 0).  When ckpt
+ * is non-NULL (ss_ckpt_size() bytes, 16-byte aligned) it also saves the
+ * chunk checkpoints, which a later ss_bwd with the same inputs can take
+ * instead of recomputing them (the usual save-for-backward of a training
+ * step).
  *   dstate            must be 16 (SS_EUNSUPPORTED otherwise).
  *   io_dtype          SS_F32 or SS_BF16: dtype of u, delta, B, C, z, out.
  *   D, z, delta_bias, h0, last_state may be NULL.
@@ -91,7 +102,7 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                  const void *u, const void *delta, const float *A, const void *B,
                  const void *C, const float *D, const void *z, const float *delta_bias,
                  int delta_softplus, const float *h0, void *out, float *last_state,
-                 void *stream);
+                 float *ckpt, void *stream);
 
 /* Bytes of device workspace ss_bwd needs for this shape (0 for empty shapes). */
 size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
@@ -110,6 +121,8 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
  *   dz                 NULL iff z is NULL.
  *   ddelta_bias        NULL iff delta_bias is NULL; summed over batch and time.
  *   dh0                optional (may be non-NULL with h0 NULL: gradient at a zero start).
+ *   ckpt               checkpoints saved by ss_fwd for exactly these inputs, or
+ *                      NULL (then they are recomputed in the workspace).
  *   workspace          device memory of at least ss_bwd_workspace_size() bytes,
  *                      16-byte aligned, owned by the caller, not read before written.
  * Every sum over batch, time or channels runs in a fixed order, with no
@@ -120,8 +133,8 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                  const void *C, const float *D, const void *z, const float *delta_bias,
                  int delta_softplus, const float *h0, const void *dout, const float *dlast,
                  void *du, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
-                 float *ddelta_bias, float *dh0, void *workspace, size_t workspace_bytes,
-                 void *stream);
+                 float *ddelta_bias, float *dh0, const float *ckpt, void *workspace,
+                 size_t workspace_bytes, void *stream);
 
 /*
  * One-token state update (decode): advances `state` (batch, dim, dstate,

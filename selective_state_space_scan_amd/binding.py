@@ -50,11 +50,13 @@ def load() -> ctypes.CDLL:
             lib.ss_last_error.restype = ctypes.c_char_p
             lib.ss_last_error.argtypes = []
             lib.ss_fwd.restype = c_int
-            lib.ss_fwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 4)
+            lib.ss_fwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 5)
+            lib.ss_ckpt_size.restype = sz
+            lib.ss_ckpt_size.argtypes = [i64] * 4
             lib.ss_bwd_workspace_size.restype = sz
             lib.ss_bwd_workspace_size.argtypes = [i64] * 4 + [c_int]
             lib.ss_bwd.restype = c_int
-            lib.ss_bwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 13
+            lib.ss_bwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 14
                                    + [sz, vp])
             lib.ss_state_update.restype = c_int
             lib.ss_state_update.argtypes = ([i64] * 3 + [c_int] + [vp] * 9 + [c_int]
@@ -108,12 +110,26 @@ def abi_version() -> int:
     return load().ss_abi_version()
 
 
+def ss_ckpt_size(batch, dim, dstate, seqlen) -> int:
+    """Bytes of the chunk checkpoints ss_fwd can save for ss_bwd."""
+    return int(load().ss_ckpt_size(batch, dim, dstate, seqlen))
+
+
+def ss_ckpt_empty(u, dstate=16):
+    """Allocate a checkpoint buffer for inputs shaped like ``u``."""
+    batch, dim, seqlen = u.shape
+    n = ss_ckpt_size(batch, dim, dstate, seqlen) // 4
+    return torch.empty(max(n, 1), dtype=torch.float32, device=u.device)
+
+
 def ss_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-           h0=None, out=None, last_state=None, return_last_state=False):
+           h0=None, out=None, last_state=None, return_last_state=False, ckpt=None):
     """Forward scan; returns ``out`` or ``(out, last_state)``.
 
     u, delta, z: (batch, dim, L); B, C: (batch, dstate, L) in float32 or bfloat16;
     A: (dim, dstate), D, delta_bias: (dim,), h0: (batch, dim, dstate) float32.
+    ckpt: optional float32 buffer (see ss_ckpt_empty) that receives the chunk
+    checkpoints for a later ss_bwd.
     """
     lib = load()
     batch, dim, seqlen = u.shape
@@ -127,7 +143,7 @@ def ss_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=Fa
     _check(lib.ss_fwd(batch, dim, dstate, seqlen, io, _ptr(u), _ptr(delta), _f32(A, "A"),
                       _ptr(B), _ptr(C), _f32(D, "D"), _ptr(z), _f32(delta_bias, "delta_bias"),
                       int(bool(delta_softplus)), _f32(h0, "h0"), _ptr(out),
-                      _f32(last_state, "last_state"), _stream()))
+                      _f32(last_state, "last_state"), _f32(ckpt, "ckpt"), _stream()))
     return (out, last_state) if (return_last_state or last_state is not None) else out
 
 
@@ -136,11 +152,12 @@ def ss_bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SS_F32) -> int:
 
 
 def ss_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-           dout=None, h0=None, dlast=None, want_dh0=False, workspace=None):
+           dout=None, h0=None, dlast=None, want_dh0=False, workspace=None, ckpt=None):
     """Backward of ``sum(dout * out) + sum(dlast * last_state)``.
 
     Returns a dict with du, ddelta, dA, dB, dC and, for the optional inputs
     given, dD, dz, ddelta_bias, plus dh0 when ``want_dh0`` or h0 is given.
+    ckpt: checkpoints saved by ss_fwd for the same inputs (skips recomputing them).
     """
     lib = load()
     batch, dim, seqlen = u.shape
@@ -167,7 +184,8 @@ def ss_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=Fa
                       int(bool(delta_softplus)), _f32(h0, "h0"), _ptr(dout), _f32(dlast, "dlast"),
                       _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                       _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
-                      _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")), _ptr(workspace),
+                      _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")), _f32(ckpt, "ckpt"),
+                      _ptr(workspace),
                       workspace.numel(), _stream()))
     return g
 

@@ -115,7 +115,7 @@ const char *ss_last_error(void) { return g_err; }
 ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
                  const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int delta_softplus,
-                 const float *h0, void *out, float *last_state, void *stream) {
+                 const float *h0, void *out, float *last_state, float *ckpt, void *stream) {
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
     const bool has_rows = batch > 0 && dim > 0;
@@ -135,6 +135,7 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     c.opt(delta_bias, "delta_bias");
     c.opt(h0, "h0");
     c.opt(last_state, "last_state");
+    c.opt(ckpt, "ckpt");
     if (c.st != SS_OK) return c.st;
     if (h0 && last_state && h0 == last_state)
         return fail(SS_EINVAL, "last_state must not alias h0");
@@ -142,10 +143,16 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.batch = batch; p.dim = dim; p.seqlen = seqlen;
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
-    p.out = out; p.last_state = last_state;
+    p.out = out; p.last_state = last_state; p.ckpt = ckpt;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
                          "ss_fwd launch");
+}
+
+size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+    if (check_dims(batch, dim, dstate, seqlen, SS_F32, true) != SS_OK) return 0;
+    const int64_t nck = (seqlen + ssk::kCkptSpacing - 1) / ssk::kCkptSpacing;
+    return size_t(batch) * size_t(dim) * size_t(nck) * 16 * sizeof(float);
 }
 
 size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
@@ -159,7 +166,8 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                  const float *D, const void *z, const float *delta_bias, int delta_softplus,
                  const float *h0, const void *dout, const float *dlast, void *du, void *ddelta,
                  float *dA, void *dB, void *dC, float *dD, void *dz, float *ddelta_bias,
-                 float *dh0, void *workspace, size_t workspace_bytes, void *stream) {
+                 float *dh0, const float *ckpt, void *workspace, size_t workspace_bytes,
+                 void *stream) {
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
     const bool has_rows = batch > 0 && dim > 0;
@@ -181,6 +189,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     c.opt(D, "D"); c.opt(z, "z"); c.opt(delta_bias, "delta_bias"); c.opt(h0, "h0");
     c.opt(dlast, "dlast"); c.opt(dD, "dD"); c.opt(dz, "dz"); c.opt(ddelta_bias, "ddelta_bias");
     c.opt(dh0, "dh0");
+    c.opt(ckpt, "ckpt");
     c.pair(dD, D, "dD", "D");
     c.pair(dz, z, "dz", "z");
     c.pair(ddelta_bias, delta_bias, "ddelta_bias", "delta_bias");
@@ -198,7 +207,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.dout = dout; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB;
-    p.dC = dC; p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0;
+    p.dC = dC; p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0; p.ckpt = ckpt;
     p.workspace = workspace;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),

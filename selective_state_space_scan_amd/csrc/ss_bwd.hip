@@ -44,7 +44,7 @@ namespace ssk {
 namespace {
 
 constexpr int kRows = 16;
-constexpr int kC = 32;          // checkpoint spacing = reverse-pass chunk length
+constexpr int kC = kCkptSpacing;  // checkpoint spacing = reverse-pass chunk length
 constexpr int kThreads = 256;
 constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
 constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row
@@ -525,15 +525,18 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
 template <typename T>
 hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
     Workspace ws = carve(p.workspace, p.batch, p.dim, p.seqlen, nullptr);
+    if (p.ckpt) ws.ckpt = const_cast<float *>(p.ckpt);  // saved by the forward: read only
     if (p.batch > 0 && p.dim > 0) {
         dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch));
         constexpr int kVec = 16 / sizeof(T);
         const bool vec = (p.seqlen * int64_t(sizeof(T))) % 16 == 0;
-        if (vec)
-            hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
-        else
-            hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
-        profile_mark(stream);
+        if (!p.ckpt) {
+            if (vec)
+                hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
+            else
+                hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
+            profile_mark(stream);
+        }
         if (vec)
             hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
         else

@@ -118,6 +118,8 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
     }
     __syncthreads();
 
+    const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
+    float *ck = (p.ckpt && row_ok) ? p.ckpt + (b * Dm + d) * nck * kN + n : nullptr;
     float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
     T *gy = static_cast<T *>(p.out) + (b * Dm + d0) * L;
     for (int64_t c = 0; c < nchunks; c++) {
@@ -154,6 +156,10 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
         };
 #pragma unroll
         for (int s = 0; s < kT / 16; s++) {
+            if (ck && (16 * s) % kCkptSpacing == 0) {   // state entering a checkpoint chunk
+                const int64_t k = (t0 + 16 * s) / kCkptSpacing;
+                if (k < nck) ck[k * kN] = h;
+            }
             float4 bq[4], cq[4];
 #pragma unroll
             for (int q = 0; q < 4; q++) {

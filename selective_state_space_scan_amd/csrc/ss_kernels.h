@@ -21,9 +21,13 @@ struct ScanParams {
     const float *h0;
 };
 
+// chunk length of the checkpoints saved by the forward for the backward
+constexpr int kCkptSpacing = 32;
+
 struct FwdParams : ScanParams {
     void *out;
     float *last_state;
+    float *ckpt;  // (batch, dim, ceil(L / 32), 16) or nullptr
 };
 
 struct BwdParams : ScanParams {
@@ -36,6 +40,7 @@ struct BwdParams : ScanParams {
     void *dz;
     float *dbias;
     float *dh0;
+    const float *ckpt;  // checkpoints saved by the forward, or nullptr
     void *workspace;
 };
 

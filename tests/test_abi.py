@@ -38,13 +38,26 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 1
+    assert lib.ss_abi_version() == 2
+
+
+def test_ckpt_size(lib):
+    lib.ss_ckpt_size.restype = ctypes.c_size_t
+    lib.ss_ckpt_size.argtypes = [ctypes.c_int64] * 4
+    assert lib.ss_ckpt_size(2, 32, 16, 64) == 2 * 32 * 2 * 16 * 4
+    assert lib.ss_ckpt_size(2, 32, 16, 65) == 2 * 32 * 3 * 16 * 4
+    assert lib.ss_ckpt_size(2, 32, 16, 0) == 0
+    assert lib.ss_ckpt_size(2, 32, 8, 64) == 0
+
+
+def test_bwd_misaligned_ckpt(lib):
+    assert _bwd(lib, ckpt=MISALIGNED) == EINVAL and "ckpt" in _msg(lib)
 
 
 def _fwd(lib, batch=2, dim=32, dstate=16, seqlen=64, io=0, u=FAKE, delta=FAKE, A=FAKE, B=FAKE,
-         C=FAKE, D=None, z=None, bias=None, h0=None, out=FAKE, last=None):
+         C=FAKE, D=None, z=None, bias=None, h0=None, out=FAKE, last=None, ckpt=None):
     return lib.ss_fwd(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, bias, 1, h0, out,
-                      last, None)
+                      last, ckpt, None)
 
 
 def _msg(lib):
@@ -57,7 +70,7 @@ def test_fwd_null_required_pointer(lib, arg):
     assert arg in _msg(lib)
 
 
-@pytest.mark.parametrize("arg", ["u", "A", "D", "z", "bias", "h0", "last"])
+@pytest.mark.parametrize("arg", ["u", "A", "D", "z", "bias", "h0", "last", "ckpt"])
 def test_fwd_misaligned_pointer(lib, arg):
     assert _fwd(lib, **{arg: MISALIGNED}) == EINVAL
     name = {"bias": "delta_bias", "last": "last_state"}.get(arg, arg)
@@ -88,7 +101,7 @@ def test_fwd_last_state_must_not_alias_h0(lib):
 
 
 def _bwd(lib, batch=2, dim=32, dstate=16, seqlen=64, D=None, z=None, bias=None, dD=None, dz=None,
-         dbias=None, ws=FAKE, ws_bytes=None, **over):
+         dbias=None, ws=FAKE, ws_bytes=None, ckpt=None, **over):
     args = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, dout=FAKE, du=FAKE, ddelta=FAKE,
                 dA=FAKE, dB=FAKE, dC=FAKE)
     args.update(over)
@@ -97,7 +110,7 @@ def _bwd(lib, batch=2, dim=32, dstate=16, seqlen=64, D=None, z=None, bias=None, 
     return lib.ss_bwd(batch, dim, dstate, seqlen, 0, args["u"], args["delta"], args["A"],
                       args["B"], args["C"], D, z, bias, 1, None, args["dout"], None, args["du"],
                       args["ddelta"], args["dA"], args["dB"], args["dC"], dD, dz, dbias, None,
-                      ws, ws_bytes, None)
+                      ckpt, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("arg", ["u", "delta", "dout", "du", "ddelta", "dA", "dB", "dC", "A"])

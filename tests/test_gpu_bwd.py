@@ -79,6 +79,30 @@ def test_bwd_small_elementwise(batch, dim, L, io, flags):
             assert_close(to_host(g[k]), ref[k], tol, f"{k} state={use_state}")
 
 
+@pytest.mark.parametrize("batch,dim,L,io", [(2, 40, 100, "f32"), (1, 33, 70, "bf16"),
+                                             (2, 16, 17, "f32")])
+def test_bwd_with_forward_checkpoints_is_bit_identical(batch, dim, L, io):
+    """Checkpoints saved by the forward give the same bits as recomputing them."""
+    require_gpu()
+    w = ssin.custom("bwd", batch, dim, 16, L, io, seed=L + dim)
+    arr = ssin.make(w)
+    d = dev_inputs(arr)
+    h0 = torch.randn(batch, dim, 16, device=DEV)
+    ck = binding.ss_ckpt_empty(d["u"])
+    binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"],
+                   True, h0=h0, ckpt=ck)
+    g1 = binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                        d["delta_bias"], True, d["dout"], h0=h0)
+    g2 = binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                        d["delta_bias"], True, d["dout"], h0=h0, ckpt=ck)
+    torch.cuda.synchronize()
+    for k in g1:
+        a, b2 = g1[k], g2[k]
+        if a.dtype == torch.bfloat16:
+            a, b2 = a.view(torch.int16), b2.view(torch.int16)
+        assert torch.equal(a, b2), k
+
+
 def test_bwd_zero_length_passes_dlast_through():
     require_gpu()
     w = ssin.custom("bwd", 2, 32, 16, 0, "f32", seed=4)
