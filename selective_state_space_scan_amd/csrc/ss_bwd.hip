@@ -24,14 +24,14 @@
 //      decay and state in registers, then walks the steps backward.
 //        - sums over the 16 states (pre-gate output, the two sums behind du
 //          and ddelta) go through padded per-wave LDS transposes;
-//        - sums over channels (dB, dC) run on the matrix cores: with the
-//          lane layout (row = lane / 16, state = lane % 16) a 16x16x4 f32
-//          MFMA contracts exactly over the 4 rows of a wavefront, taking the
-//          per-lane adjoint (or state) as A and the row's delta*u (or dy),
-//          placed in the column of the current step, as B -- so one MFMA per
-//          step both multiplies and adds the 4 rows, and 16 steps fill one
-//          16 x 16 accumulator.  The 4 wavefronts' partial sums are then
-//          added through LDS and written as one partial per 16 channels;
+//        - sums over channels (dB, dC): the 4 rows of a wavefront are added
+//          in registers with the gfx950 cross-row lane swaps
+//          (v_permlane32_swap, then v_permlane16_swap), two quantities at two
+//          steps per pair of swaps, so each lane ends with one finished
+//          4-row sum; the 4 wavefronts' sums are then added through LDS and
+//          written as one partial per 16 channels.  (f32 MFMAs could do the
+//          4-row contraction too, but they do not overlap with VALU work on
+//          this chip and would use 1/16 of each instruction here);
 //   3. fold: adds the dB/dC partials over channel groups in ascending group
 //      order and the dA/dD/dbias partials over the batch in ascending batch
 //      order.
@@ -48,8 +48,6 @@ constexpr int kC = kCkptSpacing;  // checkpoint spacing = reverse-pass chunk len
 constexpr int kThreads = 256;
 constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
 constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row
-
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Workspace carve-up (all f32, 256-byte aligned pieces).
 struct Workspace {
@@ -101,6 +99,35 @@ __device__ __forceinline__ float row_sum16(float v) {
 __device__ __forceinline__ float row_ror8(float v) {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+}
+
+// Sums over the 4 DPP rows of a wavefront (rows = lanes 16 k .. 16 k + 15).
+// v_permlane32_swap trades lanes 32-63 of its first operand with lanes 0-31
+// of its second; v_permlane16_swap trades the odd rows of its first operand
+// with the even rows of its second.
+//
+// Sum of the two results of a lane swap.  The elements are copied out by
+// value first: clang 22 takes __builtin_bit_cast of a vector element from the
+// vector's first element.
+template <typename V>
+__device__ __forceinline__ float swap_sum(const V &r) {
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// rows_pair_sum(x, y) = [x0 + x2, x1 + x3, y0 + y2, y1 + y3]   (by row)
+__device__ __forceinline__ float rows_pair_sum(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, y), false, false);
+    return swap_sum(r);
+}
+// rows_quad_sum(p, q) with p, q from rows_pair_sum =
+//   [p0 + p1, q0 + q1, p2 + p3, q2 + q3]: row 0 holds the full 4-row sum of
+//   p's x, row 1 that of q's x, rows 2 and 3 those of p's and q's y.
+__device__ __forceinline__ float rows_quad_sum(float p, float q) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, p),
+                                                    __builtin_bit_cast(unsigned, q), false, false);
+    return swap_sum(r);
 }
 
 // fixed pairwise sum of 16 values
@@ -232,10 +259,13 @@ struct RevSmem {
     static constexpr uint32_t kDu = kUnEnd;                          // output tiles
     static constexpr uint32_t kDd = kDu + kRows * kC * sizeof(T);
     static constexpr uint32_t kDz = kDd + kRows * kC * sizeof(T);
-    // channel sums: [block 2][wave 4][quantity 2][step 16][state 16 + 4 pad]
+    // 4-row channel sums: [wave 4][step 32][quantity 2 x state 16 + 2 pad].
+    // The step pitch of 34 floats makes the summing threads' reads (8 steps
+    // 4 apart x 8 states per wavefront) hit 64 distinct banks.
     static constexpr uint32_t kCh = kDz + kRows * kC * sizeof(T);
-    static constexpr int kChRow = 20;
-    static constexpr uint32_t kSize = kCh + 2 * 4 * 2 * 16 * kChRow * 4;
+    static constexpr int kChStep = 34;
+    static constexpr int kChWave = kC * kChStep;
+    static constexpr uint32_t kSize = kCh + 4 * kChWave * 4;
 };
 
 template <typename T, int VEC>
@@ -377,24 +407,31 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
         }
 
         // ---- backward over the chunk, 16 steps at a time ----
+        // this lane's slot of the channel sums: lane (rw, n) receives state n
+        // of quantity rw / 2 (0: dB, 1: dC) at the odd (rw & 1) step of a pair
+        float *chw = chan + wave * SM::kChWave + (rw & 1) * SM::kChStep + (rw >> 1) * kN + n;
 #pragma unroll
         for (int s = 1; s >= 0; s--) {
-            floatx4 accB = {0.0f, 0.0f, 0.0f, 0.0f};
-            floatx4 accC = {0.0f, 0.0f, 0.0f, 0.0f};
             float sumA = 0.0f, sumB = 0.0f;
 #pragma unroll
             for (int hh = 1; hh >= 0; hh--) {
                 float qa[8], qb[8];
+                float xo = 0.0f, yo = 0.0f;  // dB / dC terms of the odd step of a pair
 #pragma unroll
                 for (int jj = 7; jj >= 0; jj--) {
                     const int j = 8 * hh + jj;
                     const int t = 16 * s + j;
-                    float dyj, dj;
+                    float dyj, dj, dluj;
                     switch (j) {
-#define SS_BC(J) case J: dyj = row_bcast<J>(dy[s]); dj = row_bcast<J>(dl[s]); break;
+#define SS_BC(J)                   \
+    case J:                        \
+        dyj = row_bcast<J>(dy[s]);   \
+        dj = row_bcast<J>(dl[s]);    \
+        dluj = row_bcast<J>(dlu[s]); \
+        break;
                         SS_BC(0) SS_BC(1) SS_BC(2) SS_BC(3) SS_BC(4) SS_BC(5) SS_BC(6) SS_BC(7)
                         SS_BC(8) SS_BC(9) SS_BC(10) SS_BC(11) SS_BC(12) SS_BC(13) SS_BC(14)
-                        default: dyj = row_bcast<15>(dy[s]); dj = row_bcast<15>(dl[s]); break;
+                        SS_BC(15)
 #undef SS_BC
                     }
                     g = __builtin_fmaf(sC[n][t], dyj, g);                 // g_t
@@ -403,10 +440,17 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
                     dA_acc = __builtin_fmaf(gp, dj, dA_acc);
                     qa[jj] = aval * gp;
                     qb[jj] = g * sB[n][t];
-                    // channel sums on the matrix core: column j of the 16 x 16 result
-                    const bool mine = (n == j);
-                    accB = __builtin_amdgcn_mfma_f32_16x16x4f32(g, mine ? dlu[s] : 0.0f, accB, 0, 0, 0);
-                    accC = __builtin_amdgcn_mfma_f32_16x16x4f32(hs[t], mine ? dy[s] : 0.0f, accC, 0, 0, 0);
+                    // per-lane terms of the channel sums dB[n,t] and dC[n,t]
+                    const float xv = g * dluj;
+                    const float yv = hs[t] * dyj;
+                    if (jj & 1) {
+                        xo = xv;
+                        yo = yv;
+                    } else {
+                        const float pe = rows_pair_sum(xv, yv);
+                        const float po = rows_pair_sum(xo, yo);
+                        chw[(16 * s + j) * SM::kChStep] = rows_quad_sum(pe, po);
+                    }
                     g = ab[t] * g;                                        // carried to t - 1
                 }
                 // sums over the 16 states: columns 0-7 carry A*g*abar*h, 8-15 g*B
@@ -433,33 +477,28 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
                 sDd[r][col] = from_f32<T>(dd);
                 if (t0 + col < L) dbias_acc += dd;
             }
-            // this wave's channel sums (4 rows): lane (rw, j) holds states 4 rw .. 4 rw + 3 of step j
-            float *cb = chan + ((s * 4 + wave) * 2) * 16 * SM::kChRow;
-            *reinterpret_cast<float4 *>(&cb[n * SM::kChRow + 4 * rw]) =
-                make_float4(accB[0], accB[1], accB[2], accB[3]);
-            *reinterpret_cast<float4 *>(&cb[16 * SM::kChRow + n * SM::kChRow + 4 * rw]) =
-                make_float4(accC[0], accC[1], accC[2], accC[3]);
         }
         __syncthreads();
 
-        // add the 4 wavefronts' channel sums: thread (state sn, step sj)
+        // add the 4 wavefronts' channel sums: thread (quantity cq, state cn,
+        // steps 4 ct .. 4 ct + 3), wavefronts in ascending order
         {
-            const int sn = tid >> 4, sj = tid & 15;
+            const int cq = tid >> 7, cn = (tid >> 3) & 15, ct = tid & 7;
+            float acc[4];
 #pragma unroll
-            for (int s = 0; s < 2; s++) {
-                float accb = 0.0f, accc = 0.0f;
+            for (int e = 0; e < 4; e++) {
+                const float *cs = chan + (4 * ct + e) * SM::kChStep + cq * kN + cn;
+                acc[e] = cs[0];
 #pragma unroll
-                for (int w = 0; w < 4; w++) {
-                    const float *cb = chan + ((s * 4 + w) * 2) * 16 * SM::kChRow;
-                    accb += cb[sj * SM::kChRow + sn];
-                    accc += cb[16 * SM::kChRow + sj * SM::kChRow + sn];
-                }
-                const int64_t t = t0 + 16 * s + sj;
-                if (t < L) {
-                    const int64_t o = ((b * groups + group) * kN + sn) * L + t;
-                    ws.dBp[o] = accb;
-                    ws.dCp[o] = accc;
-                }
+                for (int w = 1; w < 4; w++) acc[e] += cs[w * SM::kChWave];
+            }
+            float *dst = (cq ? ws.dCp : ws.dBp) + ((b * groups + group) * kN + cn) * L + t0 + 4 * ct;
+            if ((L & 3) == 0 && t0 + 4 * ct + 4 <= L) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    if (t0 + 4 * ct + e < L) dst[e] = acc[e];
             }
         }
         T *du_g = static_cast<T *>(p.du) + rowbase;

@@ -61,12 +61,13 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
 
 // Broadcast lane LANE of each 16-lane DPP row to the whole row
 // (row_newbcast; one VALU op, or folded into the consuming instruction).
+// The source lane always exists, so no "old" value is needed (bound_ctrl
+// set lets the compiler fold the broadcast into a VOP2 consumer).
 template <int LANE>
 __device__ __forceinline__ float row_bcast(float v) {
     static_assert(LANE >= 0 && LANE < 16, "lane within a DPP row");
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + LANE, 0xf,
-                                           0xf, false));
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + LANE, 0xf, 0xf, true));
 }
 
 }  // namespace ssk
