@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 2
+#define SS_ABI_VERSION 3
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -78,8 +78,8 @@ int ss_abi_version(void);
 const char *ss_last_error(void);
 
 /*
- * Bytes of the chunk checkpoints ss_fwd can save for ss_bwd: the state
- * entering every 32-step chunk, f32 (batch, dim, ceil(seqlen / 32), dstate).
+ * Bytes of the checkpoints ss_fwd can save for ss_bwd: the state entering
+ * every 16-step block, f32 (batch, dim, ceil(seqlen / 16), dstate).
  * 0 for empty or unsupported shapes.
  */
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);

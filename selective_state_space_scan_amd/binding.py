@@ -15,6 +15,8 @@ import threading
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
+# SS_ABI_VERSION of include/ss.h that these signatures follow
+ABI_VERSION = 3
 _lock = threading.Lock()
 _lib = None
 
@@ -47,6 +49,10 @@ def load() -> ctypes.CDLL:
             i64, vp, c_int, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
             lib.ss_abi_version.restype = c_int
             lib.ss_abi_version.argtypes = []
+            if lib.ss_abi_version() != ABI_VERSION:
+                raise RuntimeError(
+                    f"{_LIB_PATH} implements ABI {lib.ss_abi_version()}, this binding "
+                    f"ABI {ABI_VERSION}: rebuild it with `python -m selective_state_space_scan_amd.build`")
             lib.ss_last_error.restype = ctypes.c_char_p
             lib.ss_last_error.argtypes = []
             lib.ss_fwd.restype = c_int

@@ -44,7 +44,13 @@ namespace ssk {
 namespace {
 
 constexpr int kRows = 16;
-constexpr int kC = kCkptSpacing;  // checkpoint spacing = reverse-pass chunk length
+constexpr int kCk = kCkptSpacing;  // checkpoint spacing = reverse-pass recompute block
+#ifndef SS_REV_CHUNK
+#define SS_REV_CHUNK 32
+#endif
+constexpr int kC = SS_REV_CHUNK;   // reverse-pass staging chunk: kNB recompute blocks
+constexpr int kNB = kC / kCk;
+static_assert(kCk == 16 && (kNB == 1 || kNB == 2), "a staging chunk holds one or two 16-step blocks");
 constexpr int kThreads = 256;
 constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
 constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row
@@ -63,7 +69,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 
 __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L,
                                            size_t *total) {
-    const int64_t nck = (L + kC - 1) / kC;
+    const int64_t nck = (L + kCk - 1) / kCk;
     const int64_t groups = (dim + kRows - 1) / kRows;
     size_t off = 0;
     Workspace w;
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
     const float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float h = (row_ok && p.h0) ? p.h0[(b * Dm + d) * kN + n] : 0.0f;
-    const int64_t nck = (L + kC - 1) / kC;
+    const int64_t nck = (L + kCk - 1) / kCk;
     float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
 
     const T *gB = static_cast<const T *>(p.B) + b * kN * L;
@@ -212,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
         }
 #pragma unroll
         for (int s = 0; s < kT1 / 16; s++) {
-            if (s % (kC / 16) == 0) {
-                const int64_t k = (t0 + 16 * s) / kC;
+            if (s % (kCk / 16) == 0) {
+                const int64_t k = (t0 + 16 * s) / kCk;
                 if (row_ok && k < nck) ck[k * kN] = h;
             }
 #pragma unroll
@@ -256,20 +262,18 @@ struct RevSmem {
     static constexpr uint32_t kTr = kUn;
     static constexpr uint32_t kTrEnd = kTr + 4 * 4 * kYRow * 4;
     static constexpr uint32_t kUnEnd = kRawEnd > kTrEnd ? kRawEnd : kTrEnd;
-    static constexpr uint32_t kDu = kUnEnd;                          // output tiles
-    static constexpr uint32_t kDd = kDu + kRows * kC * sizeof(T);
-    static constexpr uint32_t kDz = kDd + kRows * kC * sizeof(T);
-    // 4-row channel sums: [wave 4][step 32][quantity 2 x state 16 + 2 pad].
-    // The step pitch of 34 floats makes the summing threads' reads (8 steps
-    // 4 apart x 8 states per wavefront) hit 64 distinct banks.
-    static constexpr uint32_t kCh = kDz + kRows * kC * sizeof(T);
-    static constexpr int kChStep = 34;
+    // 4-row channel sums: [wave 4][step kC][quantity 2 x state 16 + pad].
+    // The summing threads of a wavefront read 8 steps kC / 8 apart x 8
+    // states; a step pitch P with (kC / 8) P = 8 (mod 64) puts them in 64
+    // distinct banks.
+    static constexpr uint32_t kCh = kUnEnd;
+    static constexpr int kChStep = kC == 32 ? 34 : 36;
     static constexpr int kChWave = kC * kChStep;
     static constexpr uint32_t kSize = kCh + 4 * kChWave * 4;
 };
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
+__global__ __launch_bounds__(kThreads, kC == 16 ? 4 : 3) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
     using SM = RevSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
     float(*sB)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kB);
@@ -278,9 +282,6 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
     T(*sDl)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDl);
     T(*sZ)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kZ);
     T(*sG)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kG);
-    T(*sDu)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDu);
-    T(*sDd)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDd);
-    T(*sDz)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDz);
     float *chan = reinterpret_cast<float *>(smem + SM::kCh);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -296,8 +297,11 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
     const float a2 = aval * kLog2e;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
-    const int64_t nck = (L + kC - 1) / kC;
+    const int64_t nck = (L + kCk - 1) / kCk;   // checkpoints (16-step blocks)
+    const int64_t nch = (L + kC - 1) / kC;     // 32-step staging chunks
     const float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
+    // state entering block k; a block past the end (only padding steps) has none
+    auto ckpt_at = [&](int64_t k) { return (row_ok && k < nck) ? ck[k * kN] : 0.0f; };
 
     float g = (row_ok && p.dlast) ? p.dlast[(b * Dm + d) * kN + n] : 0.0f;
     float dA_acc = 0.0f;     // this lane's state entry, summed over time
@@ -311,6 +315,12 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
     const T *gdl = static_cast<const T *>(p.delta) + rowbase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + rowbase : nullptr;
     const T *gdo = static_cast<const T *>(p.dout) + rowbase;
+    // this lane's row of the element-wise gradients; a row's 16 lanes store
+    // 16 consecutive elements of a 16-step block
+    const int64_t myrow = (b * Dm + (row_ok ? d : d0)) * L;
+    T *du_row = static_cast<T *>(p.du) + myrow;
+    T *dd_row = static_cast<T *>(p.ddelta) + myrow;
+    T *dz_row = has_z ? static_cast<T *>(p.dz) + myrow : nullptr;
     ChunkStager<T, VEC, kC, 6, kThreads> st;
     st.init(
         [&](int i) -> TileSrc<T> {
@@ -325,22 +335,37 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
         },
         tid);
 
-    if (nck > 0) {
-        st.fetch((nck - 1) * kC, L);
+    if (nch > 0) {
+        st.fetch((nch - 1) * kC, L);
         st.stash(smem);
     }
     __syncthreads();
 
     float *tr = reinterpret_cast<float *>(smem + SM::kTr) + wave * 4 * kYRow + rw * kYRow;
-    for (int64_t c = nck - 1; c >= 0; c--) {
+    // this lane's slot of the channel sums: lane (rw, n) receives state n of
+    // quantity rw / 2 (0: dB, 1: dC) at the odd (rw & 1) step of a pair
+    float *chw = chan + wave * SM::kChWave + (rw & 1) * SM::kChStep + (rw >> 1) * kN + n;
+    // The checkpoints of the next chunk are loaded one chunk ahead and before
+    // the prefetch: loads retire in order, so a load issued after the
+    // prefetch would make its use wait for the prefetch.
+    float hn[kNB];
+#pragma unroll
+    for (int s = 0; s < kNB; s++) hn[s] = ckpt_at(kNB * (nch - 1) + s);
+    for (int64_t c = nch - 1; c >= 0; c--) {
         const int64_t t0 = c * kC;
-        if (c > 0) st.fetch(t0 - kC, L);
-        const float hstart = row_ok ? ck[c * kN] : 0.0f;
+        float hb[kNB];
+#pragma unroll
+        for (int s = 0; s < kNB; s++) hb[s] = hn[s];
+        if (c > 0) {
+#pragma unroll
+            for (int s = 0; s < kNB; s++) hn[s] = ckpt_at(kNB * (c - 1) + s);
+            st.fetch(t0 - kC, L);
+        }
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row
-        float dl[2], dlu[2], uu[2], sgd[2], dout[2], zz[2], dy[2];
+        float dl[kNB], dlu[kNB], uu[kNB], sgd[kNB], dout[kNB], zz[kNB];
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
+        for (int s = 0; s < kNB; s++) {
             const int col = 16 * s + n;
             const float raw = to_f32<T>(sDl[r][col]) + bias;
             float x = raw;
@@ -357,11 +382,14 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
         }
         __syncthreads();  // the transpose region aliases the raw tiles
 
-        // ---- forward over the chunk: decays and states in registers ----
-        float ab[kC], hs[kC];
-        float h = hstart;
+        // blocks last to first: recompute the block's 16 forward steps from
+        // its checkpoint (decays and states in registers), then walk them back
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
+        for (int s = kNB - 1; s >= 0; s--) {
+            const int col = 16 * s + n;
+            const float hstart = hb[s];
+            float ab[kCk], hs[kCk];
+            float h = hstart;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const float4 b4 = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
@@ -371,25 +399,25 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int t = 16 * s + 4 * q + e;
+                    const int j = 4 * q + e;
                     float dj, duj;
-                    switch (4 * q + e) {
+                    switch (j) {
 #define SS_BC(J) case J: dj = row_bcast<J>(dl[s]); duj = row_bcast<J>(dlu[s]); break;
                         SS_BC(0) SS_BC(1) SS_BC(2) SS_BC(3) SS_BC(4) SS_BC(5) SS_BC(6) SS_BC(7)
                         SS_BC(8) SS_BC(9) SS_BC(10) SS_BC(11) SS_BC(12) SS_BC(13) SS_BC(14)
                         default: dj = row_bcast<15>(dl[s]); duj = row_bcast<15>(dlu[s]); break;
 #undef SS_BC
                     }
-                    ab[t] = exp2_hw(dj * a2);
-                    h = __builtin_fmaf(ab[t], h, duj * bb[e]);
-                    hs[t] = h;
+                    ab[j] = exp2_hw(dj * a2);
+                    h = __builtin_fmaf(ab[j], h, duj * bb[e]);
+                    hs[j] = h;
                     v[e] = cc[e] * h;
                 }
                 if (has_z)
                     *reinterpret_cast<float4 *>(&tr[n * kYN + 4 * q]) =
                         make_float4(v[0], v[1], v[2], v[3]);
             }
-            const int col = 16 * s + n;
+            float dy;
             if (has_z) {
                 __builtin_amdgcn_wave_barrier();
                 float part[16];
@@ -398,20 +426,16 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
                 __builtin_amdgcn_wave_barrier();
                 const float ypre = tree16(part) + dskip * uu[s];
                 const float sz = sigmoid_f32(zz[s]);
-                dy[s] = dout[s] * zz[s] * sz;
-                sDz[r][col] = from_f32<T>(dout[s] * ypre * sz * (1.0f + zz[s] * (1.0f - sz)));
+                dy = dout[s] * zz[s] * sz;
+                if (row_ok && t0 + col < L)
+                    st_global(dz_row + t0 + col,
+                              from_f32<T>(dout[s] * ypre * sz * (1.0f + zz[s] * (1.0f - sz))));
             } else {
-                dy[s] = dout[s];
+                dy = dout[s];
             }
-            if (t0 + col < L) dD_acc = __builtin_fmaf(dy[s], uu[s], dD_acc);
-        }
+            if (t0 + col < L) dD_acc = __builtin_fmaf(dy, uu[s], dD_acc);
 
-        // ---- backward over the chunk, 16 steps at a time ----
-        // this lane's slot of the channel sums: lane (rw, n) receives state n
-        // of quantity rw / 2 (0: dB, 1: dC) at the odd (rw & 1) step of a pair
-        float *chw = chan + wave * SM::kChWave + (rw & 1) * SM::kChStep + (rw >> 1) * kN + n;
-#pragma unroll
-        for (int s = 1; s >= 0; s--) {
+            // ---- backward over the block, 8 steps at a time ----
             float sumA = 0.0f, sumB = 0.0f;
 #pragma unroll
             for (int hh = 1; hh >= 0; hh--) {
@@ -425,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
                     switch (j) {
 #define SS_BC(J)                   \
     case J:                        \
-        dyj = row_bcast<J>(dy[s]);   \
+        dyj = row_bcast<J>(dy);      \
         dj = row_bcast<J>(dl[s]);    \
         dluj = row_bcast<J>(dlu[s]); \
         break;
@@ -435,23 +459,23 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
 #undef SS_BC
                     }
                     g = __builtin_fmaf(sC[n][t], dyj, g);                 // g_t
-                    const float hprev = t > 0 ? hs[t - 1] : hstart;
-                    const float gp = g * (ab[t] * hprev);
+                    const float hprev = j > 0 ? hs[j - 1] : hstart;
+                    const float gp = g * (ab[j] * hprev);
                     dA_acc = __builtin_fmaf(gp, dj, dA_acc);
                     qa[jj] = aval * gp;
                     qb[jj] = g * sB[n][t];
                     // per-lane terms of the channel sums dB[n,t] and dC[n,t]
                     const float xv = g * dluj;
-                    const float yv = hs[t] * dyj;
+                    const float yv = hs[j] * dyj;
                     if (jj & 1) {
                         xo = xv;
                         yo = yv;
                     } else {
                         const float pe = rows_pair_sum(xv, yv);
                         const float po = rows_pair_sum(xo, yo);
-                        chw[(16 * s + j) * SM::kChStep] = rows_quad_sum(pe, po);
+                        chw[t * SM::kChStep] = rows_quad_sum(pe, po);
                     }
-                    g = ab[t] * g;                                        // carried to t - 1
+                    g = ab[j] * g;                                        // carried to t - 1
                 }
                 // sums over the 16 states: columns 0-7 carry A*g*abar*h, 8-15 g*B
                 *reinterpret_cast<float4 *>(&tr[n * kYN + 0]) = make_float4(qa[0], qa[1], qa[2], qa[3]);
@@ -469,47 +493,45 @@ __global__ __launch_bounds__(kThreads, 3) void ss_bwd_reverse_kernel(BwdParams p
                 if (hh == 0 && n < 8) { sumA = sum; sumB = other; }
                 if (hh == 1 && n >= 8) { sumA = other; sumB = sum; }
             }
-            {
-                const int col = 16 * s + n;
-                const float du = __builtin_fmaf(dl[s], sumB, dskip * dy[s]);
-                const float dd = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];
-                sDu[r][col] = from_f32<T>(du);
-                sDd[r][col] = from_f32<T>(dd);
-                if (t0 + col < L) dbias_acc += dd;
+            const float du = __builtin_fmaf(dl[s], sumB, dskip * dy);
+            const float dd = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];
+            if (row_ok && t0 + col < L) {
+                st_global(du_row + t0 + col, from_f32<T>(du));
+                st_global(dd_row + t0 + col, from_f32<T>(dd));
             }
+            if (t0 + col < L) dbias_acc += dd;
         }
         __syncthreads();
 
         // add the 4 wavefronts' channel sums: thread (quantity cq, state cn,
-        // steps 4 ct .. 4 ct + 3), wavefronts in ascending order
+        // steps kE ct .. kE ct + kE - 1), wavefronts in ascending order
         {
+            constexpr int kE = kC / 8;
             const int cq = tid >> 7, cn = (tid >> 3) & 15, ct = tid & 7;
-            float acc[4];
+            float acc[kE];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const float *cs = chan + (4 * ct + e) * SM::kChStep + cq * kN + cn;
+            for (int e = 0; e < kE; e++) {
+                const float *cs = chan + (kE * ct + e) * SM::kChStep + cq * kN + cn;
                 acc[e] = cs[0];
 #pragma unroll
                 for (int w = 1; w < 4; w++) acc[e] += cs[w * SM::kChWave];
             }
-            float *dst = (cq ? ws.dCp : ws.dBp) + ((b * groups + group) * kN + cn) * L + t0 + 4 * ct;
-            if ((L & 3) == 0 && t0 + 4 * ct + 4 <= L) {
-                *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            float *dst = (cq ? ws.dCp : ws.dBp) + ((b * groups + group) * kN + cn) * L + t0 + kE * ct;
+            if ((L % kE) == 0 && t0 + kE * ct + kE <= L) {
+                if constexpr (kE == 4)
+                    *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                else
+                    *reinterpret_cast<float2 *>(dst) = make_float2(acc[0], acc[1]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; e++)
-                    if (t0 + 4 * ct + e < L) dst[e] = acc[e];
+                for (int e = 0; e < kE; e++)
+                    if (t0 + kE * ct + e < L) dst[e] = acc[e];
             }
         }
-        T *du_g = static_cast<T *>(p.du) + rowbase;
-        T *dd_g = static_cast<T *>(p.ddelta) + rowbase;
-        store_tile<T, VEC, kC, kThreads>(du_g, L, valid_rows, t0, L, &sDu[0][0], tid);
-        store_tile<T, VEC, kC, kThreads>(dd_g, L, valid_rows, t0, L, &sDd[0][0], tid);
-        if (has_z) {
-            T *dz_g = static_cast<T *>(p.dz) + rowbase;
-            store_tile<T, VEC, kC, kThreads>(dz_g, L, valid_rows, t0, L, &sDz[0][0], tid);
-        }
-        if (c > 0) st.stash(smem);
+        // unconditional, so no prefetch is in flight across the loop's back
+        // edge (after the first chunk it rewrites the last chunk's words
+        // into the raw tiles, which are not read again)
+        st.stash(smem);
         __syncthreads();
     }
 

@@ -50,8 +50,7 @@ struct FwdSmem {
     static constexpr uint32_t kY = kU;                                    // aliases u / delta / z
     static constexpr uint32_t kRawEnd = kZ + kRows * kT * sizeof(T);
     static constexpr uint32_t kYEnd = kY + 4 * 4 * kYRow * 4;
-    static constexpr uint32_t kO = kRawEnd > kYEnd ? kRawEnd : kYEnd;
-    static constexpr uint32_t kSize = kO + kRows * kT * sizeof(T);
+    static constexpr uint32_t kSize = kRawEnd > kYEnd ? kRawEnd : kYEnd;
 };
 
 template <int J>
@@ -71,7 +70,6 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
     T(*sU)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kU);
     T(*sDl)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kDl);
     T(*sZ)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kZ);
-    T(*sO)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kO);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -121,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
     const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
     float *ck = (p.ckpt && row_ok) ? p.ckpt + (b * Dm + d) * nck * kN + n : nullptr;
     float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
-    T *gy = static_cast<T *>(p.out) + (b * Dm + d0) * L;
+    T *yrow = static_cast<T *>(p.out) + (b * Dm + (row_ok ? d : d0)) * L;
     for (int64_t c = 0; c < nchunks; c++) {
         const int64_t t0 = c * kT;
         if (c + 1 < nchunks) st.fetch(t0 + kT, L);
@@ -152,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
                 for (int k = 0; k < 16; k += 2 * w) part[k] += part[k + w];
             float y = part[0] + dskip * uu[s];
             if (has_z) y *= zz[s] * sigmoid_f32(zz[s]);
-            sO[r][16 * s + n] = from_f32<T>(y);
+            // a row's 16 lanes store 16 consecutive outputs
+            if (row_ok && t0 + 16 * s + n < L) st_global(yrow + t0 + 16 * s + n, from_f32<T>(y));
         };
 #pragma unroll
         for (int s = 0; s < kT / 16; s++) {
@@ -196,7 +195,6 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
         finish(kT / 16 - 1);
         __syncthreads();
 
-        store_tile<T, VEC, kT, kThreads>(gy, L, valid_rows, t0, L, &sO[0][0], tid);
         if (c + 1 < nchunks) st.stash(smem);
         __syncthreads();
     }

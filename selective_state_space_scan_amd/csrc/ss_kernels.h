@@ -22,12 +22,12 @@ struct ScanParams {
 };
 
 // chunk length of the checkpoints saved by the forward for the backward
-constexpr int kCkptSpacing = 32;
+constexpr int kCkptSpacing = 16;
 
 struct FwdParams : ScanParams {
     void *out;
     float *last_state;
-    float *ckpt;  // (batch, dim, ceil(L / 32), 16) or nullptr
+    float *ckpt;  // (batch, dim, ceil(L / 16), 16) or nullptr
 };
 
 struct BwdParams : ScanParams {

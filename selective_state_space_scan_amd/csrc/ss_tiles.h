@@ -29,6 +29,17 @@ __device__ __forceinline__ u32x4 ld_global16(const void *p) {
 __device__ __forceinline__ void st_global16(void *p, u32x4 v) {
     *(__attribute__((address_space(1))) u32x4 *)(p) = v;
 }
+// Single-element global load.  Generic (flat) loads would make every later
+// wait on the vector-memory counter a full drain, since a pending flat
+// access may be an LDS access too.
+template <typename T>
+__device__ __forceinline__ T ld_global(const T *p) {
+    return *(const __attribute__((address_space(1))) T *)(p);
+}
+template <typename T>
+__device__ __forceinline__ void st_global(T *p, T v) {
+    *(__attribute__((address_space(1))) T *)(p) = v;
+}
 
 // One tile of a chunk.
 template <typename T>
@@ -94,7 +105,7 @@ struct ChunkStager {
                 reg[k][2] = r.z;
                 reg[k][3] = r.w;
             } else {
-                T v = src[k] ? src[k][t0] : T(0);
+                T v = src[k] ? ld_global(src[k] + t0) : T(0);
                 uint32_t tmp = 0;
                 __builtin_memcpy(&tmp, &v, sizeof(T));
                 reg[k][0] = tmp;
@@ -109,7 +120,7 @@ struct ChunkStager {
             T v[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; e++)
-                v[e] = (src[k] && t0 + col[k] + e < L) ? src[k][t0 + e] : T(0);
+                v[e] = (src[k] && t0 + col[k] + e < L) ? ld_global(src[k] + t0 + e) : T(0);
             uint32_t tmp[kWords] = {};
             __builtin_memcpy(tmp, v, sizeof(v));
 #pragma unroll

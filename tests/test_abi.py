@@ -38,14 +38,14 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 2
+    assert lib.ss_abi_version() == 3
 
 
 def test_ckpt_size(lib):
     lib.ss_ckpt_size.restype = ctypes.c_size_t
     lib.ss_ckpt_size.argtypes = [ctypes.c_int64] * 4
-    assert lib.ss_ckpt_size(2, 32, 16, 64) == 2 * 32 * 2 * 16 * 4
-    assert lib.ss_ckpt_size(2, 32, 16, 65) == 2 * 32 * 3 * 16 * 4
+    assert lib.ss_ckpt_size(2, 32, 16, 64) == 2 * 32 * 4 * 16 * 4
+    assert lib.ss_ckpt_size(2, 32, 16, 65) == 2 * 32 * 5 * 16 * 4
     assert lib.ss_ckpt_size(2, 32, 16, 0) == 0
     assert lib.ss_ckpt_size(2, 32, 8, 64) == 0
 
