@@ -200,13 +200,13 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
 
     const int64_t nchunks = (L + kT1 - 1) / kT1;
     if (nchunks > 0) {
-        st.fetch(0, L);
+        st.fetch(0, L, tid);
         st.stash(smem);
     }
     __syncthreads();
     for (int64_t c = 0; c < nchunks; c++) {
         const int64_t t0 = c * kT1;
-        if (c + 1 < nchunks) st.fetch(t0 + kT1, L);
+        if (c + 1 < nchunks) st.fetch(t0 + kT1, L, tid);
         float dl[kT1 / 16], dlu[kT1 / 16];
 #pragma unroll
         for (int s = 0; s < kT1 / 16; s++) {
@@ -273,7 +273,7 @@ struct RevSmem {
 };
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads, kC == 16 ? 4 : 3) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
+__global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
     using SM = RevSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
     float(*sB)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kB);
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads, kC == 16 ? 4 : 3) void ss_bwd_reverse_ker
         tid);
 
     if (nch > 0) {
-        st.fetch((nch - 1) * kC, L);
+        st.fetch((nch - 1) * kC, L, tid);
         st.stash(smem);
     }
     __syncthreads();
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kThreads, kC == 16 ? 4 : 3) void ss_bwd_reverse_ker
         if (c > 0) {
 #pragma unroll
             for (int s = 0; s < kNB; s++) hn[s] = ckpt_at(kNB * (c - 1) + s);
-            st.fetch(t0 - kC, L);
+            st.fetch(t0 - kC, L, tid);
         }
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row

@@ -62,7 +62,7 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
 }
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, VEC == 1 ? 3 : 4) void ss_fwd_kernel(FwdParams p) {
     using SM = FwdSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
     float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + SM::kB);
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
 
     const int64_t nchunks = (L + kT - 1) / kT;
     if (nchunks > 0) {
-        st.fetch(0, L);
+        st.fetch(0, L, tid);
         st.stash(smem);
     }
     __syncthreads();
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void ss_fwd_kernel(FwdParams p) {
     T *yrow = static_cast<T *>(p.out) + (b * Dm + (row_ok ? d : d0)) * L;
     for (int64_t c = 0; c < nchunks; c++) {
         const int64_t t0 = c * kT;
-        if (c + 1 < nchunks) st.fetch(t0 + kT, L);
+        if (c + 1 < nchunks) st.fetch(t0 + kT, L, tid);
 
         // per-element work: lane (r, n) owns elements 16 s + n of its row
         float dl[kT / 16], dlu[kT / 16], uu[kT / 16], zz[kT / 16];

@@ -59,12 +59,24 @@ struct ChunkStager {
     static constexpr int kVecPerTile = 16 * kVecPerRow;
     static constexpr int kSlots = (NTILES * kVecPerTile + NTHREADS - 1) / NTHREADS;
     static constexpr int kWords = (VEC * sizeof(T) + 3) / 4;
+    // tiles of whole wavefronts of slots keep the tile index (and so its
+    // descriptor) uniform across a wavefront
+    static constexpr bool kUniformTile = kVecPerTile % 64 == 0;
 
-    const T *src[kSlots];  // slot's first element at t = 0, or nullptr
-    uint32_t dst[kSlots];  // LDS byte offset, or ~0u for slots past the last tile
-    int col[kSlots];       // slot's first time offset within the chunk
-    bool f32[kSlots];
+    // Per slot: the tile's base (uniform across the wavefront when
+    // kUniformTile, so in scalar registers) and 32-bit per-lane offsets.
+    const T *base[kSlots];  // element (row 0, t = 0) of the slot's tile; nullptr = zeros / none
+    uint32_t goff[kSlots];  // the lane's element offset in the tile (row * stride + col),
+                            // kNoRow for rows past the last valid one (read as zeros)
+    uint32_t dst[kSlots];   // LDS byte offset
+    bool f32[kSlots];       // stash as f32 (else as T); uniform
+    bool used[kSlots];      // slot maps to a tile; uniform
     uint32_t reg[kSlots][kWords];
+    static constexpr uint32_t kNoRow = ~0u;
+
+    __device__ static int slot_col(int tid, int k) {
+        return ((tid + k * NTHREADS) % kVecPerRow) * VEC;
+    }
 
     // `desc(i)` returns the TileSrc of tile i (called with constant i only).
     template <typename Desc>
@@ -72,23 +84,26 @@ struct ChunkStager {
 #pragma unroll
         for (int k = 0; k < kSlots; k++) {
             const int slot = tid + k * NTHREADS;
-            // tiles span whole wavefronts of slots: the tile index is wave-uniform
-            const int tile = __builtin_amdgcn_readfirstlane(slot / kVecPerTile);
+            const int tile = kUniformTile ? __builtin_amdgcn_readfirstlane(slot / kVecPerTile)
+                                          : slot / kVecPerTile;
             const int rem = slot % kVecPerTile;
             const int row = rem / kVecPerRow;
-            col[k] = (rem % kVecPerRow) * VEC;
-            src[k] = nullptr;
-            dst[k] = ~0u;
+            const int col = (rem % kVecPerRow) * VEC;
+            base[k] = nullptr;
+            goff[k] = kNoRow;
+            dst[k] = 0;
             f32[k] = false;
+            used[k] = tile < NTILES;
             if (tile < NTILES) {
                 TileSrc<T> ts = desc(0);
 #pragma unroll
                 for (int i = 1; i < NTILES; i++)
                     if (tile == i) ts = desc(i);
-                if (ts.base && row < ts.valid_rows) src[k] = ts.base + row * ts.row_stride + col[k];
+                base[k] = ts.base;
+                if (row < ts.valid_rows) goff[k] = uint32_t(row * ts.row_stride + col);
                 f32[k] = ts.to_f32;
                 const uint32_t esz = ts.to_f32 ? 4u : uint32_t(sizeof(T));
-                dst[k] = ts.lds_off + uint32_t(row * ts.pitch + col[k]) * esz;
+                dst[k] = ts.lds_off + uint32_t(row * ts.pitch + col) * esz;
             }
         }
     }
@@ -97,15 +112,16 @@ struct ChunkStager {
     __device__ __forceinline__ void fetch_full(int64_t t0) {
 #pragma unroll
         for (int k = 0; k < kSlots; k++) {
+            const bool on = base[k] && goff[k] != kNoRow;
             if constexpr (VEC * sizeof(T) == 16) {
                 u32x4 r = {0u, 0u, 0u, 0u};
-                if (src[k]) r = ld_global16(src[k] + t0);
+                if (on) r = ld_global16(base[k] + t0 + goff[k]);
                 reg[k][0] = r.x;
                 reg[k][1] = r.y;
                 reg[k][2] = r.z;
                 reg[k][3] = r.w;
             } else {
-                T v = src[k] ? ld_global(src[k] + t0) : T(0);
+                T v = on ? ld_global(base[k] + t0 + goff[k]) : T(0);
                 uint32_t tmp = 0;
                 __builtin_memcpy(&tmp, &v, sizeof(T));
                 reg[k][0] = tmp;
@@ -114,13 +130,15 @@ struct ChunkStager {
     }
 
     // Guarded loads of the ragged chunk that starts at t0 (t0 + KT > L).
-    __device__ __forceinline__ void fetch_tail(int64_t t0, int64_t L) {
+    __device__ __forceinline__ void fetch_tail(int64_t t0, int64_t L, int tid) {
 #pragma unroll
         for (int k = 0; k < kSlots; k++) {
+            const bool on = base[k] && goff[k] != kNoRow;
+            const int col = slot_col(tid, k);
             T v[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; e++)
-                v[e] = (src[k] && t0 + col[k] + e < L) ? ld_global(src[k] + t0 + e) : T(0);
+                v[e] = (on && t0 + col + e < L) ? ld_global(base[k] + t0 + goff[k] + e) : T(0);
             uint32_t tmp[kWords] = {};
             __builtin_memcpy(tmp, v, sizeof(v));
 #pragma unroll
@@ -128,15 +146,15 @@ struct ChunkStager {
         }
     }
 
-    __device__ __forceinline__ void fetch(int64_t t0, int64_t L) {
+    __device__ __forceinline__ void fetch(int64_t t0, int64_t L, int tid) {
         if (t0 + KT <= L) fetch_full(t0);
-        else fetch_tail(t0, L);
+        else fetch_tail(t0, L, tid);
     }
 
     __device__ __forceinline__ void stash(char *smem) {
 #pragma unroll
         for (int k = 0; k < kSlots; k++) {
-            if (dst[k] == ~0u) continue;
+            if (!used[k]) continue;
             T v[VEC];
             __builtin_memcpy(v, reg[k], sizeof(v));
             if (f32[k]) {

@@ -44,7 +44,9 @@ SMALL = [
     (2, 32, 64, "f32", dict(has_bias=False)),
     (2, 32, 64, "f32", dict(softplus=False)),
     (3, 16, 1, "f32", {}),
-    (2, 24, 70, "bf16", {}),
+    (2, 24, 70, "bf16", {}),                      # bf16 rows not 16-byte aligned (scalar path)
+    (2, 24, 96, "bf16", {}),                      # bf16, 16-byte slots
+    (2, 40, 136, "bf16", {}),                     # bf16, 16-byte slots, ragged dim and tail
 ]
 
 
@@ -80,7 +82,7 @@ def test_bwd_small_elementwise(batch, dim, L, io, flags):
 
 
 @pytest.mark.parametrize("batch,dim,L,io", [(2, 40, 100, "f32"), (1, 33, 70, "bf16"),
-                                             (2, 16, 17, "f32")])
+                                             (2, 24, 96, "bf16"), (2, 16, 17, "f32")])
 def test_bwd_with_forward_checkpoints_is_bit_identical(batch, dim, L, io):
     """Checkpoints saved by the forward give the same bits as recomputing them."""
     require_gpu()
