@@ -549,23 +549,55 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
 // ---------------------------------------------------------------------------
 // kernel 3: fixed-order folds
 // ---------------------------------------------------------------------------
-template <typename T>
+// Thread i < nbc / VT folds dB and dC at VT consecutive steps; the next
+// threads fold dA, then dD and dbias.  Every sum runs in ascending group
+// (or batch) order; the group loop keeps 4 groups of loads in flight.
+template <int VT>
+__device__ __forceinline__ void fold_add(float (&acc)[VT], const float *src) {
+    if constexpr (VT == 4) {
+        const u32x4 r = ld_global16(src);
+        // elements are converted by value (a bit cast of a vector element
+        // would read element 0 under clang 22)
+        acc[0] += __uint_as_float(r.x);
+        acc[1] += __uint_as_float(r.y);
+        acc[2] += __uint_as_float(r.z);
+        acc[3] += __uint_as_float(r.w);
+    } else {
+        acc[0] += ld_global(src);
+    }
+}
+
+template <typename T, int VT>
 __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace ws) {
     const int64_t L = p.seqlen, Dm = p.dim, Bt = p.batch;
     const int64_t groups = (Dm + kRows - 1) / kRows;
-    const int64_t nbc = Bt * kN * L;      // dB / dC elements
-    const int64_t na = Dm * kN;           // dA elements
+    const int64_t nbc = Bt * kN * L / VT;   // dB / dC work items (VT divides L)
+    const int64_t na = Dm * kN;             // dA elements
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < nbc) {
-        const int64_t bb = i / (kN * L), rem = i - bb * kN * L;  // rem = n * L + t
-        float sb = 0.0f, sc = 0.0f;
-        for (int64_t gi = 0; gi < groups; gi++) {
-            const int64_t o = (bb * groups + gi) * kN * L + rem;
-            sb += ws.dBp[o];
-            sc += ws.dCp[o];
+        const int64_t e = i * VT;                                // (bb, n, t) element
+        const int64_t bb = e / (kN * L), rem = e - bb * kN * L;  // rem = n * L + t
+        const int64_t stride = kN * L;                           // one channel group
+        const float *pb = ws.dBp + bb * groups * stride + rem;
+        const float *pc = ws.dCp + bb * groups * stride + rem;
+        float sb[VT] = {}, sc[VT] = {};
+        int64_t gi = 0;
+        for (; gi + 4 <= groups; gi += 4) {
+            // the loads of 4 groups are issued before their in-order adds
+#pragma unroll
+            for (int k = 0; k < 4; k++) fold_add<VT>(sb, pb + (gi + k) * stride);
+#pragma unroll
+            for (int k = 0; k < 4; k++) fold_add<VT>(sc, pc + (gi + k) * stride);
         }
-        static_cast<T *>(p.dB)[i] = from_f32<T>(sb);
-        static_cast<T *>(p.dC)[i] = from_f32<T>(sc);
+        for (; gi < groups; gi++) {
+            fold_add<VT>(sb, pb + gi * stride);
+            fold_add<VT>(sc, pc + gi * stride);
+        }
+#pragma unroll
+        for (int k = 0; k < VT; k++) {
+            static_cast<T *>(p.dB)[e + k] = from_f32<T>(sb[k]);
+            static_cast<T *>(p.dC)[e + k] = from_f32<T>(sc[k]);
+        }
     } else if (i < nbc + na) {
         const int64_t k = i - nbc;
         float s = 0.0f;
@@ -606,10 +638,14 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t total = p.batch * kN * p.seqlen + p.dim * kN + p.dim;
+    const bool v4 = p.seqlen % 4 == 0;   // 16-byte partial loads
+    const int64_t total = p.batch * kN * p.seqlen / (v4 ? 4 : 1) + p.dim * kN + p.dim;
     if (total > 0) {
-        hipLaunchKernelGGL((ss_bwd_fold_kernel<T>), dim3(unsigned((total + 255) / 256)), dim3(256),
-                           0, stream, p, ws);
+        const dim3 fgrid(unsigned((total + 255) / 256));
+        if (v4)
+            hipLaunchKernelGGL((ss_bwd_fold_kernel<T, 4>), fgrid, dim3(256), 0, stream, p, ws);
+        else
+            hipLaunchKernelGGL((ss_bwd_fold_kernel<T, 1>), fgrid, dim3(256), 0, stream, p, ws);
         profile_mark(stream);
     }
     return hipGetLastError();
