@@ -52,8 +52,14 @@ constexpr int kC = SS_REV_CHUNK;   // reverse-pass staging chunk: kNB recompute 
 constexpr int kNB = kC / kCk;
 static_assert(kCk == 16 && (kNB == 1 || kNB == 2), "a staging chunk holds one or two 16-step blocks");
 constexpr int kThreads = 256;
-constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
-constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row
+// Sums over the 16 states of a row: one butterfly level in registers (lane
+// n with lane 15 - n, see mirror_fold) leaves 8 values per lane, which go
+// through an 8 x 8 LDS transpose per half row.  Lane n writes its 8 values
+// as row n (two 16-byte chunks, rows kTP floats apart); lane m reads column
+// m % 8 of its half's 8 rows.  Row regions kTRow floats apart put the 4 rows
+// of a wavefront 8 banks apart, so neither access hits a bank twice.
+constexpr int kTP = 12;                // floats per lane's row (8 + 4 pad)
+constexpr int kTRow = 16 * kTP + 8;    // floats per DPP row's transpose
 
 // Workspace carve-up (all f32, 256-byte aligned pieces).
 struct Workspace {
@@ -134,6 +140,34 @@ __device__ __forceinline__ float rows_quad_sum(float p, float q) {
     const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, p),
                                                     __builtin_bit_cast(unsigned, q), false, false);
     return swap_sum(r);
+}
+
+// value of lane 15 - n of the same DPP row (row_mirror)
+__device__ __forceinline__ float row_mirror(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xf, 0xf, true));
+}
+
+// One butterfly level over the lanes of a DPP row: lanes n < 8 end with
+// lo[i] summed over lanes {n, 15 - n}, lanes n >= 8 with hi[i] summed over
+// the same pair (own value first).
+__device__ __forceinline__ void mirror_fold(const float (&lo)[8], const float (&hi)[8],
+                                            float (&out)[8], bool low_lane) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float keep = low_lane ? lo[i] : hi[i];
+        const float send = low_lane ? hi[i] : lo[i];
+        out[i] = keep + row_mirror(send);
+    }
+}
+
+// fixed pairwise sum of 8 values
+__device__ __forceinline__ float tree8(float (&x)[8]) {
+#pragma unroll
+    for (int w = 1; w < 8; w *= 2)
+#pragma unroll
+        for (int k = 0; k < 8; k += 2 * w) x[k] += x[k + w];
+    return x[0];
 }
 
 // fixed pairwise sum of 16 values
@@ -260,7 +294,7 @@ struct RevSmem {
     static constexpr uint32_t kG = kZ + kRows * kC * sizeof(T);
     static constexpr uint32_t kRawEnd = kG + kRows * kC * sizeof(T);
     static constexpr uint32_t kTr = kUn;
-    static constexpr uint32_t kTrEnd = kTr + 4 * 4 * kYRow * 4;
+    static constexpr uint32_t kTrEnd = kTr + 4 * 4 * kTRow * 4;
     static constexpr uint32_t kUnEnd = kRawEnd > kTrEnd ? kRawEnd : kTrEnd;
     // 4-row channel sums: [wave 4][step kC][quantity 2 x state 16 + pad].
     // The summing threads of a wavefront read 8 steps kC / 8 apart x 8
@@ -341,7 +375,15 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     }
     __syncthreads();
 
-    float *tr = reinterpret_cast<float *>(smem + SM::kTr) + wave * 4 * kYRow + rw * kYRow;
+    float *tr = reinterpret_cast<float *>(smem + SM::kTr) + wave * 4 * kTRow + rw * kTRow;
+    const bool low_lane = n < 8;
+    // this lane's transpose row, and its column of its half's 8 rows
+    float *const trw = tr + n * kTP;
+    const float *const trr = tr + (n >> 3) * 8 * kTP + (n & 7);
+    auto tr_write = [&](const float (&x)[8]) {
+        *reinterpret_cast<float4 *>(trw) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4 *>(trw + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    };
     // this lane's slot of the channel sums: lane (rw, n) receives state n of
     // quantity rw / 2 (0: dB, 1: dC) at the odd (rw & 1) step of a pair
     float *chw = chan + wave * SM::kChWave + (rw & 1) * SM::kChStep + (rw >> 1) * kN + n;
@@ -388,7 +430,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
         for (int s = kNB - 1; s >= 0; s--) {
             const int col = 16 * s + n;
             const float hstart = hb[s];
-            float ab[kCk], hs[kCk];
+            float ab[kCk], hs[kCk], v[kCk];
             float h = hstart;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
@@ -396,7 +438,6 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                 const float4 c4 = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
                 const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
                 const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-                float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int j = 4 * q + e;
@@ -411,20 +452,23 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                     ab[j] = exp2_hw(dj * a2);
                     h = __builtin_fmaf(ab[j], h, duj * bb[e]);
                     hs[j] = h;
-                    v[e] = cc[e] * h;
+                    v[j] = cc[e] * h;
                 }
-                if (has_z)
-                    *reinterpret_cast<float4 *>(&tr[n * kYN + 4 * q]) =
-                        make_float4(v[0], v[1], v[2], v[3]);
             }
             float dy;
             if (has_z) {
+                // sum of C h over the states: lanes n < 8 collect steps 0-7,
+                // lanes n >= 8 steps 8-15, so lane n ends with its own step
+                float f[8];
+                mirror_fold(reinterpret_cast<const float(&)[8]>(v[0]),
+                            reinterpret_cast<const float(&)[8]>(v[8]), f, low_lane);
+                tr_write(f);
                 __builtin_amdgcn_wave_barrier();
-                float part[16];
+                float part[8];
 #pragma unroll
-                for (int k = 0; k < 16; k++) part[k] = tr[k * kYN + n];
+                for (int k = 0; k < 8; k++) part[k] = trr[k * kTP];
                 __builtin_amdgcn_wave_barrier();
-                const float ypre = tree16(part) + dskip * uu[s];
+                const float ypre = tree8(part) + dskip * uu[s];
                 const float sz = sigmoid_f32(zz[s]);
                 dy = dout[s] * zz[s] * sz;
                 if (row_ok && t0 + col < L)
@@ -477,17 +521,17 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                     }
                     g = ab[j] * g;                                        // carried to t - 1
                 }
-                // sums over the 16 states: columns 0-7 carry A*g*abar*h, 8-15 g*B
-                *reinterpret_cast<float4 *>(&tr[n * kYN + 0]) = make_float4(qa[0], qa[1], qa[2], qa[3]);
-                *reinterpret_cast<float4 *>(&tr[n * kYN + 4]) = make_float4(qa[4], qa[5], qa[6], qa[7]);
-                *reinterpret_cast<float4 *>(&tr[n * kYN + 8]) = make_float4(qb[0], qb[1], qb[2], qb[3]);
-                *reinterpret_cast<float4 *>(&tr[n * kYN + 12]) = make_float4(qb[4], qb[5], qb[6], qb[7]);
+                // sums over the 16 states: lanes n < 8 collect A*g*abar*h,
+                // lanes n >= 8 g*B, lane n (mod 8) the step 8 hh + n % 8
+                float f[8];
+                mirror_fold(qa, qb, f, low_lane);
+                tr_write(f);
                 __builtin_amdgcn_wave_barrier();
-                float part[16];
+                float part[8];
 #pragma unroll
-                for (int k = 0; k < 16; k++) part[k] = tr[k * kYN + n];
+                for (int k = 0; k < 8; k++) part[k] = trr[k * kTP];
                 __builtin_amdgcn_wave_barrier();
-                const float sum = tree16(part);
+                const float sum = tree8(part);
                 const float other = row_ror8(sum);
                 // owner lanes of steps 8 hh .. 8 hh + 7 pick up both sums
                 if (hh == 0 && n < 8) { sumA = sum; sumB = other; }
