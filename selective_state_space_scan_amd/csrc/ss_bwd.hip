@@ -52,14 +52,6 @@ constexpr int kC = SS_REV_CHUNK;   // reverse-pass staging chunk: kNB recompute 
 constexpr int kNB = kC / kCk;
 static_assert(kCk == 16 && (kNB == 1 || kNB == 2), "a staging chunk holds one or two 16-step blocks");
 constexpr int kThreads = 256;
-// Sums over the 16 states of a row: one butterfly level in registers (lane
-// n with lane 15 - n, see mirror_fold) leaves 8 values per lane, which go
-// through an 8 x 8 LDS transpose per half row.  Lane n writes its 8 values
-// as row n (two 16-byte chunks, rows kTP floats apart); lane m reads column
-// m % 8 of its half's 8 rows.  Row regions kTRow floats apart put the 4 rows
-// of a wavefront 8 banks apart, so neither access hits a bank twice.
-constexpr int kTP = 12;                // floats per lane's row (8 + 4 pad)
-constexpr int kTRow = 16 * kTP + 8;    // floats per DPP row's transpose
 
 // Workspace carve-up (all f32, 256-byte aligned pieces).
 struct Workspace {
@@ -142,41 +134,47 @@ __device__ __forceinline__ float rows_quad_sum(float p, float q) {
     return swap_sum(r);
 }
 
-// value of lane 15 - n of the same DPP row (row_mirror)
-__device__ __forceinline__ float row_mirror(float v) {
+// DPP lane permutations within a 16-lane row (one VALU op each, or folded
+// into the add that consumes them): lane n reads lane n ^ 15 (row_mirror),
+// n ^ 7 (row_half_mirror), n ^ 2 and n ^ 1 (quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float dpp_lane(float v) {
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xf, 0xf, true));
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 
-// One butterfly level over the lanes of a DPP row: lanes n < 8 end with
-// lo[i] summed over lanes {n, 15 - n}, lanes n >= 8 with hi[i] summed over
-// the same pair (own value first).
-__device__ __forceinline__ void mirror_fold(const float (&lo)[8], const float (&hi)[8],
-                                            float (&out)[8], bool low_lane) {
+// One butterfly level: `x` holds 2K values; the lane keeps one half (the low
+// one when `low`) and adds the partner's copy of that half, which the partner
+// sends in place of its own kept half.  Own value first.
+template <int CTRL, int K>
+__device__ __forceinline__ void fold_level(const float *x, float *out, bool low) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const float keep = low_lane ? lo[i] : hi[i];
-        const float send = low_lane ? hi[i] : lo[i];
-        out[i] = keep + row_mirror(send);
+    for (int i = 0; i < K; i++) {
+        const float keep = low ? x[i] : x[K + i];
+        const float send = low ? x[K + i] : x[i];
+        out[i] = keep + dpp_lane<CTRL>(send);
     }
 }
 
-// fixed pairwise sum of 8 values
-__device__ __forceinline__ float tree8(float (&x)[8]) {
+// Sum over the 16 lanes of a DPP row of 16 values per lane, all in
+// registers: lane n ends with the sum of value n (lo[n] for n < 8, hi[n - 8]
+// otherwise).  Four butterfly levels pair lanes n ^ 15, n ^ 7, n ^ 2 and
+// n ^ 1; those masks generate all 16 lanes and each level joins disjoint
+// lane sets, so every lane's value is added exactly once, in an order fixed
+// by the lane index.
+__device__ __forceinline__ float row_transpose_sum(const float (&lo)[8], const float (&hi)[8],
+                                                   int n) {
+    float x16[16], x8[8], x4[4], x2[2], x1[1];
 #pragma unroll
-    for (int w = 1; w < 8; w *= 2)
-#pragma unroll
-        for (int k = 0; k < 8; k += 2 * w) x[k] += x[k + w];
-    return x[0];
-}
-
-// fixed pairwise sum of 16 values
-__device__ __forceinline__ float tree16(float (&x)[16]) {
-#pragma unroll
-    for (int w = 1; w < 16; w *= 2)
-#pragma unroll
-        for (int k = 0; k < 16; k += 2 * w) x[k] += x[k + w];
-    return x[0];
+    for (int i = 0; i < 8; i++) {
+        x16[i] = lo[i];
+        x16[8 + i] = hi[i];
+    }
+    fold_level<0x140, 8>(x16, x8, n < 8);          // row_mirror: n ^ 15
+    fold_level<0x141, 4>(x8, x4, (n & 7) < 4);     // row_half_mirror: n ^ 7
+    fold_level<0x4E, 2>(x4, x2, (n & 3) < 2);      // quad_perm [2,3,0,1]: n ^ 2
+    fold_level<0xB1, 1>(x2, x1, (n & 1) == 0);     // quad_perm [1,0,3,2]: n ^ 1
+    return x1[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -287,20 +285,16 @@ template <typename T>
 struct RevSmem {
     static constexpr uint32_t kB = 0;
     static constexpr uint32_t kCc = kB + kN * kPitch2 * 4;
-    static constexpr uint32_t kUn = kCc + kN * kPitch2 * 4;         // union: raw tiles / transposes
-    static constexpr uint32_t kU = kUn;
+    static constexpr uint32_t kU = kCc + kN * kPitch2 * 4;          // raw u / delta / z / dout
     static constexpr uint32_t kDl = kU + kRows * kC * sizeof(T);
     static constexpr uint32_t kZ = kDl + kRows * kC * sizeof(T);
     static constexpr uint32_t kG = kZ + kRows * kC * sizeof(T);
     static constexpr uint32_t kRawEnd = kG + kRows * kC * sizeof(T);
-    static constexpr uint32_t kTr = kUn;
-    static constexpr uint32_t kTrEnd = kTr + 4 * 4 * kTRow * 4;
-    static constexpr uint32_t kUnEnd = kRawEnd > kTrEnd ? kRawEnd : kTrEnd;
     // 4-row channel sums: [wave 4][step kC][quantity 2 x state 16 + pad].
     // The summing threads of a wavefront read 8 steps kC / 8 apart x 8
     // states; a step pitch P with (kC / 8) P = 8 (mod 64) puts them in 64
     // distinct banks.
-    static constexpr uint32_t kCh = kUnEnd;
+    static constexpr uint32_t kCh = kRawEnd;
     static constexpr int kChStep = kC == 32 ? 34 : 36;
     static constexpr int kChWave = kC * kChStep;
     static constexpr uint32_t kSize = kCh + 4 * kChWave * 4;
@@ -375,15 +369,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     }
     __syncthreads();
 
-    float *tr = reinterpret_cast<float *>(smem + SM::kTr) + wave * 4 * kTRow + rw * kTRow;
-    const bool low_lane = n < 8;
-    // this lane's transpose row, and its column of its half's 8 rows
-    float *const trw = tr + n * kTP;
-    const float *const trr = tr + (n >> 3) * 8 * kTP + (n & 7);
-    auto tr_write = [&](const float (&x)[8]) {
-        *reinterpret_cast<float4 *>(trw) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4 *>(trw + 4) = make_float4(x[4], x[5], x[6], x[7]);
-    };
+
     // this lane's slot of the channel sums: lane (rw, n) receives state n of
     // quantity rw / 2 (0: dB, 1: dC) at the odd (rw & 1) step of a pair
     float *chw = chan + wave * SM::kChWave + (rw & 1) * SM::kChStep + (rw >> 1) * kN + n;
@@ -422,7 +408,6 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
             dout[s] = to_f32<T>(sG[r][col]);
             zz[s] = to_f32<T>(sZ[r][col]);
         }
-        __syncthreads();  // the transpose region aliases the raw tiles
 
         // blocks last to first: recompute the block's 16 forward steps from
         // its checkpoint (decays and states in registers), then walk them back
@@ -457,18 +442,11 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
             }
             float dy;
             if (has_z) {
-                // sum of C h over the states: lanes n < 8 collect steps 0-7,
-                // lanes n >= 8 steps 8-15, so lane n ends with its own step
-                float f[8];
-                mirror_fold(reinterpret_cast<const float(&)[8]>(v[0]),
-                            reinterpret_cast<const float(&)[8]>(v[8]), f, low_lane);
-                tr_write(f);
-                __builtin_amdgcn_wave_barrier();
-                float part[8];
-#pragma unroll
-                for (int k = 0; k < 8; k++) part[k] = trr[k * kTP];
-                __builtin_amdgcn_wave_barrier();
-                const float ypre = tree8(part) + dskip * uu[s];
+                // sum of C h over the states: lane n ends with its own step
+                const float ypre =
+                    row_transpose_sum(reinterpret_cast<const float(&)[8]>(v[0]),
+                                      reinterpret_cast<const float(&)[8]>(v[8]), n) +
+                    dskip * uu[s];
                 const float sz = sigmoid_f32(zz[s]);
                 dy = dout[s] * zz[s] * sz;
                 if (row_ok && t0 + col < L)
@@ -521,17 +499,9 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                     }
                     g = ab[j] * g;                                        // carried to t - 1
                 }
-                // sums over the 16 states: lanes n < 8 collect A*g*abar*h,
-                // lanes n >= 8 g*B, lane n (mod 8) the step 8 hh + n % 8
-                float f[8];
-                mirror_fold(qa, qb, f, low_lane);
-                tr_write(f);
-                __builtin_amdgcn_wave_barrier();
-                float part[8];
-#pragma unroll
-                for (int k = 0; k < 8; k++) part[k] = trr[k * kTP];
-                __builtin_amdgcn_wave_barrier();
-                const float sum = tree8(part);
+                // sums over the 16 states: lane n < 8 gets A*g*abar*h of step
+                // 8 hh + n, lane n >= 8 g*B of step 8 hh + n - 8
+                const float sum = row_transpose_sum(qa, qb, n);
                 const float other = row_ror8(sum);
                 // owner lanes of steps 8 hh .. 8 hh + 7 pick up both sums
                 if (hh == 0 && n < 8) { sumA = sum; sumB = other; }
