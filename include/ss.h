@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 3
+#define SS_ABI_VERSION 4
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -78,8 +78,10 @@ int ss_abi_version(void);
 const char *ss_last_error(void);
 
 /*
- * Bytes of the checkpoints ss_fwd can save for ss_bwd: the state entering
- * every 16-step block, f32 (batch, dim, ceil(seqlen / 16), dstate).
+ * Bytes of what ss_fwd can save for ss_bwd (its "ckpt" buffer), all f32:
+ * the state entering every 16-step block, (batch, dim, ceil(seqlen / 16),
+ * dstate), then at the next 256-byte boundary the pre-gate output
+ * sum_n C h + D u, (batch, dim, seqlen), which is written when z is given.
  * 0 for empty or unsupported shapes.
  */
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
@@ -88,9 +90,9 @@ size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
  * Forward scan.  Writes out (batch, dim, seqlen) and, when last_state is
  * non-NULL, the final state h_{seqlen-1} (h0 when seqlen == 0).  When ckpt
  * is non-NULL (ss_ckpt_size() bytes, 16-byte aligned) it also saves the
- * chunk checkpoints, which a later ss_bwd with the same inputs can take
- * instead of recomputing them (the usual save-for-backward of a training
- * step).
+ * block states and the pre-gate output, which a later ss_bwd with the same
+ * inputs takes instead of recomputing them (the usual save-for-backward of
+ * a training step).
  *   dstate            must be 16 (SS_EUNSUPPORTED otherwise).
  *   io_dtype          SS_F32 or SS_BF16: dtype of u, delta, B, C, z, out.
  *   D, z, delta_bias, h0, last_state may be NULL.
@@ -121,8 +123,8 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
  *   dz                 NULL iff z is NULL.
  *   ddelta_bias        NULL iff delta_bias is NULL; summed over batch and time.
  *   dh0                optional (may be non-NULL with h0 NULL: gradient at a zero start).
- *   ckpt               checkpoints saved by ss_fwd for exactly these inputs, or
- *                      NULL (then they are recomputed in the workspace).
+ *   ckpt               what ss_fwd saved for exactly these inputs, or NULL
+ *                      (then the block states are recomputed in the workspace).
  *   workspace          device memory of at least ss_bwd_workspace_size() bytes,
  *                      16-byte aligned, owned by the caller, not read before written.
  * Every sum over batch, time or channels runs in a fixed order, with no

@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 3
+ABI_VERSION = 4
 _lock = threading.Lock()
 _lib = None
 

@@ -145,6 +145,7 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.out = out; p.last_state = last_state; p.ckpt = ckpt;
+    p.ypre = ckpt ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
                          "ss_fwd launch");
@@ -152,8 +153,7 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
 
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
     if (check_dims(batch, dim, dstate, seqlen, SS_F32, true) != SS_OK) return 0;
-    const int64_t nck = (seqlen + ssk::kCkptSpacing - 1) / ssk::kCkptSpacing;
-    return size_t(batch) * size_t(dim) * size_t(nck) * 16 * sizeof(float);
+    return ssk::ckpt_bytes(batch, dim, seqlen);
 }
 
 size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
@@ -209,6 +209,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.dout = dout; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB;
     p.dC = dC; p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0; p.ckpt = ckpt;
+    p.ypre = ckpt ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
     p.workspace = workspace;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),

@@ -55,7 +55,8 @@ constexpr int kThreads = 256;
 
 // Workspace carve-up (all f32, 256-byte aligned pieces).
 struct Workspace {
-    float *ckpt;     // (batch, dim, nck, 16): state entering each chunk
+    float *ckpt;     // (batch, dim, nck, 16): state entering each 16-step block
+    const float *ypre;  // pre-gate output saved by the forward, or nullptr
     float *dBp;      // (batch, groups, 16, L)
     float *dCp;      // (batch, groups, 16, L)
     float *dAp;      // (batch, dim, 16)
@@ -78,6 +79,7 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
         return r;
     };
     w.ckpt = take(size_t(batch) * dim * nck * kN);
+    w.ypre = nullptr;
     w.dBp = take(size_t(batch) * groups * kN * L);
     w.dCp = take(size_t(batch) * groups * kN * L);
     w.dAp = take(size_t(batch) * dim * kN);
@@ -134,48 +136,6 @@ __device__ __forceinline__ float rows_quad_sum(float p, float q) {
     return swap_sum(r);
 }
 
-// DPP lane permutations within a 16-lane row (one VALU op each, or folded
-// into the add that consumes them): lane n reads lane n ^ 15 (row_mirror),
-// n ^ 7 (row_half_mirror), n ^ 2 and n ^ 1 (quad_perm).
-template <int CTRL>
-__device__ __forceinline__ float dpp_lane(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
-}
-
-// One butterfly level: `x` holds 2K values; the lane keeps one half (the low
-// one when `low`) and adds the partner's copy of that half, which the partner
-// sends in place of its own kept half.  Own value first.
-template <int CTRL, int K>
-__device__ __forceinline__ void fold_level(const float *x, float *out, bool low) {
-#pragma unroll
-    for (int i = 0; i < K; i++) {
-        const float keep = low ? x[i] : x[K + i];
-        const float send = low ? x[K + i] : x[i];
-        out[i] = keep + dpp_lane<CTRL>(send);
-    }
-}
-
-// Sum over the 16 lanes of a DPP row of 16 values per lane, all in
-// registers: lane n ends with the sum of value n (lo[n] for n < 8, hi[n - 8]
-// otherwise).  Four butterfly levels pair lanes n ^ 15, n ^ 7, n ^ 2 and
-// n ^ 1; those masks generate all 16 lanes and each level joins disjoint
-// lane sets, so every lane's value is added exactly once, in an order fixed
-// by the lane index.
-__device__ __forceinline__ float row_transpose_sum(const float (&lo)[8], const float (&hi)[8],
-                                                   int n) {
-    float x16[16], x8[8], x4[4], x2[2], x1[1];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        x16[i] = lo[i];
-        x16[8 + i] = hi[i];
-    }
-    fold_level<0x140, 8>(x16, x8, n < 8);          // row_mirror: n ^ 15
-    fold_level<0x141, 4>(x8, x4, (n & 7) < 4);     // row_half_mirror: n ^ 7
-    fold_level<0x4E, 2>(x4, x2, (n & 3) < 2);      // quad_perm [2,3,0,1]: n ^ 2
-    fold_level<0xB1, 1>(x2, x1, (n & 1) == 0);     // quad_perm [1,0,3,2]: n ^ 1
-    return x1[0];
-}
 
 // ---------------------------------------------------------------------------
 // kernel 1: checkpoints (64-step staging chunks, a checkpoint every 32 steps)
@@ -300,7 +260,9 @@ struct RevSmem {
     static constexpr uint32_t kSize = kCh + 4 * kChWave * 4;
 };
 
-template <typename T, int VEC>
+// YP: the forward saved the pre-gate output (and z is given), so dz reads it
+// instead of recomputing the sum of C h over the states.
+template <typename T, int VEC, bool YP>
 __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
     using SM = RevSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
@@ -349,6 +311,10 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     T *du_row = static_cast<T *>(p.du) + myrow;
     T *dd_row = static_cast<T *>(p.ddelta) + myrow;
     T *dz_row = has_z ? static_cast<T *>(p.dz) + myrow : nullptr;
+    // the saved pre-gate output: each owner lane loads its elements straight
+    // from global memory, a chunk ahead (a row's 16 lanes read 16 floats)
+    const float *yprow = (YP && row_ok) ? ws.ypre + myrow : nullptr;
+    auto ypre_at = [&](int64_t t) { return (yprow && t < L) ? ld_global(yprow + t) : 0.0f; };
     ChunkStager<T, VEC, kC, 6, kThreads> st;
     st.init(
         [&](int i) -> TileSrc<T> {
@@ -376,17 +342,26 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     // The checkpoints of the next chunk are loaded one chunk ahead and before
     // the prefetch: loads retire in order, so a load issued after the
     // prefetch would make its use wait for the prefetch.
-    float hn[kNB];
+    float hn[kNB], ypn[kNB];
 #pragma unroll
-    for (int s = 0; s < kNB; s++) hn[s] = ckpt_at(kNB * (nch - 1) + s);
+    for (int s = 0; s < kNB; s++) {
+        hn[s] = ckpt_at(kNB * (nch - 1) + s);
+        if (YP) ypn[s] = ypre_at((nch - 1) * kC + 16 * s + n);
+    }
     for (int64_t c = nch - 1; c >= 0; c--) {
         const int64_t t0 = c * kC;
-        float hb[kNB];
+        float hb[kNB], yp[kNB];
 #pragma unroll
-        for (int s = 0; s < kNB; s++) hb[s] = hn[s];
+        for (int s = 0; s < kNB; s++) {
+            hb[s] = hn[s];
+            if (YP) yp[s] = ypn[s];
+        }
         if (c > 0) {
 #pragma unroll
-            for (int s = 0; s < kNB; s++) hn[s] = ckpt_at(kNB * (c - 1) + s);
+            for (int s = 0; s < kNB; s++) {
+                hn[s] = ckpt_at(kNB * (c - 1) + s);
+                if (YP) ypn[s] = ypre_at(t0 - kC + 16 * s + n);
+            }
             st.fetch(t0 - kC, L, tid);
         }
 
@@ -420,7 +395,8 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const float4 b4 = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
-                const float4 c4 = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
+                float4 c4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (!YP) c4 = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
                 const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
                 const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
@@ -437,16 +413,21 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                     ab[j] = exp2_hw(dj * a2);
                     h = __builtin_fmaf(ab[j], h, duj * bb[e]);
                     hs[j] = h;
-                    v[j] = cc[e] * h;
+                    if (!YP) v[j] = cc[e] * h;
                 }
             }
             float dy;
             if (has_z) {
-                // sum of C h over the states: lane n ends with its own step
-                const float ypre =
-                    row_transpose_sum(reinterpret_cast<const float(&)[8]>(v[0]),
-                                      reinterpret_cast<const float(&)[8]>(v[8]), n) +
-                    dskip * uu[s];
+                // sum of C h over the states (lane n ends with its own
+                // step), unless the forward saved it
+                float ypre;
+                if constexpr (YP) {
+                    ypre = yp[s];
+                } else {
+                    ypre = row_transpose_sum(reinterpret_cast<const float(&)[8]>(v[0]),
+                                             reinterpret_cast<const float(&)[8]>(v[8]), n) +
+                           dskip * uu[s];
+                }
                 const float sz = sigmoid_f32(zz[s]);
                 dy = dout[s] * zz[s] * sz;
                 if (row_ok && t0 + col < L)
@@ -632,7 +613,10 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
 template <typename T>
 hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
     Workspace ws = carve(p.workspace, p.batch, p.dim, p.seqlen, nullptr);
-    if (p.ckpt) ws.ckpt = const_cast<float *>(p.ckpt);  // saved by the forward: read only
+    if (p.ckpt) {  // saved by the forward: read only
+        ws.ckpt = const_cast<float *>(p.ckpt);
+        ws.ypre = p.ypre;
+    }
     if (p.batch > 0 && p.dim > 0) {
         dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch));
         constexpr int kVec = 16 / sizeof(T);
@@ -644,10 +628,15 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
                 hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
             profile_mark(stream);
         }
-        if (vec)
-            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
+        const bool yp = p.ckpt && p.ypre && p.z;
+        if (vec && yp)
+            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec, true>), grid, dim3(kThreads), 0, stream, p, ws);
+        else if (vec)
+            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec, false>), grid, dim3(kThreads), 0, stream, p, ws);
+        else if (yp)
+            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, 1, true>), grid, dim3(kThreads), 0, stream, p, ws);
         else
-            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
+            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, 1, false>), grid, dim3(kThreads), 0, stream, p, ws);
         profile_mark(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -70,4 +70,61 @@ __device__ __forceinline__ float row_bcast(float v) {
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + LANE, 0xf, 0xf, true));
 }
 
+// DPP lane permutations within a 16-lane row (one VALU op each, or folded
+// into the add that consumes them): lane n reads lane n ^ 15 (row_mirror),
+// n ^ 7 (row_half_mirror), n ^ 2 and n ^ 1 (quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float dpp_lane(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// One butterfly level: `x` holds 2K values; the lane keeps one half (the low
+// one when `low`) and adds the partner's copy of that half, which the partner
+// sends in place of its own kept half.  Own value first.
+template <int CTRL, int K>
+__device__ __forceinline__ void fold_level(const float *x, float *out, bool low) {
+#pragma unroll
+    for (int i = 0; i < K; i++) {
+        const float keep = low ? x[i] : x[K + i];
+        const float send = low ? x[K + i] : x[i];
+        out[i] = keep + dpp_lane<CTRL>(send);
+    }
+}
+
+// The same sum as row_transpose_sum, for a lane that already holds the 16
+// terms (x[k] = term of lane k): the butterfly's grouping depends only on the
+// lane masks, so it is one fixed tree over k -- pairs {k, 15 - k}, joined
+// with {k ^ 7, k ^ 8}, then across k ^ 2, then k ^ 1 -- and this returns the
+// same bits.
+__device__ __forceinline__ float row_tree_sum(const float (&x)[16]) {
+    float a[8], b[4];
+#pragma unroll
+    for (int k = 0; k < 8; k++) a[k] = x[k] + x[15 - k];
+#pragma unroll
+    for (int k = 0; k < 4; k++) b[k] = a[k] + a[7 - k];
+    return (b[0] + b[2]) + (b[1] + b[3]);
+}
+
+// Sum over the 16 lanes of a DPP row of 16 values per lane, all in
+// registers: lane n ends with the sum of value n (lo[n] for n < 8, hi[n - 8]
+// otherwise).  Four butterfly levels pair lanes n ^ 15, n ^ 7, n ^ 2 and
+// n ^ 1; those masks generate all 16 lanes and each level joins disjoint
+// lane sets, so every lane's value is added exactly once, in an order fixed
+// by the lane index.
+__device__ __forceinline__ float row_transpose_sum(const float (&lo)[8], const float (&hi)[8],
+                                                   int n) {
+    float x16[16], x8[8], x4[4], x2[2], x1[1];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        x16[i] = lo[i];
+        x16[8 + i] = hi[i];
+    }
+    fold_level<0x140, 8>(x16, x8, n < 8);          // row_mirror: n ^ 15
+    fold_level<0x141, 4>(x8, x4, (n & 7) < 4);     // row_half_mirror: n ^ 7
+    fold_level<0x4E, 2>(x4, x2, (n & 3) < 2);      // quad_perm [2,3,0,1]: n ^ 2
+    fold_level<0xB1, 1>(x2, x1, (n & 1) == 0);     // quad_perm [1,0,3,2]: n ^ 1
+    return x1[0];
+}
+
 }  // namespace ssk

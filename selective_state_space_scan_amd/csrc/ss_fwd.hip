@@ -62,7 +62,7 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
 }
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads, VEC == 1 ? 3 : 4) void ss_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : 4) void ss_fwd_kernel(FwdParams p) {
     using SM = FwdSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
     float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + SM::kB);
@@ -119,7 +119,10 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 3 : 4) void ss_fwd_kernel(FwdP
     const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
     float *ck = (p.ckpt && row_ok) ? p.ckpt + (b * Dm + d) * nck * kN + n : nullptr;
     float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
-    T *yrow = static_cast<T *>(p.out) + (b * Dm + (row_ok ? d : d0)) * L;
+    const int64_t myrow = (b * Dm + (row_ok ? d : d0)) * L;
+    T *yrow = static_cast<T *>(p.out) + myrow;
+    // the pre-gate output, saved for the backward's dz
+    float *yprow = (p.ypre && has_z) ? p.ypre + myrow : nullptr;
     for (int64_t c = 0; c < nchunks; c++) {
         const int64_t t0 = c * kT;
         if (c + 1 < nchunks) st.fetch(t0 + kT, L, tid);
@@ -144,14 +147,17 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 3 : 4) void ss_fwd_kernel(FwdP
         // at its end, so the LDS round trip overlaps the next 16 steps.
         float part[16];
         auto finish = [&](int s) {
-#pragma unroll
-            for (int w = 1; w < 16; w *= 2)
-#pragma unroll
-                for (int k = 0; k < 16; k += 2 * w) part[k] += part[k + w];
-            float y = part[0] + dskip * uu[s];
+            // in the order of the backward's register butterfly, so the
+            // saved pre-gate output matches its recomputation bit for bit
+            const float ypre = row_tree_sum(part) + dskip * uu[s];
+            float y = ypre;
             if (has_z) y *= zz[s] * sigmoid_f32(zz[s]);
             // a row's 16 lanes store 16 consecutive outputs
-            if (row_ok && t0 + 16 * s + n < L) st_global(yrow + t0 + 16 * s + n, from_f32<T>(y));
+            const int64_t t = t0 + 16 * s + n;
+            if (row_ok && t < L) {
+                st_global(yrow + t, from_f32<T>(y));
+                if (yprow) st_global(yprow + t, ypre);
+            }
         };
 #pragma unroll
         for (int s = 0; s < kT / 16; s++) {

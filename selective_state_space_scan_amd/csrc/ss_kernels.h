@@ -21,13 +21,29 @@ struct ScanParams {
     const float *h0;
 };
 
-// chunk length of the checkpoints saved by the forward for the backward
+// What the forward saves for the backward (one f32 buffer, ss_ckpt_size()
+// bytes): the state entering every 16-step block, (batch, dim, ceil(L / 16),
+// 16), then -- at the next 256-byte boundary -- the pre-gate output
+// (batch, dim, L), written when z is given (the backward's dz needs it).
 constexpr int kCkptSpacing = 16;
+
+__host__ __device__ inline size_t ckpt_state_floats(int64_t batch, int64_t dim, int64_t seqlen) {
+    return size_t(batch) * size_t(dim) * size_t((seqlen + kCkptSpacing - 1) / kCkptSpacing) * 16;
+}
+__host__ __device__ inline size_t ckpt_ypre_offset(int64_t batch, int64_t dim, int64_t seqlen) {
+    return (ckpt_state_floats(batch, dim, seqlen) + 63) / 64 * 64;  // floats
+}
+__host__ __device__ inline size_t ckpt_bytes(int64_t batch, int64_t dim, int64_t seqlen) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0) return 0;
+    return (ckpt_ypre_offset(batch, dim, seqlen) + size_t(batch) * size_t(dim) * size_t(seqlen)) *
+           sizeof(float);
+}
 
 struct FwdParams : ScanParams {
     void *out;
     float *last_state;
-    float *ckpt;  // (batch, dim, ceil(L / 16), 16) or nullptr
+    float *ckpt;  // block states, or nullptr
+    float *ypre;  // pre-gate output (written when z is given), or nullptr
 };
 
 struct BwdParams : ScanParams {
@@ -40,7 +56,8 @@ struct BwdParams : ScanParams {
     void *dz;
     float *dbias;
     float *dh0;
-    const float *ckpt;  // checkpoints saved by the forward, or nullptr
+    const float *ckpt;  // block states saved by the forward, or nullptr
+    const float *ypre;  // pre-gate output saved by the forward with ckpt, or nullptr
     void *workspace;
 };
 

@@ -38,14 +38,16 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 3
+    assert lib.ss_abi_version() == 4
 
 
 def test_ckpt_size(lib):
     lib.ss_ckpt_size.restype = ctypes.c_size_t
     lib.ss_ckpt_size.argtypes = [ctypes.c_int64] * 4
-    assert lib.ss_ckpt_size(2, 32, 16, 64) == 2 * 32 * 4 * 16 * 4
-    assert lib.ss_ckpt_size(2, 32, 16, 65) == 2 * 32 * 5 * 16 * 4
+    # block states (256-byte aligned), then the pre-gate output
+    assert lib.ss_ckpt_size(2, 32, 16, 64) == 2 * 32 * 4 * 16 * 4 + 2 * 32 * 64 * 4
+    assert lib.ss_ckpt_size(2, 32, 16, 65) == 2 * 32 * 5 * 16 * 4 + 2 * 32 * 65 * 4
+    assert lib.ss_ckpt_size(1, 1, 16, 1) == 256 + 4
     assert lib.ss_ckpt_size(2, 32, 16, 0) == 0
     assert lib.ss_ckpt_size(2, 32, 8, 64) == 0
 
