@@ -101,14 +101,17 @@ def algorithmic_bytes(kernel, batch, dim, L, esize):
 
 # Algorithmic floating-point operations per element (b, d, t) with d_state 16,
 # counted from the recurrence as the oracle writes it (multiply, add = 1,
-# fused multiply-add = 2, exp / log / reciprocal = 1); derivation in the design doc.
+# fused multiply-add = 2, exp / log / reciprocal = 1): per state 5 for the
+# forward step and 15 for the adjoint step and its sums, per element 21 for
+# softplus, the gate and the element gradients.  The reverse pass of the
+# step recomputes the forward states (the forward saved the pre-gate output,
+# so not C h and its sum: 2 more per state otherwise).
 FLOPS_PER_ELEMENT = {"ss_fwd_kernel": 16 * 7 + 11,          # 123
-                     "ss_bwd_reverse_kernel": 16 * 22 + 21,  # 373
+                     "ss_bwd_reverse_kernel": 16 * 20 + 21,  # 341
                      "ss_bwd_fold_kernel": 0}
-# Plain (non-packed) f32 FMA issue rate of MI355X: 256 CUs x 4 SIMDs x 16
-# lanes x 2 FLOP x 2.4 GHz.  The kernels are built with packed-FP32
-# instructions switched off, so the 157.3 TFLOP/s packed figure is not reachable.
-ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# MI355X f32 vector peak: 256 CUs x 128 FMA lanes per clock x 2 FLOP x
+# 2.4 GHz = 157.3 TFLOP/s.
+ALU_PEAK_TFLOPS = 256 * 128 * 2 * 2.4e9 / 1e12
 
 KERNEL_SOURCES = {
     "ss_fwd_kernel": ["ss_fwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"],
@@ -238,9 +241,10 @@ def main():
                    "z_gate": True, "D_skip": True, "delta_bias_softplus": True},
         "hbm_GBps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        # The scan kernels are limited by f32 VALU issue (16 exp + ~5 other
-        # VALU ops per element and state), not by HBM: the roofline is the
-        # ALU one; the HBM view of the same kernel follows beside it.
+        # The scan kernels are limited by f32 VALU work (an exp and ~20 other
+        # VALU ops per element and state in the reverse pass) and on-chip
+        # latency, not by HBM: the roofline is the ALU one; the HBM view of
+        # the same kernel follows beside it.
         "roofline": {"kernel": dom, "bound": "alu", "achieved": round(tflops, 2),
                      "peak": round(ALU_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(tflops / ALU_PEAK_TFLOPS, 4), "traffic": traffic,
