@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
         }
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row
-        float dl[kNB], dlu[kNB], uu[kNB], sgd[kNB], dout[kNB], zz[kNB];
+        float dl[kNB], dlu[kNB], uu[kNB], sgd[kNB], dout[kNB], zz[kNB], dyv[kNB];
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
             const int col = 16 * s + n;
@@ -382,6 +382,17 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
             dlu[s] = dl[s] * uu[s];
             dout[s] = to_f32<T>(sG[r][col]);
             zz[s] = to_f32<T>(sZ[r][col]);
+            // gradient reaching the pre-gate output; with the saved pre-gate
+            // output dz is per-element too and is written here, which keeps
+            // the block's recompute free of branches
+            dyv[s] = dout[s];
+            if (has_z) {
+                const float sz = sigmoid_f32(zz[s]);
+                dyv[s] = dout[s] * zz[s] * sz;
+                if (YP && row_ok && t0 + col < L)
+                    st_global(dz_row + t0 + col,
+                              from_f32<T>(dout[s] * yp[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
+            }
         }
 
         // blocks last to first: recompute the block's 16 forward steps from
@@ -416,29 +427,27 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                     if (!YP) v[j] = cc[e] * h;
                 }
             }
-            float dy;
-            if (has_z) {
-                // sum of C h over the states (lane n ends with its own
-                // step), unless the forward saved it
-                float ypre;
-                if constexpr (YP) {
-                    ypre = yp[s];
-                } else {
-                    ypre = row_transpose_sum(reinterpret_cast<const float(&)[8]>(v[0]),
-                                             reinterpret_cast<const float(&)[8]>(v[8]), n) +
-                           dskip * uu[s];
-                }
+            const float dy = dyv[s];
+            if (!YP && has_z) {
+                // pre-gate output: sum of C h over the states (lane n ends
+                // with its own step) plus the skip term
+                const float ypre = row_transpose_sum(reinterpret_cast<const float(&)[8]>(v[0]),
+                                                     reinterpret_cast<const float(&)[8]>(v[8]), n) +
+                                   dskip * uu[s];
                 const float sz = sigmoid_f32(zz[s]);
-                dy = dout[s] * zz[s] * sz;
                 if (row_ok && t0 + col < L)
                     st_global(dz_row + t0 + col,
                               from_f32<T>(dout[s] * ypre * sz * (1.0f + zz[s] * (1.0f - sz))));
-            } else {
-                dy = dout[s];
             }
             if (t0 + col < L) dD_acc = __builtin_fmaf(dy, uu[s], dD_acc);
 
             // ---- backward over the block, 8 steps at a time ----
+            // The walk broadcasts delta and delta*u again instead of reusing
+            // the recompute's broadcasts (which would keep 32 values live
+            // across it and cost the recompute its folded DPP multiplies):
+            // an empty asm makes its copies distinct values to the compiler.
+            float dlw = dl[s], dluw = dlu[s];
+            __asm__("" : "+v"(dlw), "+v"(dluw));
             float sumA = 0.0f, sumB = 0.0f;
 #pragma unroll
             for (int hh = 1; hh >= 0; hh--) {
@@ -453,8 +462,8 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
 #define SS_BC(J)                   \
     case J:                        \
         dyj = row_bcast<J>(dy);      \
-        dj = row_bcast<J>(dl[s]);    \
-        dluj = row_bcast<J>(dlu[s]); \
+        dj = row_bcast<J>(dlw);      \
+        dluj = row_bcast<J>(dluw);   \
         break;
                         SS_BC(0) SS_BC(1) SS_BC(2) SS_BC(3) SS_BC(4) SS_BC(5) SS_BC(6) SS_BC(7)
                         SS_BC(8) SS_BC(9) SS_BC(10) SS_BC(11) SS_BC(12) SS_BC(13) SS_BC(14)
