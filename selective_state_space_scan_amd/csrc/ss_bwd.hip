@@ -457,28 +457,28 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                 for (int jj = 7; jj >= 0; jj--) {
                     const int j = 8 * hh + jj;
                     const int t = 16 * s + j;
-                    float dyj, dj, dluj;
+                    const float hprev = j > 0 ? hs[j - 1] : hstart;
+                    float gc, gp, xv, yv;
+                    // g_t = C_t dy_t + abar_{t+1} g_{t+1}; gc = abar_t g_t is
+                    // carried to t - 1 and gp = g_t abar_t h_{t-1}; xv and yv
+                    // are this lane's terms of the channel sums dB and dC
                     switch (j) {
-#define SS_BC(J)                   \
-    case J:                        \
-        dyj = row_bcast<J>(dy);      \
-        dj = row_bcast<J>(dlw);      \
-        dluj = row_bcast<J>(dluw);   \
+#define SS_BC(J)                                          \
+    case J:                                               \
+        g = fmac_bcast<J>(g, dy, sC[n][t]);               \
+        gc = ab[j] * g;                                   \
+        gp = gc * hprev;                                  \
+        dA_acc = fmac_bcast<J>(dA_acc, dlw, gp);          \
+        xv = g * row_bcast<J>(dluw);                      \
+        yv = hs[j] * row_bcast<J>(dy);                    \
         break;
                         SS_BC(0) SS_BC(1) SS_BC(2) SS_BC(3) SS_BC(4) SS_BC(5) SS_BC(6) SS_BC(7)
                         SS_BC(8) SS_BC(9) SS_BC(10) SS_BC(11) SS_BC(12) SS_BC(13) SS_BC(14)
                         SS_BC(15)
 #undef SS_BC
                     }
-                    g = __builtin_fmaf(sC[n][t], dyj, g);                 // g_t
-                    const float hprev = j > 0 ? hs[j - 1] : hstart;
-                    const float gp = g * (ab[j] * hprev);
-                    dA_acc = __builtin_fmaf(gp, dj, dA_acc);
                     qa[jj] = aval * gp;
                     qb[jj] = g * sB[n][t];
-                    // per-lane terms of the channel sums dB[n,t] and dC[n,t]
-                    const float xv = g * dluj;
-                    const float yv = hs[j] * dyj;
                     if (jj & 1) {
                         xo = xv;
                         yo = yv;
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                         const float po = rows_pair_sum(xo, yo);
                         chw[t * SM::kChStep] = rows_quad_sum(pe, po);
                     }
-                    g = ab[j] * g;                                        // carried to t - 1
+                    g = gc;
                 }
                 // sums over the 16 states: lane n < 8 gets A*g*abar*h of step
                 // 8 hh + n, lane n >= 8 g*B of step 8 hh + n - 8

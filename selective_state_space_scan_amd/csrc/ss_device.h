@@ -70,6 +70,34 @@ __device__ __forceinline__ float row_bcast(float v) {
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + LANE, 0xf, 0xf, true));
 }
 
+// acc + (lane LANE of x's DPP row) * y as a single v_fmac_f32 with a row
+// broadcast on x; the compiler folds broadcasts into multiplies and adds but
+// not into fmac.  A DPP read of a VGPR needs two wait states after the VALU
+// op that wrote it; the s_nop in the same asm block provides them whatever
+// instruction the compiler scheduled in front.
+// The lane is spelled into the asm text: an immediate operand would make
+// the compiler treat the statement as a possible memory access and keep LDS
+// loads from moving across it.
+template <int LANE>
+__device__ __forceinline__ float fmac_bcast(float acc, float x, float y) {
+    static_assert(LANE >= 0 && LANE < 16, "lane within a DPP row");
+    switch (LANE) {
+#define SS_FMAC_BCAST(L)                                                                        \
+    case L:                                                                                     \
+        __asm__("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #L                         \
+                " row_mask:0xf bank_mask:0xf"                                                   \
+                : "+v"(acc)                                                                     \
+                : "v"(x), "v"(y));                                                              \
+        break;
+        SS_FMAC_BCAST(0) SS_FMAC_BCAST(1) SS_FMAC_BCAST(2) SS_FMAC_BCAST(3)
+        SS_FMAC_BCAST(4) SS_FMAC_BCAST(5) SS_FMAC_BCAST(6) SS_FMAC_BCAST(7)
+        SS_FMAC_BCAST(8) SS_FMAC_BCAST(9) SS_FMAC_BCAST(10) SS_FMAC_BCAST(11)
+        SS_FMAC_BCAST(12) SS_FMAC_BCAST(13) SS_FMAC_BCAST(14) SS_FMAC_BCAST(15)
+#undef SS_FMAC_BCAST
+    }
+    return acc;
+}
+
 // DPP lane permutations within a 16-lane row (one VALU op each, or folded
 // into the add that consumes them): lane n reads lane n ^ 15 (row_mirror),
 // n ^ 7 (row_half_mirror), n ^ 2 and n ^ 1 (quad_perm).
@@ -91,6 +119,53 @@ __device__ __forceinline__ void fold_level(const float *x, float *out, bool low)
         out[i] = keep + dpp_lane<CTRL>(send);
     }
 }
+
+// The first two butterfly levels select by lane bit 3 and bit 2, which are
+// the bits of the 4-lane bank within the row.  A DPP op does not write the
+// lanes of the banks its bank_mask leaves out, so each fold is two DPP adds
+// (one per kept half) and needs no select.  The sums are the same as
+// fold_level's (own + partner and partner + own are the same float).  One
+// s_nop 1 in front of each block gives the two wait states a DPP read needs
+// after the VALU op that wrote its source; within a block no DPP op reads a
+// register the block wrote fewer than two instructions earlier.  (The
+// compiler writes EXEC only with scalar instructions on this target, so the
+// longer wait after a VALU write of EXEC does not arise.)
+#define SS_FOLD2(CTRL, O, A, B, MA, MB)                                  \
+    "v_add_f32_dpp %[" #O "], %[" #A "], %[" #A "] " CTRL " row_mask:0xf bank_mask:" MA "\n\t" \
+    "v_add_f32_dpp %[" #O "], %[" #B "], %[" #B "] " CTRL " row_mask:0xf bank_mask:" MB "\n\t"
+
+// level n ^ 15: banks 0, 1 keep lo, banks 2, 3 keep hi
+__device__ __forceinline__ void fold_banks_mirror(const float (&lo)[8], const float (&hi)[8],
+                                                  float (&out)[8]) {
+    __asm__("s_nop 1\n\t"
+            SS_FOLD2("row_mirror", o0, l0, h0, "0x3", "0xc")
+            SS_FOLD2("row_mirror", o1, l1, h1, "0x3", "0xc")
+            SS_FOLD2("row_mirror", o2, l2, h2, "0x3", "0xc")
+            SS_FOLD2("row_mirror", o3, l3, h3, "0x3", "0xc")
+            SS_FOLD2("row_mirror", o4, l4, h4, "0x3", "0xc")
+            SS_FOLD2("row_mirror", o5, l5, h5, "0x3", "0xc")
+            SS_FOLD2("row_mirror", o6, l6, h6, "0x3", "0xc")
+            SS_FOLD2("row_mirror", o7, l7, h7, "0x3", "0xc")
+            : [o0] "=&v"(out[0]), [o1] "=&v"(out[1]), [o2] "=&v"(out[2]), [o3] "=&v"(out[3]),
+              [o4] "=&v"(out[4]), [o5] "=&v"(out[5]), [o6] "=&v"(out[6]), [o7] "=&v"(out[7])
+            : [l0] "v"(lo[0]), [l1] "v"(lo[1]), [l2] "v"(lo[2]), [l3] "v"(lo[3]),
+              [l4] "v"(lo[4]), [l5] "v"(lo[5]), [l6] "v"(lo[6]), [l7] "v"(lo[7]),
+              [h0] "v"(hi[0]), [h1] "v"(hi[1]), [h2] "v"(hi[2]), [h3] "v"(hi[3]),
+              [h4] "v"(hi[4]), [h5] "v"(hi[5]), [h6] "v"(hi[6]), [h7] "v"(hi[7]));
+}
+
+// level n ^ 7: banks 0, 2 keep x[0..3], banks 1, 3 keep x[4..7]
+__device__ __forceinline__ void fold_banks_half_mirror(const float (&x)[8], float (&out)[4]) {
+    __asm__("s_nop 1\n\t"
+            SS_FOLD2("row_half_mirror", o0, a0, b0, "0x5", "0xa")
+            SS_FOLD2("row_half_mirror", o1, a1, b1, "0x5", "0xa")
+            SS_FOLD2("row_half_mirror", o2, a2, b2, "0x5", "0xa")
+            SS_FOLD2("row_half_mirror", o3, a3, b3, "0x5", "0xa")
+            : [o0] "=&v"(out[0]), [o1] "=&v"(out[1]), [o2] "=&v"(out[2]), [o3] "=&v"(out[3])
+            : [a0] "v"(x[0]), [a1] "v"(x[1]), [a2] "v"(x[2]), [a3] "v"(x[3]),
+              [b0] "v"(x[4]), [b1] "v"(x[5]), [b2] "v"(x[6]), [b3] "v"(x[7]));
+}
+#undef SS_FOLD2
 
 // The same sum as row_transpose_sum, for a lane that already holds the 16
 // terms (x[k] = term of lane k): the butterfly's grouping depends only on the
@@ -114,14 +189,9 @@ __device__ __forceinline__ float row_tree_sum(const float (&x)[16]) {
 // by the lane index.
 __device__ __forceinline__ float row_transpose_sum(const float (&lo)[8], const float (&hi)[8],
                                                    int n) {
-    float x16[16], x8[8], x4[4], x2[2], x1[1];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        x16[i] = lo[i];
-        x16[8 + i] = hi[i];
-    }
-    fold_level<0x140, 8>(x16, x8, n < 8);          // row_mirror: n ^ 15
-    fold_level<0x141, 4>(x8, x4, (n & 7) < 4);     // row_half_mirror: n ^ 7
+    float x8[8], x4[4], x2[2], x1[1];
+    fold_banks_mirror(lo, hi, x8);                  // row_mirror: n ^ 15
+    fold_banks_half_mirror(x8, x4);                 // row_half_mirror: n ^ 7
     fold_level<0x4E, 2>(x4, x2, (n & 3) < 2);      // quad_perm [2,3,0,1]: n ^ 2
     fold_level<0xB1, 1>(x2, x1, (n & 1) == 0);     // quad_perm [1,0,3,2]: n ^ 1
     return x1[0];
