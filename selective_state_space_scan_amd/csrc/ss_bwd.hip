@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     const int64_t nch = (L + kC - 1) / kC;     // 32-step staging chunks
     const float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
     // state entering block k; a block past the end (only padding steps) has none
-    auto ckpt_at = [&](int64_t k) { return (row_ok && k < nck) ? ck[k * kN] : 0.0f; };
+    auto ckpt_at = [&](int64_t k) { return (row_ok && k >= 0 && k < nck) ? ck[k * kN] : 0.0f; };
 
     float g = (row_ok && p.dlast) ? p.dlast[(b * Dm + d) * kN + n] : 0.0f;
     float dA_acc = 0.0f;     // this lane's state entry, summed over time
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     // the saved pre-gate output: each owner lane loads its elements straight
     // from global memory, a chunk ahead (a row's 16 lanes read 16 floats)
     const float *yprow = (YP && row_ok) ? ws.ypre + myrow : nullptr;
-    auto ypre_at = [&](int64_t t) { return (yprow && t < L) ? ld_global(yprow + t) : 0.0f; };
+    auto ypre_at = [&](int64_t t) { return (yprow && t >= 0 && t < L) ? ld_global(yprow + t) : 0.0f; };
     ChunkStager<T, VEC, kC, 6, kThreads> st;
     st.init(
         [&](int i) -> TileSrc<T> {
@@ -342,11 +342,14 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     // The checkpoints of the next chunk are loaded one chunk ahead and before
     // the prefetch: loads retire in order, so a load issued after the
     // prefetch would make its use wait for the prefetch.
-    float hn[kNB], ypn[kNB];
+    // (with seqlen 0 there is no chunk and nothing is loaded)
+    float hn[kNB] = {}, ypn[kNB] = {};
+    if (nch > 0) {
 #pragma unroll
-    for (int s = 0; s < kNB; s++) {
-        hn[s] = ckpt_at(kNB * (nch - 1) + s);
-        if (YP) ypn[s] = ypre_at((nch - 1) * kC + 16 * s + n);
+        for (int s = 0; s < kNB; s++) {
+            hn[s] = ckpt_at(kNB * (nch - 1) + s);
+            if (YP) ypn[s] = ypre_at((nch - 1) * kC + 16 * s + n);
+        }
     }
     for (int64_t c = nch - 1; c >= 0; c--) {
         const int64_t t0 = c * kC;
