@@ -97,7 +97,8 @@ size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
  *   io_dtype          SS_F32 or SS_BF16: dtype of u, delta, B, C, z, out.
  *   D, z, delta_bias, h0, last_state may be NULL.
  *   batch, dim, seqlen >= 0; a zero size enqueues nothing but the
- *   last_state copy/zero fill it implies.
+ *   last_state copy/zero fill it implies.  seqlen <= 2^26, batch <= 65535,
+ *   dim <= 2^30 (SS_EUNSUPPORTED beyond; the same limits hold for ss_bwd).
  *   All pointers 16-byte aligned.
  */
 ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,

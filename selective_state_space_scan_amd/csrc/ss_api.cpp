@@ -34,10 +34,11 @@ ss_status ok() {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Largest extents: batch and channel groups are 32-bit grid coordinates,
-// and the kernels address 16-row tiles with 32-bit element offsets.
+// and the kernels address a 16-row tile (16 x seqlen elements of up to
+// 4 bytes) with 32-bit byte offsets from a scalar base.
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t kMaxDim = int64_t(1) << 30;
-constexpr int64_t kMaxSeq = int64_t(1) << 28;
+constexpr int64_t kMaxSeq = int64_t(1) << 26;
 
 struct Check {
     ss_status st = SS_OK;

@@ -289,9 +289,17 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
     const int64_t nck = (L + kCk - 1) / kCk;   // checkpoints (16-step blocks)
     const int64_t nch = (L + kC - 1) / kC;     // 32-step staging chunks
-    const float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
+    // Inside the chunk loop indices are 32-bit (seqlen <= 2^26), and global
+    // accesses address the group's 16 rows from a scalar base with 32-bit
+    // byte offsets (16 rows x seqlen x 4 bytes < 2^32).
+    const int Ls = int(L), nckS = int(nck);
+    const float *ckb = ws.ckpt + (b * Dm + d0) * nck * kN;
+    const uint32_t ckoff = uint32_t((r * nckS * kN + n) * 4);
     // state entering block k; a block past the end (only padding steps) has none
-    auto ckpt_at = [&](int64_t k) { return (row_ok && k >= 0 && k < nck) ? ck[k * kN] : 0.0f; };
+    auto ckpt_at = [&](int k) {
+        return (row_ok && k >= 0 && k < nckS) ? ld_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)))
+                                              : 0.0f;
+    };
 
     float g = (row_ok && p.dlast) ? p.dlast[(b * Dm + d) * kN + n] : 0.0f;
     float dA_acc = 0.0f;     // this lane's state entry, summed over time
@@ -307,14 +315,18 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     const T *gdo = static_cast<const T *>(p.dout) + rowbase;
     // this lane's row of the element-wise gradients; a row's 16 lanes store
     // 16 consecutive elements of a 16-step block
-    const int64_t myrow = (b * Dm + (row_ok ? d : d0)) * L;
-    T *du_row = static_cast<T *>(p.du) + myrow;
-    T *dd_row = static_cast<T *>(p.ddelta) + myrow;
-    T *dz_row = has_z ? static_cast<T *>(p.dz) + myrow : nullptr;
+    T *du_b = static_cast<T *>(p.du) + rowbase;
+    T *dd_b = static_cast<T *>(p.ddelta) + rowbase;
+    T *dz_b = has_z ? static_cast<T *>(p.dz) + rowbase : nullptr;
+    const int rowel = r * Ls;   // this lane's row, in elements from the group's first
+    auto elem_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(T)); };
     // the saved pre-gate output: each owner lane loads its elements straight
     // from global memory, a chunk ahead (a row's 16 lanes read 16 floats)
-    const float *yprow = (YP && row_ok) ? ws.ypre + myrow : nullptr;
-    auto ypre_at = [&](int64_t t) { return (yprow && t >= 0 && t < L) ? ld_global(yprow + t) : 0.0f; };
+    const float *ypb = ws.ypre + rowbase;
+    auto ypre_at = [&](int t) {
+        return (YP && row_ok && t >= 0 && t < Ls) ? ld_global(at_bytes(ypb, uint32_t(rowel + t) * 4u))
+                                                  : 0.0f;
+    };
     ChunkStager<T, VEC, kC, 6, kThreads> st;
     st.init(
         [&](int i) -> TileSrc<T> {
@@ -347,12 +359,12 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     if (nch > 0) {
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
-            hn[s] = ckpt_at(kNB * (nch - 1) + s);
-            if (YP) ypn[s] = ypre_at((nch - 1) * kC + 16 * s + n);
+            hn[s] = ckpt_at(kNB * (int(nch) - 1) + s);
+            if (YP) ypn[s] = ypre_at((int(nch) - 1) * kC + 16 * s + n);
         }
     }
-    for (int64_t c = nch - 1; c >= 0; c--) {
-        const int64_t t0 = c * kC;
+    for (int c = int(nch) - 1; c >= 0; c--) {
+        const int t0 = c * kC;
         float hb[kNB], yp[kNB];
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                 x = softplus_f32(raw);
                 sgd[s] = sigmoid_f32(raw);
             }
-            dl[s] = (t0 + col < L) ? x : 0.0f;   // padding steps: no decay, no input
+            dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps: no decay, no input
             uu[s] = to_f32<T>(sU[r][col]);
             dlu[s] = dl[s] * uu[s];
             dout[s] = to_f32<T>(sG[r][col]);
@@ -392,8 +404,8 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
             if (has_z) {
                 const float sz = sigmoid_f32(zz[s]);
                 dyv[s] = dout[s] * zz[s] * sz;
-                if (YP && row_ok && t0 + col < L)
-                    st_global(dz_row + t0 + col,
+                if (YP && row_ok && t0 + col < Ls)
+                    st_global(at_bytes(dz_b, elem_off(t0 + col)),
                               from_f32<T>(dout[s] * yp[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
             }
         }
@@ -438,11 +450,11 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                                                      reinterpret_cast<const float(&)[8]>(v[8]), n) +
                                    dskip * uu[s];
                 const float sz = sigmoid_f32(zz[s]);
-                if (row_ok && t0 + col < L)
-                    st_global(dz_row + t0 + col,
+                if (row_ok && t0 + col < Ls)
+                    st_global(at_bytes(dz_b, elem_off(t0 + col)),
                               from_f32<T>(dout[s] * ypre * sz * (1.0f + zz[s] * (1.0f - sz))));
             }
-            if (t0 + col < L) dD_acc = __builtin_fmaf(dy, uu[s], dD_acc);
+            if (t0 + col < Ls) dD_acc = __builtin_fmaf(dy, uu[s], dD_acc);
 
             // ---- backward over the block, 8 steps at a time ----
             // The walk broadcasts delta and delta*u again instead of reusing
@@ -502,11 +514,11 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
             }
             const float du = __builtin_fmaf(dl[s], sumB, dskip * dy);
             const float dd = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];
-            if (row_ok && t0 + col < L) {
-                st_global(du_row + t0 + col, from_f32<T>(du));
-                st_global(dd_row + t0 + col, from_f32<T>(dd));
+            if (row_ok && t0 + col < Ls) {
+                st_global(at_bytes(du_b, elem_off(t0 + col)), from_f32<T>(du));
+                st_global(at_bytes(dd_b, elem_off(t0 + col)), from_f32<T>(dd));
             }
-            if (t0 + col < L) dbias_acc += dd;
+            if (t0 + col < Ls) dbias_acc += dd;
         }
         __syncthreads();
 
@@ -514,7 +526,8 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
         // steps kE ct .. kE ct + kE - 1), wavefronts in ascending order
         {
             constexpr int kE = kC / 8;
-            const int cq = tid >> 7, cn = (tid >> 3) & 15, ct = tid & 7;
+            const int cq = __builtin_amdgcn_readfirstlane(tid >> 7);   // uniform per wavefront
+            const int cn = (tid >> 3) & 15, ct = tid & 7;
             float acc[kE];
 #pragma unroll
             for (int e = 0; e < kE; e++) {
@@ -523,8 +536,9 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
 #pragma unroll
                 for (int w = 1; w < 4; w++) acc[e] += cs[w * SM::kChWave];
             }
-            float *dst = (cq ? ws.dCp : ws.dBp) + ((b * groups + group) * kN + cn) * L + t0 + kE * ct;
-            if ((L % kE) == 0 && t0 + kE * ct + kE <= L) {
+            float *dst = at_bytes((cq ? ws.dCp : ws.dBp) + (b * groups + group) * kN * L,
+                                  uint32_t(cn * Ls + t0 + kE * ct) * 4u);
+            if ((Ls % kE) == 0 && t0 + kE * ct + kE <= Ls) {
                 if constexpr (kE == 4)
                     *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
                 else
@@ -532,7 +546,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
             } else {
 #pragma unroll
                 for (int e = 0; e < kE; e++)
-                    if (t0 + kE * ct + e < L) dst[e] = acc[e];
+                    if (t0 + kE * ct + e < Ls) dst[e] = acc[e];
             }
         }
         // unconditional, so no prefetch is in flight across the loop's back

@@ -41,6 +41,18 @@ __device__ __forceinline__ void st_global(T *p, T v) {
     *(__attribute__((address_space(1))) T *)(p) = v;
 }
 
+// Address = base + a 32-bit byte offset.  With a base that is uniform
+// across the wavefront (scalar registers), the compiler uses the scalar-base
+// form of the global instructions and needs no 64-bit vector address math.
+template <typename T>
+__device__ __forceinline__ const T *at_bytes(const T *base, uint32_t off) {
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ T *at_bytes(T *base, uint32_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
+}
+
 // One tile of a chunk.
 template <typename T>
 struct TileSrc {

@@ -84,6 +84,7 @@ def test_fwd_misaligned_pointer(lib, arg):
     (dict(seqlen=-1), EINVAL, "seqlen"), (dict(dstate=0), EINVAL, "dstate"),
     (dict(dstate=8), EUNSUP, "dstate"), (dict(dstate=64), EUNSUP, "dstate"),
     (dict(io=7), EINVAL, "io_dtype"), (dict(batch=70000), EUNSUP, "batch"),
+    (dict(seqlen=(1 << 26) + 1), EUNSUP, "seqlen"),
 ])
 def test_fwd_bad_sizes(lib, kw, status, word):
     assert _fwd(lib, **kw) == status
