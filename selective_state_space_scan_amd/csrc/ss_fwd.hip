@@ -62,7 +62,7 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
 }
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : 4) void ss_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) void ss_fwd_kernel(FwdParams p) {
     using SM = FwdSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
     float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + SM::kB);
@@ -116,15 +116,23 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : 4) void ss_fwd_kernel(FwdP
     }
     __syncthreads();
 
+    // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the
+    // stores address the group's 16 rows from a scalar base with 32-bit byte
+    // offsets (16 rows x seqlen x 4 bytes < 2^32).
+    const int Ls = int(L);
     const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
-    float *ck = (p.ckpt && row_ok) ? p.ckpt + (b * Dm + d) * nck * kN + n : nullptr;
+    const int nckS = int(nck);
+    const bool save_ck = p.ckpt != nullptr;
+    float *ckb = save_ck ? p.ckpt + (b * Dm + d0) * nck * kN : nullptr;
+    const uint32_t ckoff = uint32_t((r * nckS * kN + n) * 4);
     float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
-    const int64_t myrow = (b * Dm + (row_ok ? d : d0)) * L;
-    T *yrow = static_cast<T *>(p.out) + myrow;
+    T *yb = static_cast<T *>(p.out) + (b * Dm + d0) * L;
     // the pre-gate output, saved for the backward's dz
-    float *yprow = (p.ypre && has_z) ? p.ypre + myrow : nullptr;
-    for (int64_t c = 0; c < nchunks; c++) {
-        const int64_t t0 = c * kT;
+    const bool save_yp = p.ypre && has_z;
+    float *ypb = save_yp ? p.ypre + (b * Dm + d0) * L : nullptr;
+    const int rowel = r * Ls;   // this lane's row, in elements from the group's first
+    for (int c = 0; c < int(nchunks); c++) {
+        const int t0 = c * kT;
         if (c + 1 < nchunks) st.fetch(t0 + kT, L, tid);
 
         // per-element work: lane (r, n) owns elements 16 s + n of its row
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : 4) void ss_fwd_kernel(FwdP
             zz[s] = to_f32<T>(sZ[r][col]);
             float x = to_f32<T>(sDl[r][col]) + bias;
             if (p.softplus) x = softplus_f32(x);
-            dl[s] = (t0 + col < L) ? x : 0.0f;   // padding steps leave the state unchanged
+            dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps leave the state unchanged
             dlu[s] = dl[s] * uu[s];
         }
         __syncthreads();  // the transpose region aliases u / delta / z
@@ -153,17 +161,17 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : 4) void ss_fwd_kernel(FwdP
             float y = ypre;
             if (has_z) y *= zz[s] * sigmoid_f32(zz[s]);
             // a row's 16 lanes store 16 consecutive outputs
-            const int64_t t = t0 + 16 * s + n;
-            if (row_ok && t < L) {
-                st_global(yrow + t, from_f32<T>(y));
-                if (yprow) st_global(yprow + t, ypre);
+            const int t = t0 + 16 * s + n;
+            if (row_ok && t < Ls) {
+                st_global(at_bytes(yb, uint32_t(rowel + t) * uint32_t(sizeof(T))), from_f32<T>(y));
+                if (save_yp) st_global(at_bytes(ypb, uint32_t(rowel + t) * 4u), ypre);
             }
         };
 #pragma unroll
         for (int s = 0; s < kT / 16; s++) {
-            if (ck && (16 * s) % kCkptSpacing == 0) {   // state entering a checkpoint chunk
-                const int64_t k = (t0 + 16 * s) / kCkptSpacing;
-                if (k < nck) ck[k * kN] = h;
+            if (save_ck && (16 * s) % kCkptSpacing == 0) {   // state entering a checkpoint chunk
+                const int k = (t0 + 16 * s) / kCkptSpacing;
+                if (row_ok && k < nckS) st_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)), h);
             }
             float4 bq[4], cq[4];
 #pragma unroll
