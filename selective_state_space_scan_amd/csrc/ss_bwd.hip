@@ -392,9 +392,12 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                 x = softplus_f32(raw);
                 sgd[s] = sigmoid_f32(raw);
             }
-            dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps: no decay, no input
+            // padding steps: no decay, no input.  Rows past the last channel
+            // read unloaded tile words; zeroing delta, delta*u and dy keeps
+            // their g and h at zero, so they add nothing to the channel sums.
+            dl[s] = (row_ok && t0 + col < Ls) ? x : 0.0f;
             uu[s] = to_f32<T>(sU[r][col]);
-            dlu[s] = dl[s] * uu[s];
+            dlu[s] = row_ok ? dl[s] * uu[s] : 0.0f;
             dout[s] = to_f32<T>(sG[r][col]);
             zz[s] = to_f32<T>(sZ[r][col]);
             // gradient reaching the pre-gate output; with the saved pre-gate
@@ -408,6 +411,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
                     st_global(at_bytes(dz_b, elem_off(t0 + col)),
                               from_f32<T>(dout[s] * yp[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
             }
+            if (!row_ok) dyv[s] = 0.0f;
         }
 
         // blocks last to first: recompute the block's 16 forward steps from

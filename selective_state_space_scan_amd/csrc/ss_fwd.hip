@@ -86,9 +86,9 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) 
     const int valid_rows = static_cast<int>(Dm - d0 < kRows ? Dm - d0 : kRows);
     const bool has_z = p.z != nullptr;
 
-    const float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;  // A in base-2 exponent units
-    const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
-    const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
+    float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;  // A in base-2 exponent units
+    float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
+    float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
     float h = (row_ok && p.h0) ? p.h0[(b * Dm + d) * kN + n] : 0.0f;
 
     const T *gu = static_cast<const T *>(p.u) + (b * Dm + d0) * L;
@@ -114,6 +114,10 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) 
         st.fetch(0, L, tid);
         st.stash(smem);
     }
+    // Make the per-row parameter loads complete here.  Left pending into the
+    // chunk loop, their first use there would be a wait on the in-order
+    // memory counter that also drains the chunk prefetch.
+    __asm__("" : "+v"(a2), "+v"(bias), "+v"(dskip), "+v"(h));
     __syncthreads();
 
     // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the

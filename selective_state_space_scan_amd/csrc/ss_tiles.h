@@ -74,23 +74,30 @@ struct ChunkStager {
     // tiles of whole wavefronts of slots keep the tile index (and so its
     // descriptor) uniform across a wavefront
     static constexpr bool kUniformTile = kVecPerTile % 64 == 0;
+    static_assert(kSlots <= 32, "slot flags fit one 32-bit mask");
 
     // Per slot: the tile's base (uniform across the wavefront when
     // kUniformTile, so in scalar registers) and 32-bit per-lane offsets.
-    const T *base[kSlots];  // element (row 0, t = 0) of the slot's tile; nullptr = zeros / none
-    uint32_t goff[kSlots];  // the lane's element offset in the tile (row * stride + col),
-                            // kNoRow for rows past the last valid one (read as zeros)
+    // A slot of an absent tile or of a row past the last valid one is not
+    // live: it still loads (from row 0 of tile 0 or of its own tile, which
+    // always exist, so a full chunk's loads need no branch) but its words are
+    // garbage; the ragged chunk reads zeros for it.  Kernels never read an
+    // absent tile and give rows past the last valid one no part in any sum
+    // across rows.
+    const T *base[kSlots];  // element (row 0, t = 0) of the tile the slot loads from
+    uint32_t goff[kSlots];  // the lane's element offset in that tile (row * stride + col)
     uint32_t dst[kSlots];   // LDS byte offset
     bool f32[kSlots];       // stash as f32 (else as T); uniform
     bool used[kSlots];      // slot maps to a tile; uniform
+    uint32_t live = 0;      // bit k: slot k's words are real data
     uint32_t reg[kSlots][kWords];
-    static constexpr uint32_t kNoRow = ~0u;
 
     __device__ static int slot_col(int tid, int k) {
         return ((tid + k * NTHREADS) % kVecPerRow) * VEC;
     }
 
-    // `desc(i)` returns the TileSrc of tile i (called with constant i only).
+    // `desc(i)` returns the TileSrc of tile i (called with constant i only);
+    // tile 0 must be present.
     template <typename Desc>
     __device__ __forceinline__ void init(Desc desc, int tid) {
 #pragma unroll
@@ -101,8 +108,8 @@ struct ChunkStager {
             const int rem = slot % kVecPerTile;
             const int row = rem / kVecPerRow;
             const int col = (rem % kVecPerRow) * VEC;
-            base[k] = nullptr;
-            goff[k] = kNoRow;
+            base[k] = desc(0).base;
+            goff[k] = uint32_t(col);
             dst[k] = 0;
             f32[k] = false;
             used[k] = tile < NTILES;
@@ -111,8 +118,11 @@ struct ChunkStager {
 #pragma unroll
                 for (int i = 1; i < NTILES; i++)
                     if (tile == i) ts = desc(i);
-                base[k] = ts.base;
-                if (row < ts.valid_rows) goff[k] = uint32_t(row * ts.row_stride + col);
+                if (ts.base && row < ts.valid_rows) live |= 1u << k;
+                if (ts.base) {
+                    base[k] = ts.base;
+                    goff[k] = uint32_t((row < ts.valid_rows ? row : 0) * ts.row_stride + col);
+                }
                 f32[k] = ts.to_f32;
                 const uint32_t esz = ts.to_f32 ? 4u : uint32_t(sizeof(T));
                 dst[k] = ts.lds_off + uint32_t(row * ts.pitch + col) * esz;
@@ -121,19 +131,19 @@ struct ChunkStager {
     }
 
     // Issues the loads of a full chunk that starts at t0 (t0 + KT <= L).
+    // Every slot loads, from a valid address (unused slots from tile 0), so
+    // the loads need no branch.
     __device__ __forceinline__ void fetch_full(int64_t t0) {
 #pragma unroll
         for (int k = 0; k < kSlots; k++) {
-            const bool on = base[k] && goff[k] != kNoRow;
             if constexpr (VEC * sizeof(T) == 16) {
-                u32x4 r = {0u, 0u, 0u, 0u};
-                if (on) r = ld_global16(base[k] + t0 + goff[k]);
+                const u32x4 r = ld_global16(base[k] + t0 + goff[k]);
                 reg[k][0] = r.x;
                 reg[k][1] = r.y;
                 reg[k][2] = r.z;
                 reg[k][3] = r.w;
             } else {
-                T v = on ? ld_global(base[k] + t0 + goff[k]) : T(0);
+                const T v = ld_global(base[k] + t0 + goff[k]);
                 uint32_t tmp = 0;
                 __builtin_memcpy(&tmp, &v, sizeof(T));
                 reg[k][0] = tmp;
@@ -145,7 +155,7 @@ struct ChunkStager {
     __device__ __forceinline__ void fetch_tail(int64_t t0, int64_t L, int tid) {
 #pragma unroll
         for (int k = 0; k < kSlots; k++) {
-            const bool on = base[k] && goff[k] != kNoRow;
+            const bool on = (live >> k) & 1u;
             const int col = slot_col(tid, k);
             T v[VEC];
 #pragma unroll
