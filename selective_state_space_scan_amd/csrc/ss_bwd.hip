@@ -36,6 +36,8 @@
 //      order and the dA/dD/dbias partials over the batch in ascending batch
 //      order.
 // Every sum runs in an order fixed by the shape, with no atomics.
+#include <atomic>
+
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_tiles.h"
@@ -57,8 +59,9 @@ constexpr int kThreads = 256;
 struct Workspace {
     float *ckpt;     // (batch, dim, nck, 16): state entering each 16-step block
     const float *ypre;  // pre-gate output saved by the forward, or nullptr
-    float *dBp;      // (batch, groups, 16, L)
+    float *dBp;      // (batch, groups, 16, L); sized for 16-channel groups
     float *dCp;      // (batch, groups, 16, L)
+    int64_t groups;  // channel groups of the reverse pass that wrote them
     float *dAp;      // (batch, dim, 16)
     float *dDp;      // (batch, dim)
     float *dbiasp;   // (batch, dim)
@@ -82,6 +85,7 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
     w.ypre = nullptr;
     w.dBp = take(size_t(batch) * groups * kN * L);
     w.dCp = take(size_t(batch) * groups * kN * L);
+    w.groups = groups;
     w.dAp = take(size_t(batch) * dim * kN);
     w.dDp = take(size_t(batch) * dim);
     w.dbiasp = take(size_t(batch) * dim);
@@ -241,30 +245,43 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
 // ---------------------------------------------------------------------------
 constexpr int kPitch2 = kC + 4;
 
-template <typename T>
+// NW wavefronts, 4 NW channels per workgroup.
+template <typename T, int NW>
 struct RevSmem {
+    static constexpr int kR = 4 * NW;                                 // channels
     static constexpr uint32_t kB = 0;
     static constexpr uint32_t kCc = kB + kN * kPitch2 * 4;
     static constexpr uint32_t kU = kCc + kN * kPitch2 * 4;          // raw u / delta / z / dout
-    static constexpr uint32_t kDl = kU + kRows * kC * sizeof(T);
-    static constexpr uint32_t kZ = kDl + kRows * kC * sizeof(T);
-    static constexpr uint32_t kG = kZ + kRows * kC * sizeof(T);
-    static constexpr uint32_t kRawEnd = kG + kRows * kC * sizeof(T);
-    // 4-row channel sums: [wave 4][step kC][quantity 2 x state 16 + pad].
-    // The summing threads of a wavefront read 8 steps kC / 8 apart x 8
-    // states; a step pitch P with (kC / 8) P = 8 (mod 64) puts them in 64
-    // distinct banks.
+    static constexpr uint32_t kDl = kU + kR * kC * sizeof(T);
+    static constexpr uint32_t kZ = kDl + kR * kC * sizeof(T);
+    static constexpr uint32_t kG = kZ + kR * kC * sizeof(T);
+    static constexpr uint32_t kRawEnd = kG + kR * kC * sizeof(T);
+    // 4-row channel sums, two chunks' worth (a chunk's are added up during
+    // the next chunk): [chunk 2][wave NW][step kC][quantity 2 x state 16 + pad].
+    // At the end of a chunk thread (quantity, state, step group) adds kE
+    // consecutive steps over the wavefronts: 2 steps per thread when the
+    // workgroup has the threads for it, else 4.  A wavefront's threads read
+    // 16 (or 8) step groups x 4 (or 8) states, and the step pitch puts them
+    // in 64 distinct banks.
     static constexpr uint32_t kCh = kRawEnd;
     static constexpr int kChStep = kC == 32 ? 34 : 36;
     static constexpr int kChWave = kC * kChStep;
-    static constexpr uint32_t kSize = kCh + 4 * kChWave * 4;
+    static constexpr int kChBuf = NW * kChWave;   // floats of one chunk's sums
+    static constexpr uint32_t kSize = kCh + 2 * kChBuf * 4;   // two chunks
+    static constexpr int kE = 2 * kN * kC / 2 <= 64 * NW ? 2 : 4;
+    static constexpr int kSG = kC / kE;
+    static_assert(2 * kN * kSG <= 64 * NW, "one channel-sum item per thread");
 };
 
 // YP: the forward saved the pre-gate output (and z is given), so dz reads it
 // instead of recomputing the sum of C h over the states.
-template <typename T, int VEC, bool YP>
-__global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
-    using SM = RevSmem<T>;
+// NW: wavefronts per workgroup (4 or 12; 4 NW channels).  Either way the
+// launch bound leaves 3 wavefronts per SIMD (2 for single-element loads).
+template <typename T, int VEC, bool YP, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) : 1) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
+    using SM = RevSmem<T, NW>;
+    constexpr int kRowsG = SM::kR;
+    constexpr int kThr = 64 * NW;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
     float(*sB)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kB);
     float(*sC)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kCc);
@@ -277,11 +294,13 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rw = lane >> 4, n = lane & 15, r = wave * 4 + rw;
     const int64_t L = p.seqlen, Dm = p.dim, b = blockIdx.y;
-    const int64_t d0 = int64_t(blockIdx.x) * kRows, d = d0 + r;
+    const int64_t d0 = int64_t(blockIdx.x) * kRowsG, d = d0 + r;
     const int64_t group = blockIdx.x, groups = gridDim.x;
     const bool row_ok = d < Dm;
-    const int valid_rows = int(Dm - d0 < kRows ? Dm - d0 : kRows);
+    const int valid_rows = int(Dm - d0 < kRowsG ? Dm - d0 : kRowsG);
     const bool has_z = p.z != nullptr;
+    // the wavefront's first row, uniform (scalar) across the wavefront
+    const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
     const float aval = row_ok ? p.A[d * kN + n] : 0.0f;
     const float a2 = aval * kLog2e;
@@ -290,11 +309,11 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     const int64_t nck = (L + kCk - 1) / kCk;   // checkpoints (16-step blocks)
     const int64_t nch = (L + kC - 1) / kC;     // 32-step staging chunks
     // Inside the chunk loop indices are 32-bit (seqlen <= 2^26), and global
-    // accesses address the group's 16 rows from a scalar base with 32-bit
-    // byte offsets (16 rows x seqlen x 4 bytes < 2^32).
+    // accesses address the wavefront's 4 rows from a scalar base with 32-bit
+    // byte offsets (4 rows x seqlen x 4 bytes < 2^32).
     const int Ls = int(L), nckS = int(nck);
-    const float *ckb = ws.ckpt + (b * Dm + d0) * nck * kN;
-    const uint32_t ckoff = uint32_t((r * nckS * kN + n) * 4);
+    const float *ckb = ws.ckpt + (b * Dm + dw) * nck * kN;
+    const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
     // state entering block k; a block past the end (only padding steps) has none
     auto ckpt_at = [&](int k) {
         return (row_ok && k >= 0 && k < nckS) ? ld_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)))
@@ -315,29 +334,33 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     const T *gdo = static_cast<const T *>(p.dout) + rowbase;
     // this lane's row of the element-wise gradients; a row's 16 lanes store
     // 16 consecutive elements of a 16-step block
-    T *du_b = static_cast<T *>(p.du) + rowbase;
-    T *dd_b = static_cast<T *>(p.ddelta) + rowbase;
-    T *dz_b = has_z ? static_cast<T *>(p.dz) + rowbase : nullptr;
-    const int rowel = r * Ls;   // this lane's row, in elements from the group's first
+    const int64_t wavebase = (b * Dm + dw) * L;
+    T *du_b = static_cast<T *>(p.du) + wavebase;
+    T *dd_b = static_cast<T *>(p.ddelta) + wavebase;
+    T *dz_b = has_z ? static_cast<T *>(p.dz) + wavebase : nullptr;
+    const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
     auto elem_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(T)); };
     // the saved pre-gate output: each owner lane loads its elements straight
     // from global memory, a chunk ahead (a row's 16 lanes read 16 floats)
-    const float *ypb = ws.ypre + rowbase;
+    const float *ypb = ws.ypre + wavebase;
     auto ypre_at = [&](int t) {
         return (YP && row_ok && t >= 0 && t < Ls) ? ld_global(at_bytes(ypb, uint32_t(rowel + t) * 4u))
                                                   : 0.0f;
     };
-    ChunkStager<T, VEC, kC, 6, kThreads> st;
+    // tiles: B, C, then u, delta, z, dout in 16-row pieces.  A piece with
+    // no valid row points at the group's first row (it is not read).
+    constexpr int kPieces = kRowsG / 16;
+    ChunkStager<T, VEC, kC, 2 + 4 * kPieces, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
-            switch (i) {
-                case 0: return {gB, L, kN, SM::kB, kPitch2, true};
-                case 1: return {gC, L, kN, SM::kCc, kPitch2, true};
-                case 2: return {gu, L, valid_rows, SM::kU, kC, false};
-                case 3: return {gdl, L, valid_rows, SM::kDl, kC, false};
-                case 4: return {gz, L, valid_rows, SM::kZ, kC, false};
-                default: return {gdo, L, valid_rows, SM::kG, kC, false};
-            }
+            if (i == 0) return {gB, L, kN, SM::kB, kPitch2, true};
+            if (i == 1) return {gC, L, kN, SM::kCc, kPitch2, true};
+            const int q = (i - 2) / kPieces, j = (i - 2) % kPieces;
+            const T *g = q == 0 ? gu : q == 1 ? gdl : q == 2 ? gz : gdo;
+            const uint32_t lds = q == 0 ? SM::kU : q == 1 ? SM::kDl : q == 2 ? SM::kZ : SM::kG;
+            const int vr = valid_rows - 16 * j;
+            return {(g && vr > 0) ? g + int64_t(16 * j) * L : g, L, vr > 16 ? 16 : (vr > 0 ? vr : 0),
+                    lds + uint32_t(16 * j * kC * sizeof(T)), kC, false};
         },
         tid);
 
@@ -350,7 +373,38 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
 
     // this lane's slot of the channel sums: lane (rw, n) receives state n of
     // quantity rw / 2 (0: dB, 1: dC) at the odd (rw & 1) step of a pair
-    float *chw = chan + wave * SM::kChWave + (rw & 1) * SM::kChStep + (rw >> 1) * kN + n;
+    float *chw0 = chan + wave * SM::kChWave + (rw & 1) * SM::kChStep + (rw >> 1) * kN + n;
+    // Adds up the wavefronts' channel sums of the chunk at tc (buffer cb):
+    // thread (quantity cq, state cn, steps kE ct .. kE ct + kE - 1),
+    // wavefronts in ascending order, and stores the group's partial.
+    auto chan_sums = [&](int tc, int cb) {
+        if (tid < 2 * kN * SM::kSG) {
+            constexpr int kE = SM::kE, kSG = SM::kSG;
+            const int cq = __builtin_amdgcn_readfirstlane(tid / (kN * kSG));   // uniform per wavefront
+            const int cn = (tid / kSG) % kN, ct = tid % kSG;
+            float acc[kE];
+#pragma unroll
+            for (int e = 0; e < kE; e++) {
+                const float *cs = chan + cb * SM::kChBuf + (kE * ct + e) * SM::kChStep + cq * kN + cn;
+                acc[e] = cs[0];
+#pragma unroll
+                for (int w = 1; w < NW; w++) acc[e] += cs[w * SM::kChWave];
+            }
+            float *dst = at_bytes((cq ? ws.dCp : ws.dBp) + (b * groups + group) * kN * L,
+                                  uint32_t(cn * Ls + tc + kE * ct) * 4u);
+            if ((Ls % kE) == 0 && tc + kE * ct + kE <= Ls) {
+                if constexpr (kE == 4)
+                    *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                else
+                    *reinterpret_cast<float2 *>(dst) = make_float2(acc[0], acc[1]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < kE; e++)
+                    if (tc + kE * ct + e < Ls) dst[e] = acc[e];
+            }
+        }
+    };
+
     // The checkpoints of the next chunk are loaded one chunk ahead and before
     // the prefetch: loads retire in order, so a load issued after the
     // prefetch would make its use wait for the prefetch.
@@ -365,6 +419,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
     }
     for (int c = int(nch) - 1; c >= 0; c--) {
         const int t0 = c * kC;
+        float *chw = chw0 + (c & 1) * SM::kChBuf;   // this chunk's channel-sum buffer
         float hb[kNB], yp[kNB];
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
@@ -413,6 +468,9 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
             }
             if (!row_ok) dyv[s] = 0.0f;
         }
+        // the previous (later) chunk's channel sums, complete since the last
+        // barrier and not rewritten before the next one
+        if (c < int(nch) - 1) chan_sums(t0 + kC, (c + 1) & 1);
 
         // blocks last to first: recompute the block's 16 forward steps from
         // its checkpoint (decays and states in registers), then walk them back
@@ -526,39 +584,14 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) void s
         }
         __syncthreads();
 
-        // add the 4 wavefronts' channel sums: thread (quantity cq, state cn,
-        // steps kE ct .. kE ct + kE - 1), wavefronts in ascending order
-        {
-            constexpr int kE = kC / 8;
-            const int cq = __builtin_amdgcn_readfirstlane(tid >> 7);   // uniform per wavefront
-            const int cn = (tid >> 3) & 15, ct = tid & 7;
-            float acc[kE];
-#pragma unroll
-            for (int e = 0; e < kE; e++) {
-                const float *cs = chan + (kE * ct + e) * SM::kChStep + cq * kN + cn;
-                acc[e] = cs[0];
-#pragma unroll
-                for (int w = 1; w < 4; w++) acc[e] += cs[w * SM::kChWave];
-            }
-            float *dst = at_bytes((cq ? ws.dCp : ws.dBp) + (b * groups + group) * kN * L,
-                                  uint32_t(cn * Ls + t0 + kE * ct) * 4u);
-            if ((Ls % kE) == 0 && t0 + kE * ct + kE <= Ls) {
-                if constexpr (kE == 4)
-                    *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                else
-                    *reinterpret_cast<float2 *>(dst) = make_float2(acc[0], acc[1]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < kE; e++)
-                    if (t0 + kE * ct + e < Ls) dst[e] = acc[e];
-            }
-        }
         // unconditional, so no prefetch is in flight across the loop's back
         // edge (after the first chunk it rewrites the last chunk's words
         // into the raw tiles, which are not read again)
         st.stash(smem);
         __syncthreads();
     }
+
+    if (nch > 0) chan_sums(0, 0);   // chunk 0, complete since the loop's last barrier
 
     // per-row partials of the parameter gradients
     if (row_ok) ws.dAp[(b * Dm + d) * kN + n] = dA_acc;
@@ -595,7 +628,7 @@ __device__ __forceinline__ void fold_add(float (&acc)[VT], const float *src) {
 template <typename T, int VT>
 __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace ws) {
     const int64_t L = p.seqlen, Dm = p.dim, Bt = p.batch;
-    const int64_t groups = (Dm + kRows - 1) / kRows;
+    const int64_t groups = ws.groups;
     const int64_t nbc = Bt * kN * L / VT;   // dB / dC work items (VT divides L)
     const int64_t na = Dm * kN;             // dA elements
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -640,6 +673,38 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
     }
 }
 
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Wavefronts per reverse-pass workgroup.  A 12-wavefront (48-channel)
+// group stages B and C once for three times the channels and writes a third
+// of the dB/dC partials; it is taken when such groups fill every compute unit
+// in no more rounds than 4-wavefront groups (3 per compute unit) would.
+int reverse_waves(const BwdParams &p, bool vec) {
+    if (!vec || kC != 32) return 4;
+    const int64_t cus = device_cus();
+    const int64_t wg4 = p.batch * ((p.dim + 15) / 16), wg12 = p.batch * ((p.dim + 47) / 48);
+    const int64_t rounds4 = (wg4 + 3 * cus - 1) / (3 * cus), rounds12 = (wg12 + cus - 1) / cus;
+    return (wg12 >= cus && rounds12 <= rounds4) ? 12 : 4;
+}
+
+template <typename T, int VEC, bool YP, int NW>
+void launch_reverse(const BwdParams &p, Workspace ws, hipStream_t stream) {
+    const dim3 grid(unsigned((p.dim + 4 * NW - 1) / (4 * NW)), unsigned(p.batch));
+    hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW>), grid, dim3(64 * NW), 0, stream, p, ws);
+}
+
 template <typename T>
 hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
     Workspace ws = carve(p.workspace, p.batch, p.dim, p.seqlen, nullptr);
@@ -659,14 +724,18 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
             profile_mark(stream);
         }
         const bool yp = p.ckpt && p.ypre && p.z;
-        if (vec && yp)
-            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec, true>), grid, dim3(kThreads), 0, stream, p, ws);
-        else if (vec)
-            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, kVec, false>), grid, dim3(kThreads), 0, stream, p, ws);
-        else if (yp)
-            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, 1, true>), grid, dim3(kThreads), 0, stream, p, ws);
-        else
-            hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, 1, false>), grid, dim3(kThreads), 0, stream, p, ws);
+        const int nw = reverse_waves(p, vec);
+        ws.groups = (p.dim + 4 * nw - 1) / (4 * nw);   // the partials the fold reads
+        if (vec && nw == 12) {
+            if (yp) launch_reverse<T, kVec, true, 12>(p, ws, stream);
+            else launch_reverse<T, kVec, false, 12>(p, ws, stream);
+        } else if (vec) {
+            if (yp) launch_reverse<T, kVec, true, 4>(p, ws, stream);
+            else launch_reverse<T, kVec, false, 4>(p, ws, stream);
+        } else {
+            if (yp) launch_reverse<T, 1, true, 4>(p, ws, stream);
+            else launch_reverse<T, 1, false, 4>(p, ws, stream);
+        }
         profile_mark(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -47,6 +47,10 @@ SMALL = [
     (2, 24, 70, "bf16", {}),                      # bf16 rows not 16-byte aligned (scalar path)
     (2, 24, 96, "bf16", {}),                      # bf16, 16-byte slots
     (2, 40, 136, "bf16", {}),                     # bf16, 16-byte slots, ragged dim and tail
+    # Enough 48-channel groups to fill a 256-CU device: these take the
+    # 12-wavefront reverse pass (the first with a last group of 8 channels).
+    (8, 1544, 64, "f32", {}),
+    (8, 1536, 96, "bf16", {}),
 ]
 
 
@@ -82,7 +86,8 @@ def test_bwd_small_elementwise(batch, dim, L, io, flags):
 
 
 @pytest.mark.parametrize("batch,dim,L,io", [(2, 40, 100, "f32"), (1, 33, 70, "bf16"),
-                                             (2, 24, 96, "bf16"), (2, 16, 17, "f32")])
+                                             (2, 24, 96, "bf16"), (2, 16, 17, "f32"),
+                                             (8, 1544, 64, "f32")])
 def test_bwd_with_forward_checkpoints_is_bit_identical(batch, dim, L, io):
     """Checkpoints saved by the forward give the same bits as recomputing them."""
     require_gpu()
