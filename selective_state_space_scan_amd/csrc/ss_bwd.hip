@@ -245,17 +245,16 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
 // ---------------------------------------------------------------------------
 constexpr int kPitch2 = kC + 4;
 
-// NW wavefronts, 4 NW channels per workgroup.
+// NW wavefronts, 4 NW channels per workgroup.  Only B and C go through LDS
+// (they are shared by all channels), in two buffers: chunk c uses buffer
+// c & 1 while the next chunk's tiles are stashed into the other.
 template <typename T, int NW>
 struct RevSmem {
     static constexpr int kR = 4 * NW;                                 // channels
-    static constexpr uint32_t kB = 0;
+    static constexpr uint32_t kB = 0;                                 // within a buffer
     static constexpr uint32_t kCc = kB + kN * kPitch2 * 4;
-    static constexpr uint32_t kU = kCc + kN * kPitch2 * 4;          // raw u / delta / z / dout
-    static constexpr uint32_t kDl = kU + kR * kC * sizeof(T);
-    static constexpr uint32_t kZ = kDl + kR * kC * sizeof(T);
-    static constexpr uint32_t kG = kZ + kR * kC * sizeof(T);
-    static constexpr uint32_t kRawEnd = kG + kR * kC * sizeof(T);
+    static constexpr uint32_t kBC = kCc + kN * kPitch2 * 4;         // one buffer
+    static constexpr uint32_t kRawEnd = 2 * kBC;
     // 4-row channel sums, two chunks' worth (a chunk's are added up during
     // the next chunk): [chunk 2][wave NW][step kC][quantity 2 x state 16 + pad].
     // At the end of a chunk thread (quantity, state, step group) adds kE
@@ -283,12 +282,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     constexpr int kRowsG = SM::kR;
     constexpr int kThr = 64 * NW;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
-    float(*sB)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kB);
-    float(*sC)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(smem + SM::kCc);
-    T(*sU)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kU);
-    T(*sDl)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kDl);
-    T(*sZ)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kZ);
-    T(*sG)[kC] = reinterpret_cast<T(*)[kC]>(smem + SM::kG);
     float *chan = reinterpret_cast<float *>(smem + SM::kCh);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -297,7 +290,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const int64_t d0 = int64_t(blockIdx.x) * kRowsG, d = d0 + r;
     const int64_t group = blockIdx.x, groups = gridDim.x;
     const bool row_ok = d < Dm;
-    const int valid_rows = int(Dm - d0 < kRowsG ? Dm - d0 : kRowsG);
     const bool has_z = p.z != nullptr;
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
@@ -327,14 +319,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
 
     const T *gB = static_cast<const T *>(p.B) + b * kN * L;
     const T *gC = static_cast<const T *>(p.C) + b * kN * L;
-    const int64_t rowbase = (b * Dm + d0) * L;
-    const T *gu = static_cast<const T *>(p.u) + rowbase;
-    const T *gdl = static_cast<const T *>(p.delta) + rowbase;
-    const T *gz = has_z ? static_cast<const T *>(p.z) + rowbase : nullptr;
-    const T *gdo = static_cast<const T *>(p.dout) + rowbase;
-    // this lane's row of the element-wise gradients; a row's 16 lanes store
-    // 16 consecutive elements of a 16-step block
+    // this lane's row of the element-wise tensors; a row's 16 lanes load and
+    // store 16 consecutive elements of a 16-step block
     const int64_t wavebase = (b * Dm + dw) * L;
+    const T *gu = static_cast<const T *>(p.u) + wavebase;
+    const T *gdl = static_cast<const T *>(p.delta) + wavebase;
+    const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
+    const T *gdo = static_cast<const T *>(p.dout) + wavebase;
     T *du_b = static_cast<T *>(p.du) + wavebase;
     T *dd_b = static_cast<T *>(p.ddelta) + wavebase;
     T *dz_b = has_z ? static_cast<T *>(p.dz) + wavebase : nullptr;
@@ -347,28 +338,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         return (YP && row_ok && t >= 0 && t < Ls) ? ld_global(at_bytes(ypb, uint32_t(rowel + t) * 4u))
                                                   : 0.0f;
     };
-    // tiles: B, C, then u, delta, z, dout in 16-row pieces.  A piece with
-    // no valid row points at the group's first row (it is not read).
-    constexpr int kPieces = kRowsG / 16;
-    ChunkStager<T, VEC, kC, 2 + 4 * kPieces, kThr> st;
+    // element t of this lane's row of u, delta, z or dout (0 past the end
+    // and for rows past the last channel)
+    auto elem_at = [&](const T *g, int t) {
+        return (row_ok && t < Ls) ? to_f32<T>(ld_global(at_bytes(g, elem_off(t)))) : 0.0f;
+    };
+    // B and C tiles of a chunk, staged through LDS
+    ChunkStager<T, VEC, kC, 2, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
             if (i == 0) return {gB, L, kN, SM::kB, kPitch2, true};
-            if (i == 1) return {gC, L, kN, SM::kCc, kPitch2, true};
-            const int q = (i - 2) / kPieces, j = (i - 2) % kPieces;
-            const T *g = q == 0 ? gu : q == 1 ? gdl : q == 2 ? gz : gdo;
-            const uint32_t lds = q == 0 ? SM::kU : q == 1 ? SM::kDl : q == 2 ? SM::kZ : SM::kG;
-            const int vr = valid_rows - 16 * j;
-            return {(g && vr > 0) ? g + int64_t(16 * j) * L : g, L, vr > 16 ? 16 : (vr > 0 ? vr : 0),
-                    lds + uint32_t(16 * j * kC * sizeof(T)), kC, false};
+            return {gC, L, kN, SM::kCc, kPitch2, true};
         },
         tid);
-
-    if (nch > 0) {
-        st.fetch((nch - 1) * kC, L, tid);
-        st.stash(smem);
-    }
-    __syncthreads();
 
 
     // this lane's slot of the channel sums: lane (rw, n) receives state n of
@@ -405,42 +387,48 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         }
     };
 
-    // The checkpoints of the next chunk are loaded one chunk ahead and before
-    // the prefetch: loads retire in order, so a load issued after the
-    // prefetch would make its use wait for the prefetch.
+    // The per-lane values of a chunk (checkpoints, the saved pre-gate
+    // output, the owned elements of u, delta, z, dout) are loaded during the
+    // chunk before it, once that chunk's per-element phase has consumed its
+    // own, so the loads land in the same registers without copies.
     // (with seqlen 0 there is no chunk and nothing is loaded)
-    float hn[kNB] = {}, ypn[kNB] = {};
-    if (nch > 0) {
+    float hn[kNB] = {}, ypn[kNB] = {}, un[kNB] = {}, dn[kNB] = {}, zn[kNB] = {}, gn[kNB] = {};
+    auto load_next = [&](int tc) {
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
-            hn[s] = ckpt_at(kNB * (int(nch) - 1) + s);
-            if (YP) ypn[s] = ypre_at((int(nch) - 1) * kC + 16 * s + n);
+            const int t = tc + 16 * s + n;
+            hn[s] = ckpt_at(kNB * (tc / kC) + s);
+            if (YP) ypn[s] = ypre_at(t);
+            un[s] = elem_at(gu, t);
+            dn[s] = elem_at(gdl, t);
+            if (has_z) zn[s] = elem_at(gz, t);
+            gn[s] = elem_at(gdo, t);
         }
+    };
+    if (nch > 0) {
+        load_next((int(nch) - 1) * kC);
+        st.fetch((nch - 1) * kC, L, tid);
+        st.stash(smem + ((nch - 1) & 1) * SM::kBC);
     }
+    __syncthreads();
+
     for (int c = int(nch) - 1; c >= 0; c--) {
         const int t0 = c * kC;
         float *chw = chw0 + (c & 1) * SM::kChBuf;   // this chunk's channel-sum buffer
-        float hb[kNB], yp[kNB];
+        char *bc = smem + (c & 1) * SM::kBC;          // and its B / C tiles
+        float(*sB)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(bc + SM::kB);
+        float(*sC)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(bc + SM::kCc);
+        float hb[kNB];   // block states, used by the blocks after the reload
 #pragma unroll
-        for (int s = 0; s < kNB; s++) {
-            hb[s] = hn[s];
-            if (YP) yp[s] = ypn[s];
-        }
-        if (c > 0) {
-#pragma unroll
-            for (int s = 0; s < kNB; s++) {
-                hn[s] = ckpt_at(kNB * (c - 1) + s);
-                if (YP) ypn[s] = ypre_at(t0 - kC + 16 * s + n);
-            }
-            st.fetch(t0 - kC, L, tid);
-        }
+        for (int s = 0; s < kNB; s++) hb[s] = hn[s];
+        if (c > 0) st.fetch(t0 - kC, L, tid);
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row
         float dl[kNB], dlu[kNB], uu[kNB], sgd[kNB], dout[kNB], zz[kNB], dyv[kNB];
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
             const int col = 16 * s + n;
-            const float raw = to_f32<T>(sDl[r][col]) + bias;
+            const float raw = dn[s] + bias;
             float x = raw;
             sgd[s] = 1.0f;
             if (p.softplus) {
@@ -448,13 +436,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                 sgd[s] = sigmoid_f32(raw);
             }
             // padding steps: no decay, no input.  Rows past the last channel
-            // read unloaded tile words; zeroing delta, delta*u and dy keeps
-            // their g and h at zero, so they add nothing to the channel sums.
+            // get zero delta, delta*u and dy, which keeps their g and h at
+            // zero, so they add nothing to the channel sums.
             dl[s] = (row_ok && t0 + col < Ls) ? x : 0.0f;
-            uu[s] = to_f32<T>(sU[r][col]);
+            uu[s] = un[s];
             dlu[s] = row_ok ? dl[s] * uu[s] : 0.0f;
-            dout[s] = to_f32<T>(sG[r][col]);
-            zz[s] = to_f32<T>(sZ[r][col]);
+            dout[s] = gn[s];
+            zz[s] = zn[s];
             // gradient reaching the pre-gate output; with the saved pre-gate
             // output dz is per-element too and is written here, which keeps
             // the block's recompute free of branches
@@ -464,10 +452,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                 dyv[s] = dout[s] * zz[s] * sz;
                 if (YP && row_ok && t0 + col < Ls)
                     st_global(at_bytes(dz_b, elem_off(t0 + col)),
-                              from_f32<T>(dout[s] * yp[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
+                              from_f32<T>(dout[s] * ypn[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
             }
             if (!row_ok) dyv[s] = 0.0f;
         }
+        if (c > 0) load_next(t0 - kC);
         // the previous (later) chunk's channel sums, complete since the last
         // barrier and not rewritten before the next one
         if (c < int(nch) - 1) chan_sums(t0 + kC, (c + 1) & 1);
@@ -582,12 +571,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             }
             if (t0 + col < Ls) dbias_acc += dd;
         }
-        __syncthreads();
 
-        // unconditional, so no prefetch is in flight across the loop's back
-        // edge (after the first chunk it rewrites the last chunk's words
-        // into the raw tiles, which are not read again)
-        st.stash(smem);
+        // The next chunk's B / C go to the other buffer, whose last readers
+        // (the chunk before this one) are behind the previous barrier.
+        if (c > 0) st.stash(smem + ((c - 1) & 1) * SM::kBC);
         __syncthreads();
     }
 
