@@ -3,6 +3,7 @@
 // Validates every argument on the host before anything is enqueued, keeps a
 // thread-local message naming what failed, and hands valid requests to the
 // kernel launchers.  Nothing here allocates device memory or synchronizes.
+#include <atomic>
 #include "ss.h"
 
 #include <cstdarg>
@@ -94,6 +95,27 @@ ss_status device_status(hipError_t e, const char *what) {
 namespace ssk {
 void profile_mark(hipStream_t stream) {
     if (g_prof && g_prof_used < g_prof_count) (void)hipEventRecord(g_prof[g_prof_used++], stream);
+}
+
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+int scan_waves(int64_t batch, int64_t dim) {
+    const int64_t cus = device_cus();
+    const int64_t wg4 = batch * ((dim + 15) / 16), wg12 = batch * ((dim + 47) / 48);
+    const int64_t rounds4 = (wg4 + 3 * cus - 1) / (3 * cus), rounds12 = (wg12 + cus - 1) / cus;
+    return (wg12 >= cus && rounds12 <= rounds4) ? 12 : 4;
 }
 }  // namespace ssk
 

@@ -16,28 +16,32 @@
 // "Features").
 //
 // Three kernels on the caller's stream:
-//   1. checkpoint: the forward recurrence again, writing the state entering
-//      every 32-step chunk to the workspace;
-//   2. reverse: per workgroup of 16 channels x 16 states (one lane per state
-//      entry, as in the forward), chunks are visited last to first.  Each
-//      chunk re-runs its 32 forward steps from its checkpoint, keeping every
-//      decay and state in registers, then walks the steps backward.
-//        - sums over the 16 states (pre-gate output, the two sums behind du
-//          and ddelta) go through padded per-wave LDS transposes;
+//   1. checkpoint (only when the forward did not save them): the forward
+//      recurrence again, writing the state entering every 16-step block to
+//      the workspace;
+//   2. reverse: one lane per (channel, state) as in the forward, workgroups
+//      of 16 or 48 channels (4 or 12 wavefronts).  32-step chunks are
+//      visited last to first; each 16-step block re-runs its forward steps
+//      from its checkpoint, keeping every decay and state in registers, then
+//      walks the steps backward.
+//        - sums over the 16 states (the two sums behind du and ddelta) are a
+//          register butterfly of DPP adds (the first two levels select by
+//          bank mask, the last two with a select);
 //        - sums over channels (dB, dC): the 4 rows of a wavefront are added
 //          in registers with the gfx950 cross-row lane swaps
 //          (v_permlane32_swap, then v_permlane16_swap), two quantities at two
 //          steps per pair of swaps, so each lane ends with one finished
-//          4-row sum; the 4 wavefronts' sums are then added through LDS and
-//          written as one partial per 16 channels.  (f32 MFMAs could do the
-//          4-row contraction too, but they do not overlap with VALU work on
-//          this chip and would use 1/16 of each instruction here);
+//          4-row sum; the wavefronts' sums go through LDS (two buffers) and
+//          are added up during the next chunk into one partial per group.
+//          (f32 MFMAs could do the 4-row contraction too, but they do not
+//          overlap with VALU work on this chip and would use 1/16 of each
+//          instruction here);
+//        - B and C are staged through two LDS buffers; u, delta, z and dout
+//          are loaded by the lane that owns each element, a chunk ahead;
 //   3. fold: adds the dB/dC partials over channel groups in ascending group
 //      order and the dA/dD/dbias partials over the batch in ascending batch
 //      order.
 // Every sum runs in an order fixed by the shape, with no atomics.
-#include <atomic>
-
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_tiles.h"
@@ -660,30 +664,11 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
     }
 }
 
-// Compute units of the current device, looked up once per device.
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v <= 0) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cache[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
-}
-
-// Wavefronts per reverse-pass workgroup.  A 12-wavefront (48-channel)
-// group stages B and C once for three times the channels and writes a third
-// of the dB/dC partials; it is taken when such groups fill every compute unit
-// in no more rounds than 4-wavefront groups (3 per compute unit) would.
+// Wavefronts per reverse-pass workgroup: scan_waves' choice for 16-byte
+// rows and 32-step chunks, else 4.
 int reverse_waves(const BwdParams &p, bool vec) {
     if (!vec || kC != 32) return 4;
-    const int64_t cus = device_cus();
-    const int64_t wg4 = p.batch * ((p.dim + 15) / 16), wg12 = p.batch * ((p.dim + 47) / 48);
-    const int64_t rounds4 = (wg4 + 3 * cus - 1) / (3 * cus), rounds12 = (wg12 + cus - 1) / cus;
-    return (wg12 >= cus && rounds12 <= rounds4) ? 12 : 4;
+    return scan_waves(p.batch, p.dim);
 }
 
 template <typename T, int VEC, bool YP, int NW>

@@ -15,12 +15,15 @@
 //     exp, a multiply for delta*A, one for delta*u*B and one FMA); the
 //     parallelism comes from the batch x channel x state lanes, which fill
 //     3-5 waves per SIMD at the Mamba layer shapes;
-//   * time is staged through LDS in chunks of 64 steps with coalesced
-//     16-byte loads, prefetched one chunk ahead into registers;
+//   * time runs in chunks of 64 steps.  B and C, which all channels share,
+//     are staged through LDS with coalesced 16-byte loads into two buffers
+//     (one barrier per chunk), prefetched a chunk ahead into registers;
 //   * per-element work (softplus, delta*u, gate) is done once per element by
 //     the lane whose index in its DPP row equals the element's step within a
-//     16-step block; the scan lanes take delta and delta*u from it with a DPP
-//     row broadcast folded into their multiplies;
+//     16-step block; that lane loads its u, delta and z straight from global
+//     memory a chunk ahead (a row's 16 lanes read 16 consecutive elements),
+//     and the scan lanes take delta and delta*u from it with a DPP row
+//     broadcast folded into their multiplies;
 //   * the output's sum over the 16 states goes through a per-wave LDS
 //     transpose every 16 steps, padded so that neither the 16-byte writes
 //     nor the 4-byte reads hit the same bank twice, and is added in a fixed
@@ -33,24 +36,22 @@
 namespace ssk {
 namespace {
 
-constexpr int kRows = 16;       // channels per workgroup
 constexpr int kT = 64;          // time steps per LDS chunk
-constexpr int kThreads = 256;   // 4 wavefronts
 constexpr int kPitch = kT + 4;  // f32 B / C tile pitch (conflict-free 16-byte reads)
 constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
 constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row (row offset = 16 banks)
 
-template <typename T>
+// NW wavefronts (4 NW channels) per workgroup.  Only B and C go through LDS
+// (they are shared by all channels), in two buffers: chunk c uses buffer
+// c & 1 while the next chunk's tiles are stashed into the other.  Each
+// wavefront has its own transpose region for the sums over the states.
+template <int NW>
 struct FwdSmem {
-    static constexpr uint32_t kB = 0;
+    static constexpr uint32_t kB = 0;                          // within a buffer
     static constexpr uint32_t kC = kB + kN * kPitch * 4;
-    static constexpr uint32_t kU = kC + kN * kPitch * 4;                  // union start
-    static constexpr uint32_t kDl = kU + kRows * kT * sizeof(T);
-    static constexpr uint32_t kZ = kDl + kRows * kT * sizeof(T);
-    static constexpr uint32_t kY = kU;                                    // aliases u / delta / z
-    static constexpr uint32_t kRawEnd = kZ + kRows * kT * sizeof(T);
-    static constexpr uint32_t kYEnd = kY + 4 * 4 * kYRow * 4;
-    static constexpr uint32_t kSize = kRawEnd > kYEnd ? kRawEnd : kYEnd;
+    static constexpr uint32_t kBC = kC + kN * kPitch * 4;      // one buffer
+    static constexpr uint32_t kY = 2 * kBC;                    // [wave NW][row 4][kYRow]
+    static constexpr uint32_t kSize = kY + NW * 4 * kYRow * 4;
 };
 
 template <int J>
@@ -61,15 +62,13 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
     v = c * h;
 }
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) void ss_fwd_kernel(FwdParams p) {
-    using SM = FwdSmem<T>;
+// NW: wavefronts per workgroup (4 or 12; 4 NW channels).
+template <typename T, int VEC, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) : 1) void ss_fwd_kernel(FwdParams p) {
+    using SM = FwdSmem<NW>;
+    constexpr int kRowsG = 4 * NW;
+    constexpr int kThr = 64 * NW;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
-    float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + SM::kB);
-    float(*sC)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + SM::kC);
-    T(*sU)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kU);
-    T(*sDl)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kDl);
-    T(*sZ)[kT] = reinterpret_cast<T(*)[kT]>(smem + SM::kZ);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -80,37 +79,61 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) 
     const int64_t L = p.seqlen;
     const int64_t Dm = p.dim;
     const int64_t b = blockIdx.y;
-    const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kRows;
+    const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kRowsG;
     const int64_t d = d0 + r;
     const bool row_ok = d < Dm;
-    const int valid_rows = static_cast<int>(Dm - d0 < kRows ? Dm - d0 : kRows);
     const bool has_z = p.z != nullptr;
+    // the wavefront's first row, uniform (scalar) across the wavefront
+    const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
     float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;  // A in base-2 exponent units
     float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
     float h = (row_ok && p.h0) ? p.h0[(b * Dm + d) * kN + n] : 0.0f;
 
-    const T *gu = static_cast<const T *>(p.u) + (b * Dm + d0) * L;
-    const T *gdl = static_cast<const T *>(p.delta) + (b * Dm + d0) * L;
-    const T *gz = has_z ? static_cast<const T *>(p.z) + (b * Dm + d0) * L : nullptr;
+    // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the
+    // per-row accesses address the wavefront's 4 rows from a scalar base with
+    // 32-bit byte offsets (4 rows x seqlen x 4 bytes < 2^32).
+    const int Ls = int(L);
+    const int64_t wavebase = (b * Dm + dw) * L;
+    const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
+    const T *gu = static_cast<const T *>(p.u) + wavebase;
+    const T *gdl = static_cast<const T *>(p.delta) + wavebase;
+    const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
     const T *gB = static_cast<const T *>(p.B) + b * kN * L;
     const T *gC = static_cast<const T *>(p.C) + b * kN * L;
-    ChunkStager<T, VEC, kT, 5, kThreads> st;
+    // element t of this lane's row (0 past the end and for rows past the
+    // last channel); a row's 16 lanes read 16 consecutive elements
+    auto elem_at = [&](const T *g, int t) {
+        return (row_ok && t < Ls)
+                   ? to_f32<T>(ld_global(at_bytes(g, uint32_t(rowel + t) * uint32_t(sizeof(T)))))
+                   : 0.0f;
+    };
+    ChunkStager<T, VEC, kT, 2, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
-            switch (i) {
-                case 0: return {gB, L, kN, SM::kB, kPitch, true};
-                case 1: return {gC, L, kN, SM::kC, kPitch, true};
-                case 2: return {gu, L, valid_rows, SM::kU, kT, false};
-                case 3: return {gdl, L, valid_rows, SM::kDl, kT, false};
-                default: return {gz, L, valid_rows, SM::kZ, kT, false};
-            }
+            if (i == 0) return {gB, L, kN, SM::kB, kPitch, true};
+            return {gC, L, kN, SM::kC, kPitch, true};
         },
         tid);
 
-    const int64_t nchunks = (L + kT - 1) / kT;
+    // The owned elements of a chunk (16 s + n of the lane's row) are loaded
+    // during the chunk before it, once that chunk's per-element phase has
+    // consumed its own, so the loads land in the same registers.
+    constexpr int kE = kT / 16;
+    float un[kE] = {}, dn[kE] = {}, zn[kE] = {};
+    auto load_next = [&](int tc) {
+#pragma unroll
+        for (int s = 0; s < kE; s++) {
+            const int t = tc + 16 * s + n;
+            un[s] = elem_at(gu, t);
+            dn[s] = elem_at(gdl, t);
+            if (has_z) zn[s] = elem_at(gz, t);
+        }
+    };
+    const int nchunks = int((L + kT - 1) / kT);
     if (nchunks > 0) {
+        load_next(0);
         st.fetch(0, L, tid);
         st.stash(smem);
     }
@@ -120,38 +143,36 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) 
     __asm__("" : "+v"(a2), "+v"(bias), "+v"(dskip), "+v"(h));
     __syncthreads();
 
-    // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the
-    // stores address the group's 16 rows from a scalar base with 32-bit byte
-    // offsets (16 rows x seqlen x 4 bytes < 2^32).
-    const int Ls = int(L);
     const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
     const int nckS = int(nck);
     const bool save_ck = p.ckpt != nullptr;
-    float *ckb = save_ck ? p.ckpt + (b * Dm + d0) * nck * kN : nullptr;
-    const uint32_t ckoff = uint32_t((r * nckS * kN + n) * 4);
+    float *ckb = save_ck ? p.ckpt + (b * Dm + dw) * nck * kN : nullptr;
+    const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
     float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
-    T *yb = static_cast<T *>(p.out) + (b * Dm + d0) * L;
+    T *yb = static_cast<T *>(p.out) + wavebase;
     // the pre-gate output, saved for the backward's dz
     const bool save_yp = p.ypre && has_z;
-    float *ypb = save_yp ? p.ypre + (b * Dm + d0) * L : nullptr;
-    const int rowel = r * Ls;   // this lane's row, in elements from the group's first
-    for (int c = 0; c < int(nchunks); c++) {
+    float *ypb = save_yp ? p.ypre + wavebase : nullptr;
+    for (int c = 0; c < nchunks; c++) {
         const int t0 = c * kT;
+        char *bc = smem + (c & 1) * SM::kBC;   // this chunk's B / C tiles
+        float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(bc + SM::kB);
+        float(*sC)[kPitch] = reinterpret_cast<float(*)[kPitch]>(bc + SM::kC);
         if (c + 1 < nchunks) st.fetch(t0 + kT, L, tid);
 
         // per-element work: lane (r, n) owns elements 16 s + n of its row
-        float dl[kT / 16], dlu[kT / 16], uu[kT / 16], zz[kT / 16];
+        float dl[kE], dlu[kE], uu[kE], zz[kE];
 #pragma unroll
-        for (int s = 0; s < kT / 16; s++) {
+        for (int s = 0; s < kE; s++) {
             const int col = 16 * s + n;
-            uu[s] = to_f32<T>(sU[r][col]);
-            zz[s] = to_f32<T>(sZ[r][col]);
-            float x = to_f32<T>(sDl[r][col]) + bias;
+            uu[s] = un[s];
+            zz[s] = zn[s];
+            float x = dn[s] + bias;
             if (p.softplus) x = softplus_f32(x);
             dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps leave the state unchanged
             dlu[s] = dl[s] * uu[s];
         }
-        __syncthreads();  // the transpose region aliases u / delta / z
+        if (c + 1 < nchunks) load_next(t0 + kT);
 
         // Output sums over the 16 states go through this wave's LDS region:
         // block s writes its per-state terms four steps at a time; their
@@ -172,7 +193,7 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) 
             }
         };
 #pragma unroll
-        for (int s = 0; s < kT / 16; s++) {
+        for (int s = 0; s < kE; s++) {
             if (save_ck && (16 * s) % kCkptSpacing == 0) {   // state entering a checkpoint chunk
                 const int k = (t0 + 16 * s) / kCkptSpacing;
                 if (row_ok && k < nckS) st_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)), h);
@@ -210,25 +231,35 @@ __global__ __launch_bounds__(kThreads, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) 
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int k = 0; k < 16; k++) part[k] = ybuf[k * kYN + n];
-        finish(kT / 16 - 1);
-        __syncthreads();
+        finish(kE - 1);
 
-        if (c + 1 < nchunks) st.stash(smem);
+        // The next chunk's B / C go to the other buffer, whose last readers
+        // (the chunk before this one) are behind the previous barrier.
+        if (c + 1 < nchunks) st.stash(smem + ((c + 1) & 1) * SM::kBC);
         __syncthreads();
     }
 
     if (p.last_state && row_ok) p.last_state[(b * Dm + d) * kN + n] = h;
 }
 
+template <typename T, int VEC, int NW>
+void launch_scan(const FwdParams &p, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((p.dim + 4 * NW - 1) / (4 * NW)),
+                    static_cast<unsigned>(p.batch));
+    hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW>), grid, dim3(64 * NW), 0, stream, p);
+}
+
 template <typename T>
 hipError_t launch_typed(const FwdParams &p, hipStream_t stream) {
-    dim3 grid(static_cast<unsigned>((p.dim + kRows - 1) / kRows), static_cast<unsigned>(p.batch));
     constexpr int kVec = 16 / sizeof(T);
     // 16-byte vectors need every row start aligned: seqlen * sizeof(T) % 16 == 0
+    // 4 wavefronts per workgroup: 12 would cut the B / C reads by two thirds,
+    // but this pass is not bound by memory, and three independent
+    // workgroups per compute unit overlap their barriers and LDS phases.
     if ((p.seqlen * static_cast<int64_t>(sizeof(T))) % 16 == 0)
-        hipLaunchKernelGGL((ss_fwd_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p);
+        launch_scan<T, kVec, 4>(p, stream);
     else
-        hipLaunchKernelGGL((ss_fwd_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p);
+        launch_scan<T, 1, 4>(p, stream);
     profile_mark(stream);
     return hipGetLastError();
 }

@@ -77,6 +77,16 @@ struct DecodeParams {
 // Records the next armed profiling event on `stream` (no-op when unarmed).
 void profile_mark(hipStream_t stream);
 
+// Compute units of the current device, looked up once per device.
+int device_cus();
+
+// Wavefronts per workgroup of the reverse pass (4 channels each).  A
+// 12-wavefront (48-channel) group stages B and C once for three times the
+// channels and writes a third of the dB / dC partials; it is taken when such
+// groups fill every compute unit in no more rounds than 4-wavefront groups
+// (3 per compute unit) would.  Else 4.
+int scan_waves(int64_t batch, int64_t dim);
+
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen);
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);

@@ -40,6 +40,9 @@ SMALL = [
     (1, 32, 96, "bf16", dict(has_z=False, has_D=False, has_bias=False)),
     (2, 16, 1, "f32", {}),                        # single step
     (1, 8, 31, "f32", {}),                        # fewer rows than a workgroup, one chunk
+    # many workgroups: a last group of 8 channels and a ragged tail; no z
+    (8, 1544, 100, "f32", {}),
+    (8, 1536, 128, "bf16", dict(has_z=False)),
 ]
 
 
