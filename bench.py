@@ -292,6 +292,38 @@ def main():
                             "hbm_frac_of_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                             "input_sets_rotated": reps}
             del sets, outs
+        # the same fwd + bwd step with bf16 tensors
+        wb = ssin.WORKLOADS["mamba130m_bwd_bf16_8x1536x2048"]
+        db = {k: to_dev(v) for k, v in ssin.make(wb).items()}
+        yb = torch.empty_like(db["u"])
+        ckb = binding.ss_ckpt_empty(db["u"])
+        wsb = torch.empty(binding.ss_bwd_workspace_size(wb.batch, wb.dim, 16, wb.seqlen, 1),
+                          dtype=torch.uint8, device=dev)
+
+        def step_bf16():
+            binding.ss_fwd(db["u"], db["delta"], db["A"], db["B"], db["C"], db["D"], db["z"],
+                           db["delta_bias"], True, out=yb, ckpt=ckb)
+            binding.ss_bwd(db["u"], db["delta"], db["A"], db["B"], db["C"], db["D"], db["z"],
+                           db["delta_bias"], True, db["dout"], workspace=wsb, ckpt=ckb)
+        for _ in range(3):
+            step_bf16()
+        iters = 10
+        tm = KernelTimer(hip, lib, per_step * iters)
+        torch.cuda.synchronize()
+        tm.arm()
+        for _ in range(iters):
+            step_bf16()
+        torch.cuda.synchronize()
+        tm.disarm()
+        kb16 = {n: float(np.mean([tm.ms(s * per_step + i, s * per_step + j) for s in range(iters)]))
+                for n, (i, j) in zip(names, pairs)}
+        tm.close()
+        detail["mamba130m_step_bf16_8x1536x2048"] = {
+            **{n.replace("ss_", "").replace("_kernel", "") + "_ms": round(v, 5) for n, v in kb16.items()},
+            "step_kernels_ms": round(sum(kb16.values()), 5),
+            "elements_per_s": E / (sum(kb16.values()) * 1e-3)}
+        del db, yb, ckb, wsb
+
         # the backward on its own (checkpoints recomputed inside ss_bwd)
         iters = 10
         tm = KernelTimer(hip, lib, 4 * iters)

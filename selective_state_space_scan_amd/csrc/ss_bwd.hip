@@ -249,15 +249,21 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
 // ---------------------------------------------------------------------------
 constexpr int kPitch2 = kC + 4;
 
-// NW wavefronts, 4 NW channels per workgroup.  Only B and C go through LDS
-// (they are shared by all channels), in two buffers: chunk c uses buffer
-// c & 1 while the next chunk's tiles are stashed into the other.
+// NW wavefronts, 4 NW channels per workgroup.  B and C (shared by all
+// channels) and, for 2-byte types, the element tiles go through LDS in two
+// buffers: chunk c uses buffer c & 1 while the next chunk's tiles are
+// stashed into the other.
 template <typename T, int NW>
 struct RevSmem {
     static constexpr int kR = 4 * NW;                                 // channels
     static constexpr uint32_t kB = 0;                                 // within a buffer
     static constexpr uint32_t kCc = kB + kN * kPitch2 * 4;
-    static constexpr uint32_t kBC = kCc + kN * kPitch2 * 4;         // one buffer
+    static constexpr uint32_t kU = kCc + kN * kPitch2 * 4;          // element tiles [row kR][kC]
+    static constexpr uint32_t kElem = kStageElems<T> ? kR * kC * sizeof(T) : 0;
+    static constexpr uint32_t kDl = kU + kElem;
+    static constexpr uint32_t kZ = kDl + kElem;
+    static constexpr uint32_t kG = kZ + kElem;
+    static constexpr uint32_t kBC = kG + kElem;                     // one buffer
     static constexpr uint32_t kRawEnd = 2 * kBC;
     // 4-row channel sums, two chunks' worth (a chunk's are added up during
     // the next chunk): [chunk 2][wave NW][step kC][quantity 2 x state 16 + pad].
@@ -283,6 +289,7 @@ struct RevSmem {
 template <typename T, int VEC, bool YP, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) : 1) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
     using SM = RevSmem<T, NW>;
+    constexpr bool kStage = kStageElems<T>;
     constexpr int kRowsG = SM::kR;
     constexpr int kThr = 64 * NW;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
@@ -294,6 +301,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const int64_t d0 = int64_t(blockIdx.x) * kRowsG, d = d0 + r;
     const int64_t group = blockIdx.x, groups = gridDim.x;
     const bool row_ok = d < Dm;
+    const int valid_rows = int(Dm - d0 < kRowsG ? Dm - d0 : kRowsG);
     const bool has_z = p.z != nullptr;
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
@@ -347,12 +355,24 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     auto elem_at = [&](const T *g, int t) {
         return (row_ok && t < Ls) ? to_f32<T>(ld_global(at_bytes(g, elem_off(t)))) : 0.0f;
     };
-    // B and C tiles of a chunk, staged through LDS
-    ChunkStager<T, VEC, kC, 2, kThr> st;
+    // B and C tiles of a chunk (and the element tiles of the group's rows
+    // when staged) through LDS
+    const int64_t groupbase = (b * Dm + d0) * L;
+    constexpr int kPieces = kRowsG / 16;
+    ChunkStager<T, VEC, kC, kStage ? 2 + 4 * kPieces : 2, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
             if (i == 0) return {gB, L, kN, SM::kB, kPitch2, true};
-            return {gC, L, kN, SM::kCc, kPitch2, true};
+            if (i == 1) return {gC, L, kN, SM::kCc, kPitch2, true};
+            // element tiles in 16-row pieces; a piece with no valid row points
+            // at the group's first row (it is not read)
+            const int q = (i - 2) / kPieces, j = (i - 2) % kPieces;
+            const void *src = q == 0 ? p.u : q == 1 ? p.delta : q == 2 ? p.z : p.dout;
+            const T *g = src ? static_cast<const T *>(src) + groupbase : nullptr;
+            const uint32_t lds = q == 0 ? SM::kU : q == 1 ? SM::kDl : q == 2 ? SM::kZ : SM::kG;
+            const int vr = valid_rows - 16 * j;
+            return {(g && vr > 0) ? g + int64_t(16 * j) * L : g, L, vr > 16 ? 16 : (vr > 0 ? vr : 0),
+                    lds + uint32_t(16 * j * kC * sizeof(T)), kC, false};
         },
         tid);
 
@@ -403,10 +423,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             const int t = tc + 16 * s + n;
             hn[s] = ckpt_at(kNB * (tc / kC) + s);
             if (YP) ypn[s] = ypre_at(t);
-            un[s] = elem_at(gu, t);
-            dn[s] = elem_at(gdl, t);
-            if (has_z) zn[s] = elem_at(gz, t);
-            gn[s] = elem_at(gdo, t);
+            if constexpr (!kStage) {
+                un[s] = elem_at(gu, t);
+                dn[s] = elem_at(gdl, t);
+                if (has_z) zn[s] = elem_at(gz, t);
+                gn[s] = elem_at(gdo, t);
+            }
         }
     };
     if (nch > 0) {
@@ -419,9 +441,23 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     for (int c = int(nch) - 1; c >= 0; c--) {
         const int t0 = c * kC;
         float *chw = chw0 + (c & 1) * SM::kChBuf;   // this chunk's channel-sum buffer
-        char *bc = smem + (c & 1) * SM::kBC;          // and its B / C tiles
+        char *bc = smem + (c & 1) * SM::kBC;          // and its staged tiles
         float(*sB)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(bc + SM::kB);
         float(*sC)[kPitch2] = reinterpret_cast<float(*)[kPitch2]>(bc + SM::kCc);
+        const T(*sU)[kC] = reinterpret_cast<const T(*)[kC]>(bc + SM::kU);
+        const T(*sDl)[kC] = reinterpret_cast<const T(*)[kC]>(bc + SM::kDl);
+        const T(*sZ)[kC] = reinterpret_cast<const T(*)[kC]>(bc + SM::kZ);
+        const T(*sG)[kC] = reinterpret_cast<const T(*)[kC]>(bc + SM::kG);
+        if constexpr (kStage) {
+#pragma unroll
+            for (int s = 0; s < kNB; s++) {
+                const int col = 16 * s + n;
+                un[s] = to_f32<T>(sU[r][col]);
+                dn[s] = to_f32<T>(sDl[r][col]);
+                zn[s] = has_z ? to_f32<T>(sZ[r][col]) : 0.0f;
+                gn[s] = to_f32<T>(sG[r][col]);
+            }
+        }
         float hb[kNB];   // block states, used by the blocks after the reload
 #pragma unroll
         for (int s = 0; s < kNB; s++) hb[s] = hn[s];

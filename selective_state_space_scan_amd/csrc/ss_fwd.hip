@@ -41,15 +41,20 @@ constexpr int kPitch = kT + 4;  // f32 B / C tile pitch (conflict-free 16-byte r
 constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
 constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row (row offset = 16 banks)
 
-// NW wavefronts (4 NW channels) per workgroup.  Only B and C go through LDS
-// (they are shared by all channels), in two buffers: chunk c uses buffer
-// c & 1 while the next chunk's tiles are stashed into the other.  Each
-// wavefront has its own transpose region for the sums over the states.
-template <int NW>
+// NW wavefronts (4 NW channels) per workgroup.  B and C (shared by all
+// channels) and, for 2-byte types, the element tiles go through LDS in two
+// buffers: chunk c uses buffer c & 1 while the next chunk's tiles are
+// stashed into the other.  Each wavefront has its own transpose region for
+// the sums over the states.
+template <typename T, int NW>
 struct FwdSmem {
     static constexpr uint32_t kB = 0;                          // within a buffer
     static constexpr uint32_t kC = kB + kN * kPitch * 4;
-    static constexpr uint32_t kBC = kC + kN * kPitch * 4;      // one buffer
+    static constexpr uint32_t kU = kC + kN * kPitch * 4;       // element tiles [row 4 NW][kT]
+    static constexpr uint32_t kElem = kStageElems<T> ? 4 * NW * kT * sizeof(T) : 0;
+    static constexpr uint32_t kDl = kU + kElem;
+    static constexpr uint32_t kZ = kDl + kElem;
+    static constexpr uint32_t kBC = kZ + kElem;                // one buffer
     static constexpr uint32_t kY = 2 * kBC;                    // [wave NW][row 4][kYRow]
     static constexpr uint32_t kSize = kY + NW * 4 * kYRow * 4;
 };
@@ -65,7 +70,8 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
 // NW: wavefronts per workgroup (4 or 12; 4 NW channels).
 template <typename T, int VEC, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) : 1) void ss_fwd_kernel(FwdParams p) {
-    using SM = FwdSmem<NW>;
+    using SM = FwdSmem<T, NW>;
+    constexpr bool kStage = kStageElems<T>;
     constexpr int kRowsG = 4 * NW;
     constexpr int kThr = 64 * NW;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kRowsG;
     const int64_t d = d0 + r;
     const bool row_ok = d < Dm;
+    const int valid_rows = int(Dm - d0 < kRowsG ? Dm - d0 : kRowsG);
     const bool has_z = p.z != nullptr;
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
@@ -100,6 +107,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     const T *gu = static_cast<const T *>(p.u) + wavebase;
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
+    const int64_t groupbase = (b * Dm + d0) * L;   // the group's first row (staged tiles)
     const T *gB = static_cast<const T *>(p.B) + b * kN * L;
     const T *gC = static_cast<const T *>(p.C) + b * kN * L;
     // element t of this lane's row (0 past the end and for rows past the
@@ -109,11 +117,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
                    ? to_f32<T>(ld_global(at_bytes(g, uint32_t(rowel + t) * uint32_t(sizeof(T)))))
                    : 0.0f;
     };
-    ChunkStager<T, VEC, kT, 2, kThr> st;
+    // B and C (and the element tiles of the group's rows when staged)
+    ChunkStager<T, VEC, kT, kStage ? 2 + 3 * (kRowsG / 16) : 2, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
             if (i == 0) return {gB, L, kN, SM::kB, kPitch, true};
-            return {gC, L, kN, SM::kC, kPitch, true};
+            if (i == 1) return {gC, L, kN, SM::kC, kPitch, true};
+            // element tiles in 16-row pieces; a piece with no valid row points
+            // at the group's first row (it is not read)
+            constexpr int kPieces = kRowsG / 16;
+            const int q = (i - 2) / kPieces, j = (i - 2) % kPieces;
+            const void *src = q == 0 ? p.u : q == 1 ? p.delta : p.z;
+            const T *g = src ? static_cast<const T *>(src) + groupbase : nullptr;
+            const uint32_t lds = q == 0 ? SM::kU : q == 1 ? SM::kDl : SM::kZ;
+            const int vr = valid_rows - 16 * j;
+            return {(g && vr > 0) ? g + int64_t(16 * j) * L : g, L, vr > 16 ? 16 : (vr > 0 ? vr : 0),
+                    lds + uint32_t(16 * j * kT * sizeof(T)), kT, false};
         },
         tid);
 
@@ -123,6 +142,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     constexpr int kE = kT / 16;
     float un[kE] = {}, dn[kE] = {}, zn[kE] = {};
     auto load_next = [&](int tc) {
+        if constexpr (kStage) return;
 #pragma unroll
         for (int s = 0; s < kE; s++) {
             const int t = tc + 16 * s + n;
@@ -155,9 +175,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     float *ypb = save_yp ? p.ypre + wavebase : nullptr;
     for (int c = 0; c < nchunks; c++) {
         const int t0 = c * kT;
-        char *bc = smem + (c & 1) * SM::kBC;   // this chunk's B / C tiles
+        char *bc = smem + (c & 1) * SM::kBC;   // this chunk's staged tiles
         float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(bc + SM::kB);
         float(*sC)[kPitch] = reinterpret_cast<float(*)[kPitch]>(bc + SM::kC);
+        const T(*sU)[kT] = reinterpret_cast<const T(*)[kT]>(bc + SM::kU);
+        const T(*sDl)[kT] = reinterpret_cast<const T(*)[kT]>(bc + SM::kDl);
+        const T(*sZ)[kT] = reinterpret_cast<const T(*)[kT]>(bc + SM::kZ);
         if (c + 1 < nchunks) st.fetch(t0 + kT, L, tid);
 
         // per-element work: lane (r, n) owns elements 16 s + n of its row
@@ -165,9 +188,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
 #pragma unroll
         for (int s = 0; s < kE; s++) {
             const int col = 16 * s + n;
-            uu[s] = un[s];
-            zz[s] = zn[s];
-            float x = dn[s] + bias;
+            float x;
+            if constexpr (kStage) {
+                uu[s] = to_f32<T>(sU[r][col]);
+                zz[s] = has_z ? to_f32<T>(sZ[r][col]) : 0.0f;
+                x = to_f32<T>(sDl[r][col]) + bias;
+            } else {
+                uu[s] = un[s];
+                zz[s] = zn[s];
+                x = dn[s] + bias;
+            }
             if (p.softplus) x = softplus_f32(x);
             dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps leave the state unchanged
             dlu[s] = dl[s] * uu[s];

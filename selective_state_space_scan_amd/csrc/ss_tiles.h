@@ -53,6 +53,14 @@ __device__ __forceinline__ T *at_bytes(T *base, uint32_t off) {
     return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
 }
 
+// Element tensors (u, delta, z, dout) reach the lanes that own their
+// elements straight from global memory when 4 bytes wide; 2-byte elements
+// are staged through LDS with the B / C tiles (per-lane 2-byte loads split
+// every cache line into four requests, which costs more than the LDS round
+// trip).
+template <typename T>
+constexpr bool kStageElems = sizeof(T) == 2;
+
 // One tile of a chunk.
 template <typename T>
 struct TileSrc {

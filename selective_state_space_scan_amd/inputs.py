@@ -68,6 +68,8 @@ WORKLOADS = {
                  seed=SEED_BASE + 3),
         Workload("decode_bf16_256x5120", "decode", 256, 5120, 16, 1, "bf16",
                  seed=SEED_BASE + 4),
+        Workload("mamba130m_bwd_bf16_8x1536x2048", "bwd", 8, 1536, 16, 2048, "bf16",
+                 seed=SEED_BASE + 5),
     ]
 }
 
