@@ -65,7 +65,8 @@ struct Workspace {
     const float *ypre;  // pre-gate output saved by the forward, or nullptr
     float *dBp;      // (batch, groups, 16, L); sized for 16-channel groups
     float *dCp;      // (batch, groups, 16, L)
-    int64_t groups;  // channel groups of the reverse pass that wrote them
+    int64_t groups;  // partials per (batch, state, step) that the reverse pass wrote
+    int sub;         // 16-channel blocks per partial (1: 16-channel groups, 3: 48)
     float *dAp;      // (batch, dim, 16)
     float *dDp;      // (batch, dim)
     float *dbiasp;   // (batch, dim)
@@ -90,6 +91,7 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
     w.dBp = take(size_t(batch) * groups * kN * L);
     w.dCp = take(size_t(batch) * groups * kN * L);
     w.groups = groups;
+    w.sub = 1;
     w.dAp = take(size_t(batch) * dim * kN);
     w.dDp = take(size_t(batch) * dim);
     w.dbiasp = take(size_t(batch) * dim);
@@ -302,6 +304,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const int64_t group = blockIdx.x, groups = gridDim.x;
     const bool row_ok = d < Dm;
     const int valid_rows = int(Dm - d0 < kRowsG ? Dm - d0 : kRowsG);
+    const int nsub = (valid_rows + 15) / 16;   // 16-channel blocks with a valid channel
     const bool has_z = p.z != nullptr;
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
@@ -388,13 +391,27 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             constexpr int kE = SM::kE, kSG = SM::kSG;
             const int cq = __builtin_amdgcn_readfirstlane(tid / (kN * kSG));   // uniform per wavefront
             const int cn = (tid / kSG) % kN, ct = tid % kSG;
+            // 16-channel blocks (4 wavefronts each, in ascending order), then
+            // the blocks with a valid channel in ascending order: the order the
+            // fold uses for 16-channel partials, so the bits do not depend on
+            // the group size
             float acc[kE];
 #pragma unroll
             for (int e = 0; e < kE; e++) {
                 const float *cs = chan + cb * SM::kChBuf + (kE * ct + e) * SM::kChStep + cq * kN + cn;
-                acc[e] = cs[0];
+                float a = cs[0];
 #pragma unroll
-                for (int w = 1; w < NW; w++) acc[e] += cs[w * SM::kChWave];
+                for (int w = 1; w < 4; w++) a += cs[w * SM::kChWave];
+#pragma unroll
+                for (int sbk = 1; sbk < NW / 4; sbk++) {
+                    if (sbk < nsub) {
+                        float t = cs[4 * sbk * SM::kChWave];
+#pragma unroll
+                        for (int w = 1; w < 4; w++) t += cs[(4 * sbk + w) * SM::kChWave];
+                        a += t;
+                    }
+                }
+                acc[e] = a;
             }
             float *dst = at_bytes((cq ? ws.dCp : ws.dBp) + (b * groups + group) * kN * L,
                                   uint32_t(cn * Ls + tc + kE * ct) * 4u);
@@ -652,6 +669,19 @@ __device__ __forceinline__ void fold_add(float (&acc)[VT], const float *src) {
     }
 }
 
+template <int VT>
+__device__ __forceinline__ void fold_set(float (&acc)[VT], const float *src) {
+    if constexpr (VT == 4) {
+        const u32x4 r = ld_global16(src);
+        acc[0] = __uint_as_float(r.x);
+        acc[1] = __uint_as_float(r.y);
+        acc[2] = __uint_as_float(r.z);
+        acc[3] = __uint_as_float(r.w);
+    } else {
+        acc[0] = ld_global(src);
+    }
+}
+
 template <typename T, int VT>
 __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace ws) {
     const int64_t L = p.seqlen, Dm = p.dim, Bt = p.batch;
@@ -660,23 +690,48 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
     const int64_t na = Dm * kN;             // dA elements
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < nbc) {
+        // The sum over channels has one order whatever the reverse pass's
+        // group size: 16-channel partials p (each summed the same way), added
+        // three at a time, q = (p0 + p1) + p2, and the q in ascending order.
+        // A 48-channel pass writes q itself; a 16-channel pass writes p.
         const int64_t e = i * VT;                                // (bb, n, t) element
         const int64_t bb = e / (kN * L), rem = e - bb * kN * L;  // rem = n * L + t
-        const int64_t stride = kN * L;                           // one channel group
+        const int64_t stride = kN * L;                           // one partial
         const float *pb = ws.dBp + bb * groups * stride + rem;
         const float *pc = ws.dCp + bb * groups * stride + rem;
         float sb[VT] = {}, sc[VT] = {};
-        int64_t gi = 0;
-        for (; gi + 4 <= groups; gi += 4) {
-            // the loads of 4 groups are issued before their in-order adds
+        if (ws.sub == 1) {   // partials are the q
+            int64_t gi = 0;
+            for (; gi + 4 <= groups; gi += 4) {
+                // the loads of 4 partials are issued before their in-order adds
 #pragma unroll
-            for (int k = 0; k < 4; k++) fold_add<VT>(sb, pb + (gi + k) * stride);
+                for (int k = 0; k < 4; k++) fold_add<VT>(sb, pb + (gi + k) * stride);
 #pragma unroll
-            for (int k = 0; k < 4; k++) fold_add<VT>(sc, pc + (gi + k) * stride);
-        }
-        for (; gi < groups; gi++) {
-            fold_add<VT>(sb, pb + gi * stride);
-            fold_add<VT>(sc, pc + gi * stride);
+                for (int k = 0; k < 4; k++) fold_add<VT>(sc, pc + (gi + k) * stride);
+            }
+            for (; gi < groups; gi++) {
+                fold_add<VT>(sb, pb + gi * stride);
+                fold_add<VT>(sc, pc + gi * stride);
+            }
+        } else {             // partials are the p: form each q first
+            for (int64_t gi = 0; gi < groups; gi += 3) {
+                float qb[VT] = {}, qc[VT] = {};
+                fold_set<VT>(qb, pb + gi * stride);
+                fold_set<VT>(qc, pc + gi * stride);
+                if (gi + 1 < groups) {
+                    fold_add<VT>(qb, pb + (gi + 1) * stride);
+                    fold_add<VT>(qc, pc + (gi + 1) * stride);
+                }
+                if (gi + 2 < groups) {
+                    fold_add<VT>(qb, pb + (gi + 2) * stride);
+                    fold_add<VT>(qc, pc + (gi + 2) * stride);
+                }
+#pragma unroll
+                for (int k = 0; k < VT; k++) {
+                    sb[k] += qb[k];
+                    sc[k] += qc[k];
+                }
+            }
         }
 #pragma unroll
         for (int k = 0; k < VT; k++) {
@@ -734,6 +789,7 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         const bool yp = p.ckpt && p.ypre && p.z;
         const int nw = reverse_waves(p, vec);
         ws.groups = (p.dim + 4 * nw - 1) / (4 * nw);   // the partials the fold reads
+        ws.sub = nw == 12 ? 1 : 3;
         if (vec && nw == 12) {
             if (yp) launch_reverse<T, kVec, true, 12>(p, ws, stream);
             else launch_reverse<T, kVec, false, 12>(p, ws, stream);

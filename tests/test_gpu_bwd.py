@@ -110,6 +110,28 @@ def test_bwd_with_forward_checkpoints_is_bit_identical(batch, dim, L, io):
         assert torch.equal(a, b2), k
 
 
+@pytest.mark.parametrize("dim,L,io", [(1536, 64, "f32"), (1544, 96, "bf16")])
+def test_bwd_rows_do_not_depend_on_batch(dim, L, io):
+    """A batch entry's du, ddelta, dz, dB and dC are the same bits run alone
+    as inside a batch of 8.  On a 256-CU device the batch of 8 takes the
+    48-channel reverse pass and the single entry the 16-channel one, so this
+    also pins their common order of the sums over channels."""
+    require_gpu()
+    w = ssin.custom("bwd", 8, dim, 16, L, io, seed=dim + L)
+    d = dev_inputs(ssin.make(w))
+    g = run_bwd(d, w)
+    per_entry = ("u", "delta", "B", "C", "z", "dout")
+    for bi in (0, 5):
+        one = {k: (v[bi:bi + 1].contiguous() if k in per_entry else v) for k, v in d.items()}
+        g1 = run_bwd(one, w)
+        torch.cuda.synchronize()
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            a, b1 = g[k][bi:bi + 1], g1[k]
+            if a.dtype == torch.bfloat16:
+                a, b1 = a.view(torch.int16), b1.view(torch.int16)
+            assert torch.equal(a, b1), f"{k} entry {bi}"
+
+
 def test_bwd_zero_length_passes_dlast_through():
     require_gpu()
     w = ssin.custom("bwd", 2, 32, 16, 0, "f32", seed=4)
