@@ -67,7 +67,7 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 typedef enum {
     SS_OK = 0,
     SS_EINVAL = 1,       /* bad argument: null/misaligned pointer, bad size, bad combination */
-    SS_EUNSUPPORTED = 2, /* valid request this build does not implement (e.g. dstate != 16) */
+    SS_EUNSUPPORTED = 2, /* valid request this build does not implement (e.g. dstate > 16) */
     SS_EDEVICE = 3       /* a HIP call or kernel launch failed */
 } ss_status;
 
@@ -80,7 +80,8 @@ const char *ss_last_error(void);
 /*
  * Bytes of what ss_fwd can save for ss_bwd (its "ckpt" buffer), all f32:
  * the state entering every 16-step block, (batch, dim, ceil(seqlen / 16),
- * dstate), then at the next 256-byte boundary the pre-gate output
+ * 16) -- 16 entries for any dstate, the unused ones zero -- then at the
+ * next 256-byte boundary the pre-gate output
  * sum_n C h + D u, (batch, dim, seqlen), which is written when z is given.
  * 0 for empty or unsupported shapes.
  */
@@ -93,7 +94,7 @@ size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
  * block states and the pre-gate output, which a later ss_bwd with the same
  * inputs takes instead of recomputing them (the usual save-for-backward of
  * a training step).
- *   dstate            must be 16 (SS_EUNSUPPORTED otherwise).
+ *   dstate            1..16 (SS_EUNSUPPORTED above 16).
  *   io_dtype          SS_F32 or SS_BF16: dtype of u, delta, B, C, z, out.
  *   D, z, delta_bias, h0, last_state may be NULL.
  *   batch, dim, seqlen >= 0; a zero size enqueues nothing but the
@@ -145,7 +146,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
  * z (batch, dim) and B, C (batch, dstate), and writes out (batch, dim).
  * Each (b, d) row is computed by its own lanes in one fixed order, so a row
  * gives the same bits whether it is stepped alone or inside any batch.
- *   dstate must be 16; D, z, delta_bias may be NULL.
+ *   dstate 1..16; D, z, delta_bias may be NULL.
  */
 ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
                           float *state, const void *u, const void *delta, const float *A,

@@ -69,8 +69,8 @@ ss_status check_dims(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
     if (dstate <= 0) return fail(SS_EINVAL, "dstate must be > 0 (got %lld)", (long long)dstate);
     if (io != SS_F32 && io != SS_BF16)
         return fail(SS_EINVAL, "io_dtype must be SS_F32 (0) or SS_BF16 (1) (got %d)", io);
-    if (dstate != 16)
-        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (this build handles 16)",
+    if (dstate > 16)
+        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (this build handles 1..16)",
                     (long long)dstate);
     if (scan && batch > kMaxBatch)
         return fail(SS_EUNSUPPORTED, "batch %lld exceeds %lld", (long long)batch,
@@ -164,7 +164,7 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     if (h0 && last_state && h0 == last_state)
         return fail(SS_EINVAL, "last_state must not alias h0");
     ssk::FwdParams p{};
-    p.batch = batch; p.dim = dim; p.seqlen = seqlen;
+    p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.nstate = int(dstate);
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.out = out; p.last_state = last_state; p.ckpt = ckpt;
@@ -227,7 +227,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                         workspace_bytes, need);
     }
     ssk::BwdParams p{};
-    p.batch = batch; p.dim = dim; p.seqlen = seqlen;
+    p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.nstate = int(dstate);
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.dout = dout; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB;
@@ -254,7 +254,7 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dty
     c.opt(D, "D"); c.opt(z, "z"); c.opt(delta_bias, "delta_bias");
     if (c.st != SS_OK) return c.st;
     ssk::DecodeParams p{};
-    p.batch = batch; p.dim = dim; p.state = state; p.u = u; p.delta = delta; p.A = A;
+    p.batch = batch; p.dim = dim; p.nstate = int(dstate); p.state = state; p.u = u; p.delta = delta; p.A = A;
     p.B = B; p.C = C; p.D = D; p.z = z; p.bias = delta_bias; p.softplus = delta_softplus != 0;
     p.out = out;
     ssk::profile_mark(static_cast<hipStream_t>(stream));

@@ -180,20 +180,23 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
     const int64_t d0 = int64_t(blockIdx.x) * kRows, d = d0 + r;
     const bool row_ok = d < Dm;
     const int valid_rows = int(Dm - d0 < kRows ? Dm - d0 : kRows);
-    const float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;
+    const int Ns = p.nstate;   // state lanes n >= Ns carry zero A and B
+    const bool st_ok = row_ok && n < Ns;
+    const float a2 = st_ok ? p.A[d * Ns + n] * kLog2e : 0.0f;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
-    float h = (row_ok && p.h0) ? p.h0[(b * Dm + d) * kN + n] : 0.0f;
+    float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Ns + n] : 0.0f;
     const int64_t nck = (L + kCk - 1) / kCk;
     float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
 
-    const T *gB = static_cast<const T *>(p.B) + b * kN * L;
+    const T *gB = static_cast<const T *>(p.B) + b * Ns * L;
+    const bool zero_dead = Ns < kN;   // B rows past dstate must read as zeros
     const T *gu = static_cast<const T *>(p.u) + (b * Dm + d0) * L;
     const T *gdl = static_cast<const T *>(p.delta) + (b * Dm + d0) * L;
     ChunkStager<T, VEC, kT1, 3, kThreads> st;
     st.init(
         [&](int i) -> TileSrc<T> {
             switch (i) {
-                case 0: return {gB, L, kN, SM::kB, kPitch1, true};
+                case 0: return {gB, L, Ns, SM::kB, kPitch1, true};
                 case 1: return {gu, L, valid_rows, SM::kU, kT1, false};
                 default: return {gdl, L, valid_rows, SM::kDl, kT1, false};
             }
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
     const int64_t nchunks = (L + kT1 - 1) / kT1;
     if (nchunks > 0) {
         st.fetch(0, L, tid);
-        st.stash(smem);
+        st.stash(smem, zero_dead);
     }
     __syncthreads();
     for (int64_t c = 0; c < nchunks; c++) {
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
             }
         }
         __syncthreads();
-        if (c + 1 < nchunks) st.stash(smem);
+        if (c + 1 < nchunks) st.stash(smem, zero_dead);
         __syncthreads();
     }
 }
@@ -309,7 +312,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
-    const float aval = row_ok ? p.A[d * kN + n] : 0.0f;
+    const int Ns = p.nstate;   // state lanes n >= Ns carry zero A, B, C
+    const bool st_ok = row_ok && n < Ns;
+    const float aval = st_ok ? p.A[d * Ns + n] : 0.0f;
     const float a2 = aval * kLog2e;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
@@ -327,13 +332,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                                               : 0.0f;
     };
 
-    float g = (row_ok && p.dlast) ? p.dlast[(b * Dm + d) * kN + n] : 0.0f;
+    float g = (st_ok && p.dlast) ? p.dlast[(b * Dm + d) * Ns + n] : 0.0f;
     float dA_acc = 0.0f;     // this lane's state entry, summed over time
     float dD_acc = 0.0f;     // elements owned by this lane
     float dbias_acc = 0.0f;
 
-    const T *gB = static_cast<const T *>(p.B) + b * kN * L;
-    const T *gC = static_cast<const T *>(p.C) + b * kN * L;
+    const T *gB = static_cast<const T *>(p.B) + b * Ns * L;
+    const T *gC = static_cast<const T *>(p.C) + b * Ns * L;
+    const bool zero_dead = Ns < kN;   // B / C rows past dstate must read as zeros
     // this lane's row of the element-wise tensors; a row's 16 lanes load and
     // store 16 consecutive elements of a 16-step block
     const int64_t wavebase = (b * Dm + dw) * L;
@@ -365,8 +371,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     ChunkStager<T, VEC, kC, kStage ? 2 + 4 * kPieces : 2, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
-            if (i == 0) return {gB, L, kN, SM::kB, kPitch2, true};
-            if (i == 1) return {gC, L, kN, SM::kCc, kPitch2, true};
+            if (i == 0) return {gB, L, Ns, SM::kB, kPitch2, true};
+            if (i == 1) return {gC, L, Ns, SM::kCc, kPitch2, true};
             // element tiles in 16-row pieces; a piece with no valid row points
             // at the group's first row (it is not read)
             const int q = (i - 2) / kPieces, j = (i - 2) % kPieces;
@@ -451,7 +457,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     if (nch > 0) {
         load_next((int(nch) - 1) * kC);
         st.fetch((nch - 1) * kC, L, tid);
-        st.stash(smem + ((nch - 1) & 1) * SM::kBC);
+        st.stash(smem + ((nch - 1) & 1) * SM::kBC, zero_dead);
     }
     __syncthreads();
 
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
 
         // The next chunk's B / C go to the other buffer, whose last readers
         // (the chunk before this one) are behind the previous barrier.
-        if (c > 0) st.stash(smem + ((c - 1) & 1) * SM::kBC);
+        if (c > 0) st.stash(smem + ((c - 1) & 1) * SM::kBC, zero_dead);
         __syncthreads();
     }
 
@@ -645,7 +651,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         ws.dDp[b * Dm + d] = dD_acc;
         ws.dbiasp[b * Dm + d] = dbias_acc;
     }
-    if (p.dh0 && row_ok) p.dh0[(b * Dm + d) * kN + n] = g;
+    if (p.dh0 && st_ok) p.dh0[(b * Dm + d) * Ns + n] = g;
 }
 
 // ---------------------------------------------------------------------------
@@ -686,8 +692,9 @@ template <typename T, int VT>
 __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace ws) {
     const int64_t L = p.seqlen, Dm = p.dim, Bt = p.batch;
     const int64_t groups = ws.groups;
-    const int64_t nbc = Bt * kN * L / VT;   // dB / dC work items (VT divides L)
-    const int64_t na = Dm * kN;             // dA elements
+    const int64_t Ns = p.nstate;
+    const int64_t nbc = Bt * Ns * L / VT;   // dB / dC work items (VT divides L)
+    const int64_t na = Dm * Ns;             // dA elements
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < nbc) {
         // The sum over channels has one order whatever the reverse pass's
@@ -695,8 +702,8 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
         // three at a time, q = (p0 + p1) + p2, and the q in ascending order.
         // A 48-channel pass writes q itself; a 16-channel pass writes p.
         const int64_t e = i * VT;                                // (bb, n, t) element
-        const int64_t bb = e / (kN * L), rem = e - bb * kN * L;  // rem = n * L + t
-        const int64_t stride = kN * L;                           // one partial
+        const int64_t bb = e / (Ns * L), rem = e - bb * Ns * L;  // rem = n * L + t
+        const int64_t stride = kN * L;                           // one partial (16 states)
         const float *pb = ws.dBp + bb * groups * stride + rem;
         const float *pc = ws.dCp + bb * groups * stride + rem;
         float sb[VT] = {}, sc[VT] = {};
@@ -739,9 +746,10 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
             static_cast<T *>(p.dC)[e + k] = from_f32<T>(sc[k]);
         }
     } else if (i < nbc + na) {
-        const int64_t k = i - nbc;
+        const int64_t k = i - nbc;                      // (d, n) of dA
+        const int64_t src = (k / Ns) * kN + k % Ns;     // the 16-wide partial
         float s = 0.0f;
-        for (int64_t bb = 0; bb < Bt; bb++) s += ws.dAp[bb * na + k];
+        for (int64_t bb = 0; bb < Bt; bb++) s += ws.dAp[bb * Dm * kN + src];
         p.dA[k] = s;
     } else if (i < nbc + na + Dm) {
         const int64_t dd = i - nbc - na;
@@ -805,7 +813,7 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const bool v4 = p.seqlen % 4 == 0;   // 16-byte partial loads
-    const int64_t total = p.batch * kN * p.seqlen / (v4 ? 4 : 1) + p.dim * kN + p.dim;
+    const int64_t total = p.batch * p.nstate * p.seqlen / (v4 ? 4 : 1) + p.dim * p.nstate + p.dim;
     if (total > 0) {
         const dim3 fgrid(unsigned((total + 255) / 256));
         if (v4)

@@ -93,10 +93,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
-    float a2 = row_ok ? p.A[d * kN + n] * kLog2e : 0.0f;  // A in base-2 exponent units
+    const int Ns = p.nstate;       // state lanes n >= Ns carry zero A, B, C
+    const bool st_ok = row_ok && n < Ns;
+    float a2 = st_ok ? p.A[d * Ns + n] * kLog2e : 0.0f;  // A in base-2 exponent units
     float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
-    float h = (row_ok && p.h0) ? p.h0[(b * Dm + d) * kN + n] : 0.0f;
+    float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Ns + n] : 0.0f;
 
     // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the
     // per-row accesses address the wavefront's 4 rows from a scalar base with
@@ -108,8 +110,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
     const int64_t groupbase = (b * Dm + d0) * L;   // the group's first row (staged tiles)
-    const T *gB = static_cast<const T *>(p.B) + b * kN * L;
-    const T *gC = static_cast<const T *>(p.C) + b * kN * L;
+    const T *gB = static_cast<const T *>(p.B) + b * Ns * L;
+    const T *gC = static_cast<const T *>(p.C) + b * Ns * L;
+    const bool zero_dead = Ns < kN;   // B / C rows past dstate must read as zeros
     // element t of this lane's row (0 past the end and for rows past the
     // last channel); a row's 16 lanes read 16 consecutive elements
     auto elem_at = [&](const T *g, int t) {
@@ -121,8 +124,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     ChunkStager<T, VEC, kT, kStage ? 2 + 3 * (kRowsG / 16) : 2, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
-            if (i == 0) return {gB, L, kN, SM::kB, kPitch, true};
-            if (i == 1) return {gC, L, kN, SM::kC, kPitch, true};
+            if (i == 0) return {gB, L, Ns, SM::kB, kPitch, true};
+            if (i == 1) return {gC, L, Ns, SM::kC, kPitch, true};
             // element tiles in 16-row pieces; a piece with no valid row points
             // at the group's first row (it is not read)
             constexpr int kPieces = kRowsG / 16;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     if (nchunks > 0) {
         load_next(0);
         st.fetch(0, L, tid);
-        st.stash(smem);
+        st.stash(smem, zero_dead);
     }
     // Make the per-row parameter loads complete here.  Left pending into the
     // chunk loop, their first use there would be a wait on the in-order
@@ -265,11 +268,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
 
         // The next chunk's B / C go to the other buffer, whose last readers
         // (the chunk before this one) are behind the previous barrier.
-        if (c + 1 < nchunks) st.stash(smem + ((c + 1) & 1) * SM::kBC);
+        if (c + 1 < nchunks) st.stash(smem + ((c + 1) & 1) * SM::kBC, zero_dead);
         __syncthreads();
     }
 
-    if (p.last_state && row_ok) p.last_state[(b * Dm + d) * kN + n] = h;
+    if (p.last_state && st_ok) p.last_state[(b * Dm + d) * Ns + n] = h;
 }
 
 template <typename T, int VEC, int NW>

@@ -9,8 +9,13 @@
 
 namespace ssk {
 
+// Kernels keep 16 state lanes per row; with dstate N < 16 the lanes n >= N
+// carry zero A, B and C (their state stays exactly zero) and the per-state
+// tensors are read and written with stride N.  Internal buffers (saved
+// block states, workspace partials) stay 16 wide.
 struct ScanParams {
     int64_t batch, dim, seqlen;
+    int nstate;   // dstate, 1..16
     const void *u, *delta;
     const float *A;
     const void *B, *C;
@@ -63,6 +68,7 @@ struct BwdParams : ScanParams {
 
 struct DecodeParams {
     int64_t batch, dim;
+    int nstate;   // dstate, 1..16
     float *state;
     const void *u, *delta;
     const float *A;

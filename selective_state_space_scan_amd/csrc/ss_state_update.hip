@@ -27,7 +27,10 @@ __device__ __forceinline__ float xor_lane(float v) {
         float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (MASK << 10) | 0x1f));
 }
 
-template <typename T>
+// kFull: dstate 16, every lane a float4 of the state.  Otherwise (dstate
+// 1..15) the same lanes and sums with element loads, states n >= dstate
+// held at zero.
+template <typename T, bool kFull>
 __global__ __launch_bounds__(kThreads) void ss_state_update_kernel(DecodeParams p) {
     const int64_t rows = p.batch * p.dim;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 2);
@@ -47,13 +50,31 @@ __global__ __launch_bounds__(kThreads) void ss_state_update_kernel(DecodeParams 
     float4 a = h;
     float bb[4] = {0.f, 0.f, 0.f, 0.f}, cc[4] = {0.f, 0.f, 0.f, 0.f};
     float uu = 0.f, dlr = 0.f, zz = 0.f, bias = 0.f, dskip = 0.f;
+    const int Ns = kFull ? kN : p.nstate;
     if (ok) {
-        h = reinterpret_cast<const float4 *>(p.state)[rr * 4 + q];
-        a = reinterpret_cast<const float4 *>(p.A)[d * 4 + q];
+        if constexpr (kFull) {
+            h = reinterpret_cast<const float4 *>(p.state)[rr * 4 + q];
+            a = reinterpret_cast<const float4 *>(p.A)[d * 4 + q];
+        } else {
+            float hs[4] = {0.f, 0.f, 0.f, 0.f}, as[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int n = 4 * q + e;
+                if (n < Ns) {
+                    hs[e] = p.state[rr * Ns + n];
+                    as[e] = p.A[d * Ns + n];
+                }
+            }
+            h = make_float4(hs[0], hs[1], hs[2], hs[3]);
+            a = make_float4(as[0], as[1], as[2], as[3]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            bb[e] = to_f32<T>(gB[b * kN + 4 * q + e]);
-            cc[e] = to_f32<T>(gC[b * kN + 4 * q + e]);
+            const int n = 4 * q + e;
+            if (kFull || n < Ns) {
+                bb[e] = to_f32<T>(gB[b * Ns + n]);
+                cc[e] = to_f32<T>(gC[b * Ns + n]);
+            }
         }
         uu = to_f32<T>(gu[rr]);
         dlr = to_f32<T>(gdl[rr]);
@@ -76,7 +97,13 @@ __global__ __launch_bounds__(kThreads) void ss_state_update_kernel(DecodeParams 
     part += xor_lane<1>(part);
     part += xor_lane<2>(part);
     if (ok) {
-        reinterpret_cast<float4 *>(p.state)[rr * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        if constexpr (kFull) {
+            reinterpret_cast<float4 *>(p.state)[rr * 4 + q] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                if (4 * q + e < Ns) p.state[rr * Ns + 4 * q + e] = hv[e];
+        }
         if (q == 0) {
             float y = part + dskip * uu;
             if (p.z) y *= zz * sigmoid_f32(zz);
@@ -91,10 +118,15 @@ hipError_t launch_state_update(const DecodeParams &p, bool bf16, hipStream_t str
     const int64_t rows = p.batch * p.dim;
     if (rows == 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    if (bf16)
-        hipLaunchKernelGGL((ss_state_update_kernel<bf16_t>), grid, dim3(kThreads), 0, stream, p);
+    const bool full = p.nstate == kN;
+    if (bf16 && full)
+        hipLaunchKernelGGL((ss_state_update_kernel<bf16_t, true>), grid, dim3(kThreads), 0, stream, p);
+    else if (bf16)
+        hipLaunchKernelGGL((ss_state_update_kernel<bf16_t, false>), grid, dim3(kThreads), 0, stream, p);
+    else if (full)
+        hipLaunchKernelGGL((ss_state_update_kernel<float, true>), grid, dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((ss_state_update_kernel<float>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((ss_state_update_kernel<float, false>), grid, dim3(kThreads), 0, stream, p);
     profile_mark(stream);
     return hipGetLastError();
 }

@@ -181,7 +181,17 @@ struct ChunkStager {
         else fetch_tail(t0, L, tid);
     }
 
-    __device__ __forceinline__ void stash(char *smem) {
+    // Writes the prefetched words to LDS.  With zero_dead (uniform) the words
+    // of slots that are not live are written as zeros, for tiles whose dead
+    // rows are read (the unused state rows of B and C when dstate < 16).
+    __device__ __forceinline__ void stash(char *smem, bool zero_dead = false) {
+        if (zero_dead) {
+#pragma unroll
+            for (int k = 0; k < kSlots; k++)
+                if (!((live >> k) & 1u))
+#pragma unroll
+                    for (int w = 0; w < kWords; w++) reg[k][w] = 0u;
+        }
 #pragma unroll
         for (int k = 0; k < kSlots; k++) {
             if (!used[k]) continue;

@@ -49,7 +49,9 @@ def test_ckpt_size(lib):
     assert lib.ss_ckpt_size(2, 32, 16, 65) == 2 * 32 * 5 * 16 * 4 + 2 * 32 * 65 * 4
     assert lib.ss_ckpt_size(1, 1, 16, 1) == 256 + 4
     assert lib.ss_ckpt_size(2, 32, 16, 0) == 0
-    assert lib.ss_ckpt_size(2, 32, 8, 64) == 0
+    # the block states are 16 wide for any dstate up to 16
+    assert lib.ss_ckpt_size(2, 32, 8, 64) == lib.ss_ckpt_size(2, 32, 16, 64)
+    assert lib.ss_ckpt_size(2, 32, 17, 64) == 0
 
 
 def test_bwd_misaligned_ckpt(lib):
@@ -82,7 +84,7 @@ def test_fwd_misaligned_pointer(lib, arg):
 @pytest.mark.parametrize("kw,status,word", [
     (dict(batch=-1), EINVAL, "batch"), (dict(dim=-3), EINVAL, "dim"),
     (dict(seqlen=-1), EINVAL, "seqlen"), (dict(dstate=0), EINVAL, "dstate"),
-    (dict(dstate=8), EUNSUP, "dstate"), (dict(dstate=64), EUNSUP, "dstate"),
+    (dict(dstate=17), EUNSUP, "dstate"), (dict(dstate=64), EUNSUP, "dstate"),
     (dict(io=7), EINVAL, "io_dtype"), (dict(batch=70000), EUNSUP, "batch"),
     (dict(seqlen=(1 << 26) + 1), EUNSUP, "seqlen"),
 ])
@@ -144,7 +146,9 @@ def test_workspace_size_is_monotone_and_zero_when_invalid(lib):
     assert lib.ss_bwd_workspace_size(4, 32, 16, 64, 0) > base
     assert lib.ss_bwd_workspace_size(2, 64, 16, 64, 0) > base
     assert lib.ss_bwd_workspace_size(2, 32, 16, 128, 0) > base
-    assert lib.ss_bwd_workspace_size(2, 32, 8, 64, 0) == 0
+    # internal buffers are 16 states wide for any dstate up to 16
+    assert lib.ss_bwd_workspace_size(2, 32, 8, 64, 0) == base
+    assert lib.ss_bwd_workspace_size(2, 32, 17, 64, 0) == 0
     assert lib.ss_bwd_workspace_size(-1, 32, 16, 64, 0) == 0
 
 
@@ -152,7 +156,7 @@ def test_decode_checks(lib):
     st = lib.ss_state_update(4, 32, 16, 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
                              1, FAKE, None)
     assert st == EINVAL and "state" in _msg(lib)
-    st = lib.ss_state_update(4, 32, 12, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+    st = lib.ss_state_update(4, 32, 17, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
                              1, FAKE, None)
     assert st == EUNSUP and "dstate" in _msg(lib)
     assert lib.ss_state_update(0, 32, 16, 1, None, None, None, None, None, None, None, None,

@@ -132,6 +132,42 @@ def test_bwd_rows_do_not_depend_on_batch(dim, L, io):
             assert torch.equal(a, b1), f"{k} entry {bi}"
 
 
+@pytest.mark.parametrize("batch,dim,N,L,io", [(2, 40, 1, 64, "f32"), (2, 40, 5, 96, "bf16"),
+                                              (2, 24, 12, 70, "f32"), (8, 1544, 8, 64, "f32")])
+def test_bwd_smaller_dstate(batch, dim, N, L, io):
+    """d_state below 16, every gradient against the oracle (the last shape
+    takes the 48-channel reverse pass), and a backward with the forward's
+    saved record giving the same bits as one that recomputes it."""
+    require_gpu()
+    w = ssin.custom("bwd", batch, dim, N, L, io, seed=17 * N + L + dim)
+    arr = ssin.make(w)
+    say(f"bwd dstate {w.name}")
+    d = dev_inputs(arr)
+    rng = np.random.default_rng(N + 1)
+    h0 = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    dl = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    g = run_bwd(d, w, h0=to_dev(h0), dlast=to_dev(dl), want_dh0=True)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(arr, w, h0=h0.astype(np.float64), dlast=dl.astype(np.float64))
+    for k in KEYS:
+        if k not in ref:
+            continue
+        tol = TOL["f32"] if k in ("dA", "dD", "ddelta_bias", "dh0") else TOL[io]
+        assert_close(to_host(g[k]), ref[k], tol, f"{k} N={N}")
+    ck = binding.ss_ckpt_empty(d["u"], dstate=N)
+    binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"],
+                   w.softplus, h0=to_dev(h0), ckpt=ck)
+    g2 = binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                        d["delta_bias"], w.softplus, d["dout"], h0=to_dev(h0), dlast=to_dev(dl),
+                        want_dh0=True, ckpt=ck)
+    torch.cuda.synchronize()
+    for k in g:
+        a, b2 = g[k], g2[k]
+        if a.dtype == torch.bfloat16:
+            a, b2 = a.view(torch.int16), b2.view(torch.int16)
+        assert torch.equal(a, b2), f"{k} with saved record"
+
+
 def test_bwd_zero_length_passes_dlast_through():
     require_gpu()
     w = ssin.custom("bwd", 2, 32, 16, 0, "f32", seed=4)

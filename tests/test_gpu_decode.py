@@ -57,6 +57,23 @@ def test_decode_full_size_and_batch_invariance(io):
             assert torch.equal(y1[0], y[b]), f"y row {b}"
 
 
+@pytest.mark.parametrize("N,io", [(1, "f32"), (6, "bf16"), (13, "f32")])
+def test_decode_smaller_dstate(N, io):
+    """d_state below 16 (element loads, unused state lanes held at zero)."""
+    require_gpu()
+    w = ssin.custom("decode", 8, 40, N, 1, io, seed=N)
+    arr = ssin.make(w)
+    d = dev_inputs(arr)
+    st = to_dev(arr["state"])
+    y = step(d, w, st)
+    torch.cuda.synchronize()
+    x = {k: widen(v) for k, v in arr.items()}
+    rs, ry = oracle.state_update(x["state"], x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"],
+                                 x["z"], x["delta_bias"], True, threads=8)
+    assert_close(to_host(y), ry, TOL[io], f"y N={N}")
+    assert_close(to_host(st), rs, TOL["f32"], f"state N={N}")
+
+
 def test_decode_ragged_rows_and_flags():
     require_gpu()
     for flags in ({}, dict(has_z=False, has_D=False, has_bias=False)):

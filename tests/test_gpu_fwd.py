@@ -72,6 +72,25 @@ def test_fwd_small_elementwise(batch, dim, L, io, flags):
         assert_close(to_host(last), rl, TOL["f32"], f"last_state h0={use_h0}")
 
 
+@pytest.mark.parametrize("N,io,L", [(1, "f32", 70), (4, "bf16", 64), (7, "f32", 100),
+                                    (12, "bf16", 40)])
+def test_fwd_smaller_dstate(N, io, L):
+    """d_state below 16: the kernels keep 16 state lanes and the unused ones
+    must add nothing (scalar and 16-byte load paths)."""
+    require_gpu()
+    w = ssin.custom("fwd", 2, 40, N, L, io, seed=31 * N + L)
+    arr = ssin.make(w)
+    say(f"fwd dstate {w.name}")
+    d = dev_inputs(arr)
+    h0 = np.random.default_rng(N).standard_normal((2, 40, N)).astype(np.float32)
+    for use_h0 in (False, True):
+        y, last = run_fwd(d, w, h0=to_dev(h0) if use_h0 else None, last=True)
+        torch.cuda.synchronize()
+        ry, rl = oracle_fwd(arr, w.softplus, h0=h0.astype(np.float64) if use_h0 else None)
+        assert_close(to_host(y), ry, TOL[io], f"y N={N} h0={use_h0}")
+        assert_close(to_host(last), rl, TOL["f32"], f"last_state N={N} h0={use_h0}")
+
+
 def test_fwd_empty_and_zero_length():
     require_gpu()
     w = ssin.custom("fwd", 2, 32, 16, 0, "f32", seed=3)
