@@ -10,7 +10,8 @@ back as float64 numpy arrays.  The arithmetic itself lives entirely in
 ``ss_oracle.c``; this file only marshals arrays and, when asked for more
 than one thread, splits independent rows (forward, state update) or batch
 entries (backward) across threads and folds the per-thread parameter
-gradients in ascending batch order.
+gradients in ascending batch order.  The causal convolution routines
+(``conv_fwd``, ``conv_bwd``, ``conv_update``) follow the same pattern.
 """
 from __future__ import annotations
 
@@ -61,6 +62,12 @@ def _load():
             lib.sso_state_update.argtypes = ([i64, i64, i64] + [dp] * 9 + [c_int] + [dp]
                                              + [i64, i64])
             lib.sso_state_update.restype = None
+            lib.sso_conv_fwd.argtypes = [i64] * 4 + [dp] * 3 + [c_int] + [dp] * 3 + [i64, i64]
+            lib.sso_conv_fwd.restype = None
+            lib.sso_conv_bwd.argtypes = [i64] * 4 + [dp] * 3 + [c_int] + [dp] * 6 + [i64, i64]
+            lib.sso_conv_bwd.restype = None
+            lib.sso_conv_update.argtypes = [i64] * 3 + [dp] * 4 + [c_int] + [dp]
+            lib.sso_conv_update.restype = None
             _lib = lib
     return _lib
 
@@ -186,3 +193,82 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
             list(ex.map(lambda rg: lib.sso_state_update(*args, rg[0], rg[1]),
                         _split(rows, threads)))
     return st, y
+
+
+def conv_fwd(x, weight, bias=None, silu=True, init_state=None, threads: int = 1):
+    """Causal depthwise convolution (+ SiLU).  Returns ``(out, final_state)``.
+
+    x: (batch, dim, L); weight: (dim, K); bias: (dim,) or None;
+    init_state: (batch, dim, K-1) inputs before t = 0, or None (zeros).
+    final_state: (batch, dim, K-1), the last K-1 inputs.
+    """
+    lib = _load()
+    x, weight, bias, s0 = map(_f64, (x, weight, bias, init_state))
+    nb, nd, nl = x.shape
+    nk = weight.shape[1]
+    out = np.zeros((nb, nd, nl))
+    sf = np.zeros((nb, nd, nk - 1))
+    args = (nb, nd, nl, nk, _p(x), _p(weight), _p(bias), int(bool(silu)), _p(s0), _p(out),
+            _p(sf))
+    rows = nb * nd
+    if threads <= 1 or rows < 2:
+        lib.sso_conv_fwd(*args, 0, rows)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda rg: lib.sso_conv_fwd(*args, rg[0], rg[1]),
+                        _split(rows, threads)))
+    return out, sf
+
+
+def conv_bwd(x, weight, bias=None, silu=True, init_state=None, dout=None, threads: int = 1):
+    """Backward of ``sum(dout * conv_fwd(...)[0])``.
+
+    Returns a dict with dx, dweight and, when given, dbias and dinit_state.
+    """
+    lib = _load()
+    x, weight, bias, s0, dout = map(_f64, (x, weight, bias, init_state, dout))
+    nb, nd, nl = x.shape
+    nk = weight.shape[1]
+    dx = np.zeros((nb, nd, nl))
+    ds0 = np.zeros((nb, nd, nk - 1)) if s0 is not None else None
+    pieces = _split(nb, threads)
+    part = [(np.zeros((nd, nk)), np.zeros(nd)) for _ in pieces]
+
+    def run(i):
+        b0, b1 = pieces[i]
+        dw_i, db_i = part[i]
+        lib.sso_conv_bwd(nb, nd, nl, nk, _p(x), _p(weight), _p(bias), int(bool(silu)),
+                         _p(s0), _p(dout), _p(dx), _p(dw_i), _p(db_i), _p(ds0), b0, b1)
+
+    if len(pieces) == 1:
+        run(0)
+    else:
+        with ThreadPoolExecutor(len(pieces)) as ex:
+            list(ex.map(run, range(len(pieces))))
+    dw = np.zeros((nd, nk))
+    db = np.zeros(nd)
+    for dw_i, db_i in part:
+        dw += dw_i
+        db += db_i
+    out = dict(dx=dx, dweight=dw)
+    if bias is not None:
+        out["dbias"] = db
+    if s0 is not None:
+        out["dinit_state"] = ds0
+    return out
+
+
+def conv_update(state, x, weight, bias=None, silu=True):
+    """One input per row.  Returns ``(new_state, out)``; the input is not modified.
+
+    state: (batch, dim, K-1); x: (batch, dim); weight: (dim, K).
+    """
+    lib = _load()
+    st = _f64(state).copy()
+    x, weight, bias = map(_f64, (x, weight, bias))
+    nb, nd = x.shape
+    nk = weight.shape[1]
+    out = np.zeros((nb, nd))
+    lib.sso_conv_update(nb, nd, nk, _p(st), _p(x), _p(weight), _p(bias), int(bool(silu)),
+                        _p(out))
+    return st, out

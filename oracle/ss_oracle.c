@@ -245,3 +245,122 @@ void sso_state_update(int64_t nb, int64_t nd, int64_t ns,
         y[r] = ypre;
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Causal depthwise convolution over time, optionally followed by SiLU.
+ *
+ * The state-spaces/mamba README's Mamba block ("Usage / Mamba Block")
+ * configures a local convolution of width d_conv (4) in front of the
+ * selective SSM, and the mamba-rs README's "Quick start (CPU)" carries its
+ * window in the decoding state (MambaState::zeros(..., d_conv)).  Neither
+ * page prints the operation; the reading used here is the causal, per
+ * channel (depthwise) convolution of width K, with SiLU applied when asked:
+ *
+ *   pre_t = bias[d] + sum_{k=0}^{K-1} w[d,k] * x_{t-(K-1)+k}
+ *   out_t = silu(pre_t)  (or pre_t)
+ *
+ * where the inputs before t = 0 come from an initial window s0[b,d,j] =
+ * x_{j-(K-1)} (j = 0..K-2), zero when no window is given.  The final window
+ * is x_{L-(K-1)+j}, j = 0..K-2 (entries before t = 0 again from s0 or 0).
+ * The decode update steps that window by one input.
+ *
+ * Layouts: x, out, dout, dx (nb, nd, nl); w, dw (nd, nk); bias, dbias (nd);
+ *          s0, s_final, ds0, decode state (nb, nd, nk - 1); decode x, out
+ *          (nb, nd).
+ * ------------------------------------------------------------------------ */
+
+/* x_tt of row r, tt in [-(nk-1), nl): from x, or from the initial window */
+static double sso_conv_in(const double *x, const double *s0, int64_t r, int64_t nl,
+                          int64_t nk, int64_t tt)
+{
+    if (tt >= 0) return x[r * nl + tt];
+    return s0 ? s0[r * (nk - 1) + (tt + nk - 1)] : 0.0;
+}
+
+static double sso_conv_pre(const double *x, const double *w, const double *bias,
+                           const double *s0, int64_t r, int64_t d, int64_t nl, int64_t nk,
+                           int64_t t)
+{
+    double acc = bias ? bias[d] : 0.0;
+    for (int64_t k = 0; k < nk; k++)
+        acc += w[d * nk + k] * sso_conv_in(x, s0, r, nl, nk, t - (nk - 1) + k);
+    return acc;
+}
+
+/* rows r0 <= r < r1 */
+void sso_conv_fwd(int64_t nb, int64_t nd, int64_t nl, int64_t nk,
+                  const double *x, const double *w, const double *bias, int silu,
+                  const double *s0, double *out, double *s_final, int64_t r0, int64_t r1)
+{
+    (void)nb;
+    for (int64_t r = r0; r < r1; r++) {
+        int64_t d = r % nd;
+        for (int64_t t = 0; t < nl; t++) {
+            double pre = sso_conv_pre(x, w, bias, s0, r, d, nl, nk, t);
+            out[r * nl + t] = silu ? pre * sso_sigmoid(pre) : pre;
+        }
+        if (s_final)
+            for (int64_t j = 0; j < nk - 1; j++)
+                s_final[r * (nk - 1) + j] = sso_conv_in(x, s0, r, nl, nk, nl - (nk - 1) + j);
+    }
+}
+
+/*
+ * Backward of sum(dout * out).  With g_t = dout_t * silu'(pre_t) (or dout_t),
+ * silu'(p) = s (1 + p (1 - s)), s = sigmoid(p):
+ *   dx_tt   = sum over (t, k) with t - (K-1) + k = tt of w[d,k] g_t
+ *   ds0_j   = the same sum for tt = j - (K-1) < 0
+ *   dw[d,k] = sum_{b,t} g_t x_{t-(K-1)+k},   dbias[d] = sum_{b,t} g_t
+ * Batch entries b0 <= b < b1; dw and dbias are accumulated (the caller
+ * zeroes them), over b, then t, ascending.
+ */
+void sso_conv_bwd(int64_t nb, int64_t nd, int64_t nl, int64_t nk,
+                  const double *x, const double *w, const double *bias, int silu,
+                  const double *s0, const double *dout, double *dx, double *dw,
+                  double *dbias, double *ds0, int64_t b0, int64_t b1)
+{
+    (void)nb;
+    for (int64_t b = b0; b < b1; b++) {
+        for (int64_t d = 0; d < nd; d++) {
+            int64_t r = b * nd + d;
+            for (int64_t t = 0; t < nl; t++) dx[r * nl + t] = 0.0;
+            if (ds0)
+                for (int64_t j = 0; j < nk - 1; j++) ds0[r * (nk - 1) + j] = 0.0;
+            for (int64_t t = 0; t < nl; t++) {
+                double pre = sso_conv_pre(x, w, bias, s0, r, d, nl, nk, t);
+                double g = dout[r * nl + t];
+                if (silu) {
+                    double s = sso_sigmoid(pre);
+                    g *= s * (1.0 + pre * (1.0 - s));
+                }
+                if (dbias) dbias[d] += g;
+                for (int64_t k = 0; k < nk; k++) {
+                    int64_t tt = t - (nk - 1) + k;
+                    dw[d * nk + k] += g * sso_conv_in(x, s0, r, nl, nk, tt);
+                    if (tt >= 0)
+                        dx[r * nl + tt] += w[d * nk + k] * g;
+                    else if (ds0)
+                        ds0[r * (nk - 1) + (tt + nk - 1)] += w[d * nk + k] * g;
+                }
+            }
+        }
+    }
+}
+
+/* One input per row: out = silu(bias + sum_k w[k] window_k) with window =
+ * (state[0..K-2], x); the state then drops its oldest entry and takes x. */
+void sso_conv_update(int64_t nb, int64_t nd, int64_t nk, double *state, const double *x,
+                     const double *w, const double *bias, int silu, double *out)
+{
+    for (int64_t r = 0; r < nb * nd; r++) {
+        int64_t d = r % nd;
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < nk; k++) {
+            double v = (k < nk - 1) ? state[r * (nk - 1) + k] : x[r];
+            acc += w[d * nk + k] * v;
+        }
+        out[r] = silu ? acc * sso_sigmoid(acc) : acc;
+        for (int64_t j = 0; j < nk - 1; j++)
+            state[r * (nk - 1) + j] = (j + 1 < nk - 1) ? state[r * (nk - 1) + j + 1] : x[r];
+    }
+}

@@ -42,6 +42,18 @@ MUTATIONS = {
                               "raw_grad *= 1.0;"),
     "state_update_B_batch_ignored": ("*h = abar * *h + dt * B[b * ns + n] * ut;",
                                      "*h = abar * *h + dt * B[n] * ut;"),
+    "conv_taps_reversed": ("acc += w[d * nk + k] * sso_conv_in(x, s0, r, nl, nk, t - (nk - 1) + k);",
+                           "acc += w[d * nk + (nk - 1 - k)] * sso_conv_in(x, s0, r, nl, nk, t - (nk - 1) + k);"),
+    "conv_window_offset": ("return s0 ? s0[r * (nk - 1) + (tt + nk - 1)] : 0.0;",
+                           "return s0 ? s0[r * (nk - 1) + (-tt - 1)] : 0.0;"),
+    "conv_bias_dropped": ("    double acc = bias ? bias[d] : 0.0;\n    for (int64_t k = 0; k < nk; k++)\n        acc += w[d * nk + k] * sso_conv_in",
+                          "    double acc = 0.0;\n    for (int64_t k = 0; k < nk; k++)\n        acc += w[d * nk + k] * sso_conv_in"),
+    "conv_silu_derivative_wrong": ("g *= s * (1.0 + pre * (1.0 - s));", "g *= s;"),
+    "conv_dx_wrong_tap": ("dx[r * nl + tt] += w[d * nk + k] * g;", "dx[r * nl + tt] += w[d * nk + (nk - 1 - k)] * g;"),
+    "conv_dwindow_dropped": ("ds0[r * (nk - 1) + (tt + nk - 1)] += w[d * nk + k] * g;",
+                             "ds0[r * (nk - 1) + (tt + nk - 1)] += 0.0 * g;"),
+    "conv_update_shift_wrong": ("state[r * (nk - 1) + j] = (j + 1 < nk - 1) ? state[r * (nk - 1) + j + 1] : x[r];",
+                                "state[r * (nk - 1) + j] = (j > 0) ? state[r * (nk - 1) + j - 1] : x[r];"),
 }
 
 
@@ -61,6 +73,7 @@ def test_pins_catch_planted_mistake(name):
         res = subprocess.run(
             [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
              os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-             os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py")],
+             os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py"),
+             os.path.join(ROOT, "tests", "test_oracle_conv_pins.py")],
             cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
         assert res.returncode != 0, f"pins did not catch mutation {name}:\n{res.stdout[-2000:]}"
