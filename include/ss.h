@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 4
+#define SS_ABI_VERSION 5
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -155,9 +155,72 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dty
                           void *stream);
 
 /*
+ * Causal depthwise convolution over time, the local convolution of width
+ * d_conv (4 in the state-spaces/mamba README, "Usage", Mamba block) that
+ * feeds the scan's u, with the window the mamba-rs README ("Quick start
+ * (CPU)") keeps in its decode state.  For batch b, channel d, K = width,
+ * H = K - 1:
+ *
+ *   pre_t = bias[d] + sum_{k=0}^{K-1} weight[d,k] * x_{t-H+k}
+ *   out_t = silu(pre_t) if silu != 0, else pre_t
+ *
+ * where x_{-H} .. x_{-1} are init_state[b,d,0..H-1] (zeros when init_state
+ * is NULL).  The pages print no formula; this is the plainest reading of a
+ * causal per-channel convolution in front of the scan.
+ *
+ * Layouts (row-major, contiguous):
+ *   x, out, dout, dx            : (batch, dim, seqlen)   io dtype
+ *   weight, dweight             : (dim, width)           float
+ *   bias, dbias                 : (dim)                  float
+ *   init_state, final_state,
+ *   dinit_state, decode state   : (batch, dim, width-1)  float
+ *   decode x, out               : (batch, dim)           io dtype
+ * width 1..4 (SS_EUNSUPPORTED above 4); seqlen <= 2^26; all pointers
+ * 16-byte aligned.  Every sum runs in f32 in a fixed order; results are
+ * bit-reproducible and a row's out / dx do not depend on the batch size.
+ */
+
+/*
+ * Forward.  Writes out and, when final_state is non-NULL, the last H inputs
+ * x_{L-H} .. x_{L-1} (reaching into init_state, or zeros, when seqlen < H),
+ * so a following call with init_state = that final_state continues the
+ * sequence.  bias, init_state, final_state may be NULL; final_state must
+ * not overlap init_state.
+ */
+ss_status ss_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,
+                        const void *x, const float *weight, const float *bias, int silu,
+                        const float *init_state, void *out, float *final_state, void *stream);
+
+/* Bytes of device workspace ss_conv1d_bwd needs (0 for empty shapes). */
+size_t ss_conv1d_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t width);
+
+/*
+ * Backward of sum(dout * out) with respect to x (dx, required), weight
+ * (dweight, required; summed over batch and time), bias (dbias, given
+ * exactly when bias is) and the initial window (dinit_state, optional; may
+ * be given without init_state: the gradient at a zero window).  workspace:
+ * ss_conv1d_bwd_workspace_size() bytes of caller-owned device memory,
+ * 16-byte aligned, not read before written.
+ */
+ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,
+                        const void *x, const float *weight, const float *bias, int silu,
+                        const float *init_state, const void *dout, void *dx, float *dweight,
+                        float *dbias, float *dinit_state, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * Decode step: out = act(bias + sum_k weight[d,k] * window_k) with window =
+ * (state[b,d,0..H-1], x[b,d]); then state drops its oldest entry and takes
+ * x (in place).  state may be NULL when width == 1.
+ */
+ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dtype, float *state,
+                           const void *x, const float *weight, const float *bias, int silu,
+                           void *out, void *stream);
+
+/*
  * Profiling aid for callers that time the library's kernels one by one
  * (not needed for normal use).  When `events` is non-NULL, every later
- * ss_fwd / ss_bwd / ss_state_update call on this thread records the next
+ * ss_fwd / ss_bwd / ss_state_update / ss_conv1d_* call on this thread records the next
  * unused entry of `events` (each a hipEvent_t created by the caller) on its
  * stream before its first kernel and after each kernel it launches, until
  * `count` entries are used.  ss_profile_events(NULL, 0) switches it off.

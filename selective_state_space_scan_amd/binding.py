@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 4
+ABI_VERSION = 5
 _lock = threading.Lock()
 _lib = None
 
@@ -67,6 +67,15 @@ def load() -> ctypes.CDLL:
             lib.ss_state_update.restype = c_int
             lib.ss_state_update.argtypes = ([i64] * 3 + [c_int] + [vp] * 9 + [c_int]
                                             + [vp] * 2)
+            lib.ss_conv1d_fwd.restype = c_int
+            lib.ss_conv1d_fwd.argtypes = [i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 4
+            lib.ss_conv1d_bwd_workspace_size.restype = sz
+            lib.ss_conv1d_bwd_workspace_size.argtypes = [i64] * 4
+            lib.ss_conv1d_bwd.restype = c_int
+            lib.ss_conv1d_bwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 7
+                                          + [sz, vp])
+            lib.ss_conv1d_update.restype = c_int
+            lib.ss_conv1d_update.argtypes = [i64] * 3 + [c_int] + [vp] * 4 + [c_int] + [vp] * 2
             _lib = lib
     return _lib
 
@@ -213,4 +222,74 @@ def ss_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
                                _ptr(delta), _f32(A, "A"), _ptr(B), _ptr(C), _f32(D, "D"),
                                _ptr(z), _f32(delta_bias, "delta_bias"), int(bool(delta_softplus)),
                                _ptr(out), _stream()))
+    return out
+
+
+def ss_conv1d_fwd(x, weight, bias=None, silu=True, init_state=None, out=None,
+                  final_state=None, return_final_state=False):
+    """Causal depthwise convolution (+ SiLU); returns ``out`` or ``(out, final_state)``.
+
+    x: (batch, dim, L) float32 or bfloat16; weight: (dim, width), bias: (dim,),
+    init_state / final_state: (batch, dim, width - 1), all float32.
+    """
+    lib = load()
+    batch, dim, seqlen = x.shape
+    width = weight.shape[1]
+    io = _io_dtype(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if return_final_state and final_state is None:
+        final_state = torch.empty(batch, dim, width - 1, dtype=torch.float32, device=x.device)
+    _check(lib.ss_conv1d_fwd(batch, dim, seqlen, width, io, _ptr(x), _f32(weight, "weight"),
+                             _f32(bias, "bias"), int(bool(silu)), _f32(init_state, "init_state"),
+                             _ptr(out), _f32(final_state, "final_state"), _stream()))
+    return (out, final_state) if (return_final_state or final_state is not None) else out
+
+
+def ss_conv1d_bwd_workspace_size(batch, dim, seqlen, width) -> int:
+    return int(load().ss_conv1d_bwd_workspace_size(batch, dim, seqlen, width))
+
+
+def ss_conv1d_bwd(x, weight, bias=None, silu=True, init_state=None, dout=None,
+                  want_dinit_state=False, workspace=None):
+    """Backward of ``sum(dout * ss_conv1d_fwd(...))``.
+
+    Returns a dict with dx, dweight, and dbias when bias is given, dinit_state
+    when init_state is given or ``want_dinit_state``.
+    """
+    lib = load()
+    batch, dim, seqlen = x.shape
+    width = weight.shape[1]
+    io = _io_dtype(x)
+    _same_io(io, dout)
+    dev = x.device
+    g = dict(dx=torch.empty_like(x),
+             dweight=torch.empty(dim, width, dtype=torch.float32, device=dev))
+    if bias is not None:
+        g["dbias"] = torch.empty(dim, dtype=torch.float32, device=dev)
+    if want_dinit_state or init_state is not None:
+        g["dinit_state"] = torch.empty(batch, dim, width - 1, dtype=torch.float32, device=dev)
+    need = ss_conv1d_bwd_workspace_size(batch, dim, seqlen, width)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.ss_conv1d_bwd(batch, dim, seqlen, width, io, _ptr(x), _f32(weight, "weight"),
+                             _f32(bias, "bias"), int(bool(silu)), _f32(init_state, "init_state"),
+                             _ptr(dout), _ptr(g["dx"]), _ptr(g["dweight"]), _ptr(g.get("dbias")),
+                             _ptr(g.get("dinit_state")), _ptr(workspace), workspace.numel(),
+                             _stream()))
+    return g
+
+
+def ss_conv1d_update(state, x, weight, bias=None, silu=True, out=None):
+    """Decode step of the convolution; ``state`` (batch, dim, width - 1) float32
+    is shifted in place.  x: (batch, dim).  Returns the output (batch, dim)."""
+    lib = load()
+    batch, dim = x.shape
+    width = weight.shape[1]
+    io = _io_dtype(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.ss_conv1d_update(batch, dim, width, io, _f32(state, "state"), _ptr(x),
+                                _f32(weight, "weight"), _f32(bias, "bias"), int(bool(silu)),
+                                _ptr(out), _stream()))
     return out

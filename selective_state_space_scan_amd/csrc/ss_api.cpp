@@ -264,3 +264,133 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dty
 }
 
 }  // extern "C"
+
+namespace {
+
+ss_status check_conv_dims(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io) {
+    if (batch < 0) return fail(SS_EINVAL, "batch must be >= 0 (got %lld)", (long long)batch);
+    if (dim < 0) return fail(SS_EINVAL, "dim must be >= 0 (got %lld)", (long long)dim);
+    if (seqlen < 0) return fail(SS_EINVAL, "seqlen must be >= 0 (got %lld)", (long long)seqlen);
+    if (width < 1) return fail(SS_EINVAL, "width must be >= 1 (got %lld)", (long long)width);
+    if (io != SS_F32 && io != SS_BF16)
+        return fail(SS_EINVAL, "io_dtype must be SS_F32 (0) or SS_BF16 (1) (got %d)", io);
+    if (width > ssk::kConvMaxWidth)
+        return fail(SS_EUNSUPPORTED, "width %lld is not supported (this build handles 1..%d)",
+                    (long long)width, ssk::kConvMaxWidth);
+    if (seqlen > kMaxSeq)
+        return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
+                    (long long)kMaxSeq);
+    if (dim > kMaxDim)
+        return fail(SS_EUNSUPPORTED, "dim %lld exceeds %lld", (long long)dim, (long long)kMaxDim);
+    // one wavefront per (row, segment), at most 2^32 of them (2^30 workgroups)
+    if (batch > 0 && dim > 0 &&
+        batch > (int64_t(1) << 32) / dim / ssk::conv_segments(seqlen))
+        return fail(SS_EUNSUPPORTED, "batch * dim * segments too large");
+    return SS_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,
+                        const void *x, const float *weight, const float *bias, int silu,
+                        const float *init_state, void *out, float *final_state, void *stream) {
+    ss_status st = check_conv_dims(batch, dim, seqlen, width, io_dtype);
+    if (st != SS_OK) return st;
+    Check c;
+    if (batch > 0 && dim > 0 && seqlen > 0) { c.need(x, "x"); c.need(out, "out"); }
+    else { c.opt(x, "x"); c.opt(out, "out"); }
+    if (dim > 0) c.need(weight, "weight"); else c.opt(weight, "weight");
+    c.opt(bias, "bias");
+    c.opt(init_state, "init_state");
+    c.opt(final_state, "final_state");
+    if (c.st != SS_OK) return c.st;
+    const size_t win = size_t(batch) * size_t(dim) * size_t(width - 1) * sizeof(float);
+    if (overlaps(init_state, win, final_state, win))
+        return fail(SS_EINVAL, "final_state must not overlap init_state");
+    ssk::ConvFwdParams p{};
+    p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.width = int(width);
+    p.x = x; p.w = weight; p.bias = bias; p.silu = silu != 0; p.init = init_state;
+    p.out = out; p.final_state = final_state;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
+    return device_status(
+        ssk::launch_conv_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+        "ss_conv1d_fwd launch");
+}
+
+size_t ss_conv1d_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t width) {
+    if (check_conv_dims(batch, dim, seqlen, width, SS_F32) != SS_OK) return 0;
+    return ssk::conv_bwd_workspace_bytes(batch, dim, seqlen, int(width));
+}
+
+ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,
+                        const void *x, const float *weight, const float *bias, int silu,
+                        const float *init_state, const void *dout, void *dx, float *dweight,
+                        float *dbias, float *dinit_state, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    ss_status st = check_conv_dims(batch, dim, seqlen, width, io_dtype);
+    if (st != SS_OK) return st;
+    Check c;
+    if (batch > 0 && dim > 0 && seqlen > 0) {
+        c.need(x, "x"); c.need(dout, "dout"); c.need(dx, "dx");
+    } else {
+        c.opt(x, "x"); c.opt(dout, "dout"); c.opt(dx, "dx");
+    }
+    if (dim > 0) { c.need(weight, "weight"); c.need(dweight, "dweight"); }
+    else { c.opt(weight, "weight"); c.opt(dweight, "dweight"); }
+    c.opt(bias, "bias"); c.opt(dbias, "dbias");
+    c.opt(init_state, "init_state"); c.opt(dinit_state, "dinit_state");
+    c.pair(dbias, bias, "dbias", "bias");
+    if (c.st != SS_OK) return c.st;
+    const size_t need = ssk::conv_bwd_workspace_bytes(batch, dim, seqlen, int(width));
+    if (need > 0) {
+        if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
+        if (!aligned16(workspace)) return fail(SS_EINVAL, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(SS_EINVAL, "workspace_bytes %zu is smaller than the %zu bytes needed",
+                        workspace_bytes, need);
+    }
+    ssk::ConvBwdParams p{};
+    p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.width = int(width);
+    p.x = x; p.w = weight; p.bias = bias; p.silu = silu != 0; p.init = init_state;
+    p.dout = dout; p.dx = dx; p.dw = dweight; p.dbias = dbias; p.dinit = dinit_state;
+    p.partial = static_cast<float *>(workspace);
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
+    return device_status(
+        ssk::launch_conv_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+        "ss_conv1d_bwd launch");
+}
+
+ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dtype, float *state,
+                           const void *x, const float *weight, const float *bias, int silu,
+                           void *out, void *stream) {
+    ss_status st = check_conv_dims(batch, dim, 1, width, io_dtype);
+    if (st != SS_OK) return st;
+    if (batch * dim > (int64_t(1) << 38))
+        return fail(SS_EUNSUPPORTED, "batch * dim too large");
+    Check c;
+    if (batch > 0 && dim > 0) {
+        c.need(x, "x"); c.need(weight, "weight"); c.need(out, "out");
+        if (width > 1) c.need(state, "state"); else c.opt(state, "state");
+    } else {
+        c.opt(x, "x"); c.opt(weight, "weight"); c.opt(out, "out"); c.opt(state, "state");
+    }
+    c.opt(bias, "bias");
+    if (c.st != SS_OK) return c.st;
+    ssk::ConvUpdateParams p{};
+    p.batch = batch; p.dim = dim; p.width = int(width); p.state = state; p.x = x;
+    p.w = weight; p.bias = bias; p.silu = silu != 0; p.out = out;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
+    return device_status(
+        ssk::launch_conv_update(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+        "ss_conv1d_update launch");
+}
+
+}  // extern "C"

@@ -80,6 +80,43 @@ struct DecodeParams {
     void *out;
 };
 
+// Causal depthwise convolution over time (+ SiLU) in front of the scan.
+// x, out, dout, dx: (batch, dim, seqlen) io dtype; w, dw: (dim, width) f32;
+// bias, dbias: (dim) f32; windows (init, final, dinit, decode state):
+// (batch, dim, width - 1) f32.
+constexpr int kConvMaxWidth = 4;
+
+struct ConvParams {
+    int64_t batch, dim, seqlen;
+    int width;  // 1..kConvMaxWidth
+    const void *x;
+    const float *w, *bias;
+    int silu;
+    const float *init;  // or nullptr (zeros)
+};
+
+struct ConvFwdParams : ConvParams {
+    void *out;
+    float *final_state;  // or nullptr
+};
+
+struct ConvBwdParams : ConvParams {
+    const void *dout;
+    void *dx;
+    float *dw, *dbias, *dinit;  // dbias, dinit may be nullptr
+    float *partial;             // workspace: per-(row, segment) sums of dw and dbias
+};
+
+struct ConvUpdateParams {
+    int64_t batch, dim;
+    int width;
+    float *state;
+    const void *x;
+    const float *w, *bias;
+    int silu;
+    void *out;
+};
+
 // Records the next armed profiling event on `stream` (no-op when unarmed).
 void profile_mark(hipStream_t stream);
 
@@ -97,5 +134,13 @@ hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen);
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);
 hipError_t launch_state_update(const DecodeParams &p, bool bf16, hipStream_t stream);
+
+// Segments (one wavefront each) a row of the convolution is cut into, and
+// the workspace of its backward (f32 partial sums, 0 for empty shapes).
+int64_t conv_segments(int64_t seqlen);
+size_t conv_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int width);
+hipError_t launch_conv_fwd(const ConvFwdParams &p, bool bf16, hipStream_t stream);
+hipError_t launch_conv_bwd(const ConvBwdParams &p, bool bf16, hipStream_t stream);
+hipError_t launch_conv_update(const ConvUpdateParams &p, bool bf16, hipStream_t stream);
 
 }  // namespace ssk

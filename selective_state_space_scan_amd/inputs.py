@@ -135,3 +135,73 @@ def make(w: Workload | str) -> dict:
     a_row = (-np.exp(np.log(np.arange(1, w.dstate + 1, dtype=np.float64)))).astype(np.float32)
     out["A"] = np.ascontiguousarray(np.broadcast_to(a_row, (w.dim, w.dstate)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the causal convolution in front of the scan
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class ConvWorkload:
+    """Shape of the causal depthwise convolution (x: batch x dim x seqlen)."""
+    name: str
+    batch: int
+    dim: int
+    seqlen: int  # 1 for a decode step
+    width: int
+    io: str
+    has_bias: bool = True
+    has_init: bool = False
+    decode: bool = False
+    seed: int = SEED_BASE
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+
+CONV_WORKLOADS = {
+    w.name: w
+    for w in [
+        ConvWorkload("mamba130m_conv_f32_8x1536x2048", 8, 1536, 2048, 4, "f32",
+                     seed=SEED_BASE + 10),
+        ConvWorkload("mamba130m_conv_bf16_8x1536x2048", 8, 1536, 2048, 4, "bf16",
+                     seed=SEED_BASE + 11),
+        ConvWorkload("conv_decode_bf16_256x5120", 256, 5120, 1, 4, "bf16", decode=True,
+                     seed=SEED_BASE + 12),
+    ]
+}
+
+
+def conv_custom(batch: int, dim: int, seqlen: int, width: int = 4, io: str = "f32",
+                seed: int = 1, **flags) -> ConvWorkload:
+    name = f"conv_{io}_{batch}x{dim}x{seqlen}_k{width}_s{seed}"
+    return ConvWorkload(name, batch, dim, seqlen, width, io, seed=seed, **flags)
+
+
+def make_conv(w: ConvWorkload | str) -> dict:
+    """Draw the arrays of a convolution workload.
+
+    Draw order: x, weight, bias, init (window), dout, state (decode).
+    x, dout, init, state ~ N(0, 1); weight and bias ~ U(-1/sqrt(width),
+    1/sqrt(width)), the default initialisation of a depthwise Conv1d layer
+    (fan-in = width).  Shapes: x, dout (batch, dim, seqlen) -- (batch, dim)
+    for a decode step; weight (dim, width); bias (dim,); init and state
+    (batch, dim, width - 1) float32.  x and dout are stored in the io dtype,
+    the rest in float32.
+    """
+    if isinstance(w, str):
+        w = CONV_WORKLOADS[w]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    row_shape = (w.batch, w.dim) if w.decode else (w.batch, w.dim, w.seqlen)
+    bound = 1.0 / np.sqrt(w.width)
+    out = {"x": _store(rng.standard_normal(row_shape), w.io)}
+    out["weight"] = rng.uniform(-bound, bound, (w.dim, w.width)).astype(np.float32)
+    if w.has_bias:
+        out["bias"] = rng.uniform(-bound, bound, w.dim).astype(np.float32)
+    if w.has_init:
+        out["init"] = rng.standard_normal((w.batch, w.dim, w.width - 1)).astype(np.float32)
+    if not w.decode:
+        out["dout"] = _store(rng.standard_normal(row_shape), w.io)
+    else:
+        out["state"] = rng.standard_normal((w.batch, w.dim, w.width - 1)).astype(np.float32)
+    return out

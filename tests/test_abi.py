@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 4
+    assert lib.ss_abi_version() == 5
 
 
 def test_ckpt_size(lib):
@@ -176,3 +176,69 @@ def test_error_message_is_per_thread(lib):
     t.join()
     assert seen["msg"] == ""
     assert "u" in _msg(lib)
+
+
+# ---------------------------------------------------------------------------
+# causal convolution
+# ---------------------------------------------------------------------------
+def _cfwd(lib, batch=2, dim=8, seqlen=64, width=4, io=0, x=FAKE, w=FAKE, bias=None, init=None,
+          out=FAKE, final=None):
+    return lib.ss_conv1d_fwd(batch, dim, seqlen, width, io, x, w, bias, 1, init, out, final, None)
+
+
+def _cbwd(lib, batch=2, dim=8, seqlen=64, width=4, x=FAKE, w=FAKE, bias=None, dout=FAKE, dx=FAKE,
+          dw=FAKE, dbias=None, dinit=None, ws=FAKE, ws_bytes=1 << 20):
+    return lib.ss_conv1d_bwd(batch, dim, seqlen, width, 0, x, w, bias, 1, None, dout, dx, dw,
+                             dbias, dinit, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("arg", ["x", "w", "out"])
+def test_conv_fwd_null_required_pointer(lib, arg):
+    assert _cfwd(lib, **{arg: None}) == EINVAL and _msg(lib).startswith(
+        {"w": "weight"}.get(arg, arg))
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(width=0), EINVAL, "width"), (dict(width=5), EUNSUP, "width"),
+    (dict(seqlen=-1), EINVAL, "seqlen"), (dict(seqlen=(1 << 26) + 1), EUNSUP, "seqlen"),
+    (dict(io=2), EINVAL, "io_dtype"), (dict(x=MISALIGNED), EINVAL, "aligned"),
+])
+def test_conv_fwd_bad_arguments(lib, kw, status, word):
+    assert _cfwd(lib, **kw) == status and word in _msg(lib)
+
+
+def test_conv_fwd_windows_must_not_overlap(lib):
+    # (2 * 8 * 3) floats per window: a final window 16 bytes into the initial one overlaps it
+    assert _cfwd(lib, init=FAKE, final=FAKE + 16) == EINVAL and "overlap" in _msg(lib)
+
+
+def test_conv_empty_shapes_are_noops(lib):
+    assert _cfwd(lib, batch=0, x=None, out=None) == 0
+    assert _cbwd(lib, dim=0, x=None, w=None, dout=None, dx=None, dw=None, ws=None) == 0
+    assert lib.ss_conv1d_update(0, 8, 4, 0, None, None, None, None, 1, None, None) == 0
+
+
+def test_conv_bwd_checks(lib):
+    assert _cbwd(lib, bias=FAKE) == EINVAL and "dbias" in _msg(lib)
+    assert _cbwd(lib, dbias=FAKE) == EINVAL and "dbias" in _msg(lib)
+    assert _cbwd(lib, dw=None) == EINVAL and "dweight" in _msg(lib)
+    need = lib.ss_conv1d_bwd_workspace_size(2, 8, 64, 4)
+    assert need == 2 * 8 * 1 * 5 * 4
+    assert _cbwd(lib, ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
+    assert _cbwd(lib, ws=None) == EINVAL and "workspace" in _msg(lib)
+
+
+def test_conv_workspace_size(lib):
+    base = lib.ss_conv1d_bwd_workspace_size(2, 8, 2048, 4)
+    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 2049, 4) == 2 * base   # two segments
+    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 0, 4) == base          # one empty segment
+    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 64, 2) == base * 3 // 5
+    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 64, 5) == 0
+    assert lib.ss_conv1d_bwd_workspace_size(0, 8, 64, 4) == 0
+
+
+def test_conv_update_checks(lib):
+    st = lib.ss_conv1d_update(2, 8, 4, 0, None, FAKE, FAKE, None, 1, FAKE, None)
+    assert st == EINVAL and "state" in _msg(lib)
+    st = lib.ss_conv1d_update(2, 8, 5, 0, FAKE, FAKE, FAKE, None, 1, FAKE, None)
+    assert st == EUNSUP and "width" in _msg(lib)
