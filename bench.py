@@ -11,8 +11,9 @@ inputs already resident in HBM.  The line printed is
 with each library kernel also timed on its own (HIP events recorded between
 the kernels on the stream they run on), the dominant kernel set against the
 MI355X roofline, and the plain f64 oracle timed on a bounded sample of the
-same workload on the host cores.  The forward-only and decode workloads are
-timed as well and reported under "detail".
+same workload on the host cores.  The forward-only and decode workloads,
+and the causal convolution (width 4) that feeds the scan, are timed as well
+and reported under "detail".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -99,6 +100,20 @@ def algorithmic_bytes(kernel, batch, dim, L, esize):
     raise KeyError(kernel)
 
 
+def conv_algorithmic_bytes(kernel, batch, dim, L, width, esize):
+    """The same count for the causal convolution kernels (width-tap weights
+    and bias, and their gradients, in f32)."""
+    E = batch * dim * L
+    params = dim * (width + 1) * 4
+    if kernel == "conv_fwd":      # x in, out
+        return 2 * E * esize + params
+    if kernel == "conv_bwd":      # x, dout in, dx out
+        return 3 * E * esize + params
+    if kernel == "conv_update":   # window in and out, x in, out
+        return batch * dim * (2 * (width - 1) * 4 + 2 * esize) + params
+    raise KeyError(kernel)
+
+
 # Algorithmic floating-point operations per element (b, d, t) with d_state 16,
 # counted from the recurrence as the oracle writes it (multiply, add = 1,
 # fused multiply-add = 2, exp / log / reciprocal = 1): per state 5 for the
@@ -144,6 +159,82 @@ def measured_traffic(kernel, workload):
         return None
 
 
+def timed_calls(hip, lib, calls, marks, iters):
+    """Mean duration of each kernel of a library call: the calls rotate over
+    their input sets; `marks` profiling events are recorded per call (one at
+    the start and one after each kernel)."""
+    import numpy as np
+    import torch
+    for c in calls:
+        c()
+    tm = KernelTimer(hip, lib, marks * iters)
+    torch.cuda.synchronize()
+    tm.arm()
+    for i in range(iters):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    tm.disarm()
+    out = [float(np.mean([tm.ms(marks * i + a, marks * i + a + 1) for i in range(iters)]))
+           for a in range(marks - 1)]
+    tm.close()
+    return out
+
+
+def conv_detail(hip, lib, to_dev, dev):
+    """The causal convolution (width 4) in front of the scan: forward and
+    backward at the Mamba-130m layer shape in bf16 and f32, and the decode
+    step at 256 x 5120."""
+    import torch
+
+    from selective_state_space_scan_amd import binding
+    from selective_state_space_scan_amd import inputs as ssin
+    detail = {}
+    for cname, reps in (("mamba130m_conv_bf16_8x1536x2048", 4),
+                        ("mamba130m_conv_f32_8x1536x2048", 2)):
+        wc = ssin.CONV_WORKLOADS[cname]
+        ac = ssin.make_conv(wc)
+        es = 2 if wc.io == "bf16" else 4
+        csets = [{k: to_dev(v) for k, v in ac.items()} for _ in range(reps)]
+        couts = [torch.empty_like(c["x"]) for c in csets]
+        fwd_calls = [lambda c=c, o=o: binding.ss_conv1d_fwd(c["x"], c["weight"], c["bias"],
+                                                            True, out=o)
+                     for c, o in zip(csets, couts)]
+        bwd_calls = [lambda c=c: binding.ss_conv1d_bwd(c["x"], c["weight"], c["bias"], True,
+                                                       None, c["dout"])
+                     for c in csets]
+        (fms,) = timed_calls(hip, lib, fwd_calls, 2, 20)
+        (bms,) = timed_calls(hip, lib, bwd_calls, 2, 20)
+        Ec = wc.elements
+        fb = conv_algorithmic_bytes("conv_fwd", wc.batch, wc.dim, wc.seqlen, wc.width, es)
+        bb = conv_algorithmic_bytes("conv_bwd", wc.batch, wc.dim, wc.seqlen, wc.width, es)
+        detail[cname] = {
+            "fwd_kernel_ms": round(fms, 5), "fwd_algorithmic_bytes": fb,
+            "fwd_algorithmic_GBps": round(fb / (fms * 1e-3) / 1e9, 1),
+            "fwd_hbm_frac_of_peak": round(fb / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_kernel_ms": round(bms, 5), "bwd_algorithmic_bytes": bb,
+            "bwd_algorithmic_GBps": round(bb / (bms * 1e-3) / 1e9, 1),
+            "bwd_hbm_frac_of_peak": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "fwd_elements_per_s": Ec / (fms * 1e-3),
+            "input_sets_rotated": reps}
+        del csets, couts
+    wcd = ssin.CONV_WORKLOADS["conv_decode_bf16_256x5120"]
+    acd = ssin.make_conv(wcd)
+    dsets = [{k: to_dev(v) for k, v in acd.items()} for _ in range(4)]
+    douts = [torch.empty_like(c["x"]) for c in dsets]
+    dec_calls = [lambda c=c, o=o: binding.ss_conv1d_update(c["state"], c["x"], c["weight"],
+                                                           c["bias"], True, out=o)
+                 for c, o in zip(dsets, douts)]
+    (ums,) = timed_calls(hip, lib, dec_calls, 2, 40)
+    ub = conv_algorithmic_bytes("conv_update", wcd.batch, wcd.dim, 1, wcd.width, 2)
+    detail["conv_decode_bf16_256x5120"] = {
+        "kernel_ms": round(ums, 5), "rows_per_s": wcd.batch * wcd.dim / (ums * 1e-3),
+        "algorithmic_GBps": round(ub / (ums * 1e-3) / 1e9, 1),
+        "hbm_frac_of_peak": round(ub / (ums * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "input_sets_rotated": 4}
+    del dsets, douts
+    return detail
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +242,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--conv-only", action="store_true",
+                    help="time only the causal convolution kernels (prints their detail)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the selective scan's "
@@ -172,6 +265,10 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
+
+    if args.conv_only:
+        print(json.dumps({"detail": conv_detail(hip, lib, to_dev, dev)}), flush=True)
+        return
 
     # ---------------- the step: fwd + bwd at 8 x 1536 x 2048, f32 ----------------
     w = ssin.WORKLOADS["mamba130m_bwd_f32_8x1536x2048"]
@@ -370,6 +467,8 @@ def main():
             "hbm_frac_of_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "input_sets_rotated": reps}
         del sets, outs
+
+        detail.update(conv_detail(hip, lib, to_dev, dev))
         result["detail"] = detail
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------

@@ -191,22 +191,17 @@ ss_status ss_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t widt
                         const void *x, const float *weight, const float *bias, int silu,
                         const float *init_state, void *out, float *final_state, void *stream);
 
-/* Bytes of device workspace ss_conv1d_bwd needs (0 for empty shapes). */
-size_t ss_conv1d_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t width);
-
 /*
  * Backward of sum(dout * out) with respect to x (dx, required), weight
  * (dweight, required; summed over batch and time), bias (dbias, given
  * exactly when bias is) and the initial window (dinit_state, optional; may
- * be given without init_state: the gradient at a zero window).  workspace:
- * ss_conv1d_bwd_workspace_size() bytes of caller-owned device memory,
- * 16-byte aligned, not read before written.
+ * be given without init_state: the gradient at a zero window).  Needs no
+ * workspace: the sums over batch and time stay on chip.
  */
 ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,
                         const void *x, const float *weight, const float *bias, int silu,
                         const float *init_state, const void *dout, void *dx, float *dweight,
-                        float *dbias, float *dinit_state, void *workspace,
-                        size_t workspace_bytes, void *stream);
+                        float *dbias, float *dinit_state, void *stream);
 
 /*
  * Decode step: out = act(bias + sum_k weight[d,k] * window_k) with window =

@@ -69,11 +69,8 @@ def load() -> ctypes.CDLL:
                                             + [vp] * 2)
             lib.ss_conv1d_fwd.restype = c_int
             lib.ss_conv1d_fwd.argtypes = [i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 4
-            lib.ss_conv1d_bwd_workspace_size.restype = sz
-            lib.ss_conv1d_bwd_workspace_size.argtypes = [i64] * 4
             lib.ss_conv1d_bwd.restype = c_int
-            lib.ss_conv1d_bwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 7
-                                          + [sz, vp])
+            lib.ss_conv1d_bwd.argtypes = [i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 7
             lib.ss_conv1d_update.restype = c_int
             lib.ss_conv1d_update.argtypes = [i64] * 3 + [c_int] + [vp] * 4 + [c_int] + [vp] * 2
             _lib = lib
@@ -246,12 +243,8 @@ def ss_conv1d_fwd(x, weight, bias=None, silu=True, init_state=None, out=None,
     return (out, final_state) if (return_final_state or final_state is not None) else out
 
 
-def ss_conv1d_bwd_workspace_size(batch, dim, seqlen, width) -> int:
-    return int(load().ss_conv1d_bwd_workspace_size(batch, dim, seqlen, width))
-
-
 def ss_conv1d_bwd(x, weight, bias=None, silu=True, init_state=None, dout=None,
-                  want_dinit_state=False, workspace=None):
+                  want_dinit_state=False):
     """Backward of ``sum(dout * ss_conv1d_fwd(...))``.
 
     Returns a dict with dx, dweight, and dbias when bias is given, dinit_state
@@ -269,14 +262,10 @@ def ss_conv1d_bwd(x, weight, bias=None, silu=True, init_state=None, dout=None,
         g["dbias"] = torch.empty(dim, dtype=torch.float32, device=dev)
     if want_dinit_state or init_state is not None:
         g["dinit_state"] = torch.empty(batch, dim, width - 1, dtype=torch.float32, device=dev)
-    need = ss_conv1d_bwd_workspace_size(batch, dim, seqlen, width)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(lib.ss_conv1d_bwd(batch, dim, seqlen, width, io, _ptr(x), _f32(weight, "weight"),
                              _f32(bias, "bias"), int(bool(silu)), _f32(init_state, "init_state"),
                              _ptr(dout), _ptr(g["dx"]), _ptr(g["dweight"]), _ptr(g.get("dbias")),
-                             _ptr(g.get("dinit_state")), _ptr(workspace), workspace.numel(),
-                             _stream()))
+                             _ptr(g.get("dinit_state")), _stream()))
     return g
 
 

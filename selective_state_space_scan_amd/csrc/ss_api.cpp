@@ -325,16 +325,10 @@ ss_status ss_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t widt
         "ss_conv1d_fwd launch");
 }
 
-size_t ss_conv1d_bwd_workspace_size(int64_t batch, int64_t dim, int64_t seqlen, int64_t width) {
-    if (check_conv_dims(batch, dim, seqlen, width, SS_F32) != SS_OK) return 0;
-    return ssk::conv_bwd_workspace_bytes(batch, dim, seqlen, int(width));
-}
-
 ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,
                         const void *x, const float *weight, const float *bias, int silu,
                         const float *init_state, const void *dout, void *dx, float *dweight,
-                        float *dbias, float *dinit_state, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        float *dbias, float *dinit_state, void *stream) {
     ss_status st = check_conv_dims(batch, dim, seqlen, width, io_dtype);
     if (st != SS_OK) return st;
     Check c;
@@ -349,19 +343,10 @@ ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t widt
     c.opt(init_state, "init_state"); c.opt(dinit_state, "dinit_state");
     c.pair(dbias, bias, "dbias", "bias");
     if (c.st != SS_OK) return c.st;
-    const size_t need = ssk::conv_bwd_workspace_bytes(batch, dim, seqlen, int(width));
-    if (need > 0) {
-        if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
-        if (!aligned16(workspace)) return fail(SS_EINVAL, "workspace must be 16-byte aligned");
-        if (workspace_bytes < need)
-            return fail(SS_EINVAL, "workspace_bytes %zu is smaller than the %zu bytes needed",
-                        workspace_bytes, need);
-    }
     ssk::ConvBwdParams p{};
     p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.width = int(width);
     p.x = x; p.w = weight; p.bias = bias; p.silu = silu != 0; p.init = init_state;
     p.dout = dout; p.dx = dx; p.dw = dweight; p.dbias = dbias; p.dinit = dinit_state;
-    p.partial = static_cast<float *>(workspace);
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(
         ssk::launch_conv_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),

@@ -21,8 +21,8 @@
 // of V take a per-element path that reads each window from memory.
 //
 // The HBM traffic is the algorithmic one: the forward reads x and writes
-// out once; the backward reads x and dout and writes dx once (the weight
-// gradients go through a small per-segment partial buffer).
+// out once; the backward reads x and dout and writes dx once, and sums the
+// weight and bias gradients on chip (one workgroup per channel).
 #include <type_traits>
 
 #include "ss_kernels.h"
@@ -130,19 +130,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <int K>
-__device__ __forceinline__ void write_partials(const ConvBwdParams &p, int64_t wave_idx,
-                                               const float (&acc_w)[K], float acc_b, int lane) {
-    float s[K + 1];
-#pragma unroll
-    for (int k = 0; k < K; k++) s[k] = wave_sum(acc_w[k]);
-    s[K] = wave_sum(acc_b);
-    if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k <= K; k++) p.partial[wave_idx * (K + 1) + k] = s[k];
-    }
-}
-
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
@@ -233,47 +220,48 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_fwd_elem(ConvFwdParams p
 // ---------------------------------------------------------------------------
 // backward: g_t = dout_t act'(pre_t);  dx_s = sum_k w[k] g_{s+H-k};
 // dw[k] = sum g_t x_{t-H+k};  dbias = sum g_t;  dinit_j = sum_{k<=j} w[k] g_{j-k}
+//
+// One workgroup per channel d.  Its wavefronts take the (batch, segment)
+// items of the channel in turn (wavefront v: items v, v + W, ...), keep the
+// dw / dbias sums in registers across items, and the workgroup adds the
+// per-wavefront sums in ascending order at the end: no partial buffer and
+// no second kernel.  The order depends on the shape only.
 // ---------------------------------------------------------------------------
+constexpr int kBwdWaves = 2;  // wavefronts per workgroup (one channel)
+
+// One (row, segment) item on the vector path: writes dx (and dinit for the
+// first segment) and adds the item's dw / dbias sums to acc_w / acc_b.
 template <typename T, int K, bool SILU>
-__global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_vec(ConvBwdParams p, int64_t nseg) {
+__device__ __forceinline__ void bwd_vec_item(const ConvBwdParams &p, const float (&w)[K], float b,
+                                             int64_t r, int64_t seg, int lane, float (&acc_w)[K],
+                                             float &acc_b) {
     constexpr int V = VecOf<T>::n, H = K - 1, J = kConvSeg / (64 * V);
     constexpr int HS = H > 0 ? H : 1;
     constexpr int W0 = ((V - HS) * int(sizeof(T))) / 4;
-    const int lane = threadIdx.x & 63;
-    const ConvWave cw = conv_wave(p, nseg);
-    if (!cw.live) return;
     const int64_t L = p.seqlen;
-    const T *xr = static_cast<const T *>(p.x) + cw.r * L;
-    const T *gr = static_cast<const T *>(p.dout) + cw.r * L;
-    T *dxr = static_cast<T *>(p.dx) + cw.r * L;
+    const int64_t t0 = seg * kConvSeg;
+    const T *xr = static_cast<const T *>(p.x) + r * L;
+    const T *gr = static_cast<const T *>(p.dout) + r * L;
+    T *dxr = static_cast<T *>(p.dx) + r * L;
 
-    float acc_w[K], acc_b = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; k++) acc_w[k] = 0.0f;
-
-    if (cw.t0 < L) {
-        float w[K];
-#pragma unroll
-        for (int k = 0; k < K; k++) w[k] = p.w[cw.d * K + k];
-        const float b = p.bias ? p.bias[cw.d] : 0.0f;
-
+    if (t0 < L) {
         u32x4 v[J], go[J];
 #pragma unroll
         for (int j = 0; j < J; j++) {
-            const int64_t t = cw.t0 + int64_t(j * 64 + lane) * V;
+            const int64_t t = t0 + int64_t(j * 64 + lane) * V;
             const uint32_t off = uint32_t((t < L ? t : L - V) * int64_t(sizeof(T)));
             v[j] = ld_global16(at_bytes(xr, off));
             go[j] = ld_global16(at_bytes(gr, off));
         }
         float carry[HS];
 #pragma unroll
-        for (int m = 0; m < H; m++) carry[m] = x_at<T, H>(p, xr, cw.r, cw.t0 - H + m);
+        for (int m = 0; m < H; m++) carry[m] = x_at<T, H>(p, xr, r, t0 - H + m);
 
         // gradients at the pre-activation, zero past the row end
         float g[J][V];
 #pragma unroll
         for (int j = 0; j < J; j++) {
-            const int64_t t = cw.t0 + int64_t(j * 64 + lane) * V;
+            const int64_t t = t0 + int64_t(j * 64 + lane) * V;
             u32x4 rv = v[j];
 #pragma unroll
             for (int q = W0; q < 4; q++) rv[q] = wave_ror1(v[j][q]);
@@ -306,7 +294,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_vec(ConvBwdParams p,
         float gnext[HS];
 #pragma unroll
         for (int m = 0; m < H; m++) {
-            const int64_t tt = cw.t0 + kConvSeg + m;
+            const int64_t tt = t0 + kConvSeg + m;
             float gg = 0.0f;
             if (tt < L) {
                 float pre = b;
@@ -327,7 +315,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_vec(ConvBwdParams p,
 
 #pragma unroll
         for (int j = 0; j < J; j++) {
-            const int64_t t = cw.t0 + int64_t(j * 64 + lane) * V;
+            const int64_t t = t0 + int64_t(j * 64 + lane) * V;
             float nxt[HS];
 #pragma unroll
             for (int m = 0; m < H; m++)
@@ -346,19 +334,18 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_vec(ConvBwdParams p,
             if (t < L) st_global16(at_bytes(dxr, uint32_t(t * int64_t(sizeof(T)))), vpack<T, V>(o));
         }
 
-        if (p.dinit && cw.seg == 0 && lane == 0) {
+        if (p.dinit && seg == 0 && lane == 0) {
 #pragma unroll
             for (int jj = 0; jj < H; jj++) {
                 float acc = 0.0f;
 #pragma unroll
                 for (int k = jj; k >= 0; k--) acc = fmaf(w[k], g[0][jj - k], acc);
-                p.dinit[cw.r * H + jj] = acc;
+                p.dinit[r * H + jj] = acc;
             }
         }
     } else if (p.dinit && H > 0 && lane < H) {
-        p.dinit[cw.r * H + lane] = 0.0f;  // empty rows: no gradient reaches the window
+        p.dinit[r * H + lane] = 0.0f;  // empty rows: no gradient reaches the window
     }
-    write_partials<K>(p, cw.r * nseg + cw.seg, acc_w, acc_b, lane);
 }
 
 template <typename T, int K, bool SILU>
@@ -373,65 +360,79 @@ __device__ __forceinline__ float g_at(const ConvBwdParams &p, const T *xr, const
 }
 
 template <typename T, int K, bool SILU>
-__global__ __launch_bounds__(64 * kConvWaves) void conv_bwd_elem(ConvBwdParams p, int64_t nseg) {
+__device__ __forceinline__ void bwd_elem_item(const ConvBwdParams &p, const float (&w)[K], float b,
+                                              int64_t r, int64_t seg, int lane,
+                                              float (&acc_w)[K], float &acc_b) {
     constexpr int H = K - 1;
-    const int lane = threadIdx.x & 63;
-    const ConvWave cw = conv_wave(p, nseg);
-    if (!cw.live) return;
     const int64_t L = p.seqlen;
-    const T *xr = static_cast<const T *>(p.x) + cw.r * L;
-    const T *gr = static_cast<const T *>(p.dout) + cw.r * L;
-    T *dxr = static_cast<T *>(p.dx) + cw.r * L;
-    float w[K], acc_w[K], acc_b = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; k++) {
-        w[k] = p.w[cw.d * K + k];
-        acc_w[k] = 0.0f;
-    }
-    const float b = p.bias ? p.bias[cw.d] : 0.0f;
+    const int64_t t0 = seg * kConvSeg;
+    const T *xr = static_cast<const T *>(p.x) + r * L;
+    const T *gr = static_cast<const T *>(p.dout) + r * L;
+    T *dxr = static_cast<T *>(p.dx) + r * L;
     for (int j = 0; j < kConvSeg / 64; j++) {
-        const int64_t t = cw.t0 + j * 64 + lane;
-        if (cw.t0 + j * 64 >= L) break;
+        const int64_t t = t0 + j * 64 + lane;
+        if (t0 + j * 64 >= L) break;
         if (t < L) {
-            const float gt = g_at<T, K, SILU>(p, xr, gr, w, b, cw.r, t);
+            const float gt = g_at<T, K, SILU>(p, xr, gr, w, b, r, t);
             acc_b += gt;
 #pragma unroll
             for (int k = 0; k < K; k++)
-                acc_w[k] = fmaf(gt, x_at<T, H>(p, xr, cw.r, t - H + k), acc_w[k]);
+                acc_w[k] = fmaf(gt, x_at<T, H>(p, xr, r, t - H + k), acc_w[k]);
             float acc = 0.0f;
 #pragma unroll
             for (int k = K - 1; k >= 0; k--)
-                acc = fmaf(w[k], k == H ? gt : g_at<T, K, SILU>(p, xr, gr, w, b, cw.r, t + H - k),
+                acc = fmaf(w[k], k == H ? gt : g_at<T, K, SILU>(p, xr, gr, w, b, r, t + H - k),
                            acc);
             st_global(dxr + t, from_f32<T>(acc));
         }
     }
-    if (p.dinit && cw.seg == 0 && H > 0 && lane < H) {
+    if (p.dinit && seg == 0 && H > 0 && lane < H) {
         float acc = 0.0f;
 #pragma unroll
         for (int k = K - 1; k >= 0; k--)
-            if (k <= lane) acc = fmaf(w[k], g_at<T, K, SILU>(p, xr, gr, w, b, cw.r, lane - k), acc);
-        p.dinit[cw.r * H + lane] = acc;
+            if (k <= lane) acc = fmaf(w[k], g_at<T, K, SILU>(p, xr, gr, w, b, r, lane - k), acc);
+        p.dinit[r * H + lane] = acc;
     }
-    write_partials<K>(p, cw.r * nseg + cw.seg, acc_w, acc_b, lane);
 }
 
-// dw[d,k] and dbias[d]: sums of the per-(row, segment) partials over batch
-// (outer, ascending) and segments (inner, ascending).
-template <int K>
-__global__ __launch_bounds__(256) void conv_fold(ConvBwdParams p, int64_t nseg) {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= p.dim * (K + 1)) return;
-    const int64_t d = i / (K + 1);
-    const int k = int(i - d * (K + 1));
-    if (k == K && !p.dbias) return;
-    float s = 0.0f;
-    for (int64_t bb = 0; bb < p.batch; bb++) {
-        const float *src = p.partial + ((bb * p.dim + d) * nseg) * (K + 1) + k;
-        for (int64_t sg = 0; sg < nseg; sg++) s += src[sg * (K + 1)];
+// The backward kernel: workgroup = channel d, see above.
+template <typename T, int K, bool SILU, bool VEC>
+__global__ __launch_bounds__(64 * kBwdWaves) void conv_bwd_kernel(ConvBwdParams p, int64_t nseg) {
+    __shared__ float red[kBwdWaves][K + 1];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t d = blockIdx.x;
+    float w[K], acc_w[K], acc_b = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        w[k] = p.w[d * K + k];
+        acc_w[k] = 0.0f;
     }
-    if (k < K) p.dw[d * K + k] = s;
-    else p.dbias[d] = s;
+    const float b = p.bias ? p.bias[d] : 0.0f;
+    const int64_t items = p.batch * nseg;
+    for (int64_t it = wv; it < items; it += kBwdWaves) {
+        const int64_t bb = it / nseg, seg = it - bb * nseg;
+        if constexpr (VEC)
+            bwd_vec_item<T, K, SILU>(p, w, b, bb * p.dim + d, seg, lane, acc_w, acc_b);
+        else
+            bwd_elem_item<T, K, SILU>(p, w, b, bb * p.dim + d, seg, lane, acc_w, acc_b);
+    }
+    float sum[K + 1];
+#pragma unroll
+    for (int k = 0; k < K; k++) sum[k] = wave_sum(acc_w[k]);
+    sum[K] = wave_sum(acc_b);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k <= K; k++) red[wv][k] = sum[k];
+    }
+    __syncthreads();
+    if (threadIdx.x <= K) {
+        const int k = threadIdx.x;
+        float t = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kBwdWaves; v++) t += red[v][k];
+        if (k < K) p.dw[d * K + k] = t;
+        else if (p.dbias) p.dbias[d] = t;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -495,18 +496,19 @@ hipError_t conv_fwd_typed(const ConvFwdParams &p, hipStream_t stream) {
 template <typename T>
 hipError_t conv_bwd_typed(const ConvBwdParams &p, hipStream_t stream) {
     const int64_t nseg = conv_segments(p.seqlen);
-    const dim3 grid = wave_grid(p.batch * p.dim * nseg), block(64 * kConvWaves);
+    const dim3 grid(static_cast<unsigned>(p.dim)), block(64 * kBwdWaves);
     const bool vec = p.seqlen % VecOf<T>::n == 0;
     return by_width(p, [&](auto kc) {
         constexpr int K = decltype(kc)::value;
         if (vec && p.silu)
-            hipLaunchKernelGGL((conv_bwd_vec<T, K, true>), grid, block, 0, stream, p, nseg);
+            hipLaunchKernelGGL((conv_bwd_kernel<T, K, true, true>), grid, block, 0, stream, p, nseg);
         else if (vec)
-            hipLaunchKernelGGL((conv_bwd_vec<T, K, false>), grid, block, 0, stream, p, nseg);
+            hipLaunchKernelGGL((conv_bwd_kernel<T, K, false, true>), grid, block, 0, stream, p, nseg);
         else if (p.silu)
-            hipLaunchKernelGGL((conv_bwd_elem<T, K, true>), grid, block, 0, stream, p, nseg);
+            hipLaunchKernelGGL((conv_bwd_kernel<T, K, true, false>), grid, block, 0, stream, p, nseg);
         else
-            hipLaunchKernelGGL((conv_bwd_elem<T, K, false>), grid, block, 0, stream, p, nseg);
+            hipLaunchKernelGGL((conv_bwd_kernel<T, K, false, false>), grid, block, 0, stream, p,
+                               nseg);
     });
 }
 
@@ -528,12 +530,6 @@ int64_t conv_segments(int64_t seqlen) {
     return seqlen <= 0 ? 1 : (seqlen + kConvSeg - 1) / kConvSeg;
 }
 
-size_t conv_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int width) {
-    if (batch <= 0 || dim <= 0) return 0;
-    return size_t(batch) * size_t(dim) * size_t(conv_segments(seqlen)) * size_t(width + 1) *
-           sizeof(float);
-}
-
 hipError_t launch_conv_fwd(const ConvFwdParams &p, bool bf16, hipStream_t stream) {
     if (p.batch * p.dim == 0) return hipSuccess;
     hipError_t e = bf16 ? conv_fwd_typed<bf16_t>(p, stream) : conv_fwd_typed<float>(p, stream);
@@ -543,19 +539,7 @@ hipError_t launch_conv_fwd(const ConvFwdParams &p, bool bf16, hipStream_t stream
 
 hipError_t launch_conv_bwd(const ConvBwdParams &p, bool bf16, hipStream_t stream) {
     if (p.dim == 0) return hipSuccess;
-    const int64_t nseg = conv_segments(p.seqlen);
-    if (p.batch > 0) {
-        hipError_t e = bf16 ? conv_bwd_typed<bf16_t>(p, stream) : conv_bwd_typed<float>(p, stream);
-        profile_mark(stream);
-        if (e != hipSuccess) return e;
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const dim3 grid(static_cast<unsigned>((p.dim * (p.width + 1) + 255) / 256)), block(256);
-    hipError_t e = by_width(p, [&](auto kc) {
-        constexpr int K = decltype(kc)::value;
-        hipLaunchKernelGGL((conv_fold<K>), grid, block, 0, stream, p, nseg);
-    });
+    hipError_t e = bf16 ? conv_bwd_typed<bf16_t>(p, stream) : conv_bwd_typed<float>(p, stream);
     profile_mark(stream);
     return e != hipSuccess ? e : hipGetLastError();
 }

@@ -104,7 +104,6 @@ struct ConvBwdParams : ConvParams {
     const void *dout;
     void *dx;
     float *dw, *dbias, *dinit;  // dbias, dinit may be nullptr
-    float *partial;             // workspace: per-(row, segment) sums of dw and dbias
 };
 
 struct ConvUpdateParams {
@@ -135,10 +134,8 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen);
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);
 hipError_t launch_state_update(const DecodeParams &p, bool bf16, hipStream_t stream);
 
-// Segments (one wavefront each) a row of the convolution is cut into, and
-// the workspace of its backward (f32 partial sums, 0 for empty shapes).
+// Segments (one wavefront each) a row of the convolution is cut into.
 int64_t conv_segments(int64_t seqlen);
-size_t conv_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int width);
 hipError_t launch_conv_fwd(const ConvFwdParams &p, bool bf16, hipStream_t stream);
 hipError_t launch_conv_bwd(const ConvBwdParams &p, bool bf16, hipStream_t stream);
 hipError_t launch_conv_update(const ConvUpdateParams &p, bool bf16, hipStream_t stream);

@@ -187,9 +187,9 @@ def _cfwd(lib, batch=2, dim=8, seqlen=64, width=4, io=0, x=FAKE, w=FAKE, bias=No
 
 
 def _cbwd(lib, batch=2, dim=8, seqlen=64, width=4, x=FAKE, w=FAKE, bias=None, dout=FAKE, dx=FAKE,
-          dw=FAKE, dbias=None, dinit=None, ws=FAKE, ws_bytes=1 << 20):
+          dw=FAKE, dbias=None, dinit=None):
     return lib.ss_conv1d_bwd(batch, dim, seqlen, width, 0, x, w, bias, 1, None, dout, dx, dw,
-                             dbias, dinit, ws, ws_bytes, None)
+                             dbias, dinit, None)
 
 
 @pytest.mark.parametrize("arg", ["x", "w", "out"])
@@ -214,7 +214,7 @@ def test_conv_fwd_windows_must_not_overlap(lib):
 
 def test_conv_empty_shapes_are_noops(lib):
     assert _cfwd(lib, batch=0, x=None, out=None) == 0
-    assert _cbwd(lib, dim=0, x=None, w=None, dout=None, dx=None, dw=None, ws=None) == 0
+    assert _cbwd(lib, dim=0, x=None, w=None, dout=None, dx=None, dw=None) == 0
     assert lib.ss_conv1d_update(0, 8, 4, 0, None, None, None, None, 1, None, None) == 0
 
 
@@ -222,19 +222,8 @@ def test_conv_bwd_checks(lib):
     assert _cbwd(lib, bias=FAKE) == EINVAL and "dbias" in _msg(lib)
     assert _cbwd(lib, dbias=FAKE) == EINVAL and "dbias" in _msg(lib)
     assert _cbwd(lib, dw=None) == EINVAL and "dweight" in _msg(lib)
-    need = lib.ss_conv1d_bwd_workspace_size(2, 8, 64, 4)
-    assert need == 2 * 8 * 1 * 5 * 4
-    assert _cbwd(lib, ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
-    assert _cbwd(lib, ws=None) == EINVAL and "workspace" in _msg(lib)
-
-
-def test_conv_workspace_size(lib):
-    base = lib.ss_conv1d_bwd_workspace_size(2, 8, 2048, 4)
-    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 2049, 4) == 2 * base   # two segments
-    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 0, 4) == base          # one empty segment
-    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 64, 2) == base * 3 // 5
-    assert lib.ss_conv1d_bwd_workspace_size(2, 8, 64, 5) == 0
-    assert lib.ss_conv1d_bwd_workspace_size(0, 8, 64, 4) == 0
+    assert _cbwd(lib, dout=None) == EINVAL and "dout" in _msg(lib)
+    assert _cbwd(lib, width=5) == EUNSUP and "width" in _msg(lib)
 
 
 def test_conv_update_checks(lib):
