@@ -180,6 +180,39 @@ def timed_calls(hip, lib, calls, marks, iters):
     return out
 
 
+def wide_state_detail(hip, lib, to_dev, dev):
+    """The fwd + bwd step at the Mamba-130m layer shape with d_state 64 (four
+    16-state slices plus the combine kernels), f32 io."""
+    import torch
+
+    from selective_state_space_scan_amd import binding
+    from selective_state_space_scan_amd import inputs as ssin
+    w = ssin.custom("bwd", 8, 1536, 64, 2048, "f32", seed=ssin.SEED_BASE + 20)
+    d = {k: to_dev(v) for k, v in ssin.make(w).items()}
+    y = torch.empty_like(d["u"])
+    ck = binding.ss_ckpt_empty(d["u"], dstate=64)
+    fws = torch.empty(binding.ss_fwd_workspace_size(w.batch, w.dim, 64, w.seqlen),
+                      dtype=torch.uint8, device=dev)
+    bws = torch.empty(binding.ss_bwd_workspace_size(w.batch, w.dim, 64, w.seqlen, 0),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                       d["delta_bias"], True, out=y, ckpt=ck, workspace=fws)
+        binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                       d["delta_bias"], True, d["dout"], workspace=bws, ckpt=ck)
+    # per step: fwd [start, slices, combine]; bwd [start, reverse slices, combine, fold]
+    parts = timed_calls(hip, lib, [step], 7, 5)
+    names = ["fwd_slices_ms", "fwd_combine_ms", None, "bwd_reverse_slices_ms",
+             "bwd_combine_ms", "bwd_fold_ms"]
+    out = {n: round(v, 5) for n, v in zip(names, parts) if n}
+    tot = sum(v for n, v in zip(names, parts) if n)
+    out["step_kernels_ms"] = round(tot, 5)
+    out["elements_per_s"] = w.elements / (tot * 1e-3)
+    del d, y, ck, fws, bws
+    return {"mamba130m_step_f32_8x1536x2048_dstate64": out}
+
+
 def conv_detail(hip, lib, to_dev, dev):
     """The causal convolution (width 4) in front of the scan: forward and
     backward at the Mamba-130m layer shape in bf16 and f32, and the decode
@@ -468,6 +501,7 @@ def main():
             "input_sets_rotated": reps}
         del sets, outs
 
+        detail.update(wide_state_detail(hip, lib, to_dev, dev))
         detail.update(conv_detail(hip, lib, to_dev, dev))
         result["detail"] = detail
 

@@ -60,14 +60,14 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 5
+#define SS_ABI_VERSION 6
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
 typedef enum {
     SS_OK = 0,
     SS_EINVAL = 1,       /* bad argument: null/misaligned pointer, bad size, bad combination */
-    SS_EUNSUPPORTED = 2, /* valid request this build does not implement (e.g. dstate > 16) */
+    SS_EUNSUPPORTED = 2, /* valid request this build does not implement (e.g. dstate > 256) */
     SS_EDEVICE = 3       /* a HIP call or kernel launch failed */
 } ss_status;
 
@@ -79,22 +79,33 @@ const char *ss_last_error(void);
 
 /*
  * Bytes of what ss_fwd can save for ss_bwd (its "ckpt" buffer), all f32:
- * the state entering every 16-step block, (batch, dim, ceil(seqlen / 16),
- * 16) -- 16 entries for any dstate, the unused ones zero -- then at the
- * next 256-byte boundary the pre-gate output
- * sum_n C h + D u, (batch, dim, seqlen), which is written when z is given.
- * 0 for empty or unsupported shapes.
+ * the state entering every 16-step block, per slice of 16 states,
+ * (ceil(dstate / 16), batch, dim, ceil(seqlen / 16), 16) -- 16 entries per
+ * slice, the unused ones zero.  With dstate <= 16 it is followed, at the
+ * next 256-byte boundary, by the pre-gate output sum_n C h + D u, (batch,
+ * dim, seqlen), which is written when z is given.  0 for empty or
+ * unsupported shapes.
  */
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
+
+/* Bytes of device workspace ss_fwd needs: 0 for dstate <= 16; above, the
+ * f32 per-slice partial sums over states, ceil(dstate / 16) * batch * dim *
+ * seqlen floats. */
+size_t ss_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 
 /*
  * Forward scan.  Writes out (batch, dim, seqlen) and, when last_state is
  * non-NULL, the final state h_{seqlen-1} (h0 when seqlen == 0).  When ckpt
  * is non-NULL (ss_ckpt_size() bytes, 16-byte aligned) it also saves the
- * block states and the pre-gate output, which a later ss_bwd with the same
- * inputs takes instead of recomputing them (the usual save-for-backward of
- * a training step).
- *   dstate            1..16 (SS_EUNSUPPORTED above 16).
+ * block states (and, for dstate <= 16, the pre-gate output), which a later
+ * ss_bwd with the same inputs takes instead of recomputing them (the usual
+ * save-for-backward of a training step).
+ *   dstate            1..256 (SS_EUNSUPPORTED above; the mamba-rs README,
+ *                     "Features", sizes state dimensions up to 256).  Above
+ *                     16 the scan runs one pass per 16-state slice and adds
+ *                     the slices' sums in ascending order.
+ *   workspace         ss_fwd_workspace_size() bytes of caller-owned device
+ *                     memory, 16-byte aligned (NULL when that is 0).
  *   io_dtype          SS_F32 or SS_BF16: dtype of u, delta, B, C, z, out.
  *   D, z, delta_bias, h0, last_state may be NULL.
  *   batch, dim, seqlen >= 0; a zero size enqueues nothing but the
@@ -106,7 +117,7 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                  const void *u, const void *delta, const float *A, const void *B,
                  const void *C, const float *D, const void *z, const float *delta_bias,
                  int delta_softplus, const float *h0, void *out, float *last_state,
-                 float *ckpt, void *stream);
+                 float *ckpt, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace ss_bwd needs for this shape (0 for empty shapes). */
 size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
@@ -146,7 +157,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
  * z (batch, dim) and B, C (batch, dstate), and writes out (batch, dim).
  * Each (b, d) row is computed by its own lanes in one fixed order, so a row
  * gives the same bits whether it is stepped alone or inside any batch.
- *   dstate 1..16; D, z, delta_bias may be NULL.
+ *   dstate 1..256; D, z, delta_bias may be NULL.
  */
 ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
                           float *state, const void *u, const void *delta, const float *A,

@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 5
+ABI_VERSION = 6
 _lock = threading.Lock()
 _lib = None
 
@@ -56,7 +56,10 @@ def load() -> ctypes.CDLL:
             lib.ss_last_error.restype = ctypes.c_char_p
             lib.ss_last_error.argtypes = []
             lib.ss_fwd.restype = c_int
-            lib.ss_fwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 5)
+            lib.ss_fwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 5
+                                   + [sz, vp])
+            lib.ss_fwd_workspace_size.restype = sz
+            lib.ss_fwd_workspace_size.argtypes = [i64] * 4
             lib.ss_ckpt_size.restype = sz
             lib.ss_ckpt_size.argtypes = [i64] * 4
             lib.ss_bwd_workspace_size.restype = sz
@@ -134,14 +137,21 @@ def ss_ckpt_empty(u, dstate=16):
     return torch.empty(max(n, 1), dtype=torch.float32, device=u.device)
 
 
+def ss_fwd_workspace_size(batch, dim, dstate, seqlen) -> int:
+    return int(load().ss_fwd_workspace_size(batch, dim, dstate, seqlen))
+
+
 def ss_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-           h0=None, out=None, last_state=None, return_last_state=False, ckpt=None):
+           h0=None, out=None, last_state=None, return_last_state=False, ckpt=None,
+           workspace=None):
     """Forward scan; returns ``out`` or ``(out, last_state)``.
 
     u, delta, z: (batch, dim, L); B, C: (batch, dstate, L) in float32 or bfloat16;
     A: (dim, dstate), D, delta_bias: (dim,), h0: (batch, dim, dstate) float32.
     ckpt: optional float32 buffer (see ss_ckpt_empty) that receives the chunk
-    checkpoints for a later ss_bwd.
+    checkpoints for a later ss_bwd.  workspace: device buffer of at least
+    ss_fwd_workspace_size() bytes (allocated here when None and needed, i.e.
+    dstate > 16).
     """
     lib = load()
     batch, dim, seqlen = u.shape
@@ -152,10 +162,15 @@ def ss_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=Fa
         out = torch.empty_like(u)
     if return_last_state and last_state is None:
         last_state = torch.empty(batch, dim, dstate, dtype=torch.float32, device=u.device)
+    need = ss_fwd_workspace_size(batch, dim, dstate, seqlen)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
     _check(lib.ss_fwd(batch, dim, dstate, seqlen, io, _ptr(u), _ptr(delta), _f32(A, "A"),
                       _ptr(B), _ptr(C), _f32(D, "D"), _ptr(z), _f32(delta_bias, "delta_bias"),
                       int(bool(delta_softplus)), _f32(h0, "h0"), _ptr(out),
-                      _f32(last_state, "last_state"), _f32(ckpt, "ckpt"), _stream()))
+                      _f32(last_state, "last_state"), _f32(ckpt, "ckpt"), _ptr(workspace),
+                      0 if workspace is None else workspace.numel() * workspace.element_size(),
+                      _stream()))
     return (out, last_state) if (return_last_state or last_state is not None) else out
 
 

@@ -69,9 +69,9 @@ ss_status check_dims(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
     if (dstate <= 0) return fail(SS_EINVAL, "dstate must be > 0 (got %lld)", (long long)dstate);
     if (io != SS_F32 && io != SS_BF16)
         return fail(SS_EINVAL, "io_dtype must be SS_F32 (0) or SS_BF16 (1) (got %d)", io);
-    if (dstate > 16)
-        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (this build handles 1..16)",
-                    (long long)dstate);
+    if (dstate > ssk::kMaxState)
+        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (this build handles 1..%d)",
+                    (long long)dstate, ssk::kMaxState);
     if (scan && batch > kMaxBatch)
         return fail(SS_EUNSUPPORTED, "batch %lld exceeds %lld", (long long)batch,
                     (long long)kMaxBatch);
@@ -136,10 +136,16 @@ int ss_abi_version(void) { return SS_ABI_VERSION; }
 
 const char *ss_last_error(void) { return g_err; }
 
+size_t ss_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+    if (check_dims(batch, dim, dstate, seqlen, SS_F32, true) != SS_OK) return 0;
+    return ssk::fwd_workspace_bytes(batch, dim, seqlen, int(dstate));
+}
+
 ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
                  const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int delta_softplus,
-                 const float *h0, void *out, float *last_state, float *ckpt, void *stream) {
+                 const float *h0, void *out, float *last_state, float *ckpt, void *workspace,
+                 size_t workspace_bytes, void *stream) {
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
     const bool has_rows = batch > 0 && dim > 0;
@@ -163,12 +169,22 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     if (c.st != SS_OK) return c.st;
     if (h0 && last_state && h0 == last_state)
         return fail(SS_EINVAL, "last_state must not alias h0");
+    const size_t need = ssk::fwd_workspace_bytes(batch, dim, seqlen, int(dstate));
+    if (need > 0) {
+        if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
+        if (!aligned16(workspace)) return fail(SS_EINVAL, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(SS_EINVAL, "workspace_bytes %zu is smaller than the %zu bytes needed",
+                        workspace_bytes, need);
+    }
     ssk::FwdParams p{};
     p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.nstate = int(dstate);
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.out = out; p.last_state = last_state; p.ckpt = ckpt;
-    p.ypre = ckpt ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
+    p.ypre = (ckpt && ssk::state_slices(int(dstate)) == 1)
+                 ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
+    p.ypart = static_cast<float *>(workspace);
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
                          "ss_fwd launch");
@@ -176,13 +192,13 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
 
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
     if (check_dims(batch, dim, dstate, seqlen, SS_F32, true) != SS_OK) return 0;
-    return ssk::ckpt_bytes(batch, dim, seqlen);
+    return ssk::ckpt_bytes(batch, dim, seqlen, int(dstate));
 }
 
 size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                              int io_dtype) {
     if (check_dims(batch, dim, dstate, seqlen, io_dtype, true) != SS_OK) return 0;
-    return ssk::bwd_workspace_bytes(batch, dim, seqlen);
+    return ssk::bwd_workspace_bytes(batch, dim, seqlen, int(dstate));
 }
 
 ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
@@ -218,7 +234,7 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     c.pair(dz, z, "dz", "z");
     c.pair(ddelta_bias, delta_bias, "ddelta_bias", "delta_bias");
     if (c.st != SS_OK) return c.st;
-    const size_t need = ssk::bwd_workspace_bytes(batch, dim, seqlen);
+    const size_t need = ssk::bwd_workspace_bytes(batch, dim, seqlen, int(dstate));
     if (need > 0) {
         if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
         if (!aligned16(workspace)) return fail(SS_EINVAL, "workspace must be 16-byte aligned");
@@ -232,7 +248,8 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.dout = dout; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB;
     p.dC = dC; p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0; p.ckpt = ckpt;
-    p.ypre = ckpt ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
+    p.ypre = (ckpt && ssk::state_slices(int(dstate)) == 1)
+                 ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
     p.workspace = workspace;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),

@@ -42,6 +42,8 @@
 //      order and the dA/dD/dbias partials over the batch in ascending batch
 //      order.
 // Every sum runs in an order fixed by the shape, with no atomics.
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_tiles.h"
@@ -59,9 +61,13 @@ constexpr int kNB = kC / kCk;
 static_assert(kCk == 16 && (kNB == 1 || kNB == 2), "a staging chunk holds one or two 16-step blocks");
 constexpr int kThreads = 256;
 
-// Workspace carve-up (all f32, 256-byte aligned pieces).
+// Workspace carve-up (all f32, 256-byte aligned pieces).  With several
+// 16-state slices the block states hold every slice, the partials of the
+// sums over channels, batch and time come once per slice (slice k's at
+// slice_bytes k further on, see slice_ws), and three (slice, batch, dim, L)
+// buffers take the per-slice partial du, ddelta and dz.
 struct Workspace {
-    float *ckpt;     // (batch, dim, nck, 16): state entering each 16-step block
+    float *ckpt;     // (slice, batch, dim, nck, 16): state entering each 16-step block
     const float *ypre;  // pre-gate output saved by the forward, or nullptr
     float *dBp;      // (batch, groups, 16, L); sized for 16-channel groups
     float *dCp;      // (batch, groups, 16, L)
@@ -70,14 +76,17 @@ struct Workspace {
     float *dAp;      // (batch, dim, 16)
     float *dDp;      // (batch, dim)
     float *dbiasp;   // (batch, dim)
+    size_t slice_bytes;       // distance between two slices' dBp .. dbiasp
+    float *dup, *ddp, *dzp;   // several slices: (slice, batch, dim, L) partials
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L,
-                                           size_t *total) {
+                                           int nstate, size_t *total) {
     const int64_t nck = (L + kCk - 1) / kCk;
     const int64_t groups = (dim + kRows - 1) / kRows;
+    const int slices = state_slices(nstate);
     size_t off = 0;
     Workspace w;
     char *p = static_cast<char *>(base);
@@ -86,8 +95,9 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
         off += align256(floats * sizeof(float));
         return r;
     };
-    w.ckpt = take(size_t(batch) * dim * nck * kN);
+    w.ckpt = take(size_t(slices) * batch * dim * nck * kN);
     w.ypre = nullptr;
+    const size_t first = off;
     w.dBp = take(size_t(batch) * groups * kN * L);
     w.dCp = take(size_t(batch) * groups * kN * L);
     w.groups = groups;
@@ -95,7 +105,27 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
     w.dAp = take(size_t(batch) * dim * kN);
     w.dDp = take(size_t(batch) * dim);
     w.dbiasp = take(size_t(batch) * dim);
+    w.slice_bytes = off - first;
+    off += (slices - 1) * w.slice_bytes;
+    w.dup = w.ddp = w.dzp = nullptr;
+    if (slices > 1) {
+        const size_t e = size_t(slices) * batch * dim * L;
+        w.dup = take(e);
+        w.ddp = take(e);
+        w.dzp = take(e);
+    }
     if (total) *total = off;
+    return w;
+}
+
+// The per-slice partial pointers of slice k.
+__host__ __device__ inline Workspace slice_ws(Workspace w, int k) {
+    const size_t sh = size_t(k) * w.slice_bytes / sizeof(float);
+    w.dBp += sh;
+    w.dCp += sh;
+    w.dAp += sh;
+    w.dDp += sh;
+    w.dbiasp += sh;
     return w;
 }
 
@@ -180,15 +210,19 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
     const int64_t d0 = int64_t(blockIdx.x) * kRows, d = d0 + r;
     const bool row_ok = d < Dm;
     const int valid_rows = int(Dm - d0 < kRows ? Dm - d0 : kRows);
-    const int Ns = p.nstate;   // state lanes n >= Ns carry zero A and B
+    // this slice (grid z) holds states s0 .. s0 + Ns - 1 of Nst; lanes
+    // n >= Ns carry zero A and B
+    const int Nst = p.nstate, s0 = 16 * int(blockIdx.z);
+    const int Ns = Nst - s0 < kN ? Nst - s0 : kN;
     const bool st_ok = row_ok && n < Ns;
-    const float a2 = st_ok ? p.A[d * Ns + n] * kLog2e : 0.0f;
+    const float a2 = st_ok ? p.A[d * Nst + s0 + n] * kLog2e : 0.0f;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
-    float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Ns + n] : 0.0f;
+    float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Nst + s0 + n] : 0.0f;
     const int64_t nck = (L + kCk - 1) / kCk;
-    float *ck = ws.ckpt + (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
+    float *ck = ws.ckpt + blockIdx.z * ckpt_state_floats(p.batch, Dm, L) +
+                (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
 
-    const T *gB = static_cast<const T *>(p.B) + b * Ns * L;
+    const T *gB = static_cast<const T *>(p.B) + (b * Nst + s0) * L;
     const bool zero_dead = Ns < kN;   // B rows past dstate must read as zeros
     const T *gu = static_cast<const T *>(p.u) + (b * Dm + d0) * L;
     const T *gdl = static_cast<const T *>(p.delta) + (b * Dm + d0) * L;
@@ -291,9 +325,14 @@ struct RevSmem {
 // instead of recomputing the sum of C h over the states.
 // NW: wavefronts per workgroup (4 or 12; 4 NW channels).  Either way the
 // launch bound leaves 3 wavefronts per SIMD (2 for single-element loads).
-template <typename T, int VEC, bool YP, int NW>
+// PART: one 16-state slice of several (grid z): du, ddelta and dz are this
+// slice's f32 partials (the combine kernel adds the slices and the D terms).
+template <typename T, int VEC, bool YP, int NW, bool PART>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) : 1) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
     using SM = RevSmem<T, NW>;
+    using OutT = std::conditional_t<PART, float, T>;
+    static_assert(!(PART && YP), "slices recompute their share of the pre-gate output");
+    if (PART) ws = slice_ws(ws, int(blockIdx.z));
     constexpr bool kStage = kStageElems<T>;
     constexpr int kRowsG = SM::kR;
     constexpr int kThr = 64 * NW;
@@ -312,9 +351,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
-    const int Ns = p.nstate;   // state lanes n >= Ns carry zero A, B, C
+    // this slice (grid z) holds states s0 .. s0 + Ns - 1 of Nst; lanes
+    // n >= Ns carry zero A, B, C
+    const int Nst = p.nstate, s0 = 16 * int(blockIdx.z);
+    const int Ns = Nst - s0 < kN ? Nst - s0 : kN;
     const bool st_ok = row_ok && n < Ns;
-    const float aval = st_ok ? p.A[d * Ns + n] : 0.0f;
+    const float aval = st_ok ? p.A[d * Nst + s0 + n] : 0.0f;
     const float a2 = aval * kLog2e;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
@@ -324,7 +366,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // accesses address the wavefront's 4 rows from a scalar base with 32-bit
     // byte offsets (4 rows x seqlen x 4 bytes < 2^32).
     const int Ls = int(L), nckS = int(nck);
-    const float *ckb = ws.ckpt + (b * Dm + dw) * nck * kN;
+    const float *ckb = ws.ckpt + blockIdx.z * ckpt_state_floats(p.batch, Dm, L) + (b * Dm + dw) * nck * kN;
     const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
     // state entering block k; a block past the end (only padding steps) has none
     auto ckpt_at = [&](int k) {
@@ -332,13 +374,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                                               : 0.0f;
     };
 
-    float g = (st_ok && p.dlast) ? p.dlast[(b * Dm + d) * Ns + n] : 0.0f;
+    float g = (st_ok && p.dlast) ? p.dlast[(b * Dm + d) * Nst + s0 + n] : 0.0f;
     float dA_acc = 0.0f;     // this lane's state entry, summed over time
     float dD_acc = 0.0f;     // elements owned by this lane
     float dbias_acc = 0.0f;
 
-    const T *gB = static_cast<const T *>(p.B) + b * Ns * L;
-    const T *gC = static_cast<const T *>(p.C) + b * Ns * L;
+    const T *gB = static_cast<const T *>(p.B) + (b * Nst + s0) * L;
+    const T *gC = static_cast<const T *>(p.C) + (b * Nst + s0) * L;
     const bool zero_dead = Ns < kN;   // B / C rows past dstate must read as zeros
     // this lane's row of the element-wise tensors; a row's 16 lanes load and
     // store 16 consecutive elements of a 16-step block
@@ -347,11 +389,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
     const T *gdo = static_cast<const T *>(p.dout) + wavebase;
-    T *du_b = static_cast<T *>(p.du) + wavebase;
-    T *dd_b = static_cast<T *>(p.ddelta) + wavebase;
-    T *dz_b = has_z ? static_cast<T *>(p.dz) + wavebase : nullptr;
+    const size_t slice_el = PART ? blockIdx.z * size_t(p.batch * Dm * L) : 0;
+    OutT *du_b = (PART ? reinterpret_cast<OutT *>(ws.dup + slice_el) : static_cast<OutT *>(p.du)) + wavebase;
+    OutT *dd_b = (PART ? reinterpret_cast<OutT *>(ws.ddp + slice_el) : static_cast<OutT *>(p.ddelta)) + wavebase;
+    OutT *dz_b = has_z ? (PART ? reinterpret_cast<OutT *>(ws.dzp + slice_el) : static_cast<OutT *>(p.dz)) + wavebase
+                       : nullptr;
     const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
     auto elem_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(T)); };
+    auto out_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(OutT)); };
     // the saved pre-gate output: each owner lane loads its elements straight
     // from global memory, a chunk ahead (a row's 16 lanes read 16 floats)
     const float *ypb = ws.ypre + wavebase;
@@ -514,8 +559,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                 const float sz = sigmoid_f32(zz[s]);
                 dyv[s] = dout[s] * zz[s] * sz;
                 if (YP && row_ok && t0 + col < Ls)
-                    st_global(at_bytes(dz_b, elem_off(t0 + col)),
-                              from_f32<T>(dout[s] * ypn[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
+                    st_global(at_bytes(dz_b, out_off(t0 + col)),
+                              from_f32<OutT>(dout[s] * ypn[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
             }
             if (!row_ok) dyv[s] = 0.0f;
         }
@@ -565,8 +610,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                                    dskip * uu[s];
                 const float sz = sigmoid_f32(zz[s]);
                 if (row_ok && t0 + col < Ls)
-                    st_global(at_bytes(dz_b, elem_off(t0 + col)),
-                              from_f32<T>(dout[s] * ypre * sz * (1.0f + zz[s] * (1.0f - sz))));
+                    st_global(at_bytes(dz_b, out_off(t0 + col)),
+                              from_f32<OutT>(dout[s] * ypre * sz * (1.0f + zz[s] * (1.0f - sz))));
             }
             if (t0 + col < Ls) dD_acc = __builtin_fmaf(dy, uu[s], dD_acc);
 
@@ -629,8 +674,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             const float du = __builtin_fmaf(dl[s], sumB, dskip * dy);
             const float dd = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];
             if (row_ok && t0 + col < Ls) {
-                st_global(at_bytes(du_b, elem_off(t0 + col)), from_f32<T>(du));
-                st_global(at_bytes(dd_b, elem_off(t0 + col)), from_f32<T>(dd));
+                st_global(at_bytes(du_b, out_off(t0 + col)), from_f32<OutT>(du));
+                st_global(at_bytes(dd_b, out_off(t0 + col)), from_f32<OutT>(dd));
             }
             if (t0 + col < Ls) dbias_acc += dd;
         }
@@ -651,7 +696,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         ws.dDp[b * Dm + d] = dD_acc;
         ws.dbiasp[b * Dm + d] = dbias_acc;
     }
-    if (p.dh0 && st_ok) p.dh0[(b * Dm + d) * Ns + n] = g;
+    if (p.dh0 && st_ok) p.dh0[(b * Dm + d) * Nst + s0 + n] = g;
 }
 
 // ---------------------------------------------------------------------------
@@ -692,7 +737,7 @@ template <typename T, int VT>
 __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace ws) {
     const int64_t L = p.seqlen, Dm = p.dim, Bt = p.batch;
     const int64_t groups = ws.groups;
-    const int64_t Ns = p.nstate;
+    const int64_t Ns = p.nstate;            // all slices
     const int64_t nbc = Bt * Ns * L / VT;   // dB / dC work items (VT divides L)
     const int64_t na = Dm * Ns;             // dA elements
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -703,9 +748,12 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
         // A 48-channel pass writes q itself; a 16-channel pass writes p.
         const int64_t e = i * VT;                                // (bb, n, t) element
         const int64_t bb = e / (Ns * L), rem = e - bb * Ns * L;  // rem = n * L + t
+        const int64_t ns = rem / L;                              // state n: slice ns / 16
+        const Workspace wk = slice_ws(ws, int(ns / kN));
+        const int64_t lrem = rem - (ns - ns % kN) * L;           // n % 16 * L + t
         const int64_t stride = kN * L;                           // one partial (16 states)
-        const float *pb = ws.dBp + bb * groups * stride + rem;
-        const float *pc = ws.dCp + bb * groups * stride + rem;
+        const float *pb = wk.dBp + bb * groups * stride + lrem;
+        const float *pc = wk.dCp + bb * groups * stride + lrem;
         float sb[VT] = {}, sc[VT] = {};
         if (ws.sub == 1) {   // partials are the q
             int64_t gi = 0;
@@ -747,20 +795,56 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
         }
     } else if (i < nbc + na) {
         const int64_t k = i - nbc;                      // (d, n) of dA
-        const int64_t src = (k / Ns) * kN + k % Ns;     // the 16-wide partial
+        const int64_t nn = k % Ns;
+        const float *dap = slice_ws(ws, int(nn / kN)).dAp;
+        const int64_t src = (k / Ns) * kN + nn % kN;    // the 16-wide partial of n's slice
         float s = 0.0f;
-        for (int64_t bb = 0; bb < Bt; bb++) s += ws.dAp[bb * Dm * kN + src];
+        for (int64_t bb = 0; bb < Bt; bb++) s += dap[bb * Dm * kN + src];
         p.dA[k] = s;
     } else if (i < nbc + na + Dm) {
+        // dD from the first slice (every slice sums the same dy u); dbias
+        // over batch, then slices, ascending
         const int64_t dd = i - nbc - na;
+        const int slices = state_slices(p.nstate);
         float sD = 0.0f, sb = 0.0f;
         for (int64_t bb = 0; bb < Bt; bb++) {
             sD += ws.dDp[bb * Dm + dd];
-            sb += ws.dbiasp[bb * Dm + dd];
+            for (int k = 0; k < slices; k++) sb += slice_ws(ws, k).dbiasp[bb * Dm + dd];
         }
         if (p.dD) p.dD[dd] = sD;
         if (p.dbias) p.dbias[dd] = sb;
     }
+}
+
+// Several slices: du = sum of the slices' partials + D dy, ddelta = sum of
+// the partials, dz = sum of the partials + dout (D u) silu'(z); the slices
+// in ascending order, one element per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Workspace ws, int slices) {
+    const int64_t E = p.batch * p.dim * p.seqlen;
+    const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= E) return;
+    const int64_t d = (e / p.seqlen) % p.dim;
+    const float u = to_f32<T>(ld_global(static_cast<const T *>(p.u) + e));
+    const float g = to_f32<T>(ld_global(static_cast<const T *>(p.dout) + e));
+    const float dskip = p.D ? p.D[d] : 0.0f;
+    float du = ld_global(ws.dup + e), dd = ld_global(ws.ddp + e);
+    for (int k = 1; k < slices; k++) {
+        du += ld_global(ws.dup + k * E + e);
+        dd += ld_global(ws.ddp + k * E + e);
+    }
+    float dy = g;
+    if (p.z) {
+        const float z = to_f32<T>(ld_global(static_cast<const T *>(p.z) + e));
+        const float sz = sigmoid_f32(z);
+        dy = g * z * sz;
+        float dz = ld_global(ws.dzp + e);
+        for (int k = 1; k < slices; k++) dz += ld_global(ws.dzp + k * E + e);
+        dz += g * (dskip * u) * sz * (1.0f + z * (1.0f - sz));
+        st_global(static_cast<T *>(p.dz) + e, from_f32<T>(dz));
+    }
+    st_global(static_cast<T *>(p.du) + e, from_f32<T>(du + dskip * dy));
+    st_global(static_cast<T *>(p.ddelta) + e, from_f32<T>(dd));
 }
 
 // Wavefronts per reverse-pass workgroup: scan_waves' choice for 16-byte
@@ -770,21 +854,23 @@ int reverse_waves(const BwdParams &p, bool vec) {
     return scan_waves(p.batch, p.dim);
 }
 
-template <typename T, int VEC, bool YP, int NW>
+template <typename T, int VEC, bool YP, int NW, bool PART = false>
 void launch_reverse(const BwdParams &p, Workspace ws, hipStream_t stream) {
-    const dim3 grid(unsigned((p.dim + 4 * NW - 1) / (4 * NW)), unsigned(p.batch));
-    hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW>), grid, dim3(64 * NW), 0, stream, p, ws);
+    const dim3 grid(unsigned((p.dim + 4 * NW - 1) / (4 * NW)), unsigned(p.batch),
+                    unsigned(state_slices(p.nstate)));
+    hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW, PART>), grid, dim3(64 * NW), 0, stream, p, ws);
 }
 
 template <typename T>
 hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
-    Workspace ws = carve(p.workspace, p.batch, p.dim, p.seqlen, nullptr);
+    Workspace ws = carve(p.workspace, p.batch, p.dim, p.seqlen, p.nstate, nullptr);
+    const int slices = state_slices(p.nstate);
     if (p.ckpt) {  // saved by the forward: read only
         ws.ckpt = const_cast<float *>(p.ckpt);
-        ws.ypre = p.ypre;
+        ws.ypre = slices == 1 ? p.ypre : nullptr;
     }
     if (p.batch > 0 && p.dim > 0) {
-        dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch));
+        dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch), unsigned(slices));
         constexpr int kVec = 16 / sizeof(T);
         const bool vec = (p.seqlen * int64_t(sizeof(T))) % 16 == 0;
         if (!p.ckpt) {
@@ -794,11 +880,19 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
                 hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
             profile_mark(stream);
         }
-        const bool yp = p.ckpt && p.ypre && p.z;
+        const bool yp = slices == 1 && p.ckpt && p.ypre && p.z;
         const int nw = reverse_waves(p, vec);
         ws.groups = (p.dim + 4 * nw - 1) / (4 * nw);   // the partials the fold reads
         ws.sub = nw == 12 ? 1 : 3;
-        if (vec && nw == 12) {
+        // slices see no D term (the combine adds it and its gradients)
+        BwdParams q = p;
+        q.D = nullptr;
+        q.ypre = nullptr;
+        if (slices > 1) {
+            if (vec && nw == 12) launch_reverse<T, kVec, false, 12, true>(q, ws, stream);
+            else if (vec) launch_reverse<T, kVec, false, 4, true>(q, ws, stream);
+            else launch_reverse<T, 1, false, 4, true>(q, ws, stream);
+        } else if (vec && nw == 12) {
             if (yp) launch_reverse<T, kVec, true, 12>(p, ws, stream);
             else launch_reverse<T, kVec, false, 12>(p, ws, stream);
         } else if (vec) {
@@ -811,6 +905,12 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         profile_mark(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        const int64_t E = p.batch * p.dim * p.seqlen;
+        if (slices > 1 && E > 0) {
+            hipLaunchKernelGGL((ss_bwd_combine_kernel<T>), dim3(unsigned((E + 255) / 256)),
+                               dim3(256), 0, stream, p, ws, slices);
+            profile_mark(stream);
+        }
     }
     const bool v4 = p.seqlen % 4 == 0;   // 16-byte partial loads
     const int64_t total = p.batch * p.nstate * p.seqlen / (v4 ? 4 : 1) + p.dim * p.nstate + p.dim;
@@ -827,9 +927,9 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen) {
+size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate) {
     size_t total = 0;
-    carve(nullptr, batch, dim, seqlen, &total);
+    carve(nullptr, batch, dim, seqlen, nstate, &total);
     return total;
 }
 

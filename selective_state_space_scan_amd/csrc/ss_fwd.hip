@@ -28,7 +28,13 @@
 //     transpose every 16 steps, padded so that neither the 16-byte writes
 //     nor the 4-byte reads hit the same bank twice, and is added in a fixed
 //     order -- a row's bits do not depend on the batch size or on the other
-//     rows of its workgroup.
+//     rows of its workgroup;
+//   * d_state above 16 runs one 16-state slice per grid z: each slice
+//     writes its sums over its states as f32 partials (no D term, no gate),
+//     and a combine kernel adds the slices in ascending order, adds D u and
+//     applies the gate.
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_tiles.h"
@@ -67,9 +73,11 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
     v = c * h;
 }
 
-// NW: wavefronts per workgroup (4 or 12; 4 NW channels).
-template <typename T, int VEC, int NW>
+// NW: wavefronts per workgroup (4 or 12; 4 NW channels).  PART: one slice
+// of several (grid z); the output is the slice's f32 partial sum of C h.
+template <typename T, int VEC, int NW, bool PART>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) : 1) void ss_fwd_kernel(FwdParams p) {
+    using OutT = std::conditional_t<PART, float, T>;
     using SM = FwdSmem<T, NW>;
     constexpr bool kStage = kStageElems<T>;
     constexpr int kRowsG = 4 * NW;
@@ -93,12 +101,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
-    const int Ns = p.nstate;       // state lanes n >= Ns carry zero A, B, C
+    // this slice's states: s0 .. s0 + Ns - 1 of Nst; lanes n >= Ns carry
+    // zero A, B, C
+    const int Nst = p.nstate;
+    const int s0 = PART ? 16 * int(blockIdx.z) : 0;
+    const int Ns = PART ? (Nst - s0 < kN ? Nst - s0 : kN) : Nst;
     const bool st_ok = row_ok && n < Ns;
-    float a2 = st_ok ? p.A[d * Ns + n] * kLog2e : 0.0f;  // A in base-2 exponent units
+    float a2 = st_ok ? p.A[d * Nst + s0 + n] * kLog2e : 0.0f;  // A in base-2 exponent units
     float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
-    float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Ns + n] : 0.0f;
+    float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Nst + s0 + n] : 0.0f;
 
     // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the
     // per-row accesses address the wavefront's 4 rows from a scalar base with
@@ -110,8 +122,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
     const int64_t groupbase = (b * Dm + d0) * L;   // the group's first row (staged tiles)
-    const T *gB = static_cast<const T *>(p.B) + b * Ns * L;
-    const T *gC = static_cast<const T *>(p.C) + b * Ns * L;
+    const T *gB = static_cast<const T *>(p.B) + (b * Nst + s0) * L;
+    const T *gC = static_cast<const T *>(p.C) + (b * Nst + s0) * L;
     const bool zero_dead = Ns < kN;   // B / C rows past dstate must read as zeros
     // element t of this lane's row (0 past the end and for rows past the
     // last channel); a row's 16 lanes read 16 consecutive elements
@@ -169,10 +181,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
     const int nckS = int(nck);
     const bool save_ck = p.ckpt != nullptr;
-    float *ckb = save_ck ? p.ckpt + (b * Dm + dw) * nck * kN : nullptr;
+    float *ckb = save_ck ? p.ckpt + blockIdx.z * ckpt_state_floats(p.batch, Dm, L) +
+                               (b * Dm + dw) * nck * kN
+                         : nullptr;
     const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
     float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
-    T *yb = static_cast<T *>(p.out) + wavebase;
+    OutT *yb = (PART ? reinterpret_cast<OutT *>(p.ypart + blockIdx.z * size_t(p.batch * Dm * L))
+                     : static_cast<OutT *>(p.out)) +
+               wavebase;
     // the pre-gate output, saved for the backward's dz
     const bool save_yp = p.ypre && has_z;
     float *ypb = save_yp ? p.ypre + wavebase : nullptr;
@@ -221,7 +237,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
             // a row's 16 lanes store 16 consecutive outputs
             const int t = t0 + 16 * s + n;
             if (row_ok && t < Ls) {
-                st_global(at_bytes(yb, uint32_t(rowel + t) * uint32_t(sizeof(T))), from_f32<T>(y));
+                st_global(at_bytes(yb, uint32_t(rowel + t) * uint32_t(sizeof(OutT))), from_f32<OutT>(y));
                 if (save_yp) st_global(at_bytes(ypb, uint32_t(rowel + t) * 4u), ypre);
             }
         };
@@ -272,14 +288,33 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
         __syncthreads();
     }
 
-    if (p.last_state && st_ok) p.last_state[(b * Dm + d) * Ns + n] = h;
+    if (p.last_state && st_ok) p.last_state[(b * Dm + d) * Nst + s0 + n] = h;
 }
 
-template <typename T, int VEC, int NW>
+// Several slices: out = (sum of the slices' partials, ascending, + D u) *
+// silu(z), one element per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void ss_fwd_combine_kernel(FwdParams p, int slices) {
+    const int64_t E = p.batch * p.dim * p.seqlen;
+    const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= E) return;
+    const int64_t d = (e / p.seqlen) % p.dim;
+    float s = ld_global(p.ypart + e);
+    for (int k = 1; k < slices; k++) s += ld_global(p.ypart + k * E + e);
+    const float u = to_f32<T>(ld_global(static_cast<const T *>(p.u) + e));
+    float y = s + (p.D ? p.D[d] : 0.0f) * u;
+    if (p.z) {
+        const float z = to_f32<T>(ld_global(static_cast<const T *>(p.z) + e));
+        y *= z * sigmoid_f32(z);
+    }
+    st_global(static_cast<T *>(p.out) + e, from_f32<T>(y));
+}
+
+template <typename T, int VEC, int NW, bool PART>
 void launch_scan(const FwdParams &p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((p.dim + 4 * NW - 1) / (4 * NW)),
-                    static_cast<unsigned>(p.batch));
-    hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW>), grid, dim3(64 * NW), 0, stream, p);
+                    static_cast<unsigned>(p.batch), static_cast<unsigned>(state_slices(p.nstate)));
+    hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW, PART>), grid, dim3(64 * NW), 0, stream, p);
 }
 
 template <typename T>
@@ -289,15 +324,40 @@ hipError_t launch_typed(const FwdParams &p, hipStream_t stream) {
     // 4 wavefronts per workgroup: 12 would cut the B / C reads by two thirds,
     // but this pass is not bound by memory, and three independent
     // workgroups per compute unit overlap their barriers and LDS phases.
-    if ((p.seqlen * static_cast<int64_t>(sizeof(T))) % 16 == 0)
-        launch_scan<T, kVec, 4>(p, stream);
-    else
-        launch_scan<T, 1, 4>(p, stream);
+    const bool vec = (p.seqlen * static_cast<int64_t>(sizeof(T))) % 16 == 0;
+    const int slices = state_slices(p.nstate);
+    if (slices == 1) {
+        if (vec) launch_scan<T, kVec, 4, false>(p, stream);
+        else launch_scan<T, 1, 4, false>(p, stream);
+        profile_mark(stream);
+        return hipGetLastError();
+    }
+    // the slices see no D term and no gate; the combine adds them
+    FwdParams q = p;
+    q.D = nullptr;
+    q.z = nullptr;
+    q.ypre = nullptr;
+    if (vec) launch_scan<T, kVec, 4, true>(q, stream);
+    else launch_scan<T, 1, 4, true>(q, stream);
     profile_mark(stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t E = p.batch * p.dim * p.seqlen;
+    if (E > 0) {
+        hipLaunchKernelGGL((ss_fwd_combine_kernel<T>), dim3(unsigned((E + 255) / 256)), dim3(256),
+                           0, stream, p, slices);
+        profile_mark(stream);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
+
+size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate) {
+    const int slices = state_slices(nstate);
+    if (slices == 1 || batch <= 0 || dim <= 0 || seqlen <= 0) return 0;
+    return size_t(slices) * size_t(batch) * size_t(dim) * size_t(seqlen) * sizeof(float);
+}
 
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream) {
     if (p.batch == 0 || p.dim == 0) return hipSuccess;

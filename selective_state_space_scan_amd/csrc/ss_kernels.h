@@ -9,13 +9,22 @@
 
 namespace ssk {
 
-// Kernels keep 16 state lanes per row; with dstate N < 16 the lanes n >= N
-// carry zero A, B and C (their state stays exactly zero) and the per-state
-// tensors are read and written with stride N.  Internal buffers (saved
-// block states, workspace partials) stay 16 wide.
+// Kernels keep 16 state lanes per row.  dstate N is cut into slices of 16
+// states (grid z = slice): slice k holds states 16k .. 16k + 15, and with
+// fewer than 16 left its lanes past N carry zero A, B and C (their state
+// stays exactly zero).  Per-state tensors are read and written with stride
+// N.  Internal buffers (saved block states, workspace partials) are 16 wide
+// per slice.  With more than one slice the scan kernels write each slice's
+// per-element sums over its states as f32 partials, and a combine kernel
+// adds the slices in ascending order together with the per-element terms
+// (D u, the gate, their gradients).
+constexpr int kMaxState = 256;
+
+__host__ __device__ inline int state_slices(int nstate) { return (nstate + 15) / 16; }
+
 struct ScanParams {
     int64_t batch, dim, seqlen;
-    int nstate;   // dstate, 1..16
+    int nstate;   // dstate, 1..kMaxState
     const void *u, *delta;
     const float *A;
     const void *B, *C;
@@ -27,19 +36,25 @@ struct ScanParams {
 };
 
 // What the forward saves for the backward (one f32 buffer, ss_ckpt_size()
-// bytes): the state entering every 16-step block, (batch, dim, ceil(L / 16),
-// 16), then -- at the next 256-byte boundary -- the pre-gate output
-// (batch, dim, L), written when z is given (the backward's dz needs it).
+// bytes): the state entering every 16-step block, (slice, batch, dim,
+// ceil(L / 16), 16), then -- with one slice only, at the next 256-byte
+// boundary -- the pre-gate output (batch, dim, L), written when z is given
+// (the backward's dz reads it; with several slices the backward adds dz up
+// from per-slice partials instead).
 constexpr int kCkptSpacing = 16;
 
+// block states of one slice, in floats
 __host__ __device__ inline size_t ckpt_state_floats(int64_t batch, int64_t dim, int64_t seqlen) {
     return size_t(batch) * size_t(dim) * size_t((seqlen + kCkptSpacing - 1) / kCkptSpacing) * 16;
 }
 __host__ __device__ inline size_t ckpt_ypre_offset(int64_t batch, int64_t dim, int64_t seqlen) {
     return (ckpt_state_floats(batch, dim, seqlen) + 63) / 64 * 64;  // floats
 }
-__host__ __device__ inline size_t ckpt_bytes(int64_t batch, int64_t dim, int64_t seqlen) {
+__host__ __device__ inline size_t ckpt_bytes(int64_t batch, int64_t dim, int64_t seqlen,
+                                             int nstate) {
     if (batch <= 0 || dim <= 0 || seqlen <= 0) return 0;
+    const int ns = state_slices(nstate);
+    if (ns > 1) return ckpt_state_floats(batch, dim, seqlen) * ns * sizeof(float);
     return (ckpt_ypre_offset(batch, dim, seqlen) + size_t(batch) * size_t(dim) * size_t(seqlen)) *
            sizeof(float);
 }
@@ -47,8 +62,9 @@ __host__ __device__ inline size_t ckpt_bytes(int64_t batch, int64_t dim, int64_t
 struct FwdParams : ScanParams {
     void *out;
     float *last_state;
-    float *ckpt;  // block states, or nullptr
-    float *ypre;  // pre-gate output (written when z is given), or nullptr
+    float *ckpt;   // block states, or nullptr
+    float *ypre;   // pre-gate output (written when z is given), or nullptr
+    float *ypart;  // workspace, several slices: (slice, batch, dim, L) partial sums of C h
 };
 
 struct BwdParams : ScanParams {
@@ -68,7 +84,7 @@ struct BwdParams : ScanParams {
 
 struct DecodeParams {
     int64_t batch, dim;
-    int nstate;   // dstate, 1..16
+    int nstate;   // dstate, 1..kMaxState
     float *state;
     const void *u, *delta;
     const float *A;
@@ -129,8 +145,9 @@ int device_cus();
 // (3 per compute unit) would.  Else 4.
 int scan_waves(int64_t batch, int64_t dim);
 
+size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate);
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream);
-size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen);
+size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate);
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);
 hipError_t launch_state_update(const DecodeParams &p, bool bf16, hipStream_t stream);
 

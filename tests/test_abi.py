@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 5
+    assert lib.ss_abi_version() == 6
 
 
 def test_ckpt_size(lib):
@@ -51,7 +51,10 @@ def test_ckpt_size(lib):
     assert lib.ss_ckpt_size(2, 32, 16, 0) == 0
     # the block states are 16 wide for any dstate up to 16
     assert lib.ss_ckpt_size(2, 32, 8, 64) == lib.ss_ckpt_size(2, 32, 16, 64)
-    assert lib.ss_ckpt_size(2, 32, 17, 64) == 0
+    # above 16: 16 states per slice, no saved pre-gate output
+    assert lib.ss_ckpt_size(2, 32, 17, 64) == 2 * 2 * 32 * 4 * 16 * 4
+    assert lib.ss_ckpt_size(2, 32, 256, 64) == 16 * 2 * 32 * 4 * 16 * 4
+    assert lib.ss_ckpt_size(2, 32, 257, 64) == 0
 
 
 def test_bwd_misaligned_ckpt(lib):
@@ -59,9 +62,10 @@ def test_bwd_misaligned_ckpt(lib):
 
 
 def _fwd(lib, batch=2, dim=32, dstate=16, seqlen=64, io=0, u=FAKE, delta=FAKE, A=FAKE, B=FAKE,
-         C=FAKE, D=None, z=None, bias=None, h0=None, out=FAKE, last=None, ckpt=None):
+         C=FAKE, D=None, z=None, bias=None, h0=None, out=FAKE, last=None, ckpt=None, ws=None,
+         ws_bytes=0):
     return lib.ss_fwd(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, bias, 1, h0, out,
-                      last, ckpt, None)
+                      last, ckpt, ws, ws_bytes, None)
 
 
 def _msg(lib):
@@ -84,7 +88,7 @@ def test_fwd_misaligned_pointer(lib, arg):
 @pytest.mark.parametrize("kw,status,word", [
     (dict(batch=-1), EINVAL, "batch"), (dict(dim=-3), EINVAL, "dim"),
     (dict(seqlen=-1), EINVAL, "seqlen"), (dict(dstate=0), EINVAL, "dstate"),
-    (dict(dstate=17), EUNSUP, "dstate"), (dict(dstate=64), EUNSUP, "dstate"),
+    (dict(dstate=257), EUNSUP, "dstate"), (dict(dstate=1000), EUNSUP, "dstate"),
     (dict(io=7), EINVAL, "io_dtype"), (dict(batch=70000), EUNSUP, "batch"),
     (dict(seqlen=(1 << 26) + 1), EUNSUP, "seqlen"),
 ])
@@ -148,7 +152,9 @@ def test_workspace_size_is_monotone_and_zero_when_invalid(lib):
     assert lib.ss_bwd_workspace_size(2, 32, 16, 128, 0) > base
     # internal buffers are 16 states wide for any dstate up to 16
     assert lib.ss_bwd_workspace_size(2, 32, 8, 64, 0) == base
-    assert lib.ss_bwd_workspace_size(2, 32, 17, 64, 0) == 0
+    # above 16 states: per-slice partials and (slice, batch, dim, L) buffers
+    assert lib.ss_bwd_workspace_size(2, 32, 17, 64, 0) > 2 * base
+    assert lib.ss_bwd_workspace_size(2, 32, 257, 64, 0) == 0
     assert lib.ss_bwd_workspace_size(-1, 32, 16, 64, 0) == 0
 
 
@@ -156,7 +162,7 @@ def test_decode_checks(lib):
     st = lib.ss_state_update(4, 32, 16, 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
                              1, FAKE, None)
     assert st == EINVAL and "state" in _msg(lib)
-    st = lib.ss_state_update(4, 32, 17, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+    st = lib.ss_state_update(4, 32, 257, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
                              1, FAKE, None)
     assert st == EUNSUP and "dstate" in _msg(lib)
     assert lib.ss_state_update(0, 32, 16, 1, None, None, None, None, None, None, None, None,
@@ -231,3 +237,15 @@ def test_conv_update_checks(lib):
     assert st == EINVAL and "state" in _msg(lib)
     st = lib.ss_conv1d_update(2, 8, 5, 0, FAKE, FAKE, FAKE, None, 1, FAKE, None)
     assert st == EUNSUP and "width" in _msg(lib)
+
+
+def test_fwd_workspace(lib):
+    # no workspace up to 16 states; above, one f32 partial per slice and element
+    assert lib.ss_fwd_workspace_size(2, 32, 16, 64) == 0
+    assert lib.ss_fwd_workspace_size(2, 32, 17, 64) == 2 * 2 * 32 * 64 * 4
+    assert lib.ss_fwd_workspace_size(2, 32, 256, 64) == 16 * 2 * 32 * 64 * 4
+    assert lib.ss_fwd_workspace_size(2, 32, 257, 64) == 0
+    need = lib.ss_fwd_workspace_size(2, 32, 64, 64)
+    assert _fwd(lib, dstate=64) == EINVAL and "workspace" in _msg(lib)
+    assert _fwd(lib, dstate=64, ws=FAKE, ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
+    assert _fwd(lib, dstate=64, ws=MISALIGNED, ws_bytes=need) == EINVAL and "aligned" in _msg(lib)

@@ -133,11 +133,15 @@ def test_bwd_rows_do_not_depend_on_batch(dim, L, io):
 
 
 @pytest.mark.parametrize("batch,dim,N,L,io", [(2, 40, 1, 64, "f32"), (2, 40, 5, 96, "bf16"),
-                                              (2, 24, 12, 70, "f32"), (8, 1544, 8, 64, "f32")])
+                                              (2, 24, 12, 70, "f32"), (8, 1544, 8, 64, "f32"),
+                                              (2, 40, 17, 64, "f32"), (2, 40, 48, 96, "bf16"),
+                                              (2, 24, 100, 70, "f32"), (2, 40, 256, 32, "f32"),
+                                              (8, 1544, 64, 64, "f32")])
 def test_bwd_smaller_dstate(batch, dim, N, L, io):
-    """d_state below 16, every gradient against the oracle (the last shape
-    takes the 48-channel reverse pass), and a backward with the forward's
-    saved record giving the same bits as one that recomputes it."""
+    """d_state other than 16, every gradient against the oracle (the
+    1544-channel shapes take the 48-channel reverse pass; above 16 states the
+    slices' partials go through the combine kernel), and a backward with the
+    forward's saved record giving the same bits as one that recomputes it."""
     require_gpu()
     w = ssin.custom("bwd", batch, dim, N, L, io, seed=17 * N + L + dim)
     arr = ssin.make(w)

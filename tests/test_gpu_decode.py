@@ -57,7 +57,8 @@ def test_decode_full_size_and_batch_invariance(io):
             assert torch.equal(y1[0], y[b]), f"y row {b}"
 
 
-@pytest.mark.parametrize("N,io", [(1, "f32"), (6, "bf16"), (13, "f32")])
+@pytest.mark.parametrize("N,io", [(1, "f32"), (6, "bf16"), (13, "f32"), (17, "f32"),
+                                  (64, "bf16"), (100, "f32"), (256, "bf16")])
 def test_decode_smaller_dstate(N, io):
     """d_state below 16 (element loads, unused state lanes held at zero)."""
     require_gpu()

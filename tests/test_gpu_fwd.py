@@ -73,10 +73,12 @@ def test_fwd_small_elementwise(batch, dim, L, io, flags):
 
 
 @pytest.mark.parametrize("N,io,L", [(1, "f32", 70), (4, "bf16", 64), (7, "f32", 100),
-                                    (12, "bf16", 40)])
+                                    (12, "bf16", 40), (17, "f32", 70), (32, "bf16", 64),
+                                    (64, "f32", 100), (100, "bf16", 40), (256, "f32", 48)])
 def test_fwd_smaller_dstate(N, io, L):
-    """d_state below 16: the kernels keep 16 state lanes and the unused ones
-    must add nothing (scalar and 16-byte load paths)."""
+    """d_state other than 16: the kernels keep 16 state lanes and the unused
+    ones must add nothing (scalar and 16-byte load paths); above 16 the
+    states run in 16-state slices whose sums a combine kernel adds."""
     require_gpu()
     w = ssin.custom("fwd", 2, 40, N, L, io, seed=31 * N + L)
     arr = ssin.make(w)
@@ -160,3 +162,20 @@ def test_fwd_full_size_sampled_rows_deterministic(name):
         torch.cuda.synchronize()
         assert torch.equal(ya[0].view(torch.int16), y1[b].view(torch.int16)), f"batch row {b}"
         assert torch.equal(la[0], l1[b])
+
+
+def test_fwd_wide_state_rows_do_not_depend_on_batch():
+    """With several state slices a row's output is still the same bits alone
+    and inside a batch."""
+    require_gpu()
+    w = ssin.custom("fwd", 4, 48, 64, 160, "bf16", seed=5)
+    arr = ssin.make(w)
+    d = dev_inputs(arr)
+    y, last = run_fwd(d, w, last=True)
+    for bi in (0, 3):
+        one = {k: (v[bi:bi + 1].contiguous() if k in ("u", "delta", "z", "B", "C") else v)
+               for k, v in d.items()}
+        y1, l1 = run_fwd(one, w, last=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0].view(torch.int16), y[bi].view(torch.int16)), f"y entry {bi}"
+        assert torch.equal(l1[0], last[bi]), f"last_state entry {bi}"
