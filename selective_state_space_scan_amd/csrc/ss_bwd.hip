@@ -818,33 +818,59 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
 
 // Several slices: du = sum of the slices' partials + D dy, ddelta = sum of
 // the partials, dz = sum of the partials + dout (D u) silu'(z); the slices
-// in ascending order, one element per thread.
-template <typename T>
+// in ascending order.  Each thread takes V consecutive elements of one row
+// (V = 4 when seqlen is a multiple of 4: 16-byte partial loads).
+template <int V>
+__device__ __forceinline__ void sum_slices(const float *src, int64_t E, int slices, float (&s)[V]) {
+    if constexpr (V == 4) {
+        float4 a = *reinterpret_cast<const float4 *>(src);
+        for (int k = 1; k < slices; k++) {
+            const float4 b = *reinterpret_cast<const float4 *>(src + k * E);
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+    } else {
+        s[0] = ld_global(src);
+        for (int k = 1; k < slices; k++) s[0] += ld_global(src + k * E);
+    }
+}
+
+template <typename T, int V>
 __global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Workspace ws, int slices) {
     const int64_t E = p.batch * p.dim * p.seqlen;
-    const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= E) return;
-    const int64_t d = (e / p.seqlen) % p.dim;
-    const float u = to_f32<T>(ld_global(static_cast<const T *>(p.u) + e));
-    const float g = to_f32<T>(ld_global(static_cast<const T *>(p.dout) + e));
+    const int64_t e0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * V;
+    if (e0 >= E) return;
+    const int64_t d = (e0 / p.seqlen) % p.dim;
     const float dskip = p.D ? p.D[d] : 0.0f;
-    float du = ld_global(ws.dup + e), dd = ld_global(ws.ddp + e);
-    for (int k = 1; k < slices; k++) {
-        du += ld_global(ws.dup + k * E + e);
-        dd += ld_global(ws.ddp + k * E + e);
+    float du[V], dd[V], dz[V];
+    sum_slices<V>(ws.dup + e0, E, slices, du);
+    sum_slices<V>(ws.ddp + e0, E, slices, dd);
+    if (p.z) sum_slices<V>(ws.dzp + e0, E, slices, dz);
+    auto ldv = [&](const void *src, float (&v)[V]) {
+        if constexpr (V == 4) ld4<T>(static_cast<const T *>(src) + e0, v);
+        else v[0] = to_f32<T>(ld_global(static_cast<const T *>(src) + e0));
+    };
+    auto stv = [&](void *dst, const float (&v)[V]) {
+        if constexpr (V == 4) st4<T>(static_cast<T *>(dst) + e0, v);
+        else st_global(static_cast<T *>(dst) + e0, from_f32<T>(v[0]));
+    };
+    float u[V], g[V], z[V], dy[V];
+    ldv(p.u, u);
+    ldv(p.dout, g);
+    if (p.z) ldv(p.z, z);
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+        dy[i] = g[i];
+        if (p.z) {
+            const float sz = sigmoid_f32(z[i]);
+            dy[i] = g[i] * z[i] * sz;
+            dz[i] += g[i] * (dskip * u[i]) * sz * (1.0f + z[i] * (1.0f - sz));
+        }
+        du[i] += dskip * dy[i];
     }
-    float dy = g;
-    if (p.z) {
-        const float z = to_f32<T>(ld_global(static_cast<const T *>(p.z) + e));
-        const float sz = sigmoid_f32(z);
-        dy = g * z * sz;
-        float dz = ld_global(ws.dzp + e);
-        for (int k = 1; k < slices; k++) dz += ld_global(ws.dzp + k * E + e);
-        dz += g * (dskip * u) * sz * (1.0f + z * (1.0f - sz));
-        st_global(static_cast<T *>(p.dz) + e, from_f32<T>(dz));
-    }
-    st_global(static_cast<T *>(p.du) + e, from_f32<T>(du + dskip * dy));
-    st_global(static_cast<T *>(p.ddelta) + e, from_f32<T>(dd));
+    if (p.z) stv(p.dz, dz);
+    stv(p.du, du);
+    stv(p.ddelta, dd);
 }
 
 // Wavefronts per reverse-pass workgroup: scan_waves' choice for 16-byte
@@ -907,8 +933,12 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         if (e != hipSuccess) return e;
         const int64_t E = p.batch * p.dim * p.seqlen;
         if (slices > 1 && E > 0) {
-            hipLaunchKernelGGL((ss_bwd_combine_kernel<T>), dim3(unsigned((E + 255) / 256)),
-                               dim3(256), 0, stream, p, ws, slices);
+            if (p.seqlen % 4 == 0)
+                hipLaunchKernelGGL((ss_bwd_combine_kernel<T, 4>), dim3(unsigned((E / 4 + 255) / 256)),
+                                   dim3(256), 0, stream, p, ws, slices);
+            else
+                hipLaunchKernelGGL((ss_bwd_combine_kernel<T, 1>), dim3(unsigned((E + 255) / 256)),
+                                   dim3(256), 0, stream, p, ws, slices);
             profile_mark(stream);
         }
     }

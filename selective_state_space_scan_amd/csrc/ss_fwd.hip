@@ -292,22 +292,42 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
 }
 
 // Several slices: out = (sum of the slices' partials, ascending, + D u) *
-// silu(z), one element per thread.
-template <typename T>
+// silu(z).  Each thread takes V consecutive elements of one row (V = 4 when
+// seqlen is a multiple of 4, so the partials move as 16-byte vectors).
+template <typename T, int V>
 __global__ __launch_bounds__(256) void ss_fwd_combine_kernel(FwdParams p, int slices) {
     const int64_t E = p.batch * p.dim * p.seqlen;
-    const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= E) return;
-    const int64_t d = (e / p.seqlen) % p.dim;
-    float s = ld_global(p.ypart + e);
-    for (int k = 1; k < slices; k++) s += ld_global(p.ypart + k * E + e);
-    const float u = to_f32<T>(ld_global(static_cast<const T *>(p.u) + e));
-    float y = s + (p.D ? p.D[d] : 0.0f) * u;
-    if (p.z) {
-        const float z = to_f32<T>(ld_global(static_cast<const T *>(p.z) + e));
-        y *= z * sigmoid_f32(z);
+    const int64_t e0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * V;
+    if (e0 >= E) return;
+    const int64_t d = (e0 / p.seqlen) % p.dim;
+    const float dskip = p.D ? p.D[d] : 0.0f;
+    float s[V];
+    if constexpr (V == 4) {
+        float4 a = *reinterpret_cast<const float4 *>(p.ypart + e0);
+        for (int k = 1; k < slices; k++) {
+            const float4 b = *reinterpret_cast<const float4 *>(p.ypart + k * E + e0);
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+    } else {
+        s[0] = ld_global(p.ypart + e0);
+        for (int k = 1; k < slices; k++) s[0] += ld_global(p.ypart + k * E + e0);
     }
-    st_global(static_cast<T *>(p.out) + e, from_f32<T>(y));
+    float u[V], z[V], y[V];
+    if constexpr (V == 4) {
+        ld4<T>(static_cast<const T *>(p.u) + e0, u);
+        if (p.z) ld4<T>(static_cast<const T *>(p.z) + e0, z);
+    } else {
+        u[0] = to_f32<T>(ld_global(static_cast<const T *>(p.u) + e0));
+        if (p.z) z[0] = to_f32<T>(ld_global(static_cast<const T *>(p.z) + e0));
+    }
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+        y[i] = s[i] + dskip * u[i];
+        if (p.z) y[i] *= z[i] * sigmoid_f32(z[i]);
+    }
+    if constexpr (V == 4) st4<T>(static_cast<T *>(p.out) + e0, y);
+    else st_global(static_cast<T *>(p.out) + e0, from_f32<T>(y[0]));
 }
 
 template <typename T, int VEC, int NW, bool PART>
@@ -344,8 +364,12 @@ hipError_t launch_typed(const FwdParams &p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int64_t E = p.batch * p.dim * p.seqlen;
     if (E > 0) {
-        hipLaunchKernelGGL((ss_fwd_combine_kernel<T>), dim3(unsigned((E + 255) / 256)), dim3(256),
-                           0, stream, p, slices);
+        if (p.seqlen % 4 == 0)
+            hipLaunchKernelGGL((ss_fwd_combine_kernel<T, 4>), dim3(unsigned((E / 4 + 255) / 256)),
+                               dim3(256), 0, stream, p, slices);
+        else
+            hipLaunchKernelGGL((ss_fwd_combine_kernel<T, 1>), dim3(unsigned((E + 255) / 256)),
+                               dim3(256), 0, stream, p, slices);
         profile_mark(stream);
     }
     return hipGetLastError();

@@ -41,6 +41,38 @@ __device__ __forceinline__ void st_global(T *p, T v) {
     *(__attribute__((address_space(1))) T *)(p) = v;
 }
 
+// Four consecutive elements of T (16 bytes of f32, 8 of bf16) widened to
+// f32, and the reverse; the address must be aligned to the access size.
+template <typename T>
+__device__ __forceinline__ void ld4(const T *p, float (&v)[4]) {
+    if constexpr (sizeof(T) == 4) {
+        const u32x4 r = ld_global16(p);
+        v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y);
+        v[2] = __uint_as_float(r.z); v[3] = __uint_as_float(r.w);
+    } else {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 r = *(const __attribute__((address_space(1))) u32x2 *)(p);
+        const uint32_t r0 = r.x, r1 = r.y;
+        v[0] = __uint_as_float(r0 << 16); v[1] = __uint_as_float(r0 & 0xffff0000u);
+        v[2] = __uint_as_float(r1 << 16); v[3] = __uint_as_float(r1 & 0xffff0000u);
+    }
+}
+template <typename T>
+__device__ __forceinline__ void st4(T *p, const float (&v)[4]) {
+    if constexpr (sizeof(T) == 4) {
+        u32x4 r;
+        r.x = __float_as_uint(v[0]); r.y = __float_as_uint(v[1]);
+        r.z = __float_as_uint(v[2]); r.w = __float_as_uint(v[3]);
+        st_global16(p, r);
+    } else {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 r;
+        r.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+        r.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+        *(__attribute__((address_space(1))) u32x2 *)(p) = r;
+    }
+}
+
 // Address = base + a 32-bit byte offset.  With a base that is uniform
 // across the wavefront (scalar registers), the compiler uses the scalar-base
 // form of the global instructions and needs no 64-bit vector address math.
