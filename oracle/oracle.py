@@ -11,7 +11,8 @@ back as float64 numpy arrays.  The arithmetic itself lives entirely in
 than one thread, splits independent rows (forward, state update) or batch
 entries (backward) across threads and folds the per-thread parameter
 gradients in ascending batch order.  The causal convolution routines
-(``conv_fwd``, ``conv_bwd``, ``conv_update``) follow the same pattern.
+(``conv_fwd``, ``conv_bwd``, ``conv_update``) and the Mamba-2 SSD forward
+(``ssd_fwd``) follow the same pattern.
 """
 from __future__ import annotations
 
@@ -68,6 +69,8 @@ def _load():
             lib.sso_conv_bwd.restype = None
             lib.sso_conv_update.argtypes = [i64] * 3 + [dp] * 4 + [c_int] + [dp]
             lib.sso_conv_update.restype = None
+            lib.sso_ssd_fwd.argtypes = [i64] * 6 + [dp] * 7 + [c_int] + [dp] * 3 + [i64, i64]
+            lib.sso_ssd_fwd.restype = c_int
             _lib = lib
     return _lib
 
@@ -272,3 +275,33 @@ def conv_update(state, x, weight, bias=None, silu=True):
     lib.sso_conv_update(nb, nd, nk, _p(st), _p(x), _p(weight), _p(bias), int(bool(silu)),
                         _p(out))
     return st, out
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, h0=None, threads: int = 1):
+    """Mamba-2 SSD forward (scalar A per head).  Returns ``(y, last_state)``.
+
+    x: (batch, L, nheads, headdim); dt: (batch, L, nheads); A, D, dt_bias:
+    (nheads,); B, C: (batch, L, ngroups, dstate); h0: (batch, nheads,
+    headdim, dstate) or None.
+    """
+    lib = _load()
+    x, dt, A, B, C = map(_f64, (x, dt, A, B, C))
+    D, dt_bias, h0 = map(_f64, (D, dt_bias, h0))
+    nb, nl, nh, npd = x.shape
+    ng, ns = B.shape[2], B.shape[3]
+    y = np.zeros((nb, nl, nh, npd))
+    last = np.zeros((nb, nh, npd, ns))
+    args = (nb, nl, nh, npd, ng, ns, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(dt_bias),
+            int(bool(softplus)), _p(h0), _p(y), _p(last))
+
+    def run(rg):
+        if lib.sso_ssd_fwd(*args, rg[0], rg[1]) != 0:
+            raise MemoryError("oracle SSD could not allocate its state")
+
+    pieces = _split(nb, threads)
+    if len(pieces) == 1:
+        run(pieces[0])
+    else:
+        with ThreadPoolExecutor(len(pieces)) as ex:
+            list(ex.map(run, pieces))
+    return y, last

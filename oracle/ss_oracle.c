@@ -364,3 +364,61 @@ void sso_conv_update(int64_t nb, int64_t nd, int64_t nk, double *state, const do
             state[r * (nk - 1) + j] = (j + 1 < nk - 1) ? state[r * (nk - 1) + j + 1] : x[r];
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Mamba-2 SSD: the selective scan with a scalar A per head.
+ *
+ * The state-spaces/mamba README ("Mamba-2", "SSD") names the Mamba-2 block
+ * and its inner SSD module with d_state typically 64 or 128; the pages print
+ * no formula.  The reading: per batch b and head h, a state H of headdim x
+ * d_state entries,
+ *
+ *   dt_t   = softplus(dt_raw[b,t,h] + dt_bias[h])      (bias, softplus optional)
+ *   H_t    = exp(dt_t A[h]) H_{t-1} + dt_t x_t B_t^T     (x_t: headdim, B_t: d_state)
+ *   y_t    = H_t C_t + D[h] x_t
+ *
+ * with B, C shared by the heads of a group (group = h / (nheads / ngroups))
+ * and H_{-1} = h0 (zero without one).  Layouts (time-major, as the mamba-rs
+ * scratch buffers of the Mamba-3 block lay out their per-step tensors):
+ * x, y (nb, nl, nh, np); dt (nb, nl, nh); B, C (nb, nl, ng, ns);
+ * A, D, dt_bias (nh); h0, last (nb, nh, np, ns).
+ * (b, h) pairs with b0 <= b < b1 are computed.
+ * ------------------------------------------------------------------------ */
+int sso_ssd_fwd(int64_t nb, int64_t nl, int64_t nh, int64_t np, int64_t ng, int64_t ns,
+                const double *x, const double *dtr, const double *A, const double *B,
+                const double *C, const double *D, const double *dt_bias, int softplus,
+                const double *h0, double *y, double *last, int64_t b0, int64_t b1)
+{
+    (void)nb;
+    double *H = (double *)malloc(sizeof(double) * (size_t)(np * ns > 0 ? np * ns : 1));
+    if (!H) return 1;
+    for (int64_t b = b0; b < b1; b++) {
+        for (int64_t h = 0; h < nh; h++) {
+            const int64_t g = h / (nh / ng);
+            for (int64_t i = 0; i < np * ns; i++)
+                H[i] = h0 ? h0[(b * nh + h) * np * ns + i] : 0.0;
+            for (int64_t t = 0; t < nl; t++) {
+                double dt = dtr[(b * nl + t) * nh + h] + (dt_bias ? dt_bias[h] : 0.0);
+                if (softplus) dt = sso_softplus(dt);
+                const double decay = exp(dt * A[h]);
+                const double *xt = x + ((b * nl + t) * nh + h) * np;
+                const double *bt = B + ((b * nl + t) * ng + g) * ns;
+                const double *ct = C + ((b * nl + t) * ng + g) * ns;
+                double *yt = y + ((b * nl + t) * nh + h) * np;
+                for (int64_t p = 0; p < np; p++) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < ns; n++) {
+                        double *hv = &H[p * ns + n];
+                        *hv = decay * *hv + dt * xt[p] * bt[n];
+                        acc += ct[n] * *hv;
+                    }
+                    yt[p] = acc + (D ? D[h] * xt[p] : 0.0);
+                }
+            }
+            if (last)
+                for (int64_t i = 0; i < np * ns; i++) last[(b * nh + h) * np * ns + i] = H[i];
+        }
+    }
+    free(H);
+    return 0;
+}

@@ -54,6 +54,14 @@ MUTATIONS = {
                              "ds0[r * (nk - 1) + (tt + nk - 1)] += 0.0 * g;"),
     "conv_update_shift_wrong": ("state[r * (nk - 1) + j] = (j + 1 < nk - 1) ? state[r * (nk - 1) + j + 1] : x[r];",
                                 "state[r * (nk - 1) + j] = (j > 0) ? state[r * (nk - 1) + j - 1] : x[r];"),
+    "ssd_decay_sign_flipped": ("const double decay = exp(dt * A[h]);",
+                               "const double decay = exp(-dt * A[h]);"),
+    "ssd_input_without_dt": ("*hv = decay * *hv + dt * xt[p] * bt[n];",
+                             "*hv = decay * *hv + xt[p] * bt[n];"),
+    "ssd_output_uses_B": ("acc += ct[n] * *hv;", "acc += bt[n] * *hv;"),
+    "ssd_group_map_wrong": ("const int64_t g = h / (nh / ng);", "const int64_t g = h % ng;"),
+    "ssd_skip_dropped": ("yt[p] = acc + (D ? D[h] * xt[p] : 0.0);", "yt[p] = acc;"),
+    "ssd_h0_ignored": ("H[i] = h0 ? h0[(b * nh + h) * np * ns + i] : 0.0;", "H[i] = 0.0;"),
 }
 
 
@@ -74,6 +82,7 @@ def test_pins_catch_planted_mistake(name):
             [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
              os.path.join(ROOT, "tests", "test_oracle_pins.py"),
              os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py"),
-             os.path.join(ROOT, "tests", "test_oracle_conv_pins.py")],
+             os.path.join(ROOT, "tests", "test_oracle_conv_pins.py"),
+             os.path.join(ROOT, "tests", "test_oracle_ssd_pins.py")],
             cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
         assert res.returncode != 0, f"pins did not catch mutation {name}:\n{res.stdout[-2000:]}"
