@@ -12,8 +12,8 @@ with each library kernel also timed on its own (HIP events recorded between
 the kernels on the stream they run on), the dominant kernel set against the
 MI355X roofline, and the plain f64 oracle timed on a bounded sample of the
 same workload on the host cores.  The forward-only and decode workloads,
-and the causal convolution (width 4) that feeds the scan, are timed as well
-and reported under "detail".
+the d_state 64 step, the causal convolution (width 4) that feeds the scan
+and the Mamba-2 SSD forward are timed as well and reported under "detail".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -213,6 +213,39 @@ def wide_state_detail(hip, lib, to_dev, dev):
     return {"mamba130m_step_f32_8x1536x2048_dstate64": out}
 
 
+def ssd_detail(hip, lib, to_dev, dev):
+    """The Mamba-2 SSD forward at the 130M layer shape (batch 8, L 2048,
+    24 heads of 64, d_state 128, one group, bf16), inputs rotated over two
+    copies."""
+    import torch
+
+    from selective_state_space_scan_amd import binding
+    from selective_state_space_scan_amd import inputs as ssin
+    w = ssin.SSD_WORKLOADS["mamba2_130m_ssd_bf16_8x2048x24x64_n128"]
+    a = ssin.make_ssd(w)
+    sets = [{k: to_dev(v) for k, v in a.items()} for _ in range(2)]
+    outs = [torch.empty_like(c["x"]) for c in sets]
+    calls = [lambda c=c, o=o: binding.ss_ssd_fwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"],
+                                                 c["dt_bias"], True, out=o)
+             for c, o in zip(sets, outs)]
+    (ms,) = timed_calls(hip, lib, calls, 2, 20)
+    E = w.elements
+    by = (2 * E * 2 + w.batch * w.seqlen * w.nheads * 2
+          + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * 2 + 3 * w.nheads * 4)
+    # the chunked form's products per (batch, head, 64-step chunk): C B^T and
+    # W x over the lower triangle, C H^T and the state update in full
+    Q, N, P = 64, w.dstate, w.headdim
+    fl = (Q * Q * N + Q * Q * P + 4 * Q * N * P) * w.batch * w.nheads * (w.seqlen // Q)
+    del sets, outs
+    return {w.name: {"kernel_ms": round(ms, 5), "elements_per_s": E / (ms * 1e-3),
+                     "algorithmic_bytes": by,
+                     "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac_of_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "chunk_form_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2),
+                     "bf16_dense_peak_TFLOPs": 2500.0,
+                     "input_sets_rotated": 2}}
+
+
 def conv_detail(hip, lib, to_dev, dev):
     """The causal convolution (width 4) in front of the scan: forward and
     backward at the Mamba-130m layer shape in bf16 and f32, and the decode
@@ -277,6 +310,8 @@ def main():
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--conv-only", action="store_true",
                     help="time only the causal convolution kernels (prints their detail)")
+    ap.add_argument("--ssd-only", action="store_true",
+                    help="time only the Mamba-2 SSD kernel (prints its detail)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the selective scan's "
@@ -301,6 +336,9 @@ def main():
 
     if args.conv_only:
         print(json.dumps({"detail": conv_detail(hip, lib, to_dev, dev)}), flush=True)
+        return
+    if args.ssd_only:
+        print(json.dumps({"detail": ssd_detail(hip, lib, to_dev, dev)}), flush=True)
         return
 
     # ---------------- the step: fwd + bwd at 8 x 1536 x 2048, f32 ----------------
@@ -503,6 +541,7 @@ def main():
 
         detail.update(wide_state_detail(hip, lib, to_dev, dev))
         detail.update(conv_detail(hip, lib, to_dev, dev))
+        detail.update(ssd_detail(hip, lib, to_dev, dev))
         result["detail"] = detail
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 6
+#define SS_ABI_VERSION 7
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -224,9 +224,45 @@ ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dty
                            void *out, void *stream);
 
 /*
+ * Mamba-2 SSD forward: the selective scan with a scalar A per head (the SSD
+ * module the state-spaces/mamba README names under "Mamba-2"; d_state
+ * typically 64 or 128).  The pages print no formula; the reading is, per
+ * batch b and head h with a headdim x dstate state H,
+ *
+ *   dt_t = softplus(dt[b,t,h] + dt_bias[h])    (bias, softplus optional)
+ *   H_t  = exp(dt_t A[h]) H_{t-1} + dt_t x_t B_t^T
+ *   y_t  = H_t C_t + D[h] x_t
+ *
+ * with B and C shared by a group of nheads / ngroups consecutive heads and
+ * H_{-1} = h0 (zero when NULL).  Computed in chunks of 64 steps on bf16
+ * matrix cores with f32 accumulation.  The chunked form needs decays:
+ * dt_t A[h] <= 0 (A negative, and dt non-negative, which softplus ensures);
+ * a growing state overflows.
+ *
+ * Layouts (row-major, contiguous; time-major like the mamba-rs Mamba-3
+ * scratch buffers):
+ *   x, out          : (batch, seqlen, nheads, headdim)   bf16
+ *   dt              : (batch, seqlen, nheads)            bf16 (raw, before bias/softplus)
+ *   B, C            : (batch, seqlen, ngroups, dstate)   bf16
+ *   A, D, dt_bias   : (nheads)                           float
+ *   h0, last_state  : (batch, nheads, headdim, dstate)   float
+ * io_dtype must be SS_BF16 (SS_EUNSUPPORTED otherwise); headdim 16, 32, 48
+ * or 64; dstate 32, 64, 96 or 128; ngroups divides nheads; seqlen <= 2^26.
+ * D, dt_bias, h0, last_state may be NULL; last_state must not overlap h0.
+ * Pointers 16-byte aligned, except dt (2-byte aligned suffices).
+ * Each (batch, head) is computed by one workgroup in a fixed order, so the
+ * results are bit-reproducible and do not depend on the batch size.
+ */
+ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                     int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const float *dt_bias, int dt_softplus, const float *h0, void *out,
+                     float *last_state, void *stream);
+
+/*
  * Profiling aid for callers that time the library's kernels one by one
  * (not needed for normal use).  When `events` is non-NULL, every later
- * ss_fwd / ss_bwd / ss_state_update / ss_conv1d_* call on this thread records the next
+ * ss_fwd / ss_bwd / ss_state_update / ss_conv1d_* / ss_ssd_fwd call on this thread records the next
  * unused entry of `events` (each a hipEvent_t created by the caller) on its
  * stream before its first kernel and after each kernel it launches, until
  * `count` entries are used.  ss_profile_events(NULL, 0) switches it off.

@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 6
+ABI_VERSION = 7
 _lock = threading.Lock()
 _lib = None
 
@@ -70,6 +70,8 @@ def load() -> ctypes.CDLL:
             lib.ss_state_update.restype = c_int
             lib.ss_state_update.argtypes = ([i64] * 3 + [c_int] + [vp] * 9 + [c_int]
                                             + [vp] * 2)
+            lib.ss_ssd_fwd.restype = c_int
+            lib.ss_ssd_fwd.argtypes = [i64] * 6 + [c_int] + [vp] * 7 + [c_int] + [vp] * 4
             lib.ss_conv1d_fwd.restype = c_int
             lib.ss_conv1d_fwd.argtypes = [i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 4
             lib.ss_conv1d_bwd.restype = c_int
@@ -297,3 +299,28 @@ def ss_conv1d_update(state, x, weight, bias=None, silu=True, out=None):
                                 _f32(weight, "weight"), _f32(bias, "bias"), int(bool(silu)),
                                 _ptr(out), _stream()))
     return out
+
+
+def ss_ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, h0=None, out=None,
+               last_state=None, return_last_state=False):
+    """Mamba-2 SSD forward; returns ``out`` or ``(out, last_state)``.
+
+    x: (batch, L, nheads, headdim), dt: (batch, L, nheads), B, C: (batch, L,
+    ngroups, dstate), all bfloat16; A, D, dt_bias: (nheads,) float32;
+    h0 / last_state: (batch, nheads, headdim, dstate) float32.
+    """
+    lib = load()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    io = _io_dtype(x)
+    _same_io(io, dt, B, C)
+    if out is None:
+        out = torch.empty_like(x)
+    if return_last_state and last_state is None:
+        last_state = torch.empty(batch, nheads, headdim, dstate, dtype=torch.float32,
+                                 device=x.device)
+    _check(lib.ss_ssd_fwd(batch, seqlen, nheads, headdim, ngroups, dstate, io, _ptr(x), _ptr(dt),
+                          _f32(A, "A"), _ptr(B), _ptr(C), _f32(D, "D"), _f32(dt_bias, "dt_bias"),
+                          int(bool(dt_softplus)), _f32(h0, "h0"), _ptr(out),
+                          _f32(last_state, "last_state"), _stream()))
+    return (out, last_state) if (return_last_state or last_state is not None) else out

@@ -370,6 +370,58 @@ ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t widt
         "ss_conv1d_bwd launch");
 }
 
+ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                     int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const float *dt_bias, int dt_softplus, const float *h0, void *out,
+                     float *last_state, void *stream) {
+    if (batch < 0) return fail(SS_EINVAL, "batch must be >= 0 (got %lld)", (long long)batch);
+    if (seqlen < 0) return fail(SS_EINVAL, "seqlen must be >= 0 (got %lld)", (long long)seqlen);
+    if (nheads < 0) return fail(SS_EINVAL, "nheads must be >= 0 (got %lld)", (long long)nheads);
+    if (ngroups < 1 || (nheads > 0 && nheads % ngroups != 0))
+        return fail(SS_EINVAL, "ngroups (%lld) must be >= 1 and divide nheads (%lld)",
+                    (long long)ngroups, (long long)nheads);
+    if (io_dtype != SS_F32 && io_dtype != SS_BF16)
+        return fail(SS_EINVAL, "io_dtype must be SS_F32 (0) or SS_BF16 (1) (got %d)", io_dtype);
+    if (io_dtype != SS_BF16)
+        return fail(SS_EUNSUPPORTED, "ss_ssd_fwd runs on bf16 matrix cores: io_dtype must be SS_BF16");
+    if (headdim != 16 && headdim != 32 && headdim != 48 && headdim != 64)
+        return fail(SS_EUNSUPPORTED, "headdim %lld is not supported (16, 32, 48 or 64)",
+                    (long long)headdim);
+    if (dstate != 32 && dstate != 64 && dstate != 96 && dstate != 128)
+        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (32, 64, 96 or 128)",
+                    (long long)dstate);
+    if (seqlen > kMaxSeq)
+        return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
+                    (long long)kMaxSeq);
+    if (batch * nheads > (int64_t(1) << 31) - 1)
+        return fail(SS_EUNSUPPORTED, "batch * nheads too large");
+    Check c;
+    if (batch > 0 && nheads > 0 && seqlen > 0) {
+        c.need(x, "x"); c.need(B, "B"); c.need(C, "C"); c.need(out, "out");
+        if (!dt) return fail(SS_EINVAL, "dt must not be NULL");
+    } else {
+        c.opt(x, "x"); c.opt(B, "B"); c.opt(C, "C"); c.opt(out, "out");
+    }
+    // dt is read one 2-byte element at a time
+    if (dt && (reinterpret_cast<uintptr_t>(dt) & 1u))
+        return fail(SS_EINVAL, "dt must be 2-byte aligned");
+    if (nheads > 0) c.need(A, "A"); else c.opt(A, "A");
+    c.opt(D, "D"); c.opt(dt_bias, "dt_bias"); c.opt(h0, "h0"); c.opt(last_state, "last_state");
+    if (c.st != SS_OK) return c.st;
+    const size_t st = size_t(batch) * size_t(nheads) * size_t(headdim) * size_t(dstate) * 4;
+    if (overlaps(h0, st, last_state, st))
+        return fail(SS_EINVAL, "last_state must not overlap h0");
+    ssk::SsdParams p{};
+    p.batch = batch; p.seqlen = seqlen; p.nheads = nheads; p.ngroups = ngroups;
+    p.headdim = int(headdim); p.dstate = int(dstate);
+    p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.dt_bias = dt_bias;
+    p.softplus = dt_softplus != 0; p.h0 = h0; p.out = out; p.last_state = last_state;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
+    return device_status(ssk::launch_ssd_fwd(p, static_cast<hipStream_t>(stream)),
+                         "ss_ssd_fwd launch");
+}
+
 ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dtype, float *state,
                            const void *x, const float *weight, const float *bias, int silu,
                            void *out, void *stream) {

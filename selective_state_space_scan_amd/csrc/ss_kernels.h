@@ -151,6 +151,24 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstat
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);
 hipError_t launch_state_update(const DecodeParams &p, bool bf16, hipStream_t stream);
 
+// Mamba-2 SSD forward: scalar A per head, state headdim x dstate per head.
+// x, out: (batch, L, nheads, headdim) bf16; dt: (batch, L, nheads) bf16;
+// B, C: (batch, L, ngroups, dstate) bf16; A, D, dt_bias: (nheads) f32;
+// h0, last_state: (batch, nheads, headdim, dstate) f32.
+struct SsdParams {
+    int64_t batch, seqlen, nheads, ngroups;
+    int headdim, dstate;
+    const void *x, *dt;
+    const float *A;
+    const void *B, *C;
+    const float *D, *dt_bias;
+    int softplus;
+    const float *h0;
+    void *out;
+    float *last_state;
+};
+hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream);
+
 // Segments (one wavefront each) a row of the convolution is cut into.
 int64_t conv_segments(int64_t seqlen);
 hipError_t launch_conv_fwd(const ConvFwdParams &p, bool bf16, hipStream_t stream);

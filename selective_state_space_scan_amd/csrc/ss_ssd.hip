@@ -1,0 +1,348 @@
+// ss_ssd.hip -- Mamba-2 SSD forward (scalar A per head) on gfx950 matrix cores.
+//
+// The state-spaces/mamba README ("Mamba-2", "SSD") names the SSD module of
+// the Mamba-2 block (d_state typically 64 or 128).  Per batch b and head h,
+// with a headdim x dstate state H:
+//   dt_t = softplus(dt_raw[b,t,h] + dt_bias[h]),  a_t = dt_t A[h]
+//   H_t  = exp(a_t) H_{t-1} + dt_t x_t B_t^T,      y_t = H_t C_t + D[h] x_t
+// B and C belong to the head's group (contiguous groups of heads).
+//
+// Chunked form.  Time runs in chunks of kQ = 64 steps.  With cum_t the sum
+// of a over the chunk up to and including t (so exp(cum_t - cum_s) is the
+// decay from step s to t), a chunk's output and end state are
+//   y_t   = exp(cum_t) C_t . H_in  +  sum_{s<=t} exp(cum_t - cum_s) (C_t . B_s) dt_s x_s
+//   H_out = exp(cum_last) H_in    +  sum_s exp(cum_last - cum_s) dt_s x_s B_s^T
+// which is the recurrence regrouped (the quadratic "dual" form inside a
+// chunk, the recurrence between chunks).  All four products are dense
+// contractions and run on bf16 MFMAs with f32 accumulation:
+//   G^T = B C^T (over d_state; 16x16x32), Y += W X (over the chunk; 16x16x16),
+//   Y += C H^T (over d_state; 16x16x16), H^T += B^T (w X) (over the chunk; 16x16x32).
+//
+// Work mapping.  One workgroup per (batch, head); wavefront q owns the 16
+// columns 16q .. 16q + 15 of the head (headdim / 16 wavefronts).  The state
+// lives in MFMA accumulators as H^T tiles (16 states x 16 columns); their
+// registers are, after rounding to bf16, exactly the B operand of the
+// C H^T product.  G^T is computed (rather than G) because its accumulator
+// registers, scaled by exp(cum_t - cum_s) dt_s, are exactly the A operand of
+// the W X product -- neither needs a trip through LDS.  Every wavefront
+// computes the chunk's G^T itself (it is the same for all columns).
+// A chunk's B, C (row-major, d_state contiguous), B^T and x^T (time
+// contiguous) and dt go through LDS; the next chunk is loaded into
+// registers while the current one is computed.
+//
+// Rounding: B, C, x arrive as bf16.  The three operands made on chip -- W,
+// the state H and w x -- are each split into a bf16 high part and a bf16
+// low part (v = hi + lo to about 2^-16 relative) and multiplied as two
+// products, so they add no error beyond f32 accumulation; a single bf16
+// rounding of them would cost up to 2% of the output at d_state 128, as
+// each output element sums 128 state terms.  Sums and the carried state
+// are f32.
+#include "ss_device.h"
+#include "ss_kernels.h"
+#include "ss_tiles.h"
+
+namespace ssk {
+namespace {
+
+constexpr int kQ = 64;  // chunk length
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int N, int P>
+struct SsdSmem {
+    static constexpr int kPB = N + 8;   // row pitch of B and C (bf16), 16-byte multiple
+    static constexpr int kPT = kQ + 8;  // row pitch of B^T and x^T (bf16)
+    static constexpr uint32_t kBs = 0;
+    static constexpr uint32_t kCs = kBs + kQ * kPB * 2;
+    static constexpr uint32_t kBT = kCs + kQ * kPB * 2;
+    static constexpr uint32_t kXT = kBT + N * kPT * 2;
+    static constexpr uint32_t kCum = kXT + P * kPT * 2;  // f32 [kQ]
+    static constexpr uint32_t kDt = kCum + kQ * 4;       // f32 [kQ]
+    static constexpr uint32_t kW = kDt + kQ * 4;         // f32 [kQ]: exp(cum_last - cum_s) dt_s
+    static constexpr uint32_t kSize = kW + kQ * 4;
+};
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8_t a, bf16x8_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ short bfs(float v) { return static_cast<short>(f32_to_bf16(v)); }
+
+// v = hi + lo with hi = bfs(v) and lo = lo_bf(v, hi): the part of v that
+// one bf16 misses, in a second bf16
+__device__ __forceinline__ short lo_bf(float v, short hi) {
+    return bfs(v - bf16_to_f32(static_cast<bf16_t>(hi)));
+}
+
+// N: dstate (multiple of 32, <= 128); P: headdim (multiple of 16, <= 64).
+template <int N, int P>
+__global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
+    constexpr int kWaves = P / 16, kThr = 64 * kWaves;
+    constexpr int kNT = N / 16;                      // state tiles of 16
+    constexpr int kVB = kQ * N / 8;                  // 16-byte vectors of a B (or C) chunk
+    constexpr int kBV = (kVB + kThr - 1) / kThr;     // per thread
+    constexpr int kVX = kQ * P / 8;                  // 16-byte vectors of an x chunk
+    constexpr int kXV = kVX / kThr;                  // per thread (2)
+    static_assert(kVX % kThr == 0, "x chunk splits evenly");
+    using SM = SsdSmem<N, P>;
+    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
+    bf16_t *Bs = reinterpret_cast<bf16_t *>(smem + SM::kBs);
+    bf16_t *Cs = reinterpret_cast<bf16_t *>(smem + SM::kCs);
+    bf16_t *BT = reinterpret_cast<bf16_t *>(smem + SM::kBT);
+    bf16_t *XT = reinterpret_cast<bf16_t *>(smem + SM::kXT);
+    float *cum = reinterpret_cast<float *>(smem + SM::kCum);
+    float *dts = reinterpret_cast<float *>(smem + SM::kDt);
+    float *wts = reinterpret_cast<float *>(smem + SM::kW);
+
+    const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t H = p.nheads, G = p.ngroups, L = p.seqlen;
+    const int64_t b = blockIdx.x / H, h = blockIdx.x - b * H;
+    const int64_t g = h / (H / G);
+    const float a2 = p.A[h] * kLog2e;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float dskip = p.D ? p.D[h] : 0.0f;
+    const int64_t xrow = H * P, brow = G * N;   // element strides between time steps
+    const bf16_t *xg = static_cast<const bf16_t *>(p.x) + (b * L * H + h) * P;
+    const bf16_t *dtg = static_cast<const bf16_t *>(p.dt) + b * L * H + h;
+    const bf16_t *Bg = static_cast<const bf16_t *>(p.B) + (b * L * G + g) * N;
+    const bf16_t *Cg = static_cast<const bf16_t *>(p.C) + (b * L * G + g) * N;
+    bf16_t *yg = static_cast<bf16_t *>(p.out) + (b * L * H + h) * P;
+
+    // state tiles: lane holds H^T[n = 16 m + 4 lg + r][col = 16 q + li]
+    const int col = 16 * q + li;
+    const float *h0 = p.h0 ? p.h0 + ((b * H + h) * P + col) * N : nullptr;
+    f32x4 Hs[kNT];
+#pragma unroll
+    for (int m = 0; m < kNT; m++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) Hs[m][r] = h0 ? h0[16 * m + 4 * lg + r] : 0.0f;
+
+    // the next chunk, in registers
+    u32x4 rb[kBV], rc[kBV], rx[kXV];
+    uint32_t rdt = 0;
+    auto load_chunk = [&](int64_t c0) {
+#pragma unroll
+        for (int k = 0; k < kBV; k++) {
+            const int v = tid + k * kThr;
+            if (v < kVB) {
+                const int s = v / (N / 8), c8 = v % (N / 8);
+                const int64_t t = c0 + s < L ? c0 + s : L - 1;
+                rb[k] = ld_global16(Bg + t * brow + 8 * c8);
+                rc[k] = ld_global16(Cg + t * brow + 8 * c8);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kXV; k++) {
+            const int v = tid + k * kThr;
+            const int s = v / (P / 8), c8 = v % (P / 8);
+            const int64_t t = c0 + s < L ? c0 + s : L - 1;
+            rx[k] = ld_global16(xg + t * xrow + 8 * c8);
+        }
+        if (tid < kQ) {
+            const int64_t t = c0 + tid < L ? c0 + tid : L - 1;
+            rdt = ld_global(dtg + t * H);
+        }
+    };
+    // registers -> LDS; steps past the end become zeros (no input, no decay)
+    auto stash_chunk = [&](int64_t c0) {
+#pragma unroll
+        for (int k = 0; k < kBV; k++) {
+            const int v = tid + k * kThr;
+            if (v < kVB) {
+                const int s = v / (N / 8), c8 = v % (N / 8);
+                const bool live = c0 + s < L;
+                u32x4 vb = rb[k], vc = rc[k];
+                if (!live) vb = vc = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(Bs + s * SM::kPB + 8 * c8) = vb;
+                *reinterpret_cast<u32x4 *>(Cs + s * SM::kPB + 8 * c8) = vc;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    BT[(8 * c8 + 2 * e) * SM::kPT + s] = bf16_t(vb[e] & 0xffffu);
+                    BT[(8 * c8 + 2 * e + 1) * SM::kPT + s] = bf16_t(vb[e] >> 16);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kXV; k++) {
+            const int v = tid + k * kThr;
+            const int s = v / (P / 8), c8 = v % (P / 8);
+            u32x4 vx = rx[k];
+            if (!(c0 + s < L)) vx = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                XT[(8 * c8 + 2 * e) * SM::kPT + s] = bf16_t(vx[e] & 0xffffu);
+                XT[(8 * c8 + 2 * e + 1) * SM::kPT + s] = bf16_t(vx[e] >> 16);
+            }
+        }
+        if (tid < kQ) {   // wavefront 0: dt, the running sum of dt A, and w
+            float dv = 0.0f;
+            if (c0 + tid < L) {
+                dv = bf_lo(rdt & 0xffffu) + bias;
+                if (p.softplus) dv = softplus_f32(dv);
+            }
+            float a = dv * a2;   // base-2 exponent units
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(a, off, 64);
+                if (lane >= off) a += o;
+            }
+            const float total = __shfl(a, 63, 64);
+            cum[tid] = a;
+            dts[tid] = dv;
+            wts[tid] = exp2_hw(total - a) * dv;
+        }
+    };
+
+    const int64_t nch = (L + kQ - 1) / kQ;
+    if (nch > 0) {
+        load_chunk(0);
+        stash_chunk(0);
+    }
+    __syncthreads();
+    for (int64_t c = 0; c < nch; c++) {
+        const int64_t c0 = c * kQ;
+        if (c + 1 < nch) load_chunk(c0 + kQ);
+
+        // y = exp(cum_t) C H_in (+ the chunk's own part below)
+        s16x4 hbh[kNT], hbl[kNT];
+#pragma unroll
+        for (int m = 0; m < kNT; m++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const short hi = bfs(Hs[m][r]);
+                hbh[m][r] = hi;
+                hbl[m][r] = lo_bf(Hs[m][r], hi);
+            }
+        f32x4 Y[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int m = 0; m < kNT; m++) {
+                const s16x4 a = *reinterpret_cast<const s16x4 *>(Cs + (16 * i + li) * SM::kPB + 16 * m + 4 * lg);
+                acc = mfma16(a, hbh[m], acc);
+                acc = mfma16(a, hbl[m], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] *= exp2_hw(cum[16 * i + 4 * lg + r]);
+            Y[i] = acc;
+        }
+        // the chunk's own part: W = G . exp(cum_t - cum_s) dt_s (s <= t), Y += W x
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int t = 16 * i + li;
+            const float ct = cum[t];
+#pragma unroll
+            for (int j = 0; j <= i; j++) {
+                f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};   // G^T[s = 16 j + 4 lg + r][t]
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += 32) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Bs + (16 * j + li) * SM::kPB + k0 + 8 * lg);
+                    const bf16x8_t bb = *reinterpret_cast<const bf16x8_t *>(Cs + t * SM::kPB + k0 + 8 * lg);
+                    gt = mfma32(a, bb, gt);
+                }
+                s16x4 wh, wl;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int s = 16 * j + 4 * lg + r;
+                    const float wv = s <= t ? gt[r] * exp2_hw(ct - cum[s]) * dts[s] : 0.0f;
+                    const short hi = bfs(wv);
+                    wh[r] = hi;
+                    wl[r] = lo_bf(wv, hi);
+                }
+                const s16x4 xb = *reinterpret_cast<const s16x4 *>(XT + col * SM::kPT + 16 * j + 4 * lg);
+                Y[i] = mfma16(wh, xb, Y[i]);
+                Y[i] = mfma16(wl, xb, Y[i]);
+            }
+        }
+        // y + D x, stored: lane holds y[t = 16 i + 4 lg + r][col]
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int t = 16 * i + 4 * lg + r;
+                if (c0 + t < L) {
+                    const float xv = bf16_to_f32(XT[col * SM::kPT + t]);
+                    st_global(yg + (c0 + t) * xrow + col, f32_to_bf16(Y[i][r] + dskip * xv));
+                }
+            }
+        }
+        // H_out = exp(cum_last) H_in + B^T (w x)
+        const float decay = exp2_hw(cum[kQ - 1]);
+        bf16x8_t xsh[2], xsl[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            const u32x4 xr = *reinterpret_cast<const u32x4 *>(XT + col * SM::kPT + 32 * kk + 8 * lg);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int s = 32 * kk + 8 * lg + e;
+                const float v = ((e & 1) ? bf_hi(xr[e >> 1]) : bf_lo(xr[e >> 1])) * wts[s];
+                const __bf16 hi = static_cast<__bf16>(v);
+                xsh[kk][e] = hi;
+                xsl[kk][e] = static_cast<__bf16>(v - static_cast<float>(hi));
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kNT; m++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) Hs[m][r] *= decay;
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(BT + (16 * m + li) * SM::kPT + 32 * kk + 8 * lg);
+                Hs[m] = mfma32(a, xsh[kk], Hs[m]);
+                Hs[m] = mfma32(a, xsl[kk], Hs[m]);
+            }
+        }
+        __syncthreads();
+        if (c + 1 < nch) stash_chunk(c0 + kQ);
+        __syncthreads();
+    }
+
+    if (p.last_state) {
+        float *ls = p.last_state + ((b * H + h) * P + col) * N;
+#pragma unroll
+        for (int m = 0; m < kNT; m++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) ls[16 * m + 4 * lg + r] = Hs[m][r];
+    }
+}
+
+template <int N>
+hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.batch * p.nheads));
+    switch (p.headdim) {
+        case 16: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 16>), grid, dim3(64), 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 32>), grid, dim3(128), 0, stream, p); break;
+        case 48: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 48>), grid, dim3(192), 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 64>), grid, dim3(256), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream) {
+    if (p.batch == 0 || p.nheads == 0) return hipSuccess;
+    hipError_t e;
+    switch (p.dstate) {
+        case 32: e = launch_n<32>(p, stream); break;
+        case 64: e = launch_n<64>(p, stream); break;
+        case 96: e = launch_n<96>(p, stream); break;
+        case 128: e = launch_n<128>(p, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    profile_mark(stream);
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
+}  // namespace ssk

@@ -205,3 +205,70 @@ def make_conv(w: ConvWorkload | str) -> dict:
     else:
         out["state"] = rng.standard_normal((w.batch, w.dim, w.width - 1)).astype(np.float32)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the Mamba-2 SSD scan (scalar A per head)
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class SsdWorkload:
+    """Shape of an SSD forward: x (batch, seqlen, nheads, headdim)."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    has_D: bool = True
+    has_bias: bool = True
+    has_h0: bool = False
+    seed: int = SEED_BASE
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim
+
+
+SSD_WORKLOADS = {
+    w.name: w
+    for w in [
+        # d_model 768 (the 130M size), expand 2 -> 1536 channels = 24 heads of 64,
+        # d_state 128, one group
+        SsdWorkload("mamba2_130m_ssd_bf16_8x2048x24x64_n128", 8, 2048, 24, 64, 1, 128,
+                    seed=SEED_BASE + 30),
+    ]
+}
+
+
+def ssd_custom(batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int, dstate: int,
+               seed: int = 1, **flags) -> SsdWorkload:
+    name = f"ssd_{batch}x{seqlen}x{nheads}x{headdim}_g{ngroups}_n{dstate}_s{seed}"
+    return SsdWorkload(name, batch, seqlen, nheads, headdim, ngroups, dstate, seed=seed, **flags)
+
+
+def make_ssd(w: SsdWorkload | str) -> dict:
+    """Draw the arrays of an SSD workload.
+
+    Draw order: x, dt, B, C, U(A), D, U(dt_bias), h0.  x, B, C, D, h0 ~
+    N(0, 1); dt (raw) ~ 0.5 N(0, 1); A_h = -(1 + 15 U), U ~ Uniform[0, 1],
+    one per head (the decay range of the Mamba-1 A, -1 .. -16);
+    dt_bias = log(expm1(U[1e-3, 1e-1])) as for the Mamba-1 delta.  x, dt, B,
+    C are stored as bf16 bits; A, D, dt_bias, h0 as float32.
+    """
+    if isinstance(w, str):
+        w = SSD_WORKLOADS[w]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    out = {"x": _store(rng.standard_normal((w.batch, w.seqlen, w.nheads, w.headdim)), "bf16")}
+    out["dt"] = _store(0.5 * rng.standard_normal((w.batch, w.seqlen, w.nheads)), "bf16")
+    out["B"] = _store(rng.standard_normal((w.batch, w.seqlen, w.ngroups, w.dstate)), "bf16")
+    out["C"] = _store(rng.standard_normal((w.batch, w.seqlen, w.ngroups, w.dstate)), "bf16")
+    out["A"] = (-(1.0 + 15.0 * rng.uniform(0.0, 1.0, w.nheads))).astype(np.float32)
+    if w.has_D:
+        out["D"] = rng.standard_normal(w.nheads).astype(np.float32)
+    if w.has_bias:
+        U = rng.uniform(1e-3, 1e-1, w.nheads)
+        out["dt_bias"] = np.log(np.expm1(U)).astype(np.float32)
+    if w.has_h0:
+        out["h0"] = rng.standard_normal((w.batch, w.nheads, w.headdim, w.dstate)).astype(np.float32)
+    return out

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 6
+    assert lib.ss_abi_version() == 7
 
 
 def test_ckpt_size(lib):
@@ -249,3 +249,36 @@ def test_fwd_workspace(lib):
     assert _fwd(lib, dstate=64) == EINVAL and "workspace" in _msg(lib)
     assert _fwd(lib, dstate=64, ws=FAKE, ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
     assert _fwd(lib, dstate=64, ws=MISALIGNED, ws_bytes=need) == EINVAL and "aligned" in _msg(lib)
+
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 SSD
+# ---------------------------------------------------------------------------
+def _ssd(lib, batch=2, seqlen=64, nheads=4, headdim=64, ngroups=1, dstate=128, io=1, x=FAKE,
+         dt=FAKE, A=FAKE, B=FAKE, C=FAKE, out=FAKE, h0=None, last=None):
+    return lib.ss_ssd_fwd(batch, seqlen, nheads, headdim, ngroups, dstate, io, x, dt, A, B, C,
+                          None, None, 1, h0, out, last, None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(io=0), EUNSUP, "bf16"), (dict(headdim=24), EUNSUP, "headdim"),
+    (dict(dstate=16), EUNSUP, "dstate"), (dict(dstate=256), EUNSUP, "dstate"),
+    (dict(ngroups=3), EINVAL, "ngroups"), (dict(ngroups=0), EINVAL, "ngroups"),
+    (dict(seqlen=-1), EINVAL, "seqlen"), (dict(x=None), EINVAL, "x"),
+    (dict(B=MISALIGNED), EINVAL, "aligned"), (dict(A=None), EINVAL, "A"),
+])
+def test_ssd_bad_arguments(lib, kw, status, word):
+    assert _ssd(lib, **kw) == status and word in _msg(lib)
+
+
+def test_ssd_dt_needs_only_element_alignment(lib):
+    # validation passes for a dt at a 2-byte offset; the call then has nothing to run
+    assert _ssd(lib, batch=0, dt=FAKE + 2) == 0
+    assert _ssd(lib, dt=FAKE + 1) == EINVAL and "dt" in _msg(lib)
+
+
+def test_ssd_state_overlap_and_empty(lib):
+    assert _ssd(lib, h0=FAKE, last=FAKE + 256) == EINVAL and "overlap" in _msg(lib)
+    assert _ssd(lib, batch=0, x=None, dt=None, B=None, C=None, out=None) == 0
+    assert _ssd(lib, nheads=0, A=None, x=None, dt=None, B=None, C=None, out=None) == 0
