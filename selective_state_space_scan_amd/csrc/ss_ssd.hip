@@ -129,12 +129,16 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     // the next chunk, in registers
     u32x4 rb[kBV], rc[kBV], rx[kXV];
     uint32_t rdt = 0;
+    // Vector v of a chunk is 8 values (16 bytes) of step s = v % kQ, from
+    // value 8 c8 on, c8 = v / kQ: the 64 lanes of a wavefront take 64
+    // consecutive steps, so the transposed LDS writes below go to 64
+    // consecutive 2-byte slots (no bank conflicts).
     auto load_chunk = [&](int64_t c0) {
 #pragma unroll
         for (int k = 0; k < kBV; k++) {
             const int v = tid + k * kThr;
             if (v < kVB) {
-                const int s = v / (N / 8), c8 = v % (N / 8);
+                const int s = v % kQ, c8 = v / kQ;
                 const int64_t t = c0 + s < L ? c0 + s : L - 1;
                 rb[k] = ld_global16(Bg + t * brow + 8 * c8);
                 rc[k] = ld_global16(Cg + t * brow + 8 * c8);
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
         for (int k = 0; k < kXV; k++) {
             const int v = tid + k * kThr;
-            const int s = v / (P / 8), c8 = v % (P / 8);
+            const int s = v % kQ, c8 = v / kQ;
             const int64_t t = c0 + s < L ? c0 + s : L - 1;
             rx[k] = ld_global16(xg + t * xrow + 8 * c8);
         }
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         for (int k = 0; k < kBV; k++) {
             const int v = tid + k * kThr;
             if (v < kVB) {
-                const int s = v / (N / 8), c8 = v % (N / 8);
+                const int s = v % kQ, c8 = v / kQ;
                 const bool live = c0 + s < L;
                 u32x4 vb = rb[k], vc = rc[k];
                 if (!live) vb = vc = u32x4{0u, 0u, 0u, 0u};
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
         for (int k = 0; k < kXV; k++) {
             const int v = tid + k * kThr;
-            const int s = v / (P / 8), c8 = v % (P / 8);
+            const int s = v % kQ, c8 = v / kQ;
             u32x4 vx = rx[k];
             if (!(c0 + s < L)) vx = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -213,24 +217,38 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         if (c + 1 < nch) load_chunk(c0 + kQ);
 
         // y = exp(cum_t) C H_in (+ the chunk's own part below)
-        s16x4 hbh[kNT], hbl[kNT];
+        // The 16x16x32 product over state tiles 2 m2 and 2 m2 + 1 at once:
+        // its k index runs over (tile, 4 lg + r) in the order the state
+        // accumulators hold them, and C is read in that same order.
+        bf16x8_t hbh[kNT / 2], hbl[kNT / 2];
 #pragma unroll
         for (int m = 0; m < kNT; m++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const short hi = bfs(Hs[m][r]);
-                hbh[m][r] = hi;
-                hbl[m][r] = lo_bf(Hs[m][r], hi);
+                const __bf16 hi = static_cast<__bf16>(Hs[m][r]);
+                hbh[m / 2][4 * (m & 1) + r] = hi;
+                hbl[m / 2][4 * (m & 1) + r] = static_cast<__bf16>(Hs[m][r] - static_cast<float>(hi));
             }
         f32x4 Y[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int m = 0; m < kNT; m++) {
-                const s16x4 a = *reinterpret_cast<const s16x4 *>(Cs + (16 * i + li) * SM::kPB + 16 * m + 4 * lg);
-                acc = mfma16(a, hbh[m], acc);
-                acc = mfma16(a, hbl[m], acc);
+            for (int m2 = 0; m2 < kNT / 2; m2++) {
+                const bf16_t *crow = Cs + (16 * i + li) * SM::kPB + 32 * m2 + 4 * lg;
+                const s16x4 a0 = *reinterpret_cast<const s16x4 *>(crow);
+                const s16x4 a1 = *reinterpret_cast<const s16x4 *>(crow + 16);
+                // elements copied out by value before the bit cast: a bit
+                // cast of a vector element would read element 0 under clang 22
+                bf16x8_t a;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const short v0 = a0[e], v1 = a1[e];
+                    a[e] = __builtin_bit_cast(__bf16, v0);
+                    a[4 + e] = __builtin_bit_cast(__bf16, v1);
+                }
+                acc = mfma32(a, hbh[m2], acc);
+                acc = mfma32(a, hbl[m2], acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[r] *= exp2_hw(cum[16 * i + 4 * lg + r]);
