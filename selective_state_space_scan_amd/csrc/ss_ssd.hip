@@ -18,17 +18,19 @@
 //   G^T = B C^T (over d_state; 16x16x32), Y += W X (over the chunk; 16x16x16),
 //   Y += C H^T (over d_state; 16x16x16), H^T += B^T (w X) (over the chunk; 16x16x32).
 //
-// Work mapping.  One workgroup per (batch, head); wavefront q owns the 16
-// columns 16q .. 16q + 15 of the head (headdim / 16 wavefronts).  The state
-// lives in MFMA accumulators as H^T tiles (16 states x 16 columns); their
-// registers are, after rounding to bf16, exactly the B operand of the
-// C H^T product.  G^T is computed (rather than G) because its accumulator
+// Work mapping.  One workgroup per (batch, head); two wavefronts own the 16
+// columns 16q .. 16q + 15 of the head (see the kernel).  The state lives in
+// MFMA accumulators as H^T tiles (16 states x 16 columns); their registers
+// are, after the bf16 split, exactly the B operand of the C H^T product.  G^T is computed (rather than G) because its accumulator
 // registers, scaled by exp(cum_t - cum_s) dt_s, are exactly the A operand of
 // the W X product -- neither needs a trip through LDS.  Every wavefront
 // computes the chunk's G^T itself (it is the same for all columns).
 // A chunk's B, C (row-major, d_state contiguous), B^T and x^T (time
 // contiguous) and dt go through LDS; the next chunk is loaded into
-// registers while the current one is computed.
+// registers while the current one is computed.  The chunk's output is
+// gathered in LDS and written in whole 16-byte pieces of full rows (a
+// head's row is headdim contiguous values): 2-byte stores of a wavefront's
+// 16 columns cost more than the rest of the kernel together.
 //
 // Rounding: B, C, x arrive as bf16.  The three operands made on chip -- W,
 // the state H and w x -- are each split into a bf16 high part and a bf16
@@ -37,6 +39,8 @@
 // rounding of them would cost up to 2% of the output at d_state 128, as
 // each output element sums 128 state terms.  Sums and the carried state
 // are f32.
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_tiles.h"
@@ -61,7 +65,12 @@ struct SsdSmem {
     static constexpr uint32_t kCum = kXT + P * kPT * 2;  // f32 [kQ]
     static constexpr uint32_t kDt = kCum + kQ * 4;       // f32 [kQ]
     static constexpr uint32_t kW = kDt + kQ * 4;         // f32 [kQ]: exp(cum_last - cum_s) dt_s
-    static constexpr uint32_t kSize = kW + kQ * 4;
+    static constexpr int kPY = P + 8;                     // row pitch of the output tile (bf16)
+    static constexpr uint32_t kYs = kW + kQ * 4;          // bf16 [kQ][kPY]: the chunk's output
+    // state exchange, per chunk parity: [column tile][state tile][lane] x 16 bytes
+    static constexpr uint32_t kHx = kYs + kQ * kPY * 2;
+    static constexpr uint32_t kHxPar = (P / 16) * (N / 16) * 64 * 16;
+    static constexpr uint32_t kSize = kHx + 2 * kHxPar;
 };
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -83,15 +92,21 @@ __device__ __forceinline__ short lo_bf(float v, short hi) {
 }
 
 // N: dstate (multiple of 32, <= 128); P: headdim (multiple of 16, <= 64).
+// Two wavefronts per 16-column tile q: wavefront (q, hf) computes the
+// outputs of time tiles {0, 3} (hf = 0) or {1, 2} (hf = 1) -- five of the
+// ten lower-triangle B C^T tiles each -- and carries state tiles
+// hf N / 32 .. (hf + 1) N / 32 - 1.  C H^T needs all state tiles, so after
+// each chunk's update the wavefronts publish their state (as the bf16
+// hi/lo operands) in an LDS exchange buffer, double-buffered by chunk.
 template <int N, int P>
-__global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
-    constexpr int kWaves = P / 16, kThr = 64 * kWaves;
-    constexpr int kNT = N / 16;                      // state tiles of 16
+__global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
+    constexpr int kCT = P / 16;                      // column tiles
+    constexpr int kWaves = 2 * kCT, kThr = 64 * kWaves;
+    constexpr int kNT = N / 16, kNH = kNT / 2;       // state tiles, per wavefront
     constexpr int kVB = kQ * N / 8;                  // 16-byte vectors of a B (or C) chunk
     constexpr int kBV = (kVB + kThr - 1) / kThr;     // per thread
     constexpr int kVX = kQ * P / 8;                  // 16-byte vectors of an x chunk
-    constexpr int kXV = kVX / kThr;                  // per thread (2)
-    static_assert(kVX % kThr == 0, "x chunk splits evenly");
+    static_assert(kVX == kThr, "one x vector per thread");
     using SM = SsdSmem<N, P>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
     bf16_t *Bs = reinterpret_cast<bf16_t *>(smem + SM::kBs);
@@ -101,8 +116,10 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     float *cum = reinterpret_cast<float *>(smem + SM::kCum);
     float *dts = reinterpret_cast<float *>(smem + SM::kDt);
     float *wts = reinterpret_cast<float *>(smem + SM::kW);
+    bf16_t *Ys = reinterpret_cast<bf16_t *>(smem + SM::kYs);
 
-    const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int q = wv % kCT, hf = wv / kCT;
     const int li = lane & 15, lg = lane >> 4;
     const int64_t H = p.nheads, G = p.ngroups, L = p.seqlen;
     const int64_t b = blockIdx.x / H, h = blockIdx.x - b * H;
@@ -117,17 +134,45 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     const bf16_t *Cg = static_cast<const bf16_t *>(p.C) + (b * L * G + g) * N;
     bf16_t *yg = static_cast<bf16_t *>(p.out) + (b * L * H + h) * P;
 
-    // state tiles: lane holds H^T[n = 16 m + 4 lg + r][col = 16 q + li]
+    // this wavefront's state tiles m = hf kNH + mm: lane holds
+    // H^T[n = 16 m + 4 lg + r][col = 16 q + li]
     const int col = 16 * q + li;
-    const float *h0 = p.h0 ? p.h0 + ((b * H + h) * P + col) * N : nullptr;
-    f32x4 Hs[kNT];
+    const int m0 = hf * kNH;
+    f32x4 Hs[kNH];
+    if (p.h0) {   // one test for all loads, so they are issued together
+        const float *h0 = p.h0 + ((b * H + h) * P + col) * N;
 #pragma unroll
-    for (int m = 0; m < kNT; m++)
+        for (int mm = 0; mm < kNH; mm++)
+            Hs[mm] = *reinterpret_cast<const f32x4 *>(h0 + 16 * (m0 + mm) + 4 * lg);
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; r++) Hs[m][r] = h0 ? h0[16 * m + 4 * lg + r] : 0.0f;
+        for (int mm = 0; mm < kNH; mm++) Hs[mm] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // exchange entry of state tile m of column tile q: this lane's 4 bf16
+    // high parts, then its 4 low parts
+    auto hx = [&](int par, int m) {
+        return reinterpret_cast<s16x4 *>(smem + SM::kHx + par * SM::kHxPar +
+                                         ((q * kNT + m) * 64 + lane) * 16);
+    };
+    auto publish = [&](int par) {
+#pragma unroll
+        for (int mm = 0; mm < kNH; mm++) {
+            s16x4 hi, lo;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const short v = bfs(Hs[mm][r]);
+                hi[r] = v;
+                lo[r] = lo_bf(Hs[mm][r], v);
+            }
+            s16x4 *e = hx(par, m0 + mm);
+            e[0] = hi;
+            e[1] = lo;
+        }
+    };
+    publish(0);
 
     // the next chunk, in registers
-    u32x4 rb[kBV], rc[kBV], rx[kXV];
+    u32x4 rb[kBV], rc[kBV], rx;
     uint32_t rdt = 0;
     // Vector v of a chunk is 8 values (16 bytes) of step s = v % kQ, from
     // value 8 c8 on, c8 = v / kQ: the 64 lanes of a wavefront take 64
@@ -144,12 +189,10 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 rc[k] = ld_global16(Cg + t * brow + 8 * c8);
             }
         }
-#pragma unroll
-        for (int k = 0; k < kXV; k++) {
-            const int v = tid + k * kThr;
-            const int s = v % kQ, c8 = v / kQ;
+        {
+            const int s = tid % kQ, c8 = tid / kQ;
             const int64_t t = c0 + s < L ? c0 + s : L - 1;
-            rx[k] = ld_global16(xg + t * xrow + 8 * c8);
+            rx = ld_global16(xg + t * xrow + 8 * c8);
         }
         if (tid < kQ) {
             const int64_t t = c0 + tid < L ? c0 + tid : L - 1;
@@ -175,11 +218,9 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 }
             }
         }
-#pragma unroll
-        for (int k = 0; k < kXV; k++) {
-            const int v = tid + k * kThr;
-            const int s = v % kQ, c8 = v / kQ;
-            u32x4 vx = rx[k];
+        {
+            const int s = tid % kQ, c8 = tid / kQ;
+            u32x4 vx = rx;
             if (!(c0 + s < L)) vx = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
@@ -206,44 +247,48 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         }
     };
 
-    const int64_t nch = (L + kQ - 1) / kQ;
-    if (nch > 0) {
-        load_chunk(0);
-        stash_chunk(0);
-    }
-    __syncthreads();
-    for (int64_t c = 0; c < nch; c++) {
-        const int64_t c0 = c * kQ;
-        if (c + 1 < nch) load_chunk(c0 + kQ);
-
-        // y = exp(cum_t) C H_in (+ the chunk's own part below)
-        // The 16x16x32 product over state tiles 2 m2 and 2 m2 + 1 at once:
-        // its k index runs over (tile, 4 lg + r) in the order the state
-        // accumulators hold them, and C is read in that same order.
+    // One chunk for this wavefront; HF = hf as a compile-time constant so
+    // that the time tiles and the triangle loops unroll.
+    auto chunk = [&](auto hfc, int par) {
+        constexpr int HF = decltype(hfc)::value;
+        constexpr int kT[2] = {HF ? 1 : 0, HF ? 2 : 3};
+        // C H_in, from every state tile: the 16x16x32 product runs over state
+        // tiles 2 m2 and 2 m2 + 1 at once, its k index over (tile, 4 lg + r)
+        // in the order the state accumulators hold them, and C is read in
+        // that same order
         bf16x8_t hbh[kNT / 2], hbl[kNT / 2];
 #pragma unroll
-        for (int m = 0; m < kNT; m++)
+        for (int m2 = 0; m2 < kNT / 2; m2++) {
+            const s16x4 *e0 = hx(par, 2 * m2), *e1 = hx(par, 2 * m2 + 1);
+            const s16x4 h0v = e0[0], l0v = e0[1], h1v = e1[0], l1v = e1[1];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const __bf16 hi = static_cast<__bf16>(Hs[m][r]);
-                hbh[m / 2][4 * (m & 1) + r] = hi;
-                hbl[m / 2][4 * (m & 1) + r] = static_cast<__bf16>(Hs[m][r] - static_cast<float>(hi));
+                // by value before the bit cast (clang 22 would read element 0)
+                const short a0 = h0v[r], a1 = h1v[r], b0 = l0v[r], b1 = l1v[r];
+                hbh[m2][r] = __builtin_bit_cast(__bf16, a0);
+                hbh[m2][4 + r] = __builtin_bit_cast(__bf16, a1);
+                hbl[m2][r] = __builtin_bit_cast(__bf16, b0);
+                hbl[m2][4 + r] = __builtin_bit_cast(__bf16, b1);
             }
-        f32x4 Y[4];
+        }
+        f32x4 Y[2];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ii = 0; ii < 2; ii++) {
+            const int i = kT[ii];
+            s16x4 a0[kNT / 2], a1[kNT / 2];
 #pragma unroll
             for (int m2 = 0; m2 < kNT / 2; m2++) {
                 const bf16_t *crow = Cs + (16 * i + li) * SM::kPB + 32 * m2 + 4 * lg;
-                const s16x4 a0 = *reinterpret_cast<const s16x4 *>(crow);
-                const s16x4 a1 = *reinterpret_cast<const s16x4 *>(crow + 16);
-                // elements copied out by value before the bit cast: a bit
-                // cast of a vector element would read element 0 under clang 22
+                a0[m2] = *reinterpret_cast<const s16x4 *>(crow);
+                a1[m2] = *reinterpret_cast<const s16x4 *>(crow + 16);
+            }
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int m2 = 0; m2 < kNT / 2; m2++) {
                 bf16x8_t a;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const short v0 = a0[e], v1 = a1[e];
+                    const short v0 = a0[m2][e], v1 = a1[m2][e];
                     a[e] = __builtin_bit_cast(__bf16, v0);
                     a[4 + e] = __builtin_bit_cast(__bf16, v1);
                 }
@@ -252,49 +297,64 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
             }
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[r] *= exp2_hw(cum[16 * i + 4 * lg + r]);
-            Y[i] = acc;
+            Y[ii] = acc;
         }
-        // the chunk's own part: W = G . exp(cum_t - cum_s) dt_s (s <= t), Y += W x
+        // the chunk's own part: W = G . exp(cum_t - cum_s) dt_s (s <= t),
+        // Y += W x.  This lane's s are 16 j + 4 lg + r and its t 16 i + li.
+        f32x4 cs[4], ds[4];
+        s16x4 xb[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int j = 0; j < 4; j++) {
+            if (j > kT[1]) break;
+            cs[j] = *reinterpret_cast<const f32x4 *>(cum + 16 * j + 4 * lg);
+            ds[j] = *reinterpret_cast<const f32x4 *>(dts + 16 * j + 4 * lg);
+            xb[j] = *reinterpret_cast<const s16x4 *>(XT + col * SM::kPT + 16 * j + 4 * lg);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++) {
+            const int i = kT[ii];
             const int t = 16 * i + li;
             const float ct = cum[t];
+            bf16x8_t cb[N / 32];
+#pragma unroll
+            for (int k = 0; k < N / 32; k++)
+                cb[k] = *reinterpret_cast<const bf16x8_t *>(Cs + t * SM::kPB + 32 * k + 8 * lg);
 #pragma unroll
             for (int j = 0; j <= i; j++) {
+                bf16x8_t ba[N / 32];
+#pragma unroll
+                for (int k = 0; k < N / 32; k++)
+                    ba[k] = *reinterpret_cast<const bf16x8_t *>(Bs + (16 * j + li) * SM::kPB + 32 * k + 8 * lg);
                 f32x4 gt = {0.0f, 0.0f, 0.0f, 0.0f};   // G^T[s = 16 j + 4 lg + r][t]
 #pragma unroll
-                for (int k0 = 0; k0 < N; k0 += 32) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Bs + (16 * j + li) * SM::kPB + k0 + 8 * lg);
-                    const bf16x8_t bb = *reinterpret_cast<const bf16x8_t *>(Cs + t * SM::kPB + k0 + 8 * lg);
-                    gt = mfma32(a, bb, gt);
-                }
+                for (int k = 0; k < N / 32; k++) gt = mfma32(ba[k], cb[k], gt);
                 s16x4 wh, wl;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const int s = 16 * j + 4 * lg + r;
-                    const float wv = s <= t ? gt[r] * exp2_hw(ct - cum[s]) * dts[s] : 0.0f;
-                    const short hi = bfs(wv);
+                    float wvv = gt[r] * exp2_hw(ct - cs[j][r]) * ds[j][r];
+                    // below the diagonal s < t always; on it keep s <= t (a
+                    // select: both sides are computed, no branch)
+                    if (j == i) wvv = (4 * lg + r <= li) ? wvv : 0.0f;
+                    const short hi = bfs(wvv);
                     wh[r] = hi;
-                    wl[r] = lo_bf(wv, hi);
+                    wl[r] = lo_bf(wvv, hi);
                 }
-                const s16x4 xb = *reinterpret_cast<const s16x4 *>(XT + col * SM::kPT + 16 * j + 4 * lg);
-                Y[i] = mfma16(wh, xb, Y[i]);
-                Y[i] = mfma16(wl, xb, Y[i]);
+                Y[ii] = mfma16(wh, xb[j], Y[ii]);
+                Y[ii] = mfma16(wl, xb[j], Y[ii]);
             }
         }
-        // y + D x, stored: lane holds y[t = 16 i + 4 lg + r][col]
+        // y + D x into the output tile (lane holds y[t = 16 i + 4 lg + r][col]);
+        // it leaves in whole rows after the barrier
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int ii = 0; ii < 2; ii++) {
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int t = 16 * i + 4 * lg + r;
-                if (c0 + t < L) {
-                    const float xv = bf16_to_f32(XT[col * SM::kPT + t]);
-                    st_global(yg + (c0 + t) * xrow + col, f32_to_bf16(Y[i][r] + dskip * xv));
-                }
+                const int t = 16 * kT[ii] + 4 * lg + r;
+                const float xv = bf16_to_f32(XT[col * SM::kPT + t]);
+                Ys[t * SM::kPY + col] = f32_to_bf16(Y[ii][r] + dskip * xv);
             }
         }
-        // H_out = exp(cum_last) H_in + B^T (w x)
+        // this wavefront's state tiles: H_out = exp(cum_last) H_in + B^T (w x)
         const float decay = exp2_hw(cum[kQ - 1]);
         bf16x8_t xsh[2], xsl[2];
 #pragma unroll
@@ -310,17 +370,41 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
             }
         }
 #pragma unroll
-        for (int m = 0; m < kNT; m++) {
+        for (int mm = 0; mm < kNH; mm++) {
 #pragma unroll
-            for (int r = 0; r < 4; r++) Hs[m][r] *= decay;
+            for (int r = 0; r < 4; r++) Hs[mm][r] *= decay;
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(BT + (16 * m + li) * SM::kPT + 32 * kk + 8 * lg);
-                Hs[m] = mfma32(a, xsh[kk], Hs[m]);
-                Hs[m] = mfma32(a, xsl[kk], Hs[m]);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(BT + (16 * (m0 + mm) + li) * SM::kPT + 32 * kk + 8 * lg);
+                Hs[mm] = mfma32(a, xsh[kk], Hs[mm]);
+                Hs[mm] = mfma32(a, xsl[kk], Hs[mm]);
             }
         }
+    };
+
+    const int64_t nch = (L + kQ - 1) / kQ;
+    if (nch > 0) {
+        load_chunk(0);
+        stash_chunk(0);
+    }
+    __syncthreads();
+    for (int64_t c = 0; c < nch; c++) {
+        const int64_t c0 = c * kQ;
+        if (c + 1 < nch) load_chunk(c0 + kQ);
+        const int par = int(c & 1);
+        if (hf) chunk(std::integral_constant<int, 1>{}, par);
+        else chunk(std::integral_constant<int, 0>{}, par);
+        // the new state for the next chunk's C H_in (the other buffer: its
+        // last readers were the previous chunk's, behind the last barrier)
+        publish(par ^ 1);
         __syncthreads();
+        // the chunk's output rows: 16-byte stores, P / 8 lanes per row
+        {
+            const int t = tid / (P / 8), c8 = tid % (P / 8);
+            if (c0 + t < L)
+                st_global16(yg + (c0 + t) * xrow + 8 * c8,
+                            *reinterpret_cast<const u32x4 *>(Ys + t * SM::kPY + 8 * c8));
+        }
         if (c + 1 < nch) stash_chunk(c0 + kQ);
         __syncthreads();
     }
@@ -328,9 +412,8 @@ __global__ __launch_bounds__(4 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     if (p.last_state) {
         float *ls = p.last_state + ((b * H + h) * P + col) * N;
 #pragma unroll
-        for (int m = 0; m < kNT; m++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) ls[16 * m + 4 * lg + r] = Hs[m][r];
+        for (int mm = 0; mm < kNH; mm++)
+            *reinterpret_cast<f32x4 *>(ls + 16 * (m0 + mm) + 4 * lg) = Hs[mm];
     }
 }
 
@@ -338,10 +421,10 @@ template <int N>
 hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.batch * p.nheads));
     switch (p.headdim) {
-        case 16: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 16>), grid, dim3(64), 0, stream, p); break;
-        case 32: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 32>), grid, dim3(128), 0, stream, p); break;
-        case 48: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 48>), grid, dim3(192), 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 64>), grid, dim3(256), 0, stream, p); break;
+        case 16: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 16>), grid, dim3(128), 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 32>), grid, dim3(256), 0, stream, p); break;
+        case 48: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 48>), grid, dim3(384), 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 64>), grid, dim3(512), 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipSuccess;
