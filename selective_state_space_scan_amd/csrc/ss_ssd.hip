@@ -122,7 +122,10 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     const int q = wv % kCT, hf = wv / kCT;
     const int li = lane & 15, lg = lane >> 4;
     const int64_t H = p.nheads, G = p.ngroups, L = p.seqlen;
-    const int64_t b = blockIdx.x / H, h = blockIdx.x - b * H;
+    // consecutive workgroups go to the 8 XCDs in turn: with the batch index
+    // the fast one, the heads of a batch entry (which share its B and C)
+    // land on the same XCD's L2 when batch is a multiple of 8
+    const int64_t b = blockIdx.x % p.batch, h = blockIdx.x / p.batch;
     const int64_t g = h / (H / G);
     const float a2 = p.A[h] * kLog2e;
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
