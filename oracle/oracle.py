@@ -71,6 +71,8 @@ def _load():
             lib.sso_conv_update.restype = None
             lib.sso_ssd_fwd.argtypes = [i64] * 6 + [dp] * 7 + [c_int] + [dp] * 3 + [i64, i64]
             lib.sso_ssd_fwd.restype = c_int
+            lib.sso_ssd_bwd.argtypes = [i64] * 6 + [dp] * 7 + [c_int] + [dp] * 11 + [i64, i64]
+            lib.sso_ssd_bwd.restype = c_int
             _lib = lib
     return _lib
 
@@ -305,3 +307,56 @@ def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, h0=None, thread
         with ThreadPoolExecutor(len(pieces)) as ex:
             list(ex.map(run, pieces))
     return y, last
+
+
+def ssd_bwd(x, dt, A, B, C, D=None, dt_bias=None, softplus=True, h0=None, dy=None,
+            dlast=None, threads: int = 1):
+    """Backward of ``sum(dy * y) (+ sum(dlast * last_state))`` for ``ssd_fwd``.
+
+    Returns a dict with dx, ddt (w.r.t. the raw dt), dA, dB, dC, dh0 and, for
+    the optional inputs given, dD and ddt_bias.
+    """
+    lib = _load()
+    x, dt, A, B, C, dy = map(_f64, (x, dt, A, B, C, dy))
+    D, dt_bias, h0, dlast = map(_f64, (D, dt_bias, h0, dlast))
+    nb, nl, nh, npd = x.shape
+    ng, ns = B.shape[2], B.shape[3]
+    dx = np.zeros_like(x)
+    ddt = np.zeros((nb, nl, nh))
+    dh0 = np.zeros((nb, nh, npd, ns))
+    pieces = _split(nb, threads)
+    part = [(np.zeros(nh), np.zeros((nb, nl, ng, ns)), np.zeros((nb, nl, ng, ns)), np.zeros(nh),
+             np.zeros(nh)) for _ in pieces]
+
+    def run(i):
+        b0, b1 = pieces[i]
+        dA_i, dB_i, dC_i, dD_i, db_i = part[i]
+        rc = lib.sso_ssd_bwd(nb, nl, nh, npd, ng, ns, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                             _p(dt_bias), int(bool(softplus)), _p(h0), _p(dy), _p(dlast), _p(dx),
+                             _p(ddt), _p(dA_i), _p(dB_i), _p(dC_i), _p(dD_i), _p(db_i), _p(dh0),
+                             b0, b1)
+        if rc != 0:
+            raise MemoryError("oracle SSD backward could not allocate its states")
+
+    if len(pieces) == 1:
+        run(0)
+    else:
+        with ThreadPoolExecutor(len(pieces)) as ex:
+            list(ex.map(run, range(len(pieces))))
+    dA = np.zeros(nh)
+    dB = np.zeros((nb, nl, ng, ns))
+    dC = np.zeros((nb, nl, ng, ns))
+    dD = np.zeros(nh)
+    dbias = np.zeros(nh)
+    for dA_i, dB_i, dC_i, dD_i, db_i in part:
+        dA += dA_i
+        dB += dB_i      # disjoint batch entries per piece
+        dC += dC_i
+        dD += dD_i
+        dbias += db_i
+    out = dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dh0=dh0)
+    if D is not None:
+        out["dD"] = dD
+    if dt_bias is not None:
+        out["ddt_bias"] = dbias
+    return out

@@ -422,3 +422,90 @@ int sso_ssd_fwd(int64_t nb, int64_t nl, int64_t nh, int64_t np, int64_t ng, int6
     free(H);
     return 0;
 }
+
+/*
+ * Backward of sum(dy * y) + sum(dlast * H_last) for sso_ssd_fwd, by
+ * back-propagation through time.  With G_t = dL/dH_t (headdim x d_state),
+ *   G_t      = dlast (t = L-1) or exp(dt_{t+1} A) G_{t+1}, plus dy_t C_t^T
+ *   dx_t     = dt_t G_t B_t + D dy_t
+ *   dB_t    += dt_t G_t^T x_t          (summed over the heads of the group)
+ *   dC_t    += H_t^T dy_t              (likewise)
+ *   d dt_t   = < G_t, A exp(dt_t A) H_{t-1} + x_t B_t^T >
+ *   dA      += dt_t exp(dt_t A) < G_t, H_{t-1} >
+ *   dD      += < x_t, dy_t >
+ *   dh0      = exp(dt_0 A) G_0
+ * and the raw dt gets d dt_t times softplus'(raw) = sigmoid(raw) when
+ * softplus is on; d dt_bias sums it.  dA, dD, ddt_bias, dB, dC accumulate
+ * (the caller zeroes them); batches b0 <= b < b1.
+ */
+int sso_ssd_bwd(int64_t nb, int64_t nl, int64_t nh, int64_t np, int64_t ng, int64_t ns,
+                const double *x, const double *dtr, const double *A, const double *B,
+                const double *C, const double *D, const double *dt_bias, int softplus,
+                const double *h0, const double *dy, const double *dlast, double *dx,
+                double *ddt, double *dA, double *dB, double *dC, double *dD, double *ddt_bias,
+                double *dh0, int64_t b0, int64_t b1)
+{
+    (void)nb;
+    const int64_t ps = np * ns;
+    double *Hs = (double *)malloc(sizeof(double) * (size_t)(ps > 0 ? ps : 1) * (size_t)(nl + 1));
+    double *Gs = (double *)malloc(sizeof(double) * (size_t)(ps > 0 ? ps : 1));
+    double *dtv = (double *)malloc(sizeof(double) * (size_t)(nl > 0 ? nl : 1));
+    if (!Hs || !Gs || !dtv) { free(Hs); free(Gs); free(dtv); return 1; }
+    for (int64_t b = b0; b < b1; b++) {
+        for (int64_t h = 0; h < nh; h++) {
+            const int64_t g = h / (nh / ng);
+            /* forward states H_{-1} .. H_{L-1} at Hs[(t + 1) * ps] */
+            for (int64_t i = 0; i < ps; i++) Hs[i] = h0 ? h0[(b * nh + h) * ps + i] : 0.0;
+            for (int64_t t = 0; t < nl; t++) {
+                double dt = dtr[(b * nl + t) * nh + h] + (dt_bias ? dt_bias[h] : 0.0);
+                if (softplus) dt = sso_softplus(dt);
+                dtv[t] = dt;
+                const double a = exp(dt * A[h]);
+                const double *xt = x + ((b * nl + t) * nh + h) * np;
+                const double *bt = B + ((b * nl + t) * ng + g) * ns;
+                for (int64_t p = 0; p < np; p++)
+                    for (int64_t n = 0; n < ns; n++)
+                        Hs[(t + 1) * ps + p * ns + n] = a * Hs[t * ps + p * ns + n] + dt * xt[p] * bt[n];
+            }
+            for (int64_t i = 0; i < ps; i++) Gs[i] = dlast ? dlast[(b * nh + h) * ps + i] : 0.0;
+            for (int64_t t = nl - 1; t >= 0; t--) {
+                const double dt = dtv[t], a = exp(dt * A[h]);
+                const double *xt = x + ((b * nl + t) * nh + h) * np;
+                const double *bt = B + ((b * nl + t) * ng + g) * ns;
+                const double *ct = C + ((b * nl + t) * ng + g) * ns;
+                const double *dyt = dy + ((b * nl + t) * nh + h) * np;
+                double *dxt = dx + ((b * nl + t) * nh + h) * np;
+                double *dbt = dB + ((b * nl + t) * ng + g) * ns;
+                double *dct = dC + ((b * nl + t) * ng + g) * ns;
+                const double *Ht = Hs + (t + 1) * ps, *Hp = Hs + t * ps;
+                double d_dt = 0.0, d_a = 0.0;
+                for (int64_t p = 0; p < np; p++) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < ns; n++) {
+                        double *gv = &Gs[p * ns + n];
+                        *gv += dyt[p] * ct[n];                /* G_t */
+                        acc += *gv * bt[n];
+                        dbt[n] += dt * *gv * xt[p];
+                        dct[n] += Ht[p * ns + n] * dyt[p];
+                        d_dt += *gv * xt[p] * bt[n];
+                        d_a += *gv * Hp[p * ns + n];
+                    }
+                    dxt[p] = dt * acc + (D ? D[h] * dyt[p] : 0.0);
+                    if (dD) dD[h] += xt[p] * dyt[p];
+                }
+                d_dt += A[h] * a * d_a;
+                dA[h] += dt * a * d_a;
+                double raw_grad = d_dt;
+                if (softplus)
+                    raw_grad *= sso_sigmoid(dtr[(b * nl + t) * nh + h] + (dt_bias ? dt_bias[h] : 0.0));
+                ddt[(b * nl + t) * nh + h] = raw_grad;
+                if (ddt_bias) ddt_bias[h] += raw_grad;
+                for (int64_t i = 0; i < ps; i++) Gs[i] *= a;   /* carried to t - 1 */
+            }
+            if (dh0)
+                for (int64_t i = 0; i < ps; i++) dh0[(b * nh + h) * ps + i] = Gs[i];
+        }
+    }
+    free(Hs); free(Gs); free(dtv);
+    return 0;
+}

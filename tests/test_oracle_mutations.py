@@ -62,6 +62,11 @@ MUTATIONS = {
     "ssd_group_map_wrong": ("const int64_t g = h / (nh / ng);", "const int64_t g = h % ng;"),
     "ssd_skip_dropped": ("yt[p] = acc + (D ? D[h] * xt[p] : 0.0);", "yt[p] = acc;"),
     "ssd_h0_ignored": ("H[i] = h0 ? h0[(b * nh + h) * np * ns + i] : 0.0;", "H[i] = 0.0;"),
+    "ssd_bwd_carry_missing": ("for (int64_t i = 0; i < ps; i++) Gs[i] *= a;   /* carried to t - 1 */",
+                              "for (int64_t i = 0; i < ps; i++) Gs[i] *= 1.0;"),
+    "ssd_bwd_dB_without_dt": ("dbt[n] += dt * *gv * xt[p];", "dbt[n] += *gv * xt[p];"),
+    "ssd_bwd_dA_without_decay": ("dA[h] += dt * a * d_a;", "dA[h] += dt * d_a;"),
+    "ssd_bwd_dC_previous_state": ("dct[n] += Ht[p * ns + n] * dyt[p];", "dct[n] += Hp[p * ns + n] * dyt[p];"),
 }
 
 

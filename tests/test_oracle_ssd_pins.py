@@ -1,4 +1,4 @@
-"""Pins of the oracle's Mamba-2 SSD forward against things other than itself.
+"""Pins of the oracle's Mamba-2 SSD forward and backward against things other than itself.
 
 The reading pinned here (the pages name SSD without printing it): per
 batch and head a headdim x d_state state, H_t = exp(dt_t A_h) H_{t-1} +
@@ -15,9 +15,15 @@ group (heads grouped contiguously).  Expected values come from
   * structural facts: continuation from the last state, no decay and no
     input at dt = 0.
 
+The backward (back-propagation through time) is pinned to central
+differences of the forward for every input, with and without softplus and
+with two groups, and, with one group, to the Mamba-1 oracle's backward with
+the tied parameters' gradients summed.
+
 A wrong decay sign, a dropped dt on the input, C and B exchanged, a wrong
-head-to-group map, a dropped D term or an ignored initial state fails at
-least one of them.
+head-to-group map, a dropped D term, an ignored initial state, a missing
+adjoint carry, dB without dt, dA without the decay, or dC from the
+previous state fails at least one of them.
 """
 import numpy as np
 import pytest
@@ -126,3 +132,80 @@ def test_threads_split_batch_only():
                             c["h0"], threads=3)
     np.testing.assert_array_equal(y1, y3)
     np.testing.assert_array_equal(l1, l3)
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+def _loss(c, dy, dlast, softplus=True):
+    y, last = _run(c, softplus)
+    return float(np.sum(y * dy) + np.sum(last * dlast))
+
+
+def _central(fn, arr, eps=1e-6):
+    g = np.zeros_like(arr)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        keep = arr[i]
+        arr[i] = keep + eps
+        fp = fn()
+        arr[i] = keep - eps
+        fm = fn()
+        arr[i] = keep
+        g[i] = (fp - fm) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("ng", [1, 2])
+def test_backward_matches_central_differences(softplus, ng):
+    c = _case(40 + ng, nb=2, nl=7, nh=2, npd=2, ng=ng, ns=3)
+    if not softplus:
+        c["dt"] = np.abs(c["dt"])
+        c["dt_bias"] = np.zeros_like(c["dt_bias"])
+    r = np.random.default_rng(50 + ng)
+    dy = r.standard_normal(c["x"].shape)
+    dlast = r.standard_normal(c["h0"].shape)
+    g = oracle.ssd_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], c["dt_bias"], softplus,
+                       c["h0"], dy, dlast)
+    f = lambda: _loss(c, dy, dlast, softplus)  # noqa: E731
+    for name, key in (("dx", "x"), ("ddt", "dt"), ("dA", "A"), ("dB", "B"), ("dC", "C"),
+                      ("dD", "D"), ("ddt_bias", "dt_bias"), ("dh0", "h0")):
+        np.testing.assert_allclose(g[name], _central(f, c[key]), rtol=1e-6, atol=1e-7,
+                                   err_msg=name)
+
+
+def test_backward_one_group_is_the_selective_scan_backward():
+    c = _case(60, nb=2, nl=19, nh=3, npd=4, ng=1, ns=5)
+    nb, nl, nh, npd = c["x"].shape
+    ns = c["B"].shape[3]
+    r = np.random.default_rng(61)
+    dy = r.standard_normal(c["x"].shape)
+    dlast = r.standard_normal(c["h0"].shape)
+    g = oracle.ssd_bwd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], c["dt_bias"], True,
+                       c["h0"], dy, dlast)
+    u = c["x"].reshape(nb, nl, nh * npd).transpose(0, 2, 1)
+    delta = np.repeat(c["dt"], npd, axis=2).transpose(0, 2, 1)
+    A = np.repeat(c["A"], npd)[:, None] * np.ones((1, ns))
+    Bs = c["B"][:, :, 0, :].transpose(0, 2, 1)
+    Cs = c["C"][:, :, 0, :].transpose(0, 2, 1)
+    D = np.repeat(c["D"], npd)
+    bias = np.repeat(c["dt_bias"], npd)
+    s6 = oracle.bwd(u, delta, A, Bs, Cs, D, None, bias, True,
+                    dy.reshape(nb, nl, nh * npd).transpose(0, 2, 1),
+                    c["h0"].reshape(nb, nh * npd, ns), dlast.reshape(nb, nh * npd, ns))
+    tie = lambda a: a.reshape(nh, npd, *a.shape[1:]).sum(axis=1)  # noqa: E731
+    np.testing.assert_allclose(g["dx"], s6["du"].transpose(0, 2, 1).reshape(c["x"].shape),
+                               rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(g["ddt"], s6["ddelta"].reshape(nb, nh, npd, nl).sum(axis=2)
+                               .transpose(0, 2, 1), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(g["dA"], tie(s6["dA"]).sum(axis=1), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(g["dB"][:, :, 0, :], s6["dB"].transpose(0, 2, 1), rtol=1e-11,
+                               atol=1e-11)
+    np.testing.assert_allclose(g["dC"][:, :, 0, :], s6["dC"].transpose(0, 2, 1), rtol=1e-11,
+                               atol=1e-11)
+    np.testing.assert_allclose(g["dD"], tie(s6["dD"]), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(g["ddt_bias"], tie(s6["ddelta_bias"]), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(g["dh0"].reshape(nb, nh * npd, ns), s6["dh0"], rtol=1e-11,
+                               atol=1e-11)
