@@ -59,7 +59,8 @@ MUTATIONS = {
     "ssd_input_without_dt": ("*hv = decay * *hv + dt * xt[p] * bt[n];",
                              "*hv = decay * *hv + xt[p] * bt[n];"),
     "ssd_output_uses_B": ("acc += ct[n] * *hv;", "acc += bt[n] * *hv;"),
-    "ssd_group_map_wrong": ("const int64_t g = h / (nh / ng);", "const int64_t g = h % ng;"),
+    "ssd_group_map_wrong": ("const int64_t g = h / (nh / ng);\n            for (int64_t i = 0; i < np * ns; i++)\n                H[i]",
+                            "const int64_t g = h % ng;\n            for (int64_t i = 0; i < np * ns; i++)\n                H[i]"),
     "ssd_skip_dropped": ("yt[p] = acc + (D ? D[h] * xt[p] : 0.0);", "yt[p] = acc;"),
     "ssd_h0_ignored": ("H[i] = h0 ? h0[(b * nh + h) * np * ns + i] : 0.0;", "H[i] = 0.0;"),
     "ssd_bwd_carry_missing": ("for (int64_t i = 0; i < ps; i++) Gs[i] *= a;   /* carried to t - 1 */",
