@@ -237,7 +237,30 @@ def ssd_detail(hip, lib, to_dev, dev):
     Q, N, P = 64, w.dstate, w.headdim
     fl = (Q * Q * N + Q * Q * P + 4 * Q * N * P) * w.batch * w.nheads * (w.seqlen // Q)
     del sets, outs
-    return {w.name: {"kernel_ms": round(ms, 5), "elements_per_s": E / (ms * 1e-3),
+    # the backward (through the selective-scan backward), timed as a whole call
+    wb = ssin.SSD_WORKLOADS["mamba2_130m_ssd_bwd_bf16_8x2048x24x64_n128"]
+    db = {k: to_dev(v) for k, v in ssin.make_ssd(wb).items()}
+    wsb = torch.empty(binding.ss_ssd_bwd_workspace_size(wb.batch, wb.seqlen, wb.nheads,
+                                                        wb.headdim, wb.ngroups, wb.dstate),
+                      dtype=torch.uint8, device=dev)
+
+    def bwd():
+        binding.ss_ssd_bwd(db["x"], db["dt"], db["A"], db["B"], db["C"], db["D"], db["dt_bias"],
+                           True, dout=db["dout"], workspace=wsb)
+    bwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / 5
+    del db, wsb
+    return {wb.name: {"call_ms": round(bms, 4), "elements_per_s": E / (bms * 1e-3),
+                      "note": "selective-scan backward on the tied (head, column) channels, "
+                              "with layout changes; not the chunked form"},
+            w.name: {"kernel_ms": round(ms, 5), "elements_per_s": E / (ms * 1e-3),
                      "algorithmic_bytes": by,
                      "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac_of_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

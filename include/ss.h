@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 7
+#define SS_ABI_VERSION 8
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -259,10 +259,40 @@ ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      const float *dt_bias, int dt_softplus, const float *h0, void *out,
                      float *last_state, void *stream);
 
+/* Bytes of device workspace ss_ssd_bwd needs (0 for empty shapes). */
+size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                 int64_t ngroups, int64_t dstate);
+
+/*
+ * Mamba-2 SSD backward: gradients of sum(dout * out) + sum(dlast * last_state)
+ * for ss_ssd_fwd with the same arguments (same shapes, dtypes and limits).
+ *   dout           (batch, seqlen, nheads, headdim) bf16, required
+ *   dlast          (batch, nheads, headdim, dstate) f32 or NULL
+ *   dx             like x, bf16, required
+ *   ddt            like dt, bf16, required (w.r.t. the raw dt)
+ *   dA             (nheads) f32, required; summed over batch and time
+ *   dB, dC         like B, C, bf16, required; summed over the group's heads
+ *   dD, ddt_bias   NULL iff D / dt_bias is NULL
+ *   dh0            optional (may be given without h0: the gradient at a zero start)
+ *   workspace      ss_ssd_bwd_workspace_size() bytes, 16-byte aligned
+ * The SSD recurrence with one group is the selective scan over the heads'
+ * columns with tied parameters, and this call runs the selective-scan
+ * backward (f32 inside) on that layout and sums the tied gradients per
+ * head in a fixed order; with several groups it runs once per (batch entry,
+ * group).  Exact and deterministic, but not the chunked matrix-core form.
+ */
+ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                     int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const float *dt_bias, int dt_softplus, const float *h0, const void *dout,
+                     const float *dlast, void *dx, void *ddt, float *dA, void *dB, void *dC,
+                     float *dD, float *ddt_bias, float *dh0, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /*
  * Profiling aid for callers that time the library's kernels one by one
  * (not needed for normal use).  When `events` is non-NULL, every later
- * ss_fwd / ss_bwd / ss_state_update / ss_conv1d_* / ss_ssd_fwd call on this thread records the next
+ * ss_fwd / ss_bwd / ss_state_update / ss_conv1d_* / ss_ssd_* call on this thread records the next
  * unused entry of `events` (each a hipEvent_t created by the caller) on its
  * stream before its first kernel and after each kernel it launches, until
  * `count` entries are used.  ss_profile_events(NULL, 0) switches it off.

@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 7
+ABI_VERSION = 8
 _lock = threading.Lock()
 _lib = None
 
@@ -72,6 +72,11 @@ def load() -> ctypes.CDLL:
                                             + [vp] * 2)
             lib.ss_ssd_fwd.restype = c_int
             lib.ss_ssd_fwd.argtypes = [i64] * 6 + [c_int] + [vp] * 7 + [c_int] + [vp] * 4
+            lib.ss_ssd_bwd_workspace_size.restype = sz
+            lib.ss_ssd_bwd_workspace_size.argtypes = [i64] * 6
+            lib.ss_ssd_bwd.restype = c_int
+            lib.ss_ssd_bwd.argtypes = ([i64] * 6 + [c_int] + [vp] * 7 + [c_int] + [vp] * 12
+                                       + [sz, vp])
             lib.ss_conv1d_fwd.restype = c_int
             lib.ss_conv1d_fwd.argtypes = [i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 4
             lib.ss_conv1d_bwd.restype = c_int
@@ -324,3 +329,42 @@ def ss_ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, h0=None, 
                           int(bool(dt_softplus)), _f32(h0, "h0"), _ptr(out),
                           _f32(last_state, "last_state"), _stream()))
     return (out, last_state) if (return_last_state or last_state is not None) else out
+
+
+def ss_ssd_bwd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate) -> int:
+    return int(load().ss_ssd_bwd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate))
+
+
+def ss_ssd_bwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, h0=None, dout=None,
+               dlast=None, want_dh0=False, workspace=None):
+    """Backward of ``sum(dout * y) + sum(dlast * last_state)`` for ss_ssd_fwd.
+
+    Returns a dict with dx, ddt, dA, dB, dC and, for the optional inputs
+    given, dD, ddt_bias, plus dh0 when ``want_dh0`` or h0 is given.
+    """
+    lib = load()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    io = _io_dtype(x)
+    _same_io(io, dt, B, C, dout)
+    dev = x.device
+    g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt),
+             dA=torch.empty(nheads, dtype=torch.float32, device=dev),
+             dB=torch.empty_like(B), dC=torch.empty_like(C))
+    if D is not None:
+        g["dD"] = torch.empty(nheads, dtype=torch.float32, device=dev)
+    if dt_bias is not None:
+        g["ddt_bias"] = torch.empty(nheads, dtype=torch.float32, device=dev)
+    if want_dh0 or h0 is not None:
+        g["dh0"] = torch.empty(batch, nheads, headdim, dstate, dtype=torch.float32, device=dev)
+    need = ss_ssd_bwd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.ss_ssd_bwd(batch, seqlen, nheads, headdim, ngroups, dstate, io, _ptr(x), _ptr(dt),
+                          _f32(A, "A"), _ptr(B), _ptr(C), _f32(D, "D"), _f32(dt_bias, "dt_bias"),
+                          int(bool(dt_softplus)), _f32(h0, "h0"), _ptr(dout),
+                          _f32(dlast, "dlast"), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]),
+                          _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+                          _ptr(g.get("ddt_bias")), _ptr(g.get("dh0")), _ptr(workspace),
+                          workspace.numel(), _stream()))
+    return g

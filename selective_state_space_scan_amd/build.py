@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libss.so")
-SOURCES = ["ss_api.cpp", "ss_fwd.hip", "ss_bwd.hip", "ss_state_update.hip", "ss_conv.hip", "ss_ssd.hip"]
+SOURCES = ["ss_api.cpp", "ss_fwd.hip", "ss_bwd.hip", "ss_state_update.hip", "ss_conv.hip", "ss_ssd.hip", "ss_ssd_bwd.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instruction selection is switched off: every kernel issues

@@ -306,6 +306,32 @@ ss_status check_conv_dims(int64_t batch, int64_t dim, int64_t seqlen, int64_t wi
     return SS_OK;
 }
 
+ss_status check_ssd_dims(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                         int64_t ngroups, int64_t dstate, int io_dtype) {
+    if (batch < 0) return fail(SS_EINVAL, "batch must be >= 0 (got %lld)", (long long)batch);
+    if (seqlen < 0) return fail(SS_EINVAL, "seqlen must be >= 0 (got %lld)", (long long)seqlen);
+    if (nheads < 0) return fail(SS_EINVAL, "nheads must be >= 0 (got %lld)", (long long)nheads);
+    if (ngroups < 1 || (nheads > 0 && nheads % ngroups != 0))
+        return fail(SS_EINVAL, "ngroups (%lld) must be >= 1 and divide nheads (%lld)",
+                    (long long)ngroups, (long long)nheads);
+    if (io_dtype != SS_F32 && io_dtype != SS_BF16)
+        return fail(SS_EINVAL, "io_dtype must be SS_F32 (0) or SS_BF16 (1) (got %d)", io_dtype);
+    if (io_dtype != SS_BF16)
+        return fail(SS_EUNSUPPORTED, "the SSD scan runs on bf16 matrix cores: io_dtype must be SS_BF16");
+    if (headdim != 16 && headdim != 32 && headdim != 48 && headdim != 64)
+        return fail(SS_EUNSUPPORTED, "headdim %lld is not supported (16, 32, 48 or 64)",
+                    (long long)headdim);
+    if (dstate != 32 && dstate != 64 && dstate != 96 && dstate != 128)
+        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (32, 64, 96 or 128)",
+                    (long long)dstate);
+    if (seqlen > kMaxSeq)
+        return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
+                    (long long)kMaxSeq);
+    if (batch * nheads > (int64_t(1) << 31) - 1 || batch > kMaxBatch)
+        return fail(SS_EUNSUPPORTED, "batch * nheads too large");
+    return SS_OK;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -375,27 +401,8 @@ ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      const float *A, const void *B, const void *C, const float *D,
                      const float *dt_bias, int dt_softplus, const float *h0, void *out,
                      float *last_state, void *stream) {
-    if (batch < 0) return fail(SS_EINVAL, "batch must be >= 0 (got %lld)", (long long)batch);
-    if (seqlen < 0) return fail(SS_EINVAL, "seqlen must be >= 0 (got %lld)", (long long)seqlen);
-    if (nheads < 0) return fail(SS_EINVAL, "nheads must be >= 0 (got %lld)", (long long)nheads);
-    if (ngroups < 1 || (nheads > 0 && nheads % ngroups != 0))
-        return fail(SS_EINVAL, "ngroups (%lld) must be >= 1 and divide nheads (%lld)",
-                    (long long)ngroups, (long long)nheads);
-    if (io_dtype != SS_F32 && io_dtype != SS_BF16)
-        return fail(SS_EINVAL, "io_dtype must be SS_F32 (0) or SS_BF16 (1) (got %d)", io_dtype);
-    if (io_dtype != SS_BF16)
-        return fail(SS_EUNSUPPORTED, "ss_ssd_fwd runs on bf16 matrix cores: io_dtype must be SS_BF16");
-    if (headdim != 16 && headdim != 32 && headdim != 48 && headdim != 64)
-        return fail(SS_EUNSUPPORTED, "headdim %lld is not supported (16, 32, 48 or 64)",
-                    (long long)headdim);
-    if (dstate != 32 && dstate != 64 && dstate != 96 && dstate != 128)
-        return fail(SS_EUNSUPPORTED, "dstate %lld is not supported (32, 64, 96 or 128)",
-                    (long long)dstate);
-    if (seqlen > kMaxSeq)
-        return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
-                    (long long)kMaxSeq);
-    if (batch * nheads > (int64_t(1) << 31) - 1)
-        return fail(SS_EUNSUPPORTED, "batch * nheads too large");
+    ss_status st0 = check_ssd_dims(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype);
+    if (st0 != SS_OK) return st0;
     Check c;
     if (batch > 0 && nheads > 0 && seqlen > 0) {
         c.need(x, "x"); c.need(B, "B"); c.need(C, "C"); c.need(out, "out");
@@ -420,6 +427,60 @@ ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_ssd_fwd(p, static_cast<hipStream_t>(stream)),
                          "ss_ssd_fwd launch");
+}
+
+size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                 int64_t ngroups, int64_t dstate) {
+    if (check_ssd_dims(batch, seqlen, nheads, headdim, ngroups, dstate, SS_BF16) != SS_OK) return 0;
+    return ssk::ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate);
+}
+
+ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                     int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const float *dt_bias, int dt_softplus, const float *h0, const void *dout,
+                     const float *dlast, void *dx, void *ddt, float *dA, void *dB, void *dC,
+                     float *dD, float *ddt_bias, float *dh0, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    ss_status st0 = check_ssd_dims(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype);
+    if (st0 != SS_OK) return st0;
+    Check c;
+    if (batch > 0 && nheads > 0 && seqlen > 0) {
+        c.need(x, "x"); c.need(B, "B"); c.need(C, "C"); c.need(dout, "dout");
+        c.need(dx, "dx"); c.need(dB, "dB"); c.need(dC, "dC");
+        if (!dt) return fail(SS_EINVAL, "dt must not be NULL");
+        if (!ddt) return fail(SS_EINVAL, "ddt must not be NULL");
+    } else {
+        c.opt(x, "x"); c.opt(B, "B"); c.opt(C, "C"); c.opt(dout, "dout");
+        c.opt(dx, "dx"); c.opt(dB, "dB"); c.opt(dC, "dC");
+    }
+    if ((dt && (reinterpret_cast<uintptr_t>(dt) & 1u)) ||
+        (ddt && (reinterpret_cast<uintptr_t>(ddt) & 1u)))
+        return fail(SS_EINVAL, "dt and ddt must be 2-byte aligned");
+    if (nheads > 0) { c.need(A, "A"); c.need(dA, "dA"); } else { c.opt(A, "A"); c.opt(dA, "dA"); }
+    c.opt(D, "D"); c.opt(dt_bias, "dt_bias"); c.opt(h0, "h0"); c.opt(dlast, "dlast");
+    c.opt(dD, "dD"); c.opt(ddt_bias, "ddt_bias"); c.opt(dh0, "dh0");
+    c.pair(dD, D, "dD", "D");
+    c.pair(ddt_bias, dt_bias, "ddt_bias", "dt_bias");
+    if (c.st != SS_OK) return c.st;
+    const size_t need = ssk::ssd_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (need > 0) {
+        if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
+        if (!aligned16(workspace)) return fail(SS_EINVAL, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(SS_EINVAL, "workspace_bytes %zu is smaller than the %zu bytes needed",
+                        workspace_bytes, need);
+    }
+    ssk::SsdBwdParams p{};
+    p.batch = batch; p.seqlen = seqlen; p.nheads = nheads; p.ngroups = ngroups;
+    p.headdim = int(headdim); p.dstate = int(dstate);
+    p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.dt_bias = dt_bias;
+    p.softplus = dt_softplus != 0; p.h0 = h0; p.out = nullptr; p.last_state = nullptr;
+    p.dout = dout; p.dlast = dlast; p.dx = dx; p.ddt = ddt; p.dA = dA; p.dB = dB; p.dC = dC;
+    p.dD = dD; p.ddt_bias = ddt_bias; p.dh0 = dh0; p.workspace = workspace;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
+    return device_status(ssk::launch_ssd_bwd(p, static_cast<hipStream_t>(stream)),
+                         "ss_ssd_bwd launch");
 }
 
 ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dtype, float *state,

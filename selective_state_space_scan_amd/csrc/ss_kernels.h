@@ -169,6 +169,23 @@ struct SsdParams {
 };
 hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream);
 
+// Mamba-2 SSD backward (through the selective-scan backward).  dout, dx:
+// (batch, L, nheads, headdim) bf16; ddt: (batch, L, nheads) bf16; dB, dC:
+// (batch, L, ngroups, dstate) bf16; dA, dD, ddt_bias: (nheads) f32; dlast,
+// dh0: (batch, nheads, headdim, dstate) f32.
+struct SsdBwdParams : SsdParams {
+    const void *dout;
+    const float *dlast;
+    void *dx, *ddt;
+    float *dA;
+    void *dB, *dC;
+    float *dD, *ddt_bias, *dh0;
+    void *workspace;
+};
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t ngroups, int64_t dstate);
+hipError_t launch_ssd_bwd(const SsdBwdParams &p, hipStream_t stream);
+
 // Segments (one wavefront each) a row of the convolution is cut into.
 int64_t conv_segments(int64_t seqlen);
 hipError_t launch_conv_fwd(const ConvFwdParams &p, bool bf16, hipStream_t stream);

@@ -223,6 +223,7 @@ class SsdWorkload:
     has_D: bool = True
     has_bias: bool = True
     has_h0: bool = False
+    bwd: bool = False  # also draw dout and dlast (after every forward input)
     seed: int = SEED_BASE
 
     @property
@@ -237,6 +238,8 @@ SSD_WORKLOADS = {
         # d_state 128, one group
         SsdWorkload("mamba2_130m_ssd_bf16_8x2048x24x64_n128", 8, 2048, 24, 64, 1, 128,
                     seed=SEED_BASE + 30),
+        SsdWorkload("mamba2_130m_ssd_bwd_bf16_8x2048x24x64_n128", 8, 2048, 24, 64, 1, 128,
+                    bwd=True, seed=SEED_BASE + 31),
     ]
 }
 
@@ -250,7 +253,8 @@ def ssd_custom(batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int,
 def make_ssd(w: SsdWorkload | str) -> dict:
     """Draw the arrays of an SSD workload.
 
-    Draw order: x, dt, B, C, U(A), D, U(dt_bias), h0.  x, B, C, D, h0 ~
+    Draw order: x, dt, B, C, U(A), D, U(dt_bias), h0, and for a backward
+    workload dout (bf16) and dlast (float32), both N(0, 1).  x, B, C, D, h0 ~
     N(0, 1); dt (raw) ~ 0.5 N(0, 1); A_h = -(1 + 15 U), U ~ Uniform[0, 1],
     one per head (the decay range of the Mamba-1 A, -1 .. -16);
     dt_bias = log(expm1(U[1e-3, 1e-1])) as for the Mamba-1 delta.  x, dt, B,
@@ -271,4 +275,7 @@ def make_ssd(w: SsdWorkload | str) -> dict:
         out["dt_bias"] = np.log(np.expm1(U)).astype(np.float32)
     if w.has_h0:
         out["h0"] = rng.standard_normal((w.batch, w.nheads, w.headdim, w.dstate)).astype(np.float32)
+    if w.bwd:
+        out["dout"] = _store(rng.standard_normal((w.batch, w.seqlen, w.nheads, w.headdim)), "bf16")
+        out["dlast"] = rng.standard_normal((w.batch, w.nheads, w.headdim, w.dstate)).astype(np.float32)
     return out

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 7
+    assert lib.ss_abi_version() == 8
 
 
 def test_ckpt_size(lib):
@@ -282,3 +282,27 @@ def test_ssd_state_overlap_and_empty(lib):
     assert _ssd(lib, h0=FAKE, last=FAKE + 256) == EINVAL and "overlap" in _msg(lib)
     assert _ssd(lib, batch=0, x=None, dt=None, B=None, C=None, out=None) == 0
     assert _ssd(lib, nheads=0, A=None, x=None, dt=None, B=None, C=None, out=None) == 0
+
+
+
+def test_ssd_bwd_checks(lib):
+    def bwd(**kw):
+        a = dict(batch=2, seqlen=64, nheads=4, headdim=64, ngroups=1, dstate=128, io=1, x=FAKE,
+                 dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, bias=None, h0=None, dout=FAKE, dlast=None,
+                 dx=FAKE, ddt=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dbias=None, dh0=None,
+                 ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.ss_ssd_bwd(a["batch"], a["seqlen"], a["nheads"], a["headdim"], a["ngroups"],
+                              a["dstate"], a["io"], a["x"], a["dt"], a["A"], a["B"], a["C"],
+                              a["D"], a["bias"], 1, a["h0"], a["dout"], a["dlast"], a["dx"],
+                              a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dbias"], a["dh0"],
+                              a["ws"], a["ws_bytes"], None)
+    assert bwd(dout=None) == EINVAL and "dout" in _msg(lib)
+    assert bwd(D=FAKE) == EINVAL and "dD" in _msg(lib)
+    assert bwd(io=0) == EUNSUP and "bf16" in _msg(lib)
+    need = lib.ss_ssd_bwd_workspace_size(2, 64, 4, 64, 1, 128)
+    assert need > 0
+    assert bwd(ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
+    assert bwd(ws=None) == EINVAL and "workspace" in _msg(lib)
+    assert lib.ss_ssd_bwd_workspace_size(2, 64, 4, 64, 1, 256) == 0
+    assert bwd(batch=0, x=None, B=None, C=None, dout=None, dx=None, dB=None, dC=None) == 0
