@@ -258,8 +258,8 @@ def ssd_detail(hip, lib, to_dev, dev):
     bms = e0.elapsed_time(e1) / 5
     del db, wsb
     return {wb.name: {"call_ms": round(bms, 4), "elements_per_s": E / (bms * 1e-3),
-                      "note": "selective-scan backward on the tied (head, column) channels, "
-                              "with layout changes; not the chunked form"},
+                      "note": "chunked backward: states pass, reverse chunk kernel, dt, "
+                              "head fold and parameter sums (one call)"},
             w.name: {"kernel_ms": round(ms, 5), "elements_per_s": E / (ms * 1e-3),
                      "algorithmic_bytes": by,
                      "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1),

@@ -274,12 +274,17 @@ size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, 
  *   dB, dC         like B, C, bf16, required; summed over the group's heads
  *   dD, ddt_bias   NULL iff D / dt_bias is NULL
  *   dh0            optional (may be given without h0: the gradient at a zero start)
- *   workspace      ss_ssd_bwd_workspace_size() bytes, 16-byte aligned
- * The SSD recurrence with one group is the selective scan over the heads'
- * columns with tied parameters, and this call runs the selective-scan
- * backward (f32 inside) on that layout and sums the tied gradients per
- * head in a fixed order; with several groups it runs once per (batch entry,
- * group).  Exact and deterministic, but not the chunked matrix-core form.
+ *   workspace      ss_ssd_bwd_workspace_size() bytes, 16-byte aligned; it holds
+ *                  the state entering every chunk of 64 steps (f32), the
+ *                  per-head dB / dC terms (f32) and per-step partials, about
+ *                  4 * batch * nheads * ceil(seqlen / 64) * 64 * dstate *
+ *                  (headdim / 64 + 2) bytes
+ * The gradients are taken in the same chunked form as the forward
+ * (back-propagation through time regrouped by chunk, on bf16 matrix cores
+ * with f32 accumulation): a states pass, one reverse pass per (batch, head)
+ * carrying the state's adjoint, then the suffix sums that give ddt and dA,
+ * and the sums of dB, dC over each group's heads.  Every sum runs in a fixed
+ * order: results are deterministic and do not depend on the batch size.
  */
 ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                      int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,

@@ -166,8 +166,12 @@ struct SsdParams {
     const float *h0;
     void *out;
     float *last_state;
+    // states pass only: H_in of every chunk of 64 steps, (batch, head,
+    // chunk, dstate, headdim) f32
+    float *states;
 };
 hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream);
+hipError_t launch_ssd_states(const SsdParams &p, hipStream_t stream);
 
 // Mamba-2 SSD backward (through the selective-scan backward).  dout, dx:
 // (batch, L, nheads, headdim) bf16; ddt: (batch, L, nheads) bf16; dB, dC:

@@ -43,16 +43,13 @@
 
 #include "ss_device.h"
 #include "ss_kernels.h"
+#include "ss_mfma.h"
 #include "ss_tiles.h"
 
 namespace ssk {
 namespace {
 
 constexpr int kQ = 64;  // chunk length
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int N, int P>
 struct SsdSmem {
@@ -65,31 +62,14 @@ struct SsdSmem {
     static constexpr uint32_t kCum = kXT + P * kPT * 2;  // f32 [kQ]
     static constexpr uint32_t kDt = kCum + kQ * 4;       // f32 [kQ]
     static constexpr uint32_t kW = kDt + kQ * 4;         // f32 [kQ]: exp(cum_last - cum_s) dt_s
+    static constexpr uint32_t kCumLo = kW + kQ * 4;      // f32 [kQ]: low part of the running sum
     static constexpr int kPY = P + 8;                     // row pitch of the output tile (bf16)
-    static constexpr uint32_t kYs = kW + kQ * 4;          // bf16 [kQ][kPY]: the chunk's output
+    static constexpr uint32_t kYs = kCumLo + kQ * 4;      // bf16 [kQ][kPY]: the chunk's output
     // state exchange, per chunk parity: [column tile][state tile][lane] x 16 bytes
     static constexpr uint32_t kHx = kYs + kQ * kPY * 2;
     static constexpr uint32_t kHxPar = (P / 16) * (N / 16) * 64 * 16;
     static constexpr uint32_t kSize = kHx + 2 * kHxPar;
 };
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma32(bf16x8_t a, bf16x8_t b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ short bfs(float v) { return static_cast<short>(f32_to_bf16(v)); }
-
-// v = hi + lo with hi = bfs(v) and lo = lo_bf(v, hi): the part of v that
-// one bf16 misses, in a second bf16
-__device__ __forceinline__ short lo_bf(float v, short hi) {
-    return bfs(v - bf16_to_f32(static_cast<bf16_t>(hi)));
-}
 
 // N: dstate (multiple of 32, <= 128); P: headdim (multiple of 16, <= 64).
 // Two wavefronts per 16-column tile q: wavefront (q, hf) computes the
@@ -98,7 +78,13 @@ __device__ __forceinline__ short lo_bf(float v, short hi) {
 // hf N / 32 .. (hf + 1) N / 32 - 1.  C H^T needs all state tiles, so after
 // each chunk's update the wavefronts publish their state (as the bf16
 // hi/lo operands) in an LDS exchange buffer, double-buffered by chunk.
-template <int N, int P>
+//
+// kStates: the states pass of the backward.  Only the recurrence runs (no
+// output, no C H_in, no W X): at the start of chunk c each wavefront stores
+// its state tiles as H_in[c] to p.states, (batch, head, chunk) blocks of a
+// dstate x headdim f32 matrix (headdim contiguous).  Its wavefronts need
+// no state exchange.
+template <int N, int P, bool kStates>
 __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     constexpr int kCT = P / 16;                      // column tiles
     constexpr int kWaves = 2 * kCT, kThr = 64 * kWaves;
@@ -114,6 +100,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     bf16_t *BT = reinterpret_cast<bf16_t *>(smem + SM::kBT);
     bf16_t *XT = reinterpret_cast<bf16_t *>(smem + SM::kXT);
     float *cum = reinterpret_cast<float *>(smem + SM::kCum);
+    float *cumlo = reinterpret_cast<float *>(smem + SM::kCumLo);
     float *dts = reinterpret_cast<float *>(smem + SM::kDt);
     float *wts = reinterpret_cast<float *>(smem + SM::kW);
     bf16_t *Ys = reinterpret_cast<bf16_t *>(smem + SM::kYs);
@@ -172,7 +159,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
             e[1] = lo;
         }
     };
-    publish(0);
+    if constexpr (!kStates) publish(0);
 
     // the next chunk, in registers
     u32x4 rb[kBV], rc[kBV], rx;
@@ -189,7 +176,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 const int s = v % kQ, c8 = v / kQ;
                 const int64_t t = c0 + s < L ? c0 + s : L - 1;
                 rb[k] = ld_global16(Bg + t * brow + 8 * c8);
-                rc[k] = ld_global16(Cg + t * brow + 8 * c8);
+                if constexpr (!kStates) rc[k] = ld_global16(Cg + t * brow + 8 * c8);
             }
         }
         {
@@ -210,10 +197,14 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
             if (v < kVB) {
                 const int s = v % kQ, c8 = v / kQ;
                 const bool live = c0 + s < L;
-                u32x4 vb = rb[k], vc = rc[k];
-                if (!live) vb = vc = u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(Bs + s * SM::kPB + 8 * c8) = vb;
-                *reinterpret_cast<u32x4 *>(Cs + s * SM::kPB + 8 * c8) = vc;
+                u32x4 vb = rb[k];
+                if (!live) vb = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (!kStates) {
+                    u32x4 vc = rc[k];
+                    if (!live) vc = u32x4{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(Bs + s * SM::kPB + 8 * c8) = vb;
+                    *reinterpret_cast<u32x4 *>(Cs + s * SM::kPB + 8 * c8) = vc;
+                }
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     BT[(8 * c8 + 2 * e) * SM::kPT + s] = bf16_t(vb[e] & 0xffffu);
@@ -237,16 +228,13 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 dv = bf_lo(rdt & 0xffffu) + bias;
                 if (p.softplus) dv = softplus_f32(dv);
             }
-            float a = dv * a2;   // base-2 exponent units
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(a, off, 64);
-                if (lane >= off) a += o;
-            }
-            const float total = __shfl(a, 63, 64);
+            float a, alo;   // running sum of dt A in base-2 exponent units, hi + lo
+            running_sum2(dv * a2, lane, a, alo);
+            const float total = __shfl(a, 63, 64), tlo = __shfl(alo, 63, 64);
             cum[tid] = a;
+            cumlo[tid] = alo;
             dts[tid] = dv;
-            wts[tid] = exp2_hw(total - a) * dv;
+            wts[tid] = exp2_hw((total - a) + (tlo - alo)) * dv;
         }
     };
 
@@ -255,6 +243,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     auto chunk = [&](auto hfc, int par) {
         constexpr int HF = decltype(hfc)::value;
         constexpr int kT[2] = {HF ? 1 : 0, HF ? 2 : 3};
+        if constexpr (!kStates) {
         // C H_in, from every state tile: the 16x16x32 product runs over state
         // tiles 2 m2 and 2 m2 + 1 at once, its k index over (tile, 4 lg + r)
         // in the order the state accumulators hold them, and C is read in
@@ -299,17 +288,19 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 acc = mfma32(a, hbl[m2], acc);
             }
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[r] *= exp2_hw(cum[16 * i + 4 * lg + r]);
+            for (int r = 0; r < 4; r++)
+                acc[r] *= exp2_hw(cum[16 * i + 4 * lg + r] + cumlo[16 * i + 4 * lg + r]);
             Y[ii] = acc;
         }
         // the chunk's own part: W = G . exp(cum_t - cum_s) dt_s (s <= t),
         // Y += W x.  This lane's s are 16 j + 4 lg + r and its t 16 i + li.
-        f32x4 cs[4], ds[4];
+        f32x4 cs[4], csl[4], ds[4];
         s16x4 xb[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             if (j > kT[1]) break;
             cs[j] = *reinterpret_cast<const f32x4 *>(cum + 16 * j + 4 * lg);
+            csl[j] = *reinterpret_cast<const f32x4 *>(cumlo + 16 * j + 4 * lg);
             ds[j] = *reinterpret_cast<const f32x4 *>(dts + 16 * j + 4 * lg);
             xb[j] = *reinterpret_cast<const s16x4 *>(XT + col * SM::kPT + 16 * j + 4 * lg);
         }
@@ -317,7 +308,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         for (int ii = 0; ii < 2; ii++) {
             const int i = kT[ii];
             const int t = 16 * i + li;
-            const float ct = cum[t];
+            const float ct = cum[t], ctl = cumlo[t];
             bf16x8_t cb[N / 32];
 #pragma unroll
             for (int k = 0; k < N / 32; k++)
@@ -334,7 +325,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 s16x4 wh, wl;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    float wvv = gt[r] * exp2_hw(ct - cs[j][r]) * ds[j][r];
+                    float wvv = gt[r] * exp2_hw((ct - cs[j][r]) + (ctl - csl[j][r])) * ds[j][r];
                     // below the diagonal s < t always; on it keep s <= t (a
                     // select: both sides are computed, no branch)
                     if (j == i) wvv = (4 * lg + r <= li) ? wvv : 0.0f;
@@ -357,8 +348,9 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 Ys[t * SM::kPY + col] = f32_to_bf16(Y[ii][r] + dskip * xv);
             }
         }
+        }  // !kStates
         // this wavefront's state tiles: H_out = exp(cum_last) H_in + B^T (w x)
-        const float decay = exp2_hw(cum[kQ - 1]);
+        const float decay = exp2_hw(cum[kQ - 1] + cumlo[kQ - 1]);
         bf16x8_t xsh[2], xsl[2];
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {
@@ -394,15 +386,25 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     for (int64_t c = 0; c < nch; c++) {
         const int64_t c0 = c * kQ;
         if (c + 1 < nch) load_chunk(c0 + kQ);
+        if constexpr (kStates) {
+            // H_in of this chunk: lane holds H^T[n][col], 16 lanes one row piece
+            float *st = p.states + (((b * H + h) * nch + c) * N) * P + col;
+#pragma unroll
+            for (int mm = 0; mm < kNH; mm++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) st[(16 * (m0 + mm) + 4 * lg + r) * P] = Hs[mm][r];
+        }
         const int par = int(c & 1);
         if (hf) chunk(std::integral_constant<int, 1>{}, par);
         else chunk(std::integral_constant<int, 0>{}, par);
+        if constexpr (!kStates) {
         // the new state for the next chunk's C H_in (the other buffer: its
         // last readers were the previous chunk's, behind the last barrier)
         publish(par ^ 1);
+        }
         __syncthreads();
         // the chunk's output rows: 16-byte stores, P / 8 lanes per row
-        {
+        if constexpr (!kStates) {
             const int t = tid / (P / 8), c8 = tid % (P / 8);
             if (c0 + t < L)
                 st_global16(yg + (c0 + t) * xrow + 8 * c8,
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         __syncthreads();
     }
 
-    if (p.last_state) {
+    if (!kStates && p.last_state) {
         float *ls = p.last_state + ((b * H + h) * P + col) * N;
 #pragma unroll
         for (int mm = 0; mm < kNH; mm++)
@@ -420,33 +422,42 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     }
 }
 
-template <int N>
+template <int N, bool kStates>
 hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.batch * p.nheads));
     switch (p.headdim) {
-        case 16: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 16>), grid, dim3(128), 0, stream, p); break;
-        case 32: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 32>), grid, dim3(256), 0, stream, p); break;
-        case 48: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 48>), grid, dim3(384), 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 64>), grid, dim3(512), 0, stream, p); break;
+        case 16: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 16, kStates>), grid, dim3(128), 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 32, kStates>), grid, dim3(256), 0, stream, p); break;
+        case 48: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 48, kStates>), grid, dim3(384), 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((ss_ssd_fwd_kernel<N, 64, kStates>), grid, dim3(512), 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipSuccess;
 }
 
-}  // namespace
-
-hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream) {
+template <bool kStates>
+hipError_t launch_any(const SsdParams &p, hipStream_t stream) {
     if (p.batch == 0 || p.nheads == 0) return hipSuccess;
     hipError_t e;
     switch (p.dstate) {
-        case 32: e = launch_n<32>(p, stream); break;
-        case 64: e = launch_n<64>(p, stream); break;
-        case 96: e = launch_n<96>(p, stream); break;
-        case 128: e = launch_n<128>(p, stream); break;
+        case 32: e = launch_n<32, kStates>(p, stream); break;
+        case 64: e = launch_n<64, kStates>(p, stream); break;
+        case 96: e = launch_n<96, kStates>(p, stream); break;
+        case 128: e = launch_n<128, kStates>(p, stream); break;
         default: return hipErrorInvalidValue;
     }
     profile_mark(stream);
     return e != hipSuccess ? e : hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream) {
+    return launch_any<false>(p, stream);
+}
+
+hipError_t launch_ssd_states(const SsdParams &p, hipStream_t stream) {
+    return launch_any<true>(p, stream);
 }
 
 }  // namespace ssk

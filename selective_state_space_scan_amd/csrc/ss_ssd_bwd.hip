@@ -1,246 +1,908 @@
-// ss_ssd_bwd.hip -- Mamba-2 SSD backward through the selective-scan backward.
+// ss_ssd_bwd.hip -- Mamba-2 SSD backward in chunked form on gfx950 matrix cores.
 //
-// With one group, the SSD recurrence of a head (a headdim x d_state state,
-// scalar A, shared dt, B and C) is exactly the selective scan of the
-// state-spaces/mamba README ("Usage / Selective SSM") over headdim
-// channels with tied parameters: channel (h, p) has u = x[.., h, p],
-// delta = dt[.., h], A[(h, p), n] = A[h], D = D[h], and B, C those of the
-// group.  The backward therefore runs the selective-scan backward kernels
-// (ss_bwd.hip, f32 inside) on the SSD tensors laid out as its
-// (channel, time) rows, and sums the tied gradients back per head:
-//   dx = du,  ddt[t, h] = sum_p ddelta[(h, p), t],
-//   dA[h] = sum_{p,n} dA[(h, p), n],  dD[h] = sum_p dD,  ddt_bias[h] = sum_p.
-// dB, dC, dh0 come out directly (h0 / dh0 have the same layout in both).
+// The forward (ss_ssd.hip; the SSD module that the state-spaces/mamba README
+// names under "Mamba-2") is, per batch b and head h, with dt_t after bias and
+// softplus, a_t = dt_t A[h] and cum_t the running sum of a over a chunk of
+// kQ = 64 steps,
+//   y_t   = exp(cum_t) H_in C_t + sum_{s<=t} exp(cum_t - cum_s) (C_t . B_s) dt_s x_s + D x_t
+//   H_out = exp(cum_last) H_in  + sum_s exp(cum_last - cum_s) dt_s x_s B_s^T.
+// Back-propagation through time, regrouped by chunk.  With dH = dL/dH_out
+// of the chunk, L_ts = exp(cum_t - cum_s) (s <= t, else 0), G_ts = C_t . B_s,
+// M_ts = dy_t . x_s, wB_s = exp(cum_last - cum_s):
+//   dx_s   = sum_t G_ts L_ts dt_s dy_t + dt_s wB_s dH B_s + D dy_s
+//   dC_t   = sum_s (M_ts L_ts dt_s) B_s + exp(cum_t) H_in^T dy_t
+//   dB_s   = sum_t (M_ts L_ts dt_s) C_t + dt_s wB_s dH^T x_s
+//   dH_in  = exp(cum_last) dH + sum_t exp(cum_t) dy_t C_t^T
+// and, through dt directly (u) and through the running sums (v, the
+// gradient w.r.t. cum_t; the gradient w.r.t. a_s is then sum_{t>=s} v_t):
+//   u_s = sum_t G_ts L_ts M_ts + q_s,  q_s = wB_s x_s^T dH B_s
+//   v_t = sum_s G_ts L_ts M_ts dt_s - dt_t u_t + exp(cum_t) dy_t^T H_in C_t
+//         (+ exp(cum_last) <dH, H_in> + sum_s dt_s q_s at the last step)
+//   d(dt_s) = u_s + A sum_{t>=s} v_t,  dA = sum_s dt_s sum_{t>=s} v_t.
 //
-// This is exact but not the chunked (matrix-core) form: it moves each
-// element between layouts and runs the sequential per-state scan, so it is
-// several times slower than the forward.  Several groups run one call per
-// (batch entry, group).
+// Kernels, in order:
+//   1. states pass (ss_ssd.hip): H_in of every chunk, f32, to the workspace;
+//   2. ss_ssd_bwd_kernel: one workgroup per (batch, head) walks the chunks
+//      last to first with dH in matrix-core accumulators; writes dx, the
+//      head's dB and dC terms (f32, per head), u and v per step, and dh0;
+//   3. ssd_bwd_dt_kernel: per chunk, the suffix sums of v, ddt, and the
+//      chunk's dA and ddt_bias terms;
+//   4. ssd_bwd_fold_kernel: dB and dC summed over the heads of a group;
+//   5. ssd_bwd_param_kernel: dA, dD, ddt_bias summed over batch and chunks.
+// Every sum runs in a fixed order: results are bit-reproducible and do not
+// depend on the batch size.
+//
+// Rounding: x, dy, B, C are bf16 already.  Operands made on chip (the W and
+// dGm tiles, H_in, dH, exp(cum) dy) are split into a bf16 high and low part
+// and multiplied as two products, as in the forward; sums are f32.  dA is
+// the exception that needs more: it is a sum over the chunk of suffix sums
+// in which large terms cancel.  So the running sums of dt A are carried as
+// compensated hi + lo pairs, the per-step sums that build v (and dA itself)
+// are f64, and dH and H_in enter the products behind q and r in three bf16
+// parts (2^-27).
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_kernels.h"
+#include "ss_mfma.h"
 #include "ss_tiles.h"
 
 namespace ssk {
 namespace {
 
-constexpr int kTile = 64;
+constexpr int kQ = 64;  // chunk length
+constexpr int kWaves = 8, kThr = 64 * kWaves;
 
-// dst (nb, cw, L) f32  <-  src (nb, L, ctot) bf16, columns c0 .. c0 + cw - 1
-__global__ __launch_bounds__(256) void rows_from_time_major(const bf16_t *src, int64_t ctot,
-                                                            int64_t c0, int64_t cw, int64_t L,
-                                                            float *dst) {
-    __shared__ float tile[kTile][kTile + 1];
-    const int64_t b = blockIdx.z;
-    const int64_t t0 = int64_t(blockIdx.x) * kTile, k0 = int64_t(blockIdx.y) * kTile;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    // read: consecutive threads take consecutive columns of one time step
-    for (int r = ty; r < kTile; r += 4) {
-        const int64_t t = t0 + r, c = k0 + tx;
-        float v = 0.0f;
-        if (t < L && c < cw) v = bf16_to_f32(src[(b * L + t) * ctot + c0 + c]);
-        tile[r][tx] = v;
-    }
-    __syncthreads();
-    // write: consecutive threads take consecutive time steps of one column
-    for (int r = ty; r < kTile; r += 4) {
-        const int64_t c = k0 + r, t = t0 + tx;
-        if (t < L && c < cw) dst[(b * cw + c) * L + t] = tile[tx][r];
-    }
-}
-
-// dst (nb, L, ctot) bf16, columns c0 .. c0 + cw - 1  <-  src (nb, cw, L) f32
-__global__ __launch_bounds__(256) void time_major_from_rows(const float *src, int64_t ctot,
-                                                            int64_t c0, int64_t cw, int64_t L,
-                                                            bf16_t *dst) {
-    __shared__ float tile[kTile][kTile + 1];
-    const int64_t b = blockIdx.z;
-    const int64_t t0 = int64_t(blockIdx.x) * kTile, k0 = int64_t(blockIdx.y) * kTile;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int r = ty; r < kTile; r += 4) {
-        const int64_t c = k0 + r, t = t0 + tx;
-        float v = 0.0f;
-        if (t < L && c < cw) v = src[(b * cw + c) * L + t];
-        tile[r][tx] = v;
-    }
-    __syncthreads();
-    for (int r = ty; r < kTile; r += 4) {
-        const int64_t t = t0 + r, c = k0 + tx;
-        if (t < L && c < cw) dst[(b * L + t) * ctot + c0 + c] = f32_to_bf16(tile[tx][r]);
-    }
-}
-
-// delta rows (nb, nhg * P, L) f32 from dt (nb, L, H) bf16, heads h0 .. h0 + nhg - 1
-__global__ __launch_bounds__(256) void delta_rows(const bf16_t *dt, int64_t H, int64_t h0,
-                                                  int64_t nhg, int64_t P, int64_t L, int64_t nb,
-                                                  float *dst) {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t total = nb * nhg * P * L;
-    if (i >= total) return;
-    const int64_t t = i % L, rest = i / L;
-    const int64_t c = rest % (nhg * P), b = rest / (nhg * P);
-    dst[i] = bf16_to_f32(dt[(b * L + t) * H + h0 + c / P]);
-}
-
-// ddt (nb, L, H) bf16, heads h0 .. h0 + nhg - 1  <-  sum over p of ddelta rows
-__global__ __launch_bounds__(256) void ddt_from_rows(const float *dd, int64_t H, int64_t h0,
-                                                     int64_t nhg, int64_t P, int64_t L,
-                                                     int64_t nb, bf16_t *ddt) {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= nb * nhg * L) return;
-    const int64_t t = i % L, rest = i / L;
-    const int64_t hh = rest % nhg, b = rest / nhg;
-    const float *src = dd + ((b * nhg + hh) * P) * L + t;
-    float s = 0.0f;
-    for (int64_t pp = 0; pp < P; pp++) s += src[pp * L];
-    ddt[(b * L + t) * H + h0 + hh] = f32_to_bf16(s);
-}
-
-// the tied per-channel parameters of heads h0 .. h0 + nhg - 1
-__global__ __launch_bounds__(256) void expand_params(const float *A, const float *D,
-                                                     const float *bias, int64_t h0, int64_t nhg,
-                                                     int64_t P, int64_t N, float *As, float *Ds,
-                                                     float *bs) {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= nhg * P * N) return;
-    const int64_t c = i / N, h = h0 + c / P;
-    As[i] = A[h];
-    if (i % N == 0) {
-        if (D) Ds[c] = D[h];
-        if (bias) bs[c] = bias[h];
-    }
-}
-
-// dA[h] (+)= sum_{p,n}, dD[h], ddt_bias[h] (+)= sum_p, in ascending order
-__global__ __launch_bounds__(256) void reduce_params(const float *dAs, const float *dDs,
-                                                     const float *dbs, int64_t h0, int64_t nhg,
-                                                     int64_t P, int64_t N, int accumulate,
-                                                     float *dA, float *dD, float *dbias) {
-    const int64_t hh = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (hh >= nhg) return;
-    float sa = 0.0f, sd = 0.0f, sb = 0.0f;
-    for (int64_t pp = 0; pp < P; pp++) {
-        const int64_t c = hh * P + pp;
-        for (int64_t n = 0; n < N; n++) sa += dAs[c * N + n];
-        if (dD) sd += dDs[c];
-        if (dbias) sb += dbs[c];
-    }
-    const int64_t h = h0 + hh;
-    dA[h] = accumulate ? dA[h] + sa : sa;
-    if (dD) dD[h] = accumulate ? dD[h] + sd : sd;
-    if (dbias) dbias[h] = accumulate ? dbias[h] + sb : sb;
-}
-
-// Workspace carve-up for calls over nbc batch entries and nhg heads.
-struct SsdBwdWs {
-    float *u, *delta, *dout, *du, *ddelta, *Bt, *Ct, *dBt, *dCt;
-    float *As, *Ds, *bs, *dAs, *dDs, *dbs;
-    void *s6;
-    size_t s6_bytes;
+struct BwdWs {
+    float *states;     // (batch, head, chunk, dstate, headdim): H_in
+    float *pdB, *pdC;  // (batch, head, chunk, time tile, state tile, lane, 4): per-head terms
+    float *u;          // (batch, head, chunk, kQ)
+    double *v;         // (batch, head, chunk, kQ)
+    double *dAp;       // (batch, head, chunk)
+    float *dbp;        // (batch, head, chunk)
+    float *dDp;        // (batch, head)
 };
 
-inline size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
-
-SsdBwdWs carve_ssd(void *base, int64_t nbc, int64_t nhg, int64_t P, int64_t N, int64_t L,
-                   size_t *total) {
-    const int64_t dim = nhg * P;
-    char *p = static_cast<char *>(base);
+BwdWs carve(void *base, int64_t batch, int64_t nheads, int64_t nch, int64_t P, int64_t N,
+            size_t *total) {
+    BwdWs w{};
     size_t off = 0;
-    auto take = [&](size_t floats) {
-        float *r = reinterpret_cast<float *>(p + off);
-        off += a256(floats * sizeof(float));
-        return r;
+    char *b = static_cast<char *>(base);
+    auto take = [&](auto **dst, int64_t count) {
+        using T = std::remove_reference_t<decltype(**dst)>;
+        *dst = base ? reinterpret_cast<T *>(b + off) : nullptr;
+        off += (size_t(count) * sizeof(T) + 255) / 256 * 256;
     };
-    SsdBwdWs w;
-    const size_t E = size_t(nbc) * dim * L, bc = size_t(nbc) * N * L;
-    w.u = take(E); w.delta = take(E); w.dout = take(E); w.du = take(E); w.ddelta = take(E);
-    w.Bt = take(bc); w.Ct = take(bc); w.dBt = take(bc); w.dCt = take(bc);
-    w.As = take(size_t(dim) * N); w.Ds = take(dim); w.bs = take(dim);
-    w.dAs = take(size_t(dim) * N); w.dDs = take(dim); w.dbs = take(dim);
-    w.s6_bytes = bwd_workspace_bytes(nbc, dim, L, int(N));
-    w.s6 = p + off;
-    off += a256(w.s6_bytes);
+    const int64_t bhc = batch * nheads * nch;
+    take(&w.states, bhc * N * P);
+    take(&w.pdB, bhc * kQ * N);
+    take(&w.pdC, bhc * kQ * N);
+    take(&w.u, bhc * kQ);
+    take(&w.v, bhc * kQ);
+    take(&w.dAp, bhc);
+    take(&w.dbp, bhc);
+    take(&w.dDp, batch * nheads);
     if (total) *total = off;
     return w;
 }
 
-dim3 tgrid(int64_t L, int64_t cw, int64_t nb) {
-    return dim3(unsigned((L + kTile - 1) / kTile), unsigned((cw + kTile - 1) / kTile), unsigned(nb));
+template <int N, int P>
+struct BwdSmem {
+    static constexpr int kPB = N + 8;   // row pitch of B, C (bf16)
+    static constexpr int kPT = kQ + 8;  // row pitch of B^T, C^T, dy^T (bf16)
+    static constexpr int kPX = P + 8;   // row pitch of x, dy, dx (bf16)
+    static constexpr int kPH = P + 4;   // row pitch of dH stored [n][p] (f32)
+    static constexpr uint32_t kBs = 0;
+    static constexpr uint32_t kCs = kBs + kQ * kPB * 2;
+    static constexpr uint32_t kBT = kCs + kQ * kPB * 2;
+    static constexpr uint32_t kCT = kBT + N * kPT * 2;
+    static constexpr uint32_t kXs = kCT + N * kPT * 2;
+    static constexpr uint32_t kYs = kXs + kQ * kPX * 2;
+    static constexpr uint32_t kYT = kYs + kQ * kPX * 2;
+    static constexpr uint32_t kHf = kYT + P * kPT * 2;   // f32 [N][kPH]: dH of the chunk's end
+    static constexpr uint32_t kDX = kHf + N * kPH * 4;
+    static constexpr uint32_t kCum = kDX + kQ * kPX * 2;  // f32: running sum of dt A, base 2
+    static constexpr uint32_t kDt = kCum + kQ * 4;        // f32: dt
+    static constexpr uint32_t kEc = kDt + kQ * 4;         // f32: exp(cum_t)
+    static constexpr uint32_t kWb = kEc + kQ * 4;         // f32: exp(cum_last - cum_s)
+    static constexpr uint32_t kUg = kWb + kQ * 4;         // f64 [2][kQ]: sum_t G L M per class
+    static constexpr uint32_t kVr = kUg + 2 * kQ * 8;     // f64 [2][kQ]: sum_s G L M dt_s per class
+    static constexpr uint32_t kQa = kVr + 2 * kQ * 8;     // f32 [8][kQ]: q terms per wavefront
+    static constexpr uint32_t kRa = kQa + 8 * kQ * 4;     // f32 [8][kQ]: H_in terms per wavefront
+    static constexpr uint32_t kHd = kRa + 8 * kQ * 4;     // f32 [8]: <dH, H_in> per wavefront
+    static constexpr uint32_t kCumLo = kHd + 8 * 4;       // f32: low part of the running sum
+    static constexpr uint32_t kSize = kCumLo + kQ * 4;
+};
+
+__device__ __forceinline__ float sum16(float v) {   // over the 16 lanes of a row
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    return v;
 }
-dim3 lgrid(int64_t n) { return dim3(unsigned((n + 255) / 256)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = sum16(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+__device__ __forceinline__ double sum16d(double v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sumd(double v) {
+    v = sum16d(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+__device__ __forceinline__ double pick4d(const double (&v)[4], int k) {
+    return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
+}
+
+__device__ __forceinline__ float pick4(const float (&v)[4], int k) {
+    return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
+}
+
+// One workgroup of 8 wavefronts per (batch, head).  Wavefront wv = 2 sg + cls.
+// Class cls owns time tiles {0, 3} (cls 0) or {1, 2} (cls 1) -- as s tiles of
+// the dx and dB products and as t tiles of the dC product, five of the ten
+// lower-triangle tiles each -- and sg splits the columns: dx column tile sg,
+// state tiles sg, sg + 4.  The carried dH^T tiles k = wv + 8 kk (state tile
+// k / (P / 16), column tile k % (P / 16)) are spread over all wavefronts and
+// published in LDS as [state][column] bf16 high and low parts each chunk.
+template <int N, int P>
+__global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs ws) {
+    constexpr int kCT = P / 16, kNT = N / 16;
+    constexpr int kVB = kQ * N / 8;                      // 16-byte vectors of a B (or C) chunk
+    constexpr int kBV = (kVB + kThr - 1) / kThr;
+    constexpr int kVX = kQ * P / 8;                      // 16-byte vectors of an x (or dy) chunk
+    static_assert(kVX <= kThr, "one x vector per thread at most");
+    constexpr int kDH = (kNT * kCT + kWaves - 1) / kWaves;   // dH tiles per wavefront
+    constexpr int kNS = (kNT + 3) / 4;                   // state tiles per wavefront
+    using SM = BwdSmem<N, P>;
+    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
+    bf16_t *Bs = reinterpret_cast<bf16_t *>(smem + SM::kBs);
+    bf16_t *Cs = reinterpret_cast<bf16_t *>(smem + SM::kCs);
+    bf16_t *BT = reinterpret_cast<bf16_t *>(smem + SM::kBT);
+    bf16_t *CT = reinterpret_cast<bf16_t *>(smem + SM::kCT);
+    bf16_t *Xs = reinterpret_cast<bf16_t *>(smem + SM::kXs);
+    bf16_t *Ys = reinterpret_cast<bf16_t *>(smem + SM::kYs);
+    bf16_t *YT = reinterpret_cast<bf16_t *>(smem + SM::kYT);
+    float *Hf = reinterpret_cast<float *>(smem + SM::kHf);
+    bf16_t *DX = reinterpret_cast<bf16_t *>(smem + SM::kDX);
+    float *cum = reinterpret_cast<float *>(smem + SM::kCum);
+    float *cumlo = reinterpret_cast<float *>(smem + SM::kCumLo);
+    float *dts = reinterpret_cast<float *>(smem + SM::kDt);
+    float *ecum = reinterpret_cast<float *>(smem + SM::kEc);
+    float *wbs = reinterpret_cast<float *>(smem + SM::kWb);
+    double *Ug = reinterpret_cast<double *>(smem + SM::kUg);
+    double *Vr = reinterpret_cast<double *>(smem + SM::kVr);
+    float *Qa = reinterpret_cast<float *>(smem + SM::kQa);
+    float *Ra = reinterpret_cast<float *>(smem + SM::kRa);
+    float *Hd = reinterpret_cast<float *>(smem + SM::kHd);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int cls = wv & 1, sg = wv >> 1;
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t H = p.nheads, G = p.ngroups, L = p.seqlen;
+    const int64_t b = blockIdx.x % p.batch, h = blockIdx.x / p.batch;
+    const int64_t g = h / (H / G), bh = b * H + h;
+    const int64_t nch = (L + kQ - 1) / kQ;
+    const float a2 = p.A[h] * kLog2e;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float dskip = p.D ? p.D[h] : 0.0f;
+    const int64_t xrow = H * P, brow = G * N;
+    const bf16_t *xg = static_cast<const bf16_t *>(p.x) + (b * L * H + h) * P;
+    const bf16_t *yg = static_cast<const bf16_t *>(p.dout) + (b * L * H + h) * P;
+    const bf16_t *dtg = static_cast<const bf16_t *>(p.dt) + b * L * H + h;
+    const bf16_t *Bg = static_cast<const bf16_t *>(p.B) + (b * L * G + g) * N;
+    const bf16_t *Cg = static_cast<const bf16_t *>(p.C) + (b * L * G + g) * N;
+    bf16_t *dxg = static_cast<bf16_t *>(p.dx) + (b * L * H + h) * P;
+    const float *hin_g = ws.states + bh * nch * N * P;
+    float *pdB = ws.pdB + bh * nch * kQ * N, *pdC = ws.pdC + bh * nch * kQ * N;
+    float *ug = ws.u + bh * nch * kQ;
+    double *vg = ws.v + bh * nch * kQ;
+
+    // carried dH^T tiles: lane holds dH^T[n = 16 nt + 4 lg + r][p = 16 q + li]
+    f32x4 dH[kDH];
+#pragma unroll
+    for (int kk = 0; kk < kDH; kk++) {
+        const int k = wv + kWaves * kk;
+        dH[kk] = kZero4;
+        if (k < kNT * kCT && p.dlast) {
+            const int nt = k / kCT, q = k % kCT;
+            dH[kk] = *reinterpret_cast<const f32x4 *>(p.dlast + (bh * P + 16 * q + li) * N +
+                                                     16 * nt + 4 * lg);
+        }
+    }
+    auto publish = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < kDH; kk++) {
+            const int k = wv + kWaves * kk;
+            if (k < kNT * kCT) {
+                const int nt = k / kCT, q = k % kCT;
+#pragma unroll
+                for (int r = 0; r < 4; r++) Hf[(16 * nt + 4 * lg + r) * SM::kPH + 16 * q + li] = dH[kk][r];
+            }
+        }
+    };
+
+    // the next chunk (in time: the previous one), in registers
+    u32x4 rb[kBV], rc[kBV], rx = {0u, 0u, 0u, 0u}, ry = {0u, 0u, 0u, 0u};
+    uint32_t rdt = 0;
+    // vector v of a chunk: 8 values of step s = v % kQ from value 8 (v / kQ)
+    // on, so 64 lanes take 64 consecutive steps (conflict-free transposes)
+    auto load_chunk = [&](int64_t c0) {
+#pragma unroll
+        for (int k = 0; k < kBV; k++) {
+            const int v = tid + k * kThr;
+            if (v < kVB) {
+                const int s = v % kQ, c8 = v / kQ;
+                const int64_t t = c0 + s < L ? c0 + s : L - 1;
+                rb[k] = ld_global16(Bg + t * brow + 8 * c8);
+                rc[k] = ld_global16(Cg + t * brow + 8 * c8);
+            }
+        }
+        if (tid < kVX) {
+            const int s = tid % kQ, c8 = tid / kQ;
+            const int64_t t = c0 + s < L ? c0 + s : L - 1;
+            rx = ld_global16(xg + t * xrow + 8 * c8);
+            ry = ld_global16(yg + t * xrow + 8 * c8);
+        }
+        if (tid < kQ) {
+            const int64_t t = c0 + tid < L ? c0 + tid : L - 1;
+            rdt = ld_global(dtg + t * H);
+        }
+    };
+    // registers -> LDS; steps past the end become zeros (no input, no decay)
+    auto stash_chunk = [&](int64_t c0) {
+#pragma unroll
+        for (int k = 0; k < kBV; k++) {
+            const int v = tid + k * kThr;
+            if (v < kVB) {
+                const int s = v % kQ, c8 = v / kQ;
+                const bool live = c0 + s < L;
+                u32x4 vb = rb[k], vc = rc[k];
+                if (!live) vb = vc = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(Bs + s * SM::kPB + 8 * c8) = vb;
+                *reinterpret_cast<u32x4 *>(Cs + s * SM::kPB + 8 * c8) = vc;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    BT[(8 * c8 + 2 * e) * SM::kPT + s] = bf16_t(vb[e] & 0xffffu);
+                    BT[(8 * c8 + 2 * e + 1) * SM::kPT + s] = bf16_t(vb[e] >> 16);
+                    CT[(8 * c8 + 2 * e) * SM::kPT + s] = bf16_t(vc[e] & 0xffffu);
+                    CT[(8 * c8 + 2 * e + 1) * SM::kPT + s] = bf16_t(vc[e] >> 16);
+                }
+            }
+        }
+        if (tid < kVX) {
+            const int s = tid % kQ, c8 = tid / kQ;
+            u32x4 vx = rx, vy = ry;
+            if (!(c0 + s < L)) vx = vy = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(Xs + s * SM::kPX + 8 * c8) = vx;
+            *reinterpret_cast<u32x4 *>(Ys + s * SM::kPX + 8 * c8) = vy;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                YT[(8 * c8 + 2 * e) * SM::kPT + s] = bf16_t(vy[e] & 0xffffu);
+                YT[(8 * c8 + 2 * e + 1) * SM::kPT + s] = bf16_t(vy[e] >> 16);
+            }
+        }
+        if (tid < kQ) {   // wavefront 0: dt, the running sum of dt A and its exponentials
+            float dv = 0.0f;
+            if (c0 + tid < L) {
+                dv = bf_lo(rdt & 0xffffu) + bias;
+                if (p.softplus) dv = softplus_f32(dv);
+            }
+            float a, alo;   // running sum of dt A in base-2 exponent units, hi + lo
+            running_sum2(dv * a2, lane, a, alo);
+            const float total = __shfl(a, 63, 64), tlo = __shfl(alo, 63, 64);
+            cum[tid] = a;
+            cumlo[tid] = alo;
+            dts[tid] = dv;
+            ecum[tid] = exp2_hw(a + alo);
+            wbs[tid] = exp2_hw((total - a) + (tlo - alo));
+        }
+    };
+
+    float dd = 0.0f;   // sum of dy . x over the class tiles' diagonals (sg == 0 wavefronts)
+
+    // One chunk for this wavefront; HF = cls as a compile-time constant.
+    auto chunk = [&](auto hfc, int64_t c) {
+        constexpr int HF = decltype(hfc)::value;
+        constexpr int kT[2] = {HF ? 1 : 0, HF ? 2 : 3};
+        // (t tile, s tile) pairs, s <= t: with the s tile in kT (kPi, kPj) and
+        // with the t tile in kT (kRi, kRj)
+        constexpr int kPi[5] = {HF ? 1 : 0, HF ? 2 : 1, HF ? 3 : 2, HF ? 2 : 3, 3};
+        constexpr int kPj[5] = {HF ? 1 : 0, HF ? 1 : 0, HF ? 1 : 0, HF ? 2 : 0, HF ? 2 : 3};
+        constexpr int kRi[5] = {HF ? 1 : 0, HF ? 1 : 3, HF ? 2 : 3, HF ? 2 : 3, HF ? 2 : 3};
+        constexpr int kRj[5] = {0, HF ? 1 : 0, HF ? 0 : 1, HF ? 1 : 2, HF ? 2 : 3};
+        const float elast = ecum[kQ - 1];
+
+        // ---- dH^T <- exp(cum_last) dH^T + C^T (exp(cum) dy), this wavefront's tiles
+#pragma unroll
+        for (int kk = 0; kk < kDH; kk++) {
+            const int k = wv + kWaves * kk;
+            if (k < kNT * kCT) {
+                const int nt = k / kCT, q = k % kCT;
+                f32x4 acc = dH[kk];
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[r] *= elast;
+#pragma unroll
+                for (int k2 = 0; k2 < kQ / 32; k2++) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(CT + (16 * nt + li) * SM::kPT + 32 * k2 + 8 * lg);
+                    const u32x4 yr = *reinterpret_cast<const u32x4 *>(YT + (16 * q + li) * SM::kPT + 32 * k2 + 8 * lg);
+                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(ecum + 32 * k2 + 8 * lg);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(ecum + 32 * k2 + 8 * lg + 4);
+                    bf16x8_t bh, bl;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const float ev = e < 4 ? e0[e] : e1[e - 4];
+                        const float v = ((e & 1) ? bf_hi(yr[e >> 1]) : bf_lo(yr[e >> 1])) * ev;
+                        const __bf16 hi = static_cast<__bf16>(v);
+                        bh[e] = hi;
+                        bl[e] = static_cast<__bf16>(v - static_cast<float>(hi));
+                    }
+                    acc = mfma32(a, bh, acc);
+                    acc = mfma32(a, bl, acc);
+                }
+                dH[kk] = acc;
+            }
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- the dH parts of dx and dB for s tiles kT (lane: s = 16 j + 4 lg + r):
+        // dx = dt_s wB_s B dH^T + D dy (column tile sg), dB = dt_s wB_s x dH
+        // (state tiles sg + 4 ks), and q_s = wB_s sum_n B[s][n] (x dH)[s][n]
+        const bool has_dx = sg < kCT;
+        f32x4 dxa[2] = {kZero4, kZero4}, dba[2][kNS];
+        if (has_dx) {
+            const int q = sg;
+#pragma unroll
+            for (int k = 0; k < N / 32; k++) {
+                // dH^T[n = 32 k + 8 lg + e][p = 16 q + li]: a column of the [n][p] store
+                bf16x8_t hb, lb;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float v = Hf[(32 * k + 8 * lg + e) * SM::kPH + 16 * q + li];
+                    const __bf16 hi = static_cast<__bf16>(v);
+                    hb[e] = hi;
+                    lb[e] = static_cast<__bf16>(v - static_cast<float>(hi));
+                }
+#pragma unroll
+                for (int jj = 0; jj < 2; jj++) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Bs + (16 * kT[jj] + li) * SM::kPB + 32 * k + 8 * lg);
+                    dxa[jj] = mfma32(a, hb, dxa[jj]);
+                    dxa[jj] = mfma32(a, lb, dxa[jj]);
+                }
+                // one k step of 2-byte column reads at a time (registers)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        float qacc[2][4];
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            const int s0 = 16 * kT[jj] + 4 * lg;
+            const f32x4 dv = *reinterpret_cast<const f32x4 *>(dts + s0);
+            const f32x4 wb = *reinterpret_cast<const f32x4 *>(wbs + s0);
+            if (has_dx) {
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    dxa[jj][r] = dv[r] * wb[r] * dxa[jj][r] +
+                                 dskip * bf16_to_f32(Ys[(s0 + r) * SM::kPX + 16 * sg + li]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r++) qacc[jj][r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < kNS; ks++) {
+                const int nt = sg + 4 * ks;
+                dba[jj][ks] = kZero4;
+                if (nt < kNT) {
+                    f32x4 acc = kZero4;
+#pragma unroll
+                    for (int kk = 0; kk < kCT; kk++) {
+                        // dH[p = 16 kk + 4 lg + e][n = 16 nt + li], in three
+                        // parts: q is summed over the chunk for dA, where
+                        // two-part rounding would show
+                        s16x4 hv, mv, lv;
+                        split4x3(*reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + 16 * kk + 4 * lg),
+                                 hv, mv, lv);
+                        const s16x4 a = *reinterpret_cast<const s16x4 *>(Xs + (16 * kT[jj] + li) * SM::kPX + 16 * kk + 4 * lg);
+                        acc = mfma16(a, hv, acc);
+                        acc = mfma16(a, lv, acc);
+                        acc = mfma16(a, mv, acc);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        qacc[jj][r] += bf16_to_f32(Bs[(s0 + r) * SM::kPB + 16 * nt + li]) * acc[r];
+                        acc[r] *= dv[r] * wb[r];
+                    }
+                    dba[jj][ks] = acc;
+                }
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            float tot[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) tot[r] = sum16(qacc[jj][r]);
+            if (li < 4) Qa[wv * kQ + 16 * kT[jj] + 4 * lg + li] = pick4(tot, li);
+        }
+
+        // ---- (t, s) tile pairs with the s tile in kT, one at a time: G and M
+        // give W = G L dt_s and dGm = M L dt_s, which enter dx += W^T dy and
+        // dB += dGm^T C as A operands.  Lane: t = 16 i + 4 lg + r, s = 16 j + li.
+        // The per-step sums below are f64: the gradient w.r.t. a_s is their
+        // suffix sum, in which the row and column sums largely cancel.
+        double colg[2] = {0.0, 0.0};   // sum_t G L M for s = 16 kT[jj] + li, this lane's t
+        // sum_s G L M dt_s for t = 16 i + 4 lg + li (li < 4), per t tile i
+        double rowv[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int pp = 0; pp < 5; pp++) {
+            const int i = kPi[pp], j = kPj[pp], jj = j == kT[0] ? 0 : 1;
+            f32x4 gacc = kZero4, macc = kZero4;
+#pragma unroll
+            for (int k = 0; k < N / 32; k++) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Cs + (16 * i + li) * SM::kPB + 32 * k + 8 * lg);
+                const bf16x8_t bb = *reinterpret_cast<const bf16x8_t *>(Bs + (16 * j + li) * SM::kPB + 32 * k + 8 * lg);
+                gacc = mfma32(a, bb, gacc);
+            }
+#pragma unroll
+            for (int kk = 0; kk < kCT; kk++) {
+                const s16x4 a = *reinterpret_cast<const s16x4 *>(Ys + (16 * i + li) * SM::kPX + 16 * kk + 4 * lg);
+                const s16x4 bb = *reinterpret_cast<const s16x4 *>(Xs + (16 * j + li) * SM::kPX + 16 * kk + 4 * lg);
+                macc = mfma16(a, bb, macc);
+            }
+            const int s = 16 * j + li;
+            const float cs = cum[s], csl = cumlo[s], dsv = dts[s];
+            const f32x4 ct = *reinterpret_cast<const f32x4 *>(cum + 16 * i + 4 * lg);
+            const f32x4 ctl = *reinterpret_cast<const f32x4 *>(cumlo + 16 * i + 4 * lg);
+            f32x4 w4, d4;
+            double rd[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                float e = exp2_hw((ct[r] - cs) + (ctl[r] - csl));
+                if (i == j) e = (4 * lg + r >= li) ? e : 0.0f;
+                const float gl = gacc[r] * e;
+                w4[r] = gl * dsv;
+                d4[r] = macc[r] * e * dsv;
+                const float glm = gl * macc[r];
+                // S = G L M dt_s enters a row sum here and, as dt_t times
+                // the column sum, the row's own v: exact f64 products, so
+                // that the two cancel as they do in exact arithmetic
+                colg[jj] += static_cast<double>(glm);
+                rd[r] = static_cast<double>(glm) * static_cast<double>(dsv);
+                if (i == j) dd += (4 * lg + r == li) ? macc[r] : 0.0f;
+            }
+            if (sg == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) rd[r] = sum16d(rd[r]);
+                rowv[i] += pick4d(rd, li & 3);
+            }
+            s16x4 wh, wl, mh, ml;
+            split4(w4, wh, wl);
+            split4(d4, mh, ml);
+            if (has_dx) {
+                const s16x4 bop = *reinterpret_cast<const s16x4 *>(YT + (16 * sg + li) * SM::kPT + 16 * i + 4 * lg);
+                dxa[jj] = mfma16(wh, bop, dxa[jj]);
+                dxa[jj] = mfma16(wl, bop, dxa[jj]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < kNS; ks++) {
+                const int nt = sg + 4 * ks;
+                if (nt < kNT) {
+                    const s16x4 bop = *reinterpret_cast<const s16x4 *>(CT + (16 * nt + li) * SM::kPT + 16 * i + 4 * lg);
+                    dba[jj][ks] = mfma16(mh, bop, dba[jj][ks]);
+                    dba[jj][ks] = mfma16(ml, bop, dba[jj][ks]);
+                }
+            }
+            // keep the pairs apart: the scheduler would otherwise start all
+            // five at once and run out of registers
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (sg == 0) {
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                double v = colg[jj];
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                if (lg == 0) Ug[cls * kQ + 16 * kT[jj] + li] = v;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (li < 4) Vr[cls * kQ + 16 * i + 4 * lg + li] = rowv[i];
+        }
+        // dx into the row-staging tile, dB terms to the workspace
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            const int s0 = 16 * kT[jj] + 4 * lg;
+            if (has_dx) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) DX[(s0 + r) * SM::kPX + 16 * sg + li] = f32_to_bf16(dxa[jj][r]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < kNS; ks++) {
+                const int nt = sg + 4 * ks;
+                if (nt < kNT)
+                    *reinterpret_cast<f32x4 *>(pdB + ((c * 4 + kT[jj]) * kNT + nt) * 256 + lane * 4) = dba[jj][ks];
+            }
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        // H_in of this chunk as the B operand of dy H_in: hin[ks][kk][e] = H_in[p = 16 kk + 4 lg + e][n = 16 (sg + 4 ks) + li]
+        f32x4 hin[kNS][kCT];
+        {
+            const float *hs = hin_g + c * N * P;
+#pragma unroll
+            for (int ks = 0; ks < kNS; ks++) {
+                const int nt = sg + 4 * ks;
+#pragma unroll
+                for (int kk = 0; kk < kCT; kk++)
+                    hin[ks][kk] = nt < kNT ? *reinterpret_cast<const f32x4 *>(hs + (16 * nt + li) * P + 16 * kk + 4 * lg)
+                                           : kZero4;
+            }
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- dC for t tiles kT, state tiles sg + 4 ks (lane: t = 16 i + 4 lg + r,
+        // n = 16 nt + li): first exp(cum_t) dy H_in and r_t = exp(cum_t) sum_n C (dy H_in)
+        f32x4 dca[2][kNS];
+        float racc[2][4];
+        float hdot = 0.0f;   // <dH, H_in> over this wavefront's (n, p) (class 0)
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) racc[ii][r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kNS; ks++) {
+            const int nt = sg + 4 * ks;
+            s16x4 hh4[kCT], hm4[kCT], hl4[kCT];
+#pragma unroll
+            for (int kk = 0; kk < kCT; kk++) {
+                split4x3(hin[ks][kk], hh4[kk], hm4[kk], hl4[kk]);
+                if (HF == 0 && nt < kNT) {
+                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + 16 * kk + 4 * lg);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) hdot += hin[ks][kk][e] * dv[e];
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < 2; ii++) {
+                const int i = kT[ii];
+                dca[ii][ks] = kZero4;
+                if (nt < kNT) {
+                    f32x4 acc = kZero4;
+#pragma unroll
+                    for (int kk = 0; kk < kCT; kk++) {
+                        const s16x4 a = *reinterpret_cast<const s16x4 *>(Ys + (16 * i + li) * SM::kPX + 16 * kk + 4 * lg);
+                        acc = mfma16(a, hh4[kk], acc);
+                        acc = mfma16(a, hm4[kk], acc);
+                        acc = mfma16(a, hl4[kk], acc);
+                    }
+                    const int t0 = 16 * i + 4 * lg;
+                    const f32x4 ec = *reinterpret_cast<const f32x4 *>(ecum + t0);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        racc[ii][r] += bf16_to_f32(Cs[(t0 + r) * SM::kPB + 16 * nt + li]) * acc[r];
+                        acc[r] *= ec[r];
+                    }
+                    dca[ii][ks] = acc;
+                }
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++) {
+            float tot[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) tot[r] = sum16(racc[ii][r]);
+            if (li < 4) Ra[wv * kQ + 16 * kT[ii] + 4 * lg + li] = pick4(tot, li);
+        }
+        if (HF == 0) {
+            hdot = wave_sum(hdot);
+            if (lane == 0) Hd[wv] = hdot;
+        }
+        // then the (s, t) tile pairs with the t tile in kT, one at a time:
+        // dGm^T = M^T L dt_s (lane: s = 16 j + 4 lg + r, t = 16 i + li) enters
+        // dC += dGm B as the A operand
+#pragma unroll
+        for (int pp = 0; pp < 5; pp++) {
+            const int i = kRi[pp], j = kRj[pp], ii = i == kT[0] ? 0 : 1;
+            f32x4 macc = kZero4;
+#pragma unroll
+            for (int kk = 0; kk < kCT; kk++) {
+                const s16x4 a = *reinterpret_cast<const s16x4 *>(Xs + (16 * j + li) * SM::kPX + 16 * kk + 4 * lg);
+                const s16x4 bb = *reinterpret_cast<const s16x4 *>(Ys + (16 * i + li) * SM::kPX + 16 * kk + 4 * lg);
+                macc = mfma16(a, bb, macc);
+            }
+            const float ctv = cum[16 * i + li], ctvl = cumlo[16 * i + li];
+            const f32x4 cs4 = *reinterpret_cast<const f32x4 *>(cum + 16 * j + 4 * lg);
+            const f32x4 cs4l = *reinterpret_cast<const f32x4 *>(cumlo + 16 * j + 4 * lg);
+            const f32x4 ds4 = *reinterpret_cast<const f32x4 *>(dts + 16 * j + 4 * lg);
+            f32x4 d4;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                float e = exp2_hw((ctv - cs4[r]) + (ctvl - cs4l[r]));
+                if (i == j) e = (4 * lg + r <= li) ? e : 0.0f;
+                d4[r] = macc[r] * e * ds4[r];
+            }
+            s16x4 th, tl;
+            split4(d4, th, tl);
+#pragma unroll
+            for (int ks = 0; ks < kNS; ks++) {
+                const int nt = sg + 4 * ks;
+                if (nt < kNT) {
+                    const s16x4 bop = *reinterpret_cast<const s16x4 *>(BT + (16 * nt + li) * SM::kPT + 16 * j + 4 * lg);
+                    dca[ii][ks] = mfma16(th, bop, dca[ii][ks]);
+                    dca[ii][ks] = mfma16(tl, bop, dca[ii][ks]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+            for (int ks = 0; ks < kNS; ks++) {
+                const int nt = sg + 4 * ks;
+                if (nt < kNT)
+                    *reinterpret_cast<f32x4 *>(pdC + ((c * 4 + kT[ii]) * kNT + nt) * 256 + lane * 4) = dca[ii][ks];
+            }
+    };
+
+    if (nch > 0) {
+        load_chunk((nch - 1) * kQ);
+        stash_chunk((nch - 1) * kQ);
+    }
+    publish();
+    __syncthreads();
+    for (int64_t c = nch - 1; c >= 0; c--) {
+        const int64_t c0 = c * kQ;
+        if (c > 0) load_chunk(c0 - kQ);
+        if (cls) chunk(std::integral_constant<int, 1>{}, c);
+        else chunk(std::integral_constant<int, 0>{}, c);
+        __syncthreads();
+        publish();
+        if (wv == 0) {
+            // per-step results u, v (before this wavefront stashes the next dt)
+            const int s = lane, tt = s >> 4;
+            const int cl = (tt == 1 || tt == 2) ? 1 : 0;
+            float q = 0.0f, R = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; s2++) {
+                q += Qa[(2 * s2 + cl) * kQ + s];
+                R += Ra[(2 * s2 + cl) * kQ + s];
+            }
+            const double dsv = dts[s];
+            q *= wbs[s];
+            R *= ecum[s];
+            const double u = Ug[cl * kQ + s] + q;
+            double v = Vr[s] + Vr[kQ + s] + R - dsv * u;
+            const double tq = wave_sumd(dsv * q);
+            const float hsum = Hd[0] + Hd[2] + Hd[4] + Hd[6];
+            if (s == kQ - 1) v += tq + ecum[kQ - 1] * hsum;
+            ug[c * kQ + s] = static_cast<float>(u);
+            vg[c * kQ + s] = v;
+        }
+        // the chunk's dx rows: 16-byte stores, P / 8 lanes per row
+        if (tid < kVX) {
+            const int t = tid / (P / 8), c8 = tid % (P / 8);
+            if (c0 + t < L)
+                st_global16(dxg + (c0 + t) * xrow + 8 * c8,
+                            *reinterpret_cast<const u32x4 *>(DX + t * SM::kPX + 8 * c8));
+        }
+        if (c > 0) stash_chunk(c0 - kQ);
+        __syncthreads();
+    }
+
+    if (p.dh0) {
+#pragma unroll
+        for (int kk = 0; kk < kDH; kk++) {
+            const int k = wv + kWaves * kk;
+            if (k < kNT * kCT) {
+                const int nt = k / kCT, q = k % kCT;
+                *reinterpret_cast<f32x4 *>(p.dh0 + (bh * P + 16 * q + li) * N + 16 * nt + 4 * lg) = dH[kk];
+            }
+        }
+    }
+    // dD term of this (batch, head): the two sg == 0 wavefronts' diagonal sums
+    if (sg == 0) {
+        const float t = wave_sum(dd);
+        if (lane == 0) Hd[cls] = t;
+    }
+    __syncthreads();
+    if (tid == 0) ws.dDp[bh] = Hd[0] + Hd[1];
+}
+
+// Per (batch, head, chunk), one wavefront: the suffix sums of v give the
+// gradient w.r.t. a_s = dt_s A; then ddt (w.r.t. the raw dt) and the
+// chunk's dA and ddt_bias terms.
+__global__ __launch_bounds__(256) void ssd_bwd_dt_kernel(SsdBwdParams p, BwdWs ws, int64_t nch) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t H = p.nheads, L = p.seqlen;
+    if (item >= p.batch * H * nch) return;   // whole wavefronts
+    const int64_t c = item % nch, bh = item / nch, h = bh % H, b = bh / H;
+    const int64_t t = c * kQ + lane;
+    const bool live = t < L;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    float raw = 0.0f, dtv = 0.0f;
+    if (live) {
+        raw = bf16_to_f32(static_cast<const bf16_t *>(p.dt)[(b * L + t) * H + h]) + bias;
+        dtv = p.softplus ? softplus_f32(raw) : raw;
+    }
+    const float u = ws.u[item * kQ + lane];
+    double da = ws.v[item * kQ + lane];   // f64: the suffix sums cancel heavily
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_down(da, off, 64);
+        if (lane + off < 64) da += o;
+    }
+    const float post = u + p.A[h] * static_cast<float>(da);
+    const float draw = live ? post * (p.softplus ? sigmoid_f32(raw) : 1.0f) : 0.0f;
+    if (live) static_cast<bf16_t *>(p.ddt)[(b * L + t) * H + h] = f32_to_bf16(draw);
+    const double sa = wave_sumd(static_cast<double>(dtv) * da);
+    const float sb = wave_sum(draw);
+    if (lane == 0) {
+        ws.dAp[item] = sa;
+        ws.dbp[item] = sb;
+    }
+}
+
+// dB (or dC) of one (batch, chunk, group): the per-head terms summed over the
+// group's heads in order, then written as bf16 rows.
+template <int N>
+__global__ __launch_bounds__(256) void ssd_bwd_fold_kernel(SsdBwdParams p, BwdWs ws, int64_t nch) {
+    constexpr int kNT = N / 16, kSlots = 4 * kNT * 64;
+    __shared__ float tile[kQ][N + 4];
+    const int tid = threadIdx.x;
+    const int64_t H = p.nheads, G = p.ngroups, L = p.seqlen, hpg = H / G;
+    const int which = blockIdx.x & 1;
+    const int64_t rest = blockIdx.x >> 1;
+    const int64_t g = rest % G, bc = rest / G, c = bc % nch, b = bc / nch;
+    const float *src = (which ? ws.pdC : ws.pdB) + ((b * H + g * hpg) * nch + c) * kQ * N;
+    const int64_t hstride = nch * kQ * N;
+    for (int slot = tid; slot < kSlots; slot += 256) {
+        f32x4 acc = kZero4;
+        for (int64_t hh = 0; hh < hpg; hh++) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(src + hh * hstride + slot * 4);
+            acc += v;
+        }
+        const int ti = slot >> 6, l = slot & 63;
+        const int i = ti / kNT, nt = ti % kNT;
+#pragma unroll
+        for (int r = 0; r < 4; r++) tile[16 * i + 4 * (l >> 4) + r][16 * nt + (l & 15)] = acc[r];
+    }
+    __syncthreads();
+    bf16_t *dst = static_cast<bf16_t *>(which ? p.dC : p.dB) + ((b * L + c * kQ) * G + g) * N;
+    for (int v = tid; v < kQ * N / 8; v += 256) {
+        const int t = v / (N / 8), c8 = v % (N / 8);
+        if (c * kQ + t < L) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                o[e] = uint32_t(f32_to_bf16(tile[t][8 * c8 + 2 * e])) |
+                       (uint32_t(f32_to_bf16(tile[t][8 * c8 + 2 * e + 1])) << 16);
+            st_global16(dst + t * G * N + 8 * c8, o);
+        }
+    }
+}
+
+// dA, ddt_bias, dD of one head: sums over (batch, chunk) in a fixed order.
+__global__ __launch_bounds__(256) void ssd_bwd_param_kernel(SsdBwdParams p, BwdWs ws, int64_t nch) {
+    __shared__ double red[3][256];
+    const int tid = threadIdx.x;
+    const int64_t h = blockIdx.x, H = p.nheads;
+    double sa = 0.0, sb = 0.0, sd = 0.0;
+    const int64_t items = p.batch * nch;
+    for (int64_t k = tid; k < items; k += 256) {
+        const int64_t b = k / nch, c = k % nch;
+        const int64_t o = (b * H + h) * nch + c;
+        sa += ws.dAp[o];
+        sb += ws.dbp[o];
+    }
+    for (int64_t b = tid; b < p.batch; b += 256) sd += ws.dDp[b * H + h];
+    red[0][tid] = sa;
+    red[1][tid] = sb;
+    red[2][tid] = sd;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) {
+            red[0][tid] += red[0][tid + w];
+            red[1][tid] += red[1][tid + w];
+            red[2][tid] += red[2][tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        p.dA[h] = static_cast<float>(red[0][0]);
+        if (p.ddt_bias) p.ddt_bias[h] = static_cast<float>(red[1][0]);
+        if (p.dD) p.dD[h] = static_cast<float>(red[2][0]);
+    }
+}
+
+template <int N, int P>
+void launch_main(const SsdBwdParams &p, const BwdWs &w, hipStream_t stream) {
+    hipLaunchKernelGGL((ss_ssd_bwd_kernel<N, P>), dim3(static_cast<unsigned>(p.batch * p.nheads)),
+                       dim3(kThr), 0, stream, p, w);
+}
+
+template <int N>
+hipError_t launch_main_n(const SsdBwdParams &p, const BwdWs &w, hipStream_t stream) {
+    switch (p.headdim) {
+        case 16: launch_main<N, 16>(p, w, stream); break;
+        case 32: launch_main<N, 32>(p, w, stream); break;
+        case 48: launch_main<N, 48>(p, w, stream); break;
+        case 64: launch_main<N, 64>(p, w, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+}
+
+template <int N>
+void launch_fold(const SsdBwdParams &p, const BwdWs &w, int64_t nch, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.batch * nch * p.ngroups * 2));
+    hipLaunchKernelGGL(ssd_bwd_fold_kernel<N>, grid, dim3(256), 0, stream, p, w, nch);
+}
 
 }  // namespace
 
 size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                                int64_t ngroups, int64_t dstate) {
-    if (batch <= 0 || nheads <= 0 || ngroups <= 0) return 0;
-    const int64_t nbc = ngroups == 1 ? batch : 1;
+    (void)ngroups;
+    if (batch <= 0 || nheads <= 0) return 0;
     size_t total = 0;
-    carve_ssd(nullptr, nbc, nheads / ngroups, headdim, dstate, seqlen, &total);
+    carve(nullptr, batch, nheads, (seqlen + kQ - 1) / kQ, headdim, dstate, &total);
     return total;
 }
 
 hipError_t launch_ssd_bwd(const SsdBwdParams &p, hipStream_t stream) {
-    const int64_t Bt = p.batch, L = p.seqlen, H = p.nheads, G = p.ngroups;
-    const int64_t P = p.headdim, N = p.dstate, nhg = H / G, dim = nhg * P;
-    if (Bt == 0 || H == 0) return hipSuccess;
-    const bool one = G == 1;
-    const int64_t nbc = one ? Bt : 1;
-    SsdBwdWs w = carve_ssd(p.workspace, nbc, nhg, P, N, L, nullptr);
-    const bf16_t *x = static_cast<const bf16_t *>(p.x), *dt = static_cast<const bf16_t *>(p.dt);
-    const bf16_t *B = static_cast<const bf16_t *>(p.B), *C = static_cast<const bf16_t *>(p.C);
-    const bf16_t *dy = static_cast<const bf16_t *>(p.dout);
-    bf16_t *dx = static_cast<bf16_t *>(p.dx), *ddt = static_cast<bf16_t *>(p.ddt);
-    bf16_t *dB = static_cast<bf16_t *>(p.dB), *dC = static_cast<bf16_t *>(p.dC);
-    const int64_t calls_b = one ? 1 : Bt;
-    for (int64_t g = 0; g < G; g++) {
-        const int64_t h0 = g * nhg;
-        hipLaunchKernelGGL(expand_params, lgrid(dim * N), dim3(256), 0, stream, p.A, p.D,
-                           p.dt_bias, h0, nhg, P, N, w.As, w.Ds, w.bs);
-        for (int64_t cb = 0; cb < calls_b; cb++) {
-            // batch entries cb .. cb + nbc - 1 of group g
-            const int64_t xo = cb * L * H * P, bo = cb * L * G * N, dto = cb * L * H;
-            const int64_t L_ = L;
-            if (L_ > 0) {
-                hipLaunchKernelGGL(rows_from_time_major, tgrid(L, dim, nbc), dim3(256), 0, stream,
-                                   x + xo, H * P, h0 * P, dim, L, w.u);
-                hipLaunchKernelGGL(rows_from_time_major, tgrid(L, dim, nbc), dim3(256), 0, stream,
-                                   dy + xo, H * P, h0 * P, dim, L, w.dout);
-                hipLaunchKernelGGL(rows_from_time_major, tgrid(L, N, nbc), dim3(256), 0, stream,
-                                   B + bo, G * N, g * N, N, L, w.Bt);
-                hipLaunchKernelGGL(rows_from_time_major, tgrid(L, N, nbc), dim3(256), 0, stream,
-                                   C + bo, G * N, g * N, N, L, w.Ct);
-                hipLaunchKernelGGL(delta_rows, lgrid(nbc * dim * L), dim3(256), 0, stream,
-                                   dt + dto, H, h0, nhg, P, L, nbc, w.delta);
-            }
-            const size_t so = size_t(cb * H + h0) * P * N;   // h0 / dlast / dh0 slice
-            BwdParams q{};
-            q.batch = nbc; q.dim = dim; q.seqlen = L; q.nstate = int(N);
-            q.u = w.u; q.delta = w.delta; q.A = w.As; q.B = w.Bt; q.C = w.Ct;
-            q.D = p.D ? w.Ds : nullptr; q.z = nullptr;
-            q.bias = p.dt_bias ? w.bs : nullptr; q.softplus = p.softplus;
-            q.h0 = p.h0 ? p.h0 + so : nullptr;
-            q.dout = w.dout; q.dlast = p.dlast ? p.dlast + so : nullptr;
-            q.du = w.du; q.ddelta = w.ddelta; q.dA = w.dAs; q.dB = w.dBt; q.dC = w.dCt;
-            q.dD = p.D ? w.dDs : nullptr; q.dz = nullptr; q.dbias = p.dt_bias ? w.dbs : nullptr;
-            q.dh0 = p.dh0 ? p.dh0 + so : nullptr;
-            q.ckpt = nullptr; q.ypre = nullptr; q.workspace = w.s6;
-            hipError_t e = launch_bwd(q, false, stream);
+    const int64_t Bt = p.batch, L = p.seqlen, H = p.nheads;
+    if (H == 0) return hipSuccess;
+    const int64_t nch = (L + kQ - 1) / kQ;
+    const BwdWs w = carve(p.workspace, Bt, H, nch, p.headdim, p.dstate, nullptr);
+    hipError_t e = hipSuccess;
+    if (Bt > 0) {
+        if (nch > 0) {
+            SsdParams sp = p;   // the forward's arguments
+            sp.out = nullptr;
+            sp.last_state = nullptr;
+            sp.states = w.states;
+            e = launch_ssd_states(sp, stream);
             if (e != hipSuccess) return e;
-            if (L_ > 0) {
-                hipLaunchKernelGGL(time_major_from_rows, tgrid(L, dim, nbc), dim3(256), 0, stream,
-                                   w.du, H * P, h0 * P, dim, L, dx + xo);
-                hipLaunchKernelGGL(time_major_from_rows, tgrid(L, N, nbc), dim3(256), 0, stream,
-                                   w.dBt, G * N, g * N, N, L, dB + bo);
-                hipLaunchKernelGGL(time_major_from_rows, tgrid(L, N, nbc), dim3(256), 0, stream,
-                                   w.dCt, G * N, g * N, N, L, dC + bo);
-                hipLaunchKernelGGL(ddt_from_rows, lgrid(nbc * nhg * L), dim3(256), 0, stream,
-                                   w.ddelta, H, h0, nhg, P, L, nbc, ddt + dto);
+        }
+        switch (p.dstate) {
+            case 32: e = launch_main_n<32>(p, w, stream); break;
+            case 64: e = launch_main_n<64>(p, w, stream); break;
+            case 96: e = launch_main_n<96>(p, w, stream); break;
+            case 128: e = launch_main_n<128>(p, w, stream); break;
+            default: return hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+        profile_mark(stream);
+        if (nch > 0) {
+            const int64_t items = Bt * H * nch;
+            hipLaunchKernelGGL(ssd_bwd_dt_kernel, dim3(static_cast<unsigned>((items + 3) / 4)),
+                               dim3(256), 0, stream, p, w, nch);
+            profile_mark(stream);
+            switch (p.dstate) {
+                case 32: launch_fold<32>(p, w, nch, stream); break;
+                case 64: launch_fold<64>(p, w, nch, stream); break;
+                case 96: launch_fold<96>(p, w, nch, stream); break;
+                case 128: launch_fold<128>(p, w, nch, stream); break;
+                default: return hipErrorInvalidValue;
             }
-            hipLaunchKernelGGL(reduce_params, lgrid(nhg), dim3(256), 0, stream, w.dAs,
-                               w.dDs, w.dbs, h0, nhg, P, N, int(cb > 0), p.dA,
-                               p.D ? p.dD : nullptr, p.dt_bias ? p.ddt_bias : nullptr);
+            profile_mark(stream);
         }
     }
+    hipLaunchKernelGGL(ssd_bwd_param_kernel, dim3(static_cast<unsigned>(H)), dim3(256), 0, stream,
+                       p, w, nch);
     profile_mark(stream);
     return hipGetLastError();
 }

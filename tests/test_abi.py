@@ -305,4 +305,6 @@ def test_ssd_bwd_checks(lib):
     assert bwd(ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
     assert bwd(ws=None) == EINVAL and "workspace" in _msg(lib)
     assert lib.ss_ssd_bwd_workspace_size(2, 64, 4, 64, 1, 256) == 0
-    assert bwd(batch=0, x=None, B=None, C=None, dout=None, dx=None, dB=None, dC=None) == 0
+    # nothing to launch without heads (an empty batch still zeroes dA on the device)
+    assert bwd(nheads=0, A=None, dA=None, x=None, B=None, C=None, dout=None, dx=None, dB=None,
+               dC=None) == 0

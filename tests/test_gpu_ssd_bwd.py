@@ -89,6 +89,18 @@ def test_ssd_bwd_empty_sequence_passes_dlast_through():
     assert not g["dA"].any() and not g["dD"].any() and not g["ddt_bias"].any()
 
 
+def test_ssd_bwd_empty_batch_zeroes_parameter_gradients():
+    require_gpu()
+    w = ssin.ssd_custom(1, 64, 4, 64, 1, 128, seed=5, bwd=True)
+    d = {k: (v[:0].contiguous() if k in ("x", "dt", "B", "C", "dout", "dlast", "h0") else v)
+         for k, v in dev_inputs(ssin.make_ssd(w)).items()}
+    g = _run(d)
+    torch.cuda.synchronize()
+    assert g["dx"].numel() == 0 and g["dB"].numel() == 0
+    for k in ("dA", "dD", "ddt_bias"):
+        assert g[k].shape == (4,) and not g[k].any(), k
+
+
 def test_ssd_bwd_full_size():
     require_gpu()
     w = ssin.SSD_WORKLOADS["mamba2_130m_ssd_bwd_bf16_8x2048x24x64_n128"]
