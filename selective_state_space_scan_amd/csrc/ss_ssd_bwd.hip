@@ -318,6 +318,13 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
     // One chunk for this wavefront; HF = cls as a compile-time constant.
     auto chunk = [&](auto hfc, int64_t c) {
         constexpr int HF = decltype(hfc)::value;
+        // The lane index, opaque to the compiler once per chunk: the LDS
+        // addresses below are then computed inside the loop instead of being
+        // hoisted out of it, where a hundred of them would stay live (and
+        // spill) across every chunk.
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        const int li = lane_o & 15, lg = lane_o >> 4;
         constexpr int kT[2] = {HF ? 1 : 0, HF ? 2 : 3};
         // (t tile, s tile) pairs, s <= t: with the s tile in kT (kPi, kPj) and
         // with the t tile in kT (kRi, kRj)
