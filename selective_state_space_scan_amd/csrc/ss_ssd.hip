@@ -62,9 +62,8 @@ struct SsdSmem {
     static constexpr uint32_t kCum = kXT + P * kPT * 2;  // f32 [kQ]
     static constexpr uint32_t kDt = kCum + kQ * 4;       // f32 [kQ]
     static constexpr uint32_t kW = kDt + kQ * 4;         // f32 [kQ]: exp(cum_last - cum_s) dt_s
-    static constexpr uint32_t kCumLo = kW + kQ * 4;      // f32 [kQ]: low part of the running sum
     static constexpr int kPY = P + 8;                     // row pitch of the output tile (bf16)
-    static constexpr uint32_t kYs = kCumLo + kQ * 4;      // bf16 [kQ][kPY]: the chunk's output
+    static constexpr uint32_t kYs = kW + kQ * 4;          // bf16 [kQ][kPY]: the chunk's output
     // state exchange, per chunk parity: [column tile][state tile][lane] x 16 bytes
     static constexpr uint32_t kHx = kYs + kQ * kPY * 2;
     static constexpr uint32_t kHxPar = (P / 16) * (N / 16) * 64 * 16;
@@ -100,7 +99,6 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     bf16_t *BT = reinterpret_cast<bf16_t *>(smem + SM::kBT);
     bf16_t *XT = reinterpret_cast<bf16_t *>(smem + SM::kXT);
     float *cum = reinterpret_cast<float *>(smem + SM::kCum);
-    float *cumlo = reinterpret_cast<float *>(smem + SM::kCumLo);
     float *dts = reinterpret_cast<float *>(smem + SM::kDt);
     float *wts = reinterpret_cast<float *>(smem + SM::kW);
     bf16_t *Ys = reinterpret_cast<bf16_t *>(smem + SM::kYs);
@@ -228,13 +226,19 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 dv = bf_lo(rdt & 0xffffu) + bias;
                 if (p.softplus) dv = softplus_f32(dv);
             }
-            float a, alo;   // running sum of dt A in base-2 exponent units, hi + lo
-            running_sum2(dv * a2, lane, a, alo);
-            const float total = __shfl(a, 63, 64), tlo = __shfl(alo, 63, 64);
+            // running sum of dt A in base-2 exponent units (plain f32: the
+            // rounding of large sums stays far below the bf16 output's; the
+            // backward, whose dA needs more, carries it compensated)
+            float a = dv * a2;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(a, off, 64);
+                if (lane >= off) a += o;
+            }
+            const float total = __shfl(a, 63, 64);
             cum[tid] = a;
-            cumlo[tid] = alo;
             dts[tid] = dv;
-            wts[tid] = exp2_hw((total - a) + (tlo - alo)) * dv;
+            wts[tid] = exp2_hw(total - a) * dv;
         }
     };
 
@@ -288,19 +292,17 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 acc = mfma32(a, hbl[m2], acc);
             }
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-                acc[r] *= exp2_hw(cum[16 * i + 4 * lg + r] + cumlo[16 * i + 4 * lg + r]);
+            for (int r = 0; r < 4; r++) acc[r] *= exp2_hw(cum[16 * i + 4 * lg + r]);
             Y[ii] = acc;
         }
         // the chunk's own part: W = G . exp(cum_t - cum_s) dt_s (s <= t),
         // Y += W x.  This lane's s are 16 j + 4 lg + r and its t 16 i + li.
-        f32x4 cs[4], csl[4], ds[4];
+        f32x4 cs[4], ds[4];
         s16x4 xb[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             if (j > kT[1]) break;
             cs[j] = *reinterpret_cast<const f32x4 *>(cum + 16 * j + 4 * lg);
-            csl[j] = *reinterpret_cast<const f32x4 *>(cumlo + 16 * j + 4 * lg);
             ds[j] = *reinterpret_cast<const f32x4 *>(dts + 16 * j + 4 * lg);
             xb[j] = *reinterpret_cast<const s16x4 *>(XT + col * SM::kPT + 16 * j + 4 * lg);
         }
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         for (int ii = 0; ii < 2; ii++) {
             const int i = kT[ii];
             const int t = 16 * i + li;
-            const float ct = cum[t], ctl = cumlo[t];
+            const float ct = cum[t];
             bf16x8_t cb[N / 32];
 #pragma unroll
             for (int k = 0; k < N / 32; k++)
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
                 s16x4 wh, wl;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    float wvv = gt[r] * exp2_hw((ct - cs[j][r]) + (ctl - csl[j][r])) * ds[j][r];
+                    float wvv = gt[r] * exp2_hw(ct - cs[j][r]) * ds[j][r];
                     // below the diagonal s < t always; on it keep s <= t (a
                     // select: both sides are computed, no branch)
                     if (j == i) wvv = (4 * lg + r <= li) ? wvv : 0.0f;
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         }
         }  // !kStates
         // this wavefront's state tiles: H_out = exp(cum_last) H_in + B^T (w x)
-        const float decay = exp2_hw(cum[kQ - 1] + cumlo[kQ - 1]);
+        const float decay = exp2_hw(cum[kQ - 1]);
         bf16x8_t xsh[2], xsl[2];
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {
