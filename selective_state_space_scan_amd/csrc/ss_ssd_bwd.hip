@@ -148,6 +148,20 @@ __device__ __forceinline__ double pick4d(const double (&v)[4], int k) {
     return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
 }
 
+// Sums of four values over the 16 lanes of a row, scattered: lane li gets
+// the sum of x[li / 4 % 4].  Five exchanges (two, then one per level) in
+// place of four full butterflies.
+template <typename T>
+__device__ __forceinline__ T sum16x4(const T (&x)[4], int li) {
+    const bool b3 = li & 8, b2 = li & 4;
+    const T y0 = (b3 ? x[2] : x[0]) + __shfl_xor(b3 ? x[0] : x[2], 8, 64);
+    const T y1 = (b3 ? x[3] : x[1]) + __shfl_xor(b3 ? x[1] : x[3], 8, 64);
+    T z = (b2 ? y1 : y0) + __shfl_xor(b2 ? y0 : y1, 4, 64);
+    z += __shfl_xor(z, 2, 64);
+    z += __shfl_xor(z, 1, 64);
+    return z;
+}
+
 __device__ __forceinline__ float pick4(const float (&v)[4], int k) {
     return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
 }
@@ -438,10 +452,8 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
         }
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
-            float tot[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) tot[r] = sum16(qacc[jj][r]);
-            if (li < 4) Qa[wv * kQ + 16 * kT[jj] + 4 * lg + li] = pick4(tot, li);
+            const float tot = sum16x4(qacc[jj], li);
+            if ((li & 3) == 0) Qa[wv * kQ + 16 * kT[jj] + 4 * lg + (li >> 2)] = tot;
         }
 
         // ---- (t, s) tile pairs with the s tile in kT, one at a time: G and M
@@ -489,11 +501,7 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
                 rd[r] = static_cast<double>(glm) * static_cast<double>(dsv);
                 if (i == j) dd += (4 * lg + r == li) ? macc[r] : 0.0f;
             }
-            if (sg == 0) {
-#pragma unroll
-                for (int r = 0; r < 4; r++) rd[r] = sum16d(rd[r]);
-                rowv[i] += pick4d(rd, li & 3);
-            }
+            if (sg == 0) rowv[i] += sum16x4(rd, li);   // row 4 lg + li / 4
             s16x4 wh, wl, mh, ml;
             split4(w4, wh, wl);
             split4(d4, mh, ml);
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             }
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                if (li < 4) Vr[cls * kQ + 16 * i + 4 * lg + li] = rowv[i];
+                if ((li & 3) == 0) Vr[cls * kQ + 16 * i + 4 * lg + (li >> 2)] = rowv[i];
         }
         // dx into the row-staging tile, dB terms to the workspace
 #pragma unroll
@@ -607,10 +615,8 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
         }
 #pragma unroll
         for (int ii = 0; ii < 2; ii++) {
-            float tot[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) tot[r] = sum16(racc[ii][r]);
-            if (li < 4) Ra[wv * kQ + 16 * kT[ii] + 4 * lg + li] = pick4(tot, li);
+            const float tot = sum16x4(racc[ii], li);
+            if ((li & 3) == 0) Ra[wv * kQ + 16 * kT[ii] + 4 * lg + (li >> 2)] = tot;
         }
         if (HF == 0) {
             hdot = wave_sum(hdot);
