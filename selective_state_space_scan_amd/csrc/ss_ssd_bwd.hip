@@ -105,9 +105,9 @@ struct BwdSmem {
     static constexpr uint32_t kDt = kCum + kQ * 4;        // f32: dt
     static constexpr uint32_t kEc = kDt + kQ * 4;         // f32: exp(cum_t)
     static constexpr uint32_t kWb = kEc + kQ * 4;         // f32: exp(cum_last - cum_s)
-    static constexpr uint32_t kUg = kWb + kQ * 4;         // f64 [2][kQ]: sum_t G L M per class
-    static constexpr uint32_t kVr = kUg + 2 * kQ * 8;     // f64 [2][kQ]: sum_s G L M dt_s per class
-    static constexpr uint32_t kQa = kVr + 2 * kQ * 8;     // f32 [8][kQ]: q terms per wavefront
+    static constexpr uint32_t kUg = kWb + kQ * 4;         // f64 [8][kQ]: sum_t G L M per wavefront
+    static constexpr uint32_t kVr = kUg + 8 * kQ * 8;     // f64 [8][kQ]: sum_s G L M dt_s per wavefront
+    static constexpr uint32_t kQa = kVr + 8 * kQ * 8;     // f32 [8][kQ]: q terms per wavefront
     static constexpr uint32_t kRa = kQa + 8 * kQ * 4;     // f32 [8][kQ]: H_in terms per wavefront
     static constexpr uint32_t kHd = kRa + 8 * kQ * 4;     // f32 [8]: <dH, H_in> per wavefront
     static constexpr uint32_t kCumLo = kHd + 8 * 4;       // f32: low part of the running sum
@@ -460,10 +460,11 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
         // give W = G L dt_s and dGm = M L dt_s, which enter dx += W^T dy and
         // dB += dGm^T C as A operands.  Lane: t = 16 i + 4 lg + r, s = 16 j + li.
         // The per-step sums below are f64: the gradient w.r.t. a_s is their
-        // suffix sum, in which the row and column sums largely cancel.
-        double colg[2] = {0.0, 0.0};   // sum_t G L M for s = 16 kT[jj] + li, this lane's t
-        // sum_s G L M dt_s for t = 16 i + 4 lg + li (li < 4), per t tile i
-        double rowv[4] = {0.0, 0.0, 0.0, 0.0};
+        // suffix sum, in which the row and column sums largely cancel.  The
+        // four wavefronts of a class hold the same tiles; wavefront sg adds
+        // the rows t = 16 i + 4 lg + sg.
+        double colg[2] = {0.0, 0.0};   // sum over this lane's row of G L M, s = 16 kT[jj] + li
+        double rowv[4] = {0.0, 0.0, 0.0, 0.0};   // sum_s G L M dt_s, row 16 i + 4 lg + sg
 #pragma unroll
         for (int pp = 0; pp < 5; pp++) {
             const int i = kPi[pp], j = kPj[pp], jj = j == kT[0] ? 0 : 1;
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             const f32x4 ct = *reinterpret_cast<const f32x4 *>(cum + 16 * i + 4 * lg);
             const f32x4 ctl = *reinterpret_cast<const f32x4 *>(cumlo + 16 * i + 4 * lg);
             f32x4 w4, d4;
-            double rd[4];
+            float glr[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 float e = exp2_hw((ct[r] - cs) + (ctl[r] - csl));
@@ -494,14 +495,17 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
                 w4[r] = gl * dsv;
                 d4[r] = macc[r] * e * dsv;
                 const float glm = gl * macc[r];
+                glr[r] = glm;
+                if (i == j) dd += (4 * lg + r == li) ? macc[r] : 0.0f;
+            }
+            {
                 // S = G L M dt_s enters a row sum here and, as dt_t times
                 // the column sum, the row's own v: exact f64 products, so
                 // that the two cancel as they do in exact arithmetic
-                colg[jj] += static_cast<double>(glm);
-                rd[r] = static_cast<double>(glm) * static_cast<double>(dsv);
-                if (i == j) dd += (4 * lg + r == li) ? macc[r] : 0.0f;
+                const double gs = pick4(glr, sg);
+                colg[jj] += gs;
+                rowv[i] += sum16d(gs * static_cast<double>(dsv));
             }
-            if (sg == 0) rowv[i] += sum16x4(rd, li);   // row 4 lg + li / 4
             s16x4 wh, wl, mh, ml;
             split4(w4, wh, wl);
             split4(d4, mh, ml);
@@ -523,18 +527,16 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             // five at once and run out of registers
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (sg == 0) {
 #pragma unroll
-            for (int jj = 0; jj < 2; jj++) {
-                double v = colg[jj];
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                if (lg == 0) Ug[cls * kQ + 16 * kT[jj] + li] = v;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                if ((li & 3) == 0) Vr[cls * kQ + 16 * i + 4 * lg + (li >> 2)] = rowv[i];
+        for (int jj = 0; jj < 2; jj++) {
+            double v = colg[jj];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (lg == 0) Ug[wv * kQ + 16 * kT[jj] + li] = v;
         }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (li == 0) Vr[wv * kQ + 16 * i + 4 * lg + sg] = rowv[i];
         // dx into the row-staging tile, dB terms to the workspace
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
@@ -687,16 +689,20 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             const int s = lane, tt = s >> 4;
             const int cl = (tt == 1 || tt == 2) ? 1 : 0;
             float q = 0.0f, R = 0.0f;
+            double ugs = 0.0;
 #pragma unroll
             for (int s2 = 0; s2 < 4; s2++) {
                 q += Qa[(2 * s2 + cl) * kQ + s];
                 R += Ra[(2 * s2 + cl) * kQ + s];
+                ugs += Ug[(2 * s2 + cl) * kQ + s];
             }
+            // row s was summed by the wavefronts with sg = s % 4, one per class
+            const double vrs = Vr[(2 * (s & 3)) * kQ + s] + Vr[(2 * (s & 3) + 1) * kQ + s];
             const double dsv = dts[s];
             q *= wbs[s];
             R *= ecum[s];
-            const double u = Ug[cl * kQ + s] + q;
-            double v = Vr[s] + Vr[kQ + s] + R - dsv * u;
+            const double u = ugs + q;
+            double v = vrs + R - dsv * u;
             const double tq = wave_sumd(dsv * q);
             const float hsum = Hd[0] + Hd[2] + Hd[4] + Hd[6];
             if (s == kQ - 1) v += tq + ecum[kQ - 1] * hsum;
