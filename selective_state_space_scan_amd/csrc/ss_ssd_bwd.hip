@@ -788,11 +788,21 @@ __global__ __launch_bounds__(256) void ssd_bwd_fold_kernel(SsdBwdParams p, BwdWs
     const float *src = (which ? ws.pdC : ws.pdB) + ((b * H + g * hpg) * nch + c) * kQ * N;
     const int64_t hstride = nch * kQ * N;
     for (int slot = tid; slot < kSlots; slot += 256) {
+        // heads in order; four loads in flight at a time
+        const float *sp = src + slot * 4;
         f32x4 acc = kZero4;
-        for (int64_t hh = 0; hh < hpg; hh++) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(src + hh * hstride + slot * 4);
-            acc += v;
+        int64_t hh = 0;
+        for (; hh + 4 <= hpg; hh += 4) {
+            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(sp + hh * hstride);
+            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(sp + (hh + 1) * hstride);
+            const f32x4 v2 = *reinterpret_cast<const f32x4 *>(sp + (hh + 2) * hstride);
+            const f32x4 v3 = *reinterpret_cast<const f32x4 *>(sp + (hh + 3) * hstride);
+            acc += v0;
+            acc += v1;
+            acc += v2;
+            acc += v3;
         }
+        for (; hh < hpg; hh++) acc += *reinterpret_cast<const f32x4 *>(sp + hh * hstride);
         const int ti = slot >> 6, l = slot & 63;
         const int i = ti / kNT, nt = ti % kNT;
 #pragma unroll
