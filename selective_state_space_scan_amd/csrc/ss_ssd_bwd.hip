@@ -144,10 +144,6 @@ __device__ __forceinline__ double wave_sumd(double v) {
     return v;
 }
 
-__device__ __forceinline__ double pick4d(const double (&v)[4], int k) {
-    return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
-}
-
 // Sums of four values over the 16 lanes of a row, scattered: lane li gets
 // the sum of x[li / 4 % 4].  Five exchanges (two, then one per level) in
 // place of four full butterflies.
@@ -327,7 +323,7 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
         }
     };
 
-    float dd = 0.0f;   // sum of dy . x over the class tiles' diagonals (sg == 0 wavefronts)
+    float dd = 0.0f;   // sum of dy . x over the class tiles' diagonals (used from sg == 0)
 
     // One chunk for this wavefront; HF = cls as a compile-time constant.
     auto chunk = [&](auto hfc, int64_t c) {
