@@ -404,6 +404,30 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // x dH for both s tiles, each dH operand split once: dH[p = 16 kk +
+        // 4 lg + e][n = 16 nt + li] in three parts (q is summed over the chunk
+        // for dA, where two-part rounding would show)
+#pragma unroll
+        for (int ks = 0; ks < kNS; ks++) {
+            const int nt = sg + 4 * ks;
+            dba[0][ks] = kZero4;
+            dba[1][ks] = kZero4;
+            if (nt < kNT) {
+#pragma unroll
+                for (int kk = 0; kk < kCT; kk++) {
+                    s16x4 hv, mv, lv;
+                    split4x3(*reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + 16 * kk + 4 * lg),
+                             hv, mv, lv);
+#pragma unroll
+                    for (int jj = 0; jj < 2; jj++) {
+                        const s16x4 a = *reinterpret_cast<const s16x4 *>(Xs + (16 * kT[jj] + li) * SM::kPX + 16 * kk + 4 * lg);
+                        dba[jj][ks] = mfma16(a, hv, dba[jj][ks]);
+                        dba[jj][ks] = mfma16(a, lv, dba[jj][ks]);
+                        dba[jj][ks] = mfma16(a, mv, dba[jj][ks]);
+                    }
+                }
+            }
+        }
         float qacc[2][4];
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
@@ -421,28 +445,12 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
 #pragma unroll
             for (int ks = 0; ks < kNS; ks++) {
                 const int nt = sg + 4 * ks;
-                dba[jj][ks] = kZero4;
                 if (nt < kNT) {
-                    f32x4 acc = kZero4;
-#pragma unroll
-                    for (int kk = 0; kk < kCT; kk++) {
-                        // dH[p = 16 kk + 4 lg + e][n = 16 nt + li], in three
-                        // parts: q is summed over the chunk for dA, where
-                        // two-part rounding would show
-                        s16x4 hv, mv, lv;
-                        split4x3(*reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + 16 * kk + 4 * lg),
-                                 hv, mv, lv);
-                        const s16x4 a = *reinterpret_cast<const s16x4 *>(Xs + (16 * kT[jj] + li) * SM::kPX + 16 * kk + 4 * lg);
-                        acc = mfma16(a, hv, acc);
-                        acc = mfma16(a, lv, acc);
-                        acc = mfma16(a, mv, acc);
-                    }
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        qacc[jj][r] += bf16_to_f32(Bs[(s0 + r) * SM::kPB + 16 * nt + li]) * acc[r];
-                        acc[r] *= dv[r] * wb[r];
+                        qacc[jj][r] += bf16_to_f32(Bs[(s0 + r) * SM::kPB + 16 * nt + li]) * dba[jj][ks][r];
+                        dba[jj][ks][r] *= dv[r] * wb[r];
                     }
-                    dba[jj][ks] = acc;
                 }
             }
         }
