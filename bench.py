@@ -214,9 +214,10 @@ def wide_state_detail(hip, lib, to_dev, dev):
 
 
 def ssd_detail(hip, lib, to_dev, dev):
-    """The Mamba-2 SSD forward at the 130M layer shape (batch 8, L 2048,
-    24 heads of 64, d_state 128, one group, bf16), inputs rotated over two
-    copies."""
+    """The Mamba-2 SSD at the 130M layer shape (batch 8, L 2048, 24 heads of
+    64, d_state 128, one group, bf16): the forward kernel (inputs rotated over
+    two copies), the backward call, and a forward + backward step in which
+    the forward saves the chunk states for the backward."""
     import torch
 
     from selective_state_space_scan_amd import binding
@@ -256,10 +257,29 @@ def ssd_detail(hip, lib, to_dev, dev):
     e1.record()
     torch.cuda.synchronize()
     bms = e0.elapsed_time(e1) / 5
-    del db, wsb
+    # a training step: the forward saves the chunk states, the backward takes them
+    ck = binding.ss_ssd_ckpt_empty(db["x"], wb.dstate)
+    yb = torch.empty_like(db["x"])
+
+    def step():
+        binding.ss_ssd_fwd(db["x"], db["dt"], db["A"], db["B"], db["C"], db["D"], db["dt_bias"],
+                           True, out=yb, ckpt=ck)
+        binding.ss_ssd_bwd(db["x"], db["dt"], db["A"], db["B"], db["C"], db["D"], db["dt_bias"],
+                           True, dout=db["dout"], workspace=wsb, ckpt=ck)
+    step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    sms = e0.elapsed_time(e1) / 5
+    del db, wsb, ck, yb
     return {wb.name: {"call_ms": round(bms, 4), "elements_per_s": E / (bms * 1e-3),
                       "note": "chunked backward: states pass, reverse chunk kernel, dt, "
-                              "head fold and parameter sums (one call)"},
+                              "head fold and parameter sums (one call)",
+                      "fwd_bwd_step_with_ckpt_ms": round(sms, 4),
+                      "fwd_bwd_step_elements_per_s": E / (sms * 1e-3)},
             w.name: {"kernel_ms": round(ms, 5), "elements_per_s": E / (ms * 1e-3),
                      "algorithmic_bytes": by,
                      "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1),

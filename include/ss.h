@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 8
+#define SS_ABI_VERSION 9
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -249,6 +249,10 @@ ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dty
  * io_dtype must be SS_BF16 (SS_EUNSUPPORTED otherwise); headdim 16, 32, 48
  * or 64; dstate 32, 64, 96 or 128; ngroups divides nheads; seqlen <= 2^26.
  * D, dt_bias, h0, last_state may be NULL; last_state must not overlap h0.
+ * ckpt, when non-NULL (ss_ssd_ckpt_size() bytes, f32), receives the state
+ * entering every chunk of 64 steps, which a later ss_ssd_bwd with the same
+ * inputs takes instead of recomputing it (save-for-backward); it must not
+ * overlap h0 or last_state.
  * Pointers 16-byte aligned, except dt (2-byte aligned suffices).
  * Each (batch, head) is computed by one workgroup in a fixed order, so the
  * results are bit-reproducible and do not depend on the batch size.
@@ -257,7 +261,12 @@ ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,
                      const float *A, const void *B, const void *C, const float *D,
                      const float *dt_bias, int dt_softplus, const float *h0, void *out,
-                     float *last_state, void *stream);
+                     float *last_state, float *ckpt, void *stream);
+
+/* Bytes of the chunk states ss_ssd_fwd saves in ckpt: batch * nheads *
+ * ceil(seqlen / 64) * dstate * headdim * 4 (0 for empty shapes). */
+size_t ss_ssd_ckpt_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate);
 
 /* Bytes of device workspace ss_ssd_bwd needs (0 for empty shapes). */
 size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
@@ -274,6 +283,8 @@ size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, 
  *   dB, dC         like B, C, bf16, required; summed over the group's heads
  *   dD, ddt_bias   NULL iff D / dt_bias is NULL
  *   dh0            optional (may be given without h0: the gradient at a zero start)
+ *   ckpt           what ss_ssd_fwd saved for exactly these inputs, or NULL (then
+ *                  the states are recomputed in the workspace)
  *   workspace      ss_ssd_bwd_workspace_size() bytes, 16-byte aligned; it holds
  *                  the state entering every chunk of 64 steps (f32), the
  *                  per-head dB / dC terms (f32) and per-step partials, about
@@ -281,7 +292,7 @@ size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, 
  *                  (headdim / 64 + 2) bytes
  * The gradients are taken in the same chunked form as the forward
  * (back-propagation through time regrouped by chunk, on bf16 matrix cores
- * with f32 accumulation): a states pass, one reverse pass per (batch, head)
+ * with f32 accumulation): a states pass (unless ckpt), one reverse pass per (batch, head)
  * carrying the state's adjoint, then the suffix sums that give ddt and dA,
  * and the sums of dB, dC over each group's heads.  Every sum runs in a fixed
  * order: results are deterministic and do not depend on the batch size.
@@ -291,8 +302,8 @@ ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      const float *A, const void *B, const void *C, const float *D,
                      const float *dt_bias, int dt_softplus, const float *h0, const void *dout,
                      const float *dlast, void *dx, void *ddt, float *dA, void *dB, void *dC,
-                     float *dD, float *ddt_bias, float *dh0, void *workspace,
-                     size_t workspace_bytes, void *stream);
+                     float *dD, float *ddt_bias, float *dh0, const float *ckpt,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Profiling aid for callers that time the library's kernels one by one

@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 8
+ABI_VERSION = 9
 _lock = threading.Lock()
 _lib = None
 
@@ -71,11 +71,13 @@ def load() -> ctypes.CDLL:
             lib.ss_state_update.argtypes = ([i64] * 3 + [c_int] + [vp] * 9 + [c_int]
                                             + [vp] * 2)
             lib.ss_ssd_fwd.restype = c_int
-            lib.ss_ssd_fwd.argtypes = [i64] * 6 + [c_int] + [vp] * 7 + [c_int] + [vp] * 4
+            lib.ss_ssd_fwd.argtypes = [i64] * 6 + [c_int] + [vp] * 7 + [c_int] + [vp] * 5
+            lib.ss_ssd_ckpt_size.restype = sz
+            lib.ss_ssd_ckpt_size.argtypes = [i64] * 5
             lib.ss_ssd_bwd_workspace_size.restype = sz
             lib.ss_ssd_bwd_workspace_size.argtypes = [i64] * 6
             lib.ss_ssd_bwd.restype = c_int
-            lib.ss_ssd_bwd.argtypes = ([i64] * 6 + [c_int] + [vp] * 7 + [c_int] + [vp] * 12
+            lib.ss_ssd_bwd.argtypes = ([i64] * 6 + [c_int] + [vp] * 7 + [c_int] + [vp] * 13
                                        + [sz, vp])
             lib.ss_conv1d_fwd.restype = c_int
             lib.ss_conv1d_fwd.argtypes = [i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 4
@@ -306,13 +308,27 @@ def ss_conv1d_update(state, x, weight, bias=None, silu=True, out=None):
     return out
 
 
+def ss_ssd_ckpt_size(batch, seqlen, nheads, headdim, dstate) -> int:
+    """Bytes of the chunk states ss_ssd_fwd can save for ss_ssd_bwd."""
+    return int(load().ss_ssd_ckpt_size(batch, seqlen, nheads, headdim, dstate))
+
+
+def ss_ssd_ckpt_empty(x, dstate):
+    """A float32 device buffer for ss_ssd_fwd's ckpt (x: the forward's input)."""
+    batch, seqlen, nheads, headdim = x.shape
+    n = ss_ssd_ckpt_size(batch, seqlen, nheads, headdim, dstate) // 4
+    return torch.empty(max(n, 1), dtype=torch.float32, device=x.device)
+
+
 def ss_ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, h0=None, out=None,
-               last_state=None, return_last_state=False):
+               last_state=None, return_last_state=False, ckpt=None):
     """Mamba-2 SSD forward; returns ``out`` or ``(out, last_state)``.
 
     x: (batch, L, nheads, headdim), dt: (batch, L, nheads), B, C: (batch, L,
     ngroups, dstate), all bfloat16; A, D, dt_bias: (nheads,) float32;
     h0 / last_state: (batch, nheads, headdim, dstate) float32.
+    ckpt: optional float32 buffer (see ss_ssd_ckpt_empty) that receives the
+    state entering every chunk of 64 steps, for ss_ssd_bwd.
     """
     lib = load()
     batch, seqlen, nheads, headdim = x.shape
@@ -327,7 +343,7 @@ def ss_ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, h0=None, 
     _check(lib.ss_ssd_fwd(batch, seqlen, nheads, headdim, ngroups, dstate, io, _ptr(x), _ptr(dt),
                           _f32(A, "A"), _ptr(B), _ptr(C), _f32(D, "D"), _f32(dt_bias, "dt_bias"),
                           int(bool(dt_softplus)), _f32(h0, "h0"), _ptr(out),
-                          _f32(last_state, "last_state"), _stream()))
+                          _f32(last_state, "last_state"), _f32(ckpt, "ckpt"), _stream()))
     return (out, last_state) if (return_last_state or last_state is not None) else out
 
 
@@ -336,11 +352,13 @@ def ss_ssd_bwd_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate) -
 
 
 def ss_ssd_bwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, h0=None, dout=None,
-               dlast=None, want_dh0=False, workspace=None):
+               dlast=None, want_dh0=False, workspace=None, ckpt=None):
     """Backward of ``sum(dout * y) + sum(dlast * last_state)`` for ss_ssd_fwd.
 
     Returns a dict with dx, ddt, dA, dB, dC and, for the optional inputs
     given, dD, ddt_bias, plus dh0 when ``want_dh0`` or h0 is given.
+    ckpt: chunk states saved by ss_ssd_fwd for the same inputs (skips the
+    states pass).
     """
     lib = load()
     batch, seqlen, nheads, headdim = x.shape
@@ -365,6 +383,6 @@ def ss_ssd_bwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, h0=None, 
                           int(bool(dt_softplus)), _f32(h0, "h0"), _ptr(dout),
                           _f32(dlast, "dlast"), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]),
                           _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
-                          _ptr(g.get("ddt_bias")), _ptr(g.get("dh0")), _ptr(workspace),
-                          workspace.numel(), _stream()))
+                          _ptr(g.get("ddt_bias")), _ptr(g.get("dh0")), _f32(ckpt, "ckpt"),
+                          _ptr(workspace), workspace.numel(), _stream()))
     return g

@@ -400,7 +400,7 @@ ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,
                      const float *A, const void *B, const void *C, const float *D,
                      const float *dt_bias, int dt_softplus, const float *h0, void *out,
-                     float *last_state, void *stream) {
+                     float *last_state, float *ckpt, void *stream) {
     ss_status st0 = check_ssd_dims(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype);
     if (st0 != SS_OK) return st0;
     Check c;
@@ -415,18 +415,29 @@ ss_status ss_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
         return fail(SS_EINVAL, "dt must be 2-byte aligned");
     if (nheads > 0) c.need(A, "A"); else c.opt(A, "A");
     c.opt(D, "D"); c.opt(dt_bias, "dt_bias"); c.opt(h0, "h0"); c.opt(last_state, "last_state");
+    c.opt(ckpt, "ckpt");
     if (c.st != SS_OK) return c.st;
     const size_t st = size_t(batch) * size_t(nheads) * size_t(headdim) * size_t(dstate) * 4;
     if (overlaps(h0, st, last_state, st))
         return fail(SS_EINVAL, "last_state must not overlap h0");
+    const size_t ck = ssk::ssd_ckpt_bytes(batch, seqlen, nheads, headdim, dstate);
+    if (overlaps(ckpt, ck, h0, st) || overlaps(ckpt, ck, last_state, st))
+        return fail(SS_EINVAL, "ckpt must not overlap h0 or last_state");
     ssk::SsdParams p{};
     p.batch = batch; p.seqlen = seqlen; p.nheads = nheads; p.ngroups = ngroups;
     p.headdim = int(headdim); p.dstate = int(dstate);
     p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.dt_bias = dt_bias;
     p.softplus = dt_softplus != 0; p.h0 = h0; p.out = out; p.last_state = last_state;
+    p.states = ckpt;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_ssd_fwd(p, static_cast<hipStream_t>(stream)),
                          "ss_ssd_fwd launch");
+}
+
+size_t ss_ssd_ckpt_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate) {
+    if (check_ssd_dims(batch, seqlen, nheads, headdim, 1, dstate, SS_BF16) != SS_OK) return 0;
+    return ssk::ssd_ckpt_bytes(batch, seqlen, nheads, headdim, dstate);
 }
 
 size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
@@ -440,8 +451,8 @@ ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      const float *A, const void *B, const void *C, const float *D,
                      const float *dt_bias, int dt_softplus, const float *h0, const void *dout,
                      const float *dlast, void *dx, void *ddt, float *dA, void *dB, void *dC,
-                     float *dD, float *ddt_bias, float *dh0, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+                     float *dD, float *ddt_bias, float *dh0, const float *ckpt,
+                     void *workspace, size_t workspace_bytes, void *stream) {
     ss_status st0 = check_ssd_dims(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype);
     if (st0 != SS_OK) return st0;
     Check c;
@@ -459,7 +470,7 @@ ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
         return fail(SS_EINVAL, "dt and ddt must be 2-byte aligned");
     if (nheads > 0) { c.need(A, "A"); c.need(dA, "dA"); } else { c.opt(A, "A"); c.opt(dA, "dA"); }
     c.opt(D, "D"); c.opt(dt_bias, "dt_bias"); c.opt(h0, "h0"); c.opt(dlast, "dlast");
-    c.opt(dD, "dD"); c.opt(ddt_bias, "ddt_bias"); c.opt(dh0, "dh0");
+    c.opt(dD, "dD"); c.opt(ddt_bias, "ddt_bias"); c.opt(dh0, "dh0"); c.opt(ckpt, "ckpt");
     c.pair(dD, D, "dD", "D");
     c.pair(ddt_bias, dt_bias, "ddt_bias", "dt_bias");
     if (c.st != SS_OK) return c.st;
@@ -477,7 +488,7 @@ ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
     p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.dt_bias = dt_bias;
     p.softplus = dt_softplus != 0; p.h0 = h0; p.out = nullptr; p.last_state = nullptr;
     p.dout = dout; p.dlast = dlast; p.dx = dx; p.ddt = ddt; p.dA = dA; p.dB = dB; p.dC = dC;
-    p.dD = dD; p.ddt_bias = ddt_bias; p.dh0 = dh0; p.workspace = workspace;
+    p.dD = dD; p.ddt_bias = ddt_bias; p.dh0 = dh0; p.workspace = workspace; p.ckpt = ckpt;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_ssd_bwd(p, static_cast<hipStream_t>(stream)),
                          "ss_ssd_bwd launch");

@@ -172,6 +172,9 @@ struct SsdParams {
 };
 hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream);
 hipError_t launch_ssd_states(const SsdParams &p, hipStream_t stream);
+// Bytes of the chunk states ss_ssd_fwd can save for ss_ssd_bwd.
+size_t ssd_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                      int64_t dstate);
 
 // Mamba-2 SSD backward (through the selective-scan backward).  dout, dx:
 // (batch, L, nheads, headdim) bf16; ddt: (batch, L, nheads) bf16; dB, dC:
@@ -184,6 +187,7 @@ struct SsdBwdParams : SsdParams {
     float *dA;
     void *dB, *dC;
     float *dD, *ddt_bias, *dh0;
+    const float *ckpt;   // chunk states saved by the forward, or NULL
     void *workspace;
 };
 size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,

@@ -78,11 +78,11 @@ struct SsdSmem {
 // each chunk's update the wavefronts publish their state (as the bf16
 // hi/lo operands) in an LDS exchange buffer, double-buffered by chunk.
 //
-// kStates: the states pass of the backward.  Only the recurrence runs (no
-// output, no C H_in, no W X): at the start of chunk c each wavefront stores
-// its state tiles as H_in[c] to p.states, (batch, head, chunk) blocks of a
-// dstate x headdim f32 matrix (headdim contiguous).  Its wavefronts need
-// no state exchange.
+// The state entering chunk c is stored to p.states, when given, as (batch,
+// head, chunk) blocks of a dstate x headdim f32 matrix (headdim contiguous):
+// the forward's checkpoint for the backward.  kStates: the backward's own
+// states pass, when no checkpoint was saved.  Only the recurrence runs (no
+// output, no C H_in, no W X), and its wavefronts need no state exchange.
 template <int N, int P, bool kStates>
 __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     constexpr int kCT = P / 16;                      // column tiles
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(8 * P) void ss_ssd_fwd_kernel(SsdParams p) {
     for (int64_t c = 0; c < nch; c++) {
         const int64_t c0 = c * kQ;
         if (c + 1 < nch) load_chunk(c0 + kQ);
-        if constexpr (kStates) {
+        if (kStates || p.states) {
             // H_in of this chunk: lane holds H^T[n][col], 16 lanes one row piece
             float *st = p.states + (((b * H + h) * nch + c) * N) * P + col;
 #pragma unroll
@@ -460,6 +460,13 @@ hipError_t launch_ssd_fwd(const SsdParams &p, hipStream_t stream) {
 
 hipError_t launch_ssd_states(const SsdParams &p, hipStream_t stream) {
     return launch_any<true>(p, stream);
+}
+
+size_t ssd_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                      int64_t dstate) {
+    if (batch <= 0 || nheads <= 0 || seqlen <= 0) return 0;
+    return size_t(batch) * size_t(nheads) * size_t((seqlen + kQ - 1) / kQ) * size_t(dstate) *
+           size_t(headdim) * 4;
 }
 
 }  // namespace ssk

@@ -21,7 +21,8 @@
 //   d(dt_s) = u_s + A sum_{t>=s} v_t,  dA = sum_s dt_s sum_{t>=s} v_t.
 //
 // Kernels, in order:
-//   1. states pass (ss_ssd.hip): H_in of every chunk, f32, to the workspace;
+//   1. states pass (ss_ssd.hip): H_in of every chunk, f32, to the workspace
+//      (skipped when the forward saved them: ckpt);
 //   2. ss_ssd_bwd_kernel: one workgroup per (batch, head) walks the chunks
 //      last to first with dH in matrix-core accumulators; writes dx, the
 //      head's dB and dC terms (f32, per head), u and v per step, and dh0;
@@ -899,10 +900,11 @@ hipError_t launch_ssd_bwd(const SsdBwdParams &p, hipStream_t stream) {
     const int64_t Bt = p.batch, L = p.seqlen, H = p.nheads;
     if (H == 0) return hipSuccess;
     const int64_t nch = (L + kQ - 1) / kQ;
-    const BwdWs w = carve(p.workspace, Bt, H, nch, p.headdim, p.dstate, nullptr);
+    BwdWs w = carve(p.workspace, Bt, H, nch, p.headdim, p.dstate, nullptr);
+    if (p.ckpt) w.states = const_cast<float *>(p.ckpt);   // read only
     hipError_t e = hipSuccess;
     if (Bt > 0) {
-        if (nch > 0) {
+        if (nch > 0 && !p.ckpt) {
             SsdParams sp = p;   // the forward's arguments
             sp.out = nullptr;
             sp.last_state = nullptr;

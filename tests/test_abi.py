@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 8
+    assert lib.ss_abi_version() == 9
 
 
 def test_ckpt_size(lib):
@@ -256,9 +256,9 @@ def test_fwd_workspace(lib):
 # Mamba-2 SSD
 # ---------------------------------------------------------------------------
 def _ssd(lib, batch=2, seqlen=64, nheads=4, headdim=64, ngroups=1, dstate=128, io=1, x=FAKE,
-         dt=FAKE, A=FAKE, B=FAKE, C=FAKE, out=FAKE, h0=None, last=None):
+         dt=FAKE, A=FAKE, B=FAKE, C=FAKE, out=FAKE, h0=None, last=None, ckpt=None):
     return lib.ss_ssd_fwd(batch, seqlen, nheads, headdim, ngroups, dstate, io, x, dt, A, B, C,
-                          None, None, 1, h0, out, last, None)
+                          None, None, 1, h0, out, last, ckpt, None)
 
 
 @pytest.mark.parametrize("kw,status,word", [
@@ -278,6 +278,16 @@ def test_ssd_dt_needs_only_element_alignment(lib):
     assert _ssd(lib, dt=FAKE + 1) == EINVAL and "dt" in _msg(lib)
 
 
+def test_ssd_ckpt_size_and_checks(lib):
+    lib.ss_ssd_ckpt_size.restype = ctypes.c_size_t
+    # one f32 dstate x headdim state per (batch, head, chunk of 64 steps)
+    assert lib.ss_ssd_ckpt_size(2, 130, 4, 64, 128) == 2 * 4 * 3 * 128 * 64 * 4
+    assert lib.ss_ssd_ckpt_size(2, 0, 4, 64, 128) == 0
+    assert lib.ss_ssd_ckpt_size(2, 64, 4, 64, 256) == 0
+    assert _ssd(lib, ckpt=MISALIGNED) == EINVAL and "ckpt" in _msg(lib)
+    assert _ssd(lib, h0=FAKE, ckpt=FAKE + 256) == EINVAL and "overlap" in _msg(lib)
+
+
 def test_ssd_state_overlap_and_empty(lib):
     assert _ssd(lib, h0=FAKE, last=FAKE + 256) == EINVAL and "overlap" in _msg(lib)
     assert _ssd(lib, batch=0, x=None, dt=None, B=None, C=None, out=None) == 0
@@ -290,14 +300,15 @@ def test_ssd_bwd_checks(lib):
         a = dict(batch=2, seqlen=64, nheads=4, headdim=64, ngroups=1, dstate=128, io=1, x=FAKE,
                  dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, bias=None, h0=None, dout=FAKE, dlast=None,
                  dx=FAKE, ddt=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dbias=None, dh0=None,
-                 ws=FAKE, ws_bytes=1 << 40)
+                 ckpt=None, ws=FAKE, ws_bytes=1 << 40)
         a.update(kw)
         return lib.ss_ssd_bwd(a["batch"], a["seqlen"], a["nheads"], a["headdim"], a["ngroups"],
                               a["dstate"], a["io"], a["x"], a["dt"], a["A"], a["B"], a["C"],
                               a["D"], a["bias"], 1, a["h0"], a["dout"], a["dlast"], a["dx"],
                               a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dbias"], a["dh0"],
-                              a["ws"], a["ws_bytes"], None)
+                              a["ckpt"], a["ws"], a["ws_bytes"], None)
     assert bwd(dout=None) == EINVAL and "dout" in _msg(lib)
+    assert bwd(ckpt=MISALIGNED) == EINVAL and "ckpt" in _msg(lib)
     assert bwd(D=FAKE) == EINVAL and "dD" in _msg(lib)
     assert bwd(io=0) == EUNSUP and "bf16" in _msg(lib)
     need = lib.ss_ssd_bwd_workspace_size(2, 64, 4, 64, 1, 128)

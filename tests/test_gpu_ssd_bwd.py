@@ -101,6 +101,31 @@ def test_ssd_bwd_empty_batch_zeroes_parameter_gradients():
         assert g[k].shape == (4,) and not g[k].any(), k
 
 
+@pytest.mark.parametrize("shape", [(2, 130, 4, 64, 1, 128), (3, 97, 6, 48, 2, 96),
+                                   (1, 64, 2, 16, 1, 32)])
+def test_ssd_bwd_from_forward_checkpoint(shape):
+    # the forward's saved chunk states are the states pass's: same bits
+    require_gpu()
+    b, L, H, P, G, N = shape
+    w = ssin.ssd_custom(b, L, H, P, G, N, seed=L + P, has_h0=True, bwd=True)
+    d = dev_inputs(ssin.make_ssd(w))
+    say(f"ssd bwd from checkpoint {w.name}")
+    ck = binding.ss_ssd_ckpt_empty(d["x"], N)
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dt_bias"], True)
+    y0, l0 = binding.ss_ssd_fwd(*args, h0=d["h0"], return_last_state=True)
+    y1, l1 = binding.ss_ssd_fwd(*args, h0=d["h0"], return_last_state=True, ckpt=ck)
+    g0 = _run(d)
+    g1 = binding.ss_ssd_bwd(*args, h0=d["h0"], dout=d["dout"], dlast=d["dlast"], want_dh0=True,
+                            ckpt=ck)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)) and torch.equal(l0, l1)
+    for k in g0:
+        a, c = g0[k], g1[k]
+        if a.dtype == torch.bfloat16:
+            a, c = a.view(torch.int16), c.view(torch.int16)
+        assert torch.equal(a, c), k
+
+
 def test_ssd_bwd_full_size():
     require_gpu()
     w = ssin.SSD_WORKLOADS["mamba2_130m_ssd_bwd_bf16_8x2048x24x64_n128"]
