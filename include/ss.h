@@ -296,6 +296,8 @@ size_t ss_ssd_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, 
  * carrying the state's adjoint, then the suffix sums that give ddt and dA,
  * and the sums of dB, dC over each group's heads.  Every sum runs in a fixed
  * order: results are deterministic and do not depend on the batch size.
+ * Besides ss_ssd_fwd's limits: batch * nheads * ceil(seqlen / 64) <= 2^31 - 1
+ * (SS_EUNSUPPORTED beyond).
  */
 ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                      int64_t ngroups, int64_t dstate, int io_dtype, const void *x, const void *dt,

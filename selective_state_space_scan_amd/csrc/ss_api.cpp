@@ -455,6 +455,9 @@ ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      void *workspace, size_t workspace_bytes, void *stream) {
     ss_status st0 = check_ssd_dims(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype);
     if (st0 != SS_OK) return st0;
+    // the per-chunk kernels launch about batch * nheads * chunks blocks
+    if (batch * nheads * ((seqlen + 63) / 64) > (int64_t(1) << 31) - 1)
+        return fail(SS_EUNSUPPORTED, "batch * nheads * ceil(seqlen / 64) exceeds 2^31 - 1");
     Check c;
     if (batch > 0 && nheads > 0 && seqlen > 0) {
         c.need(x, "x"); c.need(B, "B"); c.need(C, "C"); c.need(dout, "dout");

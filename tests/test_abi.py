@@ -309,6 +309,7 @@ def test_ssd_bwd_checks(lib):
                               a["ckpt"], a["ws"], a["ws_bytes"], None)
     assert bwd(dout=None) == EINVAL and "dout" in _msg(lib)
     assert bwd(ckpt=MISALIGNED) == EINVAL and "ckpt" in _msg(lib)
+    assert bwd(batch=4096, nheads=4096, seqlen=1 << 20) == EUNSUP and "seqlen / 64" in _msg(lib)
     assert bwd(D=FAKE) == EINVAL and "dD" in _msg(lib)
     assert bwd(io=0) == EUNSUP and "bf16" in _msg(lib)
     need = lib.ss_ssd_bwd_workspace_size(2, 64, 4, 64, 1, 128)
