@@ -324,6 +324,29 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
         }
     };
 
+    // 16 x 16 tile of U V^T over the headdim, U and V row tiles (at rows u0,
+    // v0) of two [kQ][kPX] LDS arrays: 16x16x32 products when the headdim
+    // allows, 16-byte operand reads (li_, lg_: the caller's lane index)
+    auto rows_dot = [&](const bf16_t *U, int u0, const bf16_t *V, int v0, int li_, int lg_) {
+        f32x4 acc = kZero4;
+        if constexpr (P % 32 == 0) {
+#pragma unroll
+            for (int k = 0; k < P / 32; k++) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(U + (u0 + li_) * SM::kPX + 32 * k + 8 * lg_);
+                const bf16x8_t bb = *reinterpret_cast<const bf16x8_t *>(V + (v0 + li_) * SM::kPX + 32 * k + 8 * lg_);
+                acc = mfma32(a, bb, acc);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < kCT; kk++) {
+                const s16x4 a = *reinterpret_cast<const s16x4 *>(U + (u0 + li_) * SM::kPX + 16 * kk + 4 * lg_);
+                const s16x4 bb = *reinterpret_cast<const s16x4 *>(V + (v0 + li_) * SM::kPX + 16 * kk + 4 * lg_);
+                acc = mfma16(a, bb, acc);
+            }
+        }
+        return acc;
+    };
+
     float dd = 0.0f;   // sum of dy . x over the class tiles' diagonals (used from sg == 0)
 
     // One chunk for this wavefront; HF = cls as a compile-time constant.
@@ -473,19 +496,14 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
 #pragma unroll
         for (int pp = 0; pp < 5; pp++) {
             const int i = kPi[pp], j = kPj[pp], jj = j == kT[0] ? 0 : 1;
-            f32x4 gacc = kZero4, macc = kZero4;
+            f32x4 gacc = kZero4;
 #pragma unroll
             for (int k = 0; k < N / 32; k++) {
                 const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Cs + (16 * i + li) * SM::kPB + 32 * k + 8 * lg);
                 const bf16x8_t bb = *reinterpret_cast<const bf16x8_t *>(Bs + (16 * j + li) * SM::kPB + 32 * k + 8 * lg);
                 gacc = mfma32(a, bb, gacc);
             }
-#pragma unroll
-            for (int kk = 0; kk < kCT; kk++) {
-                const s16x4 a = *reinterpret_cast<const s16x4 *>(Ys + (16 * i + li) * SM::kPX + 16 * kk + 4 * lg);
-                const s16x4 bb = *reinterpret_cast<const s16x4 *>(Xs + (16 * j + li) * SM::kPX + 16 * kk + 4 * lg);
-                macc = mfma16(a, bb, macc);
-            }
+            const f32x4 macc = rows_dot(Ys, 16 * i, Xs, 16 * j, li, lg);   // M = dy x^T
             const int s = 16 * j + li;
             const float cs = cum[s], csl = cumlo[s], dsv = dts[s];
             const f32x4 ct = *reinterpret_cast<const f32x4 *>(cum + 16 * i + 4 * lg);
@@ -635,13 +653,7 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
 #pragma unroll
         for (int pp = 0; pp < 5; pp++) {
             const int i = kRi[pp], j = kRj[pp], ii = i == kT[0] ? 0 : 1;
-            f32x4 macc = kZero4;
-#pragma unroll
-            for (int kk = 0; kk < kCT; kk++) {
-                const s16x4 a = *reinterpret_cast<const s16x4 *>(Xs + (16 * j + li) * SM::kPX + 16 * kk + 4 * lg);
-                const s16x4 bb = *reinterpret_cast<const s16x4 *>(Ys + (16 * i + li) * SM::kPX + 16 * kk + 4 * lg);
-                macc = mfma16(a, bb, macc);
-            }
+            const f32x4 macc = rows_dot(Xs, 16 * j, Ys, 16 * i, li, lg);   // M^T = x dy^T
             const float ctv = cum[16 * i + li], ctvl = cumlo[16 * i + li];
             const f32x4 cs4 = *reinterpret_cast<const f32x4 *>(cum + 16 * j + 4 * lg);
             const f32x4 cs4l = *reinterpret_cast<const f32x4 *>(cumlo + 16 * j + 4 * lg);
