@@ -58,6 +58,19 @@ __device__ __forceinline__ void split4x3(const f32x4 &v, s16x4 &hi, s16x4 &mid, 
     }
 }
 
+// two 4-value halves as one 8-value operand (elements copied by value:
+// clang takes the bit cast of a vector element from element 0)
+__device__ __forceinline__ bf16x8_t cat8(const s16x4 &a, const s16x4 &b) {
+    bf16x8_t r;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const short x = a[e], y = b[e];
+        r[e] = __builtin_bit_cast(__bf16, x);
+        r[4 + e] = __builtin_bit_cast(__bf16, y);
+    }
+    return r;
+}
+
 constexpr f32x4 kZero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
 // Inclusive running sum of a over the 64 lanes of a wavefront as an

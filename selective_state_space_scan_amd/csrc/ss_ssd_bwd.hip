@@ -437,17 +437,35 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             dba[0][ks] = kZero4;
             dba[1][ks] = kZero4;
             if (nt < kNT) {
+                if constexpr (P % 32 == 0) {   // 16x16x32: p = 32 k + 8 lg + e
 #pragma unroll
-                for (int kk = 0; kk < kCT; kk++) {
-                    s16x4 hv, mv, lv;
-                    split4x3(*reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + 16 * kk + 4 * lg),
-                             hv, mv, lv);
+                    for (int k = 0; k < P / 32; k++) {
+                        const float *hp = Hf + (16 * nt + li) * SM::kPH + 32 * k + 8 * lg;
+                        s16x4 h0, m0, l0, h1, m1, l1;
+                        split4x3(*reinterpret_cast<const f32x4 *>(hp), h0, m0, l0);
+                        split4x3(*reinterpret_cast<const f32x4 *>(hp + 4), h1, m1, l1);
+                        const bf16x8_t hv = cat8(h0, h1), mv = cat8(m0, m1), lv = cat8(l0, l1);
 #pragma unroll
-                    for (int jj = 0; jj < 2; jj++) {
-                        const s16x4 a = *reinterpret_cast<const s16x4 *>(Xs + (16 * kT[jj] + li) * SM::kPX + 16 * kk + 4 * lg);
-                        dba[jj][ks] = mfma16(a, hv, dba[jj][ks]);
-                        dba[jj][ks] = mfma16(a, lv, dba[jj][ks]);
-                        dba[jj][ks] = mfma16(a, mv, dba[jj][ks]);
+                        for (int jj = 0; jj < 2; jj++) {
+                            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Xs + (16 * kT[jj] + li) * SM::kPX + 32 * k + 8 * lg);
+                            dba[jj][ks] = mfma32(a, hv, dba[jj][ks]);
+                            dba[jj][ks] = mfma32(a, lv, dba[jj][ks]);
+                            dba[jj][ks] = mfma32(a, mv, dba[jj][ks]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < kCT; kk++) {
+                        s16x4 hv, mv, lv;
+                        split4x3(*reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + 16 * kk + 4 * lg),
+                                 hv, mv, lv);
+#pragma unroll
+                        for (int jj = 0; jj < 2; jj++) {
+                            const s16x4 a = *reinterpret_cast<const s16x4 *>(Xs + (16 * kT[jj] + li) * SM::kPX + 16 * kk + 4 * lg);
+                            dba[jj][ks] = mfma16(a, hv, dba[jj][ks]);
+                            dba[jj][ks] = mfma16(a, lv, dba[jj][ks]);
+                            dba[jj][ks] = mfma16(a, mv, dba[jj][ks]);
+                        }
                     }
                 }
             }
@@ -577,7 +595,12 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
         }
 
         __builtin_amdgcn_sched_barrier(0);
-        // H_in of this chunk as the B operand of dy H_in: hin[ks][kk][e] = H_in[p = 16 kk + 4 lg + e][n = 16 (sg + 4 ks) + li]
+        // H_in of this chunk as the B operand of dy H_in:
+        // hin[ks][kk][e] = H_in[p = poff(kk) + e][n = 16 (sg + 4 ks) + li]: for
+        // 16x16x32 products kk = 2 k, 2 k + 1 hold p = 32 k + 8 lg + 0..7
+        auto poff = [&](int kk) {
+            return P % 32 == 0 ? 32 * (kk >> 1) + 8 * lg + 4 * (kk & 1) : 16 * kk + 4 * lg;
+        };
         f32x4 hin[kNS][kCT];
         {
             const float *hs = hin_g + c * N * P;
@@ -586,7 +609,7 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
                 const int nt = sg + 4 * ks;
 #pragma unroll
                 for (int kk = 0; kk < kCT; kk++)
-                    hin[ks][kk] = nt < kNT ? *reinterpret_cast<const f32x4 *>(hs + (16 * nt + li) * P + 16 * kk + 4 * lg)
+                    hin[ks][kk] = nt < kNT ? *reinterpret_cast<const f32x4 *>(hs + (16 * nt + li) * P + poff(kk))
                                            : kZero4;
             }
         }
@@ -609,7 +632,7 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             for (int kk = 0; kk < kCT; kk++) {
                 split4x3(hin[ks][kk], hh4[kk], hm4[kk], hl4[kk]);
                 if (HF == 0 && nt < kNT) {
-                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + 16 * kk + 4 * lg);
+                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(Hf + (16 * nt + li) * SM::kPH + poff(kk));
 #pragma unroll
                     for (int e = 0; e < 4; e++) hdot += hin[ks][kk][e] * dv[e];
                 }
@@ -620,12 +643,22 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
                 dca[ii][ks] = kZero4;
                 if (nt < kNT) {
                     f32x4 acc = kZero4;
+                    if constexpr (P % 32 == 0) {
 #pragma unroll
-                    for (int kk = 0; kk < kCT; kk++) {
-                        const s16x4 a = *reinterpret_cast<const s16x4 *>(Ys + (16 * i + li) * SM::kPX + 16 * kk + 4 * lg);
-                        acc = mfma16(a, hh4[kk], acc);
-                        acc = mfma16(a, hm4[kk], acc);
-                        acc = mfma16(a, hl4[kk], acc);
+                        for (int k = 0; k < P / 32; k++) {
+                            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Ys + (16 * i + li) * SM::kPX + 32 * k + 8 * lg);
+                            acc = mfma32(a, cat8(hh4[2 * k], hh4[2 * k + 1]), acc);
+                            acc = mfma32(a, cat8(hm4[2 * k], hm4[2 * k + 1]), acc);
+                            acc = mfma32(a, cat8(hl4[2 * k], hl4[2 * k + 1]), acc);
+                        }
+                    } else {
+#pragma unroll
+                        for (int kk = 0; kk < kCT; kk++) {
+                            const s16x4 a = *reinterpret_cast<const s16x4 *>(Ys + (16 * i + li) * SM::kPX + 16 * kk + 4 * lg);
+                            acc = mfma16(a, hh4[kk], acc);
+                            acc = mfma16(a, hm4[kk], acc);
+                            acc = mfma16(a, hl4[kk], acc);
+                        }
                     }
                     const int t0 = 16 * i + 4 * lg;
                     const f32x4 ec = *reinterpret_cast<const f32x4 *>(ecum + t0);
