@@ -167,9 +167,11 @@ __device__ __forceinline__ float pick4(const float (&v)[4], int k) {
 // Class cls owns time tiles {0, 3} (cls 0) or {1, 2} (cls 1) -- as s tiles of
 // the dx and dB products and as t tiles of the dC product, five of the ten
 // lower-triangle tiles each -- and sg splits the columns: dx column tile sg,
-// state tiles sg, sg + 4.  The carried dH^T tiles k = wv + 8 kk (state tile
-// k / (P / 16), column tile k % (P / 16)) are spread over all wavefronts and
-// published in LDS as [state][column] bf16 high and low parts each chunk.
+// state tiles sg, sg + 4; the per-step sums of a class's tiles are split by
+// rows (wavefront sg adds rows 4 lg + sg).  The carried dH^T tiles k = wv +
+// 8 kk (state tile k / (P / 16), column tile k % (P / 16)) are spread over
+// all wavefronts and published in LDS as an f32 [state][column] matrix each
+// chunk, split into bf16 parts where it is used.
 template <int N, int P>
 __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs ws) {
     constexpr int kCT = P / 16, kNT = N / 16;
