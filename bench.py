@@ -114,20 +114,6 @@ def conv_algorithmic_bytes(kernel, batch, dim, L, width, esize):
     raise KeyError(kernel)
 
 
-# Algorithmic floating-point operations per element (b, d, t) with d_state 16,
-# counted from the recurrence as the oracle writes it (multiply, add = 1,
-# fused multiply-add = 2, exp / log / reciprocal = 1): per state 5 for the
-# forward step and 15 for the adjoint step and its sums, per element 21 for
-# softplus, the gate and the element gradients.  The reverse pass of the
-# step recomputes the forward states (the forward saved the pre-gate output,
-# so not C h and its sum: 2 more per state otherwise).
-FLOPS_PER_ELEMENT = {"ss_fwd_kernel": 16 * 7 + 11,          # 123
-                     "ss_bwd_reverse_kernel": 16 * 20 + 21,  # 341
-                     "ss_bwd_fold_kernel": 0}
-# MI355X f32 vector peak: 256 CUs x 128 FMA lanes per clock x 2 FLOP x
-# 2.4 GHz = 157.3 TFLOP/s.
-ALU_PEAK_TFLOPS = 256 * 128 * 2 * 2.4e9 / 1e12
-
 KERNEL_SOURCES = {
     "ss_fwd_kernel": ["ss_fwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"],
     "ss_bwd_reverse_kernel": ["ss_bwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"],
@@ -135,16 +121,138 @@ KERNEL_SOURCES = {
 }
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
-    when the summary is missing or the kernel's sources changed since."""
+# rocprofv3 counter passes behind a committed summary: five runs of
+# `rocprofv3 --pmc <pass> -- python3 bench.py --only <workload> --steps 3
+# --warmup 1`, then one `--kernel-trace --stats` run with --steps 20.
+PMC_PASSES = [
+    "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR "
+    "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SMEM GRBM_GUI_ACTIVE",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY "
+    "SQ_WAIT_ANY SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU2 GRBM_GUI_ACTIVE",
+    "SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_THREAD_CYCLES_VALU SQ_INSTS_BRANCH SQ_CYCLES "
+    "SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_MISC GRBM_GUI_ACTIVE",
+    "FETCH_SIZE",
+    "WRITE_SIZE",
+]
+# Issue cost of one wave64 f32 VALU instruction in SIMD cycles, measured on
+# this chip with independent FMA chains at 4-8 waves per SIMD (4.1-4.4;
+# v_exp_f32 alone 8.3, but it overlaps the next plain op).  The VALU issue
+# floor of a kernel is its VALU instruction count times this cost, spread
+# over 1024 SIMDs at the 2.4 GHz peak clock.
+VALU_ISSUE_CYCLES = 4.1
+SIMDS = 1024
+CLOCK_HZ = 2.4e9
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_profile(prof_dir, copy_dir, kernel, workload, title, only, sources):
+    """Markdown summary of the counter passes and the kernel trace of one
+    kernel (a substring of its name) in `prof_dir` (p1 .. p5 and trace, as
+    written by the commands the summary quotes); `copy_dir` holds the same
+    FETCH_SIZE / WRITE_SIZE passes over the 1 GiB device copy that calibrates
+    them."""
+    import glob
+    import hashlib
+    vals = {}
+    meta = None
+    for i in range(1, len(PMC_PASSES) + 1):
+        for f in glob.glob(os.path.join(prof_dir, f"p{i}", "**", "*counter_collection.csv"),
+                           recursive=True):
+            for r in _read_csv(f):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                meta = meta or r
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    cp = {}
+    for i in (4, 5):
+        for f in glob.glob(os.path.join(copy_dir, f"p{i}", "**", "*counter_collection.csv"),
+                           recursive=True):
+            for r in _read_csv(f):
+                if "copyBuffer" in r["Kernel_Name"]:
+                    cp.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    gib_kib = float(1 << 20)
+    fs = gib_kib / max(cp["FETCH_SIZE"]) if cp.get("FETCH_SIZE") else None
+    ws = gib_kib / max(cp["WRITE_SIZE"]) if cp.get("WRITE_SIZE") else None
+    stats = []
+    for f in glob.glob(os.path.join(prof_dir, "trace", "**", "*kernel_stats.csv"), recursive=True):
+        stats += _read_csv(f)
+    row = next(r for r in stats if kernel in r["Name"])
+    ns = float(row["AverageNs"])
+    waves = avg.get("SQ_WAVES", 0.0)
+    gui = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8.0   # summed over the 8 XCDs
+    out = [f"# {kernel} -- {title}", "",
+           "Measured on one MI355X (gfx950) with rocprofv3; raw outputs stay in gpurun_out/.", "",
+           "## Commands", "",
+           "Counters, one run per pass (each pass fits the per-block counter limits):", ""]
+    for p in PMC_PASSES:
+        out.append(f"- `timeout -s KILL 120 rocprofv3 --pmc {p} -d <dir>/pN -o pN --output-format "
+                   f"csv -- python3 bench.py --only {only} --steps 3 --warmup 1`")
+    out += ["", f"Trace: `timeout -s KILL 120 rocprofv3 --kernel-trace --stats -d <dir>/trace -o "
+                f"trace --output-format csv -- python3 bench.py --only {only} --steps 20 --warmup 3`",
+            "", "Traffic calibration: the FETCH_SIZE and WRITE_SIZE passes above with "
+                "`--only copy_1GiB` (a 1 GiB device copy).", "",
+            "Summary: `python3 bench.py --summarize <dir> --copy-dir <copy dir> "
+            f"--kernel {kernel} --only {only}`", "",
+            "## Launch", "",
+            f"grid {meta['Grid_Size']} work-items, workgroup {meta['Workgroup_Size']}, "
+            f"LDS {meta['LDS_Block_Size']} B, VGPRs {meta['VGPR_Count']}, "
+            f"SGPRs {meta['SGPR_Count']}, scratch {meta['Scratch_Size']} B", "",
+            "## Trace", "",
+            f"average {ns:.0f} ns over {row['Calls']} calls (min {row['MinNs']}, max {row['MaxNs']})",
+            "", "## Counters (per launch)", "", "| counter | value | per wave |", "|---|---|---|"]
+    for k in sorted(avg):
+        pw = f"{avg[k] / waves:.1f}" if waves and k.startswith("SQ_INSTS") else ""
+        out.append(f"| {k} | {avg[k]:.6g} | {pw} |")
+    valu = avg.get("SQ_INSTS_VALU", 0.0)
+    floor_ns = valu * VALU_ISSUE_CYCLES / SIMDS / CLOCK_HZ * 1e9
+    traffic = None
+    if fs and ws and "FETCH_SIZE" in avg and "WRITE_SIZE" in avg:
+        traffic = int(avg["FETCH_SIZE"] * 1024 * fs + avg["WRITE_SIZE"] * 1024 * ws)
+    out += ["", "## Derived", "", "| quantity | value |", "|---|---|",
+            f"| kernel clock-cycles per XCD (GRBM_GUI_ACTIVE / 8) | {gui:.0f} |"]
+    if gui and "SQ_ACTIVE_INST_VALU" in avg:
+        out.append(f"| VALU busy (4 x SQ_ACTIVE_INST_VALU / (1024 SIMDs x cycles)) | "
+                   f"{100 * 4 * avg['SQ_ACTIVE_INST_VALU'] / SIMDS / gui:.1f}% |")
+    if gui and "SQ_ACTIVE_INST_LDS" in avg:
+        out.append(f"| LDS instruction activity per CU (4 x SQ_ACTIVE_INST_LDS / (256 x cycles)) | "
+                   f"{100 * 4 * avg['SQ_ACTIVE_INST_LDS'] / 256 / gui:.1f}% |")
+    out.append(f"| VALU instructions per launch | {valu:.0f} |")
+    out.append(f"| VALU issue floor ({VALU_ISSUE_CYCLES} cycles per wave64 op, {SIMDS} SIMDs, "
+               f"{CLOCK_HZ / 1e9} GHz) | {floor_ns:.0f} ns = {100 * floor_ns / ns:.1f}% of the "
+               f"trace time |")
+    if traffic:
+        out += [f"| FETCH scale (1 GiB copy) | {fs:.3f} |", f"| WRITE scale (1 GiB copy) | {ws:.3f} |",
+                f"| HBM bytes per launch (scaled) | {traffic} |",
+                f"| measured HBM rate | {traffic / ns:.1f} GB/s |"]
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "selective_state_space_scan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    out += ["", "## Values read by bench.py", ""]
+    if traffic:
+        out.append(f"traffic_bytes_per_launch: {traffic}")
+    out += [f"valu_insts_per_launch: {valu:.0f}", f"trace_avg_ns: {ns:.0f}",
+            f"sources_sha256_16: {h.hexdigest()[:16]}",
+            "sources: " + " ".join("selective_state_space_scan_amd/csrc/" + f for f in sources)]
+    return "\n".join(out) + "\n"
+
+
+def profile_value(kernel, workload, key):
+    """A value from the committed rocprofv3 summary of `kernel` on `workload`,
+    or None when the summary is missing or the kernel's sources changed."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
     if not os.path.exists(path):
         return None
     vals = {}
     for line in open(path):
-        if ":" in line and not line.startswith(("|", "#", "`")):
+        if ":" in line and not line.startswith(("|", "#", "`", "-")):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     h = hashlib.sha256()
@@ -154,9 +262,39 @@ def measured_traffic(kernel, workload):
     if vals.get("sources_sha256_16") != h.hexdigest()[:16]:
         return None
     try:
-        return int(float(vals["traffic_bytes_per_launch"]))
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def copy_ceiling_gbps(dev, iters=10):
+    """Device-to-device copy rate of a 1 GiB buffer (read + write bytes per
+    second): the ceiling a streaming kernel can reach on this machine."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del src, dst
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def timed_calls(hip, lib, calls, marks, iters):
@@ -344,6 +482,75 @@ def conv_detail(hip, lib, to_dev, dev):
     return detail
 
 
+def _scan_call(name, to_dev, dev):
+    """One library call pattern of a named scan workload, with its inputs
+    resident on the GPU."""
+    import torch
+
+    from selective_state_space_scan_amd import binding
+    from selective_state_space_scan_amd import inputs as ssin
+    if name == "copy_1GiB":
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        return lambda: dst.copy_(src), (src, dst)
+    wname = PROFILE_WORKLOADS[name]
+    w = ssin.WORKLOADS[wname]
+    d = {k: to_dev(v) for k, v in ssin.make(w).items()}
+    io = 1 if w.io == "bf16" else 0
+    if w.kind == "decode":
+        out = torch.empty_like(d["u"])
+        return (lambda: binding.ss_state_update(d["state"], d["u"], d["delta"], d["A"], d["B"],
+                                                d["C"], d["D"], d["z"], d["delta_bias"], True,
+                                                out=out)), (d, out)
+    y = torch.empty_like(d["u"])
+    last = (torch.empty(w.batch, w.dim, w.dstate, device=dev) if w.last_state else None)
+    if w.kind == "fwd":
+        return (lambda: binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                       d["delta_bias"], True, out=y, last_state=last)), (d, y, last)
+    ws = torch.empty(binding.ss_bwd_workspace_size(w.batch, w.dim, w.dstate, w.seqlen, io),
+                     dtype=torch.uint8, device=dev)
+    if name.endswith("standalone"):
+        return (lambda: binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                       d["delta_bias"], True, d["dout"], workspace=ws)), (d, ws)
+    ck = binding.ss_ckpt_empty(d["u"], dstate=w.dstate)
+
+    def step():
+        binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                       d["delta_bias"], True, out=y, ckpt=ck)
+        binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                       d["delta_bias"], True, d["dout"], workspace=ws, ckpt=ck)
+    return step, (d, y, ws, ck)
+
+
+# --only NAME: the workloads a profiler run can select (scan workload name, or
+# the 1 GiB device copy that calibrates the traffic counters)
+PROFILE_WORKLOADS = {
+    "step_f32_8x1536x2048": "mamba130m_bwd_f32_8x1536x2048",
+    "step_bf16_8x1536x2048": "mamba130m_bwd_bf16_8x1536x2048",
+    "bwd_f32_8x1536x2048_standalone": "mamba130m_bwd_f32_8x1536x2048",
+    "fwd_bf16_8x1536x2048": "mamba130m_fwd_bf16_8x1536x2048",
+    "fwd_bf16_4x5120x4096": "mamba2p8b_fwd_bf16_4x5120x4096",
+    "decode_bf16_256x5120": "decode_bf16_256x5120",
+    "copy_1GiB": None,
+}
+
+
+def run_only(name, steps, warmup, to_dev, dev):
+    import torch
+    call, keep = _scan_call(name, to_dev, dev)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    del keep
+    return {"only": name, "steps": steps, "ms_per_call": e0.elapsed_time(e1) / max(steps, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,7 +562,22 @@ def main():
                     help="time only the causal convolution kernels (prints their detail)")
     ap.add_argument("--ssd-only", action="store_true",
                     help="time only the Mamba-2 SSD kernel (prints its detail)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="print the markdown summary of the rocprofv3 passes in DIR for --kernel "
+                         "(with --only naming the workload and --copy-dir the calibration)")
+    ap.add_argument("--copy-dir", metavar="DIR")
+    ap.add_argument("--kernel")
+    ap.add_argument("--only", choices=sorted(PROFILE_WORKLOADS),
+                    help="run one workload --steps times after --warmup (for rocprofv3 "
+                         "traces and counters) and print its mean call time")
     args = ap.parse_args()
+    if args.summarize:
+        w = PROFILE_WORKLOADS[args.only]
+        key = args.kernel if args.kernel in KERNEL_SOURCES else None
+        srcs = KERNEL_SOURCES.get(key, []) if key else []
+        print(summarize_profile(args.summarize, args.copy_dir, args.kernel, w,
+                                f"{args.only} ({w})", args.only, srcs), end="")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the selective scan's "
               "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
@@ -382,6 +604,9 @@ def main():
         return
     if args.ssd_only:
         print(json.dumps({"detail": ssd_detail(hip, lib, to_dev, dev)}), flush=True)
+        return
+    if args.only:
+        print(json.dumps(run_only(args.only, args.steps, args.warmup, to_dev, dev)), flush=True)
         return
 
     # ---------------- the step: fwd + bwd at 8 x 1536 x 2048, f32 ----------------
@@ -428,11 +653,20 @@ def main():
     step_bytes = kb["ss_fwd_kernel"] + kb["ss_bwd_reverse_kernel"] + kb["ss_bwd_fold_kernel"]
     dom = max(names, key=lambda n: kern_ms[n])
     ach = kb[dom] / (kern_ms[dom] * 1e-3) / 1e9
-    tflops = FLOPS_PER_ELEMENT[dom] * E / (kern_ms[dom] * 1e-3) / 1e12
-    traffic = measured_traffic(dom, "mamba130m_f32_8x1536x2048")
+    wl = PROFILE_WORKLOADS["step_f32_8x1536x2048"]
+    traffic = profile_value(dom, wl, "traffic_bytes_per_launch")
+    valu = profile_value(dom, wl, "valu_insts_per_launch")
+    copy_gbps = copy_ceiling_gbps(dev)
     kernels = {n: {"avg_ms": round(kern_ms[n], 5), "algorithmic_bytes": kb[n],
-                   "algorithmic_GBps": round(kb[n] / (kern_ms[n] * 1e-3) / 1e9, 1)}
+                   "algorithmic_GBps": round(kb[n] / (kern_ms[n] * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(kb[n] / (kern_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                for n in names}
+    issue = None
+    if valu:
+        floor_ms = valu * VALU_ISSUE_CYCLES / SIMDS / CLOCK_HZ * 1e3
+        issue = {"valu_insts_per_launch": int(valu), "cycles_per_valu_inst": VALU_ISSUE_CYCLES,
+                 "simds": SIMDS, "clock_GHz": CLOCK_HZ / 1e9,
+                 "floor_ms": round(floor_ms, 5), "frac": round(floor_ms / kern_ms[dom], 4)}
 
     result = {
         "metric": METRIC,
@@ -452,18 +686,20 @@ def main():
                    "z_gate": True, "D_skip": True, "delta_bias_softplus": True},
         "hbm_GBps_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        # The scan kernels are limited by f32 VALU work (an exp and ~20 other
-        # VALU ops per element and state in the reverse pass) and on-chip
-        # latency, not by HBM: the roofline is the ALU one; the HBM view of
-        # the same kernel follows beside it.
-        "roofline": {"kernel": dom, "bound": "alu", "achieved": round(tflops, 2),
-                     "peak": round(ALU_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(tflops / ALU_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "flops_per_element": FLOPS_PER_ELEMENT[dom],
-                     "hbm_algorithmic_GBps": round(ach, 1), "hbm_peak_GBps": HBM_PEAK_GBS,
-                     "hbm_frac": round(ach / HBM_PEAK_GBS, 4),
-                     "hbm_measured_GBps": (round(traffic / (kern_ms[dom] * 1e-3) / 1e9, 1)
-                                           if traffic else None)},
+        # The dominant kernel against the HBM roofline (algorithmic bytes per
+        # launch / its average duration, HIP events on its stream), with the
+        # measured copy ceiling beside it, and its VALU issue floor (the
+        # committed counter summary's VALU instruction count at the measured
+        # issue cost) -- the scan kernels are bound by instruction issue.
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": int(traffic) if traffic else None,
+                     "algorithmic_bytes": kb[dom], "avg_ms": round(kern_ms[dom], 5),
+                     "copy_ceiling_GBps": round(copy_gbps, 1),
+                     "frac_of_copy_ceiling": round(ach / copy_gbps, 4),
+                     "measured_GBps": (round(traffic / (kern_ms[dom] * 1e-3) / 1e9, 1)
+                                       if traffic else None),
+                     "valu_issue": issue},
         "kernels": kernels,
     }
 
@@ -590,26 +826,27 @@ def main():
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     if not args.no_cpu_baseline:
         from oracle import oracle
-        threads = min(8, os.cpu_count() or 1)
-        nd = 1536  # the whole workload: 8 x 1536 x 2048 elements, about 10 s of host work
-        x = {k: (v[:, :nd] if k in ("u", "delta", "z", "dout") else v).astype(np.float64)
-             for k, v in arr.items()}
-        x["A"], x["D"], x["delta_bias"] = (arr["A"][:nd].astype(np.float64),
-                                           arr["D"][:nd].astype(np.float64),
-                                           arr["delta_bias"][:nd].astype(np.float64))
-        t0 = time.perf_counter()
-        oracle.fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                   True, threads=threads)
-        oracle.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                   True, x["dout"], threads=threads)
-        dt = time.perf_counter() - t0
-        Es = w.batch * nd * w.seqlen
-        result["cpu_baseline"] = {"value": Es / dt, "unit": "elements/s", "cores": threads,
-                                  "kind": "oracle",
-                                  "sample": f"fwd+bwd (f64 oracle, incl. the dB/dC sums over "
-                                            f"channels) of the whole workload, {w.batch} x {nd} x "
-                                            f"{w.seqlen} = {Es} elements, {threads} threads, "
-                                            f"{dt:.2f} s wall"}
+        nproc = os.cpu_count() or 1
+        threads = max(1, min(16, nproc))   # the host-core share of one GPU
+
+        def oracle_step(nb, nthreads):
+            x = {k: (v[:nb] if k in ("u", "delta", "z", "dout", "B", "C") else v).astype(np.float64)
+                 for k, v in arr.items()}
+            t0 = time.perf_counter()
+            oracle.fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
+                       x["delta_bias"], True, threads=nthreads)
+            oracle.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
+                       x["delta_bias"], True, x["dout"], threads=nthreads)
+            return nb * w.dim * w.seqlen / (time.perf_counter() - t0)
+        one = oracle_step(1, 1)                  # one batch entry, one thread
+        allc = oracle_step(w.batch, threads)     # the whole workload, all threads
+        result["cpu_baseline"] = {
+            "value": allc, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "nproc": nproc, "cpu_model": cpu_model(),
+            "single_thread_elements_per_s": one, "all_core_elements_per_s": allc,
+            "sample": f"f64 oracle fwd+bwd (incl. the dB/dC sums over channels): one batch "
+                      f"entry ({w.dim} x {w.seqlen}) on 1 thread, then the whole workload "
+                      f"({w.batch} x {w.dim} x {w.seqlen}) on {threads} threads"}
     print(json.dumps(result), flush=True)
 
 

@@ -45,10 +45,16 @@
  * kernels on `stream` (a hipStream_t; NULL = the default stream) and
  * returns without synchronizing.
  *
- * Errors.  Arguments are validated on the host before anything is
- * launched; on failure nothing is enqueued, the call returns a non-zero
- * ss_status and ss_last_error() (thread-local) names the argument or the
- * HIP call that failed.  Launch failures return SS_EDEVICE.
+ * Errors.  Failures are reported as values that name what failed, never by
+ * a hidden fallback (the error convention of the mamba-rs GEMM-modes page,
+ * section "Errors", whose calls return a result carrying a message and
+ * whose deterministic mode refuses what it cannot honour).  Arguments are
+ * validated on the host before anything is launched; on failure nothing is
+ * enqueued, the call returns a non-zero ss_status and ss_last_error()
+ * (thread-local) names the argument or the HIP call that failed.  A shape
+ * whose launch grid would exceed the HIP limit of 2^32 work-items per
+ * dimension is refused with SS_EUNSUPPORTED before any launch.  Launch
+ * failures return SS_EDEVICE.
  */
 #ifndef SS_H
 #define SS_H
@@ -71,10 +77,15 @@ typedef enum {
     SS_EDEVICE = 3       /* a HIP call or kernel launch failed */
 } ss_status;
 
-/* SS_ABI_VERSION of the loaded library. */
+/* SS_ABI_VERSION of the loaded library: lets a caller refuse a library
+ * built for another argument list instead of misreading it (the explicit,
+ * erroring boundary of the mamba-rs GEMM-modes page, section "Errors"). */
 int ss_abi_version(void);
 
-/* Message of the last failed call on this thread ("" after a success). */
+/* Message of the last failed call on this thread ("" after a success): the
+ * named-failure half of the error convention of the mamba-rs GEMM-modes
+ * page, section "Errors".  The pointer stays valid until the thread's next
+ * call into the library. */
 const char *ss_last_error(void);
 
 /*

@@ -41,6 +41,47 @@ constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxSeq = int64_t(1) << 26;
 
+// HIP launches at most 2^32 - 1 work-items along a grid dimension (blocks
+// times threads per block).  Every launcher's x extent is checked against it
+// here, on the host, so an oversized shape is refused as unsupported before
+// anything is enqueued instead of failing at launch.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+
+bool grid_fits(int64_t blocks, int64_t threads) {
+    return blocks <= kMaxWorkItems / threads;
+}
+
+// Blocks of an elementwise pass over n items, v per thread, 256 threads each.
+int64_t elementwise_blocks(int64_t n, int64_t v) { return (n / v + 255) / 256; }
+
+// The x extents of the selective-scan launches for one call: the scan
+// kernels (16 or 48 channels per block of 256 or 768 threads), the slice
+// combine kernels (several 16-state slices), the backward's fold, and
+// decode's 4 lanes per row.
+ss_status check_scan_grids(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                           bool bwd) {
+    if (!grid_fits((dim + 15) / 16, 256) || !grid_fits((dim + 47) / 48, 768))
+        return fail(SS_EUNSUPPORTED,
+                    "dim %lld: the scan's launch grid would exceed 2^32 work-items",
+                    (long long)dim);
+    // batch, dim and seqlen are within check_dims' limits, but their product
+    // can pass 2^63
+    const __int128 E = static_cast<__int128>(batch) * dim * seqlen;
+    const int64_t v = seqlen % 4 == 0 ? 4 : 1;
+    if (dstate > 16 && E / v > static_cast<__int128>(kMaxWorkItems) - 255)
+        return fail(SS_EUNSUPPORTED,
+                    "batch * dim * seqlen: the state-slice combine grid would exceed 2^32 "
+                    "work-items");
+    if (bwd) {
+        const int64_t fold = batch * dstate * seqlen / v + dim * dstate + dim;
+        if (!grid_fits(elementwise_blocks(fold, 1), 256))
+            return fail(SS_EUNSUPPORTED,
+                        "batch * dstate * seqlen: the backward's fold grid would exceed 2^32 "
+                        "work-items");
+    }
+    return SS_OK;
+}
+
 struct Check {
     ss_status st = SS_OK;
     // first failure wins
@@ -80,7 +121,7 @@ ss_status check_dims(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
     if (scan && seqlen > kMaxSeq)
         return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
                     (long long)kMaxSeq);
-    if (!scan && batch * dim > (int64_t(1) << 31) * 64)
+    if (!scan && static_cast<__int128>(batch) * dim > (static_cast<__int128>(1) << 37))
         return fail(SS_EUNSUPPORTED, "batch * dim too large");
     return SS_OK;
 }
@@ -148,6 +189,8 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                  size_t workspace_bytes, void *stream) {
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
+    st = check_scan_grids(batch, dim, dstate, seqlen, false);
+    if (st != SS_OK) return st;
     const bool has_rows = batch > 0 && dim > 0;
     Check c;
     if (has_rows && seqlen > 0) {
@@ -210,6 +253,8 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                  void *stream) {
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
+    st = check_scan_grids(batch, dim, dstate, seqlen, true);
+    if (st != SS_OK) return st;
     const bool has_rows = batch > 0 && dim > 0;
     const bool has_elems = has_rows && seqlen > 0;
     Check c;
@@ -263,6 +308,11 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dty
                           void *stream) {
     ss_status st = check_dims(batch, dim, dstate, 1, io_dtype, false);
     if (st != SS_OK) return st;
+    // 4 lanes per (batch, channel) row
+    if (!grid_fits((batch * dim + 63) / 64, 256))
+        return fail(SS_EUNSUPPORTED,
+                    "batch * dim %lld: the state update's launch grid would exceed 2^32 "
+                    "work-items", (long long)(batch * dim));
     Check c;
     if (batch > 0 && dim > 0) {
         c.need(state, "state"); c.need(u, "u"); c.need(delta, "delta"); c.need(A, "A");
@@ -299,10 +349,14 @@ ss_status check_conv_dims(int64_t batch, int64_t dim, int64_t seqlen, int64_t wi
                     (long long)kMaxSeq);
     if (dim > kMaxDim)
         return fail(SS_EUNSUPPORTED, "dim %lld exceeds %lld", (long long)dim, (long long)kMaxDim);
-    // one wavefront per (row, segment), at most 2^32 of them (2^30 workgroups)
+    // forward: one wavefront per (row, segment) in 256-thread blocks;
+    // backward: one 128-thread block per channel; decode: one thread per row
     if (batch > 0 && dim > 0 &&
-        batch > (int64_t(1) << 32) / dim / ssk::conv_segments(seqlen))
-        return fail(SS_EUNSUPPORTED, "batch * dim * segments too large");
+        (batch > kMaxWorkItems / 64 / dim / ssk::conv_segments(seqlen) ||
+         !grid_fits(dim, 128) || !grid_fits((batch * dim + 255) / 256, 256)))
+        return fail(SS_EUNSUPPORTED,
+                    "batch * dim * segments: the convolution's launch grid would exceed 2^32 "
+                    "work-items");
     return SS_OK;
 }
 
@@ -327,8 +381,9 @@ ss_status check_ssd_dims(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
     if (seqlen > kMaxSeq)
         return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
                     (long long)kMaxSeq);
-    if (batch * nheads > (int64_t(1) << 31) - 1 || batch > kMaxBatch)
-        return fail(SS_EUNSUPPORTED, "batch * nheads too large");
+    if (batch > kMaxBatch || !grid_fits(batch * nheads, 512))
+        return fail(SS_EUNSUPPORTED,
+                    "batch * nheads: the SSD launch grid would exceed 2^32 work-items");
     return SS_OK;
 }
 
@@ -455,9 +510,16 @@ ss_status ss_ssd_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
                      void *workspace, size_t workspace_bytes, void *stream) {
     ss_status st0 = check_ssd_dims(batch, seqlen, nheads, headdim, ngroups, dstate, io_dtype);
     if (st0 != SS_OK) return st0;
-    // the per-chunk kernels launch about batch * nheads * chunks blocks
-    if (batch * nheads * ((seqlen + 63) / 64) > (int64_t(1) << 31) - 1)
-        return fail(SS_EUNSUPPORTED, "batch * nheads * ceil(seqlen / 64) exceeds 2^31 - 1");
+    // the per-chunk kernels: batch * nheads * chunks / 4 blocks of 256
+    // threads (dt) and batch * chunks * ngroups * 2 blocks of 256 (fold)
+    {
+        const int64_t nch = (seqlen + 63) / 64;
+        if (!grid_fits((batch * nheads * nch + 3) / 4, 256) ||
+            !grid_fits(batch * nch * ngroups * 2, 256))
+            return fail(SS_EUNSUPPORTED,
+                        "batch * nheads * ceil(seqlen / 64): the SSD backward's launch grids "
+                        "would exceed 2^32 work-items");
+    }
     Check c;
     if (batch > 0 && nheads > 0 && seqlen > 0) {
         c.need(x, "x"); c.need(B, "B"); c.need(C, "C"); c.need(dout, "dout");
@@ -502,8 +564,7 @@ ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dty
                            void *out, void *stream) {
     ss_status st = check_conv_dims(batch, dim, 1, width, io_dtype);
     if (st != SS_OK) return st;
-    if (batch * dim > (int64_t(1) << 38))
-        return fail(SS_EUNSUPPORTED, "batch * dim too large");
+
     Check c;
     if (batch > 0 && dim > 0) {
         c.need(x, "x"); c.need(weight, "weight"); c.need(out, "out");

@@ -1,5 +1,6 @@
 """Helpers shared by the GPU parity tests: moving seeded inputs to the
 device and back, and running the oracle on the same stored values."""
+import os
 import sys
 
 import numpy as np
@@ -10,6 +11,9 @@ from selective_state_space_scan_amd import binding
 from selective_state_space_scan_amd import inputs as ssin
 
 DEV = "cuda:0"
+# host threads for whole-workload oracle runs (the GPU machine gives one GPU a
+# share of 16 host cores)
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 def say(*a):

@@ -309,7 +309,7 @@ def test_ssd_bwd_checks(lib):
                               a["ckpt"], a["ws"], a["ws_bytes"], None)
     assert bwd(dout=None) == EINVAL and "dout" in _msg(lib)
     assert bwd(ckpt=MISALIGNED) == EINVAL and "ckpt" in _msg(lib)
-    assert bwd(batch=4096, nheads=4096, seqlen=1 << 20) == EUNSUP and "seqlen / 64" in _msg(lib)
+    assert bwd(batch=1024, nheads=1024, seqlen=1 << 20) == EUNSUP and "seqlen / 64" in _msg(lib)
     assert bwd(D=FAKE) == EINVAL and "dD" in _msg(lib)
     assert bwd(io=0) == EUNSUP and "bf16" in _msg(lib)
     need = lib.ss_ssd_bwd_workspace_size(2, 64, 4, 64, 1, 128)
@@ -320,3 +320,41 @@ def test_ssd_bwd_checks(lib):
     # nothing to launch without heads (an empty batch still zeroes dA on the device)
     assert bwd(nheads=0, A=None, dA=None, x=None, B=None, C=None, dout=None, dx=None, dB=None,
                dC=None) == 0
+
+
+# ---------------------------------------------------------------------------
+# launch grids: HIP takes at most 2^32 - 1 work-items along a grid dimension;
+# shapes past it are refused on the host as unsupported, not left to fail at
+# launch
+# ---------------------------------------------------------------------------
+def test_scan_grid_limit(lib):
+    # 2^28 + 16 channels fit the dim limit but not 16 channels per 256 threads
+    dim = (1 << 28) + 16
+    assert _fwd(lib, batch=1, dim=dim, seqlen=16) == EUNSUP and "2^32" in _msg(lib)
+    assert _bwd(lib, batch=1, dim=dim, seqlen=16, ws_bytes=1 << 60) == EUNSUP
+    assert "2^32" in _msg(lib)
+    # the largest dim whose grid fits passes the grid check (and fails later, on
+    # the missing workspace-free pointers it is not given)
+    assert _fwd(lib, batch=1, dim=(1 << 28) - 16, seqlen=16, u=None) == EINVAL
+
+
+def test_slice_combine_and_fold_grid_limits(lib):
+    # several state slices: one elementwise combine pass over batch * dim * seqlen
+    assert _fwd(lib, batch=65535, dim=1 << 16, dstate=32, seqlen=1 << 14) == EUNSUP
+    assert "combine" in _msg(lib)
+    # the backward's fold: batch * dstate * seqlen / 4 items
+    assert _bwd(lib, batch=65535, dim=16, seqlen=1 << 26, ws_bytes=1 << 60) == EUNSUP
+    assert "fold" in _msg(lib)
+
+
+def test_decode_grid_limit(lib):
+    st = lib.ss_state_update(1 << 20, 1 << 11, 16, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                             None, None, 1, FAKE, None)
+    assert st == EUNSUP and "2^32" in _msg(lib)
+
+
+def test_conv_and_ssd_grid_limits(lib):
+    # the convolution's backward takes one 128-thread block per channel
+    assert _cbwd(lib, batch=1, dim=1 << 26, seqlen=16) == EUNSUP and "2^32" in _msg(lib)
+    # the SSD kernels take one block of up to 512 threads per (batch, head)
+    assert _ssd(lib, batch=1 << 12, nheads=1 << 12) == EUNSUP and "2^32" in _msg(lib)

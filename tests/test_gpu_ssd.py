@@ -68,7 +68,8 @@ def test_ssd_small_parity(shape, softplus):
     torch.cuda.synchronize()
     ry, rl = _oracle(arr, softplus, h0=arr.get("h0"))
     assert_close(to_host(y), ry, TOL["bf16"], "y")
-    assert_close(to_host(last), rl, TOL["bf16"], "last_state")
+    # last_state is an f32 output: the state and its sums stay f32 on chip
+    assert_close(to_host(last), rl, TOL["f32"], "last_state")
 
 
 def test_ssd_empty_sequence():
@@ -94,7 +95,7 @@ def test_ssd_full_size():
     assert torch.equal(last, last2), "last_state differs between calls"
     ry, rl = _oracle(arr)
     e1 = assert_close(to_host(y), ry, TOL["bf16"], "y")
-    e2 = assert_close(to_host(last), rl, TOL["bf16"], "last_state")
+    e2 = assert_close(to_host(last), rl, TOL["f32"], "last_state")
     say(f"  err y {e1:.3e} last_state {e2:.3e}")
 
 
