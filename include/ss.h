@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 9
+#define SS_ABI_VERSION 10
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -161,6 +161,32 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
                  void *du, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
                  float *ddelta_bias, float *dh0, const float *ckpt, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/*
+ * ss_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and kernels as ss_bwd (bit-identical
+ * results), without the workspace: it uses a file-scope device array of
+ * ss_bwd_noalloc_max_scratch() bytes (96 MiB) that the library holds on
+ * every GPU it runs on until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *   The part a call needs is its dB / dC partials, plus the block states
+ *   when ckpt is NULL: about 68 MB at batch 8, dim 1536, seqlen 2048,
+ *   dstate 16 with the forward's ckpt.  A larger need returns
+ *   SS_EUNSUPPORTED with a message; pass ckpt or call ss_bwd.
+ *   Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   contents (each word is written before it is read, so nothing needs
+ *   clearing): calls that overlap on one GPU -- on different streams or
+ *   from several threads -- race and must be serialized by the caller.
+ */
+size_t ss_bwd_noalloc_max_scratch(void);
+ss_status ss_bwd_noalloc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                         int io_dtype, const void *u, const void *delta, const float *A,
+                         const void *B, const void *C, const float *D, const void *z,
+                         const float *delta_bias, int delta_softplus, const float *h0,
+                         const void *dout, const float *dlast, void *du, void *ddelta, float *dA,
+                         void *dB, void *dC, float *dD, void *dz, float *ddelta_bias, float *dh0,
+                         const float *ckpt, void *stream);
 
 /*
  * One-token state update (decode): advances `state` (batch, dim, dstate,

@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 9
+ABI_VERSION = 10
 _lock = threading.Lock()
 _lib = None
 
@@ -67,6 +67,11 @@ def load() -> ctypes.CDLL:
             lib.ss_bwd.restype = c_int
             lib.ss_bwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 14
                                    + [sz, vp])
+            lib.ss_bwd_noalloc.restype = c_int
+            lib.ss_bwd_noalloc.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 13
+                                           + [vp])
+            lib.ss_bwd_noalloc_max_scratch.restype = sz
+            lib.ss_bwd_noalloc_max_scratch.argtypes = []
             lib.ss_state_update.restype = c_int
             lib.ss_state_update.argtypes = ([i64] * 3 + [c_int] + [vp] * 9 + [c_int]
                                             + [vp] * 2)
@@ -223,6 +228,45 @@ def ss_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=Fa
                       _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0")), _f32(ckpt, "ckpt"),
                       _ptr(workspace),
                       workspace.numel(), _stream()))
+    return g
+
+
+def ss_bwd_noalloc_max_scratch() -> int:
+    return int(load().ss_bwd_noalloc_max_scratch())
+
+
+def ss_bwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                   dout=None, h0=None, dlast=None, want_dh0=False, ckpt=None, grads=None):
+    """ss_bwd through the allocation-free entry point (its workspace is the
+    library's device-resident scratch array).  ``grads``: preallocated
+    gradient tensors, as the dict ss_bwd returns; allocated here when None.
+    """
+    lib = load()
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    io = _io_dtype(u)
+    _same_io(io, delta, B, C, z, dout)
+    dev = u.device
+    g = grads
+    if g is None:
+        g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta),
+                 dA=torch.empty(dim, dstate, dtype=torch.float32, device=dev),
+                 dB=torch.empty_like(B), dC=torch.empty_like(C))
+        if D is not None:
+            g["dD"] = torch.empty(dim, dtype=torch.float32, device=dev)
+        if z is not None:
+            g["dz"] = torch.empty_like(z)
+        if delta_bias is not None:
+            g["ddelta_bias"] = torch.empty(dim, dtype=torch.float32, device=dev)
+        if want_dh0 or h0 is not None:
+            g["dh0"] = torch.empty(batch, dim, dstate, dtype=torch.float32, device=dev)
+    _check(lib.ss_bwd_noalloc(batch, dim, dstate, seqlen, io, _ptr(u), _ptr(delta), _f32(A, "A"),
+                              _ptr(B), _ptr(C), _f32(D, "D"), _ptr(z),
+                              _f32(delta_bias, "delta_bias"), int(bool(delta_softplus)),
+                              _f32(h0, "h0"), _ptr(dout), _f32(dlast, "dlast"), _ptr(g["du"]),
+                              _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                              _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                              _ptr(g.get("dh0")), _f32(ckpt, "ckpt"), _stream()))
     return g
 
 

@@ -244,13 +244,18 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
     return ssk::bwd_workspace_bytes(batch, dim, seqlen, int(dstate));
 }
 
-ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
-                 const void *u, const void *delta, const float *A, const void *B, const void *C,
-                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
-                 const float *h0, const void *dout, const float *dlast, void *du, void *ddelta,
-                 float *dA, void *dB, void *dC, float *dD, void *dz, float *ddelta_bias,
-                 float *dh0, const float *ckpt, void *workspace, size_t workspace_bytes,
-                 void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by ss_bwd and ss_bwd_noalloc; fills everything of the
+// kernel parameters but the workspace.
+ss_status bwd_params(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                     const void *u, const void *delta, const float *A, const void *B,
+                     const void *C, const float *D, const void *z, const float *delta_bias,
+                     int delta_softplus, const float *h0, const void *dout, const float *dlast,
+                     void *du, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
+                     float *ddelta_bias, float *dh0, const float *ckpt, ssk::BwdParams *p) {
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
     st = check_scan_grids(batch, dim, dstate, seqlen, true);
@@ -279,6 +284,33 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     c.pair(dz, z, "dz", "z");
     c.pair(ddelta_bias, delta_bias, "ddelta_bias", "delta_bias");
     if (c.st != SS_OK) return c.st;
+    *p = ssk::BwdParams{};
+    p->batch = batch; p->dim = dim; p->seqlen = seqlen; p->nstate = int(dstate);
+    p->u = u; p->delta = delta; p->A = A; p->B = B; p->C = C; p->D = D; p->z = z;
+    p->bias = delta_bias; p->softplus = delta_softplus != 0; p->h0 = h0;
+    p->dout = dout; p->dlast = dlast; p->du = du; p->ddelta = ddelta; p->dA = dA; p->dB = dB;
+    p->dC = dC; p->dD = dD; p->dz = dz; p->dbias = ddelta_bias; p->dh0 = dh0; p->ckpt = ckpt;
+    p->ypre = (ckpt && ssk::state_slices(int(dstate)) == 1)
+                  ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
+    return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                 const float *h0, const void *dout, const float *dlast, void *du, void *ddelta,
+                 float *dA, void *dB, void *dC, float *dD, void *dz, float *ddelta_bias,
+                 float *dh0, const float *ckpt, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+    ssk::BwdParams p;
+    ss_status st = bwd_params(batch, dim, dstate, seqlen, io_dtype, u, delta, A, B, C, D, z,
+                              delta_bias, delta_softplus, h0, dout, dlast, du, ddelta, dA, dB, dC,
+                              dD, dz, ddelta_bias, dh0, ckpt, &p);
+    if (st != SS_OK) return st;
     const size_t need = ssk::bwd_workspace_bytes(batch, dim, seqlen, int(dstate));
     if (need > 0) {
         if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
@@ -287,18 +319,42 @@ ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
             return fail(SS_EINVAL, "workspace_bytes %zu is smaller than the %zu bytes needed",
                         workspace_bytes, need);
     }
-    ssk::BwdParams p{};
-    p.batch = batch; p.dim = dim; p.seqlen = seqlen; p.nstate = int(dstate);
-    p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
-    p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
-    p.dout = dout; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB;
-    p.dC = dC; p.dD = dD; p.dz = dz; p.dbias = ddelta_bias; p.dh0 = dh0; p.ckpt = ckpt;
-    p.ypre = (ckpt && ssk::state_slices(int(dstate)) == 1)
-                 ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
     p.workspace = workspace;
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
                          "ss_bwd launch");
+}
+
+size_t ss_bwd_noalloc_max_scratch(void) { return ssk::kBwdScratchBytes; }
+
+ss_status ss_bwd_noalloc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                         int io_dtype, const void *u, const void *delta, const float *A,
+                         const void *B, const void *C, const float *D, const void *z,
+                         const float *delta_bias, int delta_softplus, const float *h0,
+                         const void *dout, const float *dlast, void *du, void *ddelta, float *dA,
+                         void *dB, void *dC, float *dD, void *dz, float *ddelta_bias, float *dh0,
+                         const float *ckpt, void *stream) {
+    ssk::BwdParams p;
+    ss_status st = bwd_params(batch, dim, dstate, seqlen, io_dtype, u, delta, A, B, C, D, z,
+                              delta_bias, delta_softplus, h0, dout, dlast, du, ddelta, dA, dB, dC,
+                              dD, dz, ddelta_bias, dh0, ckpt, &p);
+    if (st != SS_OK) return st;
+    const size_t need = ssk::bwd_noalloc_bytes(p, io_dtype == SS_BF16);
+    if (need > ssk::kBwdScratchBytes)
+        return fail(SS_EUNSUPPORTED,
+                    "this shape needs %zu bytes of scratch, more than the %zu ss_bwd_noalloc holds "
+                    "(pass the forward's ckpt, or call ss_bwd with a workspace)",
+                    need, ssk::kBwdScratchBytes);
+    void *scratch = nullptr;
+    if (need > 0) {
+        const hipError_t e = ssk::bwd_scratch(&scratch);
+        if (e != hipSuccess) return device_status(e, "ss_bwd_noalloc scratch lookup");
+    }
+    p.workspace = scratch;
+    p.tight_ws = 1;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
+    return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+                         "ss_bwd_noalloc launch");
 }
 
 ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,

@@ -42,6 +42,7 @@
 //      order and the dA/dD/dbias partials over the batch in ascending batch
 //      order.
 // Every sum runs in an order fixed by the shape, with no atomics.
+#include <mutex>
 #include <type_traits>
 
 #include "ss_device.h"
@@ -82,10 +83,15 @@ struct Workspace {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// `groups`: the dB / dC partials per batch entry the buffer holds room for;
+// `with_ckpt`: whether it holds the block states (not needed when the
+// forward's saved record is passed).  ss_bwd's workspace always has both at
+// their largest (16-channel groups); the allocation-free entry sizes them
+// for the call.
 __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L,
-                                           int nstate, size_t *total) {
+                                           int nstate, int64_t groups, bool with_ckpt,
+                                           size_t *total) {
     const int64_t nck = (L + kCk - 1) / kCk;
-    const int64_t groups = (dim + kRows - 1) / kRows;
     const int slices = state_slices(nstate);
     size_t off = 0;
     Workspace w;
@@ -95,7 +101,7 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
         off += align256(floats * sizeof(float));
         return r;
     };
-    w.ckpt = take(size_t(slices) * batch * dim * nck * kN);
+    w.ckpt = with_ckpt ? take(size_t(slices) * batch * dim * nck * kN) : nullptr;
     w.ypre = nullptr;
     const size_t first = off;
     w.dBp = take(size_t(batch) * groups * kN * L);
@@ -887,9 +893,21 @@ void launch_reverse(const BwdParams &p, Workspace ws, hipStream_t stream) {
     hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW, PART>), grid, dim3(64 * NW), 0, stream, p, ws);
 }
 
+// Channel groups of the reverse pass for this call (and so dB / dC partials
+// per batch entry).
+int64_t reverse_groups(const BwdParams &p, size_t esize) {
+    const bool vec = (p.seqlen * int64_t(esize)) % 16 == 0;
+    const int nw = reverse_waves(p, vec);
+    return (p.dim + 4 * nw - 1) / (4 * nw);
+}
+
 template <typename T>
 hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
-    Workspace ws = carve(p.workspace, p.batch, p.dim, p.seqlen, p.nstate, nullptr);
+    Workspace ws = p.tight_ws
+                       ? carve(p.workspace, p.batch, p.dim, p.seqlen, p.nstate,
+                               reverse_groups(p, sizeof(T)), p.ckpt == nullptr, nullptr)
+                       : carve(p.workspace, p.batch, p.dim, p.seqlen, p.nstate,
+                               (p.dim + kRows - 1) / kRows, true, nullptr);
     const int slices = state_slices(p.nstate);
     if (p.ckpt) {  // saved by the forward: read only
         ws.ckpt = const_cast<float *>(p.ckpt);
@@ -944,6 +962,7 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
     }
     const bool v4 = p.seqlen % 4 == 0;   // 16-byte partial loads
     const int64_t total = p.batch * p.nstate * p.seqlen / (v4 ? 4 : 1) + p.dim * p.nstate + p.dim;
+    if (total == 0 && !(p.batch > 0 && p.dim > 0)) return hipSuccess;   // nothing was enqueued
     if (total > 0) {
         const dim3 fgrid(unsigned((total + 255) / 256));
         if (v4)
@@ -959,8 +978,46 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
 
 size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate) {
     size_t total = 0;
-    carve(nullptr, batch, dim, seqlen, nstate, &total);
+    carve(nullptr, batch, dim, seqlen, nstate, (dim + kRows - 1) / kRows, true, &total);
     return total;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the workspace is a file-scope device array
+// ---------------------------------------------------------------------------
+// Every reverse pass and fold writes each workspace word it later reads
+// (block states, partials), so the array needs no clearing between calls;
+// it keeps the last call's contents.  Calls that overlap on one GPU share it
+// and race.
+static __device__ __align__(256) char scratch[kBwdScratchBytes];
+
+size_t bwd_noalloc_bytes(const BwdParams &p, bool bf16) {
+    if (p.batch <= 0 || p.dim <= 0) return 0;
+    size_t total = 0;
+    carve(nullptr, p.batch, p.dim, p.seqlen, p.nstate, reverse_groups(p, bf16 ? 2 : 4),
+          p.ckpt == nullptr, &total);
+    return total;
+}
+
+hipError_t bwd_scratch(void **ptr) {
+    // each device holds its own copy of the array; its address is looked up
+    // once per device, with that device current (the array's name is not a
+    // device address in host code)
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream) {

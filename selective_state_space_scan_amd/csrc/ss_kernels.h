@@ -80,6 +80,7 @@ struct BwdParams : ScanParams {
     const float *ckpt;  // block states saved by the forward, or nullptr
     const float *ypre;  // pre-gate output saved by the forward with ckpt, or nullptr
     void *workspace;
+    int tight_ws;       // workspace sized for this call (bwd_noalloc_bytes), not ss_bwd's
 };
 
 struct DecodeParams {
@@ -149,6 +150,17 @@ size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstat
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate);
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);
+
+// Allocation-free backward: its workspace is a device array of
+// kBwdScratchBytes that the library holds on every device it runs on.
+// bwd_noalloc_bytes: the part of it a call needs (its dB / dC partials for
+// the call's channel groups, and the block states unless the forward's
+// saved record is passed); bwd_scratch: the array's address on the current
+// device (looked up once per device).
+constexpr size_t kBwdScratchBytes = size_t(96) << 20;
+constexpr int kMaxDevices = 64;
+size_t bwd_noalloc_bytes(const BwdParams &p, bool bf16);
+hipError_t bwd_scratch(void **ptr);
 hipError_t launch_state_update(const DecodeParams &p, bool bf16, hipStream_t stream);
 
 // Mamba-2 SSD forward: scalar A per head, state headdim x dstate per head.

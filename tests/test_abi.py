@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 9
+    assert lib.ss_abi_version() == 10
 
 
 def test_ckpt_size(lib):
@@ -358,3 +358,24 @@ def test_conv_and_ssd_grid_limits(lib):
     assert _cbwd(lib, batch=1, dim=1 << 26, seqlen=16) == EUNSUP and "2^32" in _msg(lib)
     # the SSD kernels take one block of up to 512 threads per (batch, head)
     assert _ssd(lib, batch=1 << 12, nheads=1 << 12) == EUNSUP and "2^32" in _msg(lib)
+
+
+def test_bwd_noalloc_validates_like_ss_bwd(lib):
+    binding.load()   # sets the argument types
+    assert lib.ss_bwd_noalloc_max_scratch() == 96 << 20
+
+    def call(**over):
+        a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, dout=FAKE, du=FAKE, ddelta=FAKE,
+                 dA=FAKE, dB=FAKE, dC=FAKE, D=None, dD=None, ckpt=None, batch=2, dim=32, seqlen=64)
+        a.update(over)
+        return lib.ss_bwd_noalloc(a["batch"], a["dim"], 16, a["seqlen"], 0, a["u"], a["delta"],
+                                  a["A"], a["B"], a["C"], a["D"], None, None, 1, None, a["dout"],
+                                  None, a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"],
+                                  None, None, None, a["ckpt"], None)
+    assert call(u=None) == EINVAL and "u" in _msg(lib)
+    assert call(D=FAKE) == EINVAL and "dD" in _msg(lib)
+    assert call(ckpt=MISALIGNED) == EINVAL and "ckpt" in _msg(lib)
+    assert call(dim=(1 << 28) + 16, seqlen=16) == EUNSUP and "2^32" in _msg(lib)
+    # nothing to run: succeeds without touching the device
+    assert call(batch=0, u=None, delta=None, dout=None, du=None, ddelta=None, B=None, C=None,
+                dB=None, dC=None, dA=None, A=None, dim=0) == 0
