@@ -6,29 +6,36 @@
 // with delta_t = softplus(delta_raw_t + bias[d]) -- the selective SSM that
 // the state-spaces/mamba README names under "Usage / Selective SSM".
 //
-// Work mapping (chosen for the MI355X execution model):
-//   * one lane per (row, state index n): a 64-wide wavefront holds 4 rows x
-//     16 states, one row per 16-lane DPP row; a 256-thread workgroup holds
-//     16 consecutive channels of one batch entry;
-//   * each lane runs the recurrence sequentially in time.  This is the
-//     cheapest form of the scan in arithmetic (per step and state: one
-//     exp, a multiply for delta*A, one for delta*u*B and one FMA); the
-//     parallelism comes from the batch x channel x state lanes, which fill
-//     3-5 waves per SIMD at the Mamba layer shapes;
+// Work mapping (chosen for the MI355X execution model, where every wave64
+// VALU instruction costs about four SIMD cycles and the LDS, shared by the
+// four SIMDs of a compute unit, takes about four and a half cycles per
+// wavefront read of up to 16 bytes per lane and moves about 80 bytes per
+// cycle on writes):
+//   * one lane per (row, state index n) for the recurrence: a 64-wide
+//     wavefront holds 4 rows x 16 states, one row per 16-lane DPP row; a
+//     256-thread workgroup holds 16 consecutive channels of one batch entry;
+//   * each lane runs the recurrence sequentially in time: per step and state
+//     one exp, a multiply for delta*A, one for (delta u)*B and one FMA --
+//     the least arithmetic any form of the scan needs (the parallelism comes
+//     from the batch x channel x state lanes);
 //   * time runs in chunks of 64 steps.  B and C, which all channels share,
-//     are staged through LDS with coalesced 16-byte loads into two buffers
-//     (one barrier per chunk), prefetched a chunk ahead into registers;
-//   * per-element work (softplus, delta*u, gate) is done once per element by
-//     the lane whose index in its DPP row equals the element's step within a
-//     16-step block; that lane loads its u, delta and z straight from global
-//     memory a chunk ahead (a row's 16 lanes read 16 consecutive elements),
-//     and the scan lanes take delta and delta*u from it with a DPP row
-//     broadcast folded into their multiplies;
-//   * the output's sum over the 16 states goes through a per-wave LDS
-//     transpose every 16 steps, padded so that neither the 16-byte writes
-//     nor the 4-byte reads hit the same bank twice, and is added in a fixed
-//     order -- a row's bits do not depend on the batch size or on the other
-//     rows of its workgroup;
+//     are staged through LDS as [state][time], prefetched a chunk ahead into
+//     registers and stashed into the other of two LDS buffers, so a chunk
+//     needs one barrier;
+//   * per-element work (softplus, delta*u, the output, the gate) is done once
+//     per element by the lane whose index in its DPP row equals the
+//     element's step within a 16-step block; the scan lanes take delta and
+//     delta*u from it with a DPP row broadcast folded into their multiplies;
+//   * the output sum_n C h needs, at each step, a sum across the 16 lanes of
+//     a row.  Every 16 steps a lane holds its 16 terms C h, and a register
+//     butterfly of DPP adds over the row (levels n ^ 15 and n ^ 7 split by
+//     bank mask, n ^ 2 and n ^ 1 with a select) leaves lane n the sum of
+//     step n, in a fixed tree, with no LDS traffic.  Measured against an LDS
+//     transpose with one FMA chain per step (fewer VALU ops, but the LDS of a
+//     compute unit, shared by its four SIMDs, then became the limit) and
+//     against one DPP level plus a half transpose, the register butterfly
+//     was the fastest.  The backward recomputes the pre-gate output with the
+//     same butterfly, so a saved and a recomputed value are the same bits;
 //   * d_state above 16 runs one 16-state slice per grid z: each slice
 //     writes its sums over its states as f32 partials (no D term, no gate),
 //     and a combine kernel adds the slices in ascending order, adds D u and
@@ -44,14 +51,11 @@ namespace {
 
 constexpr int kT = 64;          // time steps per LDS chunk
 constexpr int kPitch = kT + 4;  // f32 B / C tile pitch (conflict-free 16-byte reads)
-constexpr int kYN = 20;         // transpose: floats per state entry (16 + 4 pad)
-constexpr int kYRow = 16 * kYN + 16;  // transpose: floats per row (row offset = 16 banks)
 
 // NW wavefronts (4 NW channels) per workgroup.  B and C (shared by all
 // channels) and, for 2-byte types, the element tiles go through LDS in two
 // buffers: chunk c uses buffer c & 1 while the next chunk's tiles are
-// stashed into the other.  Each wavefront has its own transpose region for
-// the sums over the states.
+// stashed into the other.
 template <typename T, int NW>
 struct FwdSmem {
     static constexpr uint32_t kB = 0;                          // within a buffer
@@ -61,8 +65,7 @@ struct FwdSmem {
     static constexpr uint32_t kDl = kU + kElem;
     static constexpr uint32_t kZ = kDl + kElem;
     static constexpr uint32_t kBC = kZ + kElem;                // one buffer
-    static constexpr uint32_t kY = 2 * kBC;                    // [wave NW][row 4][kYRow]
-    static constexpr uint32_t kSize = kY + NW * 4 * kYRow * 4;
+    static constexpr uint32_t kSize = 2 * kBC;
 };
 
 template <int J>
@@ -73,10 +76,10 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
     v = c * h;
 }
 
-// NW: wavefronts per workgroup (4 or 12; 4 NW channels).  PART: one slice
-// of several (grid z); the output is the slice's f32 partial sum of C h.
+// NW: wavefronts per workgroup (4 channels each).  PART: one slice of
+// several (grid z); the output is the slice's f32 partial sum of C h.
 template <typename T, int VEC, int NW, bool PART>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) : 1) void ss_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) void ss_fwd_kernel(FwdParams p) {
     using OutT = std::conditional_t<PART, float, T>;
     using SM = FwdSmem<T, NW>;
     constexpr bool kStage = kStageElems<T>;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
     // this slice's states: s0 .. s0 + Ns - 1 of Nst; lanes n >= Ns carry
-    // zero A, B, C
+    // zero A and B, and the C^T tile zero C
     const int Nst = p.nstate;
     const int s0 = PART ? 16 * int(blockIdx.z) : 0;
     const int Ns = PART ? (Nst - s0 < kN ? Nst - s0 : kN) : Nst;
@@ -185,7 +188,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
                                (b * Dm + dw) * nck * kN
                          : nullptr;
     const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
-    float *ybuf = reinterpret_cast<float *>(smem + SM::kY) + wave * 4 * kYRow + rw * kYRow;
     OutT *yb = (PART ? reinterpret_cast<OutT *>(p.ypart + blockIdx.z * size_t(p.batch * Dm * L))
                      : static_cast<OutT *>(p.out)) +
                wavebase;
@@ -223,15 +225,34 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
         }
         if (c + 1 < nchunks) load_next(t0 + kT);
 
-        // Output sums over the 16 states go through this wave's LDS region:
-        // block s writes its per-state terms four steps at a time; their
-        // transposed reads are issued at the start of block s + 1 and summed
-        // at its end, so the LDS round trip overlaps the next 16 steps.
-        float part[16];
-        auto finish = [&](int s) {
-            // in the order of the backward's register butterfly, so the
-            // saved pre-gate output matches its recomputation bit for bit
-            const float ypre = row_tree_sum(part) + dskip * uu[s];
+#pragma unroll
+        for (int s = 0; s < kE; s++) {
+            if (save_ck && (16 * s) % kCkptSpacing == 0) {   // state entering a checkpoint block
+                const int k = (t0 + 16 * s) / kCkptSpacing;
+                if (row_ok && k < nckS) st_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)), h);
+            }
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float4 bq = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
+                const float4 cq = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
+                switch (q) {
+#define SS_STEP4(Q)                                                                  \
+    case Q:                                                                          \
+        scan_step<4 * Q + 0>(dl[s], dlu[s], a2, bq.x, cq.x, h, v[4 * Q + 0]);        \
+        scan_step<4 * Q + 1>(dl[s], dlu[s], a2, bq.y, cq.y, h, v[4 * Q + 1]);        \
+        scan_step<4 * Q + 2>(dl[s], dlu[s], a2, bq.z, cq.z, h, v[4 * Q + 2]);        \
+        scan_step<4 * Q + 3>(dl[s], dlu[s], a2, bq.w, cq.w, h, v[4 * Q + 3]);        \
+        break;
+                    SS_STEP4(0) SS_STEP4(1) SS_STEP4(2) SS_STEP4(3)
+#undef SS_STEP4
+                }
+            }
+            // the output of the lane's own step 16 s + n: its 16 terms summed
+            // over the row by the register butterfly, + D u, the gate, the store
+            const float sum = row_transpose_sum(reinterpret_cast<const float(&)[8]>(v[0]),
+                                                reinterpret_cast<const float(&)[8]>(v[8]), n);
+            const float ypre = PART ? sum : sum + dskip * uu[s];
             float y = ypre;
             if (has_z) y *= zz[s] * sigmoid_f32(zz[s]);
             // a row's 16 lanes store 16 consecutive outputs
@@ -240,49 +261,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (sizeof(T) == 4 
                 st_global(at_bytes(yb, uint32_t(rowel + t) * uint32_t(sizeof(OutT))), from_f32<OutT>(y));
                 if (save_yp) st_global(at_bytes(ypb, uint32_t(rowel + t) * 4u), ypre);
             }
-        };
-#pragma unroll
-        for (int s = 0; s < kE; s++) {
-            if (save_ck && (16 * s) % kCkptSpacing == 0) {   // state entering a checkpoint chunk
-                const int k = (t0 + 16 * s) / kCkptSpacing;
-                if (row_ok && k < nckS) st_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)), h);
-            }
-            float4 bq[4], cq[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                bq[q] = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
-                cq[q] = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
-            }
-            if (s > 0) {
-#pragma unroll
-                for (int k = 0; k < 16; k++) part[k] = ybuf[k * kYN + n];
-            }
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                float v[4];
-                switch (q) {
-#define SS_STEP4(Q)                                                                  \
-    case Q:                                                                          \
-        scan_step<4 * Q + 0>(dl[s], dlu[s], a2, bq[Q].x, cq[Q].x, h, v[0]);          \
-        scan_step<4 * Q + 1>(dl[s], dlu[s], a2, bq[Q].y, cq[Q].y, h, v[1]);          \
-        scan_step<4 * Q + 2>(dl[s], dlu[s], a2, bq[Q].z, cq[Q].z, h, v[2]);          \
-        scan_step<4 * Q + 3>(dl[s], dlu[s], a2, bq[Q].w, cq[Q].w, h, v[3]);          \
-        break;
-                    SS_STEP4(0) SS_STEP4(1) SS_STEP4(2) SS_STEP4(3)
-#undef SS_STEP4
-                }
-                // in-order LDS: this write lands after the reads issued above
-                *reinterpret_cast<float4 *>(&ybuf[n * kYN + 4 * q]) =
-                    make_float4(v[0], v[1], v[2], v[3]);
-            }
-            if (s > 0) finish(s - 1);
         }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int k = 0; k < 16; k++) part[k] = ybuf[k * kYN + n];
-        finish(kE - 1);
 
-        // The next chunk's B / C go to the other buffer, whose last readers
+        // The next chunk's tiles go to the other buffer, whose last readers
         // (the chunk before this one) are behind the previous barrier.
         if (c + 1 < nchunks) st.stash(smem + ((c + 1) & 1) * SM::kBC, zero_dead);
         __syncthreads();
