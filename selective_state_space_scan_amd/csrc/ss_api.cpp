@@ -364,11 +364,12 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dty
                           void *stream) {
     ss_status st = check_dims(batch, dim, dstate, 1, io_dtype, false);
     if (st != SS_OK) return st;
-    // 4 lanes per (batch, channel) row
-    if (!grid_fits((batch * dim + 63) / 64, 256))
+    // 4 lanes per (batch, channel) row; grid x = channel blocks of 64 rows,
+    // grid y = batch entry (at most 65535)
+    if (batch > kMaxBatch || !grid_fits((dim + 63) / 64, 256))
         return fail(SS_EUNSUPPORTED,
-                    "batch * dim %lld: the state update's launch grid would exceed 2^32 "
-                    "work-items", (long long)(batch * dim));
+                    "batch %lld, dim %lld: the state update's launch grid would exceed 2^32 "
+                    "work-items or 65535 batch entries", (long long)batch, (long long)dim);
     Check c;
     if (batch > 0 && dim > 0) {
         c.need(state, "state"); c.need(u, "u"); c.need(delta, "delta"); c.need(A, "A");

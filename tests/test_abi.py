@@ -348,9 +348,10 @@ def test_slice_combine_and_fold_grid_limits(lib):
 
 
 def test_decode_grid_limit(lib):
+    # one grid row per batch entry: at most 65535 of them
     st = lib.ss_state_update(1 << 20, 1 << 11, 16, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                              None, None, 1, FAKE, None)
-    assert st == EUNSUP and "2^32" in _msg(lib)
+    assert st == EUNSUP and "65535" in _msg(lib)
 
 
 def test_conv_and_ssd_grid_limits(lib):
