@@ -504,7 +504,7 @@ def _scan_call(name, to_dev, dev):
                                                 out=out)), (d, out)
     y = torch.empty_like(d["u"])
     last = (torch.empty(w.batch, w.dim, w.dstate, device=dev) if w.last_state else None)
-    if w.kind == "fwd":
+    if w.kind == "fwd" or name.startswith("fwd"):
         return (lambda: binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                        d["delta_bias"], True, out=y, last_state=last)), (d, y, last)
     ws = torch.empty(binding.ss_bwd_workspace_size(w.batch, w.dim, w.dstate, w.seqlen, io),
@@ -531,6 +531,9 @@ PROFILE_WORKLOADS = {
     "fwd_bf16_8x1536x2048": "mamba130m_fwd_bf16_8x1536x2048",
     "fwd_bf16_4x5120x4096": "mamba2p8b_fwd_bf16_4x5120x4096",
     "decode_bf16_256x5120": "decode_bf16_256x5120",
+    "fwd_bf16_1x1536x16384": "mamba130m_long_bf16_1x1536x16384",
+    "step_bf16_1x1536x16384": "mamba130m_long_bf16_1x1536x16384",
+    "bwd_bf16_1x1536x16384_standalone": "mamba130m_long_bf16_1x1536x16384",
     "copy_1GiB": None,
 }
 

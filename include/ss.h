@@ -99,9 +99,17 @@ const char *ss_last_error(void);
  */
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 
-/* Bytes of device workspace ss_fwd needs: 0 for dstate <= 16; above, the
- * f32 per-slice partial sums over states, ceil(dstate / 16) * batch * dim *
- * seqlen floats. */
+/* Bytes of device workspace ss_fwd needs (f32, 0 when none):
+ *   - above 16 states, the per-slice partial sums over states,
+ *     ceil(dstate / 16) * batch * dim * seqlen floats;
+ *   - for a long sequence over few channels (seqlen >= 8192 and fewer than
+ *     3072 wavefronts of 4 channels x 16 states per batch entry), the time
+ *     segments' summaries: 2 * ceil(dstate / 16) * (nseg - 1) * batch * dim
+ *     * 16 floats, nseg = the number of segments (at most 64), after the
+ *     partials at the next 256-byte boundary.
+ * Whether the scan is cut into time segments, and into how many, depends on
+ * (dim, dstate, seqlen) only: a row's results never depend on the batch
+ * size. */
 size_t ss_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 
 /*
@@ -115,6 +123,12 @@ size_t ss_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
  *                     "Features", sizes state dimensions up to 256).  Above
  *                     16 the scan runs one pass per 16-state slice and adds
  *                     the slices' sums in ascending order.
+ *   Long sequences over few channels (see ss_fwd_workspace_size) run as
+ *   parallel time segments: a first pass gives every segment but the last
+ *   its (total decay, end state from zero) pair -- the scan's associative
+ *   operator (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) applied to the
+ *   segment -- and each segment then starts from the state those pairs give
+ *   over the segments before it, combined in ascending order.
  *   workspace         ss_fwd_workspace_size() bytes of caller-owned device
  *                     memory, 16-byte aligned (NULL when that is 0).
  *   io_dtype          SS_F32 or SS_BF16: dtype of u, delta, B, C, z, out.

@@ -152,6 +152,24 @@ int device_cus() {
     return v;
 }
 
+int scan_segments(int64_t dim, int nstate, int64_t seqlen, int *seg_len) {
+    // Wavefronts one batch entry gives the sequential scan: 4 rows of 16
+    // states each.  With fewer than 3072 (3 per SIMD of the 256-CU chip) and
+    // a long sequence, cut time into segments of at least 1024 steps until
+    // one batch entry gives about 3072.  Short sequences (< 8192 steps) keep
+    // one segment: the summary pass would cost more than it gives back.
+    const int64_t waves = (dim + 3) / 4 * state_slices(nstate);
+    *seg_len = int(seqlen);
+    if (seqlen < 8192 || waves <= 0 || waves >= 3072) return 1;
+    int64_t nseg = (6144 + waves - 1) / waves;
+    if (nseg > seqlen / 1024) nseg = seqlen / 1024;
+    if (nseg > 64) nseg = 64;
+    if (nseg < 2) return 1;
+    const int64_t len = ((seqlen + nseg - 1) / nseg + 63) / 64 * 64;
+    *seg_len = int(len);
+    return int((seqlen + len - 1) / len);
+}
+
 int scan_waves(int64_t batch, int64_t dim) {
     const int64_t cus = device_cus();
     const int64_t wg4 = batch * ((dim + 15) / 16), wg12 = batch * ((dim + 47) / 48);

@@ -135,18 +135,6 @@ __host__ __device__ inline Workspace slice_ws(Workspace w, int k) {
     return w;
 }
 
-template <int M>
-__device__ __forceinline__ float xor_add(float v) {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                                     (M << 10) | 0x1f));
-}
-
-// Sum over the 16 lanes of a DPP row; pairs are combined commutatively, so
-// every lane of the row ends with the same bits.
-__device__ __forceinline__ float row_sum16(float v) {
-    return xor_add<8>(xor_add<4>(xor_add<2>(xor_add<1>(v))));
-}
-
 // value of lane (n + 8) mod 16 of the same DPP row
 __device__ __forceinline__ float row_ror8(float v) {
     return __builtin_bit_cast(

@@ -197,4 +197,16 @@ __device__ __forceinline__ float row_transpose_sum(const float (&lo)[8], const f
     return x1[0];
 }
 
+template <int M>
+__device__ __forceinline__ float xor_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                     (M << 10) | 0x1f));
+}
+
+// Sum over the 16 lanes of a DPP row; pairs are combined commutatively, so
+// every lane of the row ends with the same bits.
+__device__ __forceinline__ float row_sum16(float v) {
+    return xor_add<8>(xor_add<4>(xor_add<2>(xor_add<1>(v))));
+}
+
 }  // namespace ssk

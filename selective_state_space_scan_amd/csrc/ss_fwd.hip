@@ -76,8 +76,131 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
     v = c * h;
 }
 
+// Where segment j's summary (end state from zero, then total decay) of
+// slice sl, batch entry b, row d, state n lives.
+__device__ __forceinline__ size_t summ_index(const FwdParams &p, int sl, int j, int64_t b,
+                                             int64_t d, int n) {
+    return ((size_t(sl) * (p.nseg - 1) + j) * p.batch + b) * p.dim * kN + d * kN + n;
+}
+__device__ __forceinline__ size_t summ_decay_offset(const FwdParams &p) {
+    return size_t(state_slices(p.nstate)) * (p.nseg - 1) * p.batch * p.dim * kN;
+}
+
+// The summary pass of a segmented scan: every segment but the last from a
+// zero state, the recurrence only, writing the segment's end state and its
+// total decay exp(A sum delta).  16 channels (4 wavefronts) per workgroup,
+// B, u and delta staged through LDS in 64-step chunks; grid z holds
+// (slice, segment < nseg - 1).
+constexpr int kTS = 64;
+constexpr int kPitchS = kTS + 4;
+
+template <typename T>
+struct SumSmem {
+    static constexpr uint32_t kB = 0;
+    static constexpr uint32_t kU = kB + kN * kPitchS * 4;
+    static constexpr uint32_t kDl = kU + 16 * kTS * sizeof(T);
+    static constexpr uint32_t kSize = kDl + 16 * kTS * sizeof(T);
+};
+
+template <int J>
+__device__ __forceinline__ float state_step(float dl, float dlu, float a2, float b, float h) {
+    return __builtin_fmaf(exp2_hw(row_bcast<J>(dl) * a2), h, row_bcast<J>(dlu) * b);
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
+    using SM = SumSmem<T>;
+    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
+    float(*sB)[kPitchS] = reinterpret_cast<float(*)[kPitchS]>(smem + SM::kB);
+    const T(*sU)[kTS] = reinterpret_cast<const T(*)[kTS]>(smem + SM::kU);
+    const T(*sDl)[kTS] = reinterpret_cast<const T(*)[kTS]>(smem + SM::kDl);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, r = wave * 4 + (lane >> 4);
+    const int64_t L = p.seqlen, Dm = p.dim, b = blockIdx.y;
+    const int64_t d0 = int64_t(blockIdx.x) * 16, d = d0 + r;
+    const bool row_ok = d < Dm;
+    const int valid_rows = int(Dm - d0 < 16 ? Dm - d0 : 16);
+    const int nz = p.nseg - 1;
+    const int slice = int(blockIdx.z) / nz, seg = int(blockIdx.z) % nz;
+    const int Nst = p.nstate, s0 = 16 * slice;
+    const int Ns = Nst - s0 < kN ? Nst - s0 : kN;
+    const bool st_ok = row_ok && n < Ns;
+    const float a2 = st_ok ? p.A[d * Nst + s0 + n] * kLog2e : 0.0f;
+    const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
+    const T *gB = static_cast<const T *>(p.B) + (b * Nst + s0) * L;
+    const T *gu = static_cast<const T *>(p.u) + (b * Dm + d0) * L;
+    const T *gdl = static_cast<const T *>(p.delta) + (b * Dm + d0) * L;
+    ChunkStager<T, VEC, kTS, 3, 256> st;
+    st.init(
+        [&](int i) -> TileSrc<T> {
+            switch (i) {
+                case 0: return {gB, L, Ns, SM::kB, kPitchS, true};
+                case 1: return {gu, L, valid_rows, SM::kU, kTS, false};
+                default: return {gdl, L, valid_rows, SM::kDl, kTS, false};
+            }
+        },
+        tid);
+    // a segment before the last: whole 64-step chunks
+    const int64_t tbeg = int64_t(seg) * p.seg_len;
+    const int nchunk = p.seg_len / kTS;
+    float h = 0.0f, dlsum = 0.0f;
+    st.fetch(tbeg, L, tid);
+    st.stash(smem, Ns < kN);
+    __syncthreads();
+    for (int c = 0; c < nchunk; c++) {
+        const int64_t t0 = tbeg + int64_t(c) * kTS;
+        if (c + 1 < nchunk) st.fetch(t0 + kTS, L, tid);
+        float dl[kTS / 16], dlu[kTS / 16];
+#pragma unroll
+        for (int s = 0; s < kTS / 16; s++) {
+            const int col = 16 * s + n;
+            float x = to_f32<T>(sDl[r][col]) + bias;
+            if (p.softplus) x = softplus_f32(x);
+            dl[s] = row_ok ? x : 0.0f;
+            dlu[s] = dl[s] * to_f32<T>(sU[r][col]);
+            dlsum += dl[s];
+        }
+#pragma unroll
+        for (int s = 0; s < kTS / 16; s++) {
+            const float dls = dl[s], dlus = dlu[s];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float4 b4 = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
+                switch (q) {
+#define SS_SSTEP4(Q)                                                       \
+    case Q:                                                                \
+        h = state_step<4 * Q + 0>(dls, dlus, a2, b4.x, h);                 \
+        h = state_step<4 * Q + 1>(dls, dlus, a2, b4.y, h);                 \
+        h = state_step<4 * Q + 2>(dls, dlus, a2, b4.z, h);                 \
+        h = state_step<4 * Q + 3>(dls, dlus, a2, b4.w, h);                 \
+        break;
+                    SS_SSTEP4(0) SS_SSTEP4(1) SS_SSTEP4(2) SS_SSTEP4(3)
+#undef SS_SSTEP4
+                }
+            }
+        }
+        // the state is complete before the barrier: left free, the
+        // register-only recurrence sinks past it into the next iteration,
+        // with every broadcast of the chunk live across the loop edge
+        __asm__ volatile("" : "+v"(h));
+        __syncthreads();
+        if (c + 1 < nchunk) st.stash(smem, Ns < kN);
+        __syncthreads();
+    }
+    // the decay exp(A sum delta) from the row's delta sum, formed in one
+    // fixed tree over its 16 lanes (every lane gets the same bits)
+    const float tot = row_sum16(dlsum);
+    if (row_ok) {
+        const size_t i = summ_index(p, slice, seg, b, d, n);
+        p.summ[i] = h;
+        p.summ[summ_decay_offset(p) + i] = exp2_hw(a2 * tot);
+    }
+}
+
 // NW: wavefronts per workgroup (4 channels each).  PART: one slice of
-// several (grid z); the output is the slice's f32 partial sum of C h.
+// several; the output is the slice's f32 partial sum of C h.  Grid z holds
+// (slice, time segment).
 template <typename T, int VEC, int NW, bool PART>
 __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) void ss_fwd_kernel(FwdParams p) {
     using OutT = std::conditional_t<PART, float, T>;
@@ -104,16 +227,29 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
-    // this slice's states: s0 .. s0 + Ns - 1 of Nst; lanes n >= Ns carry
-    // zero A and B, and the C^T tile zero C
+    // grid z: (slice, segment); this slice's states: s0 .. s0 + Ns - 1 of
+    // Nst; lanes n >= Ns carry zero A, B and C
+    const int slice = int(blockIdx.z) / p.nseg, seg = int(blockIdx.z) % p.nseg;
     const int Nst = p.nstate;
-    const int s0 = PART ? 16 * int(blockIdx.z) : 0;
+    const int s0 = PART ? 16 * slice : 0;
     const int Ns = PART ? (Nst - s0 < kN ? Nst - s0 : kN) : Nst;
     const bool st_ok = row_ok && n < Ns;
     float a2 = st_ok ? p.A[d * Nst + s0 + n] * kLog2e : 0.0f;  // A in base-2 exponent units
     float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
     float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Nst + s0 + n] : 0.0f;
+    if (seg > 0 && row_ok) {
+        // the state entering this segment: the segments before it, each a
+        // (decay, end state from zero) pair, applied in ascending order
+        const float *sh = p.summ, *sd = p.summ + summ_decay_offset(p);
+        for (int j = 0; j < seg; j++) {
+            const size_t i = summ_index(p, slice, j, b, d, n);
+            h = __builtin_fmaf(sd[i], h, sh[i]);
+        }
+    }
+    // this segment's steps and 64-step chunks
+    const int64_t tbeg = int64_t(seg) * p.seg_len;
+    const int64_t tend = tbeg + p.seg_len < p.seqlen ? tbeg + p.seg_len : p.seqlen;
 
     // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the
     // per-row accesses address the wavefront's 4 rows from a scalar base with
@@ -169,10 +305,11 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
             if (has_z) zn[s] = elem_at(gz, t);
         }
     };
-    const int nchunks = int((L + kT - 1) / kT);
-    if (nchunks > 0) {
-        load_next(0);
-        st.fetch(0, L, tid);
+    const int cbeg = int(tbeg / kT);
+    const int cend = int((tend + kT - 1) / kT);
+    if (cend > cbeg) {
+        load_next(cbeg * kT);
+        st.fetch(int64_t(cbeg) * kT, L, tid);
         st.stash(smem, zero_dead);
     }
     // Make the per-row parameter loads complete here.  Left pending into the
@@ -184,25 +321,26 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
     const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
     const int nckS = int(nck);
     const bool save_ck = p.ckpt != nullptr;
-    float *ckb = save_ck ? p.ckpt + blockIdx.z * ckpt_state_floats(p.batch, Dm, L) +
+    float *ckb = save_ck ? p.ckpt + slice * ckpt_state_floats(p.batch, Dm, L) +
                                (b * Dm + dw) * nck * kN
                          : nullptr;
     const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
-    OutT *yb = (PART ? reinterpret_cast<OutT *>(p.ypart + blockIdx.z * size_t(p.batch * Dm * L))
+    OutT *yb = (PART ? reinterpret_cast<OutT *>(p.ypart + slice * size_t(p.batch * Dm * L))
                      : static_cast<OutT *>(p.out)) +
                wavebase;
     // the pre-gate output, saved for the backward's dz
     const bool save_yp = p.ypre && has_z;
     float *ypb = save_yp ? p.ypre + wavebase : nullptr;
-    for (int c = 0; c < nchunks; c++) {
+    for (int c = cbeg; c < cend; c++) {
         const int t0 = c * kT;
-        char *bc = smem + (c & 1) * SM::kBC;   // this chunk's staged tiles
+        const bool more = c + 1 < cend;
+        char *bc = smem + ((c - cbeg) & 1) * SM::kBC;   // this chunk's staged tiles
         float(*sB)[kPitch] = reinterpret_cast<float(*)[kPitch]>(bc + SM::kB);
         float(*sC)[kPitch] = reinterpret_cast<float(*)[kPitch]>(bc + SM::kC);
         const T(*sU)[kT] = reinterpret_cast<const T(*)[kT]>(bc + SM::kU);
         const T(*sDl)[kT] = reinterpret_cast<const T(*)[kT]>(bc + SM::kDl);
         const T(*sZ)[kT] = reinterpret_cast<const T(*)[kT]>(bc + SM::kZ);
-        if (c + 1 < nchunks) st.fetch(t0 + kT, L, tid);
+        if (more) st.fetch(t0 + kT, L, tid);
 
         // per-element work: lane (r, n) owns elements 16 s + n of its row
         float dl[kE], dlu[kE], uu[kE], zz[kE];
@@ -223,7 +361,7 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
             dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps leave the state unchanged
             dlu[s] = dl[s] * uu[s];
         }
-        if (c + 1 < nchunks) load_next(t0 + kT);
+        if (more) load_next(t0 + kT);
 
 #pragma unroll
         for (int s = 0; s < kE; s++) {
@@ -265,11 +403,13 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
 
         // The next chunk's tiles go to the other buffer, whose last readers
         // (the chunk before this one) are behind the previous barrier.
-        if (c + 1 < nchunks) st.stash(smem + ((c + 1) & 1) * SM::kBC, zero_dead);
+        if (more) st.stash(smem + ((c + 1 - cbeg) & 1) * SM::kBC, zero_dead);
         __syncthreads();
     }
 
-    if (p.last_state && st_ok) p.last_state[(b * Dm + d) * Nst + s0 + n] = h;
+    if (p.last_state && st_ok && seg == p.nseg - 1) {
+        p.last_state[(b * Dm + d) * Nst + s0 + n] = h;
+    }
 }
 
 // Several slices: out = (sum of the slices' partials, ascending, + D u) *
@@ -314,22 +454,39 @@ __global__ __launch_bounds__(256) void ss_fwd_combine_kernel(FwdParams p, int sl
 template <typename T, int VEC, int NW, bool PART>
 void launch_scan(const FwdParams &p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((p.dim + 4 * NW - 1) / (4 * NW)),
-                    static_cast<unsigned>(p.batch), static_cast<unsigned>(state_slices(p.nstate)));
+                    static_cast<unsigned>(p.batch), static_cast<unsigned>(state_slices(p.nstate) * p.nseg));
     hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW, PART>), grid, dim3(64 * NW), 0, stream, p);
 }
 
-template <typename T>
-hipError_t launch_typed(const FwdParams &p, hipStream_t stream) {
+template <typename T, bool PART>
+void launch_scan_vec(const FwdParams &p, bool vec, hipStream_t stream) {
     constexpr int kVec = 16 / sizeof(T);
+    if (p.nseg > 1) {   // the segments' summaries first
+        const dim3 grid(static_cast<unsigned>((p.dim + 15) / 16), static_cast<unsigned>(p.batch),
+                        static_cast<unsigned>(state_slices(p.nstate) * (p.nseg - 1)));
+        if (vec) hipLaunchKernelGGL((ss_fwd_summary_kernel<T, kVec>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((ss_fwd_summary_kernel<T, 1>), grid, dim3(256), 0, stream, p);
+    }
+    if (vec) launch_scan<T, kVec, 4, PART>(p, stream);
+    else launch_scan<T, 1, 4, PART>(p, stream);
+}
+
+template <typename T>
+hipError_t launch_typed(const FwdParams &p0, hipStream_t stream) {
     // 16-byte vectors need every row start aligned: seqlen * sizeof(T) % 16 == 0
     // 4 wavefronts per workgroup: 12 would cut the B / C reads by two thirds,
-    // but this pass is not bound by memory, and three independent
-    // workgroups per compute unit overlap their barriers and LDS phases.
+    // but this pass is not bound by memory, and independent workgroups per
+    // compute unit overlap their barriers.
+    FwdParams p = p0;
     const bool vec = (p.seqlen * static_cast<int64_t>(sizeof(T))) % 16 == 0;
     const int slices = state_slices(p.nstate);
+    p.nseg = scan_segments(p.dim, p.nstate, p.seqlen, &p.seg_len);
+    if (p.nseg > 1) {   // summaries after the slice partials in the workspace
+        const size_t part = slices > 1 ? size_t(slices) * p.batch * p.dim * p.seqlen : 0;
+        p.summ = static_cast<float *>(p.ypart) + (part + 63) / 64 * 64;
+    }
     if (slices == 1) {
-        if (vec) launch_scan<T, kVec, 4, false>(p, stream);
-        else launch_scan<T, 1, 4, false>(p, stream);
+        launch_scan_vec<T, false>(p, vec, stream);
         profile_mark(stream);
         return hipGetLastError();
     }
@@ -338,8 +495,7 @@ hipError_t launch_typed(const FwdParams &p, hipStream_t stream) {
     q.D = nullptr;
     q.z = nullptr;
     q.ypre = nullptr;
-    if (vec) launch_scan<T, kVec, 4, true>(q, stream);
-    else launch_scan<T, 1, 4, true>(q, stream);
+    launch_scan_vec<T, true>(q, vec, stream);
     profile_mark(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -359,9 +515,14 @@ hipError_t launch_typed(const FwdParams &p, hipStream_t stream) {
 }  // namespace
 
 size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0) return 0;
     const int slices = state_slices(nstate);
-    if (slices == 1 || batch <= 0 || dim <= 0 || seqlen <= 0) return 0;
-    return size_t(slices) * size_t(batch) * size_t(dim) * size_t(seqlen) * sizeof(float);
+    int seg_len = 0;
+    const int nseg = scan_segments(dim, nstate, seqlen, &seg_len);
+    const size_t part = slices > 1 ? size_t(slices) * batch * dim * seqlen : 0;   // floats
+    const size_t summ = nseg > 1 ? 2 * size_t(slices) * (nseg - 1) * batch * dim * kN : 0;
+    if (part + summ == 0) return 0;
+    return ((part + 63) / 64 * 64 + summ) * sizeof(float);
 }
 
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream) {

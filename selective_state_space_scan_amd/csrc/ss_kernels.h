@@ -59,12 +59,29 @@ __host__ __device__ inline size_t ckpt_bytes(int64_t batch, int64_t dim, int64_t
            sizeof(float);
 }
 
+// Time segments.  A long sequence over few (row, state) lanes leaves most of
+// the chip idle, so the scan can cut time into nseg segments of seg_len
+// steps (a multiple of 64; the last one takes the rest) that run in
+// parallel: a summary pass runs every segment but the last from a zero state
+// and records its end state and its total decay exp(A sum delta) -- the
+// (decay, input) pair of the segment under the scan's associative operator
+// (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) -- and each segment then starts
+// from the state those pairs give, combined over the segments before it in
+// ascending order.  The number of segments depends on (dim, dstate, seqlen)
+// only, so a row's bits never depend on the batch size.  Returns nseg (1 =
+// one sequential pass) and sets *seg_len.
+int scan_segments(int64_t dim, int nstate, int64_t seqlen, int *seg_len);
+
 struct FwdParams : ScanParams {
     void *out;
     float *last_state;
     float *ckpt;   // block states, or nullptr
     float *ypre;   // pre-gate output (written when z is given), or nullptr
     float *ypart;  // workspace, several slices: (slice, batch, dim, L) partial sums of C h
+    int nseg = 1;          // time segments (scan_segments)
+    int seg_len = 0;       // steps per segment
+    float *summ = nullptr; // workspace, nseg > 1: per (slice, segment < nseg - 1, batch,
+                           // dim, 16) the segment's end state from zero, then its decay
 };
 
 struct BwdParams : ScanParams {

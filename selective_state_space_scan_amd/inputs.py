@@ -70,6 +70,10 @@ WORKLOADS = {
                  seed=SEED_BASE + 4),
         Workload("mamba130m_bwd_bf16_8x1536x2048", "bwd", 8, 1536, 16, 2048, "bf16",
                  seed=SEED_BASE + 5),
+        # a long prefill of one sequence: too few (row, state) lanes to fill
+        # the chip, the case the time-segmented scan serves
+        Workload("mamba130m_long_bf16_1x1536x16384", "bwd", 1, 1536, 16, 16384, "bf16",
+                 seed=SEED_BASE + 6),
     ]
 }
 

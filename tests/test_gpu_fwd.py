@@ -173,3 +173,52 @@ def test_fwd_wide_state_rows_do_not_depend_on_batch():
         torch.cuda.synchronize()
         assert torch.equal(y1[0].view(torch.int16), y[bi].view(torch.int16)), f"y entry {bi}"
         assert torch.equal(l1[0], last[bi]), f"last_state entry {bi}"
+
+
+# Long sequences over few channels take the time-segmented scan (chosen from
+# dim, dstate and seqlen only): a summary pass per segment, then every segment
+# from the state its predecessors' (decay, end state) pairs give.  Seqlen
+# 8192 and up with fewer than 3072 wavefronts per batch entry; 64 channels
+# give 8 segments of 1024+ steps.
+SEGMENTED = [
+    # batch, dim, dstate, L, io
+    (2, 64, 16, 8192, "f32"),        # 8 segments of 1024 steps
+    (2, 48, 16, 8229, "bf16"),       # ragged: segments of 1088 steps, a short ragged last one
+    (1, 40, 16, 9001, "f32"),        # rows not 16-byte aligned (scalar path), ragged channels
+    (2, 32, 40, 8300, "bf16"),       # three 16-state slices x 8 segments
+]
+
+
+@pytest.mark.parametrize("batch,dim,N,L,io", SEGMENTED)
+def test_fwd_time_segments_elementwise(batch, dim, N, L, io):
+    require_gpu()
+    w = ssin.custom("fwd", batch, dim, N, L, io, seed=batch + dim + N + L)
+    arr = ssin.make(w)
+    say(f"fwd segmented {w.name}")
+    d = dev_inputs(arr)
+    h0 = np.random.default_rng(L).standard_normal((batch, dim, N)).astype(np.float32)
+    for use_h0 in (False, True):
+        y, last = run_fwd(d, w, h0=to_dev(h0) if use_h0 else None, last=True)
+        torch.cuda.synchronize()
+        ry, rl = oracle_fwd(arr, w.softplus, h0=h0.astype(np.float64) if use_h0 else None)
+        e = assert_close(to_host(y), ry, TOL[io], f"y h0={use_h0}")
+        assert_close(to_host(last), rl, TOL["f32"], f"last_state h0={use_h0}")
+        say(f"  h0={use_h0} max err {e:.3e}")
+
+
+def test_fwd_time_segments_batch_invariant_and_deterministic():
+    require_gpu()
+    w = ssin.custom("fwd", 3, 64, 16, 8192, "bf16", seed=77)
+    d = dev_inputs(ssin.make(w))
+    y1, l1 = run_fwd(d, w, last=True)
+    y2, l2 = run_fwd(d, w, last=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    for b in range(w.batch):
+        one = {k: (v[b:b + 1].contiguous() if k in ("u", "delta", "z", "B", "C") else v)
+               for k, v in d.items()}
+        ya, la = run_fwd(one, w, last=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ya[0].view(torch.int16), y1[b].view(torch.int16)), f"entry {b}"
+        assert torch.equal(la[0], l1[b]), f"last_state entry {b}"
