@@ -167,6 +167,15 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
  *                      16-byte aligned, owned by the caller, not read before written.
  * Every sum over batch, time or channels runs in a fixed order, with no
  * atomics, so the gradients are bit-reproducible.
+ * Long sequences over few channels run as ss_fwd's time segments (the same
+ * count, from dim, dstate and seqlen only): the block states segment by
+ * segment after the forward's summary pass (when ckpt is NULL), then the
+ * reverse pass segment by segment after an adjoint summary pass -- each
+ * segment but the first records, from a zero adjoint, the adjoint leaving
+ * its first step and its total decay exp(A sum delta), and a segment's
+ * entering adjoint combines those of the later segments from the last down.
+ * The dA, dD and ddelta_bias sums then run over (batch entry, segment) in
+ * ascending order.
  */
 ss_status ss_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
                  const void *u, const void *delta, const float *A, const void *B,

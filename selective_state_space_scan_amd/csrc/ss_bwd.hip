@@ -39,8 +39,16 @@
 //        - B and C are staged through two LDS buffers; u, delta, z and dout
 //          are loaded by the lane that owns each element, a chunk ahead;
 //   3. fold: adds the dB/dC partials over channel groups in ascending group
-//      order and the dA/dD/dbias partials over the batch in ascending batch
-//      order.
+//      order and the dA/dD/dbias partials over the batch (and time segments)
+//      in ascending order.
+// A long sequence over few channels is cut into the forward's time
+// segments (scan_segments, from dim, dstate and seqlen only), each run by
+// its own workgroups: the block states segment by segment after the
+// forward's summary pass, and the reverse pass segment by segment after an
+// adjoint summary pass -- each segment but the first, from a zero adjoint,
+// records the adjoint leaving its first step and the segment's total decay,
+// and a segment's entering adjoint combines those of the segments after it,
+// from the last down.
 // Every sum runs in an order fixed by the shape, with no atomics.
 #include <mutex>
 #include <type_traits>
@@ -79,6 +87,10 @@ struct Workspace {
     float *dbiasp;   // (batch, dim)
     size_t slice_bytes;       // distance between two slices' dBp .. dbiasp
     float *dup, *ddp, *dzp;   // several slices: (slice, batch, dim, L) partials
+    int nseg;        // time segments (1: one pass over the sequence)
+    int seg_len;     // steps per segment (a multiple of 64; the last takes the rest)
+    float *fsumm;    // nseg > 1, block states recomputed here: the forward's segment summaries
+    float *asumm;    // nseg > 1: the adjoint's segment summaries (segments 1 .. nseg - 1)
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -87,12 +99,15 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 // `with_ckpt`: whether it holds the block states (not needed when the
 // forward's saved record is passed).  ss_bwd's workspace always has both at
 // their largest (16-channel groups); the allocation-free entry sizes them
-// for the call.
-__host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L,
-                                           int nstate, int64_t groups, bool with_ckpt,
-                                           size_t *total) {
+// for the call.  The dA / dD / dbias partials come per time segment, in
+// (batch, segment, ...) order.
+inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L, int nstate,
+                       int64_t groups, bool with_ckpt, size_t *total) {
     const int64_t nck = (L + kCk - 1) / kCk;
     const int slices = state_slices(nstate);
+    int seg_len = 0;
+    const int nseg = scan_segments(dim, nstate, L, &seg_len);
+    const size_t summ = nseg > 1 ? 2 * seg_summ_half(nstate, nseg, batch, dim) : 0;
     size_t off = 0;
     Workspace w;
     char *p = static_cast<char *>(base);
@@ -103,14 +118,18 @@ __host__ __device__ inline Workspace carve(void *base, int64_t batch, int64_t di
     };
     w.ckpt = with_ckpt ? take(size_t(slices) * batch * dim * nck * kN) : nullptr;
     w.ypre = nullptr;
+    w.nseg = nseg;
+    w.seg_len = seg_len;
+    w.fsumm = (with_ckpt && summ) ? take(summ) : nullptr;
+    w.asumm = summ ? take(summ) : nullptr;
     const size_t first = off;
     w.dBp = take(size_t(batch) * groups * kN * L);
     w.dCp = take(size_t(batch) * groups * kN * L);
     w.groups = groups;
     w.sub = 1;
-    w.dAp = take(size_t(batch) * dim * kN);
-    w.dDp = take(size_t(batch) * dim);
-    w.dbiasp = take(size_t(batch) * dim);
+    w.dAp = take(size_t(batch) * nseg * dim * kN);
+    w.dDp = take(size_t(batch) * nseg * dim);
+    w.dbiasp = take(size_t(batch) * nseg * dim);
     w.slice_bytes = off - first;
     off += (slices - 1) * w.slice_bytes;
     w.dup = w.ddp = w.dzp = nullptr;
@@ -204,16 +223,27 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
     const int64_t d0 = int64_t(blockIdx.x) * kRows, d = d0 + r;
     const bool row_ok = d < Dm;
     const int valid_rows = int(Dm - d0 < kRows ? Dm - d0 : kRows);
-    // this slice (grid z) holds states s0 .. s0 + Ns - 1 of Nst; lanes
-    // n >= Ns carry zero A and B
-    const int Nst = p.nstate, s0 = 16 * int(blockIdx.z);
+    // grid z: (slice, time segment).  This slice holds states s0 .. s0 + Ns
+    // - 1 of Nst; lanes n >= Ns carry zero A and B
+    const int nsg = ws.nseg;
+    const int slice = int(blockIdx.z) / nsg, seg = int(blockIdx.z) % nsg;
+    const int Nst = p.nstate, s0 = 16 * slice;
     const int Ns = Nst - s0 < kN ? Nst - s0 : kN;
     const bool st_ok = row_ok && n < Ns;
     const float a2 = st_ok ? p.A[d * Nst + s0 + n] * kLog2e : 0.0f;
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Nst + s0 + n] : 0.0f;
+    if (seg > 0 && row_ok) {
+        // the state entering this segment, as the forward forms it: the
+        // earlier segments' (decay, end state from zero) in ascending order
+        const float *sh = ws.fsumm, *sd = ws.fsumm + seg_summ_half(Nst, nsg, p.batch, Dm);
+        for (int j = 0; j < seg; j++) {
+            const size_t i = seg_summ_index(nsg, p.batch, Dm, slice, j, b, d, n);
+            h = __builtin_fmaf(sd[i], h, sh[i]);
+        }
+    }
     const int64_t nck = (L + kCk - 1) / kCk;
-    float *ck = ws.ckpt + blockIdx.z * ckpt_state_floats(p.batch, Dm, L) +
+    float *ck = ws.ckpt + slice * ckpt_state_floats(p.batch, Dm, L) +
                 (b * Dm + (row_ok ? d : 0)) * nck * kN + n;
 
     const T *gB = static_cast<const T *>(p.B) + (b * Nst + s0) * L;
@@ -231,15 +261,18 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
         },
         tid);
 
-    const int64_t nchunks = (L + kT1 - 1) / kT1;
-    if (nchunks > 0) {
-        st.fetch(0, L, tid);
+    // this segment's 64-step chunks (segments are whole chunks but the last)
+    const int64_t tbeg = int64_t(seg) * ws.seg_len;
+    const int64_t tend = tbeg + ws.seg_len < L ? tbeg + ws.seg_len : L;
+    const int64_t cbeg = tbeg / kT1, cend = (tend + kT1 - 1) / kT1;
+    if (cend > cbeg) {
+        st.fetch(cbeg * kT1, L, tid);
         st.stash(smem, zero_dead);
     }
     __syncthreads();
-    for (int64_t c = 0; c < nchunks; c++) {
+    for (int64_t c = cbeg; c < cend; c++) {
         const int64_t t0 = c * kT1;
-        if (c + 1 < nchunks) st.fetch(t0 + kT1, L, tid);
+        if (c + 1 < cend) st.fetch(t0 + kT1, L, tid);
         float dl[kT1 / 16], dlu[kT1 / 16];
 #pragma unroll
         for (int s = 0; s < kT1 / 16; s++) {
@@ -272,8 +305,137 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
             }
         }
         __syncthreads();
-        if (c + 1 < nchunks) st.stash(smem, zero_dead);
+        if (c + 1 < cend) st.stash(smem, zero_dead);
         __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// kernel 1b: adjoint summaries of the time segments
+// ---------------------------------------------------------------------------
+// Each segment but the first, from a zero adjoint: the reverse recurrence
+// g_t = c + C_t dy_t, c <- abar_t g_t over the segment's steps, last to
+// first.  The adjoint leaving the segment's first step is linear in the one
+// entering its last, c_out = (product of the segment's abar) c_in + c_out(0),
+// so the pairs (exp(A sum delta), c_out(0)) of the later segments give each
+// segment its entering adjoint.  16 channels (4 wavefronts) per workgroup;
+// C, delta, z and dout staged through LDS in 64-step chunks; grid z holds
+// (slice, segment - 1).
+template <typename T>
+struct AdjSmem {
+    static constexpr uint32_t kC = 0;
+    static constexpr uint32_t kDl = kC + kN * kPitch1 * 4;
+    static constexpr uint32_t kZ = kDl + kRows * kT1 * sizeof(T);
+    static constexpr uint32_t kG = kZ + kRows * kT1 * sizeof(T);
+    static constexpr uint32_t kSize = kG + kRows * kT1 * sizeof(T);
+};
+
+// one reverse step from the carry c entering step J of a 16-step block:
+// g = c + C dy, then the carry to the step before, abar g
+template <int J>
+__device__ __forceinline__ void adj_step(float dl, float dy, float a2, float cv, float &c) {
+    c = fmac_bcast<J>(c, dy, cv);
+    c *= exp2_hw(row_bcast<J>(dl) * a2);
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void ss_bwd_adjoint_summary_kernel(BwdParams p, Workspace ws) {
+    using SM = AdjSmem<T>;
+    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
+    float(*sC)[kPitch1] = reinterpret_cast<float(*)[kPitch1]>(smem + SM::kC);
+    const T(*sDl)[kT1] = reinterpret_cast<const T(*)[kT1]>(smem + SM::kDl);
+    const T(*sZ)[kT1] = reinterpret_cast<const T(*)[kT1]>(smem + SM::kZ);
+    const T(*sG)[kT1] = reinterpret_cast<const T(*)[kT1]>(smem + SM::kG);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, r = wave * 4 + (lane >> 4);
+    const int64_t L = p.seqlen, Dm = p.dim, b = blockIdx.y;
+    const int64_t d0 = int64_t(blockIdx.x) * kRows, d = d0 + r;
+    const bool row_ok = d < Dm;
+    const int valid_rows = int(Dm - d0 < kRows ? Dm - d0 : kRows);
+    const int nsg = ws.nseg, nz = nsg - 1;
+    const int slice = int(blockIdx.z) / nz, k = int(blockIdx.z) % nz, seg = k + 1;
+    const int Nst = p.nstate, s0 = 16 * slice;
+    const int Ns = Nst - s0 < kN ? Nst - s0 : kN;
+    const bool st_ok = row_ok && n < Ns;
+    const float a2 = st_ok ? p.A[d * Nst + s0 + n] * kLog2e : 0.0f;
+    const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
+    const bool has_z = p.z != nullptr;
+    const bool zero_dead = Ns < kN;   // C rows past dstate must read as zeros
+    const T *gC = static_cast<const T *>(p.C) + (b * Nst + s0) * L;
+    const int64_t rows0 = (b * Dm + d0) * L;
+    const T *gdl = static_cast<const T *>(p.delta) + rows0;
+    const T *gz = has_z ? static_cast<const T *>(p.z) + rows0 : nullptr;
+    const T *gdo = static_cast<const T *>(p.dout) + rows0;
+    ChunkStager<T, VEC, kT1, 4, kThreads> st;
+    st.init(
+        [&](int i) -> TileSrc<T> {
+            if (i == 0) return {gC, L, Ns, SM::kC, kPitch1, true};
+            if (i == 1) return {gdl, L, valid_rows, SM::kDl, kT1, false};
+            if (i == 2) return {gz, L, valid_rows, SM::kZ, kT1, false};
+            return {gdo, L, valid_rows, SM::kG, kT1, false};
+        },
+        tid);
+    // the segment's 64-step chunks, last to first (only the last segment
+    // has a ragged end)
+    const int64_t tbeg = int64_t(seg) * ws.seg_len;
+    const int64_t tend = tbeg + ws.seg_len < L ? tbeg + ws.seg_len : L;
+    const int64_t cbeg = tbeg / kT1, cend = (tend + kT1 - 1) / kT1;
+    float c = 0.0f, dlsum = 0.0f;
+    st.fetch((cend - 1) * kT1, L, tid);
+    st.stash(smem, zero_dead);
+    __syncthreads();
+    for (int64_t ch = cend - 1; ch >= cbeg; ch--) {
+        const int64_t t0 = ch * kT1;
+        if (ch > cbeg) st.fetch(t0 - kT1, L, tid);
+        float dl[kT1 / 16], dy[kT1 / 16];
+#pragma unroll
+        for (int s = 0; s < kT1 / 16; s++) {
+            const int col = 16 * s + n;
+            const bool live = row_ok && t0 + col < L;
+            float x = to_f32<T>(sDl[r][col]) + bias;
+            if (p.softplus) x = softplus_f32(x);
+            dl[s] = live ? x : 0.0f;
+            float g = to_f32<T>(sG[r][col]);
+            if (has_z) {
+                const float zz = to_f32<T>(sZ[r][col]);
+                g *= zz * sigmoid_f32(zz);
+            }
+            dy[s] = live ? g : 0.0f;
+            dlsum += dl[s];
+        }
+#pragma unroll
+        for (int s = kT1 / 16 - 1; s >= 0; s--) {
+            const float dls = dl[s], dys = dy[s];
+#pragma unroll
+            for (int q = 3; q >= 0; q--) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
+                switch (q) {
+#define SS_ASTEP4(Q)                                       \
+    case Q:                                                \
+        adj_step<4 * Q + 3>(dls, dys, a2, c4.w, c);        \
+        adj_step<4 * Q + 2>(dls, dys, a2, c4.z, c);        \
+        adj_step<4 * Q + 1>(dls, dys, a2, c4.y, c);        \
+        adj_step<4 * Q + 0>(dls, dys, a2, c4.x, c);        \
+        break;
+                    SS_ASTEP4(0) SS_ASTEP4(1) SS_ASTEP4(2) SS_ASTEP4(3)
+#undef SS_ASTEP4
+                }
+            }
+        }
+        // the carry is complete before the barrier (left free, the
+        // register-only recurrence sinks past it into the next iteration)
+        __asm__ volatile("" : "+v"(c));
+        __syncthreads();
+        if (ch > cbeg) st.stash(smem, zero_dead);
+        __syncthreads();
+    }
+    // the decay exp(A sum delta), the delta sum formed in one fixed tree
+    // over the row's 16 lanes
+    const float tot = row_sum16(dlsum);
+    if (row_ok) {
+        const size_t i = seg_summ_index(nsg, p.batch, Dm, slice, k, b, d, n);
+        ws.asumm[i] = c;
+        ws.asumm[seg_summ_half(Nst, nsg, p.batch, Dm) + i] = exp2_hw(a2 * tot);
     }
 }
 
@@ -326,7 +488,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     using SM = RevSmem<T, NW>;
     using OutT = std::conditional_t<PART, float, T>;
     static_assert(!(PART && YP), "slices recompute their share of the pre-gate output");
-    if (PART) ws = slice_ws(ws, int(blockIdx.z));
+    // grid z: (slice, time segment)
+    const int nsg = ws.nseg;
+    const int slice = int(blockIdx.z) / nsg, seg = int(blockIdx.z) % nsg;
+    if (PART) ws = slice_ws(ws, slice);
     constexpr bool kStage = kStageElems<T>;
     constexpr int kRowsG = SM::kR;
     constexpr int kThr = 64 * NW;
@@ -345,9 +510,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
-    // this slice (grid z) holds states s0 .. s0 + Ns - 1 of Nst; lanes
-    // n >= Ns carry zero A, B, C
-    const int Nst = p.nstate, s0 = 16 * int(blockIdx.z);
+    // this slice holds states s0 .. s0 + Ns - 1 of Nst; lanes n >= Ns carry
+    // zero A, B, C
+    const int Nst = p.nstate, s0 = 16 * slice;
     const int Ns = Nst - s0 < kN ? Nst - s0 : kN;
     const bool st_ok = row_ok && n < Ns;
     const float aval = st_ok ? p.A[d * Nst + s0 + n] : 0.0f;
@@ -355,12 +520,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     const float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
     const int64_t nck = (L + kCk - 1) / kCk;   // checkpoints (16-step blocks)
-    const int64_t nch = (L + kC - 1) / kC;     // 32-step staging chunks
+    // this segment's 32-step staging chunks cbeg .. cend - 1 (segments are
+    // whole chunks but the last)
+    const int64_t tbeg = int64_t(seg) * ws.seg_len;
+    const int64_t tend = tbeg + ws.seg_len < L ? tbeg + ws.seg_len : L;
+    const int cbeg = int(tbeg / kC), cend = int((tend + kC - 1) / kC);
     // Inside the chunk loop indices are 32-bit (seqlen <= 2^26), and global
     // accesses address the wavefront's 4 rows from a scalar base with 32-bit
     // byte offsets (4 rows x seqlen x 4 bytes < 2^32).
     const int Ls = int(L), nckS = int(nck);
-    const float *ckb = ws.ckpt + blockIdx.z * ckpt_state_floats(p.batch, Dm, L) + (b * Dm + dw) * nck * kN;
+    const float *ckb = ws.ckpt + slice * ckpt_state_floats(p.batch, Dm, L) + (b * Dm + dw) * nck * kN;
     const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
     // state entering block k; a block past the end (only padding steps) has none
     auto ckpt_at = [&](int k) {
@@ -369,6 +538,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     };
 
     float g = (st_ok && p.dlast) ? p.dlast[(b * Dm + d) * Nst + s0 + n] : 0.0f;
+    if (seg < nsg - 1 && row_ok) {
+        // the adjoint entering this segment's last step: the later segments'
+        // (decay, adjoint from zero) applied from the last segment down
+        const float *sa = ws.asumm, *sd = ws.asumm + seg_summ_half(Nst, nsg, p.batch, Dm);
+        for (int j = nsg - 1; j > seg; j--) {
+            const size_t i = seg_summ_index(nsg, p.batch, Dm, slice, j - 1, b, d, n);
+            g = __builtin_fmaf(sd[i], g, sa[i]);
+        }
+    }
     float dA_acc = 0.0f;     // this lane's state entry, summed over time
     float dD_acc = 0.0f;     // elements owned by this lane
     float dbias_acc = 0.0f;
@@ -383,7 +561,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
     const T *gdo = static_cast<const T *>(p.dout) + wavebase;
-    const size_t slice_el = PART ? blockIdx.z * size_t(p.batch * Dm * L) : 0;
+    const size_t slice_el = PART ? slice * size_t(p.batch * Dm * L) : 0;
     OutT *du_b = (PART ? reinterpret_cast<OutT *>(ws.dup + slice_el) : static_cast<OutT *>(p.du)) + wavebase;
     OutT *dd_b = (PART ? reinterpret_cast<OutT *>(ws.ddp + slice_el) : static_cast<OutT *>(p.ddelta)) + wavebase;
     OutT *dz_b = has_z ? (PART ? reinterpret_cast<OutT *>(ws.dzp + slice_el) : static_cast<OutT *>(p.dz)) + wavebase
@@ -493,14 +671,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             }
         }
     };
-    if (nch > 0) {
-        load_next((int(nch) - 1) * kC);
-        st.fetch((nch - 1) * kC, L, tid);
-        st.stash(smem + ((nch - 1) & 1) * SM::kBC, zero_dead);
+    if (cend > cbeg) {
+        load_next((cend - 1) * kC);
+        st.fetch(int64_t(cend - 1) * kC, L, tid);
+        st.stash(smem + ((cend - 1) & 1) * SM::kBC, zero_dead);
     }
     __syncthreads();
 
-    for (int c = int(nch) - 1; c >= 0; c--) {
+    for (int c = cend - 1; c >= cbeg; c--) {
         const int t0 = c * kC;
         float *chw = chw0 + (c & 1) * SM::kChBuf;   // this chunk's channel-sum buffer
         char *bc = smem + (c & 1) * SM::kBC;          // and its staged tiles
@@ -523,7 +701,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         float hb[kNB];   // block states, used by the blocks after the reload
 #pragma unroll
         for (int s = 0; s < kNB; s++) hb[s] = hn[s];
-        if (c > 0) st.fetch(t0 - kC, L, tid);
+        if (c > cbeg) st.fetch(t0 - kC, L, tid);
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row
         float dl[kNB], dlu[kNB], uu[kNB], sgd[kNB], dout[kNB], zz[kNB], dyv[kNB];
@@ -558,10 +736,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             }
             if (!row_ok) dyv[s] = 0.0f;
         }
-        if (c > 0) load_next(t0 - kC);
+        if (c > cbeg) load_next(t0 - kC);
         // the previous (later) chunk's channel sums, complete since the last
         // barrier and not rewritten before the next one
-        if (c < int(nch) - 1) chan_sums(t0 + kC, (c + 1) & 1);
+        if (c < cend - 1) chan_sums(t0 + kC, (c + 1) & 1);
 
         // blocks last to first: recompute the block's 16 forward steps from
         // its checkpoint (decays and states in registers), then walk them back
@@ -676,21 +854,23 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
 
         // The next chunk's B / C go to the other buffer, whose last readers
         // (the chunk before this one) are behind the previous barrier.
-        if (c > 0) st.stash(smem + ((c - 1) & 1) * SM::kBC, zero_dead);
+        if (c > cbeg) st.stash(smem + ((c - 1) & 1) * SM::kBC, zero_dead);
         __syncthreads();
     }
 
-    if (nch > 0) chan_sums(0, 0);   // chunk 0, complete since the loop's last barrier
+    // the segment's first chunk, complete since the loop's last barrier
+    if (cend > cbeg) chan_sums(cbeg * kC, cbeg & 1);
 
-    // per-row partials of the parameter gradients
-    if (row_ok) ws.dAp[(b * Dm + d) * kN + n] = dA_acc;
+    // per-row partials of the parameter gradients, per (batch entry, segment)
+    const int64_t bs = b * nsg + seg;
+    if (row_ok) ws.dAp[(bs * Dm + d) * kN + n] = dA_acc;
     dD_acc = row_sum16(dD_acc);
     dbias_acc = row_sum16(dbias_acc);
     if (row_ok && n == 0) {
-        ws.dDp[b * Dm + d] = dD_acc;
-        ws.dbiasp[b * Dm + d] = dbias_acc;
+        ws.dDp[bs * Dm + d] = dD_acc;
+        ws.dbiasp[bs * Dm + d] = dbias_acc;
     }
-    if (p.dh0 && st_ok) p.dh0[(b * Dm + d) * Nst + s0 + n] = g;
+    if (p.dh0 && st_ok && seg == 0) p.dh0[(b * Dm + d) * Nst + s0 + n] = g;
 }
 
 // ---------------------------------------------------------------------------
@@ -793,17 +973,17 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
         const float *dap = slice_ws(ws, int(nn / kN)).dAp;
         const int64_t src = (k / Ns) * kN + nn % kN;    // the 16-wide partial of n's slice
         float s = 0.0f;
-        for (int64_t bb = 0; bb < Bt; bb++) s += dap[bb * Dm * kN + src];
+        for (int64_t bs = 0; bs < Bt * ws.nseg; bs++) s += dap[bs * Dm * kN + src];
         p.dA[k] = s;
     } else if (i < nbc + na + Dm) {
         // dD from the first slice (every slice sums the same dy u); dbias
-        // over batch, then slices, ascending
+        // over (batch entry, segment), then slices, ascending
         const int64_t dd = i - nbc - na;
         const int slices = state_slices(p.nstate);
         float sD = 0.0f, sb = 0.0f;
-        for (int64_t bb = 0; bb < Bt; bb++) {
-            sD += ws.dDp[bb * Dm + dd];
-            for (int k = 0; k < slices; k++) sb += slice_ws(ws, k).dbiasp[bb * Dm + dd];
+        for (int64_t bs = 0; bs < Bt * ws.nseg; bs++) {
+            sD += ws.dDp[bs * Dm + dd];
+            for (int k = 0; k < slices; k++) sb += slice_ws(ws, k).dbiasp[bs * Dm + dd];
         }
         if (p.dD) p.dD[dd] = sD;
         if (p.dbias) p.dbias[dd] = sb;
@@ -868,16 +1048,19 @@ __global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Worksp
 }
 
 // Wavefronts per reverse-pass workgroup: scan_waves' choice for 16-byte
-// rows and 32-step chunks, else 4.
+// rows and 32-step chunks, else 4.  Time segments run side by side like
+// batch entries.
 int reverse_waves(const BwdParams &p, bool vec) {
     if (!vec || kC != 32) return 4;
-    return scan_waves(p.batch, p.dim);
+    int seg_len = 0;
+    const int nseg = scan_segments(p.dim, p.nstate, p.seqlen, &seg_len);
+    return scan_waves(p.batch * nseg, p.dim);
 }
 
 template <typename T, int VEC, bool YP, int NW, bool PART = false>
 void launch_reverse(const BwdParams &p, Workspace ws, hipStream_t stream) {
     const dim3 grid(unsigned((p.dim + 4 * NW - 1) / (4 * NW)), unsigned(p.batch),
-                    unsigned(state_slices(p.nstate)));
+                    unsigned(state_slices(p.nstate) * ws.nseg));
     hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW, PART>), grid, dim3(64 * NW), 0, stream, p, ws);
 }
 
@@ -902,14 +1085,34 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         ws.ypre = slices == 1 ? p.ypre : nullptr;
     }
     if (p.batch > 0 && p.dim > 0) {
-        dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch), unsigned(slices));
+        dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch), unsigned(slices * ws.nseg));
         constexpr int kVec = 16 / sizeof(T);
         const bool vec = (p.seqlen * int64_t(sizeof(T))) % 16 == 0;
         if (!p.ckpt) {
+            if (ws.nseg > 1) {   // the forward's segment summaries, then the states
+                FwdParams fp{};
+                static_cast<ScanParams &>(fp) = p;
+                fp.nseg = ws.nseg;
+                fp.seg_len = ws.seg_len;
+                fp.summ = ws.fsumm;
+                const hipError_t e = launch_fwd_summaries(fp, sizeof(T) == 2, stream);
+                if (e != hipSuccess) return e;
+            }
             if (vec)
                 hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
             else
                 hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
+            profile_mark(stream);
+        }
+        if (ws.nseg > 1) {   // the adjoint's segment summaries
+            const dim3 agrid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch),
+                             unsigned(slices * (ws.nseg - 1)));
+            if (vec)
+                hipLaunchKernelGGL((ss_bwd_adjoint_summary_kernel<T, kVec>), agrid, dim3(kThreads), 0,
+                                   stream, p, ws);
+            else
+                hipLaunchKernelGGL((ss_bwd_adjoint_summary_kernel<T, 1>), agrid, dim3(kThreads), 0,
+                                   stream, p, ws);
             profile_mark(stream);
         }
         const bool yp = slices == 1 && p.ckpt && p.ypre && p.z;

@@ -80,10 +80,10 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
 // slice sl, batch entry b, row d, state n lives.
 __device__ __forceinline__ size_t summ_index(const FwdParams &p, int sl, int j, int64_t b,
                                              int64_t d, int n) {
-    return ((size_t(sl) * (p.nseg - 1) + j) * p.batch + b) * p.dim * kN + d * kN + n;
+    return seg_summ_index(p.nseg, p.batch, p.dim, sl, j, b, d, n);
 }
 __device__ __forceinline__ size_t summ_decay_offset(const FwdParams &p) {
-    return size_t(state_slices(p.nstate)) * (p.nseg - 1) * p.batch * p.dim * kN;
+    return seg_summ_half(p.nstate, p.nseg, p.batch, p.dim);
 }
 
 // The summary pass of a segmented scan: every segment but the last from a
@@ -458,15 +458,19 @@ void launch_scan(const FwdParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW, PART>), grid, dim3(64 * NW), 0, stream, p);
 }
 
+template <typename T>
+void launch_summaries(const FwdParams &p, bool vec, hipStream_t stream) {
+    constexpr int kVec = 16 / sizeof(T);
+    const dim3 grid(static_cast<unsigned>((p.dim + 15) / 16), static_cast<unsigned>(p.batch),
+                    static_cast<unsigned>(state_slices(p.nstate) * (p.nseg - 1)));
+    if (vec) hipLaunchKernelGGL((ss_fwd_summary_kernel<T, kVec>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((ss_fwd_summary_kernel<T, 1>), grid, dim3(256), 0, stream, p);
+}
+
 template <typename T, bool PART>
 void launch_scan_vec(const FwdParams &p, bool vec, hipStream_t stream) {
     constexpr int kVec = 16 / sizeof(T);
-    if (p.nseg > 1) {   // the segments' summaries first
-        const dim3 grid(static_cast<unsigned>((p.dim + 15) / 16), static_cast<unsigned>(p.batch),
-                        static_cast<unsigned>(state_slices(p.nstate) * (p.nseg - 1)));
-        if (vec) hipLaunchKernelGGL((ss_fwd_summary_kernel<T, kVec>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((ss_fwd_summary_kernel<T, 1>), grid, dim3(256), 0, stream, p);
-    }
+    if (p.nseg > 1) launch_summaries<T>(p, vec, stream);   // the segments' summaries first
     if (vec) launch_scan<T, kVec, 4, PART>(p, stream);
     else launch_scan<T, 1, 4, PART>(p, stream);
 }
@@ -523,6 +527,13 @@ size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstat
     const size_t summ = nseg > 1 ? 2 * size_t(slices) * (nseg - 1) * batch * dim * kN : 0;
     if (part + summ == 0) return 0;
     return ((part + 63) / 64 * 64 + summ) * sizeof(float);
+}
+
+hipError_t launch_fwd_summaries(const FwdParams &p, bool bf16, hipStream_t stream) {
+    if (p.batch == 0 || p.dim == 0 || p.nseg < 2) return hipSuccess;
+    if (bf16) launch_summaries<bf16_t>(p, (p.seqlen * 2) % 16 == 0, stream);
+    else launch_summaries<float>(p, (p.seqlen * 4) % 16 == 0, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream) {

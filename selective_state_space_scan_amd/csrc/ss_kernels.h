@@ -72,6 +72,19 @@ __host__ __device__ inline size_t ckpt_bytes(int64_t batch, int64_t dim, int64_t
 // one sequential pass) and sets *seg_len.
 int scan_segments(int64_t dim, int nstate, int64_t seqlen, int *seg_len);
 
+// Segment summaries, one buffer of 2 x seg_summ_half floats: per (slice,
+// summary k < nseg - 1, batch, dim, 16 states) the segment's end value from
+// zero, then -- seg_summ_half floats further on -- its total decay.  The
+// forward keeps those of segments 0 .. nseg - 2 (k = segment), the
+// backward's adjoint those of segments 1 .. nseg - 1 (k = segment - 1).
+__host__ __device__ inline size_t seg_summ_index(int nseg, int64_t batch, int64_t dim, int sl,
+                                                 int k, int64_t b, int64_t d, int n) {
+    return ((size_t(sl) * (nseg - 1) + k) * batch + b) * dim * 16 + d * 16 + n;
+}
+__host__ __device__ inline size_t seg_summ_half(int nstate, int nseg, int64_t batch, int64_t dim) {
+    return size_t(state_slices(nstate)) * (nseg - 1) * batch * dim * 16;
+}
+
 struct FwdParams : ScanParams {
     void *out;
     float *last_state;
@@ -165,6 +178,9 @@ int scan_waves(int64_t batch, int64_t dim);
 
 size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate);
 hipError_t launch_fwd(const FwdParams &p, bool bf16, hipStream_t stream);
+// The forward's summary pass alone (p.nseg > 1, p.seg_len and p.summ set):
+// the backward runs it before recomputing block states segment by segment.
+hipError_t launch_fwd_summaries(const FwdParams &p, bool bf16, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstate);
 hipError_t launch_bwd(const BwdParams &p, bool bf16, hipStream_t stream);
 

@@ -207,3 +207,117 @@ def test_bwd_full_size_whole_tensors():
     for k in ("du", "ddelta", "dz", "dB", "dC", "dA", "dD", "ddelta_bias"):
         e = assert_close(to_host(g1[k]), ref[k], tol, k)
         say(f"  {k} err {e:.3e}")
+
+
+# Long sequences over few channels: the backward cuts time into the
+# forward's segments (block states after the forward's summary pass, the
+# reverse pass after an adjoint summary pass).
+SEGMENTED = [
+    # batch, dim, dstate, L, io
+    (2, 64, 16, 8192, "f32"),        # 8 segments of 1024 steps
+    (2, 48, 16, 8229, "bf16"),       # segments of 1088 steps, a short ragged last one
+    (1, 40, 16, 9001, "f32"),        # rows not 16-byte aligned (scalar path), ragged channels
+    (2, 32, 40, 8300, "bf16"),       # three 16-state slices x 8 segments
+]
+
+
+@pytest.mark.parametrize("batch,dim,N,L,io", SEGMENTED)
+def test_bwd_time_segments_elementwise(batch, dim, N, L, io):
+    """Every gradient against the oracle, with an initial state and a
+    gradient on the last state, and the forward's saved record giving the
+    same bits as recomputing the block states."""
+    require_gpu()
+    w = ssin.custom("bwd", batch, dim, N, L, io, seed=batch + dim + N + L)
+    arr = ssin.make(w)
+    say(f"bwd segmented {w.name}")
+    d = dev_inputs(arr)
+    rng = np.random.default_rng(L + 3)
+    h0 = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    dl = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    g = run_bwd(d, w, h0=to_dev(h0), dlast=to_dev(dl), want_dh0=True)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(arr, w, h0=h0.astype(np.float64), dlast=dl.astype(np.float64),
+                     threads=ORACLE_THREADS)
+    for k in KEYS:
+        if k not in ref:
+            continue
+        tol = TOL["f32"] if k in ("dA", "dD", "ddelta_bias", "dh0") else TOL[io]
+        e = assert_close(to_host(g[k]), ref[k], tol, f"{k} segmented")
+        say(f"  {k} err {e:.3e}")
+    ck = binding.ss_ckpt_empty(d["u"], dstate=N)
+    binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"],
+                   w.softplus, h0=to_dev(h0), ckpt=ck)
+    g2 = binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                        d["delta_bias"], w.softplus, d["dout"], h0=to_dev(h0), dlast=to_dev(dl),
+                        want_dh0=True, ckpt=ck)
+    torch.cuda.synchronize()
+    for k in g:
+        a, b2 = g[k], g2[k]
+        if a.dtype == torch.bfloat16:
+            a, b2 = a.view(torch.int16), b2.view(torch.int16)
+        assert torch.equal(a, b2), f"{k} with saved record"
+
+
+def test_bwd_time_segments_batch_invariant_and_deterministic():
+    """Segmented backward: run-to-run bit equality, and each batch entry's
+    du, ddelta, dz, dB, dC and dh0 the same bits run alone as inside the
+    batch (the segment count depends on dim, dstate and seqlen only)."""
+    require_gpu()
+    w = ssin.custom("bwd", 3, 64, 16, 8192, "bf16", seed=78)
+    d = dev_inputs(ssin.make(w))
+    h0 = torch.randn(3, 64, 16, device=DEV)
+    dl = torch.randn(3, 64, 16, device=DEV)
+    g1 = run_bwd(d, w, h0=h0, dlast=dl, want_dh0=True)
+    g2 = run_bwd(d, w, h0=h0, dlast=dl, want_dh0=True)
+    torch.cuda.synchronize()
+    for k in g1:
+        a, b2 = g1[k], g2[k]
+        if a.dtype == torch.bfloat16:
+            a, b2 = a.view(torch.int16), b2.view(torch.int16)
+        assert torch.equal(a, b2), f"{k} not deterministic"
+    per_entry = ("u", "delta", "B", "C", "z", "dout")
+    for bi in range(w.batch):
+        one = {k: (v[bi:bi + 1].contiguous() if k in per_entry else v) for k, v in d.items()}
+        ga = run_bwd(one, w, h0=h0[bi:bi + 1].contiguous(), dlast=dl[bi:bi + 1].contiguous(),
+                     want_dh0=True)
+        torch.cuda.synchronize()
+        for k in ("du", "ddelta", "dz", "dB", "dC", "dh0"):
+            a, b1 = g1[k][bi:bi + 1], ga[k]
+            if a.dtype == torch.bfloat16:
+                a, b1 = a.view(torch.int16), b1.view(torch.int16)
+            assert torch.equal(a, b1), f"{k} entry {bi}"
+
+
+def test_bwd_long_sequence_full_size_whole_tensors():
+    """One long bf16 sequence (1 x 1536 x 16384), the shape the time segments
+    serve, in the launch configuration the benchmark times: every element of
+    every gradient against the oracle, the same bits twice, and the
+    forward's saved record giving the same bits as recomputing it."""
+    require_gpu()
+    w = ssin.WORKLOADS["mamba130m_long_bf16_1x1536x16384"]
+    say("bwd long: generating inputs")
+    arr = ssin.make(w)
+    d = dev_inputs(arr)
+    say("bwd long: running")
+    g1 = run_bwd(d, w)
+    g2 = run_bwd(d, w)
+    ck = binding.ss_ckpt_empty(d["u"])
+    binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"],
+                   True, ckpt=ck)
+    g3 = binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                        d["delta_bias"], True, d["dout"], ckpt=ck)
+    torch.cuda.synchronize()
+    for k in g1:
+        a, b2, b3 = g1[k], g2[k], g3[k]
+        if a.dtype == torch.bfloat16:
+            a, b2, b3 = a.view(torch.int16), b2.view(torch.int16), b3.view(torch.int16)
+        assert torch.equal(a, b2), f"{k} not deterministic"
+        assert torch.equal(a, b3), f"{k} with saved record"
+    x = {k: widen(v) for k, v in arr.items()}
+    say(f"bwd long: oracle on the whole workload ({ORACLE_THREADS} threads)")
+    ref = oracle.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
+                     x["delta_bias"], True, x["dout"], threads=ORACLE_THREADS)
+    for k in ("du", "ddelta", "dz", "dB", "dC", "dA", "dD", "ddelta_bias"):
+        tol = TOL["f32"] if k in ("dA", "dD", "ddelta_bias") else TOL[w.io]
+        e = assert_close(to_host(g1[k]), ref[k], tol, k)
+        say(f"  {k} err {e:.3e}")

@@ -126,7 +126,9 @@ def test_fwd_tiny_named_workload_elementwise():
 
 
 @pytest.mark.parametrize("name", ["mamba130m_fwd_bf16_8x1536x2048",
-                                  "mamba2p8b_fwd_bf16_4x5120x4096"])
+                                  "mamba2p8b_fwd_bf16_4x5120x4096",
+                                  # one long sequence: the time-segmented scan
+                                  "mamba130m_long_bf16_1x1536x16384"])
 def test_fwd_full_size_whole_tensors_deterministic(name):
     """A named forward workload at full size, in the launch configuration the
     benchmark times: every element of y and of last_state against the
