@@ -114,10 +114,18 @@ def conv_algorithmic_bytes(kernel, batch, dim, L, width, esize):
     raise KeyError(kernel)
 
 
+# The sources each profiled kernel is built from: a committed summary counts
+# only while their hash is the one it was measured with.
+_FWD_SRC = ["ss_fwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"]
+_BWD_SRC = ["ss_bwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"]
 KERNEL_SOURCES = {
-    "ss_fwd_kernel": ["ss_fwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"],
-    "ss_bwd_reverse_kernel": ["ss_bwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"],
-    "ss_bwd_fold_kernel": ["ss_bwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"],
+    "ss_fwd_kernel": _FWD_SRC,
+    "ss_fwd_summary_kernel": _FWD_SRC,
+    "ss_bwd_reverse_kernel": _BWD_SRC,
+    "ss_bwd_fold_kernel": _BWD_SRC,
+    "ss_bwd_ckpt_kernel": _BWD_SRC,
+    "ss_bwd_adjoint_summary_kernel": _BWD_SRC,
+    "ss_state_update_kernel": ["ss_state_update.hip", "ss_device.h", "ss_kernels.h"],
 }
 
 
@@ -243,11 +251,17 @@ def summarize_profile(prof_dir, copy_dir, kernel, workload, title, only, sources
     return "\n".join(out) + "\n"
 
 
-def profile_value(kernel, workload, key):
-    """A value from the committed rocprofv3 summary of `kernel` on `workload`,
-    or None when the summary is missing or the kernel's sources changed."""
+def profile_path(kernel, only):
+    """Committed summary of `kernel` under the `--only` workload `only`."""
+    return os.path.join(ROOT, "profiles", f"{kernel}__{only}.md")
+
+
+def profile_value(kernel, only, key):
+    """A value from the committed rocprofv3 summary of `kernel` under the
+    `--only` workload `only`, or None when the summary is missing or the
+    kernel's sources changed."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
+    path = profile_path(kernel, only)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -538,6 +552,20 @@ PROFILE_WORKLOADS = {
 }
 
 
+def long_sequence_detail(to_dev, dev):
+    """One long bf16 sequence (1 x 1536 x 16384): few (row, state) lanes, so
+    the scan runs as time segments.  Mean call times over several calls,
+    HIP events around each kind of call (each is several kernels)."""
+    out = {}
+    for only, key in (("fwd_bf16_1x1536x16384", "fwd_ms"),
+                      ("bwd_bf16_1x1536x16384_standalone", "bwd_standalone_ms"),
+                      ("step_bf16_1x1536x16384", "step_ms")):
+        out[key] = round(run_only(only, 20, 3, to_dev, dev)["ms_per_call"], 5)
+    E = 1 * 1536 * 16384
+    out["step_elements_per_s"] = E / (out["step_ms"] * 1e-3)
+    return {"mamba130m_long_bf16_1x1536x16384": out}
+
+
 def run_only(name, steps, warmup, to_dev, dev):
     import torch
     call, keep = _scan_call(name, to_dev, dev)
@@ -656,9 +684,8 @@ def main():
     step_bytes = kb["ss_fwd_kernel"] + kb["ss_bwd_reverse_kernel"] + kb["ss_bwd_fold_kernel"]
     dom = max(names, key=lambda n: kern_ms[n])
     ach = kb[dom] / (kern_ms[dom] * 1e-3) / 1e9
-    wl = PROFILE_WORKLOADS["step_f32_8x1536x2048"]
-    traffic = profile_value(dom, wl, "traffic_bytes_per_launch")
-    valu = profile_value(dom, wl, "valu_insts_per_launch")
+    traffic = profile_value(dom, "step_f32_8x1536x2048", "traffic_bytes_per_launch")
+    valu = profile_value(dom, "step_f32_8x1536x2048", "valu_insts_per_launch")
     copy_gbps = copy_ceiling_gbps(dev)
     kernels = {n: {"avg_ms": round(kern_ms[n], 5), "algorithmic_bytes": kb[n],
                    "algorithmic_GBps": round(kb[n] / (kern_ms[n] * 1e-3) / 1e9, 1),
@@ -821,6 +848,7 @@ def main():
             "input_sets_rotated": reps}
         del sets, outs
 
+        detail.update(long_sequence_detail(to_dev, dev))
         detail.update(wide_state_detail(hip, lib, to_dev, dev))
         detail.update(conv_detail(hip, lib, to_dev, dev))
         detail.update(ssd_detail(hip, lib, to_dev, dev))
