@@ -100,8 +100,9 @@ const char *ss_last_error(void);
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 
 /* Bytes of device workspace ss_fwd needs (f32, 0 when none):
- *   - above 16 states, the per-slice partial sums over states,
- *     ceil(dstate / 16) * batch * dim * seqlen floats;
+ *   - above 64 states, the per-slice partial sums over states,
+ *     ceil(dstate / 16) * batch * dim * seqlen floats (up to 64 states the
+ *     slices of a row meet in the same lanes and need none);
  *   - for a long sequence over few channels (seqlen >= 8192 and fewer than
  *     3072 wavefronts of 4 channels x 16 states per batch entry), the time
  *     segments' summaries: 2 * ceil(dstate / 16) * (nseg - 1) * batch * dim
@@ -121,8 +122,12 @@ size_t ss_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
  * save-for-backward of a training step).
  *   dstate            1..256 (SS_EUNSUPPORTED above; the mamba-rs README,
  *                     "Features", sizes state dimensions up to 256).  Above
- *                     16 the scan runs one pass per 16-state slice and adds
- *                     the slices' sums in ascending order.
+ *                     16 the states are cut into 16-state slices: up to 64
+ *                     a lane runs one state of each slice of its row and
+ *                     adds a step's terms over the slices in ascending
+ *                     order before the sum over its row's lanes; above 64
+ *                     one pass runs per slice and the slices' sums are
+ *                     added in ascending order.
  *   Long sequences over few channels (see ss_fwd_workspace_size) run as
  *   parallel time segments: a first pass gives every segment but the last
  *   its (total decay, end state from zero) pair -- the scan's associative

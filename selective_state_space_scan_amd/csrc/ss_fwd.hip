@@ -36,10 +36,13 @@
 //     against one DPP level plus a half transpose, the register butterfly
 //     was the fastest.  The backward recomputes the pre-gate output with the
 //     same butterfly, so a saved and a recomputed value are the same bits;
-//   * d_state above 16 runs one 16-state slice per grid z: each slice
-//     writes its sums over its states as f32 partials (no D term, no gate),
-//     and a combine kernel adds the slices in ascending order, adds D u and
-//     applies the gate.
+//   * d_state above 16 is cut into 16-state slices.  Up to 64 states a lane
+//     runs the same state index of every slice of its row (states n, 16 + n,
+//     ...), and a step's terms C h are added over the slices in the lane, in
+//     ascending order, before the one butterfly: no partials leave the chip.
+//     Above 64 states one slice runs per grid z, each writing its sums over
+//     its states as f32 partials (no D term, no gate), and a combine kernel
+//     adds the slices in ascending order, adds D u and applies the gate.
 #include <type_traits>
 
 #include "ss_device.h"
@@ -52,16 +55,20 @@ namespace {
 constexpr int kT = 64;          // time steps per LDS chunk
 constexpr int kPitch = kT + 4;  // f32 B / C tile pitch (conflict-free 16-byte reads)
 
-// NW wavefronts (4 NW channels) per workgroup.  B and C (shared by all
-// channels) and, for 2-byte types, the element tiles go through LDS in two
-// buffers: chunk c uses buffer c & 1 while the next chunk's tiles are
-// stashed into the other.
-template <typename T, int NW>
+// NW wavefronts (4 NW channels) per workgroup, S 16-state slices per lane.
+// B and C (shared by all channels; S tiles of 16 states each) and, for
+// 2-byte types, the element tiles go through LDS in two buffers: chunk c
+// uses buffer c & 1 while the next chunk's tiles are stashed into the
+// other.  With three or four slices a chunk is 32 steps, so that three
+// workgroups still fit a compute unit's LDS.
+template <typename T, int NW, int S = 1>
 struct FwdSmem {
+    static constexpr int kTc = S <= 2 ? kT : 32;              // steps per chunk
+    static constexpr int kPitchC = kTc + 4;
     static constexpr uint32_t kB = 0;                          // within a buffer
-    static constexpr uint32_t kC = kB + kN * kPitch * 4;
-    static constexpr uint32_t kU = kC + kN * kPitch * 4;       // element tiles [row 4 NW][kT]
-    static constexpr uint32_t kElem = kStageElems<T> ? 4 * NW * kT * sizeof(T) : 0;
+    static constexpr uint32_t kC = kB + S * kN * kPitchC * 4;
+    static constexpr uint32_t kU = kC + S * kN * kPitchC * 4;  // element tiles [row 4 NW][kTc]
+    static constexpr uint32_t kElem = kStageElems<T> ? 4 * NW * kTc * sizeof(T) : 0;
     static constexpr uint32_t kDl = kU + kElem;
     static constexpr uint32_t kZ = kDl + kElem;
     static constexpr uint32_t kBC = kZ + kElem;                // one buffer
@@ -74,6 +81,15 @@ __device__ __forceinline__ void scan_step(float dl, float dlu, float a2, float b
     const float abar = exp2_hw(row_bcast<J>(dl) * a2);
     h = __builtin_fmaf(abar, h, row_bcast<J>(dlu) * b);
     v = c * h;
+}
+// the same step of a further slice of the lane's row: its term C h is added
+// to the step's running sum over the slices
+template <int J>
+__device__ __forceinline__ void scan_step_acc(float dl, float dlu, float a2, float b, float c,
+                                              float &h, float &v) {
+    const float abar = exp2_hw(row_bcast<J>(dl) * a2);
+    h = __builtin_fmaf(abar, h, row_bcast<J>(dlu) * b);
+    v = __builtin_fmaf(c, h, v);
 }
 
 // Where segment j's summary (end state from zero, then total decay) of
@@ -199,12 +215,18 @@ __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
 }
 
 // NW: wavefronts per workgroup (4 channels each).  PART: one slice of
-// several; the output is the slice's f32 partial sum of C h.  Grid z holds
-// (slice, time segment).
-template <typename T, int VEC, int NW, bool PART>
+// several; the output is the slice's f32 partial sum of C h.  S > 1: each
+// lane runs the same state index of S slices (states n, 16 + n, ...); the
+// terms C h of a step are added over the slices in the lane, in ascending
+// order, before the sum over the row's 16 lanes.  Grid z holds (slice, time
+// segment); with S > 1 it holds the segment only.
+template <typename T, int VEC, int NW, bool PART, int S = 1>
 __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) void ss_fwd_kernel(FwdParams p) {
+    static_assert(S >= 1 && !(PART && S > 1), "slices run either in the lane or one per grid z");
     using OutT = std::conditional_t<PART, float, T>;
-    using SM = FwdSmem<T, NW>;
+    using SM = FwdSmem<T, NW, S>;
+    constexpr int kT = SM::kTc;          // steps per chunk
+    constexpr int kPitch = SM::kPitchC;
     constexpr bool kStage = kStageElems<T>;
     constexpr int kRowsG = 4 * NW;
     constexpr int kThr = 64 * NW;
@@ -227,24 +249,34 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
     // the wavefront's first row, uniform (scalar) across the wavefront
     const int64_t dw = d0 + 4 * __builtin_amdgcn_readfirstlane(wave);
 
-    // grid z: (slice, segment); this slice's states: s0 .. s0 + Ns - 1 of
-    // Nst; lanes n >= Ns carry zero A, B and C
+    // grid z: (slice, segment).  Lane slice k holds states s0 + 16 k + n;
+    // states past dstate carry zero A, B and C
     const int slice = int(blockIdx.z) / p.nseg, seg = int(blockIdx.z) % p.nseg;
     const int Nst = p.nstate;
     const int s0 = PART ? 16 * slice : 0;
-    const int Ns = PART ? (Nst - s0 < kN ? Nst - s0 : kN) : Nst;
-    const bool st_ok = row_ok && n < Ns;
-    float a2 = st_ok ? p.A[d * Nst + s0 + n] * kLog2e : 0.0f;  // A in base-2 exponent units
+    auto slice_states = [&](int k) {   // valid states of lane slice k
+        const int first = s0 + 16 * k;
+        return (PART || S > 1) ? (Nst - first < kN ? Nst - first : kN) : Nst;
+    };
+    float a2[S], h[S];   // A in base-2 exponent units; the state
+#pragma unroll
+    for (int k = 0; k < S; k++) {
+        const bool ok = row_ok && n < slice_states(k);
+        a2[k] = ok ? p.A[d * Nst + s0 + 16 * k + n] * kLog2e : 0.0f;
+        h[k] = (ok && p.h0) ? p.h0[(b * Dm + d) * Nst + s0 + 16 * k + n] : 0.0f;
+    }
     float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
     float dskip = (row_ok && p.D) ? p.D[d] : 0.0f;
-    float h = (st_ok && p.h0) ? p.h0[(b * Dm + d) * Nst + s0 + n] : 0.0f;
     if (seg > 0 && row_ok) {
         // the state entering this segment: the segments before it, each a
         // (decay, end state from zero) pair, applied in ascending order
         const float *sh = p.summ, *sd = p.summ + summ_decay_offset(p);
-        for (int j = 0; j < seg; j++) {
-            const size_t i = summ_index(p, slice, j, b, d, n);
-            h = __builtin_fmaf(sd[i], h, sh[i]);
+#pragma unroll
+        for (int k = 0; k < S; k++) {
+            for (int j = 0; j < seg; j++) {
+                const size_t i = summ_index(p, PART ? slice : k, j, b, d, n);
+                h[k] = __builtin_fmaf(sd[i], h[k], sh[i]);
+            }
         }
     }
     // this segment's steps and 64-step chunks
@@ -263,7 +295,7 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
     const int64_t groupbase = (b * Dm + d0) * L;   // the group's first row (staged tiles)
     const T *gB = static_cast<const T *>(p.B) + (b * Nst + s0) * L;
     const T *gC = static_cast<const T *>(p.C) + (b * Nst + s0) * L;
-    const bool zero_dead = Ns < kN;   // B / C rows past dstate must read as zeros
+    const bool zero_dead = slice_states(S - 1) < kN;   // B / C rows past dstate must read as zeros
     // element t of this lane's row (0 past the end and for rows past the
     // last channel); a row's 16 lanes read 16 consecutive elements
     auto elem_at = [&](const T *g, int t) {
@@ -272,15 +304,18 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
                    : 0.0f;
     };
     // B and C (and the element tiles of the group's rows when staged)
-    ChunkStager<T, VEC, kT, kStage ? 2 + 3 * (kRowsG / 16) : 2, kThr> st;
+    ChunkStager<T, VEC, kT, kStage ? 2 * S + 3 * (kRowsG / 16) : 2 * S, kThr> st;
     st.init(
         [&](int i) -> TileSrc<T> {
-            if (i == 0) return {gB, L, Ns, SM::kB, kPitch, true};
-            if (i == 1) return {gC, L, Ns, SM::kC, kPitch, true};
+            // B of slices 0 .. S - 1, then C of slices 0 .. S - 1
+            if (i < S) return {gB + int64_t(16 * i) * L, L, slice_states(i),
+                               SM::kB + uint32_t(i * kN * kPitch * 4), kPitch, true};
+            if (i < 2 * S) return {gC + int64_t(16 * (i - S)) * L, L, slice_states(i - S),
+                                   SM::kC + uint32_t((i - S) * kN * kPitch * 4), kPitch, true};
             // element tiles in 16-row pieces; a piece with no valid row points
             // at the group's first row (it is not read)
             constexpr int kPieces = kRowsG / 16;
-            const int q = (i - 2) / kPieces, j = (i - 2) % kPieces;
+            const int q = (i - 2 * S) / kPieces, j = (i - 2 * S) % kPieces;
             const void *src = q == 0 ? p.u : q == 1 ? p.delta : p.z;
             const T *g = src ? static_cast<const T *>(src) + groupbase : nullptr;
             const uint32_t lds = q == 0 ? SM::kU : q == 1 ? SM::kDl : SM::kZ;
@@ -315,15 +350,17 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
     // Make the per-row parameter loads complete here.  Left pending into the
     // chunk loop, their first use there would be a wait on the in-order
     // memory counter that also drains the chunk prefetch.
-    __asm__("" : "+v"(a2), "+v"(bias), "+v"(dskip), "+v"(h));
+    __asm__("" : "+v"(bias), "+v"(dskip));
+#pragma unroll
+    for (int k = 0; k < S; k++) __asm__("" : "+v"(a2[k]), "+v"(h[k]));
     __syncthreads();
 
     const int64_t nck = (L + kCkptSpacing - 1) / kCkptSpacing;
     const int nckS = int(nck);
     const bool save_ck = p.ckpt != nullptr;
-    float *ckb = save_ck ? p.ckpt + slice * ckpt_state_floats(p.batch, Dm, L) +
-                               (b * Dm + dw) * nck * kN
-                         : nullptr;
+    // block states of lane slice k: k ckpt_state_floats further on
+    const size_t ck_slice = ckpt_state_floats(p.batch, Dm, L);
+    float *ckb = save_ck ? p.ckpt + slice * ck_slice + (b * Dm + dw) * nck * kN : nullptr;
     const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
     OutT *yb = (PART ? reinterpret_cast<OutT *>(p.ypart + slice * size_t(p.batch * Dm * L))
                      : static_cast<OutT *>(p.out)) +
@@ -367,23 +404,45 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
         for (int s = 0; s < kE; s++) {
             if (save_ck && (16 * s) % kCkptSpacing == 0) {   // state entering a checkpoint block
                 const int k = (t0 + 16 * s) / kCkptSpacing;
-                if (row_ok && k < nckS) st_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)), h);
+                if (row_ok && k < nckS) {
+#pragma unroll
+                    for (int i = 0; i < S; i++)
+                        st_global(at_bytes(ckb + i * ck_slice, ckoff + uint32_t(k * kN * 4)), h[i]);
+                }
             }
             float v[16];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const float4 bq = *reinterpret_cast<const float4 *>(&sB[n][16 * s + 4 * q]);
-                const float4 cq = *reinterpret_cast<const float4 *>(&sC[n][16 * s + 4 * q]);
-                switch (q) {
-#define SS_STEP4(Q)                                                                  \
-    case Q:                                                                          \
-        scan_step<4 * Q + 0>(dl[s], dlu[s], a2, bq.x, cq.x, h, v[4 * Q + 0]);        \
-        scan_step<4 * Q + 1>(dl[s], dlu[s], a2, bq.y, cq.y, h, v[4 * Q + 1]);        \
-        scan_step<4 * Q + 2>(dl[s], dlu[s], a2, bq.z, cq.z, h, v[4 * Q + 2]);        \
-        scan_step<4 * Q + 3>(dl[s], dlu[s], a2, bq.w, cq.w, h, v[4 * Q + 3]);        \
+#pragma unroll
+                for (int i = 0; i < S; i++) {
+                    // slice i's B and C rows: 16 i + n
+                    const float4 bq = *reinterpret_cast<const float4 *>(&sB[16 * i + n][16 * s + 4 * q]);
+                    const float4 cq = *reinterpret_cast<const float4 *>(&sC[16 * i + n][16 * s + 4 * q]);
+                    if (i == 0) {
+                        switch (q) {
+#define SS_STEP4(Q)                                                                        \
+    case Q:                                                                                \
+        scan_step<4 * Q + 0>(dl[s], dlu[s], a2[0], bq.x, cq.x, h[0], v[4 * Q + 0]);        \
+        scan_step<4 * Q + 1>(dl[s], dlu[s], a2[0], bq.y, cq.y, h[0], v[4 * Q + 1]);        \
+        scan_step<4 * Q + 2>(dl[s], dlu[s], a2[0], bq.z, cq.z, h[0], v[4 * Q + 2]);        \
+        scan_step<4 * Q + 3>(dl[s], dlu[s], a2[0], bq.w, cq.w, h[0], v[4 * Q + 3]);        \
         break;
-                    SS_STEP4(0) SS_STEP4(1) SS_STEP4(2) SS_STEP4(3)
+                            SS_STEP4(0) SS_STEP4(1) SS_STEP4(2) SS_STEP4(3)
 #undef SS_STEP4
+                        }
+                    } else {
+                        switch (q) {
+#define SS_STEP4(Q)                                                                            \
+    case Q:                                                                                    \
+        scan_step_acc<4 * Q + 0>(dl[s], dlu[s], a2[i], bq.x, cq.x, h[i], v[4 * Q + 0]);        \
+        scan_step_acc<4 * Q + 1>(dl[s], dlu[s], a2[i], bq.y, cq.y, h[i], v[4 * Q + 1]);        \
+        scan_step_acc<4 * Q + 2>(dl[s], dlu[s], a2[i], bq.z, cq.z, h[i], v[4 * Q + 2]);        \
+        scan_step_acc<4 * Q + 3>(dl[s], dlu[s], a2[i], bq.w, cq.w, h[i], v[4 * Q + 3]);        \
+        break;
+                            SS_STEP4(0) SS_STEP4(1) SS_STEP4(2) SS_STEP4(3)
+#undef SS_STEP4
+                        }
+                    }
                 }
             }
             // the output of the lane's own step 16 s + n: its 16 terms summed
@@ -407,8 +466,10 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
         __syncthreads();
     }
 
-    if (p.last_state && st_ok && seg == p.nseg - 1) {
-        p.last_state[(b * Dm + d) * Nst + s0 + n] = h;
+    if (p.last_state && row_ok && seg == p.nseg - 1) {
+#pragma unroll
+        for (int k = 0; k < S; k++)
+            if (n < slice_states(k)) p.last_state[(b * Dm + d) * Nst + s0 + 16 * k + n] = h[k];
     }
 }
 
@@ -451,11 +512,12 @@ __global__ __launch_bounds__(256) void ss_fwd_combine_kernel(FwdParams p, int sl
     else st_global(static_cast<T *>(p.out) + e0, from_f32<T>(y[0]));
 }
 
-template <typename T, int VEC, int NW, bool PART>
+template <typename T, int VEC, int NW, bool PART, int S = 1>
 void launch_scan(const FwdParams &p, hipStream_t stream) {
+    const int zslices = S > 1 ? 1 : state_slices(p.nstate);
     const dim3 grid(static_cast<unsigned>((p.dim + 4 * NW - 1) / (4 * NW)),
-                    static_cast<unsigned>(p.batch), static_cast<unsigned>(state_slices(p.nstate) * p.nseg));
-    hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW, PART>), grid, dim3(64 * NW), 0, stream, p);
+                    static_cast<unsigned>(p.batch), static_cast<unsigned>(zslices * p.nseg));
+    hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW, PART, S>), grid, dim3(64 * NW), 0, stream, p);
 }
 
 template <typename T>
@@ -467,12 +529,18 @@ void launch_summaries(const FwdParams &p, bool vec, hipStream_t stream) {
     else hipLaunchKernelGGL((ss_fwd_summary_kernel<T, 1>), grid, dim3(256), 0, stream, p);
 }
 
-template <typename T, bool PART>
+template <typename T, bool PART, int S = 1>
 void launch_scan_vec(const FwdParams &p, bool vec, hipStream_t stream) {
     constexpr int kVec = 16 / sizeof(T);
     if (p.nseg > 1) launch_summaries<T>(p, vec, stream);   // the segments' summaries first
-    if (vec) launch_scan<T, kVec, 4, PART>(p, stream);
-    else launch_scan<T, 1, 4, PART>(p, stream);
+    if (vec) launch_scan<T, kVec, 4, PART, S>(p, stream);
+    else launch_scan<T, 1, 4, PART, S>(p, stream);
+}
+
+// part of the forward workspace taken by per-slice partial outputs (floats)
+size_t partial_floats(int64_t batch, int64_t dim, int64_t seqlen, int nstate) {
+    const int slices = state_slices(nstate);
+    return slices > kMaxLaneSlices ? size_t(slices) * batch * dim * seqlen : 0;
 }
 
 template <typename T>
@@ -486,11 +554,17 @@ hipError_t launch_typed(const FwdParams &p0, hipStream_t stream) {
     const int slices = state_slices(p.nstate);
     p.nseg = scan_segments(p.dim, p.nstate, p.seqlen, &p.seg_len);
     if (p.nseg > 1) {   // summaries after the slice partials in the workspace
-        const size_t part = slices > 1 ? size_t(slices) * p.batch * p.dim * p.seqlen : 0;
+        const size_t part = partial_floats(p.batch, p.dim, p.seqlen, p.nstate);
         p.summ = static_cast<float *>(p.ypart) + (part + 63) / 64 * 64;
     }
-    if (slices == 1) {
-        launch_scan_vec<T, false>(p, vec, stream);
+    if (slices <= kMaxLaneSlices) {
+        if (slices > 1) p.ypre = nullptr;   // saved only with one slice
+        switch (slices) {
+            case 1: launch_scan_vec<T, false, 1>(p, vec, stream); break;
+            case 2: launch_scan_vec<T, false, 2>(p, vec, stream); break;
+            case 3: launch_scan_vec<T, false, 3>(p, vec, stream); break;
+            default: launch_scan_vec<T, false, 4>(p, vec, stream); break;
+        }
         profile_mark(stream);
         return hipGetLastError();
     }
@@ -523,7 +597,7 @@ size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstat
     const int slices = state_slices(nstate);
     int seg_len = 0;
     const int nseg = scan_segments(dim, nstate, seqlen, &seg_len);
-    const size_t part = slices > 1 ? size_t(slices) * batch * dim * seqlen : 0;   // floats
+    const size_t part = partial_floats(batch, dim, seqlen, nstate);
     const size_t summ = nseg > 1 ? 2 * size_t(slices) * (nseg - 1) * batch * dim * kN : 0;
     if (part + summ == 0) return 0;
     return ((part + 63) / 64 * 64 + summ) * sizeof(float);

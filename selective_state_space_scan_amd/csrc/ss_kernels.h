@@ -22,6 +22,11 @@ constexpr int kMaxState = 256;
 
 __host__ __device__ inline int state_slices(int nstate) { return (nstate + 15) / 16; }
 
+// Up to this many slices the forward runs a row's slices in the same lane
+// (their output terms added in registers before the sum over the row's
+// lanes): no per-slice partials and no combine kernel.
+constexpr int kMaxLaneSlices = 4;
+
 struct ScanParams {
     int64_t batch, dim, seqlen;
     int nstate;   // dstate, 1..kMaxState

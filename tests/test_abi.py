@@ -240,15 +240,25 @@ def test_conv_update_checks(lib):
 
 
 def test_fwd_workspace(lib):
-    # no workspace up to 16 states; above, one f32 partial per slice and element
+    # no workspace up to 64 states (the slices of a row run in the same
+    # lanes); above, one f32 partial per slice and element
     assert lib.ss_fwd_workspace_size(2, 32, 16, 64) == 0
-    assert lib.ss_fwd_workspace_size(2, 32, 17, 64) == 2 * 2 * 32 * 64 * 4
+    assert lib.ss_fwd_workspace_size(2, 32, 17, 64) == 0
+    assert lib.ss_fwd_workspace_size(2, 32, 64, 64) == 0
+    assert lib.ss_fwd_workspace_size(2, 32, 65, 64) == 5 * 2 * 32 * 64 * 4
     assert lib.ss_fwd_workspace_size(2, 32, 256, 64) == 16 * 2 * 32 * 64 * 4
     assert lib.ss_fwd_workspace_size(2, 32, 257, 64) == 0
-    need = lib.ss_fwd_workspace_size(2, 32, 64, 64)
-    assert _fwd(lib, dstate=64) == EINVAL and "workspace" in _msg(lib)
-    assert _fwd(lib, dstate=64, ws=FAKE, ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
-    assert _fwd(lib, dstate=64, ws=MISALIGNED, ws_bytes=need) == EINVAL and "aligned" in _msg(lib)
+    need = lib.ss_fwd_workspace_size(2, 32, 80, 64)
+    assert _fwd(lib, dstate=80) == EINVAL and "workspace" in _msg(lib)
+    assert _fwd(lib, dstate=80, ws=FAKE, ws_bytes=need - 1) == EINVAL and "workspace_bytes" in _msg(lib)
+    assert _fwd(lib, dstate=80, ws=MISALIGNED, ws_bytes=need) == EINVAL and "aligned" in _msg(lib)
+    # time segments: the segment summaries, 2 x slices x (nseg - 1) x batch
+    # x dim x 16 floats (64 channels, 8192 steps: 8 segments; 12288 channels
+    # fill the chip without them; fewer than 8192 steps never take them)
+    assert lib.ss_fwd_workspace_size(1, 12288, 16, 8192) == 0
+    assert lib.ss_fwd_workspace_size(1, 64, 16, 8191) == 0
+    assert lib.ss_fwd_workspace_size(1, 64, 16, 8192) == 2 * 7 * 64 * 16 * 4
+    assert lib.ss_fwd_workspace_size(3, 64, 16, 8192) == 3 * 2 * 7 * 64 * 16 * 4
 
 
 
