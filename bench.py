@@ -441,6 +441,43 @@ def ssd_detail(hip, lib, to_dev, dev):
                      "input_sets_rotated": 2}}
 
 
+def conv_scan_detail(hip, lib, to_dev, dev):
+    """The convolution fused into the scan's load stage (ss_fwd_conv) at the
+    c1 bf16 forward shape with a width-4 SiLU convolution, against the two
+    separate calls it replaces (ss_conv1d_fwd, then ss_fwd on its output).
+    Inputs rotated over two sets; HIP events around each kernel."""
+    import torch
+
+    from selective_state_space_scan_amd import binding
+    from selective_state_space_scan_amd import inputs as ssin
+    w = ssin.WORKLOADS["mamba130m_fwd_bf16_8x1536x2048"]
+    a = ssin.make(w)
+    ac = ssin.make_conv(ssin.CONV_WORKLOADS["mamba130m_conv_bf16_8x1536x2048"])
+    sets = [{k: to_dev(v) for k, v in a.items()} for _ in range(2)]
+    cw, cb = to_dev(ac["weight"]), to_dev(ac["bias"])
+    del a, ac
+    outs = [torch.empty_like(c["u"]) for c in sets]
+    us = [torch.empty_like(c["u"]) for c in sets]
+    fused = [lambda c=c, o=o: binding.ss_fwd_conv(c["u"], cw, c["delta"], c["A"], c["B"], c["C"],
+                                                  c["D"], c["z"], c["delta_bias"], True,
+                                                  conv_bias=cb, out=o)
+             for c, o in zip(sets, outs)]
+
+    def sep(c, o, u):
+        binding.ss_conv1d_fwd(c["u"], cw, cb, True, out=u)
+        binding.ss_fwd(u, c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"], c["delta_bias"],
+                       True, out=o)
+    separate = [lambda c=c, o=o, u=u: sep(c, o, u) for c, o, u in zip(sets, outs, us)]
+    (fms,) = timed_calls(hip, lib, fused, 2, 20)
+    conv_ms, _, scan_ms = timed_calls(hip, lib, separate, 4, 20)
+    del sets, outs, us
+    return {"mamba130m_fwd_conv_bf16_8x1536x2048": {
+        "fused_kernel_ms": round(fms, 5), "separate_conv_ms": round(conv_ms, 5),
+        "separate_scan_ms": round(scan_ms, 5),
+        "separate_total_ms": round(conv_ms + scan_ms, 5),
+        "elements_per_s": w.batch * w.dim * w.seqlen / (fms * 1e-3)}}
+
+
 def conv_detail(hip, lib, to_dev, dev):
     """The causal convolution (width 4) in front of the scan: forward and
     backward at the Mamba-130m layer shape in bf16 and f32, and the decode
@@ -518,6 +555,12 @@ def _scan_call(name, to_dev, dev):
                                                 out=out)), (d, out)
     y = torch.empty_like(d["u"])
     last = (torch.empty(w.batch, w.dim, w.dstate, device=dev) if w.last_state else None)
+    if name.startswith("fwdconv"):   # the convolution fused in front of the scan
+        ac = ssin.make_conv(ssin.CONV_WORKLOADS["mamba130m_conv_bf16_8x1536x2048"])
+        cw, cb = to_dev(ac["weight"]), to_dev(ac["bias"])
+        return (lambda: binding.ss_fwd_conv(d["u"], cw, d["delta"], d["A"], d["B"], d["C"],
+                                            d["D"], d["z"], d["delta_bias"], True,
+                                            conv_bias=cb, out=y)), (d, y, cw, cb)
     if w.kind == "fwd" or name.startswith("fwd"):
         return (lambda: binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                        d["delta_bias"], True, out=y, last_state=last)), (d, y, last)
@@ -543,6 +586,7 @@ PROFILE_WORKLOADS = {
     "step_bf16_8x1536x2048": "mamba130m_bwd_bf16_8x1536x2048",
     "bwd_f32_8x1536x2048_standalone": "mamba130m_bwd_f32_8x1536x2048",
     "fwd_bf16_8x1536x2048": "mamba130m_fwd_bf16_8x1536x2048",
+    "fwdconv_bf16_8x1536x2048": "mamba130m_fwd_bf16_8x1536x2048",
     "fwd_bf16_4x5120x4096": "mamba2p8b_fwd_bf16_4x5120x4096",
     "decode_bf16_256x5120": "decode_bf16_256x5120",
     "fwd_bf16_1x1536x16384": "mamba130m_long_bf16_1x1536x16384",
@@ -851,6 +895,7 @@ def main():
         detail.update(long_sequence_detail(to_dev, dev))
         detail.update(wide_state_detail(hip, lib, to_dev, dev))
         detail.update(conv_detail(hip, lib, to_dev, dev))
+        detail.update(conv_scan_detail(hip, lib, to_dev, dev))
         detail.update(ssd_detail(hip, lib, to_dev, dev))
         result["detail"] = detail
 

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 10
+#define SS_ABI_VERSION 11
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -287,6 +287,39 @@ ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t widt
 ss_status ss_conv1d_update(int64_t batch, int64_t dim, int64_t width, int io_dtype, float *state,
                            const void *x, const float *weight, const float *bias, int silu,
                            void *out, void *stream);
+
+/*
+ * The convolution fused into the scan's load stage: ss_fwd with
+ *   u = ss_conv1d_fwd(x, conv_weight, conv_bias, conv_silu, conv_init)
+ * computed per element inside the scan (the state-spaces/mamba README,
+ * "Usage", Mamba block: a d_conv = 4 convolution right in front of the
+ * SSM; the mamba-rs README, "Features", lists scan and convolution kernels
+ * together).  u never reaches memory.  Each u is rounded to the io dtype
+ * exactly as ss_conv1d_fwd stores it, so the outputs, last_state, the
+ * saved ckpt and conv_final are the same bits as ss_conv1d_fwd followed by
+ * ss_fwd on its output -- a training step can take the backward through
+ * ss_bwd (with u from ss_conv1d_fwd and this call's ckpt) and
+ * ss_conv1d_bwd.
+ *   x                  (batch, dim, seqlen) io dtype: the convolution's input.
+ *   conv_weight        (dim, conv_width) f32, required; conv_width 1..4.
+ *   conv_bias          (dim) f32 or NULL.
+ *   conv_init          (batch, dim, conv_width - 1) f32 or NULL (zeros).
+ *   conv_final         (batch, dim, conv_width - 1) f32 or NULL: receives the
+ *                      last conv_width - 1 inputs (as ss_conv1d_fwd's
+ *                      final_state); must not overlap conv_init.
+ *   The scan arguments are ss_fwd's.  dstate 1..64 (SS_EUNSUPPORTED above:
+ *   call ss_conv1d_fwd, then ss_fwd).  out must not overlap x (workgroups
+ *   read other rows' and steps' inputs for the convolution's window).
+ *   Workspace: ss_fwd_workspace_size().
+ */
+ss_status ss_fwd_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                      const void *x, const float *conv_weight, int64_t conv_width,
+                      const float *conv_bias, int conv_silu, const float *conv_init,
+                      const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, void *out, float *last_state,
+                      float *conv_final, float *ckpt, void *workspace, size_t workspace_bytes,
+                      void *stream);
 
 /*
  * Mamba-2 SSD forward: the selective scan with a scalar A per head (the SSD

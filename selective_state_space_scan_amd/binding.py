@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 10
+ABI_VERSION = 11
 _lock = threading.Lock()
 _lib = None
 
@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
             lib.ss_fwd.restype = c_int
             lib.ss_fwd.argtypes = ([i64] * 4 + [c_int] + [vp] * 8 + [c_int] + [vp] * 5
                                    + [sz, vp])
+            lib.ss_fwd_conv.restype = c_int
+            lib.ss_fwd_conv.argtypes = ([i64] * 4 + [c_int] + [vp] * 2 + [i64] + [vp] + [c_int]
+                                        + [vp] * 8 + [c_int] + [vp] * 6 + [sz, vp])
             lib.ss_fwd_workspace_size.restype = sz
             lib.ss_fwd_workspace_size.argtypes = [i64] * 4
             lib.ss_ckpt_size.restype = sz
@@ -186,6 +189,38 @@ def ss_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=Fa
                       0 if workspace is None else workspace.numel() * workspace.element_size(),
                       _stream()))
     return (out, last_state) if (return_last_state or last_state is not None) else out
+
+
+def ss_fwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=None,
+                delta_softplus=False, conv_bias=None, conv_silu=True, conv_init=None,
+                h0=None, out=None, last_state=None, conv_final=None, ckpt=None,
+                workspace=None):
+    """The causal convolution fused in front of the scan: ss_fwd with
+    ``u = ss_conv1d_fwd(x, conv_weight, conv_bias, conv_silu, conv_init)``
+    computed inside the scan.  Returns ``out``; last_state and conv_final,
+    when given, are filled in place.  dstate up to 64."""
+    lib = load()
+    batch, dim, seqlen = x.shape
+    dstate = A.shape[1]
+    width = conv_weight.shape[1]
+    io = _io_dtype(x)
+    _same_io(io, delta, B, C, z)
+    if out is None:
+        out = torch.empty_like(x)
+    need = ss_fwd_workspace_size(batch, dim, dstate, seqlen)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib.ss_fwd_conv(batch, dim, dstate, seqlen, io, _ptr(x),
+                           _f32(conv_weight, "conv_weight"), width,
+                           _f32(conv_bias, "conv_bias"), int(bool(conv_silu)),
+                           _f32(conv_init, "conv_init"), _ptr(delta), _f32(A, "A"), _ptr(B),
+                           _ptr(C), _f32(D, "D"), _ptr(z), _f32(delta_bias, "delta_bias"),
+                           int(bool(delta_softplus)), _f32(h0, "h0"), _ptr(out),
+                           _f32(last_state, "last_state"), _f32(conv_final, "conv_final"),
+                           _f32(ckpt, "ckpt"), _ptr(workspace),
+                           0 if workspace is None else workspace.numel() * workspace.element_size(),
+                           _stream()))
+    return out
 
 
 def ss_bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SS_F32) -> int:

@@ -202,11 +202,24 @@ size_t ss_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
     return ssk::fwd_workspace_bytes(batch, dim, seqlen, int(dstate));
 }
 
-ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
-                 const void *u, const void *delta, const float *A, const void *B, const void *C,
-                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
-                 const float *h0, void *out, float *last_state, float *ckpt, void *workspace,
-                 size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The causal convolution in front of the scan (ss_fwd_conv), already
+// validated by the caller.
+struct ConvArgs {
+    int width, silu;
+    const float *w, *b, *init;
+    float *final_state;
+};
+
+ss_status fwd_impl(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                   const void *u, const void *delta, const float *A, const void *B, const void *C,
+                   const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                   const float *h0, void *out, float *last_state, float *ckpt, void *workspace,
+                   size_t workspace_bytes, void *stream, const ConvArgs *conv) {
+    const char *uname = conv ? "x" : "u";
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
     st = check_scan_grids(batch, dim, dstate, seqlen, false);
@@ -214,13 +227,13 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     const bool has_rows = batch > 0 && dim > 0;
     Check c;
     if (has_rows && seqlen > 0) {
-        c.need(u, "u");
+        c.need(u, uname);
         c.need(delta, "delta");
         c.need(B, "B");
         c.need(C, "C");
         c.need(out, "out");
     } else {
-        c.opt(u, "u"); c.opt(delta, "delta"); c.opt(B, "B"); c.opt(C, "C"); c.opt(out, "out");
+        c.opt(u, uname); c.opt(delta, "delta"); c.opt(B, "B"); c.opt(C, "C"); c.opt(out, "out");
     }
     if (dim > 0) c.need(A, "A"); else c.opt(A, "A");
     c.opt(D, "D");
@@ -248,9 +261,31 @@ ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int
     p.ypre = (ckpt && ssk::state_slices(int(dstate)) == 1)
                  ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
     p.ypart = static_cast<float *>(workspace);
+    if (conv) {
+        p.conv_width = conv->width;
+        p.conv_silu = conv->silu;
+        p.conv_w = conv->w;
+        p.conv_b = conv->b;
+        p.conv_init = conv->init;
+        p.conv_final = conv->final_state;
+    }
     ssk::profile_mark(static_cast<hipStream_t>(stream));
     return device_status(ssk::launch_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
-                         "ss_fwd launch");
+                         conv ? "ss_fwd_conv launch" : "ss_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int delta_softplus,
+                 const float *h0, void *out, float *last_state, float *ckpt, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    return fwd_impl(batch, dim, dstate, seqlen, io_dtype, u, delta, A, B, C, D, z, delta_bias,
+                    delta_softplus, h0, out, last_state, ckpt, workspace, workspace_bytes, stream,
+                    nullptr);
 }
 
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
@@ -498,6 +533,42 @@ ss_status ss_conv1d_fwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t widt
     return device_status(
         ssk::launch_conv_fwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
         "ss_conv1d_fwd launch");
+}
+
+ss_status ss_fwd_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                      const void *x, const float *conv_weight, int64_t conv_width,
+                      const float *conv_bias, int conv_silu, const float *conv_init,
+                      const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, void *out, float *last_state,
+                      float *conv_final, float *ckpt, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    ss_status st = check_conv_dims(batch, dim, seqlen, conv_width, io_dtype);
+    if (st != SS_OK) return st;
+    if (dstate > 16 * ssk::kMaxLaneSlices && dstate <= ssk::kMaxState)
+        return fail(SS_EUNSUPPORTED,
+                    "dstate %lld: the fused convolution runs up to %d states (call "
+                    "ss_conv1d_fwd, then ss_fwd)",
+                    (long long)dstate, 16 * ssk::kMaxLaneSlices);
+    Check c;
+    if (dim > 0) c.need(conv_weight, "conv_weight"); else c.opt(conv_weight, "conv_weight");
+    c.opt(conv_bias, "conv_bias");
+    c.opt(conv_init, "conv_init");
+    c.opt(conv_final, "conv_final");
+    if (c.st != SS_OK) return c.st;
+    const size_t win = size_t(batch) * size_t(dim) * size_t(conv_width - 1) * sizeof(float);
+    if (overlaps(conv_init, win, conv_final, win))
+        return fail(SS_EINVAL, "conv_final must not overlap conv_init");
+    // workgroups read inputs of other workgroups' rows and steps (the
+    // convolution's halo), so the output may not overwrite them
+    const size_t esz = io_dtype == SS_BF16 ? 2 : 4;
+    const size_t ebytes = size_t(batch) * size_t(dim) * size_t(seqlen) * esz;
+    if (overlaps(x, ebytes, out, ebytes)) return fail(SS_EINVAL, "out must not overlap x");
+    const ConvArgs conv{int(conv_width), conv_silu != 0, conv_weight, conv_bias, conv_init,
+                        conv_final};
+    return fwd_impl(batch, dim, dstate, seqlen, io_dtype, x, delta, A, B, C, D, z, delta_bias,
+                    delta_softplus, h0, out, last_state, ckpt, workspace, workspace_bytes, stream,
+                    &conv);
 }
 
 ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,

@@ -92,6 +92,71 @@ __device__ __forceinline__ void scan_step_acc(float dl, float dlu, float a2, flo
     v = __builtin_fmaf(c, h, v);
 }
 
+// ---------------------------------------------------------------------------
+// The causal convolution in front of the scan (fused forward).  The lane
+// that owns element t of its row (step n of a 16-step block) forms
+//   u_t = act(bias + sum_k w[k] x_{t-H+k}),   H = K - 1,
+// the taps added in ascending k as the convolution kernel adds them, and
+// rounds u to the io type as that kernel stores it, so the fused forward and
+// the convolution kernel followed by the scan give the same bits.  The
+// inputs at lags 1..3 come from lanes n - 1 .. n - 3 of the same DPP row,
+// or of the previous block for the first lanes.
+struct ConvLane {
+    float wl[kConvMaxWidth];   // weight of lag j (tap K - 1 - j); zero past K
+    float b;
+    int K;
+    bool silu;
+};
+
+__device__ __forceinline__ ConvLane conv_lane(const FwdParams &p, int64_t d, bool row_ok) {
+    ConvLane c;
+    c.K = p.conv_width;
+    c.silu = p.conv_silu != 0;
+    c.b = (row_ok && p.conv_b) ? p.conv_b[d] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kConvMaxWidth; j++)
+        c.wl[j] = (row_ok && j < c.K) ? p.conv_w[d * c.K + (c.K - 1 - j)] : 0.0f;
+    return c;
+}
+
+// lane n of a DPP row: `cur` of lane n - J when n >= J, else `prev` of lane
+// n + 16 - J (a rotate of prev, then a shift of cur whose out-of-row source
+// lanes keep the rotated value)
+template <int J>
+__device__ __forceinline__ float lagged(float cur, float prev) {
+    // a rotate never leaves the row, so it needs no old value
+    const int o = __builtin_amdgcn_mov_dpp(__float_as_int(prev), 0x120 + J, 0xf, 0xf, false);
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(o, __float_as_int(cur), 0x110 + J, 0xf, 0xf, false));
+}
+
+// u of the lane's element: x its input, prev the lane's input one block
+// (16 steps) earlier.  KC: the width when fixed at compile time (4, the
+// Mamba block's), else 0 and c.K is read at run time.
+template <typename T, int KC>
+__device__ __forceinline__ float conv_u(const ConvLane &c, float x, float prev) {
+    const int K = KC > 0 ? KC : c.K;
+    float acc = c.b;
+    if (K == 4) acc = __builtin_fmaf(c.wl[3], lagged<3>(x, prev), acc);
+    if (K >= 3) acc = __builtin_fmaf(c.wl[2], lagged<2>(x, prev), acc);
+    if (K >= 2) acc = __builtin_fmaf(c.wl[1], lagged<1>(x, prev), acc);
+    acc = __builtin_fmaf(c.wl[0], x, acc);
+    const float u = c.silu ? acc * sigmoid_f32(acc) : acc;
+    return to_f32<T>(from_f32<T>(u));
+}
+
+// The input the lane would hold one block before step t0: x of its row at
+// t0 - 16 + n, the initial window for the H steps before 0, else zero.
+template <typename T>
+__device__ __forceinline__ float conv_prev(const FwdParams &p, int64_t b, int64_t d, bool row_ok,
+                                           int64_t t0, int n) {
+    const int64_t t = t0 - 16 + n;
+    const int H = p.conv_width - 1;
+    if (!row_ok || t < -H) return 0.0f;
+    if (t >= 0) return to_f32<T>(ld_global(static_cast<const T *>(p.u) + (b * p.dim + d) * p.seqlen + t));
+    return p.conv_init ? p.conv_init[(b * p.dim + d) * H + (t + H)] : 0.0f;
+}
+
 // Where segment j's summary (end state from zero, then total decay) of
 // slice sl, batch entry b, row d, state n lives.
 __device__ __forceinline__ size_t summ_index(const FwdParams &p, int sl, int j, int64_t b,
@@ -123,7 +188,7 @@ __device__ __forceinline__ float state_step(float dl, float dlu, float a2, float
     return __builtin_fmaf(exp2_hw(row_bcast<J>(dl) * a2), h, row_bcast<J>(dlu) * b);
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, int CONV = 0>
 __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
     using SM = SumSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
@@ -161,6 +226,13 @@ __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
     const int64_t tbeg = int64_t(seg) * p.seg_len;
     const int nchunk = p.seg_len / kTS;
     float h = 0.0f, dlsum = 0.0f;
+    // fused convolution: the staged u tile holds its input x
+    ConvLane cv{};
+    float xprev = 0.0f;
+    if constexpr (CONV != 0) {
+        cv = conv_lane(p, d, row_ok);
+        xprev = conv_prev<T>(p, b, d, row_ok, tbeg, n);
+    }
     st.fetch(tbeg, L, tid);
     st.stash(smem, Ns < kN);
     __syncthreads();
@@ -174,7 +246,13 @@ __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
             float x = to_f32<T>(sDl[r][col]) + bias;
             if (p.softplus) x = softplus_f32(x);
             dl[s] = row_ok ? x : 0.0f;
-            dlu[s] = dl[s] * to_f32<T>(sU[r][col]);
+            float uv = to_f32<T>(sU[r][col]);
+            if constexpr (CONV != 0) {
+                const float xin = uv;
+                uv = row_ok ? conv_u<T, (CONV > 0 ? CONV : 0)>(cv, xin, xprev) : 0.0f;
+                xprev = xin;
+            }
+            dlu[s] = dl[s] * uv;
             dlsum += dl[s];
         }
 #pragma unroll
@@ -220,9 +298,12 @@ __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
 // terms C h of a step are added over the slices in the lane, in ascending
 // order, before the sum over the row's 16 lanes.  Grid z holds (slice, time
 // segment); with S > 1 it holds the segment only.
-template <typename T, int VEC, int NW, bool PART, int S = 1>
+// CONV: 0 no convolution; 4 the fused convolution of width 4; -1 of the
+// width p.conv_width
+template <typename T, int VEC, int NW, bool PART, int S = 1, int CONV = 0>
 __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) void ss_fwd_kernel(FwdParams p) {
     static_assert(S >= 1 && !(PART && S > 1), "slices run either in the lane or one per grid z");
+    static_assert(!(PART && CONV), "the fused convolution runs with the slices in the lane");
     using OutT = std::conditional_t<PART, float, T>;
     using SM = FwdSmem<T, NW, S>;
     constexpr int kT = SM::kTc;          // steps per chunk
@@ -347,6 +428,16 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
         st.fetch(int64_t(cbeg) * kT, L, tid);
         st.stash(smem, zero_dead);
     }
+    // fused convolution: u holds its input x; the lane's input one block
+    // before the segment's first step
+    ConvLane cv{};
+    float xprev = 0.0f;
+    if constexpr (CONV != 0) {
+        cv = conv_lane(p, d, row_ok);
+        xprev = conv_prev<T>(p, b, d, row_ok, tbeg, n);
+        __asm__("" : "+v"(xprev), "+v"(cv.b), "+v"(cv.wl[0]), "+v"(cv.wl[1]), "+v"(cv.wl[2]),
+                "+v"(cv.wl[3]));
+    }
     // Make the per-row parameter loads complete here.  Left pending into the
     // chunk loop, their first use there would be a wait on the in-order
     // memory counter that also drains the chunk prefetch.
@@ -393,6 +484,11 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
                 uu[s] = un[s];
                 zz[s] = zn[s];
                 x = dn[s] + bias;
+            }
+            if constexpr (CONV != 0) {   // uu held the convolution's input
+                const float xin = uu[s];
+                uu[s] = row_ok ? conv_u<T, (CONV > 0 ? CONV : 0)>(cv, xin, xprev) : 0.0f;
+                xprev = xin;
             }
             if (p.softplus) x = softplus_f32(x);
             dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps leave the state unchanged
@@ -466,6 +562,11 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
         __syncthreads();
     }
 
+    if (CONV != 0 && p.conv_final && row_ok && seg == p.nseg - 1 && n < p.conv_width - 1) {
+        // the convolution's final window: the row's last H inputs
+        const int H = p.conv_width - 1;
+        p.conv_final[(b * Dm + d) * H + n] = conv_prev<T>(p, b, d, row_ok, L - H + 16, n);
+    }
     if (p.last_state && row_ok && seg == p.nseg - 1) {
 #pragma unroll
         for (int k = 0; k < S; k++)
@@ -512,29 +613,40 @@ __global__ __launch_bounds__(256) void ss_fwd_combine_kernel(FwdParams p, int sl
     else st_global(static_cast<T *>(p.out) + e0, from_f32<T>(y[0]));
 }
 
-template <typename T, int VEC, int NW, bool PART, int S = 1>
+template <typename T, int VEC, int NW, bool PART, int S = 1, int CONV = 0>
 void launch_scan(const FwdParams &p, hipStream_t stream) {
     const int zslices = S > 1 ? 1 : state_slices(p.nstate);
     const dim3 grid(static_cast<unsigned>((p.dim + 4 * NW - 1) / (4 * NW)),
                     static_cast<unsigned>(p.batch), static_cast<unsigned>(zslices * p.nseg));
-    hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW, PART, S>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((ss_fwd_kernel<T, VEC, NW, PART, S, CONV>), grid, dim3(64 * NW), 0, stream, p);
 }
 
-template <typename T>
+template <typename T, int CONV = 0>
 void launch_summaries(const FwdParams &p, bool vec, hipStream_t stream) {
     constexpr int kVec = 16 / sizeof(T);
     const dim3 grid(static_cast<unsigned>((p.dim + 15) / 16), static_cast<unsigned>(p.batch),
                     static_cast<unsigned>(state_slices(p.nstate) * (p.nseg - 1)));
-    if (vec) hipLaunchKernelGGL((ss_fwd_summary_kernel<T, kVec>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((ss_fwd_summary_kernel<T, 1>), grid, dim3(256), 0, stream, p);
+    if (vec) hipLaunchKernelGGL((ss_fwd_summary_kernel<T, kVec, CONV>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((ss_fwd_summary_kernel<T, 1, CONV>), grid, dim3(256), 0, stream, p);
 }
 
-template <typename T, bool PART, int S = 1>
+template <typename T, bool PART, int S = 1, int CONV = 0>
 void launch_scan_vec(const FwdParams &p, bool vec, hipStream_t stream) {
     constexpr int kVec = 16 / sizeof(T);
-    if (p.nseg > 1) launch_summaries<T>(p, vec, stream);   // the segments' summaries first
-    if (vec) launch_scan<T, kVec, 4, PART, S>(p, stream);
-    else launch_scan<T, 1, 4, PART, S>(p, stream);
+    if (p.nseg > 1) launch_summaries<T, CONV>(p, vec, stream);   // the segments' summaries first
+    if (vec) launch_scan<T, kVec, 4, PART, S, CONV>(p, stream);
+    else launch_scan<T, 1, 4, PART, S, CONV>(p, stream);
+}
+
+// up to kMaxLaneSlices slices, all in the lane
+template <typename T, int CONV>
+void launch_lane_slices(const FwdParams &p, bool vec, hipStream_t stream) {
+    switch (state_slices(p.nstate)) {
+        case 1: launch_scan_vec<T, false, 1, CONV>(p, vec, stream); break;
+        case 2: launch_scan_vec<T, false, 2, CONV>(p, vec, stream); break;
+        case 3: launch_scan_vec<T, false, 3, CONV>(p, vec, stream); break;
+        default: launch_scan_vec<T, false, 4, CONV>(p, vec, stream); break;
+    }
 }
 
 // part of the forward workspace taken by per-slice partial outputs (floats)
@@ -559,15 +671,15 @@ hipError_t launch_typed(const FwdParams &p0, hipStream_t stream) {
     }
     if (slices <= kMaxLaneSlices) {
         if (slices > 1) p.ypre = nullptr;   // saved only with one slice
-        switch (slices) {
-            case 1: launch_scan_vec<T, false, 1>(p, vec, stream); break;
-            case 2: launch_scan_vec<T, false, 2>(p, vec, stream); break;
-            case 3: launch_scan_vec<T, false, 3>(p, vec, stream); break;
-            default: launch_scan_vec<T, false, 4>(p, vec, stream); break;
-        }
+        // the fused convolution: width 4 (the Mamba block's) fixed at compile
+        // time, other widths read at run time
+        if (p.conv_width == 4) launch_lane_slices<T, 4>(p, vec, stream);
+        else if (p.conv_width > 0) launch_lane_slices<T, -1>(p, vec, stream);
+        else launch_lane_slices<T, 0>(p, vec, stream);
         profile_mark(stream);
         return hipGetLastError();
     }
+    if (p.conv_width > 0) return hipErrorInvalidValue;   // the ABI admits it up to 64 states
     // the slices see no D term and no gate; the combine adds them
     FwdParams q = p;
     q.D = nullptr;

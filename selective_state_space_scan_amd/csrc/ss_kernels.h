@@ -100,6 +100,18 @@ struct FwdParams : ScanParams {
     int seg_len = 0;       // steps per segment
     float *summ = nullptr; // workspace, nseg > 1: per (slice, segment < nseg - 1, batch,
                            // dim, 16) the segment's end state from zero, then its decay
+    // Causal convolution in front of the scan (conv_width > 0): u holds the
+    // convolution's input x, and the scan's u_t = act(bias + sum_k
+    // w[d,k] x_{t-H+k}), H = conv_width - 1, act = SiLU or identity,
+    // rounded to the io type as the convolution kernel stores it.  The H
+    // inputs before t = 0 come from conv_init (batch, dim, H) or are zero;
+    // conv_final (batch, dim, H) receives the last H inputs.
+    int conv_width = 0;
+    int conv_silu = 0;
+    const float *conv_w = nullptr;     // (dim, conv_width)
+    const float *conv_b = nullptr;     // (dim) or nullptr
+    const float *conv_init = nullptr;
+    float *conv_final = nullptr;
 };
 
 struct BwdParams : ScanParams {

@@ -19,6 +19,7 @@ HEADER = os.path.join(ROOT, "include", "ss.h")
 EINVAL, EUNSUP = binding.SS_EINVAL, binding.SS_EUNSUPPORTED
 FAKE = 0x10000          # a 16-byte aligned non-null address (never dereferenced)
 MISALIGNED = 0x10004
+FAKE2 = 0x40000000     # another one, far from FAKE (no overlap of small tensors)
 
 
 @pytest.fixture(scope="module")
@@ -32,13 +33,13 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = re.findall(r"^\w[\w\s\*]*?\b(ss_\w+)\s*\(", open(HEADER).read(), flags=re.M)
     assert set(names) >= {"ss_fwd", "ss_bwd", "ss_bwd_workspace_size", "ss_state_update",
-                          "ss_last_error", "ss_abi_version"}
+                          "ss_last_error", "ss_abi_version", "ss_fwd_conv"}
     for n in names:
         assert hasattr(lib, n), f"libss.so does not export {n}"
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 10
+    assert lib.ss_abi_version() == 11
 
 
 def test_ckpt_size(lib):
@@ -237,6 +238,29 @@ def test_conv_update_checks(lib):
     assert st == EINVAL and "state" in _msg(lib)
     st = lib.ss_conv1d_update(2, 8, 5, 0, FAKE, FAKE, FAKE, None, 1, FAKE, None)
     assert st == EUNSUP and "width" in _msg(lib)
+
+
+def _fwd_conv(lib, batch=2, dim=32, dstate=16, seqlen=64, io=0, x=FAKE, w=FAKE, width=4,
+              cb=None, init=None, delta=FAKE, out=FAKE2, final=None):
+    lib.ss_fwd_conv.argtypes = ([ctypes.c_int64] * 4 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                                + [ctypes.c_int64] + [ctypes.c_void_p] + [ctypes.c_int]
+                                + [ctypes.c_void_p] * 8 + [ctypes.c_int] + [ctypes.c_void_p] * 6
+                                + [ctypes.c_size_t, ctypes.c_void_p])
+    return lib.ss_fwd_conv(batch, dim, dstate, seqlen, io, x, w, width, cb, 1, init, delta, FAKE,
+                           FAKE, FAKE, None, None, None, 1, None, out, None, final, None, None, 0,
+                           None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(width=5), EUNSUP, "width"), (dict(width=0), EINVAL, "width"),
+    (dict(dstate=80), EUNSUP, "64"), (dict(dstate=300), EUNSUP, "dstate"),
+    (dict(w=None), EINVAL, "conv_weight"), (dict(x=None), EINVAL, "x"),
+    (dict(w=MISALIGNED), EINVAL, "aligned"), (dict(out=FAKE), EINVAL, "overlap x"),
+    (dict(init=FAKE, final=FAKE), EINVAL, "conv_final"), (dict(seqlen=-1), EINVAL, "seqlen"),
+])
+def test_fwd_conv_checks(lib, kw, status, word):
+    assert _fwd_conv(lib, **kw) == status
+    assert word in _msg(lib)
 
 
 def test_fwd_workspace(lib):
