@@ -470,12 +470,50 @@ def conv_scan_detail(hip, lib, to_dev, dev):
     separate = [lambda c=c, o=o, u=u: sep(c, o, u) for c, o, u in zip(sets, outs, us)]
     (fms,) = timed_calls(hip, lib, fused, 2, 20)
     conv_ms, _, scan_ms = timed_calls(hip, lib, separate, 4, 20)
-    del sets, outs, us
-    return {"mamba130m_fwd_conv_bf16_8x1536x2048": {
+    out = {"mamba130m_fwd_conv_bf16_8x1536x2048": {
         "fused_kernel_ms": round(fms, 5), "separate_conv_ms": round(conv_ms, 5),
         "separate_scan_ms": round(scan_ms, 5),
         "separate_total_ms": round(conv_ms + scan_ms, 5),
         "elements_per_s": w.batch * w.dim * w.seqlen / (fms * 1e-3)}}
+    # a training step of the convolution + scan: fused (ss_fwd_conv saving
+    # its record, ss_bwd_conv) against the separate calls (ss_conv1d_fwd,
+    # ss_fwd saving its record, ss_bwd, ss_conv1d_bwd on its du)
+    wb = ssin.WORKLOADS["mamba130m_bwd_bf16_8x1536x2048"]
+    c = {k: to_dev(v) for k, v in ssin.make(wb).items()}
+    ck = binding.ss_ckpt_empty(c["u"])
+    ws = torch.empty(binding.ss_bwd_workspace_size(wb.batch, wb.dim, 16, wb.seqlen, 1),
+                     dtype=torch.uint8, device=dev)
+    y, u = torch.empty_like(c["u"]), torch.empty_like(c["u"])
+
+    def fused_step():
+        binding.ss_fwd_conv(c["u"], cw, c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"],
+                            c["delta_bias"], True, conv_bias=cb, out=y, ckpt=ck)
+        binding.ss_bwd_conv(c["u"], cw, c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"],
+                            c["delta_bias"], True, c["dout"], conv_bias=cb, workspace=ws, ckpt=ck)
+
+    def separate_step():
+        binding.ss_conv1d_fwd(c["u"], cw, cb, True, out=u)
+        binding.ss_fwd(u, c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"], c["delta_bias"],
+                       True, out=y, ckpt=ck)
+        g = binding.ss_bwd(u, c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"],
+                           c["delta_bias"], True, c["dout"], workspace=ws, ckpt=ck)
+        binding.ss_conv1d_bwd(c["u"], cw, cb, True, None, g["du"])
+    res = {}
+    for name, fn in (("fused_step_ms", fused_step), ("separate_step_ms", separate_step)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / 10, 5)
+    res["elements_per_s"] = wb.batch * wb.dim * wb.seqlen / (res["fused_step_ms"] * 1e-3)
+    out["mamba130m_step_conv_bf16_8x1536x2048"] = res
+    del sets, outs, us, c, ck, ws, y, u
+    return out
 
 
 def conv_detail(hip, lib, to_dev, dev):

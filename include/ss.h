@@ -322,6 +322,35 @@ ss_status ss_fwd_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen
                       void *stream);
 
 /*
+ * Backward of ss_fwd_conv with the convolution's backward fused into the
+ * scan's reverse pass: u is recomputed from x exactly as the forward formed
+ * it, and the gradient reaching u goes straight through the convolution
+ * (du never reaches memory).  Gradients of the loss
+ *     sum(dout * out) + sum(dlast * last_state)
+ * with respect to x (dx, required, io dtype), conv_weight (dconv_weight,
+ * required, summed over batch and time), conv_bias (dconv_bias, given
+ * exactly when conv_bias is), the initial window (dconv_init, optional; may
+ * be given without conv_init: the gradient at a zero window), and the
+ * scan's other inputs as in ss_bwd.  dstate 1..16 (SS_EUNSUPPORTED above:
+ * call ss_bwd, then ss_conv1d_bwd).  ckpt: what ss_fwd_conv saved for
+ * these inputs, or NULL.  dx must not overlap x.  Workspace:
+ * ss_bwd_workspace_size().  With time segments the input gradients of a
+ * segment's last conv_width - 1 steps are completed after the reverse pass
+ * from the next segment's first pre-activation gradients, in the order one
+ * pass adds them.
+ */
+ss_status ss_bwd_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                      const void *x, const float *conv_weight, int64_t conv_width,
+                      const float *conv_bias, int conv_silu, const float *conv_init,
+                      const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, const void *dout, const float *dlast,
+                      void *dx, float *dconv_weight, float *dconv_bias, float *dconv_init,
+                      void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
+                      float *ddelta_bias, float *dh0, const float *ckpt, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * Mamba-2 SSD forward: the selective scan with a scalar A per head (the SSD
  * module the state-spaces/mamba README names under "Mamba-2"; d_state
  * typically 64 or 128).  The pages print no formula; the reading is, per

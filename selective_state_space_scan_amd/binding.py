@@ -61,6 +61,9 @@ def load() -> ctypes.CDLL:
             lib.ss_fwd_conv.restype = c_int
             lib.ss_fwd_conv.argtypes = ([i64] * 4 + [c_int] + [vp] * 2 + [i64] + [vp] + [c_int]
                                         + [vp] * 8 + [c_int] + [vp] * 6 + [sz, vp])
+            lib.ss_bwd_conv.restype = c_int
+            lib.ss_bwd_conv.argtypes = ([i64] * 4 + [c_int] + [vp] * 2 + [i64] + [vp] + [c_int]
+                                        + [vp] * 8 + [c_int] + [vp] * 17 + [sz, vp])
             lib.ss_fwd_workspace_size.restype = sz
             lib.ss_fwd_workspace_size.argtypes = [i64] * 4
             lib.ss_ckpt_size.restype = sz
@@ -221,6 +224,55 @@ def ss_fwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=None,
                            0 if workspace is None else workspace.numel() * workspace.element_size(),
                            _stream()))
     return out
+
+
+def ss_bwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=None,
+                delta_softplus=False, dout=None, conv_bias=None, conv_silu=True,
+                conv_init=None, h0=None, dlast=None, want_dh0=False, want_dconv_init=False,
+                workspace=None, ckpt=None):
+    """Backward of ss_fwd_conv (the convolution's backward fused into the
+    scan's reverse pass).  Returns a dict with dx, dconv_weight, ddelta, dA,
+    dB, dC and, for the optional inputs given, dconv_bias, dconv_init, dD,
+    dz, ddelta_bias, dh0.  dstate up to 16."""
+    lib = load()
+    batch, dim, seqlen = x.shape
+    dstate = A.shape[1]
+    width = conv_weight.shape[1]
+    io = _io_dtype(x)
+    _same_io(io, delta, B, C, z, dout)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty_like(x), dconv_weight=torch.empty(dim, width, **f32),
+             ddelta=torch.empty_like(delta), dA=torch.empty(dim, dstate, **f32),
+             dB=torch.empty_like(B), dC=torch.empty_like(C))
+    if conv_bias is not None:
+        g["dconv_bias"] = torch.empty(dim, **f32)
+    if conv_init is not None or want_dconv_init:
+        g["dconv_init"] = torch.empty(batch, dim, width - 1, **f32)
+    if D is not None:
+        g["dD"] = torch.empty(dim, **f32)
+    if z is not None:
+        g["dz"] = torch.empty_like(z)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty(dim, **f32)
+    if h0 is not None or want_dh0:
+        g["dh0"] = torch.empty(batch, dim, dstate, **f32)
+    if workspace is None:
+        need = ss_bwd_workspace_size(batch, dim, dstate, seqlen, io)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.ss_bwd_conv(batch, dim, dstate, seqlen, io, _ptr(x),
+                           _f32(conv_weight, "conv_weight"), width,
+                           _f32(conv_bias, "conv_bias"), int(bool(conv_silu)),
+                           _f32(conv_init, "conv_init"), _ptr(delta), _f32(A, "A"), _ptr(B),
+                           _ptr(C), _f32(D, "D"), _ptr(z), _f32(delta_bias, "delta_bias"),
+                           int(bool(delta_softplus)), _f32(h0, "h0"), _ptr(dout),
+                           _f32(dlast, "dlast"), _ptr(g["dx"]), _ptr(g["dconv_weight"]),
+                           _ptr(g.get("dconv_bias")), _ptr(g.get("dconv_init")),
+                           _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                           _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                           _ptr(g.get("dh0")), _f32(ckpt, "ckpt"), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream()))
+    return g
 
 
 def ss_bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype=SS_F32) -> int:

@@ -310,7 +310,10 @@ ss_status bwd_params(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                      const void *C, const float *D, const void *z, const float *delta_bias,
                      int delta_softplus, const float *h0, const void *dout, const float *dlast,
                      void *du, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
-                     float *ddelta_bias, float *dh0, const float *ckpt, ssk::BwdParams *p) {
+                     float *ddelta_bias, float *dh0, const float *ckpt, ssk::BwdParams *p,
+                     bool conv = false) {
+    // conv: u is the fused convolution's input x, and du is not an output
+    const char *uname = conv ? "x" : "u";
     ss_status st = check_dims(batch, dim, dstate, seqlen, io_dtype, true);
     if (st != SS_OK) return st;
     st = check_scan_grids(batch, dim, dstate, seqlen, true);
@@ -319,10 +322,11 @@ ss_status bwd_params(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
     const bool has_elems = has_rows && seqlen > 0;
     Check c;
     if (has_elems) {
-        c.need(u, "u"); c.need(delta, "delta"); c.need(dout, "dout");
-        c.need(du, "du"); c.need(ddelta, "ddelta");
+        c.need(u, uname); c.need(delta, "delta"); c.need(dout, "dout");
+        if (!conv) c.need(du, "du");
+        c.need(ddelta, "ddelta");
     } else {
-        c.opt(u, "u"); c.opt(delta, "delta"); c.opt(dout, "dout");
+        c.opt(u, uname); c.opt(delta, "delta"); c.opt(dout, "dout");
         c.opt(du, "du"); c.opt(ddelta, "ddelta");
     }
     if (batch > 0 && seqlen > 0) {
@@ -569,6 +573,63 @@ ss_status ss_fwd_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen
     return fwd_impl(batch, dim, dstate, seqlen, io_dtype, x, delta, A, B, C, D, z, delta_bias,
                     delta_softplus, h0, out, last_state, ckpt, workspace, workspace_bytes, stream,
                     &conv);
+}
+
+ss_status ss_bwd_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                      const void *x, const float *conv_weight, int64_t conv_width,
+                      const float *conv_bias, int conv_silu, const float *conv_init,
+                      const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, const void *dout, const float *dlast,
+                      void *dx, float *dconv_weight, float *dconv_bias, float *dconv_init,
+                      void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
+                      float *ddelta_bias, float *dh0, const float *ckpt, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    ss_status st = check_conv_dims(batch, dim, seqlen, conv_width, io_dtype);
+    if (st != SS_OK) return st;
+    if (dstate > 16 && dstate <= ssk::kMaxState)
+        return fail(SS_EUNSUPPORTED,
+                    "dstate %lld: the fused convolution's backward runs up to 16 states (call "
+                    "ss_bwd, then ss_conv1d_bwd)",
+                    (long long)dstate);
+    ssk::BwdParams p;
+    st = bwd_params(batch, dim, dstate, seqlen, io_dtype, x, delta, A, B, C, D, z, delta_bias,
+                    delta_softplus, h0, dout, dlast, nullptr, ddelta, dA, dB, dC, dD, dz,
+                    ddelta_bias, dh0, ckpt, &p, true);
+    if (st != SS_OK) return st;
+    Check c;
+    if (batch > 0 && dim > 0 && seqlen > 0) c.need(dx, "dx"); else c.opt(dx, "dx");
+    if (dim > 0) { c.need(conv_weight, "conv_weight"); c.need(dconv_weight, "dconv_weight"); }
+    else { c.opt(conv_weight, "conv_weight"); c.opt(dconv_weight, "dconv_weight"); }
+    c.opt(conv_bias, "conv_bias"); c.opt(dconv_bias, "dconv_bias");
+    c.opt(conv_init, "conv_init"); c.opt(dconv_init, "dconv_init");
+    c.pair(dconv_bias, conv_bias, "dconv_bias", "conv_bias");
+    if (c.st != SS_OK) return c.st;
+    // workgroups read inputs of other segments' steps (the convolution's
+    // window), so dx may not overwrite x
+    const size_t ebytes = size_t(batch) * size_t(dim) * size_t(seqlen) * (io_dtype == SS_BF16 ? 2 : 4);
+    if (overlaps(x, ebytes, dx, ebytes)) return fail(SS_EINVAL, "dx must not overlap x");
+    const size_t need = ssk::bwd_workspace_bytes(batch, dim, seqlen, int(dstate));
+    if (need > 0) {
+        if (!workspace) return fail(SS_EINVAL, "workspace must not be NULL (%zu bytes needed)", need);
+        if (!aligned16(workspace)) return fail(SS_EINVAL, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(SS_EINVAL, "workspace_bytes %zu is smaller than the %zu bytes needed",
+                        workspace_bytes, need);
+    }
+    p.workspace = workspace;
+    p.conv_width = int(conv_width);
+    p.conv_silu = conv_silu != 0;
+    p.conv_w = conv_weight;
+    p.conv_b = conv_bias;
+    p.conv_init = conv_init;
+    p.dx = dx;
+    p.dconv_w = dconv_weight;
+    p.dconv_b = dconv_bias;
+    p.dconv_init = dconv_init;
+    ssk::profile_mark(static_cast<hipStream_t>(stream));
+    return device_status(ssk::launch_bwd(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream)),
+                         "ss_bwd_conv launch");
 }
 
 ss_status ss_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype,

@@ -53,6 +53,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "ss_conv_lane.h"
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_tiles.h"
@@ -91,6 +92,11 @@ struct Workspace {
     int seg_len;     // steps per segment (a multiple of 64; the last takes the rest)
     float *fsumm;    // nseg > 1, block states recomputed here: the forward's segment summaries
     float *asumm;    // nseg > 1: the adjoint's segment summaries (segments 1 .. nseg - 1)
+    // the fused convolution, per (batch, segment, dim): its weight-gradient
+    // partials by lag (4) and bias-gradient partial; the pre-activation
+    // gradients of a segment's first 4 steps and the partial input
+    // gradients of its last 4 (completed across segments by a fix-up pass)
+    float *dcwp, *dcbp, *dpre_head, *dx_tail;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -132,6 +138,11 @@ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L, int ns
     w.dbiasp = take(size_t(batch) * nseg * dim);
     w.slice_bytes = off - first;
     off += (slices - 1) * w.slice_bytes;
+    const size_t bsd = size_t(batch) * nseg * dim;
+    w.dcwp = take(bsd * kConvMaxWidth);
+    w.dcbp = take(bsd);
+    w.dpre_head = take(bsd * kConvMaxWidth);
+    w.dx_tail = take(bsd * kConvMaxWidth);
     w.dup = w.ddp = w.dzp = nullptr;
     if (slices > 1) {
         const size_t e = size_t(slices) * batch * dim * L;
@@ -209,7 +220,9 @@ __device__ __forceinline__ void fwd_step(float dl, float dlu, float a2, float b,
     h = __builtin_fmaf(exp2_hw(row_bcast<J>(dl) * a2), h, row_bcast<J>(dlu) * b);
 }
 
-template <typename T, int VEC>
+// CONV: 0, or the fused convolution's width (4, or -1: read at run time);
+// the u tile then holds the convolution's input
+template <typename T, int VEC, int CONV = 0>
 __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Workspace ws) {
     using SM = CkptSmem<T>;
     __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
@@ -265,6 +278,12 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
     const int64_t tbeg = int64_t(seg) * ws.seg_len;
     const int64_t tend = tbeg + ws.seg_len < L ? tbeg + ws.seg_len : L;
     const int64_t cbeg = tbeg / kT1, cend = (tend + kT1 - 1) / kT1;
+    ConvLane cv{};
+    float xprev = 0.0f;   // the lane's convolution input one block before
+    if constexpr (CONV != 0) {
+        cv = conv_lane(p, d, row_ok);
+        xprev = conv_prev<T>(p, b, d, row_ok, tbeg, n);
+    }
     if (cend > cbeg) {
         st.fetch(cbeg * kT1, L, tid);
         st.stash(smem, zero_dead);
@@ -280,7 +299,13 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
             float x = to_f32<T>(sDl[r][col]) + bias;
             if (p.softplus) x = softplus_f32(x);
             dl[s] = (t0 + col < L) ? x : 0.0f;
-            dlu[s] = dl[s] * to_f32<T>(sU[r][col]);
+            float uv = to_f32<T>(sU[r][col]);
+            if constexpr (CONV != 0) {
+                const float xin = uv;
+                uv = row_ok ? conv_u<T, (CONV > 0 ? CONV : 0)>(cv, xin, xprev) : 0.0f;
+                xprev = xin;
+            }
+            dlu[s] = dl[s] * uv;
         }
 #pragma unroll
         for (int s = 0; s < kT1 / 16; s++) {
@@ -483,11 +508,17 @@ struct RevSmem {
 // launch bound leaves 3 wavefronts per SIMD (2 for single-element loads).
 // PART: one 16-state slice of several (grid z): du, ddelta and dz are this
 // slice's f32 partials (the combine kernel adds the slices and the D terms).
-template <typename T, int VEC, bool YP, int NW, bool PART>
+// CONV: 0, or the fused convolution's width (4, or -1: read at run time):
+// u is recomputed from the convolution's input, and the input gradient dx,
+// the weight and bias gradients (per-row partials) and the initial window's
+// gradient come out instead of du.
+template <typename T, int VEC, bool YP, int NW, bool PART, int CONV = 0>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) : 1) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
     using SM = RevSmem<T, NW>;
     using OutT = std::conditional_t<PART, float, T>;
     static_assert(!(PART && YP), "slices recompute their share of the pre-gate output");
+    static_assert(!(PART && CONV), "the fused convolution runs with one slice");
+    constexpr int KC = CONV > 0 ? CONV : 0;
     // grid z: (slice, time segment)
     const int nsg = ws.nseg;
     const int slice = int(blockIdx.z) / nsg, seg = int(blockIdx.z) % nsg;
@@ -525,6 +556,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const int64_t tbeg = int64_t(seg) * ws.seg_len;
     const int64_t tend = tbeg + ws.seg_len < L ? tbeg + ws.seg_len : L;
     const int cbeg = int(tbeg / kC), cend = int((tend + kC - 1) / kC);
+    // fused convolution: this (batch, segment, row)'s partials, and the
+    // first of a segment's last H steps, whose input gradients need the next
+    // segment's first pre-activation gradients (none for the last segment)
+    const size_t bsd = (size_t(b) * nsg + seg) * size_t(Dm) + size_t(row_ok ? d : 0);
+    const int tail_start = (CONV != 0 && seg < nsg - 1) ? int(tend) - (p.conv_width - 1) : int(L);
     // Inside the chunk loop indices are 32-bit (seqlen <= 2^26), and global
     // accesses address the wavefront's 4 rows from a scalar base with 32-bit
     // byte offsets (4 rows x seqlen x 4 bytes < 2^32).
@@ -550,6 +586,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     float dA_acc = 0.0f;     // this lane's state entry, summed over time
     float dD_acc = 0.0f;     // elements owned by this lane
     float dbias_acc = 0.0f;
+    // fused convolution: its taps, the weight (by lag) and bias gradients of
+    // the lane's elements, and the pre-activation gradients of the block
+    // after the current one (zero past the segment's end)
+    ConvLane cv{};
+    float dwl[kConvMaxWidth] = {}, dcb = 0.0f, gnext = 0.0f;
+    if constexpr (CONV != 0) cv = conv_lane(p, d, row_ok);
 
     const T *gB = static_cast<const T *>(p.B) + (b * Nst + s0) * L;
     const T *gC = static_cast<const T *>(p.C) + (b * Nst + s0) * L;
@@ -566,6 +608,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     OutT *dd_b = (PART ? reinterpret_cast<OutT *>(ws.ddp + slice_el) : static_cast<OutT *>(p.ddelta)) + wavebase;
     OutT *dz_b = has_z ? (PART ? reinterpret_cast<OutT *>(ws.dzp + slice_el) : static_cast<OutT *>(p.dz)) + wavebase
                        : nullptr;
+    OutT *dx_b = CONV != 0 ? static_cast<OutT *>(p.dx) + wavebase : nullptr;
     const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
     auto elem_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(T)); };
     auto out_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(OutT)); };
@@ -657,7 +700,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // own, so the loads land in the same registers without copies.
     // (with seqlen 0 there is no chunk and nothing is loaded)
     float hn[kNB] = {}, ypn[kNB] = {}, un[kNB] = {}, dn[kNB] = {}, zn[kNB] = {}, gn[kNB] = {};
+    // fused convolution: the lane's input one block before the chunk, as raw
+    // bits loaded a chunk ahead (the initial window's value for the chunk
+    // at step 0)
+    ConvBits<T> xhn = 0;
+    const float xwin = CONV != 0 ? conv_window(p, b, d, row_ok, n) : 0.0f;
     auto load_next = [&](int tc) {
+        if constexpr (CONV != 0) xhn = conv_prev_bits<T>(p, b, d, row_ok, tc, n);
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
             const int t = tc + 16 * s + n;
@@ -705,6 +754,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row
         float dl[kNB], dlu[kNB], uu[kNB], sgd[kNB], dout[kNB], zz[kNB], dyv[kNB];
+        // fused convolution: the inputs by lag and d act / d pre of the
+        // lane's elements (un holds the convolution's input)
+        float xl[kNB][kConvMaxWidth], gpre[kNB];
+        if constexpr (CONV != 0) {
+            float xprv = t0 > 0 ? conv_bits_f32<T>(xhn) : xwin;
+#pragma unroll
+            for (int s = 0; s < kNB; s++) {
+                const float xin = un[s];
+                const float pre = conv_pre<KC>(cv, xin, xprv, xl[s]);
+                un[s] = row_ok ? conv_act<T>(cv, pre) : 0.0f;
+                gpre[s] = conv_act_grad(cv, pre);
+                xprv = xin;
+            }
+        }
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
             const int col = 16 * s + n;
@@ -846,8 +909,26 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             const float du = __builtin_fmaf(dl[s], sumB, dskip * dy);
             const float dd = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];
             if (row_ok && t0 + col < Ls) {
-                st_global(at_bytes(du_b, out_off(t0 + col)), from_f32<OutT>(du));
+                if constexpr (CONV == 0) st_global(at_bytes(du_b, out_off(t0 + col)), from_f32<OutT>(du));
                 st_global(at_bytes(dd_b, out_off(t0 + col)), from_f32<OutT>(dd));
+            }
+            if constexpr (CONV != 0) {
+                // the convolution's backward: pre-activation gradient, its
+                // share of the weight and bias gradients, and the input
+                // gradient dx_t = sum_j wl[j] g_{t+j} (leads from the next block)
+                const float g = (row_ok && t0 + col < Ls) ? du * gpre[s] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < kConvMaxWidth; j++) dwl[j] = __builtin_fmaf(g, xl[s][j], dwl[j]);
+                dcb += g;
+                const float dxv = conv_dx<KC>(cv, g, gnext);
+                gnext = g;
+                const int t = t0 + col;
+                if (row_ok && t < Ls) {
+                    if (t >= tail_start)   // completed across the segment boundary later
+                        ws.dx_tail[bsd * kConvMaxWidth + (t - tail_start)] = dxv;
+                    else
+                        st_global(at_bytes(dx_b, out_off(t)), from_f32<OutT>(dxv));
+                }
             }
             if (t0 + col < Ls) dbias_acc += dd;
         }
@@ -871,6 +952,51 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         ws.dbiasp[bs * Dm + d] = dbias_acc;
     }
     if (p.dh0 && st_ok && seg == 0) p.dh0[(b * Dm + d) * Nst + s0 + n] = g;
+
+    if constexpr (CONV != 0) {
+        const int H = p.conv_width - 1;
+        // gnext: the pre-activation gradients of the segment's first block
+        if (row_ok && nsg > 1 && n < H) ws.dpre_head[bsd * kConvMaxWidth + n] = gnext;
+        if (seg == 0 && p.dconv_init && H > 0) {
+            // the initial window: the input gradients of a block before step 0
+            const float dv = conv_dx<KC>(cv, 0.0f, gnext);
+            if (row_ok && n >= 16 - H) p.dconv_init[(b * Dm + d) * H + (n - (16 - H))] = dv;
+        }
+        float wsum[kConvMaxWidth];
+#pragma unroll
+        for (int j = 0; j < kConvMaxWidth; j++) wsum[j] = row_sum16(dwl[j]);
+        const float bsum = row_sum16(dcb);
+        if (row_ok && n == 0) {
+#pragma unroll
+            for (int j = 0; j < kConvMaxWidth; j++) ws.dcwp[bsd * kConvMaxWidth + j] = wsum[j];
+            ws.dcbp[bsd] = bsum;
+        }
+    }
+}
+
+// The fused convolution across time segments: the input gradients of a
+// segment's last H steps, completed with the next segment's first
+// pre-activation gradients (the remaining leads, ascending, after the ones
+// inside the segment -- the order one pass would take).  Thread per
+// (batch, segment < nseg - 1, row, m < H).
+template <typename T>
+__global__ __launch_bounds__(256) void ss_bwd_conv_fixup_kernel(BwdParams p, Workspace ws) {
+    const int K = p.conv_width, H = K - 1, nsg = ws.nseg;
+    const int64_t Dm = p.dim;
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= p.batch * int64_t(nsg - 1) * Dm * H) return;
+    const int m = int(i % H);
+    const int64_t d = (i / H) % Dm;
+    const int64_t bs = i / (int64_t(H) * Dm);
+    const int64_t b = bs / (nsg - 1);
+    const int seg = int(bs % (nsg - 1));
+    const int64_t tend = int64_t(seg + 1) * ws.seg_len;
+    const size_t here = (size_t(b) * nsg + seg) * Dm + d, next = here + Dm;
+    float acc = ws.dx_tail[here * kConvMaxWidth + m];
+    for (int j = H - m; j < K; j++)
+        acc = __builtin_fmaf(p.conv_w[d * K + (K - 1 - j)], ws.dpre_head[next * kConvMaxWidth + (m + j - H)],
+                             acc);
+    static_cast<T *>(p.dx)[(b * Dm + d) * p.seqlen + tend - H + m] = from_f32<T>(acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -987,6 +1113,19 @@ __global__ __launch_bounds__(256) void ss_bwd_fold_kernel(BwdParams p, Workspace
         }
         if (p.dD) p.dD[dd] = sD;
         if (p.dbias) p.dbias[dd] = sb;
+    } else if (p.conv_width > 0 && i < nbc + na + Dm + Dm * p.conv_width) {
+        // the fused convolution's weight gradient (d, tap k = lag K - 1 - k),
+        // over (batch entry, segment) ascending
+        const int K = p.conv_width;
+        const int64_t k = i - nbc - na - Dm, dd = k / K, j = K - 1 - k % K;
+        float s = 0.0f;
+        for (int64_t bs = 0; bs < Bt * ws.nseg; bs++) s += ws.dcwp[(bs * Dm + dd) * kConvMaxWidth + j];
+        p.dconv_w[k] = s;
+    } else if (p.conv_width > 0 && i < nbc + na + 2 * Dm + Dm * p.conv_width) {
+        const int64_t dd = i - nbc - na - Dm - Dm * p.conv_width;
+        float s = 0.0f;
+        for (int64_t bs = 0; bs < Bt * ws.nseg; bs++) s += ws.dcbp[bs * Dm + dd];
+        if (p.dconv_b) p.dconv_b[dd] = s;
     }
 }
 
@@ -1057,11 +1196,36 @@ int reverse_waves(const BwdParams &p, bool vec) {
     return scan_waves(p.batch * nseg, p.dim);
 }
 
-template <typename T, int VEC, bool YP, int NW, bool PART = false>
+template <typename T, int VEC, bool YP, int NW, bool PART = false, int CONV = 0>
 void launch_reverse(const BwdParams &p, Workspace ws, hipStream_t stream) {
     const dim3 grid(unsigned((p.dim + 4 * NW - 1) / (4 * NW)), unsigned(p.batch),
                     unsigned(state_slices(p.nstate) * ws.nseg));
-    hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW, PART>), grid, dim3(64 * NW), 0, stream, p, ws);
+    hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW, PART, CONV>), grid, dim3(64 * NW), 0,
+                       stream, p, ws);
+}
+
+// one slice with the fused convolution (CONV: its width 4, or -1)
+template <typename T, int CONV>
+void launch_reverse_conv(const BwdParams &p, Workspace ws, bool vec, bool yp, int nw,
+                         hipStream_t stream) {
+    constexpr int kVec = 16 / sizeof(T);
+    if (vec && nw == 12) {
+        if (yp) launch_reverse<T, kVec, true, 12, false, CONV>(p, ws, stream);
+        else launch_reverse<T, kVec, false, 12, false, CONV>(p, ws, stream);
+    } else if (vec) {
+        if (yp) launch_reverse<T, kVec, true, 4, false, CONV>(p, ws, stream);
+        else launch_reverse<T, kVec, false, 4, false, CONV>(p, ws, stream);
+    } else {
+        if (yp) launch_reverse<T, 1, true, 4, false, CONV>(p, ws, stream);
+        else launch_reverse<T, 1, false, 4, false, CONV>(p, ws, stream);
+    }
+}
+
+template <typename T, int CONV>
+void launch_ckpt(const BwdParams &p, Workspace ws, bool vec, dim3 grid, hipStream_t stream) {
+    constexpr int kVec = 16 / sizeof(T);
+    if (vec) hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, kVec, CONV>), grid, dim3(kThreads), 0, stream, p, ws);
+    else hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1, CONV>), grid, dim3(kThreads), 0, stream, p, ws);
 }
 
 // Channel groups of the reverse pass for this call (and so dB / dC partials
@@ -1095,13 +1259,17 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
                 fp.nseg = ws.nseg;
                 fp.seg_len = ws.seg_len;
                 fp.summ = ws.fsumm;
+                fp.conv_width = p.conv_width;
+                fp.conv_silu = p.conv_silu;
+                fp.conv_w = p.conv_w;
+                fp.conv_b = p.conv_b;
+                fp.conv_init = p.conv_init;
                 const hipError_t e = launch_fwd_summaries(fp, sizeof(T) == 2, stream);
                 if (e != hipSuccess) return e;
             }
-            if (vec)
-                hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, kVec>), grid, dim3(kThreads), 0, stream, p, ws);
-            else
-                hipLaunchKernelGGL((ss_bwd_ckpt_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p, ws);
+            if (p.conv_width == 4) launch_ckpt<T, 4>(p, ws, vec, grid, stream);
+            else if (p.conv_width > 0) launch_ckpt<T, -1>(p, ws, vec, grid, stream);
+            else launch_ckpt<T, 0>(p, ws, vec, grid, stream);
             profile_mark(stream);
         }
         if (ws.nseg > 1) {   // the adjoint's segment summaries
@@ -1123,7 +1291,11 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         BwdParams q = p;
         q.D = nullptr;
         q.ypre = nullptr;
-        if (slices > 1) {
+        if (p.conv_width == 4) {
+            launch_reverse_conv<T, 4>(p, ws, vec, yp, nw, stream);
+        } else if (p.conv_width > 0) {
+            launch_reverse_conv<T, -1>(p, ws, vec, yp, nw, stream);
+        } else if (slices > 1) {
             if (vec && nw == 12) launch_reverse<T, kVec, false, 12, true>(q, ws, stream);
             else if (vec) launch_reverse<T, kVec, false, 4, true>(q, ws, stream);
             else launch_reverse<T, 1, false, 4, true>(q, ws, stream);
@@ -1140,6 +1312,12 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         profile_mark(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (p.conv_width > 1 && ws.nseg > 1) {   // the convolution across segment boundaries
+            const int64_t nfix = p.batch * int64_t(ws.nseg - 1) * p.dim * (p.conv_width - 1);
+            hipLaunchKernelGGL((ss_bwd_conv_fixup_kernel<T>), dim3(unsigned((nfix + 255) / 256)),
+                               dim3(256), 0, stream, p, ws);
+            profile_mark(stream);
+        }
         const int64_t E = p.batch * p.dim * p.seqlen;
         if (slices > 1 && E > 0) {
             if (p.seqlen % 4 == 0)
@@ -1152,7 +1330,8 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         }
     }
     const bool v4 = p.seqlen % 4 == 0;   // 16-byte partial loads
-    const int64_t total = p.batch * p.nstate * p.seqlen / (v4 ? 4 : 1) + p.dim * p.nstate + p.dim;
+    const int64_t total = p.batch * p.nstate * p.seqlen / (v4 ? 4 : 1) + p.dim * p.nstate + p.dim +
+                          (p.conv_width > 0 ? p.dim * (p.conv_width + 1) : 0);
     if (total == 0 && !(p.batch > 0 && p.dim > 0)) return hipSuccess;   // nothing was enqueued
     if (total > 0) {
         const dim3 fgrid(unsigned((total + 255) / 256));

@@ -45,6 +45,7 @@
 //     adds the slices in ascending order, adds D u and applies the gate.
 #include <type_traits>
 
+#include "ss_conv_lane.h"
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_tiles.h"
@@ -90,71 +91,6 @@ __device__ __forceinline__ void scan_step_acc(float dl, float dlu, float a2, flo
     const float abar = exp2_hw(row_bcast<J>(dl) * a2);
     h = __builtin_fmaf(abar, h, row_bcast<J>(dlu) * b);
     v = __builtin_fmaf(c, h, v);
-}
-
-// ---------------------------------------------------------------------------
-// The causal convolution in front of the scan (fused forward).  The lane
-// that owns element t of its row (step n of a 16-step block) forms
-//   u_t = act(bias + sum_k w[k] x_{t-H+k}),   H = K - 1,
-// the taps added in ascending k as the convolution kernel adds them, and
-// rounds u to the io type as that kernel stores it, so the fused forward and
-// the convolution kernel followed by the scan give the same bits.  The
-// inputs at lags 1..3 come from lanes n - 1 .. n - 3 of the same DPP row,
-// or of the previous block for the first lanes.
-struct ConvLane {
-    float wl[kConvMaxWidth];   // weight of lag j (tap K - 1 - j); zero past K
-    float b;
-    int K;
-    bool silu;
-};
-
-__device__ __forceinline__ ConvLane conv_lane(const FwdParams &p, int64_t d, bool row_ok) {
-    ConvLane c;
-    c.K = p.conv_width;
-    c.silu = p.conv_silu != 0;
-    c.b = (row_ok && p.conv_b) ? p.conv_b[d] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < kConvMaxWidth; j++)
-        c.wl[j] = (row_ok && j < c.K) ? p.conv_w[d * c.K + (c.K - 1 - j)] : 0.0f;
-    return c;
-}
-
-// lane n of a DPP row: `cur` of lane n - J when n >= J, else `prev` of lane
-// n + 16 - J (a rotate of prev, then a shift of cur whose out-of-row source
-// lanes keep the rotated value)
-template <int J>
-__device__ __forceinline__ float lagged(float cur, float prev) {
-    // a rotate never leaves the row, so it needs no old value
-    const int o = __builtin_amdgcn_mov_dpp(__float_as_int(prev), 0x120 + J, 0xf, 0xf, false);
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(o, __float_as_int(cur), 0x110 + J, 0xf, 0xf, false));
-}
-
-// u of the lane's element: x its input, prev the lane's input one block
-// (16 steps) earlier.  KC: the width when fixed at compile time (4, the
-// Mamba block's), else 0 and c.K is read at run time.
-template <typename T, int KC>
-__device__ __forceinline__ float conv_u(const ConvLane &c, float x, float prev) {
-    const int K = KC > 0 ? KC : c.K;
-    float acc = c.b;
-    if (K == 4) acc = __builtin_fmaf(c.wl[3], lagged<3>(x, prev), acc);
-    if (K >= 3) acc = __builtin_fmaf(c.wl[2], lagged<2>(x, prev), acc);
-    if (K >= 2) acc = __builtin_fmaf(c.wl[1], lagged<1>(x, prev), acc);
-    acc = __builtin_fmaf(c.wl[0], x, acc);
-    const float u = c.silu ? acc * sigmoid_f32(acc) : acc;
-    return to_f32<T>(from_f32<T>(u));
-}
-
-// The input the lane would hold one block before step t0: x of its row at
-// t0 - 16 + n, the initial window for the H steps before 0, else zero.
-template <typename T>
-__device__ __forceinline__ float conv_prev(const FwdParams &p, int64_t b, int64_t d, bool row_ok,
-                                           int64_t t0, int n) {
-    const int64_t t = t0 - 16 + n;
-    const int H = p.conv_width - 1;
-    if (!row_ok || t < -H) return 0.0f;
-    if (t >= 0) return to_f32<T>(ld_global(static_cast<const T *>(p.u) + (b * p.dim + d) * p.seqlen + t));
-    return p.conv_init ? p.conv_init[(b * p.dim + d) * H + (t + H)] : 0.0f;
 }
 
 // Where segment j's summary (end state from zero, then total decay) of
@@ -717,8 +653,17 @@ size_t fwd_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int nstat
 
 hipError_t launch_fwd_summaries(const FwdParams &p, bool bf16, hipStream_t stream) {
     if (p.batch == 0 || p.dim == 0 || p.nseg < 2) return hipSuccess;
-    if (bf16) launch_summaries<bf16_t>(p, (p.seqlen * 2) % 16 == 0, stream);
-    else launch_summaries<float>(p, (p.seqlen * 4) % 16 == 0, stream);
+    const bool vec = (p.seqlen * (bf16 ? 2 : 4)) % 16 == 0;
+    if (p.conv_width == 4) {
+        if (bf16) launch_summaries<bf16_t, 4>(p, vec, stream);
+        else launch_summaries<float, 4>(p, vec, stream);
+    } else if (p.conv_width > 0) {
+        if (bf16) launch_summaries<bf16_t, -1>(p, vec, stream);
+        else launch_summaries<float, -1>(p, vec, stream);
+    } else {
+        if (bf16) launch_summaries<bf16_t>(p, vec, stream);
+        else launch_summaries<float>(p, vec, stream);
+    }
     return hipGetLastError();
 }
 

@@ -128,6 +128,21 @@ struct BwdParams : ScanParams {
     const float *ypre;  // pre-gate output saved by the forward with ckpt, or nullptr
     void *workspace;
     int tight_ws;       // workspace sized for this call (bwd_noalloc_bytes), not ss_bwd's
+    // The causal convolution fused in front of the scan (conv_width > 0, one
+    // 16-state slice): u holds the convolution's input x and is recomputed
+    // as the forward formed it; du is not written -- dx (io type, like x),
+    // dconv_w (dim, width), dconv_b (dim, or nullptr) and dconv_init
+    // (batch, dim, width - 1, or nullptr) receive the convolution's
+    // gradients.
+    int conv_width = 0;
+    int conv_silu = 0;
+    const float *conv_w = nullptr;
+    const float *conv_b = nullptr;
+    const float *conv_init = nullptr;
+    void *dx = nullptr;
+    float *dconv_w = nullptr;
+    float *dconv_b = nullptr;
+    float *dconv_init = nullptr;
 };
 
 struct DecodeParams {

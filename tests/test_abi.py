@@ -33,7 +33,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = re.findall(r"^\w[\w\s\*]*?\b(ss_\w+)\s*\(", open(HEADER).read(), flags=re.M)
     assert set(names) >= {"ss_fwd", "ss_bwd", "ss_bwd_workspace_size", "ss_state_update",
-                          "ss_last_error", "ss_abi_version", "ss_fwd_conv"}
+                          "ss_last_error", "ss_abi_version", "ss_fwd_conv", "ss_bwd_conv"}
     for n in names:
         assert hasattr(lib, n), f"libss.so does not export {n}"
 
@@ -260,6 +260,32 @@ def _fwd_conv(lib, batch=2, dim=32, dstate=16, seqlen=64, io=0, x=FAKE, w=FAKE, 
 ])
 def test_fwd_conv_checks(lib, kw, status, word):
     assert _fwd_conv(lib, **kw) == status
+    assert word in _msg(lib)
+
+
+def _bwd_conv(lib, batch=2, dim=32, dstate=16, seqlen=64, io=0, x=FAKE, w=FAKE, width=4,
+              cb=None, dx=FAKE2, dw=FAKE, dcb=None):
+    lib.ss_bwd_conv.argtypes = ([ctypes.c_int64] * 4 + [ctypes.c_int] + [ctypes.c_void_p] * 2
+                                + [ctypes.c_int64] + [ctypes.c_void_p] + [ctypes.c_int]
+                                + [ctypes.c_void_p] * 8 + [ctypes.c_int] + [ctypes.c_void_p] * 17
+                                + [ctypes.c_size_t, ctypes.c_void_p])
+    # x, weight, width, bias, silu, init, delta, A, B, C, D, z, delta_bias, softplus, h0,
+    # dout, dlast, dx, dweight, dbias, dinit, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+    # ckpt, workspace
+    return lib.ss_bwd_conv(batch, dim, dstate, seqlen, io, x, w, width, cb, 1, None, FAKE, FAKE,
+                           FAKE, FAKE, None, None, None, 1, None, FAKE, None, dx, dw, dcb, None,
+                           FAKE, FAKE, FAKE, FAKE, None, None, None, None, None, FAKE, 1 << 40,
+                           None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(width=5), EUNSUP, "width"), (dict(dstate=17), EUNSUP, "16 states"),
+    (dict(dx=None), EINVAL, "dx"), (dict(dw=None), EINVAL, "dconv_weight"),
+    (dict(w=None), EINVAL, "conv_weight"), (dict(x=None), EINVAL, "x"),
+    (dict(dcb=FAKE), EINVAL, "dconv_bias"), (dict(dx=FAKE), EINVAL, "overlap x"),
+])
+def test_bwd_conv_checks(lib, kw, status, word):
+    assert _bwd_conv(lib, **kw) == status
     assert word in _msg(lib)
 
 

@@ -177,3 +177,113 @@ def test_fused_conv_scan_zero_length_and_empty():
     assert torch.equal(last, h0)
     # seqlen 0: the final window is the initial one
     assert torch.equal(fin, to_dev(ch))
+
+
+BWD_CASES = [
+    # batch, dim, dstate, L, io, width, silu, bias, init
+    (2, 40, 16, 100, "f32", 4, True, True, True),
+    (1, 17, 16, 33, "f32", 4, True, False, False),     # scalar path, ragged channels
+    (2, 24, 16, 96, "bf16", 4, True, True, True),
+    (2, 40, 16, 136, "bf16", 3, True, True, False),     # ragged dim and tail
+    (2, 24, 16, 70, "bf16", 2, False, True, True),      # scalar path, no SiLU
+    (2, 32, 16, 64, "f32", 1, True, True, False),       # width 1
+    (2, 20, 5, 64, "f32", 4, True, True, True),         # fewer than 16 states
+    (8, 1544, 16, 64, "f32", 4, True, True, True),      # 48-channel reverse workgroups
+    (2, 64, 16, 8192, "bf16", 4, True, True, True),     # time segments (boundary fix-up)
+    (1, 40, 16, 9001, "f32", 3, True, True, True),      # time segments, scalar path
+]
+
+SCAN_KEYS = ("ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias", "dh0")
+
+
+@pytest.mark.parametrize("batch,dim,N,L,io,width,silu,bias,init", BWD_CASES)
+def test_fused_conv_scan_backward(batch, dim, N, L, io, width, silu, bias, init):
+    """ss_bwd_conv against the oracle chain (f64 convolution, its output
+    stored in the io dtype, f64 scan and its backward, f64 convolution
+    backward of the scan's du), and its scan gradients bit-equal to ss_bwd
+    on the convolution kernel's u -- with and without the forward's saved
+    record."""
+    require_gpu()
+    w = ssin.custom("bwd", batch, dim, N, L, io, seed=5 * dim + N + L + width)
+    arr = ssin.make(w)
+    say(f"fused conv bwd {w.name} width {width} silu {silu}")
+    d = dev_inputs(arr)
+    cw, cb, ch = conv_params(dim, width, batch, seed=2 * L + width, bias=bias, init=init)
+    cw_d, cb_d, ch_d = to_dev(cw), to_dev(cb), to_dev(ch)
+    rng = np.random.default_rng(L + width)
+    h0 = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    dl = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    h0_d, dl_d = to_dev(h0), to_dev(dl)
+    x = d["u"]
+    u = binding.ss_conv1d_fwd(x, cw_d, cb_d, silu, ch_d)
+    ck = binding.ss_ckpt_empty(x, dstate=N)
+    binding.ss_fwd_conv(x, cw_d, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                        d["delta_bias"], True, conv_bias=cb_d, conv_silu=silu, conv_init=ch_d,
+                        h0=h0_d, ckpt=ck)
+    runs = {}
+    for saved in (False, True):
+        runs[saved] = binding.ss_bwd_conv(
+            x, cw_d, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["delta_bias"], True,
+            d["dout"], conv_bias=cb_d, conv_silu=silu, conv_init=ch_d, h0=h0_d, dlast=dl_d,
+            want_dconv_init=True, ckpt=ck if saved else None)
+        ref = binding.ss_bwd(u, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                             d["delta_bias"], True, d["dout"], h0=h0_d, dlast=dl_d,
+                             ckpt=ck if saved else None)
+        torch.cuda.synchronize()
+        for k in SCAN_KEYS:
+            if k in ref:
+                assert torch.equal(bits(runs[saved][k]), bits(ref[k])), f"{k} saved={saved}"
+    for k in runs[False]:
+        assert torch.equal(bits(runs[False][k]), bits(runs[True][k])), f"{k} with saved record"
+    g = runs[False]
+    # the oracle chain
+    x64 = {k: widen(v) for k, v in arr.items()}
+    u64, _ = oracle.conv_fwd(x64["u"], cw.astype(np.float64),
+                             None if cb is None else cb.astype(np.float64), silu,
+                             None if ch is None else ch.astype(np.float64),
+                             threads=ORACLE_THREADS)
+    rs = oracle.bwd(as_io(u64, io), x64["delta"], x64["A"], x64["B"], x64["C"], x64["D"],
+                    x64["z"], x64["delta_bias"], True, x64["dout"], h0.astype(np.float64),
+                    dl.astype(np.float64), threads=ORACLE_THREADS)
+    win = ch if ch is not None else np.zeros((batch, dim, width - 1), np.float32)
+    rc = oracle.conv_bwd(x64["u"], cw.astype(np.float64),
+                         None if cb is None else cb.astype(np.float64), silu,
+                         win.astype(np.float64), rs["du"], threads=ORACLE_THREADS)
+    checks = [("dx", rc["dx"], TOL[io]), ("dconv_weight", rc["dweight"], TOL["f32"]),
+              ("dconv_init", rc["dinit_state"], TOL["f32"])]
+    if cb is not None:
+        checks.append(("dconv_bias", rc["dbias"], TOL["f32"]))
+    for k in SCAN_KEYS:
+        if k in rs and k in g:
+            checks.append((k, rs[k], TOL["f32"] if k in ("dA", "dD", "ddelta_bias", "dh0")
+                           else TOL[io]))
+    for k, r, tol in checks:
+        e = assert_close(to_host(g[k]), r, tol, f"{k} vs oracle chain")
+        say(f"  {k} err {e:.3e}")
+
+
+def test_fused_conv_scan_backward_rows_do_not_depend_on_batch():
+    """Per-entry gradients (dx, ddelta, dz, dB, dC, the initial window's) of
+    a batch entry run alone equal the same entry inside the batch, with time
+    segments, and two calls give the same bits."""
+    require_gpu()
+    w = ssin.custom("bwd", 3, 64, 16, 8192, "bf16", seed=79)
+    d = dev_inputs(ssin.make(w))
+    cw, cb, ch = conv_params(64, 4, 3, seed=9)
+    cw_d, cb_d, ch_d = to_dev(cw), to_dev(cb), to_dev(ch)
+
+    def run(dd, init):
+        return binding.ss_bwd_conv(dd["u"], cw_d, dd["delta"], dd["A"], dd["B"], dd["C"],
+                                   dd["D"], dd["z"], dd["delta_bias"], True, dd["dout"],
+                                   conv_bias=cb_d, conv_init=init)
+    g1, g2 = run(d, ch_d), run(d, ch_d)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(bits(g1[k]), bits(g2[k])), f"{k} not deterministic"
+    per_entry = ("u", "delta", "B", "C", "z", "dout")
+    for bi in (0, 2):
+        one = {k: (v[bi:bi + 1].contiguous() if k in per_entry else v) for k, v in d.items()}
+        ga = run(one, ch_d[bi:bi + 1].contiguous())
+        torch.cuda.synchronize()
+        for k in ("dx", "ddelta", "dz", "dB", "dC", "dconv_init"):
+            assert torch.equal(bits(ga[k]), bits(g1[k][bi:bi + 1])), f"{k} entry {bi}"
