@@ -92,10 +92,11 @@ const char *ss_last_error(void);
  * Bytes of what ss_fwd can save for ss_bwd (its "ckpt" buffer), all f32:
  * the state entering every 16-step block, per slice of 16 states,
  * (ceil(dstate / 16), batch, dim, ceil(seqlen / 16), 16) -- 16 entries per
- * slice, the unused ones zero.  With dstate <= 16 it is followed, at the
+ * slice, the unused ones zero.  With dstate <= 64 it is followed, at the
  * next 256-byte boundary, by the pre-gate output sum_n C h + D u, (batch,
- * dim, seqlen), which is written when z is given.  0 for empty or
- * unsupported shapes.
+ * dim, seqlen), which is written when z is given (ss_bwd's dz reads it
+ * instead of adding up per-slice parts).  0 for empty or unsupported
+ * shapes.
  */
 size_t ss_ckpt_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen);
 
@@ -117,7 +118,7 @@ size_t ss_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
  * Forward scan.  Writes out (batch, dim, seqlen) and, when last_state is
  * non-NULL, the final state h_{seqlen-1} (h0 when seqlen == 0).  When ckpt
  * is non-NULL (ss_ckpt_size() bytes, 16-byte aligned) it also saves the
- * block states (and, for dstate <= 16, the pre-gate output), which a later
+ * block states (and, for dstate <= 64, the pre-gate output), which a later
  * ss_bwd with the same inputs takes instead of recomputing them (the usual
  * save-for-backward of a training step).
  *   dstate            1..256 (SS_EUNSUPPORTED above; the mamba-rs README,

@@ -258,8 +258,8 @@ ss_status fwd_impl(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
     p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
     p.bias = delta_bias; p.softplus = delta_softplus != 0; p.h0 = h0;
     p.out = out; p.last_state = last_state; p.ckpt = ckpt;
-    p.ypre = (ckpt && ssk::state_slices(int(dstate)) == 1)
-                 ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
+    p.ypre = (ckpt && ssk::ckpt_has_ypre(int(dstate)))
+                 ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen, int(dstate)) : nullptr;
     p.ypart = static_cast<float *>(workspace);
     if (conv) {
         p.conv_width = conv->width;
@@ -349,8 +349,8 @@ ss_status bwd_params(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
     p->bias = delta_bias; p->softplus = delta_softplus != 0; p->h0 = h0;
     p->dout = dout; p->dlast = dlast; p->du = du; p->ddelta = ddelta; p->dA = dA; p->dB = dB;
     p->dC = dC; p->dD = dD; p->dz = dz; p->dbias = ddelta_bias; p->dh0 = dh0; p->ckpt = ckpt;
-    p->ypre = (ckpt && ssk::state_slices(int(dstate)) == 1)
-                  ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen) : nullptr;
+    p->ypre = (ckpt && ssk::ckpt_has_ypre(int(dstate)))
+                  ? ckpt + ssk::ckpt_ypre_offset(batch, dim, seqlen, int(dstate)) : nullptr;
     return SS_OK;
 }
 

@@ -97,6 +97,9 @@ struct Workspace {
     // gradients of a segment's first 4 steps and the partial input
     // gradients of its last 4 (completed across segments by a fix-up pass)
     float *dcwp, *dcbp, *dpre_head, *dx_tail;
+    // 2..kMaxLaneSlices slices without the forward's record: the pre-gate
+    // output the forward kernel writes for this call (batch, dim, L)
+    float *ypre_ws;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -144,11 +147,15 @@ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L, int ns
     w.dpre_head = take(bsd * kConvMaxWidth);
     w.dx_tail = take(bsd * kConvMaxWidth);
     w.dup = w.ddp = w.dzp = nullptr;
+    w.ypre_ws = nullptr;
     if (slices > 1) {
+        // up to kMaxLaneSlices slices dz comes whole from the pre-gate output
+        // (the caller's record, or one built here); above, from partials
         const size_t e = size_t(slices) * batch * dim * L;
         w.dup = take(e);
         w.ddp = take(e);
-        w.dzp = take(e);
+        if (slices > kMaxLaneSlices) w.dzp = take(e);
+        else if (with_ckpt) w.ypre_ws = take(size_t(batch) * dim * L);
     }
     if (total) *total = off;
     return w;
@@ -516,7 +523,6 @@ template <typename T, int VEC, bool YP, int NW, bool PART, int CONV = 0>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 3)) : 1) void ss_bwd_reverse_kernel(BwdParams p, Workspace ws) {
     using SM = RevSmem<T, NW>;
     using OutT = std::conditional_t<PART, float, T>;
-    static_assert(!(PART && YP), "slices recompute their share of the pre-gate output");
     static_assert(!(PART && CONV), "the fused convolution runs with one slice");
     constexpr int KC = CONV > 0 ? CONV : 0;
     // grid z: (slice, time segment)
@@ -609,6 +615,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     OutT *dz_b = has_z ? (PART ? reinterpret_cast<OutT *>(ws.dzp + slice_el) : static_cast<OutT *>(p.dz)) + wavebase
                        : nullptr;
     OutT *dx_b = CONV != 0 ? static_cast<OutT *>(p.dx) + wavebase : nullptr;
+    // slices with the saved pre-gate output: dz is whole, written by slice 0
+    T *dz_whole = (PART && YP && has_z && slice == 0) ? static_cast<T *>(p.dz) + wavebase : nullptr;
     const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
     auto elem_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(T)); };
     auto out_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(OutT)); };
@@ -793,9 +801,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             if (has_z) {
                 const float sz = sigmoid_f32(zz[s]);
                 dyv[s] = dout[s] * zz[s] * sz;
-                if (YP && row_ok && t0 + col < Ls)
-                    st_global(at_bytes(dz_b, out_off(t0 + col)),
-                              from_f32<OutT>(dout[s] * ypn[s] * sz * (1.0f + zz[s] * (1.0f - sz))));
+                if (YP && row_ok && t0 + col < Ls) {
+                    const float dzv = dout[s] * ypn[s] * sz * (1.0f + zz[s] * (1.0f - sz));
+                    if constexpr (PART) {
+                        if (dz_whole) st_global(at_bytes(dz_whole, elem_off(t0 + col)), from_f32<T>(dzv));
+                    } else {
+                        st_global(at_bytes(dz_b, out_off(t0 + col)), from_f32<OutT>(dzv));
+                    }
+                }
             }
             if (!row_ok) dyv[s] = 0.0f;
         }
@@ -1148,8 +1161,10 @@ __device__ __forceinline__ void sum_slices(const float *src, int64_t E, int slic
     }
 }
 
+// dz_parts: dz comes from per-slice partials (else it is already whole)
 template <typename T, int V>
-__global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Workspace ws, int slices) {
+__global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Workspace ws, int slices,
+                                                             int dz_parts) {
     const int64_t E = p.batch * p.dim * p.seqlen;
     const int64_t e0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * V;
     if (e0 >= E) return;
@@ -1158,7 +1173,8 @@ __global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Worksp
     float du[V], dd[V], dz[V];
     sum_slices<V>(ws.dup + e0, E, slices, du);
     sum_slices<V>(ws.ddp + e0, E, slices, dd);
-    if (p.z) sum_slices<V>(ws.dzp + e0, E, slices, dz);
+    const bool do_dz = p.z && dz_parts;
+    if (do_dz) sum_slices<V>(ws.dzp + e0, E, slices, dz);
     auto ldv = [&](const void *src, float (&v)[V]) {
         if constexpr (V == 4) ld4<T>(static_cast<const T *>(src) + e0, v);
         else v[0] = to_f32<T>(ld_global(static_cast<const T *>(src) + e0));
@@ -1177,11 +1193,11 @@ __global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Worksp
         if (p.z) {
             const float sz = sigmoid_f32(z[i]);
             dy[i] = g[i] * z[i] * sz;
-            dz[i] += g[i] * (dskip * u[i]) * sz * (1.0f + z[i] * (1.0f - sz));
+            if (do_dz) dz[i] += g[i] * (dskip * u[i]) * sz * (1.0f + z[i] * (1.0f - sz));
         }
         du[i] += dskip * dy[i];
     }
-    if (p.z) stv(p.dz, dz);
+    if (do_dz) stv(p.dz, dz);
     stv(p.du, du);
     stv(p.ddelta, dd);
 }
@@ -1244,15 +1260,31 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
                        : carve(p.workspace, p.batch, p.dim, p.seqlen, p.nstate,
                                (p.dim + kRows - 1) / kRows, true, nullptr);
     const int slices = state_slices(p.nstate);
+    // 2..kMaxLaneSlices slices: the reverse pass takes dz whole from the
+    // pre-gate output, the caller's record or one the forward kernel builds
+    const bool lane_slices = slices > 1 && slices <= kMaxLaneSlices;
     if (p.ckpt) {  // saved by the forward: read only
         ws.ckpt = const_cast<float *>(p.ckpt);
-        ws.ypre = slices == 1 ? p.ypre : nullptr;
+        ws.ypre = slices <= kMaxLaneSlices ? p.ypre : nullptr;
     }
     if (p.batch > 0 && p.dim > 0) {
         dim3 grid(unsigned((p.dim + kRows - 1) / kRows), unsigned(p.batch), unsigned(slices * ws.nseg));
         constexpr int kVec = 16 / sizeof(T);
         const bool vec = (p.seqlen * int64_t(sizeof(T))) % 16 == 0;
-        if (!p.ckpt) {
+        if (!p.ckpt && lane_slices) {
+            // the record from the forward kernel (a row's slices in the lane):
+            // block states and, with z, the pre-gate output; no out
+            FwdParams fp{};
+            static_cast<ScanParams &>(fp) = p;
+            fp.out = nullptr;
+            fp.last_state = nullptr;
+            fp.ckpt = ws.ckpt;
+            fp.ypre = p.z ? ws.ypre_ws : nullptr;
+            fp.ypart = ws.fsumm;   // room for its time segments' summaries
+            const hipError_t e = launch_fwd(fp, sizeof(T) == 2, stream);
+            if (e != hipSuccess) return e;
+            ws.ypre = fp.ypre;
+        } else if (!p.ckpt) {
             if (ws.nseg > 1) {   // the forward's segment summaries, then the states
                 FwdParams fp{};
                 static_cast<ScanParams &>(fp) = p;
@@ -1283,7 +1315,7 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
                                    stream, p, ws);
             profile_mark(stream);
         }
-        const bool yp = slices == 1 && p.ckpt && p.ypre && p.z;
+        const bool yp = p.z && ws.ypre && (slices == 1 ? p.ckpt != nullptr : lane_slices);
         const int nw = reverse_waves(p, vec);
         ws.groups = (p.dim + 4 * nw - 1) / (4 * nw);   // the partials the fold reads
         ws.sub = nw == 12 ? 1 : 3;
@@ -1295,6 +1327,10 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
             launch_reverse_conv<T, 4>(p, ws, vec, yp, nw, stream);
         } else if (p.conv_width > 0) {
             launch_reverse_conv<T, -1>(p, ws, vec, yp, nw, stream);
+        } else if (slices > 1 && yp) {
+            if (vec && nw == 12) launch_reverse<T, kVec, true, 12, true>(q, ws, stream);
+            else if (vec) launch_reverse<T, kVec, true, 4, true>(q, ws, stream);
+            else launch_reverse<T, 1, true, 4, true>(q, ws, stream);
         } else if (slices > 1) {
             if (vec && nw == 12) launch_reverse<T, kVec, false, 12, true>(q, ws, stream);
             else if (vec) launch_reverse<T, kVec, false, 4, true>(q, ws, stream);
@@ -1322,10 +1358,10 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
         if (slices > 1 && E > 0) {
             if (p.seqlen % 4 == 0)
                 hipLaunchKernelGGL((ss_bwd_combine_kernel<T, 4>), dim3(unsigned((E / 4 + 255) / 256)),
-                                   dim3(256), 0, stream, p, ws, slices);
+                                   dim3(256), 0, stream, p, ws, slices, int(!yp));
             else
                 hipLaunchKernelGGL((ss_bwd_combine_kernel<T, 1>), dim3(unsigned((E + 255) / 256)),
-                                   dim3(256), 0, stream, p, ws, slices);
+                                   dim3(256), 0, stream, p, ws, slices, int(!yp));
             profile_mark(stream);
         }
     }

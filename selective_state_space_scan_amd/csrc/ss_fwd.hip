@@ -487,7 +487,8 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
             // a row's 16 lanes store 16 consecutive outputs
             const int t = t0 + 16 * s + n;
             if (row_ok && t < Ls) {
-                st_global(at_bytes(yb, uint32_t(rowel + t) * uint32_t(sizeof(OutT))), from_f32<OutT>(y));
+                // (no out: the backward builds its record with this kernel)
+                if (p.out) st_global(at_bytes(yb, uint32_t(rowel + t) * uint32_t(sizeof(OutT))), from_f32<OutT>(y));
                 if (save_yp) st_global(at_bytes(ypb, uint32_t(rowel + t) * 4u), ypre);
             }
         }
@@ -606,7 +607,6 @@ hipError_t launch_typed(const FwdParams &p0, hipStream_t stream) {
         p.summ = static_cast<float *>(p.ypart) + (part + 63) / 64 * 64;
     }
     if (slices <= kMaxLaneSlices) {
-        if (slices > 1) p.ypre = nullptr;   // saved only with one slice
         // the fused convolution: width 4 (the Mamba block's) fixed at compile
         // time, other widths read at run time
         if (p.conv_width == 4) launch_lane_slices<T, 4>(p, vec, stream);

@@ -42,25 +42,31 @@ struct ScanParams {
 
 // What the forward saves for the backward (one f32 buffer, ss_ckpt_size()
 // bytes): the state entering every 16-step block, (slice, batch, dim,
-// ceil(L / 16), 16), then -- with one slice only, at the next 256-byte
-// boundary -- the pre-gate output (batch, dim, L), written when z is given
-// (the backward's dz reads it; with several slices the backward adds dz up
-// from per-slice partials instead).
+// ceil(L / 16), 16), then -- up to kMaxLaneSlices slices (where the forward
+// forms the whole output in the lane), at the next 256-byte boundary -- the
+// pre-gate output (batch, dim, L), written when z is given (the backward's
+// dz reads it; above that the backward adds dz up from per-slice partials).
 constexpr int kCkptSpacing = 16;
 
 // block states of one slice, in floats
 __host__ __device__ inline size_t ckpt_state_floats(int64_t batch, int64_t dim, int64_t seqlen) {
     return size_t(batch) * size_t(dim) * size_t((seqlen + kCkptSpacing - 1) / kCkptSpacing) * 16;
 }
-__host__ __device__ inline size_t ckpt_ypre_offset(int64_t batch, int64_t dim, int64_t seqlen) {
-    return (ckpt_state_floats(batch, dim, seqlen) + 63) / 64 * 64;  // floats
+// where the pre-gate output starts, in floats (up to kMaxLaneSlices slices)
+__host__ __device__ inline size_t ckpt_ypre_offset(int64_t batch, int64_t dim, int64_t seqlen,
+                                                   int nstate) {
+    return (ckpt_state_floats(batch, dim, seqlen) * state_slices(nstate) + 63) / 64 * 64;
+}
+__host__ __device__ inline bool ckpt_has_ypre(int nstate) {
+    return state_slices(nstate) <= kMaxLaneSlices;
 }
 __host__ __device__ inline size_t ckpt_bytes(int64_t batch, int64_t dim, int64_t seqlen,
                                              int nstate) {
     if (batch <= 0 || dim <= 0 || seqlen <= 0) return 0;
     const int ns = state_slices(nstate);
-    if (ns > 1) return ckpt_state_floats(batch, dim, seqlen) * ns * sizeof(float);
-    return (ckpt_ypre_offset(batch, dim, seqlen) + size_t(batch) * size_t(dim) * size_t(seqlen)) *
+    if (!ckpt_has_ypre(nstate)) return ckpt_state_floats(batch, dim, seqlen) * ns * sizeof(float);
+    return (ckpt_ypre_offset(batch, dim, seqlen, nstate) +
+            size_t(batch) * size_t(dim) * size_t(seqlen)) *
            sizeof(float);
 }
 

@@ -52,8 +52,11 @@ def test_ckpt_size(lib):
     assert lib.ss_ckpt_size(2, 32, 16, 0) == 0
     # the block states are 16 wide for any dstate up to 16
     assert lib.ss_ckpt_size(2, 32, 8, 64) == lib.ss_ckpt_size(2, 32, 16, 64)
-    # above 16: 16 states per slice, no saved pre-gate output
-    assert lib.ss_ckpt_size(2, 32, 17, 64) == 2 * 2 * 32 * 4 * 16 * 4
+    # above 16: 16 states per slice; up to 64 states (slices in the lane)
+    # still the pre-gate output after them, above 64 none
+    assert lib.ss_ckpt_size(2, 32, 17, 64) == 2 * 2 * 32 * 4 * 16 * 4 + 2 * 32 * 64 * 4
+    assert lib.ss_ckpt_size(2, 32, 64, 64) == 4 * 2 * 32 * 4 * 16 * 4 + 2 * 32 * 64 * 4
+    assert lib.ss_ckpt_size(2, 32, 65, 64) == 5 * 2 * 32 * 4 * 16 * 4
     assert lib.ss_ckpt_size(2, 32, 256, 64) == 16 * 2 * 32 * 4 * 16 * 4
     assert lib.ss_ckpt_size(2, 32, 257, 64) == 0
 
