@@ -116,8 +116,8 @@ def conv_algorithmic_bytes(kernel, batch, dim, L, width, esize):
 
 # The sources each profiled kernel is built from: a committed summary counts
 # only while their hash is the one it was measured with.
-_FWD_SRC = ["ss_fwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"]
-_BWD_SRC = ["ss_bwd.hip", "ss_tiles.h", "ss_device.h", "ss_kernels.h"]
+_FWD_SRC = ["ss_fwd.hip", "ss_conv_lane.h", "ss_tiles.h", "ss_device.h", "ss_kernels.h"]
+_BWD_SRC = ["ss_bwd.hip", "ss_conv_lane.h", "ss_tiles.h", "ss_device.h", "ss_kernels.h"]
 KERNEL_SOURCES = {
     "ss_fwd_kernel": _FWD_SRC,
     "ss_fwd_summary_kernel": _FWD_SRC,
