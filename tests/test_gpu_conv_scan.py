@@ -287,3 +287,20 @@ def test_fused_conv_scan_backward_rows_do_not_depend_on_batch():
         torch.cuda.synchronize()
         for k in ("dx", "ddelta", "dz", "dB", "dC", "dconv_init"):
             assert torch.equal(bits(ga[k]), bits(g1[k][bi:bi + 1])), f"{k} entry {bi}"
+
+
+def test_fused_conv_scan_backward_zero_length():
+    """seqlen 0: dlast passes through to dh0, the initial window and the
+    parameter gradients are zero."""
+    require_gpu()
+    w = ssin.custom("bwd", 2, 32, 16, 0, "f32", seed=3)
+    d = dev_inputs(ssin.make(w))
+    cw, cb, ch = conv_params(32, 4, 2, seed=2)
+    dl = torch.randn(2, 32, 16, device=DEV)
+    g = binding.ss_bwd_conv(d["u"], to_dev(cw), d["delta"], d["A"], d["B"], d["C"], d["D"],
+                            d["z"], d["delta_bias"], True, d["dout"], conv_bias=to_dev(cb),
+                            conv_init=to_dev(ch), dlast=dl, want_dh0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dl)
+    for k in ("dconv_weight", "dconv_bias", "dconv_init", "dA", "dD", "ddelta_bias"):
+        assert torch.count_nonzero(g[k]).item() == 0, k
