@@ -16,6 +16,10 @@ namespace ssk {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -35,40 +39,55 @@ __device__ __forceinline__ short lo_bf(float v, short hi) {
     return bfs(v - bf16_to_f32(static_cast<bf16_t>(hi)));
 }
 
+// Two values rounded to nearest-even bf16 by one instruction
+// (v_cvt_pk_bf16_f32), a in the low half: the same bits as two bfs calls.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const bf16x2_t r = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// The hi / lo split of two values, each half packed as pk_bf16 packs it.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pk_bf16(a, b);
+    lo = pk_bf16(a - bf_lo(hi), b - bf_hi(hi));
+}
+
+__device__ __forceinline__ s16x4 s16x4_of(uint32_t w0, uint32_t w1) {
+    return __builtin_bit_cast(s16x4, (u32x2_t){w0, w1});
+}
+__device__ __forceinline__ bf16x8_t bf16x8_of(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    return __builtin_bit_cast(bf16x8_t, (u32x4_t){w0, w1, w2, w3});
+}
+
 // the four values of a result tile as bf16 high and low parts
 __device__ __forceinline__ void split4(const f32x4 &v, s16x4 &hi, s16x4 &lo) {
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const short h = bfs(v[r]);
-        hi[r] = h;
-        lo[r] = lo_bf(v[r], h);
-    }
+    uint32_t h0, l0, h1, l1;
+    split2(v[0], v[1], h0, l0);
+    split2(v[2], v[3], h1, l1);
+    hi = s16x4_of(h0, h1);
+    lo = s16x4_of(l0, l1);
 }
 
 // three bf16 parts, v = hi + mid + lo to about 2^-27 relative
 __device__ __forceinline__ void split4x3(const f32x4 &v, s16x4 &hi, s16x4 &mid, s16x4 &lo) {
+    uint32_t h[2], m[2], l[2];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const short h = bfs(v[r]);
-        const float r1 = v[r] - bf16_to_f32(static_cast<bf16_t>(h));
-        const short m = bfs(r1);
-        hi[r] = h;
-        mid[r] = m;
-        lo[r] = bfs(r1 - bf16_to_f32(static_cast<bf16_t>(m)));
+    for (int k = 0; k < 2; k++) {
+        const float a = v[2 * k], b = v[2 * k + 1];
+        h[k] = pk_bf16(a, b);
+        const float ra = a - bf_lo(h[k]), rb = b - bf_hi(h[k]);
+        m[k] = pk_bf16(ra, rb);
+        l[k] = pk_bf16(ra - bf_lo(m[k]), rb - bf_hi(m[k]));
     }
+    hi = s16x4_of(h[0], h[1]);
+    mid = s16x4_of(m[0], m[1]);
+    lo = s16x4_of(l[0], l[1]);
 }
 
-// two 4-value halves as one 8-value operand (elements copied by value:
-// clang takes the bit cast of a vector element from element 0)
+// two 4-value halves as one 8-value operand (whole vectors: clang takes the
+// bit cast of a single vector element from element 0)
 __device__ __forceinline__ bf16x8_t cat8(const s16x4 &a, const s16x4 &b) {
-    bf16x8_t r;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const short x = a[e], y = b[e];
-        r[e] = __builtin_bit_cast(__bf16, x);
-        r[4 + e] = __builtin_bit_cast(__bf16, y);
-    }
-    return r;
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 constexpr f32x4 kZero4 = {0.0f, 0.0f, 0.0f, 0.0f};

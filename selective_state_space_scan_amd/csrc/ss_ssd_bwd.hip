@@ -385,15 +385,15 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
                     const u32x4 yr = *reinterpret_cast<const u32x4 *>(YT + (16 * q + li) * SM::kPT + 32 * k2 + 8 * lg);
                     const f32x4 e0 = *reinterpret_cast<const f32x4 *>(ecum + 32 * k2 + 8 * lg);
                     const f32x4 e1 = *reinterpret_cast<const f32x4 *>(ecum + 32 * k2 + 8 * lg + 4);
-                    bf16x8_t bh, bl;
+                    uint32_t hw[4], lw[4];
 #pragma unroll
-                    for (int e = 0; e < 8; e++) {
-                        const float ev = e < 4 ? e0[e] : e1[e - 4];
-                        const float v = ((e & 1) ? bf_hi(yr[e >> 1]) : bf_lo(yr[e >> 1])) * ev;
-                        const __bf16 hi = static_cast<__bf16>(v);
-                        bh[e] = hi;
-                        bl[e] = static_cast<__bf16>(v - static_cast<float>(hi));
+                    for (int e = 0; e < 4; e++) {
+                        const float ea = e < 2 ? e0[2 * e] : e1[2 * e - 4];
+                        const float eb = e < 2 ? e0[2 * e + 1] : e1[2 * e - 3];
+                        split2(bf_lo(yr[e]) * ea, bf_hi(yr[e]) * eb, hw[e], lw[e]);
                     }
+                    const bf16x8_t bh = bf16x8_of(hw[0], hw[1], hw[2], hw[3]);
+                    const bf16x8_t bl = bf16x8_of(lw[0], lw[1], lw[2], lw[3]);
                     acc = mfma32(a, bh, acc);
                     acc = mfma32(a, bl, acc);
                 }
@@ -412,14 +412,13 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
 #pragma unroll
             for (int k = 0; k < N / 32; k++) {
                 // dH^T[n = 32 k + 8 lg + e][p = 16 q + li]: a column of the [n][p] store
-                bf16x8_t hb, lb;
+                uint32_t hw[4], lw[4];
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const float v = Hf[(32 * k + 8 * lg + e) * SM::kPH + 16 * q + li];
-                    const __bf16 hi = static_cast<__bf16>(v);
-                    hb[e] = hi;
-                    lb[e] = static_cast<__bf16>(v - static_cast<float>(hi));
-                }
+                for (int e = 0; e < 4; e++)
+                    split2(Hf[(32 * k + 8 * lg + 2 * e) * SM::kPH + 16 * q + li],
+                           Hf[(32 * k + 8 * lg + 2 * e + 1) * SM::kPH + 16 * q + li], hw[e], lw[e]);
+                const bf16x8_t hb = bf16x8_of(hw[0], hw[1], hw[2], hw[3]);
+                const bf16x8_t lb = bf16x8_of(lw[0], lw[1], lw[2], lw[3]);
 #pragma unroll
                 for (int jj = 0; jj < 2; jj++) {
                     const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Bs + (16 * kT[jj] + li) * SM::kPB + 32 * k + 8 * lg);
@@ -586,7 +585,11 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             const int s0 = 16 * kT[jj] + 4 * lg;
             if (has_dx) {
 #pragma unroll
-                for (int r = 0; r < 4; r++) DX[(s0 + r) * SM::kPX + 16 * sg + li] = f32_to_bf16(dxa[jj][r]);
+                for (int k = 0; k < 2; k++) {
+                    const uint32_t d2 = pk_bf16(dxa[jj][2 * k], dxa[jj][2 * k + 1]);
+                    DX[(s0 + 2 * k) * SM::kPX + 16 * sg + li] = bf16_t(d2 & 0xffffu);
+                    DX[(s0 + 2 * k + 1) * SM::kPX + 16 * sg + li] = bf16_t(d2 >> 16);
+                }
             }
 #pragma unroll
             for (int ks = 0; ks < kNS; ks++) {
@@ -868,8 +871,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_fold_kernel(SsdBwdParams p, BwdWs
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                o[e] = uint32_t(f32_to_bf16(tile[t][8 * c8 + 2 * e])) |
-                       (uint32_t(f32_to_bf16(tile[t][8 * c8 + 2 * e + 1])) << 16);
+                o[e] = pk_bf16(tile[t][8 * c8 + 2 * e], tile[t][8 * c8 + 2 * e + 1]);
             st_global16(dst + t * G * N + 8 * c8, o);
         }
     }
