@@ -334,8 +334,9 @@ def timed_calls(hip, lib, calls, marks, iters):
 
 def wide_state_detail(hip, lib, to_dev, dev):
     """The fwd + bwd step at the Mamba-130m layer shape with d_state 64 (four
-    16-state slices: the forward runs them in each lane, the backward one per
-    grid z plus its combine kernel), f32 io."""
+    16-state slices: the forward runs them in each lane, the backward one
+    launch per slice, each adding its du and ddelta to the sum so far), f32
+    io."""
     import torch
 
     from selective_state_space_scan_amd import binding
@@ -354,9 +355,9 @@ def wide_state_detail(hip, lib, to_dev, dev):
                        d["delta_bias"], True, out=y, ckpt=ck, workspace=fws)
         binding.ss_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
                        d["delta_bias"], True, d["dout"], workspace=bws, ckpt=ck)
-    # per step: fwd [start, scan]; bwd [start, reverse slices, combine, fold]
-    parts = timed_calls(hip, lib, [step], 6, 5)
-    names = ["fwd_ms", None, "bwd_reverse_slices_ms", "bwd_combine_ms", "bwd_fold_ms"]
+    # per step: fwd [start, scan]; bwd [start, reverse slices, fold]
+    parts = timed_calls(hip, lib, [step], 5, 5)
+    names = ["fwd_ms", None, "bwd_reverse_slices_ms", "bwd_fold_ms"]
     out = {n: round(v, 5) for n, v in zip(names, parts) if n}
     tot = sum(v for n, v in zip(names, parts) if n)
     out["step_kernels_ms"] = round(tot, 5)

@@ -100,6 +100,15 @@ struct Workspace {
     // 2..kMaxLaneSlices slices without the forward's record: the pre-gate
     // output the forward kernel writes for this call (batch, dim, L)
     float *ypre_ws;
+    // Slices chained one launch after another (when no dz partials are
+    // needed): slice slice_base of the launch; chain 0 writes the slice's
+    // partial du and ddelta, 1 adds the partial to the sum of the slices
+    // before it (slice 0's buffers, in place), 2 (the last slice) adds it,
+    // adds the skip term with chainD and stores du and ddelta in the io
+    // type.  The sums run in ascending slice order, as the combine kernel
+    // adds them.
+    int chain, slice_base;
+    const float *chainD;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -147,6 +156,9 @@ inline Workspace carve(void *base, int64_t batch, int64_t dim, int64_t L, int ns
     w.dpre_head = take(bsd * kConvMaxWidth);
     w.dx_tail = take(bsd * kConvMaxWidth);
     w.dup = w.ddp = w.dzp = nullptr;
+    w.chain = 0;
+    w.slice_base = 0;
+    w.chainD = nullptr;
     w.ypre_ws = nullptr;
     if (slices > 1) {
         // up to kMaxLaneSlices slices dz comes whole from the pre-gate output
@@ -527,7 +539,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     constexpr int KC = CONV > 0 ? CONV : 0;
     // grid z: (slice, time segment)
     const int nsg = ws.nseg;
-    const int slice = int(blockIdx.z) / nsg, seg = int(blockIdx.z) % nsg;
+    const int slice = ws.slice_base + int(blockIdx.z) / nsg, seg = int(blockIdx.z) % nsg;
+    const int chain = PART ? ws.chain : 0;
     if (PART) ws = slice_ws(ws, slice);
     constexpr bool kStage = kStageElems<T>;
     constexpr int kRowsG = SM::kR;
@@ -609,7 +622,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
     const T *gdo = static_cast<const T *>(p.dout) + wavebase;
-    const size_t slice_el = PART ? slice * size_t(p.batch * Dm * L) : 0;
+    const size_t slice_el = (PART && chain == 0) ? slice * size_t(p.batch * Dm * L) : 0;
     OutT *du_b = (PART ? reinterpret_cast<OutT *>(ws.dup + slice_el) : static_cast<OutT *>(p.du)) + wavebase;
     OutT *dd_b = (PART ? reinterpret_cast<OutT *>(ws.ddp + slice_el) : static_cast<OutT *>(p.ddelta)) + wavebase;
     OutT *dz_b = has_z ? (PART ? reinterpret_cast<OutT *>(ws.dzp + slice_el) : static_cast<OutT *>(p.dz)) + wavebase
@@ -617,6 +630,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     OutT *dx_b = CONV != 0 ? static_cast<OutT *>(p.dx) + wavebase : nullptr;
     // slices with the saved pre-gate output: dz is whole, written by slice 0
     T *dz_whole = (PART && YP && has_z && slice == 0) ? static_cast<T *>(p.dz) + wavebase : nullptr;
+    // the last of chained slices: the outputs in the io type, and the skip term
+    T *du_fin = static_cast<T *>(p.du) + wavebase;
+    T *dd_fin = static_cast<T *>(p.ddelta) + wavebase;
+    const float dlast = (chain == 2 && row_ok && ws.chainD) ? ws.chainD[d] : 0.0f;
     const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
     auto elem_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(T)); };
     auto out_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(OutT)); };
@@ -626,6 +643,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     auto ypre_at = [&](int t) {
         return (YP && row_ok && t >= 0 && t < Ls) ? ld_global(at_bytes(ypb, uint32_t(rowel + t) * 4u))
                                                   : 0.0f;
+    };
+    // chained slices: the earlier slices' sum of a partial, loaded the same way
+    auto acc_at = [&](const OutT *base, int t) {
+        return (row_ok && t >= 0 && t < Ls) ? float(ld_global(at_bytes(base, out_off(t)))) : 0.0f;
     };
     // element t of this lane's row of u, delta, z or dout (0 past the end
     // and for rows past the last channel)
@@ -708,6 +729,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // own, so the loads land in the same registers without copies.
     // (with seqlen 0 there is no chunk and nothing is loaded)
     float hn[kNB] = {}, ypn[kNB] = {}, un[kNB] = {}, dn[kNB] = {}, zn[kNB] = {}, gn[kNB] = {};
+    float aun[kNB] = {}, adn[kNB] = {};   // chained slices: the sums so far
     // fused convolution: the lane's input one block before the chunk, as raw
     // bits loaded a chunk ahead (the initial window's value for the chunk
     // at step 0)
@@ -720,6 +742,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             const int t = tc + 16 * s + n;
             hn[s] = ckpt_at(kNB * (tc / kC) + s);
             if (YP) ypn[s] = ypre_at(t);
+            if constexpr (PART) {
+                if (chain) {
+                    aun[s] = acc_at(du_b, t);
+                    adn[s] = acc_at(dd_b, t);
+                }
+            }
             if constexpr (!kStage) {
                 un[s] = elem_at(gu, t);
                 dn[s] = elem_at(gdl, t);
@@ -762,6 +790,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row
         float dl[kNB], dlu[kNB], uu[kNB], sgd[kNB], dout[kNB], zz[kNB], dyv[kNB];
+        float acu[kNB], acd[kNB];
+#pragma unroll
+        for (int s = 0; s < kNB; s++) {
+            acu[s] = aun[s];
+            acd[s] = adn[s];
+        }
         // fused convolution: the inputs by lag and d act / d pre of the
         // lane's elements (un holds the convolution's input)
         float xl[kNB][kConvMaxWidth], gpre[kNB];
@@ -919,11 +953,23 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                 if (hh == 0 && n < 8) { sumA = sum; sumB = other; }
                 if (hh == 1 && n >= 8) { sumA = other; sumB = sum; }
             }
-            const float du = __builtin_fmaf(dl[s], sumB, dskip * dy);
-            const float dd = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];
+            float du = __builtin_fmaf(dl[s], sumB, dskip * dy);
+            const float dd_own = __builtin_fmaf(uu[s], sumB, sumA) * sgd[s];   // this slice's
+            float dd = dd_own;
+            if constexpr (PART) {
+                if (chain) {
+                    du = acu[s] + du;
+                    dd = acd[s] + dd_own;
+                }
+            }
             if (row_ok && t0 + col < Ls) {
-                if constexpr (CONV == 0) st_global(at_bytes(du_b, out_off(t0 + col)), from_f32<OutT>(du));
-                st_global(at_bytes(dd_b, out_off(t0 + col)), from_f32<OutT>(dd));
+                if (PART && chain == 2) {
+                    st_global(at_bytes(du_fin, elem_off(t0 + col)), from_f32<T>(__builtin_fmaf(dlast, dy, du)));
+                    st_global(at_bytes(dd_fin, elem_off(t0 + col)), from_f32<T>(dd));
+                } else {
+                    if constexpr (CONV == 0) st_global(at_bytes(du_b, out_off(t0 + col)), from_f32<OutT>(du));
+                    st_global(at_bytes(dd_b, out_off(t0 + col)), from_f32<OutT>(dd));
+                }
             }
             if constexpr (CONV != 0) {
                 // the convolution's backward: pre-activation gradient, its
@@ -943,7 +989,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                         st_global(at_bytes(dx_b, out_off(t)), from_f32<OutT>(dxv));
                 }
             }
-            if (t0 + col < Ls) dbias_acc += dd;
+            if (t0 + col < Ls) dbias_acc += dd_own;
         }
 
         // The next chunk's B / C go to the other buffer, whose last readers
@@ -1195,7 +1241,7 @@ __global__ __launch_bounds__(256) void ss_bwd_combine_kernel(BwdParams p, Worksp
             dy[i] = g[i] * z[i] * sz;
             if (do_dz) dz[i] += g[i] * (dskip * u[i]) * sz * (1.0f + z[i] * (1.0f - sz));
         }
-        du[i] += dskip * dy[i];
+        du[i] = __builtin_fmaf(dskip, dy[i], du[i]);
     }
     if (do_dz) stv(p.dz, dz);
     stv(p.du, du);
@@ -1212,10 +1258,12 @@ int reverse_waves(const BwdParams &p, bool vec) {
     return scan_waves(p.batch * nseg, p.dim);
 }
 
+// zslices: the slices this launch runs side by side (grid z), from
+// ws.slice_base on; 0 for all of them
 template <typename T, int VEC, bool YP, int NW, bool PART = false, int CONV = 0>
-void launch_reverse(const BwdParams &p, Workspace ws, hipStream_t stream) {
+void launch_reverse(const BwdParams &p, Workspace ws, hipStream_t stream, int zslices = 0) {
     const dim3 grid(unsigned((p.dim + 4 * NW - 1) / (4 * NW)), unsigned(p.batch),
-                    unsigned(state_slices(p.nstate) * ws.nseg));
+                    unsigned((zslices > 0 ? zslices : state_slices(p.nstate)) * ws.nseg));
     hipLaunchKernelGGL((ss_bwd_reverse_kernel<T, VEC, YP, NW, PART, CONV>), grid, dim3(64 * NW), 0,
                        stream, p, ws);
 }
@@ -1316,6 +1364,9 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
             profile_mark(stream);
         }
         const bool yp = p.z && ws.ypre && (slices == 1 ? p.ckpt != nullptr : lane_slices);
+        // several slices and no dz partials to add: the slices run one launch
+        // after another and the last stores du and ddelta (no combine kernel)
+        const bool chained = slices > 1 && (yp || !p.z) && p.conv_width == 0;
         const int nw = reverse_waves(p, vec);
         ws.groups = (p.dim + 4 * nw - 1) / (4 * nw);   // the partials the fold reads
         ws.sub = nw == 12 ? 1 : 3;
@@ -1327,14 +1378,29 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
             launch_reverse_conv<T, 4>(p, ws, vec, yp, nw, stream);
         } else if (p.conv_width > 0) {
             launch_reverse_conv<T, -1>(p, ws, vec, yp, nw, stream);
-        } else if (slices > 1 && yp) {
-            if (vec && nw == 12) launch_reverse<T, kVec, true, 12, true>(q, ws, stream);
-            else if (vec) launch_reverse<T, kVec, true, 4, true>(q, ws, stream);
-            else launch_reverse<T, 1, true, 4, true>(q, ws, stream);
         } else if (slices > 1) {
-            if (vec && nw == 12) launch_reverse<T, kVec, false, 12, true>(q, ws, stream);
-            else if (vec) launch_reverse<T, kVec, false, 4, true>(q, ws, stream);
-            else launch_reverse<T, 1, false, 4, true>(q, ws, stream);
+            auto part = [&](Workspace w, int zsl) {
+                if (yp) {
+                    if (vec && nw == 12) launch_reverse<T, kVec, true, 12, true>(q, w, stream, zsl);
+                    else if (vec) launch_reverse<T, kVec, true, 4, true>(q, w, stream, zsl);
+                    else launch_reverse<T, 1, true, 4, true>(q, w, stream, zsl);
+                } else {
+                    if (vec && nw == 12) launch_reverse<T, kVec, false, 12, true>(q, w, stream, zsl);
+                    else if (vec) launch_reverse<T, kVec, false, 4, true>(q, w, stream, zsl);
+                    else launch_reverse<T, 1, false, 4, true>(q, w, stream, zsl);
+                }
+            };
+            if (chained) {   // one launch per slice, each adding to the sum so far
+                for (int sl = 0; sl < slices; sl++) {
+                    Workspace w = ws;
+                    w.slice_base = sl;
+                    w.chain = sl == 0 ? 0 : (sl == slices - 1 ? 2 : 1);
+                    w.chainD = p.D;
+                    part(w, 1);
+                }
+            } else {
+                part(ws, 0);
+            }
         } else if (vec && nw == 12) {
             if (yp) launch_reverse<T, kVec, true, 12>(p, ws, stream);
             else launch_reverse<T, kVec, false, 12>(p, ws, stream);
@@ -1355,7 +1421,7 @@ hipError_t launch_typed(const BwdParams &p, hipStream_t stream) {
             profile_mark(stream);
         }
         const int64_t E = p.batch * p.dim * p.seqlen;
-        if (slices > 1 && E > 0) {
+        if (slices > 1 && E > 0 && !chained) {
             if (p.seqlen % 4 == 0)
                 hipLaunchKernelGGL((ss_bwd_combine_kernel<T, 4>), dim3(unsigned((E / 4 + 255) / 256)),
                                    dim3(256), 0, stream, p, ws, slices, int(!yp));
