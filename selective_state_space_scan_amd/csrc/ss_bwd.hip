@@ -244,10 +244,9 @@ __device__ __forceinline__ void fwd_step(float dl, float dlu, float a2, float b,
 template <typename T, int VEC, int CONV = 0>
 __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Workspace ws) {
     using SM = CkptSmem<T>;
-    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
-    float(*sB)[kPitch1] = reinterpret_cast<float(*)[kPitch1]>(smem + SM::kB);
-    T(*sU)[kT1] = reinterpret_cast<T(*)[kT1]>(smem + SM::kU);
-    T(*sDl)[kT1] = reinterpret_cast<T(*)[kT1]>(smem + SM::kDl);
+    // two buffers: the next chunk is stashed into the other while this one
+    // is read (one barrier per chunk)
+    __shared__ __attribute__((aligned(16))) char smem[2 * SM::kSize];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, r = wave * 4 + (lane >> 4);
@@ -310,6 +309,10 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
     __syncthreads();
     for (int64_t c = cbeg; c < cend; c++) {
         const int64_t t0 = c * kT1;
+        char *buf = smem + ((c - cbeg) & 1) * SM::kSize;
+        float(*sB)[kPitch1] = reinterpret_cast<float(*)[kPitch1]>(buf + SM::kB);
+        T(*sU)[kT1] = reinterpret_cast<T(*)[kT1]>(buf + SM::kU);
+        T(*sDl)[kT1] = reinterpret_cast<T(*)[kT1]>(buf + SM::kDl);
         if (c + 1 < cend) st.fetch(t0 + kT1, L, tid);
         float dl[kT1 / 16], dlu[kT1 / 16];
 #pragma unroll
@@ -348,8 +351,12 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_ckpt_kernel(BwdParams p, Work
                 }
             }
         }
-        __syncthreads();
-        if (c + 1 < cend) st.stash(smem, zero_dead);
+        // the state is complete before the barrier (left free, the
+        // register-only recurrence can sink past it)
+        __asm__ volatile("" : "+v"(h));
+        // the other buffer's last readers (the chunk before) are behind the
+        // previous barrier
+        if (c + 1 < cend) st.stash(smem + ((c + 1 - cbeg) & 1) * SM::kSize, zero_dead);
         __syncthreads();
     }
 }
@@ -385,11 +392,8 @@ __device__ __forceinline__ void adj_step(float dl, float dy, float a2, float cv,
 template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void ss_bwd_adjoint_summary_kernel(BwdParams p, Workspace ws) {
     using SM = AdjSmem<T>;
-    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
-    float(*sC)[kPitch1] = reinterpret_cast<float(*)[kPitch1]>(smem + SM::kC);
-    const T(*sDl)[kT1] = reinterpret_cast<const T(*)[kT1]>(smem + SM::kDl);
-    const T(*sZ)[kT1] = reinterpret_cast<const T(*)[kT1]>(smem + SM::kZ);
-    const T(*sG)[kT1] = reinterpret_cast<const T(*)[kT1]>(smem + SM::kG);
+    // two buffers, one barrier per chunk (as in the checkpoint kernel)
+    __shared__ __attribute__((aligned(16))) char smem[2 * SM::kSize];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, r = wave * 4 + (lane >> 4);
     const int64_t L = p.seqlen, Dm = p.dim, b = blockIdx.y;
@@ -430,6 +434,11 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_adjoint_summary_kernel(BwdPar
     __syncthreads();
     for (int64_t ch = cend - 1; ch >= cbeg; ch--) {
         const int64_t t0 = ch * kT1;
+        char *buf = smem + ((cend - 1 - ch) & 1) * SM::kSize;
+        float(*sC)[kPitch1] = reinterpret_cast<float(*)[kPitch1]>(buf + SM::kC);
+        const T(*sDl)[kT1] = reinterpret_cast<const T(*)[kT1]>(buf + SM::kDl);
+        const T(*sZ)[kT1] = reinterpret_cast<const T(*)[kT1]>(buf + SM::kZ);
+        const T(*sG)[kT1] = reinterpret_cast<const T(*)[kT1]>(buf + SM::kG);
         if (ch > cbeg) st.fetch(t0 - kT1, L, tid);
         float dl[kT1 / 16], dy[kT1 / 16];
 #pragma unroll
@@ -469,8 +478,7 @@ __global__ __launch_bounds__(kThreads) void ss_bwd_adjoint_summary_kernel(BwdPar
         // the carry is complete before the barrier (left free, the
         // register-only recurrence sinks past it into the next iteration)
         __asm__ volatile("" : "+v"(c));
-        __syncthreads();
-        if (ch > cbeg) st.stash(smem, zero_dead);
+        if (ch > cbeg) st.stash(smem + ((cend - ch) & 1) * SM::kSize, zero_dead);
         __syncthreads();
     }
     // the decay exp(A sum delta), the delta sum formed in one fixed tree

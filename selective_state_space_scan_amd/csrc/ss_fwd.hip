@@ -106,8 +106,9 @@ __device__ __forceinline__ size_t summ_decay_offset(const FwdParams &p) {
 // The summary pass of a segmented scan: every segment but the last from a
 // zero state, the recurrence only, writing the segment's end state and its
 // total decay exp(A sum delta).  16 channels (4 wavefronts) per workgroup,
-// B, u and delta staged through LDS in 64-step chunks; grid z holds
-// (slice, segment < nseg - 1).
+// B, u and delta staged through LDS in 64-step chunks, two buffers (the
+// next chunk is stashed into the other while this one is read, one barrier
+// per chunk); grid z holds (slice, segment < nseg - 1).
 constexpr int kTS = 64;
 constexpr int kPitchS = kTS + 4;
 
@@ -127,10 +128,7 @@ __device__ __forceinline__ float state_step(float dl, float dlu, float a2, float
 template <typename T, int VEC, int CONV = 0>
 __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
     using SM = SumSmem<T>;
-    __shared__ __attribute__((aligned(16))) char smem[SM::kSize];
-    float(*sB)[kPitchS] = reinterpret_cast<float(*)[kPitchS]>(smem + SM::kB);
-    const T(*sU)[kTS] = reinterpret_cast<const T(*)[kTS]>(smem + SM::kU);
-    const T(*sDl)[kTS] = reinterpret_cast<const T(*)[kTS]>(smem + SM::kDl);
+    __shared__ __attribute__((aligned(16))) char smem[2 * SM::kSize];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, r = wave * 4 + (lane >> 4);
@@ -174,6 +172,10 @@ __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
     __syncthreads();
     for (int c = 0; c < nchunk; c++) {
         const int64_t t0 = tbeg + int64_t(c) * kTS;
+        char *buf = smem + (c & 1) * SM::kSize;
+        float(*sB)[kPitchS] = reinterpret_cast<float(*)[kPitchS]>(buf + SM::kB);
+        const T(*sU)[kTS] = reinterpret_cast<const T(*)[kTS]>(buf + SM::kU);
+        const T(*sDl)[kTS] = reinterpret_cast<const T(*)[kTS]>(buf + SM::kDl);
         if (c + 1 < nchunk) st.fetch(t0 + kTS, L, tid);
         float dl[kTS / 16], dlu[kTS / 16];
 #pragma unroll
@@ -214,8 +216,9 @@ __global__ __launch_bounds__(256) void ss_fwd_summary_kernel(FwdParams p) {
         // register-only recurrence sinks past it into the next iteration,
         // with every broadcast of the chunk live across the loop edge
         __asm__ volatile("" : "+v"(h));
-        __syncthreads();
-        if (c + 1 < nchunk) st.stash(smem, Ns < kN);
+        // the other buffer's last readers (the chunk before) are behind the
+        // previous barrier
+        if (c + 1 < nchunk) st.stash(smem + ((c + 1) & 1) * SM::kSize, Ns < kN);
         __syncthreads();
     }
     // the decay exp(A sum delta) from the row's delta sum, formed in one
