@@ -140,8 +140,10 @@ def test_bwd_rows_do_not_depend_on_batch(dim, L, io):
 def test_bwd_smaller_dstate(batch, dim, N, L, io):
     """d_state other than 16, every gradient against the oracle (the
     1544-channel shapes take the 48-channel reverse pass; above 16 states the
-    slices' partials go through the combine kernel), and a backward with the
-    forward's saved record giving the same bits as one that recomputes it."""
+    slices run one launch each and chain their du and ddelta sums up to 64
+    states, and go through the combine kernel above), and a backward with
+    the forward's saved record giving the same bits as one that recomputes
+    it."""
     require_gpu()
     w = ssin.custom("bwd", batch, dim, N, L, io, seed=17 * N + L + dim)
     arr = ssin.make(w)
@@ -170,6 +172,34 @@ def test_bwd_smaller_dstate(batch, dim, N, L, io):
         if a.dtype == torch.bfloat16:
             a, b2 = a.view(torch.int16), b2.view(torch.int16)
         assert torch.equal(a, b2), f"{k} with saved record"
+
+
+@pytest.mark.parametrize("batch,dim,N,L,io", [(2, 40, 40, 96, "f32"), (2, 24, 100, 70, "bf16"),
+                                              (8, 1544, 33, 64, "f32")])
+def test_bwd_slices_without_gate(batch, dim, N, L, io):
+    """Without z no slice needs dz partials, so at any d_state above 16 the
+    slices chain their du and ddelta sums launch after launch (the last adds
+    D dy): every gradient against the oracle, and the same bits on a second
+    call."""
+    require_gpu()
+    w = ssin.custom("bwd", batch, dim, N, L, io, seed=31 * N + L, has_z=False)
+    arr = ssin.make(w)
+    say(f"bwd no gate {w.name}")
+    d = dev_inputs(arr)
+    g = run_bwd(d, w)
+    g2 = run_bwd(d, w)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(arr, w)
+    for k in KEYS:
+        if k not in ref:
+            continue
+        tol = TOL["f32"] if k in ("dA", "dD", "ddelta_bias") else TOL[io]
+        assert_close(to_host(g[k]), ref[k], tol, f"{k} N={N}")
+    for k in g:
+        a, b2 = g[k], g2[k]
+        if a.dtype == torch.bfloat16:
+            a, b2 = a.view(torch.int16), b2.view(torch.int16)
+        assert torch.equal(a, b2), f"{k} differs between calls"
 
 
 def test_bwd_zero_length_passes_dlast_through():
