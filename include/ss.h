@@ -375,7 +375,9 @@ ss_status ss_bwd_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen
  *   A, D, dt_bias   : (nheads)                           float
  *   h0, last_state  : (batch, nheads, headdim, dstate)   float
  * io_dtype must be SS_BF16 (SS_EUNSUPPORTED otherwise); headdim 16, 32, 48
- * or 64; dstate 32, 64, 96 or 128; ngroups divides nheads; seqlen <= 2^26.
+ * or 64; dstate 32, 64, 96 or 128; ngroups divides nheads; seqlen <= 2^26;
+ * batch <= 65535 and batch * nheads < 2^22 (one workgroup of up to 1024
+ * threads per (batch, head); SS_EUNSUPPORTED beyond).
  * D, dt_bias, h0, last_state may be NULL; last_state must not overlap h0.
  * ckpt, when non-NULL (ss_ssd_ckpt_size() bytes, f32), receives the state
  * entering every chunk of 64 steps, which a later ss_ssd_bwd with the same

@@ -497,7 +497,9 @@ ss_status check_ssd_dims(int64_t batch, int64_t seqlen, int64_t nheads, int64_t 
     if (seqlen > kMaxSeq)
         return fail(SS_EUNSUPPORTED, "seqlen %lld exceeds %lld", (long long)seqlen,
                     (long long)kMaxSeq);
-    if (batch > kMaxBatch || !grid_fits(batch * nheads, 512))
+    // the forward takes one block of 16 * headdim (up to 1024) threads per
+    // (batch, head), the backward's chunk kernel one of 512
+    if (batch > kMaxBatch || !grid_fits(batch * nheads, 1024))
         return fail(SS_EUNSUPPORTED,
                     "batch * nheads: the SSD launch grid would exceed 2^32 work-items");
     return SS_OK;

@@ -420,8 +420,9 @@ def test_decode_grid_limit(lib):
 def test_conv_and_ssd_grid_limits(lib):
     # the convolution's backward takes one 128-thread block per channel
     assert _cbwd(lib, batch=1, dim=1 << 26, seqlen=16) == EUNSUP and "2^32" in _msg(lib)
-    # the SSD kernels take one block of up to 512 threads per (batch, head)
+    # the SSD kernels take one block of up to 1024 threads per (batch, head)
     assert _ssd(lib, batch=1 << 12, nheads=1 << 12) == EUNSUP and "2^32" in _msg(lib)
+    assert _ssd(lib, batch=1 << 10, nheads=1 << 12) == EUNSUP and "2^32" in _msg(lib)
 
 
 def test_bwd_noalloc_validates_like_ss_bwd(lib):
