@@ -600,6 +600,20 @@ def _scan_call(name, to_dev, dev):
         return (lambda: binding.ss_fwd_conv(d["u"], cw, d["delta"], d["A"], d["B"], d["C"],
                                             d["D"], d["z"], d["delta_bias"], True,
                                             conv_bias=cb, out=y)), (d, y, cw, cb)
+    if name.startswith("stepconv"):   # fused convolution + scan, forward saving its record and backward
+        ac = ssin.make_conv(ssin.CONV_WORKLOADS["mamba130m_conv_bf16_8x1536x2048"])
+        cw, cb = to_dev(ac["weight"]), to_dev(ac["bias"])
+        ck = binding.ss_ckpt_empty(d["u"], dstate=w.dstate)
+        ws = torch.empty(binding.ss_bwd_workspace_size(w.batch, w.dim, w.dstate, w.seqlen, io),
+                         dtype=torch.uint8, device=dev)
+
+        def cstep():
+            binding.ss_fwd_conv(d["u"], cw, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                d["delta_bias"], True, conv_bias=cb, out=y, ckpt=ck)
+            binding.ss_bwd_conv(d["u"], cw, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                d["delta_bias"], True, d["dout"], conv_bias=cb, workspace=ws,
+                                ckpt=ck)
+        return cstep, (d, y, cw, cb, ck, ws)
     if w.kind == "fwd" or name.startswith("fwd"):
         return (lambda: binding.ss_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                        d["delta_bias"], True, out=y, last_state=last)), (d, y, last)
@@ -626,6 +640,7 @@ PROFILE_WORKLOADS = {
     "bwd_f32_8x1536x2048_standalone": "mamba130m_bwd_f32_8x1536x2048",
     "fwd_bf16_8x1536x2048": "mamba130m_fwd_bf16_8x1536x2048",
     "fwdconv_bf16_8x1536x2048": "mamba130m_fwd_bf16_8x1536x2048",
+    "stepconv_bf16_8x1536x2048": "mamba130m_bwd_bf16_8x1536x2048",
     "fwd_bf16_4x5120x4096": "mamba2p8b_fwd_bf16_4x5120x4096",
     "decode_bf16_256x5120": "decode_bf16_256x5120",
     "fwd_bf16_1x1536x16384": "mamba130m_long_bf16_1x1536x16384",
