@@ -96,21 +96,32 @@ constexpr f32x4 kZero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 // unevaluated pair hi + lo (compensated with the error-free two-sum of
 // Knuth and Moller).  Decays exp(cum_t - cum_s) are then taken from
 // (hi_t - hi_s) + (lo_t - lo_s): a plain f32 running sum would lose the
-// low digits of a difference once the sum has grown large.
+// low digits of a difference once the sum has grown large.  The partial
+// sums move by DPP: shifts by 1, 2, 4 and 8 within each row of 16 lanes,
+// then the last lane of rows 0 and 2 into rows 1 and 3, then lane 31 into
+// rows 2 and 3; each step adds the pair it receives with the two-sum.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void running_sum2_step(float &hi, float &lo, bool take) {
+    const float oh = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(hi), CTRL, ROWS, 0xf, false));
+    const float ol = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(lo), CTRL, ROWS, 0xf, false));
+    if (take) {
+        const float s = hi + oh, bb = s - hi;
+        const float e = (hi - (s - bb)) + (oh - bb);
+        const float l = lo + ol + e;
+        hi = s + l;
+        lo = l - (hi - s);
+    }
+}
 __device__ __forceinline__ void running_sum2(float a, int lane, float &hi, float &lo) {
     hi = a;
     lo = 0.0f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float oh = __shfl_up(hi, off, 64), ol = __shfl_up(lo, off, 64);
-        if (lane >= off) {
-            const float s = hi + oh, bb = s - hi;
-            const float e = (hi - (s - bb)) + (oh - bb);
-            const float l = lo + ol + e;
-            hi = s + l;
-            lo = l - (hi - s);
-        }
-    }
+    const int lr = lane & 15, row = lane >> 4;
+    running_sum2_step<0x111, 0xf>(hi, lo, lr >= 1);   // row_shr:1
+    running_sum2_step<0x112, 0xf>(hi, lo, lr >= 2);
+    running_sum2_step<0x114, 0xf>(hi, lo, lr >= 4);
+    running_sum2_step<0x118, 0xf>(hi, lo, lr >= 8);
+    running_sum2_step<0x142, 0xa>(hi, lo, row & 1);     // row_bcast:15 into rows 1, 3
+    running_sum2_step<0x143, 0xc>(hi, lo, row >= 2);    // row_bcast:31 into rows 2, 3
 }
 
 }  // namespace ssk

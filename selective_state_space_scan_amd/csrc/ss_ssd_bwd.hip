@@ -115,47 +115,91 @@ struct BwdSmem {
     static constexpr uint32_t kSize = kCumLo + kQ * 4;
 };
 
-__device__ __forceinline__ float sum16(float v) {   // over the 16 lanes of a row
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
+// Lane exchanges on DPP moves and lane swaps (no LDS round trips).  A DPP
+// move of a 32-bit value; rotations within a row and quad permutations read
+// a lane of the same row, so every lane has a source.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+constexpr int kRor8 = 0x128, kRor4 = 0x124, kXor2 = 0x4E, kXor1 = 0xB1, kHalfMirror = 0x141;
+
+// v_permlane32_swap with both operands v hands lane i the value of lane
+// i ^ 32 in its second result; v_permlane16_swap pairs rows 0-1 and 2-3 the
+// same way.  The two results are added in the same order in both lanes.
+__device__ __forceinline__ float half_swap_sum(float v, bool rows) {
+    const unsigned x = __float_as_uint(v);
+    const auto r = rows ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                        : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __uint_as_float(r0) + __uint_as_float(r1);
+}
+__device__ __forceinline__ double half_swap_sumd(double v, bool rows) {
+    const unsigned lo = unsigned(__double2loint(v)), hi = unsigned(__double2hiint(v));
+    const auto rl = rows ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                         : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto rh = rows ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                         : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const unsigned l0 = rl[0], l1 = rl[1], h0 = rh[0], h1 = rh[1];
+    return __hiloint2double(int(h0), int(l0)) + __hiloint2double(int(h1), int(l1));
+}
+
+// Sum over the 16 lanes of a row, the same bits in every lane: lanes 8
+// apart, then 4 apart (rotations, so each pair is added in one order in both
+// of its lanes), then within quads.
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp_f<kRor8>(v);
+    v += dpp_f<kRor4>(v);
+    v += dpp_f<kXor2>(v);
+    v += dpp_f<kXor1>(v);
     return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
     v = sum16(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    v = half_swap_sum(v, false);
+    return half_swap_sum(v, true);
 }
 
 __device__ __forceinline__ double sum16d(double v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
+    v += dpp_d<kRor8>(v);
+    v += dpp_d<kRor4>(v);
+    v += dpp_d<kXor2>(v);
+    v += dpp_d<kXor1>(v);
     return v;
 }
 
 __device__ __forceinline__ double wave_sumd(double v) {
     v = sum16d(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    v = half_swap_sumd(v, false);
+    return half_swap_sumd(v, true);
 }
 
 // Sums of four values over the 16 lanes of a row, scattered: lane li gets
 // the sum of x[li / 4 % 4].  Five exchanges (two, then one per level) in
-// place of four full butterflies.
+// place of four full butterflies: lanes 8 apart (li ^ 8, a rotation by 8),
+// then across the two quads of each half row (a mirror within the half: a
+// lane reads a different lane of the other quad than li ^ 4, which the quad
+// sums after it do not notice), then within quads.
+template <typename T, int CTRL>
+__device__ __forceinline__ T dpp_any(T v) {
+    if constexpr (sizeof(T) == 8) return dpp_d<CTRL>(v);
+    else return dpp_f<CTRL>(v);
+}
 template <typename T>
 __device__ __forceinline__ T sum16x4(const T (&x)[4], int li) {
     const bool b3 = li & 8, b2 = li & 4;
-    const T y0 = (b3 ? x[2] : x[0]) + __shfl_xor(b3 ? x[0] : x[2], 8, 64);
-    const T y1 = (b3 ? x[3] : x[1]) + __shfl_xor(b3 ? x[1] : x[3], 8, 64);
-    T z = (b2 ? y1 : y0) + __shfl_xor(b2 ? y0 : y1, 4, 64);
-    z += __shfl_xor(z, 2, 64);
-    z += __shfl_xor(z, 1, 64);
+    const T y0 = (b3 ? x[2] : x[0]) + dpp_any<T, kRor8>(b3 ? x[0] : x[2]);
+    const T y1 = (b3 ? x[3] : x[1]) + dpp_any<T, kRor8>(b3 ? x[1] : x[3]);
+    T z = (b2 ? y1 : y0) + dpp_any<T, kHalfMirror>(b2 ? y0 : y1);
+    z += dpp_any<T, kXor2>(z);
+    z += dpp_any<T, kXor1>(z);
     return z;
 }
 
@@ -317,7 +361,8 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
             }
             float a, alo;   // running sum of dt A in base-2 exponent units, hi + lo
             running_sum2(dv * a2, lane, a, alo);
-            const float total = __shfl(a, 63, 64), tlo = __shfl(alo, 63, 64);
+            const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 63));
+            const float tlo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alo), 63));
             cum[tid] = a;
             cumlo[tid] = alo;
             dts[tid] = dv;
@@ -572,8 +617,8 @@ __global__ __launch_bounds__(kThr) void ss_ssd_bwd_kernel(SsdBwdParams p, BwdWs 
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
             double v = colg[jj];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
+            v = half_swap_sumd(v, false);
+            v = half_swap_sumd(v, true);
             if (lg == 0) Ug[wv * kQ + 16 * kT[jj] + li] = v;
         }
 #pragma unroll
