@@ -279,9 +279,12 @@ __global__ __launch_bounds__(16 * P) void ss_ssd_fwd_kernel(SsdParams p) {
         }
     };
     // a chunk's output rows: 16-byte stores, P / 8 lanes per row
+    // (the second half of the threads: the first wavefronts make the W tiles
+    // in the same phase)
     auto store_rows = [&](int64_t c0) {
-        const int t = tid / (P / 8), c8 = tid % (P / 8);
-        if (tid < kQ * P / 8 && c0 + t < L)
+        const int i = tid - (kThr - kQ * P / 8);
+        const int t = i / (P / 8), c8 = i % (P / 8);
+        if (i >= 0 && c0 + t < L)
             st_global16(yg + (c0 + t) * xrow + 8 * c8,
                         *reinterpret_cast<const u32x4 *>(Ys + t * SM::kPY + 8 * c8));
     };
