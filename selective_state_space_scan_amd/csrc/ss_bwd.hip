@@ -782,13 +782,23 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         const T(*sZ)[kC] = reinterpret_cast<const T(*)[kC]>(bc + SM::kZ);
         const T(*sG)[kC] = reinterpret_cast<const T(*)[kC]>(bc + SM::kG);
         if constexpr (kStage) {
+            // all reads before any use (a read behind a branch would wait for
+            // each one in turn); z's tile is read even without z
+            T su[kNB], sd[kNB], sz[kNB], sg[kNB];
 #pragma unroll
             for (int s = 0; s < kNB; s++) {
                 const int col = 16 * s + n;
-                un[s] = to_f32<T>(sU[r][col]);
-                dn[s] = to_f32<T>(sDl[r][col]);
-                zn[s] = has_z ? to_f32<T>(sZ[r][col]) : 0.0f;
-                gn[s] = to_f32<T>(sG[r][col]);
+                su[s] = sU[r][col];
+                sd[s] = sDl[r][col];
+                sz[s] = sZ[r][col];
+                sg[s] = sG[r][col];
+            }
+#pragma unroll
+            for (int s = 0; s < kNB; s++) {
+                un[s] = to_f32<T>(su[s]);
+                dn[s] = to_f32<T>(sd[s]);
+                zn[s] = has_z ? to_f32<T>(sz[s]) : 0.0f;
+                gn[s] = to_f32<T>(sg[s]);
             }
         }
         float hb[kNB];   // block states, used by the blocks after the reload

@@ -411,14 +411,26 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
 
         // per-element work: lane (r, n) owns elements 16 s + n of its row
         float dl[kE], dlu[kE], uu[kE], zz[kE];
+        // the staged elements, all read before any is used (a read behind a
+        // branch would wait for each one in turn); z's tile is read even
+        // without z (its value is then not used)
+        T su[kE], sd[kE], sz[kE];
+        if constexpr (kStage) {
+#pragma unroll
+            for (int s = 0; s < kE; s++) {
+                su[s] = sU[r][16 * s + n];
+                sd[s] = sDl[r][16 * s + n];
+                sz[s] = sZ[r][16 * s + n];
+            }
+        }
 #pragma unroll
         for (int s = 0; s < kE; s++) {
             const int col = 16 * s + n;
             float x;
             if constexpr (kStage) {
-                uu[s] = to_f32<T>(sU[r][col]);
-                zz[s] = has_z ? to_f32<T>(sZ[r][col]) : 0.0f;
-                x = to_f32<T>(sDl[r][col]) + bias;
+                uu[s] = to_f32<T>(su[s]);
+                zz[s] = has_z ? to_f32<T>(sz[s]) : 0.0f;
+                x = to_f32<T>(sd[s]) + bias;
             } else {
                 uu[s] = un[s];
                 zz[s] = zn[s];
