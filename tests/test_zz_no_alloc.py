@@ -32,19 +32,22 @@ def _equal(a, b, name):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_noalloc_matches_ss_bwd_twice_second_smaller(io):
     require_gpu()
-    cases = [  # (batch, dim, L, with the forward's saved record): large first, then smaller
-        (4, 200, 300, True),
-        (2, 72, 130, False),
+    cases = [  # (batch, dim, dstate, L, with the forward's saved record): large first, then smaller
+        (4, 200, 16, 300, True),
+        (2, 72, 16, 130, False),
+        # several 16-state slices, chained through the scratch array
+        (2, 40, 40, 96, False),
+        (1, 24, 33, 70, True),
     ]
-    for batch, dim, L, with_ckpt in cases:
-        say(f"noalloc {io} batch {batch} dim {dim} L {L} ckpt {with_ckpt}")
-        w = ssin.custom("bwd", batch, dim, 16, L, io, seed=batch * 100 + dim + L)
+    for batch, dim, N, L, with_ckpt in cases:
+        say(f"noalloc {io} batch {batch} dim {dim} dstate {N} L {L} ckpt {with_ckpt}")
+        w = ssin.custom("bwd", batch, dim, N, L, io, seed=batch * 100 + dim + L + N)
         d = dev_inputs(ssin.make(w))
         ck = None
         if with_ckpt:
-            ck = binding.ss_ckpt_empty(d["u"])
+            ck = binding.ss_ckpt_empty(d["u"], dstate=N)
             binding.ss_fwd(*_args(d), ckpt=ck)
-        dl = torch.randn(batch, dim, 16, device=d["u"].device)
+        dl = torch.randn(batch, dim, N, device=d["u"].device)
         ref = binding.ss_bwd(*_args(d), d["dout"], dlast=dl, want_dh0=True, ckpt=ck)
         got = binding.ss_bwd_noalloc(*_args(d), d["dout"], dlast=dl, want_dh0=True, ckpt=ck)
         torch.cuda.synchronize()
