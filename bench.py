@@ -195,7 +195,7 @@ def summarize_profile(prof_dir, copy_dir, kernel, workload, title, only, sources
     waves = avg.get("SQ_WAVES", 0.0)
     gui = avg.get("GRBM_GUI_ACTIVE", 0.0) / 8.0   # summed over the 8 XCDs
     out = [f"# {kernel} -- {title}", "",
-           "Measured on one MI355X (gfx950) with rocprofv3; raw outputs stay in gpurun_out/.", "",
+           "Measured on one MI355X (gfx950) with rocprofv3; the raw profiler outputs are not committed.", "",
            "## Commands", "",
            "Counters, one run per pass (each pass fits the per-block counter limits):", ""]
     for p in PMC_PASSES:
@@ -708,8 +708,8 @@ def main():
                                 f"{args.only} ({w})", args.only, srcs), end="")
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the selective scan's "
-              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); sharding the selective "
+              "scan across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -11,8 +11,8 @@ from selective_state_space_scan_amd import binding
 from selective_state_space_scan_amd import inputs as ssin
 
 DEV = "cuda:0"
-# host threads for whole-workload oracle runs (the GPU machine gives one GPU a
-# share of 16 host cores)
+# host threads for whole-workload oracle runs (one GPU's share of the host:
+# at most 16 cores)
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
