@@ -173,6 +173,12 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t
  *                      16-byte aligned, owned by the caller, not read before written.
  * Every sum over batch, time or channels runs in a fixed order, with no
  * atomics, so the gradients are bit-reproducible.
+ * Above 16 states the reverse pass runs once per 16-state slice, and du and
+ * ddelta add up over the slices in ascending order: up to 64 states with z,
+ * or at any dstate without z, the slices run one launch after another, each
+ * adding its parts to the running sums in the workspace and the last adding
+ * the D terms and writing du and ddelta; above 64 states with z they run
+ * side by side and a final pass adds their parts (dz included).
  * Long sequences over few channels run as ss_fwd's time segments (the same
  * count, from dim, dstate and seqlen only): the block states segment by
  * segment after the forward's summary pass (when ckpt is NULL), then the
