@@ -382,17 +382,20 @@ __global__ __launch_bounds__(16 * P) void ss_ssd_fwd_kernel(SsdParams p) {
             // r) in the order the state accumulators hold them, and C is read
             // in that same order
             const bf16_t *crow = Cs + (16 * ti + li) * SM::kPB + 4 * lg;
+            // (the high and low parts in two accumulators: two independent
+            // chains of products, added at the end)
+            f32x4 Ylo = kZero4;
 #pragma unroll
             for (int m2 = 0; m2 < kNT / 2; m2++) {
                 const s16x4 *e0 = hx(2 * m2), *e1 = hx(2 * m2 + 1);
                 const bf16x8_t a = cat8(*reinterpret_cast<const s16x4 *>(crow + 32 * m2),
                                         *reinterpret_cast<const s16x4 *>(crow + 32 * m2 + 16));
                 Y = mfma32(a, cat8(e0[0], e1[0]), Y);
-                Y = mfma32(a, cat8(e0[1], e1[1]), Y);
+                Ylo = mfma32(a, cat8(e0[1], e1[1]), Ylo);
             }
             const f32x4 ec = *reinterpret_cast<const f32x4 *>(scan(buf, 3) + 16 * ti + 4 * lg);
 #pragma unroll
-            for (int r = 0; r < 4; r++) Y[r] *= ec[r];
+            for (int r = 0; r < 4; r++) Y[r] = (Y[r] + Ylo[r]) * ec[r];
         }
         __syncthreads();
         // ---------------- phase 2
@@ -402,15 +405,18 @@ __global__ __launch_bounds__(16 * P) void ss_ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
             for (int j = 0; j < 4; j++)
                 if (j <= ti) xb[j] = *reinterpret_cast<const s16x4 *>(xt + col * SM::kPT + 16 * j + 4 * lg);
+            f32x4 Ylo = kZero4;   // the low parts' products, a chain of their own
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 if (j <= ti) {
                     const s16x4 *e = reinterpret_cast<const s16x4 *>(
                         smem + SM::kWx + ((ti * (ti + 1) / 2 + j) * 64 + lane) * 16);
                     Y = mfma16(e[0], xb[j], Y);
-                    Y = mfma16(e[1], xb[j], Y);
+                    Ylo = mfma16(e[1], xb[j], Ylo);
                 }
             }
+#pragma unroll
+            for (int r = 0; r < 4; r++) Y[r] += Ylo[r];
             // y + D x into the output tile (lane holds y[t = 16 ti + 4 lg + r][col];
             // x at these steps is xb[ti], two values per dword); it leaves in
             // whole rows in the next phase 1
