@@ -591,9 +591,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // Inside the chunk loop indices are 32-bit (seqlen <= 2^26), and global
     // accesses address the wavefront's 4 rows from a scalar base with 32-bit
     // byte offsets (4 rows x seqlen x 4 bytes < 2^32).
+    // Lanes of rows past the last channel load the last channel's row
+    // instead: in bounds, their values are not used and their stores are
+    // skipped, so the loads of whole chunks need no guard.
     const int Ls = int(L), nckS = int(nck);
-    const float *ckb = ws.ckpt + slice * ckpt_state_floats(p.batch, Dm, L) + (b * Dm + dw) * nck * kN;
-    const uint32_t ckoff = uint32_t((rw * nckS * kN + n) * 4);
+    const int64_t dwc = dw < Dm ? dw : Dm - 1;
+    const int rwc = int((row_ok ? d : Dm - 1) - dwc);
+    const float *ckb = ws.ckpt + slice * ckpt_state_floats(p.batch, Dm, L) + (b * Dm + dwc) * nck * kN;
+    const uint32_t ckoff = uint32_t((rwc * nckS * kN + n) * 4);
     // state entering block k; a block past the end (only padding steps) has none
     auto ckpt_at = [&](int k) {
         return (row_ok && k >= 0 && k < nckS) ? ld_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4)))
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     const bool zero_dead = Ns < kN;   // B / C rows past dstate must read as zeros
     // this lane's row of the element-wise tensors; a row's 16 lanes load and
     // store 16 consecutive elements of a 16-step block
-    const int64_t wavebase = (b * Dm + dw) * L;
+    const int64_t wavebase = (b * Dm + dwc) * L;
     const T *gu = static_cast<const T *>(p.u) + wavebase;
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     T *du_fin = static_cast<T *>(p.du) + wavebase;
     T *dd_fin = static_cast<T *>(p.ddelta) + wavebase;
     const float dlast = (chain == 2 && row_ok && ws.chainD) ? ws.chainD[d] : 0.0f;
-    const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
+    const int rowel = rwc * Ls;   // this lane's row, in elements from the wavefront's first
     auto elem_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(T)); };
     auto out_off = [&](int t) { return uint32_t(rowel + t) * uint32_t(sizeof(OutT)); };
     // the saved pre-gate output: each owner lane loads its elements straight
@@ -743,29 +748,48 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
     // at step 0)
     ConvBits<T> xhn = 0;
     const float xwin = CONV != 0 ? conv_window(p, b, d, row_ok, n) : 0.0f;
-    auto load_next = [&](int tc) {
+    // whole: every step of the chunk is before the segment's end (true for
+    // every chunk but a segment's last), so only the row needs care, and the
+    // clamped row above takes it: the loads go unguarded.
+    auto load_next = [&](int tc, bool whole) {
         if constexpr (CONV != 0) xhn = conv_prev_bits<T>(p, b, d, row_ok, tc, n);
 #pragma unroll
         for (int s = 0; s < kNB; s++) {
             const int t = tc + 16 * s + n;
-            hn[s] = ckpt_at(kNB * (tc / kC) + s);
-            if (YP) ypn[s] = ypre_at(t);
+            const int k = kNB * (tc / kC) + s;
+            hn[s] = whole ? ld_global(at_bytes(ckb, ckoff + uint32_t(k * kN * 4))) : ckpt_at(k);
+            if (YP) ypn[s] = whole ? ld_global(at_bytes(ypb, uint32_t(rowel + t) * 4u)) : ypre_at(t);
             if constexpr (PART) {
                 if (chain) {
-                    aun[s] = acc_at(du_b, t);
-                    adn[s] = acc_at(dd_b, t);
+                    aun[s] = whole ? float(ld_global(at_bytes(du_b, out_off(t)))) : acc_at(du_b, t);
+                    adn[s] = whole ? float(ld_global(at_bytes(dd_b, out_off(t)))) : acc_at(dd_b, t);
                 }
             }
             if constexpr (!kStage) {
-                un[s] = elem_at(gu, t);
-                dn[s] = elem_at(gdl, t);
-                if (has_z) zn[s] = elem_at(gz, t);
-                gn[s] = elem_at(gdo, t);
+                un[s] = whole ? to_f32<T>(ld_global(at_bytes(gu, elem_off(t)))) : elem_at(gu, t);
+                dn[s] = whole ? to_f32<T>(ld_global(at_bytes(gdl, elem_off(t)))) : elem_at(gdl, t);
+                if (has_z) zn[s] = whole ? to_f32<T>(ld_global(at_bytes(gz, elem_off(t)))) : elem_at(gz, t);
+                gn[s] = whole ? to_f32<T>(ld_global(at_bytes(gdo, elem_off(t)))) : elem_at(gdo, t);
             }
         }
     };
+    // du and ddelta of one step (of the lane's row), from its owner lane;
+    // with the fused convolution du is not an output
+    auto store_out = [&](int t, float duv, float ddv) {
+        if (row_ok && t < Ls) {
+            if (PART && chain == 2) {
+                st_global(at_bytes(du_fin, elem_off(t)), from_f32<T>(duv));
+                st_global(at_bytes(dd_fin, elem_off(t)), from_f32<T>(ddv));
+            } else {
+                if constexpr (CONV == 0) st_global(at_bytes(du_b, out_off(t)), from_f32<OutT>(duv));
+                st_global(at_bytes(dd_b, out_off(t)), from_f32<OutT>(ddv));
+            }
+        }
+    };
+    int pend_t = 0;   // the previous chunk's last block: its outputs, not yet stored
+    float pend_du = 0.0f, pend_dd = 0.0f;
     if (cend > cbeg) {
-        load_next((cend - 1) * kC);
+        load_next((cend - 1) * kC, false);
         st.fetch(int64_t(cend - 1) * kC, L, tid);
         st.stash(smem + ((cend - 1) & 1) * SM::kBC, zero_dead);
     }
@@ -803,7 +827,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         }
         float hb[kNB];   // block states, used by the blocks after the reload
 #pragma unroll
-        for (int s = 0; s < kNB; s++) hb[s] = hn[s];
+        for (int s = 0; s < kNB; s++) hb[s] = row_ok ? hn[s] : 0.0f;
         if (c > cbeg) st.fetch(t0 - kC, L, tid);
 
         // per-element values: lane (r, n) owns elements 16 s + n of its row
@@ -864,7 +888,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             }
             if (!row_ok) dyv[s] = 0.0f;
         }
-        if (c > cbeg) load_next(t0 - kC);
+        if (CONV == 0 && c < cend - 1) store_out(pend_t, pend_du, pend_dd);
+        if (c > cbeg) load_next(t0 - kC, true);
         // the previous (later) chunk's channel sums, complete since the last
         // barrier and not rewritten before the next one
         if (c < cend - 1) chan_sums(t0 + kC, (c + 1) & 1);
@@ -980,14 +1005,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                     dd = acd[s] + dd_own;
                 }
             }
-            if (row_ok && t0 + col < Ls) {
-                if (PART && chain == 2) {
-                    st_global(at_bytes(du_fin, elem_off(t0 + col)), from_f32<T>(__builtin_fmaf(dlast, dy, du)));
-                    st_global(at_bytes(dd_fin, elem_off(t0 + col)), from_f32<T>(dd));
-                } else {
-                    if constexpr (CONV == 0) st_global(at_bytes(du_b, out_off(t0 + col)), from_f32<OutT>(du));
-                    st_global(at_bytes(dd_b, out_off(t0 + col)), from_f32<OutT>(dd));
-                }
+            const float duo = (PART && chain == 2) ? __builtin_fmaf(dlast, dy, du) : du;
+            if (CONV == 0 && s == 0) {
+                // the chunk's last block: its outputs leave after the next
+                // chunk's per-element phase (issued here, their write
+                // acknowledgments would hold up the wait of the staging
+                // store before the barrier)
+                pend_t = t0 + col;
+                pend_du = duo;
+                pend_dd = dd;
+            } else {
+                store_out(t0 + col, duo, dd);
             }
             if constexpr (CONV != 0) {
                 // the convolution's backward: pre-activation gradient, its
@@ -1007,7 +1035,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                         st_global(at_bytes(dx_b, out_off(t)), from_f32<OutT>(dxv));
                 }
             }
-            if (t0 + col < Ls) dbias_acc += dd_own;
+            // the sum takes the rounded per-element gradient (kept out of an
+            // FMA with its product), whichever way the block's code is laid out
+            float ddr = dd_own;
+            __asm__("" : "+v"(ddr));
+            if (t0 + col < Ls) dbias_acc += ddr;
         }
 
         // The next chunk's B / C go to the other buffer, whose last readers
@@ -1018,6 +1050,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
 
     // the segment's first chunk, complete since the loop's last barrier
     if (cend > cbeg) chan_sums(cbeg * kC, cbeg & 1);
+    if (CONV == 0 && cend > cbeg) store_out(pend_t, pend_du, pend_dd);
 
     // per-row partials of the parameter gradients, per (batch entry, segment)
     const int64_t bs = b * nsg + seg;

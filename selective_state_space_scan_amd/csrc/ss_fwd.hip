@@ -306,9 +306,14 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
     // Inside the chunk loop time indices are 32-bit (seqlen <= 2^26), and the
     // per-row accesses address the wavefront's 4 rows from a scalar base with
     // 32-bit byte offsets (4 rows x seqlen x 4 bytes < 2^32).
+    // Lanes of rows past the last channel address the last channel's row
+    // instead: their loads stay in bounds (the values are not used) and
+    // their stores are skipped, so the loads of whole chunks need no guard.
     const int Ls = int(L);
-    const int64_t wavebase = (b * Dm + dw) * L;
-    const int rowel = rw * Ls;   // this lane's row, in elements from the wavefront's first
+    const int64_t dwc = dw < Dm ? dw : Dm - 1;
+    const int rwc = int((row_ok ? d : Dm - 1) - dwc);
+    const int64_t wavebase = (b * Dm + dwc) * L;
+    const int rowel = rwc * Ls;   // this lane's row, in elements from the wavefront's first
     const T *gu = static_cast<const T *>(p.u) + wavebase;
     const T *gdl = static_cast<const T *>(p.delta) + wavebase;
     const T *gz = has_z ? static_cast<const T *>(p.z) + wavebase : nullptr;
@@ -350,20 +355,25 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
     // consumed its own, so the loads land in the same registers.
     constexpr int kE = kT / 16;
     float un[kE] = {}, dn[kE] = {}, zn[kE] = {};
-    auto load_next = [&](int tc) {
+    // whole: every step of the chunk is before the sequence's end, and the
+    // loads go unguarded (the row is taken care of by the clamped row above)
+    auto elem_whole = [&](const T *g, int t) {
+        return to_f32<T>(ld_global(at_bytes(g, uint32_t(rowel + t) * uint32_t(sizeof(T)))));
+    };
+    auto load_next = [&](int tc, bool whole) {
         if constexpr (kStage) return;
 #pragma unroll
         for (int s = 0; s < kE; s++) {
             const int t = tc + 16 * s + n;
-            un[s] = elem_at(gu, t);
-            dn[s] = elem_at(gdl, t);
-            if (has_z) zn[s] = elem_at(gz, t);
+            un[s] = whole ? elem_whole(gu, t) : elem_at(gu, t);
+            dn[s] = whole ? elem_whole(gdl, t) : elem_at(gdl, t);
+            if (has_z) zn[s] = whole ? elem_whole(gz, t) : elem_at(gz, t);
         }
     };
     const int cbeg = int(tbeg / kT);
     const int cend = int((tend + kT - 1) / kT);
     if (cend > cbeg) {
-        load_next(cbeg * kT);
+        load_next(cbeg * kT, false);
         st.fetch(int64_t(cbeg) * kT, L, tid);
         st.stash(smem, zero_dead);
     }
@@ -443,9 +453,12 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
             }
             if (p.softplus) x = softplus_f32(x);
             dl[s] = (t0 + col < Ls) ? x : 0.0f;   // padding steps leave the state unchanged
-            dlu[s] = dl[s] * uu[s];
+            dlu[s] = row_ok ? dl[s] * uu[s] : 0.0f;
         }
-        if (more) load_next(t0 + kT);
+        if (more) {
+            if (t0 + 2 * kT <= Ls) load_next(t0 + kT, true);
+            else load_next(t0 + kT, false);
+        }
 
 #pragma unroll
         for (int s = 0; s < kE; s++) {
@@ -500,6 +513,12 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
             float y = ypre;
             if (has_z) y *= zz[s] * sigmoid_f32(zz[s]);
             // a row's 16 lanes store 16 consecutive outputs
+            // The next chunk's tiles go to the other buffer, whose last
+            // readers (the chunk before this one) are behind the previous
+            // barrier.  They go before the last block's outputs: the wait
+            // for the staged loads would otherwise also wait for the write
+            // acknowledgments of those stores.
+            if (s == kE - 1 && more) st.stash(smem + ((c + 1 - cbeg) & 1) * SM::kBC, zero_dead);
             const int t = t0 + 16 * s + n;
             if (row_ok && t < Ls) {
                 // (no out: the backward builds its record with this kernel)
@@ -507,10 +526,6 @@ __global__ __launch_bounds__(64 * NW, VEC == 1 ? 2 : (sizeof(T) == 4 ? 3 : 4)) v
                 if (save_yp) st_global(at_bytes(ypb, uint32_t(rowel + t) * 4u), ypre);
             }
         }
-
-        // The next chunk's tiles go to the other buffer, whose last readers
-        // (the chunk before this one) are behind the previous barrier.
-        if (more) st.stash(smem + ((c + 1 - cbeg) & 1) * SM::kBC, zero_dead);
         __syncthreads();
     }
 
