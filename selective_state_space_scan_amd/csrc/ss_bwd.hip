@@ -890,14 +890,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
         }
         if (CONV == 0 && c < cend - 1) store_out(pend_t, pend_du, pend_dd);
         if (c > cbeg) load_next(t0 - kC, true);
-        // the previous (later) chunk's channel sums, complete since the last
-        // barrier and not rewritten before the next one
-        if (c < cend - 1) chan_sums(t0 + kC, (c + 1) & 1);
 
         // blocks last to first: recompute the block's 16 forward steps from
         // its checkpoint (decays and states in registers), then walk them back
 #pragma unroll
         for (int s = kNB - 1; s >= 0; s--) {
+            // the previous (later) chunk's channel sums, complete since the
+            // last barrier and not rewritten before the next one; between
+            // the blocks, where their reads and adds overlap the other
+            // wavefronts' walks (at the chunk's start every wavefront would
+            // wait on them at once)
+            if (s == 0 && c < cend - 1) chan_sums(t0 + kC, (c + 1) & 1);
             const int col = 16 * s + n;
             const float hstart = hb[s];
             float ab[kCk], hs[kCk], v[kCk];
