@@ -967,10 +967,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                     switch (j) {
 #define SS_BC(J)                                          \
     case J:                                               \
-        g = fmac_bcast<J>(g, dy, sC[n][t]);               \
+        g = fmac_bcast<J, J == 15>(g, dy, sC[n][t]);      \
         gc = ab[j] * g;                                   \
         gp = gc * hprev;                                  \
-        dA_acc = fmac_bcast<J>(dA_acc, dlw, gp);          \
+        dA_acc = fmac_bcast<J, J == 15>(dA_acc, dlw, gp); \
         xv = g * row_bcast<J>(dluw);                      \
         yv = hs[j] * row_bcast<J>(dy);                    \
         break;

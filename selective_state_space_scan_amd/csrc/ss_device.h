@@ -74,20 +74,28 @@ __device__ __forceinline__ float row_bcast(float v) {
 // broadcast on x; the compiler folds broadcasts into multiplies and adds but
 // not into fmac.  A DPP read of a VGPR needs two wait states after the VALU
 // op that wrote it; the s_nop in the same asm block provides them whatever
-// instruction the compiler scheduled in front.
+// instruction the compiler scheduled in front.  NOP = false leaves it out, for
+// a chain's later steps whose broadcast source was written long before (the
+// build's assembly is checked for such reads).
 // The lane is spelled into the asm text: an immediate operand would make
 // the compiler treat the statement as a possible memory access and keep LDS
 // loads from moving across it.
-template <int LANE>
+template <int LANE, bool NOP = true>
 __device__ __forceinline__ float fmac_bcast(float acc, float x, float y) {
     static_assert(LANE >= 0 && LANE < 16, "lane within a DPP row");
     switch (LANE) {
 #define SS_FMAC_BCAST(L)                                                                        \
     case L:                                                                                     \
-        __asm__("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #L                         \
-                " row_mask:0xf bank_mask:0xf"                                                   \
-                : "+v"(acc)                                                                     \
-                : "v"(x), "v"(y));                                                              \
+        if constexpr (NOP)                                                                      \
+            __asm__("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #L                    \
+                    " row_mask:0xf bank_mask:0xf"                                               \
+                    : "+v"(acc)                                                                 \
+                    : "v"(x), "v"(y));                                                          \
+        else                                                                                    \
+            __asm__("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #L                                \
+                    " row_mask:0xf bank_mask:0xf"                                               \
+                    : "+v"(acc)                                                                 \
+                    : "v"(x), "v"(y));                                                          \
         break;
         SS_FMAC_BCAST(0) SS_FMAC_BCAST(1) SS_FMAC_BCAST(2) SS_FMAC_BCAST(3)
         SS_FMAC_BCAST(4) SS_FMAC_BCAST(5) SS_FMAC_BCAST(6) SS_FMAC_BCAST(7)
