@@ -786,8 +786,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             }
         }
     };
-    int pend_t = 0;   // the previous chunk's last block: its outputs, not yet stored
-    float pend_du = 0.0f, pend_dd = 0.0f;
     if (cend > cbeg) {
         load_next((cend - 1) * kC, false);
         st.fetch(int64_t(cend - 1) * kC, L, tid);
@@ -888,7 +886,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
             }
             if (!row_ok) dyv[s] = 0.0f;
         }
-        if (CONV == 0 && c < cend - 1) store_out(pend_t, pend_du, pend_dd);
         if (c > cbeg) load_next(t0 - kC, true);
 
         // blocks last to first: recompute the block's 16 forward steps from
@@ -1009,17 +1006,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
                 }
             }
             const float duo = (PART && chain == 2) ? __builtin_fmaf(dlast, dy, du) : du;
-            if (CONV == 0 && s == 0) {
-                // the chunk's last block: its outputs leave after the next
-                // chunk's per-element phase (issued here, their write
-                // acknowledgments would hold up the wait of the staging
-                // store before the barrier)
-                pend_t = t0 + col;
-                pend_du = duo;
-                pend_dd = dd;
-            } else {
-                store_out(t0 + col, duo, dd);
-            }
+            store_out(t0 + col, duo, dd);
             if constexpr (CONV != 0) {
                 // the convolution's backward: pre-activation gradient, its
                 // share of the weight and bias gradients, and the input
@@ -1053,7 +1040,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (VEC == 1 ? 2 : (kC == 16 ? 4 : 
 
     // the segment's first chunk, complete since the loop's last barrier
     if (cend > cbeg) chan_sums(cbeg * kC, cbeg & 1);
-    if (CONV == 0 && cend > cbeg) store_out(pend_t, pend_du, pend_dd);
 
     // per-row partials of the parameter gradients, per (batch entry, segment)
     const int64_t bs = b * nsg + seg;
