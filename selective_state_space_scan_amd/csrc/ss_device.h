@@ -42,15 +42,19 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // softplus(x) = log(1 + e^x) in f32.  For x > 20 the result equals x to
-// within e^-20 relative.  Otherwise log1p(e) with e = e^x is evaluated as
-// log(w) * e / (w - 1), w = 1 + e, which cancels the rounding of w and keeps
-// the result accurate to a few ulp even when e is tiny (w == 1 gives e).
+// within e^-20 relative.  Otherwise log1p(e) with e = e^x is log(w) plus the
+// rounding error of w = 1 + e: d = e - (w - 1) is exact, and
+// log(w + d) = log(w) + d / w + O(d^2).  d matters only while e is small
+// (w < 2), where 1 / w = 2 - w + O(e^2); beyond, d / w is below half an ulp
+// of the result and the term is dropped.  This keeps the result accurate to
+// a few ulp even when e is tiny (w == 1 gives e), with one transcendental
+// fewer than dividing by w - 1.
 __device__ __forceinline__ float softplus_f32(float x) {
     float e = exp2_hw(x * kLog2e);
     float w = 1.0f + e;
-    float wm1 = w - 1.0f;
+    float d = e - (w - 1.0f);
     float lg = __builtin_amdgcn_logf(w) * kLn2;  // v_log_f32 is log2
-    float r = (wm1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(wm1));
+    float r = __builtin_fmaf(d, __builtin_fmaxf(2.0f - w, 0.0f), lg);
     return x > 20.0f ? x : r;
 }
 
