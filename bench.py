@@ -646,8 +646,31 @@ PROFILE_WORKLOADS = {
     "fwd_bf16_1x1536x16384": "mamba130m_long_bf16_1x1536x16384",
     "step_bf16_1x1536x16384": "mamba130m_long_bf16_1x1536x16384",
     "bwd_bf16_1x1536x16384_standalone": "mamba130m_long_bf16_1x1536x16384",
+    "fwd_bf16_1x1536x2048": "mamba130m_prefill_bf16_1x1536x2048",
+    "step_bf16_1x1536x2048": "mamba130m_prefill_bf16_1x1536x2048",
     "copy_1GiB": None,
 }
+
+
+def prefill_regime_detail(to_dev, dev):
+    """One short bf16 sequence (1 x 1536 x 2048), in the automatic regime
+    (sequential at this length) and in the segmented one (ss_set_scan_regime).
+    Mean call times over several calls, HIP events around each call."""
+    from selective_state_space_scan_amd import binding
+    out = {}
+    for regime, tag in ((binding.SS_SCAN_AUTO, "auto"), (binding.SS_SCAN_SEGMENTED, "segmented")):
+        binding.set_scan_regime(regime)
+        try:
+            for only, key in (("fwd_bf16_1x1536x2048", "fwd_ms"),
+                              ("step_bf16_1x1536x2048", "step_ms")):
+                out[f"{tag}_{key}"] = round(run_only(only, 20, 3, to_dev, dev)["ms_per_call"], 5)
+        finally:
+            binding.set_scan_regime(binding.SS_SCAN_AUTO)
+    E = 1 * 1536 * 2048
+    out["segmented_step_elements_per_s"] = E / (out["segmented_step_ms"] * 1e-3)
+    out["speedup_fwd"] = round(out["auto_fwd_ms"] / out["segmented_fwd_ms"], 2)
+    out["speedup_step"] = round(out["auto_step_ms"] / out["segmented_step_ms"], 2)
+    return {"mamba130m_prefill_bf16_1x1536x2048": out}
 
 
 def long_sequence_detail(to_dev, dev):
@@ -947,6 +970,7 @@ def main():
         del sets, outs
 
         detail.update(long_sequence_detail(to_dev, dev))
+        detail.update(prefill_regime_detail(to_dev, dev))
         detail.update(wide_state_detail(hip, lib, to_dev, dev))
         detail.update(conv_detail(hip, lib, to_dev, dev))
         detail.update(conv_scan_detail(hip, lib, to_dev, dev))

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 11
+#define SS_ABI_VERSION 12
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
@@ -87,6 +87,32 @@ int ss_abi_version(void);
  * page, section "Errors".  The pointer stays valid until the thread's next
  * call into the library. */
 const char *ss_last_error(void);
+
+/*
+ * Scan regimes.  The mamba-rs GEMM-modes page, section "What is guaranteed",
+ * names a sequential and a parallel scan regime, each giving the same bits
+ * run to run; each regime here also gives a row the same bits at every
+ * batch size, because its choice depends only on (dim, dstate, seqlen),
+ * never on the batch.  The two are separate bit families (the parallel one
+ * combines per-segment (decay, end state) pairs; both agree with the
+ * oracle to the same tolerance).
+ *   SS_SCAN_AUTO (the default): time segments only for sequences of 8192
+ *     steps or more whose batch entry gives fewer than 3072 wavefronts
+ *     (dim / 4 x ceil(dstate / 16)); every other call sequential.
+ *   SS_SCAN_SEQUENTIAL: never time segments.
+ *   SS_SCAN_SEGMENTED: time segments of at least 512 steps from 1024 steps
+ *     on, for the same narrow calls: the latency regime for calls with few
+ *     rows (a batch-1 prefill), which at large batches costs about 30%.
+ * ss_set_scan_regime sets the regime of the calling thread for every later
+ * ss_fwd, ss_fwd_conv, ss_bwd, ss_bwd_conv, ss_bwd_noalloc call and
+ * workspace-size query on it (SS_EINVAL for an unknown value; the setting
+ * is unchanged then).  A backward that reads a forward's saved record
+ * should run in the forward's regime (in another it is still correct, but
+ * in neither bit family).  ss_scan_regime returns the thread's setting.
+ */
+typedef enum { SS_SCAN_AUTO = 0, SS_SCAN_SEQUENTIAL = 1, SS_SCAN_SEGMENTED = 2 } ss_scan_regime_t;
+ss_status ss_set_scan_regime(int regime);
+int ss_scan_regime(void);
 
 /*
  * Bytes of what ss_fwd can save for ss_bwd (its "ckpt" buffer), all f32:

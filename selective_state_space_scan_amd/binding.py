@@ -16,12 +16,13 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
 # SS_ABI_VERSION of include/ss.h that these signatures follow
-ABI_VERSION = 11
+ABI_VERSION = 12
 _lock = threading.Lock()
 _lib = None
 
 SS_F32, SS_BF16 = 0, 1
 SS_OK, SS_EINVAL, SS_EUNSUPPORTED, SS_EDEVICE = 0, 1, 2, 3
+SS_SCAN_AUTO, SS_SCAN_SEQUENTIAL, SS_SCAN_SEGMENTED = 0, 1, 2
 
 
 class SSError(RuntimeError):
@@ -96,6 +97,10 @@ def load() -> ctypes.CDLL:
             lib.ss_conv1d_bwd.argtypes = [i64] * 4 + [c_int] + [vp] * 3 + [c_int] + [vp] * 7
             lib.ss_conv1d_update.restype = c_int
             lib.ss_conv1d_update.argtypes = [i64] * 3 + [c_int] + [vp] * 4 + [c_int] + [vp] * 2
+            lib.ss_set_scan_regime.restype = c_int
+            lib.ss_set_scan_regime.argtypes = [c_int]
+            lib.ss_scan_regime.restype = c_int
+            lib.ss_scan_regime.argtypes = []
             _lib = lib
     return _lib
 
@@ -143,6 +148,17 @@ def _stream():
 
 def abi_version() -> int:
     return load().ss_abi_version()
+
+
+def set_scan_regime(regime: int) -> None:
+    """Scan regime of the calling thread (SS_SCAN_AUTO, SS_SCAN_SEQUENTIAL or
+    SS_SCAN_SEGMENTED) for every later scan call and workspace query on it."""
+    _check(load().ss_set_scan_regime(int(regime)))
+
+
+def scan_regime() -> int:
+    """The calling thread's scan regime."""
+    return int(load().ss_scan_regime())
 
 
 def ss_ckpt_size(batch, dim, dstate, seqlen) -> int:

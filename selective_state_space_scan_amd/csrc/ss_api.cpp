@@ -18,6 +18,7 @@ thread_local char g_err[512] = "";
 thread_local hipEvent_t *g_prof = nullptr;
 thread_local int g_prof_count = 0;
 thread_local int g_prof_used = 0;
+thread_local int g_regime = SS_SCAN_AUTO;   // ss_set_scan_regime
 
 ss_status fail(ss_status st, const char *fmt, ...) {
     va_list ap;
@@ -159,12 +160,20 @@ int scan_segments(int64_t dim, int nstate, int64_t seqlen, int *seg_len) {
     // one batch entry gives about 6144 (measured at 1536 channels x 16384
     // steps: 8 segments 253 us, 16 segments 231 us).  Short sequences
     // (< 8192 steps) keep one segment: the summary pass would cost more than
-    // it gives back.
+    // it gives back at large batches, and the rule cannot look at the batch
+    // (a row's bits must not depend on it).  The segmented regime, which a
+    // caller asks for when it knows its calls have few rows (a batch-1
+    // prefill), takes segments from 1024 steps on, of at least 512 steps
+    // (measured at 1 x 1536 x 2048 bf16: forward 75 -> 50 us, step 297 ->
+    // 176 us; at 8 x 1536 x 2048 the same segments cost 30%).
     const int64_t waves = (dim + 3) / 4 * state_slices(nstate);
     *seg_len = int(seqlen);
-    if (seqlen < 8192 || waves <= 0 || waves >= 3072) return 1;
+    const bool segmented = g_regime == SS_SCAN_SEGMENTED;
+    if (g_regime == SS_SCAN_SEQUENTIAL || waves <= 0 || waves >= 3072) return 1;
+    if (seqlen < (segmented ? 1024 : 8192)) return 1;
+    const int64_t min_len = segmented ? 512 : 1024;
     int64_t nseg = (6144 + waves - 1) / waves;
-    if (nseg > seqlen / 1024) nseg = seqlen / 1024;
+    if (nseg > seqlen / min_len) nseg = seqlen / min_len;
     if (nseg > 64) nseg = 64;
     if (nseg < 2) return 1;
     const int64_t len = ((seqlen + nseg - 1) / nseg + 63) / 64 * 64;
@@ -194,6 +203,15 @@ int ss_profile_events_used(void) { return g_prof_used; }
 
 
 int ss_abi_version(void) { return SS_ABI_VERSION; }
+
+ss_status ss_set_scan_regime(int regime) {
+    if (regime != SS_SCAN_AUTO && regime != SS_SCAN_SEQUENTIAL && regime != SS_SCAN_SEGMENTED)
+        return fail(SS_EINVAL, "unknown scan regime %d", regime);
+    g_regime = regime;
+    return ok();
+}
+
+int ss_scan_regime(void) { return g_regime; }
 
 const char *ss_last_error(void) { return g_err; }
 

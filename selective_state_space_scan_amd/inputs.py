@@ -74,6 +74,10 @@ WORKLOADS = {
         # the chip, the case the time-segmented scan serves
         Workload("mamba130m_long_bf16_1x1536x16384", "bwd", 1, 1536, 16, 16384, "bf16",
                  seed=SEED_BASE + 6),
+        # a short prefill of one sequence (384 wavefronts sequentially, for
+        # 1024 SIMDs): the case of the segmented scan regime
+        Workload("mamba130m_prefill_bf16_1x1536x2048", "bwd", 1, 1536, 16, 2048, "bf16",
+                 seed=SEED_BASE + 7),
     ]
 }
 

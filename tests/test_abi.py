@@ -39,7 +39,42 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ss_abi_version() == 11
+    assert lib.ss_abi_version() == 12
+
+
+def test_scan_regime_setting(lib):
+    assert binding.scan_regime() == binding.SS_SCAN_AUTO
+    try:
+        for r in (binding.SS_SCAN_SEQUENTIAL, binding.SS_SCAN_SEGMENTED, binding.SS_SCAN_AUTO):
+            binding.set_scan_regime(r)
+            assert binding.scan_regime() == r
+        binding.set_scan_regime(binding.SS_SCAN_SEGMENTED)
+        assert lib.ss_set_scan_regime(3) == binding.SS_EINVAL
+        assert b"regime" in lib.ss_last_error()
+        assert binding.scan_regime() == binding.SS_SCAN_SEGMENTED   # unchanged by the refusal
+    finally:
+        binding.set_scan_regime(binding.SS_SCAN_AUTO)
+
+
+def test_scan_regime_sizes_the_workspaces(lib):
+    """Time segments need summary space: at 1 x 1536 x 2048 only the
+    segmented regime cuts time, at 8192 steps the automatic one does too,
+    and the sequential one never does."""
+    def sizes(L):
+        return (int(lib.ss_fwd_workspace_size(1, 1536, 16, L)),
+                int(lib.ss_bwd_workspace_size(1, 1536, 16, L, binding.SS_BF16)))
+    try:
+        seq = {}
+        for r in (binding.SS_SCAN_SEQUENTIAL, binding.SS_SCAN_AUTO, binding.SS_SCAN_SEGMENTED):
+            binding.set_scan_regime(r)
+            seq[r] = {L: sizes(L) for L in (512, 2048, 8192)}
+    finally:
+        binding.set_scan_regime(binding.SS_SCAN_AUTO)
+    S, A, G = binding.SS_SCAN_SEQUENTIAL, binding.SS_SCAN_AUTO, binding.SS_SCAN_SEGMENTED
+    assert seq[A][2048] == seq[S][2048] and seq[A][512] == seq[S][512]
+    assert seq[G][512] == seq[S][512]                   # too short to cut
+    assert seq[G][2048][0] > seq[S][2048][0]             # the forward's summaries
+    assert seq[A][8192][0] > seq[S][8192][0] and seq[G][8192][0] >= seq[A][8192][0]
 
 
 def test_ckpt_size(lib):
