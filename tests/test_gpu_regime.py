@@ -134,3 +134,42 @@ def test_segmented_regime_leaves_short_and_wide_calls_sequential():
             yb, lb = run_fwd(d, w)
         torch.cuda.synchronize()
         assert torch.equal(bits(ya), bits(yb)) and torch.equal(la, lb), f"{batch}x{dim}x{L}"
+
+
+def test_segmented_regime_fused_convolution_matches_the_separate_calls():
+    """In the segmented regime too, the convolution fused into the scan
+    gives the bits of the separate convolution followed by the scan, forward
+    and backward (the fused backward's scan gradients, and its record-based
+    run the recomputing one's)."""
+    require_gpu()
+    batch, dim, N, L, width = 2, 40, 16, 2100, 4
+    w = ssin.custom("bwd", batch, dim, N, L, "bf16", seed=4 * dim + L)
+    d = dev_inputs(ssin.make(w))
+    rng = np.random.default_rng(L)
+    lim = 1.0 / np.sqrt(width)
+    cw = to_dev(rng.uniform(-lim, lim, (dim, width)).astype(np.float32))
+    cb = to_dev(rng.uniform(-lim, lim, dim).astype(np.float32))
+    ch = to_dev(rng.standard_normal((batch, dim, width - 1)).astype(np.float32))
+    x = d["u"]
+    with regime(binding.SS_SCAN_SEGMENTED):
+        u = binding.ss_conv1d_fwd(x, cw, cb, True, ch)
+        yf = binding.ss_fwd_conv(x, cw, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                 d["delta_bias"], True, conv_bias=cb, conv_init=ch)
+        ys = binding.ss_fwd(u, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                            d["delta_bias"], True)
+        ck = binding.ss_ckpt_empty(x, dstate=N)
+        binding.ss_fwd_conv(x, cw, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                            d["delta_bias"], True, conv_bias=cb, conv_init=ch, ckpt=ck)
+        gf = binding.ss_bwd_conv(x, cw, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                 d["delta_bias"], True, d["dout"], conv_bias=cb, conv_init=ch)
+        gk = binding.ss_bwd_conv(x, cw, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                 d["delta_bias"], True, d["dout"], conv_bias=cb, conv_init=ch,
+                                 ckpt=ck)
+        gs = binding.ss_bwd(u, d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                            d["delta_bias"], True, d["dout"])
+    torch.cuda.synchronize()
+    assert torch.equal(bits(yf), bits(ys))
+    for k in ("ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias"):
+        assert torch.equal(bits(gf[k]), bits(gs[k])), k
+    for k in gf:
+        assert torch.equal(bits(gf[k]), bits(gk[k])), f"{k} with the saved record"
